@@ -1,0 +1,401 @@
+/*
+ * milo_oracle.c -- plain, slow, obviously-correct fp64 CPU oracle for the MILO
+ * hot path (block-wise low-rank KV compression + decode attention over the
+ * compressed blocks).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may load, link or call
+ * this library: only the test-suite, the smoke check and the bench's CPU
+ * baseline leg do.  It shares no code, header, table or helper with the HIP
+ * library; it is written from the pages' description of the method, in their
+ * order and notation.
+ *
+ * Sources (cited by page and section):
+ *   [REV]  evolve.pub AI review of "MILO: Efficient Many-shot In-Context Learning
+ *          with Block-wise Low-rank Compression" (arXiv 2609.29913) -- sections
+ *          "Summary", "Key claims under review", "Strengths" (the paragraph on
+ *          principled, budget-feasible rank allocation, Eqs 5-7) and the FAQ.
+ *   [ABS]  shd-paper.top digest of the same paper -- English abstract and the
+ *          method section (technical framework).
+ *   [DIG]  ai4snews digest -- "arXivInterpretation" and the Figure 1 caption.
+ *
+ * What each routine computes:
+ *   oracle_svd_block    one-sided (Hestenes) cyclic Jacobi SVD of one T x d
+ *                       block: [REV] Summary says each block's K and V get an
+ *                       SVD of their own.  Hestenes 1958; Demmel & Veselic 1992;
+ *                       Golub & Van Loan, Matrix Computations, sec. 8.6.
+ *   oracle_allocate     the greedy of [REV] Strengths (Eqs 5-7): ranks are
+ *                       handed out one at a time to the block whose next
+ *                       singular value brings the largest marginal gain
+ *                       log(1 + sigma^2 / eps^2), until the global rank budget
+ *                       is spent.
+ *   oracle_project      the per-block factor pair A = X V_r, B = V_r^T: the cache
+ *                       is kept per block in low-rank form ([REV] FAQ).
+ *   oracle_round_bf16 / oracle_quant_int8_rows
+ *                       storage encodings.  INT8 with per-row absmax scales is
+ *                       the composition with INT8 quantisation that [REV]
+ *                       Summary and Key claims report.
+ *   oracle_rope / oracle_attention
+ *                       exact softmax attention of a rotary-embedded query over
+ *                       rotary-embedded reconstructed keys: keys are compressed
+ *                       before RoPE ([REV] Summary and Strengths; [DIG] Fig. 1
+ *                       caption), so RoPE is applied to the rebuilt keys at
+ *                       their absolute positions.
+ *
+ * All arithmetic is IEEE fp64 except where a storage format forces a narrower
+ * decision (the INT8 code decision is taken in fp32, the precision the GPU
+ * kernel takes it in).
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_version(void) { return 1; }
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------- */
+/* SVD of one block by one-sided cyclic Jacobi.                              */
+/*                                                                           */
+/* X: T x d row-major.  Outputs sigma[d] (descending) and V (d x d row-major,*/
+/* column i = right singular vector i, sign chosen so that its entry of      */
+/* largest magnitude is positive).  Returns the number of sweeps used, or    */
+/* -1 when max_sweeps were not enough.                                       */
+/* ------------------------------------------------------------------------- */
+int oracle_svd_block(const double *X, int T, int d, double *sigma, double *V,
+                     int max_sweeps)
+{
+    /* W holds the columns of X contiguously: W[i*T + t] = X[t][i]. */
+    double *W = (double *)malloc(sizeof(double) * (size_t)T * d);
+    double *Vc = (double *)malloc(sizeof(double) * (size_t)d * d); /* Vc[i*d+j] = v_i[j] */
+    double *norms = (double *)malloc(sizeof(double) * d);
+    int *order = (int *)malloc(sizeof(int) * d);
+    if (!W || !Vc || !norms || !order) {
+        free(W); free(Vc); free(norms); free(order);
+        return -2;
+    }
+    for (int t = 0; t < T; ++t)
+        for (int i = 0; i < d; ++i)
+            W[(size_t)i * T + t] = X[(size_t)t * d + i];
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j)
+            Vc[(size_t)i * d + j] = (i == j) ? 1.0 : 0.0;
+
+    /* A pair is rotated while its columns are not orthogonal to working
+     * precision; the bound grows like sqrt(T) because gamma is a length-T dot
+     * product (the usual one-sided Jacobi stopping rule). */
+    const double tol = sqrt((double)T) * DBL_EPSILON;
+    int sweeps = -1;
+    for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+        int rotated = 0;
+        for (int p = 0; p < d - 1; ++p) {
+            for (int q = p + 1; q < d; ++q) {
+                double *wp = W + (size_t)p * T, *wq = W + (size_t)q * T;
+                double alpha = 0.0, beta = 0.0, gamma = 0.0;
+                for (int t = 0; t < T; ++t) {
+                    alpha += wp[t] * wp[t];
+                    beta += wq[t] * wq[t];
+                    gamma += wp[t] * wq[t];
+                }
+                if (!(fabs(gamma) > tol * sqrt(alpha * beta)))
+                    continue;
+                /* Rotation that makes columns p and q orthogonal. */
+                double zeta = (beta - alpha) / (2.0 * gamma);
+                double tt;
+                if (fabs(zeta) > 1e150)
+                    tt = 0.5 / zeta;
+                else
+                    tt = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+                double c = 1.0 / sqrt(1.0 + tt * tt);
+                double s = c * tt;
+                for (int t = 0; t < T; ++t) {
+                    double a = wp[t], b = wq[t];
+                    wp[t] = c * a - s * b;
+                    wq[t] = s * a + c * b;
+                }
+                double *vp = Vc + (size_t)p * d, *vq = Vc + (size_t)q * d;
+                for (int j = 0; j < d; ++j) {
+                    double a = vp[j], b = vq[j];
+                    vp[j] = c * a - s * b;
+                    vq[j] = s * a + c * b;
+                }
+                rotated = 1;
+            }
+        }
+        if (!rotated) {
+            sweeps = sweep + 1;
+            break;
+        }
+    }
+
+    /* Singular values are the column norms of the rotated matrix. */
+    for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        const double *wi = W + (size_t)i * T;
+        for (int t = 0; t < T; ++t)
+            acc += wi[t] * wi[t];
+        norms[i] = sqrt(acc);
+        order[i] = i;
+    }
+    /* Stable insertion sort, descending; equal values keep index order. */
+    for (int i = 1; i < d; ++i) {
+        int key = order[i];
+        int j = i - 1;
+        while (j >= 0 && norms[order[j]] < norms[key]) {
+            order[j + 1] = order[j];
+            --j;
+        }
+        order[j + 1] = key;
+    }
+    for (int i = 0; i < d; ++i) {
+        int src = order[i];
+        sigma[i] = norms[src];
+        const double *v = Vc + (size_t)src * d;
+        int jmax = 0;
+        for (int j = 1; j < d; ++j)
+            if (fabs(v[j]) > fabs(v[jmax]))
+                jmax = j;
+        double sgn = (v[jmax] < 0.0) ? -1.0 : 1.0;
+        for (int j = 0; j < d; ++j)
+            V[(size_t)j * d + i] = sgn * v[j];
+    }
+    free(W); free(Vc); free(norms); free(order);
+    return sweeps;
+}
+
+/* Blocks are independent; the loop over them is the only parallelism. */
+int oracle_svd_blocks(const double *X, int n_blocks, int T, int d, double *sigma,
+                      double *V, int *sweeps, int max_sweeps)
+{
+    int worst = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : worst)
+    for (int b = 0; b < n_blocks; ++b) {
+        int s = oracle_svd_block(X + (size_t)b * T * d, T, d, sigma + (size_t)b * d,
+                                 V + (size_t)b * d * d, max_sweeps);
+        if (sweeps)
+            sweeps[b] = s;
+        if (s < worst)
+            worst = s;
+    }
+    return worst; /* 0 when every block converged, negative otherwise */
+}
+
+/* ------------------------------------------------------------------------- */
+/* Rank allocation within one pool ([REV] Strengths, Eqs 5-7).               */
+/*                                                                           */
+/* sigma: n x k, each row descending.  Every block starts at rank 0; each of */
+/* the R steps gives one more rank to the block whose next singular value    */
+/* has the largest gain log(1 + sigma^2/eps^2) (ties: smallest block index). */
+/* A block holds at most k = min(T, d) ranks.  objective = sum of the gains  */
+/* handed out.  Returns the number of ranks handed out (= min(R, n*k)).      */
+/* ------------------------------------------------------------------------- */
+int64_t oracle_allocate(const double *sigma, int n, int k, int64_t R, double eps2,
+                        int32_t *rank, double *objective)
+{
+    double obj = 0.0;
+    int64_t given = 0;
+    for (int b = 0; b < n; ++b)
+        rank[b] = 0;
+    for (int64_t step = 0; step < R; ++step) {
+        int best = -1;
+        double best_gain = 0.0;
+        for (int b = 0; b < n; ++b) {
+            if (rank[b] >= k)
+                continue;
+            double s = sigma[(size_t)b * k + rank[b]];
+            double gain = log1p(s * s / eps2);
+            if (best < 0 || gain > best_gain) {
+                best = b;
+                best_gain = gain;
+            }
+        }
+        if (best < 0)
+            break; /* every block is full */
+        rank[best] += 1;
+        obj += best_gain;
+        ++given;
+    }
+    if (objective)
+        *objective = obj;
+    return given;
+}
+
+/* Objective of an arbitrary allocation (used by the brute-force pin). */
+double oracle_objective(const double *sigma, int n, int k, const int32_t *rank, double eps2)
+{
+    double obj = 0.0;
+    for (int b = 0; b < n; ++b)
+        for (int i = 0; i < rank[b] && i < k; ++i) {
+            double s = sigma[(size_t)b * k + i];
+            obj += log1p(s * s / eps2);
+        }
+    return obj;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Factors of one block: A = X V_r (T x r), B = V_r^T (r x d).               */
+/* ------------------------------------------------------------------------- */
+void oracle_project(const double *X, int T, int d, const double *V, int r, double *A,
+                    double *B)
+{
+    for (int t = 0; t < T; ++t)
+        for (int i = 0; i < r; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < d; ++j)
+                acc += X[(size_t)t * d + j] * V[(size_t)j * d + i];
+            A[(size_t)t * r + i] = acc;
+        }
+    for (int i = 0; i < r; ++i)
+        for (int j = 0; j < d; ++j)
+            B[(size_t)i * d + j] = V[(size_t)j * d + i];
+}
+
+/* X_hat = A B (T x d). */
+void oracle_reconstruct(const double *A, const double *B, int T, int r, int d, double *Xhat)
+{
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < r; ++i)
+                acc += A[(size_t)t * r + i] * B[(size_t)i * d + j];
+            Xhat[(size_t)t * d + j] = acc;
+        }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Storage encodings.                                                        */
+/* ------------------------------------------------------------------------- */
+
+/* Round to the nearest bfloat16 value (8 significant bits, fp32 exponent    */
+/* range, ties to even), directly from fp64.                                  */
+double oracle_round_bf16_one(double x)
+{
+    if (x == 0.0 || !isfinite(x))
+        return x;
+    int e = ilogb(x);           /* floor(log2 |x|) */
+    if (e < -126)
+        e = -126;               /* bf16 subnormals share the fp32 spacing 2^-133 */
+    double quantum = ldexp(1.0, e - 7);
+    double r = nearbyint(x / quantum) * quantum; /* default mode: ties to even */
+    const double max_bf16 = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+    if (fabs(r) > max_bf16)
+        return x > 0 ? INFINITY : -INFINITY;
+    return r;
+}
+
+void oracle_round_bf16(const double *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_round_bf16_one(in[i]);
+}
+
+void oracle_round_f32(const double *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (double)(float)in[i];
+}
+
+/* Per-row absmax INT8: s = max|row| / 127, code = clamp(rint(x / s), +-127), */
+/* ties to even; an all-zero row has s = 0 and codes 0.  The code decision is */
+/* taken in fp32 (the kernel's precision), on the row rounded to fp32.        */
+void oracle_quant_int8_rows(const double *M, int rows, int cols, double *scale,
+                            int8_t *codes, double *dequant)
+{
+    for (int r = 0; r < rows; ++r) {
+        const double *row = M + (size_t)r * cols;
+        float m = 0.0f;
+        for (int c = 0; c < cols; ++c) {
+            float a = fabsf((float)row[c]);
+            if (a > m)
+                m = a;
+        }
+        float s = m / 127.0f;
+        scale[r] = (double)s;
+        for (int c = 0; c < cols; ++c) {
+            int q = 0;
+            if (s > 0.0f) {
+                float v = nearbyintf((float)row[c] / s);
+                if (v > 127.0f) v = 127.0f;
+                if (v < -127.0f) v = -127.0f;
+                q = (int)v;
+            }
+            codes[(size_t)r * cols + c] = (int8_t)q;
+            if (dequant)
+                dequant[(size_t)r * cols + c] = (double)((float)q * s);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Rotary position embedding, half-split pairing: for j < d/2 the pair       */
+/* (x_j, x_{j+d/2}) is rotated by pos * base^(-2j/d).                        */
+/* ------------------------------------------------------------------------- */
+void oracle_rope(double *x, int d, double pos, double base)
+{
+    int h = d / 2;
+    for (int j = 0; j < h; ++j) {
+        double theta = pow(base, -2.0 * j / (double)d);
+        double ang = pos * theta;
+        double c = cos(ang), s = sin(ang);
+        double a = x[j], b = x[j + h];
+        x[j] = a * c - b * s;
+        x[j + h] = a * s + b * c;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Softmax attention of one query over n_tok keys/values.                    */
+/* q: d (pre-RoPE), K: n_tok x d (pre-RoPE), Vv: n_tok x d, pos: n_tok.      */
+/* logit_t = scale * <RoPE(q, q_pos), RoPE(k_t, pos_t)>; out = sum softmax*v. */
+/* ------------------------------------------------------------------------- */
+int oracle_attention(const double *q, int d, int64_t q_pos, const double *K,
+                     const double *Vv, const int64_t *pos, int64_t n_tok, double base,
+                     double scale, double *out)
+{
+    double *qr = (double *)malloc(sizeof(double) * d);
+    double *kr = (double *)malloc(sizeof(double) * d);
+    double *logit = (double *)malloc(sizeof(double) * (n_tok > 0 ? n_tok : 1));
+    if (!qr || !kr || !logit) {
+        free(qr); free(kr); free(logit);
+        return -2;
+    }
+    memcpy(qr, q, sizeof(double) * d);
+    oracle_rope(qr, d, (double)q_pos, base);
+    double m = -INFINITY;
+    for (int64_t t = 0; t < n_tok; ++t) {
+        memcpy(kr, K + (size_t)t * d, sizeof(double) * d);
+        oracle_rope(kr, d, (double)pos[t], base);
+        double acc = 0.0;
+        for (int j = 0; j < d; ++j)
+            acc += qr[j] * kr[j];
+        logit[t] = scale * acc;
+        if (logit[t] > m)
+            m = logit[t];
+    }
+    for (int j = 0; j < d; ++j)
+        out[j] = 0.0;
+    double den = 0.0;
+    for (int64_t t = 0; t < n_tok; ++t) {
+        double p = exp(logit[t] - m);
+        den += p;
+        for (int j = 0; j < d; ++j)
+            out[j] += p * Vv[(size_t)t * d + j];
+    }
+    if (n_tok > 0)
+        for (int j = 0; j < d; ++j)
+            out[j] /= den;
+    free(qr); free(kr); free(logit);
+    return 0;
+}
