@@ -1,0 +1,234 @@
+"""Thin torch-facing binding of libmilo (same names as the C ABI).
+
+PyTorch only supplies device memory and the stream; every step of the path runs
+in the HIP library.  Each function marshals tensors into the C structs, calls
+the C entry point and raises MiloError on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _capi as C
+
+_TORCH_TO_MILO = {torch.float32: C.MILO_F32, torch.bfloat16: C.MILO_BF16, torch.int8: C.MILO_I8}
+_NAME_TO_MILO = {"f32": C.MILO_F32, "bf16": C.MILO_BF16, "i8": C.MILO_I8}
+_MILO_TO_TORCH = {C.MILO_F32: torch.float32, C.MILO_BF16: torch.bfloat16, C.MILO_I8: torch.int8}
+
+
+class MiloError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(message)
+
+
+def lib():
+    return C.load()
+
+
+def _check(status: int):
+    if status != C.MILO_OK:
+        L = lib()
+        raise MiloError(status, f"{L.milo_status_string(status).decode()}: "
+                                f"{L.milo_last_error().decode()}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dtype_code(dtype) -> int:
+    if isinstance(dtype, str):
+        return _NAME_TO_MILO[dtype]
+    return _TORCH_TO_MILO[dtype]
+
+
+def _host_i32(a):
+    arr = (ctypes.c_int32 * len(a))(*[int(v) for v in a])
+    return arr
+
+
+def _host_i64(a):
+    arr = (ctypes.c_int64 * len(a))(*[int(v) for v in a])
+    return arr
+
+
+@dataclass
+class Factors:
+    """Device buffers of one factor set (see milo_factors in include/milo.h)."""
+    dtype: str
+    n_blocks: int
+    block_len: int
+    head_dim: int
+    rank: torch.Tensor
+    a_off: torch.Tensor
+    b_off: torch.Tensor
+    arena: torch.Tensor
+    a_scale: torch.Tensor | None = None
+    b_scale: torch.Tensor | None = None
+
+    @staticmethod
+    def alloc(dtype: str, n_blocks: int, block_len: int, head_dim: int, arena_bytes: int,
+              device="cuda") -> "Factors":
+        dev = torch.device(device)
+        arena = torch.empty(max(int(arena_bytes), 256), dtype=torch.uint8, device=dev)
+        f = Factors(dtype, n_blocks, block_len, head_dim,
+                    rank=torch.zeros(n_blocks, dtype=torch.int32, device=dev),
+                    a_off=torch.zeros(n_blocks, dtype=torch.int64, device=dev),
+                    b_off=torch.zeros(n_blocks, dtype=torch.int64, device=dev),
+                    arena=arena)
+        if dtype == "i8":
+            f.a_scale = torch.zeros(n_blocks * block_len, dtype=torch.float32, device=dev)
+            f.b_scale = torch.zeros(n_blocks * head_dim, dtype=torch.float32, device=dev)
+        return f
+
+    def struct(self) -> C.milo_factors:
+        return C.milo_factors(_NAME_TO_MILO[self.dtype], self.n_blocks, self.block_len,
+                              self.head_dim, _p(self.rank), _p(self.a_off), _p(self.b_off),
+                              _p(self.arena), self.arena.numel(), _p(self.a_scale),
+                              _p(self.b_scale))
+
+    def nbytes(self) -> int:
+        """Bytes the factors occupy (arena payload + INT8 scales actually used)."""
+        used = int(self.rank.sum().item()) * (self.block_len + self.head_dim) * \
+            {"f32": 4, "bf16": 2, "i8": 1}[self.dtype]
+        if self.dtype == "i8":
+            used += 4 * (self.n_blocks * self.block_len + int(self.rank.sum().item()))
+        return used
+
+
+def milo_abi_version() -> int:
+    return int(lib().milo_abi_version())
+
+
+def milo_arena_bytes(dtype: str, block_len: int, head_dim: int, pool_ptr, budget) -> int:
+    n_pools = len(pool_ptr) - 1
+    n = lib().milo_arena_bytes(_NAME_TO_MILO[dtype], block_len, head_dim,
+                               ctypes.cast(_host_i32(pool_ptr), ctypes.c_void_p), n_pools,
+                               ctypes.cast(_host_i64(budget), ctypes.c_void_p))
+    if n == 0 and lib().milo_last_error():
+        raise MiloError(C.MILO_E_INVALID, lib().milo_last_error().decode())
+    return int(n)
+
+
+def milo_compress_workspace_bytes(n_blocks: int, block_len: int, head_dim: int = 128) -> int:
+    return int(lib().milo_compress_workspace_bytes(n_blocks, block_len, head_dim))
+
+
+def milo_compress_blocks(x: torch.Tensor, pool_ptr, budget, eps2: float, sigma_out: torch.Tensor,
+                         factors: Factors, objective_out: torch.Tensor | None = None,
+                         sweeps_out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, row0: torch.Tensor | None = None,
+                         row_stride: int | None = None, n_blocks: int | None = None,
+                         block_len: int | None = None, stream=None) -> None:
+    """Compress blocks of ``x``: a contiguous [n_blocks, T, d] tensor, or any tensor
+    addressed through ``row0``/``row_stride`` (with n_blocks and block_len given)."""
+    if row0 is None and row_stride is None:
+        n_blocks, block_len, d = x.shape
+        row_stride = d
+    d = factors.head_dim
+    blocks = C.milo_blocks(_p(x), _dtype_code(x.dtype), _p(row0), int(row_stride), int(n_blocks),
+                           int(block_len), int(d))
+    fs = factors.struct()
+    pp = _host_i32(pool_ptr)
+    bb = _host_i64(budget)
+    wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel())
+    st = lib().milo_compress_blocks(ctypes.byref(blocks), ctypes.cast(pp, ctypes.c_void_p),
+                                    len(pool_ptr) - 1, ctypes.cast(bb, ctypes.c_void_p),
+                                    float(eps2), _p(sigma_out), _p(objective_out),
+                                    ctypes.byref(fs), _p(sweeps_out), _p(workspace),
+                                    ctypes.byref(wsb), _stream(stream))
+    if st == C.MILO_E_WORKSPACE and workspace is None:
+        workspace = torch.empty(int(wsb.value), dtype=torch.uint8, device=x.device)
+        return milo_compress_blocks(x, pool_ptr, budget, eps2, sigma_out, factors, objective_out,
+                                    sweeps_out, workspace, row0, row_stride, n_blocks, block_len,
+                                    stream)
+    _check(st)
+
+
+def milo_allocate_ranks(sigma: torch.Tensor, max_rank: int, pool_ptr, budget, eps2: float,
+                        rank_out: torch.Tensor, objective_out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None) -> None:
+    n_blocks, d = sigma.shape
+    pp = _host_i32(pool_ptr)
+    bb = _host_i64(budget)
+    wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel())
+    st = lib().milo_allocate_ranks(_p(sigma), n_blocks, d, int(max_rank),
+                                   ctypes.cast(pp, ctypes.c_void_p), len(pool_ptr) - 1,
+                                   ctypes.cast(bb, ctypes.c_void_p), float(eps2), _p(rank_out),
+                                   _p(objective_out), _p(workspace), ctypes.byref(wsb),
+                                   _stream(stream))
+    if st == C.MILO_E_WORKSPACE and workspace is None:
+        workspace = torch.empty(int(wsb.value), dtype=torch.uint8, device=sigma.device)
+        return milo_allocate_ranks(sigma, max_rank, pool_ptr, budget, eps2, rank_out,
+                                   objective_out, workspace, stream)
+    _check(st)
+
+
+def milo_reconstruct(factors: Factors, block_ids: torch.Tensor, out: torch.Tensor,
+                     stream=None) -> None:
+    fs = factors.struct()
+    st = lib().milo_reconstruct(ctypes.byref(fs), _p(block_ids), int(block_ids.numel()), _p(out),
+                                _dtype_code(out.dtype), _stream(stream))
+    _check(st)
+
+
+def milo_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: Factors,
+                          blocks_per_seq: int, n_kv_heads: int, out: torch.Tensor,
+                          sel_ptr: torch.Tensor | None = None, sel_blk: torch.Tensor | None = None,
+                          sel_max: int = 0, tail_k: torch.Tensor | None = None,
+                          tail_v: torch.Tensor | None = None, tail_len: torch.Tensor | None = None,
+                          tail_pos0: torch.Tensor | None = None, rope_base: float = 1e6,
+                          softmax_scale: float | None = None, split_len: int = 0,
+                          workspace: torch.Tensor | None = None, stream=None) -> None:
+    batch, n_q, d = q.shape
+    ks, vs = k.struct(), v.struct()
+    tail_cap = 0 if tail_k is None else int(tail_k.shape[2])
+    args = C.milo_decode_args(
+        _p(q), _dtype_code(q.dtype), _p(q_pos), batch, n_q, int(n_kv_heads), d,
+        ctypes.pointer(ks), ctypes.pointer(vs), int(blocks_per_seq), _p(sel_ptr), _p(sel_blk),
+        int(sel_max), _p(tail_k), _p(tail_v),
+        _dtype_code(tail_k.dtype) if tail_k is not None else C.MILO_BF16, tail_cap,
+        _p(tail_len), _p(tail_pos0), float(rope_base),
+        float(softmax_scale if softmax_scale is not None else d ** -0.5), _p(out),
+        _dtype_code(out.dtype), int(split_len), _p(workspace),
+        0 if workspace is None else workspace.numel())
+    need = ctypes.c_size_t(0)
+    st = lib().milo_decode_attention(ctypes.byref(args), ctypes.byref(need), _stream(stream))
+    if st == C.MILO_E_WORKSPACE and workspace is None:
+        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=q.device)
+        return milo_decode_attention(q, q_pos, k, v, blocks_per_seq, n_kv_heads, out, sel_ptr,
+                                     sel_blk, sel_max, tail_k, tail_v, tail_len, tail_pos0,
+                                     rope_base, softmax_scale, split_len, workspace, stream)
+    _check(st)
+
+
+def decode_workspace_bytes(q: torch.Tensor, k: Factors, v: Factors, blocks_per_seq: int,
+                           n_kv_heads: int, out: torch.Tensor, **kw) -> int:
+    """Size query for milo_decode_attention (no work is enqueued)."""
+    batch, n_q, d = q.shape
+    ks, vs = k.struct(), v.struct()
+    tail_k = kw.get("tail_k")
+    args = C.milo_decode_args(
+        _p(q), _dtype_code(q.dtype), _p(kw.get("q_pos", q)), batch, n_q, int(n_kv_heads), d,
+        ctypes.pointer(ks), ctypes.pointer(vs), int(blocks_per_seq), _p(kw.get("sel_ptr")),
+        _p(kw.get("sel_blk")), int(kw.get("sel_max", 0)), _p(tail_k), _p(kw.get("tail_v")),
+        _dtype_code(tail_k.dtype) if tail_k is not None else C.MILO_BF16,
+        0 if tail_k is None else int(tail_k.shape[2]), _p(kw.get("tail_len")),
+        _p(kw.get("tail_pos0")), float(kw.get("rope_base", 1e6)), float(d ** -0.5), _p(out),
+        _dtype_code(out.dtype), int(kw.get("split_len", 0)), None, 0)
+    need = ctypes.c_size_t(0)
+    st = lib().milo_decode_attention(ctypes.byref(args), ctypes.byref(need), None)
+    if st != C.MILO_E_WORKSPACE:
+        _check(st)
+    return int(need.value)

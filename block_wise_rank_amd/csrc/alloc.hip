@@ -1,0 +1,180 @@
+// Global rank allocation within a pool of blocks.
+//
+// The allocation maximises sum_b sum_{i < r_b} log(1 + sigma_{b,i}^2 / eps^2)
+// under sum_b r_b <= R by handing out one rank at a time to the block with the
+// largest marginal gain (evolve.pub review of arXiv 2609.29913, Strengths,
+// Eqs 5-7).  The gain is strictly increasing in sigma and every block's
+// singular values are non-increasing, so the greedy hands out exactly the R'
+// = min(R, n k) largest singular values of the pool in the order
+// (sigma desc, block asc, index asc), and r_b counts block b's share.  This
+// kernel computes that selection directly:
+//   1. the R'-th largest sigma, tau, by a bitwise search over the fp32 bit
+//      patterns (monotone for sigma >= 0): 31 rounds, each counting per block
+//      with a binary search over its sorted row;
+//   2. every value > tau is taken; the remaining R' - #{> tau} ranks go to the
+//      values == tau in block order (an exclusive scan over the blocks).
+// Exact integer work on fp32 keys: the ranks do not depend on eps, and equal
+// the greedy's bit for bit.  One workgroup of 256 threads per pool; thread t
+// owns a contiguous run of blocks so prefix sums follow block order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace milo {
+namespace {
+
+__device__ __forceinline__ uint32_t key_bits(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return (u >> 31) ? 0u : u;  // -0.0 (or any negative) counts as 0
+}
+
+// Number of leading entries of a non-increasing row whose key is >= c.
+__device__ __forceinline__ int count_ge(const float *row, int k, uint32_t c) {
+    int lo = 0, hi = k;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (key_bits(row[mid]) >= c)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+template <typename Tv>
+__device__ Tv block_sum(Tv v, Tv *red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    Tv tot = red[0] + red[1] + red[2] + red[3];
+    return tot;
+}
+
+// Exclusive prefix over the 256 threads (thread order), returns the prefix.
+__device__ int64_t block_exclusive_scan(int64_t v, int64_t *buf) {
+    const int tid = threadIdx.x;
+    __syncthreads();
+    buf[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const int64_t add = tid >= o ? buf[tid - o] : 0;
+        __syncthreads();
+        buf[tid] += add;
+        __syncthreads();
+    }
+    return buf[tid] - v;
+}
+
+__global__ __launch_bounds__(256) void alloc_kernel(
+    const float *__restrict__ sigma, int pitch, int k, const int32_t *__restrict__ pool_ptr,
+    const int64_t *__restrict__ budget, const int64_t *__restrict__ pool_base, int pool_lo,
+    int blk_lo, float eps2, int32_t *__restrict__ rank, double *__restrict__ objective,
+    int64_t *__restrict__ a_off, int64_t *__restrict__ b_off, int T, int elem_bytes) {
+    __shared__ int64_t red64[4];
+    __shared__ double redd[4];
+    __shared__ int64_t scan_buf[256];
+
+    const int pool = pool_lo + blockIdx.x;
+    const int b_lo = pool_ptr[pool], b_hi = pool_ptr[pool + 1];
+    const int n = b_hi - b_lo;
+    const int tid = threadIdx.x;
+    const int per = (n + 255) / 256;
+    const int my_lo = b_lo + tid * per;
+    const int my_hi = min(b_hi, my_lo + per);
+    const int64_t cap = static_cast<int64_t>(n) * k;
+    const int64_t R = budget[pool] < cap ? budget[pool] : cap;
+
+    // 1. tau = key of the R-th largest value (only needed when 0 < R < cap).
+    uint32_t tau = 0;
+    const bool partial = R > 0 && R < cap;
+    if (partial) {
+        for (int bit = 30; bit >= 0; --bit) {
+            const uint32_t cand = tau | (1u << bit);
+            int64_t cnt = 0;
+            for (int b = my_lo; b < my_hi; ++b)
+                cnt += count_ge(sigma + static_cast<int64_t>(b - blk_lo) * pitch, k, cand);
+            cnt = block_sum<int64_t>(cnt, red64);
+            if (cnt >= R) tau = cand;  // uniform decision
+        }
+    }
+
+    // 2. ranks: strictly greater values, then ties in block order.
+    int64_t gt_sum = 0, eq_sum = 0;
+    for (int b = my_lo; b < my_hi; ++b) {
+        const float *row = sigma + static_cast<int64_t>(b - blk_lo) * pitch;
+        if (partial) {
+            const int ge = count_ge(row, k, tau);
+            const int gt = tau == 0xffffffffu ? 0 : count_ge(row, k, tau + 1);
+            gt_sum += gt;
+            eq_sum += ge - gt;
+        }
+    }
+    int64_t need = 0, eq_before = 0;
+    if (partial) {
+        const int64_t gt_tot = block_sum<int64_t>(gt_sum, red64);
+        need = R - gt_tot;
+        eq_before = block_exclusive_scan(eq_sum, scan_buf);
+    }
+    int64_t rank_sum = 0;
+    double obj = 0.0;
+    for (int b = my_lo; b < my_hi; ++b) {
+        const float *row = sigma + static_cast<int64_t>(b - blk_lo) * pitch;
+        int r;
+        if (!partial) {
+            r = R == 0 ? 0 : k;
+        } else {
+            const int ge = count_ge(row, k, tau);
+            const int gt = tau == 0xffffffffu ? 0 : count_ge(row, k, tau + 1);
+            int64_t extra = need - eq_before;
+            extra = extra < 0 ? 0 : (extra > ge - gt ? ge - gt : extra);
+            eq_before += ge - gt;
+            r = gt + static_cast<int>(extra);
+        }
+        rank[b] = r;
+        rank_sum += r;
+        for (int i = 0; i < r; ++i) {
+            const double s = static_cast<double>(row[i]);
+            obj += log1p(s * s / static_cast<double>(eps2));
+        }
+    }
+    // Objective (reduction order is fixed by the thread layout: deterministic).
+    {
+        const int lane = tid & 63, wave = tid >> 6;
+        double v = obj;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+        __syncthreads();
+        if (lane == 0) redd[wave] = v;
+        __syncthreads();
+        if (tid == 0 && objective) objective[pool] = ((redd[0] + redd[1]) + redd[2]) + redd[3];
+    }
+    // Arena offsets: the pool's blocks are laid out back to back in block order,
+    // each as A^T (r x T) followed by B (r x d).
+    if (a_off) {
+        const int64_t before = block_exclusive_scan(rank_sum, scan_buf);
+        int64_t off = pool_base[pool] + before * (T + kD) * elem_bytes;
+        for (int b = my_lo; b < my_hi; ++b) {
+            const int r = rank[b];
+            a_off[b] = off;
+            b_off[b] = off + static_cast<int64_t>(r) * T * elem_bytes;
+            off += static_cast<int64_t>(r) * (T + kD) * elem_bytes;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_alloc(const float *sigma, int sigma_pitch, int max_rank, const int32_t *pool_ptr,
+                        const int64_t *budget, const int64_t *pool_base, int pool_lo, int n_pools,
+                        int blk_lo, float eps2, int32_t *rank, double *objective, int64_t *a_off,
+                        int64_t *b_off, int block_len, int elem_bytes, hipStream_t st) {
+    if (n_pools <= 0) return hipSuccess;
+    hipLaunchKernelGGL(alloc_kernel, dim3(static_cast<unsigned>(n_pools)), dim3(256), 0, st, sigma,
+                       sigma_pitch, max_rank, pool_ptr, budget, pool_base, pool_lo, blk_lo, eps2,
+                       rank, objective, a_off, b_off, block_len, elem_bytes);
+    return hipGetLastError();
+}
+
+}  // namespace milo

@@ -1,0 +1,350 @@
+// libmilo C ABI: host-side validation, workspace planning and kernel sequencing.
+// Every check runs before anything is enqueued, so a failing call writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/milo.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+milo_status fail(milo_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+milo_status ok() {
+    g_last_error.clear();
+    return MILO_OK;
+}
+
+milo_status hip_fail(hipError_t e, const char *what) {
+    return fail(MILO_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(milo_dtype t) { return t == MILO_F32 ? 4 : (t == MILO_BF16 ? 2 : 1); }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int kD = 128;
+constexpr int kMaxSweeps = 30;
+constexpr float kJacobiTol = 1e-6f;
+constexpr size_t kMat = sizeof(float) * kD * kD;  // one 128 x 128 fp32 matrix
+
+// Split the token dimension of the Gram when there are too few blocks to fill
+// the chip (partials are summed in a fixed order by the eigensolver).
+int gram_splits(int n_blocks, int block_len) {
+    int s = 1;
+    while (n_blocks * s < 512 && s < 8 && (block_len / (s * 2)) % 64 == 0 && block_len / (s * 2) >= 64)
+        s *= 2;
+    return s;
+}
+
+size_t tables_bytes(int n_pools) {
+    return align_up(sizeof(int32_t) * (n_pools + 1), 256) + align_up(sizeof(int64_t) * n_pools, 256) * 2;
+}
+
+size_t chunk_bytes(int n_blocks, int block_len) {
+    const int s = gram_splits(n_blocks, block_len);
+    return static_cast<size_t>(n_blocks) * (s + 1) * kMat;
+}
+
+milo_status check_pools(const int32_t *pool_ptr, int32_t n_pools, const int64_t *budget,
+                        int32_t n_blocks) {
+    if (n_pools < 0) return fail(MILO_E_INVALID, "n_pools must be >= 0 (got %d)", n_pools);
+    if (!pool_ptr) return fail(MILO_E_INVALID, "pool_ptr is NULL");
+    if (n_pools > 0 && !budget) return fail(MILO_E_INVALID, "budget is NULL");
+    if (pool_ptr[0] != 0) return fail(MILO_E_INVALID, "pool_ptr[0] must be 0 (got %d)", pool_ptr[0]);
+    for (int p = 0; p < n_pools; ++p) {
+        if (pool_ptr[p + 1] < pool_ptr[p])
+            return fail(MILO_E_INVALID, "pool_ptr must be non-decreasing (pool %d)", p);
+        if (budget[p] < 0) return fail(MILO_E_INVALID, "budget[%d] is negative", p);
+    }
+    if (pool_ptr[n_pools] != n_blocks)
+        return fail(MILO_E_INVALID, "pool_ptr[n_pools] = %d but n_blocks = %d", pool_ptr[n_pools],
+                    n_blocks);
+    return MILO_OK;
+}
+
+int64_t pool_ranks(const int32_t *pool_ptr, const int64_t *budget, int p, int k) {
+    const int64_t cap = static_cast<int64_t>(pool_ptr[p + 1] - pool_ptr[p]) * k;
+    return budget[p] < cap ? budget[p] : cap;
+}
+
+}  // namespace
+
+extern "C" {
+
+int milo_abi_version(void) { return MILO_ABI_VERSION; }
+
+const char *milo_last_error(void) { return g_last_error.c_str(); }
+
+const char *milo_status_string(milo_status s) {
+    switch (s) {
+        case MILO_OK: return "MILO_OK";
+        case MILO_E_INVALID: return "MILO_E_INVALID";
+        case MILO_E_UNSUPPORTED: return "MILO_E_UNSUPPORTED";
+        case MILO_E_WORKSPACE: return "MILO_E_WORKSPACE";
+        case MILO_E_HIP: return "MILO_E_HIP";
+    }
+    return "MILO_E_UNKNOWN";
+}
+
+size_t milo_arena_bytes(milo_dtype dtype, int32_t block_len, int32_t head_dim,
+                        const int32_t *pool_ptr, int32_t n_pools, const int64_t *budget) {
+    if (dtype != MILO_F32 && dtype != MILO_BF16 && dtype != MILO_I8) {
+        fail(MILO_E_INVALID, "unknown dtype %d", static_cast<int>(dtype));
+        return 0;
+    }
+    if (block_len <= 0 || head_dim <= 0) {
+        fail(MILO_E_INVALID, "block_len and head_dim must be positive");
+        return 0;
+    }
+    if (!pool_ptr || n_pools < 0 || (n_pools > 0 && !budget)) {
+        fail(MILO_E_INVALID, "invalid pool table");
+        return 0;
+    }
+    const int k = block_len < head_dim ? block_len : head_dim;
+    size_t total = 0;
+    for (int p = 0; p < n_pools; ++p) {
+        if (pool_ptr[p + 1] < pool_ptr[p] || budget[p] < 0) {
+            fail(MILO_E_INVALID, "invalid pool %d", p);
+            return 0;
+        }
+        total += static_cast<size_t>(pool_ranks(pool_ptr, budget, p, k)) *
+                 static_cast<size_t>(block_len + head_dim) * elem_bytes(dtype);
+    }
+    g_last_error.clear();
+    return total;
+}
+
+size_t milo_compress_workspace_bytes(int32_t n_blocks, int32_t block_len, int32_t head_dim) {
+    (void)head_dim;
+    if (n_blocks < 0 || block_len <= 0) return 0;
+    // pool tables are sized for the worst case of one pool per block
+    return tables_bytes(n_blocks) + chunk_bytes(n_blocks, block_len);
+}
+
+milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr, int32_t n_pools,
+                                 const int64_t *budget, float eps2, float *sigma_out,
+                                 double *objective_out, milo_factors *out, int32_t *sweeps_out,
+                                 void *workspace, size_t *workspace_bytes, void *stream) {
+    if (!in) return fail(MILO_E_INVALID, "in is NULL");
+    if (!out) return fail(MILO_E_INVALID, "out is NULL");
+    if (!workspace_bytes) return fail(MILO_E_INVALID, "workspace_bytes is NULL");
+    if (in->head_dim != kD) return fail(MILO_E_UNSUPPORTED, "head_dim must be 128 (got %d)", in->head_dim);
+    if (in->block_len < 128 || in->block_len % 64 != 0)
+        return fail(MILO_E_UNSUPPORTED, "block_len must be a multiple of 64 and >= 128 (got %d)",
+                    in->block_len);
+    if (in->n_blocks < 0) return fail(MILO_E_INVALID, "n_blocks must be >= 0");
+    if (in->dtype != MILO_F32 && in->dtype != MILO_BF16)
+        return fail(MILO_E_UNSUPPORTED, "input dtype must be MILO_F32 or MILO_BF16");
+    if (in->row_stride < in->head_dim)
+        return fail(MILO_E_INVALID, "row_stride (%lld) must be >= head_dim",
+                    static_cast<long long>(in->row_stride));
+    const int xe = elem_bytes(in->dtype);
+    if ((in->row_stride * xe) % 16 != 0)
+        return fail(MILO_E_INVALID, "row_stride must keep rows 16-byte aligned");
+    if (in->n_blocks > 0 && (!in->x || !aligned(in->x, 16)))
+        return fail(MILO_E_INVALID, "x must be a non-NULL 16-byte aligned device pointer");
+    if (!(eps2 > 0.f) || !std::isfinite(eps2)) return fail(MILO_E_INVALID, "eps2 must be finite and > 0");
+    milo_status st = check_pools(pool_ptr, n_pools, budget, in->n_blocks);
+    if (st != MILO_OK) return st;
+    if (in->n_blocks > 0 && !sigma_out) return fail(MILO_E_INVALID, "sigma_out is NULL");
+    // factor set
+    const bool pair_ok = (in->dtype == MILO_F32 && out->dtype == MILO_F32) ||
+                         (in->dtype == MILO_BF16 && out->dtype == MILO_BF16) ||
+                         (in->dtype == MILO_BF16 && out->dtype == MILO_I8);
+    if (!pair_ok) return fail(MILO_E_UNSUPPORTED, "unsupported dtype pair (in %d -> factors %d)",
+                              static_cast<int>(in->dtype), static_cast<int>(out->dtype));
+    if (out->n_blocks != in->n_blocks || out->block_len != in->block_len || out->head_dim != in->head_dim)
+        return fail(MILO_E_INVALID, "factor set geometry does not match the blocks");
+    const size_t need_arena = milo_arena_bytes(out->dtype, in->block_len, in->head_dim, pool_ptr, n_pools, budget);
+    if (in->n_blocks > 0) {
+        if (!out->rank || !out->a_off || !out->b_off)
+            return fail(MILO_E_INVALID, "factor rank/a_off/b_off must be set");
+        if (need_arena > 0 && (!out->arena || !aligned(out->arena, 256)))
+            return fail(MILO_E_INVALID, "arena must be a non-NULL 256-byte aligned device pointer");
+        if (out->arena_bytes < need_arena)
+            return fail(MILO_E_INVALID, "arena_bytes %zu < %zu needed", out->arena_bytes, need_arena);
+        if (out->dtype == MILO_I8 && (!out->a_scale || !out->b_scale))
+            return fail(MILO_E_INVALID, "MILO_I8 factors need a_scale and b_scale");
+    }
+    // workspace plan: pool tables, then per-chunk Gram partials + eigenvectors
+    const size_t tab = tables_bytes(n_pools);
+    const size_t full = tab + chunk_bytes(in->n_blocks, in->block_len);
+    int max_pool = 0;
+    for (int p = 0; p < n_pools; ++p) max_pool = std::max(max_pool, pool_ptr[p + 1] - pool_ptr[p]);
+    // a chunk needs at least one Gram partial and the eigenvectors per block
+    const size_t minimum = tab + static_cast<size_t>(max_pool) * 2 * kMat;
+    if (!workspace || *workspace_bytes < minimum) {
+        *workspace_bytes = full;
+        return fail(MILO_E_WORKSPACE, "workspace of %zu bytes needed (minimum %zu)", full, minimum);
+    }
+    if (!aligned(workspace, 256)) return fail(MILO_E_INVALID, "workspace must be 256-byte aligned");
+    const size_t ws_cap = *workspace_bytes;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int T = in->block_len;
+    const int k = T < kD ? T : kD;
+    const int fe = elem_bytes(out->dtype);
+    const int x_type = in->dtype == MILO_F32 ? milo::kF32 : milo::kBF16;
+    const int f_type = out->dtype == MILO_F32 ? milo::kF32 : (out->dtype == MILO_BF16 ? milo::kBF16 : milo::kI8);
+
+    // pool tables -> device
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    int32_t *d_pool_ptr = reinterpret_cast<int32_t *>(ws);
+    int64_t *d_budget = reinterpret_cast<int64_t *>(ws + align_up(sizeof(int32_t) * (n_pools + 1), 256));
+    int64_t *d_base = reinterpret_cast<int64_t *>(reinterpret_cast<uint8_t *>(d_budget) +
+                                                  align_up(sizeof(int64_t) * n_pools, 256));
+    std::vector<int64_t> base(n_pools);
+    int64_t acc = 0;
+    for (int p = 0; p < n_pools; ++p) {
+        base[p] = acc;
+        acc += pool_ranks(pool_ptr, budget, p, k) * static_cast<int64_t>(T + kD) * fe;
+    }
+    hipError_t e;
+    if (n_pools > 0) {
+        e = hipMemcpyAsync(d_pool_ptr, pool_ptr, sizeof(int32_t) * (n_pools + 1), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "pool table upload");
+        e = hipMemcpyAsync(d_budget, budget, sizeof(int64_t) * n_pools, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "budget upload");
+        e = hipMemcpyAsync(d_base, base.data(), sizeof(int64_t) * n_pools, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "pool base upload");
+    }
+    uint8_t *chunk_ws = ws + tab;
+    const size_t chunk_cap = ws_cap - tab;
+
+    const uint8_t *xb = static_cast<const uint8_t *>(in->x);
+    int p0 = 0;
+    while (p0 < n_pools) {
+        // grow the chunk while its workspace fits
+        int p1 = p0 + 1;
+        while (p1 < n_pools &&
+               static_cast<size_t>(pool_ptr[p1 + 1] - pool_ptr[p0]) * 2 * kMat <= chunk_cap)
+            ++p1;
+        const int b0 = pool_ptr[p0], nb = pool_ptr[p1] - b0;
+        if (nb > 0) {
+            // Gram token splits: enough workgroups to fill the chip, within the workspace.
+            const int fit = static_cast<int>(chunk_cap / (static_cast<size_t>(nb) * kMat)) - 1;
+            int splits = gram_splits(nb, T);
+            while (splits > 1 && splits > fit) splits /= 2;  // powers of two keep T / splits % 64 == 0
+            float *gpart = reinterpret_cast<float *>(chunk_ws);
+            float *vt = reinterpret_cast<float *>(chunk_ws + static_cast<size_t>(nb) * splits * kMat);
+            // block b of the chunk: row0 points into the caller's table, else blocks back to back
+            const int64_t *row0 = in->row0 ? in->row0 + b0 : nullptr;
+            const void *xc = in->row0 ? static_cast<const void *>(xb)
+                                      : static_cast<const void *>(xb + static_cast<size_t>(b0) * T * in->row_stride * xe);
+            float *sig = sigma_out + static_cast<size_t>(b0) * kD;
+            if ((e = milo::launch_gram(xc, x_type, row0, in->row_stride, T, nb, splits, gpart, s)) != hipSuccess)
+                return hip_fail(e, "gram launch");
+            if ((e = milo::launch_jacobi(gpart, splits, nb, vt, sweeps_out ? sweeps_out + b0 : nullptr,
+                                         kMaxSweeps, kJacobiTol, s)) != hipSuccess)
+                return hip_fail(e, "jacobi launch");
+            if ((e = milo::launch_refine(xc, x_type, row0, in->row_stride, T, nb, vt, sig, s)) != hipSuccess)
+                return hip_fail(e, "refine launch");
+            if ((e = milo::launch_alloc(sig, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
+                                        eps2, out->rank, objective_out, out->a_off, out->b_off, T, fe,
+                                        s)) != hipSuccess)
+                return hip_fail(e, "alloc launch");
+            if ((e = milo::launch_project(xc, x_type, row0, in->row_stride, T, nb, vt, out->rank + b0,
+                                          out->a_off + b0, out->b_off + b0, out->arena, f_type,
+                                          out->a_scale ? out->a_scale + static_cast<size_t>(b0) * T : nullptr,
+                                          out->b_scale ? out->b_scale + static_cast<size_t>(b0) * kD : nullptr,
+                                          s)) != hipSuccess)
+                return hip_fail(e, "project launch");
+        } else {
+            if ((e = milo::launch_alloc(sigma_out, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
+                                        eps2, out->rank, objective_out, out->a_off, out->b_off, T, fe,
+                                        s)) != hipSuccess)
+                return hip_fail(e, "alloc launch");
+        }
+        p0 = p1;
+    }
+    return ok();
+}
+
+milo_status milo_allocate_ranks(const float *sigma, int32_t n_blocks, int32_t head_dim,
+                                int32_t max_rank, const int32_t *pool_ptr, int32_t n_pools,
+                                const int64_t *budget, float eps2, int32_t *rank_out,
+                                double *objective_out, void *workspace, size_t *workspace_bytes,
+                                void *stream) {
+    if (head_dim <= 0) return fail(MILO_E_INVALID, "head_dim must be > 0");
+    if (max_rank < 1 || max_rank > head_dim)
+        return fail(MILO_E_INVALID, "max_rank must be in [1, head_dim] (got %d)", max_rank);
+    if (n_blocks < 0) return fail(MILO_E_INVALID, "n_blocks must be >= 0");
+    if (n_blocks > 0 && (!sigma || !rank_out)) return fail(MILO_E_INVALID, "sigma and rank_out must be set");
+    if (!(eps2 > 0.f) || !std::isfinite(eps2)) return fail(MILO_E_INVALID, "eps2 must be finite and > 0");
+    if (!workspace_bytes) return fail(MILO_E_INVALID, "workspace_bytes is NULL");
+    milo_status st = check_pools(pool_ptr, n_pools, budget, n_blocks);
+    if (st != MILO_OK) return st;
+    const size_t need = tables_bytes(n_pools);
+    if (!workspace || *workspace_bytes < need) {
+        *workspace_bytes = need;
+        return fail(MILO_E_WORKSPACE, "workspace of %zu bytes needed", need);
+    }
+    if (!aligned(workspace, 256)) return fail(MILO_E_INVALID, "workspace must be 256-byte aligned");
+    if (n_pools == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    int32_t *d_pool_ptr = reinterpret_cast<int32_t *>(ws);
+    int64_t *d_budget = reinterpret_cast<int64_t *>(ws + align_up(sizeof(int32_t) * (n_pools + 1), 256));
+    hipError_t e;
+    if ((e = hipMemcpyAsync(d_pool_ptr, pool_ptr, sizeof(int32_t) * (n_pools + 1), hipMemcpyHostToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(d_budget, budget, sizeof(int64_t) * n_pools, hipMemcpyHostToDevice, s)) != hipSuccess)
+        return hip_fail(e, "pool table upload");
+    e = milo::launch_alloc(sigma, head_dim, max_rank, d_pool_ptr, d_budget, nullptr, 0, n_pools, 0, eps2,
+                           rank_out, objective_out, nullptr, nullptr, 0, 0, s);
+    if (e != hipSuccess) return hip_fail(e, "alloc launch");
+    return ok();
+}
+
+milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, int32_t n_ids,
+                             void *x_out, milo_dtype out_dtype, void *stream) {
+    if (!f) return fail(MILO_E_INVALID, "factor set is NULL");
+    if (f->head_dim != kD) return fail(MILO_E_UNSUPPORTED, "head_dim must be 128");
+    if (f->block_len < 128 || f->block_len % 64 != 0)
+        return fail(MILO_E_UNSUPPORTED, "block_len must be a multiple of 64 and >= 128");
+    if (f->dtype != MILO_F32 && f->dtype != MILO_BF16 && f->dtype != MILO_I8)
+        return fail(MILO_E_INVALID, "unknown factor dtype");
+    if (out_dtype != MILO_F32 && out_dtype != MILO_BF16)
+        return fail(MILO_E_UNSUPPORTED, "out_dtype must be MILO_F32 or MILO_BF16");
+    if (n_ids < 0) return fail(MILO_E_INVALID, "n_ids must be >= 0");
+    if (n_ids == 0) return ok();
+    if (!block_ids || !x_out) return fail(MILO_E_INVALID, "block_ids and x_out must be set");
+    if (!f->rank || !f->a_off || !f->b_off || !f->arena)
+        return fail(MILO_E_INVALID, "factor set pointers must be set");
+    if (f->dtype == MILO_I8 && (!f->a_scale || !f->b_scale))
+        return fail(MILO_E_INVALID, "MILO_I8 factors need scales");
+    const int ft = f->dtype == MILO_F32 ? milo::kF32 : (f->dtype == MILO_BF16 ? milo::kBF16 : milo::kI8);
+    hipError_t e = milo::launch_reconstruct(f->arena, ft, f->rank, f->a_off, f->b_off, f->a_scale,
+                                            f->b_scale, f->block_len, block_ids, n_ids, x_out,
+                                            out_dtype == MILO_F32 ? milo::kF32 : milo::kBF16,
+                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "reconstruct launch");
+    return ok();
+}
+
+milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_needed,
+                                  void *stream) {
+    (void)a; (void)workspace_needed; (void)stream;
+    return fail(MILO_E_UNSUPPORTED, "decode attention is not available in this build");
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Device helpers shared by the libmilo kernels (gfx950 / CDNA4 only).
+//
+// MFMA operand layouts used throughout (wave64):
+//   v_mfma_f32_32x32x16_bf16: lane l supplies A[m = l%32][k = 8*(l/32) + e] and
+//     B[k = 8*(l/32) + e][n = l%32] for e = 0..7; it receives
+//     C[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32] in accumulator i = 0..15.
+//   v_mfma_f32_16x16x32_bf16: lane l supplies A[m = l%16][k = 8*(l/16) + e] and
+//     B[k = 8*(l/16) + e][n = l%16]; it receives C[m = 4*(l/16) + i][n = l%16],
+//     i = 0..3.
+// Because a contraction only needs A and B to agree on which k each slot
+// holds, kernels freely permute k inside a step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace milo {
+
+constexpr int kD = 128;  // head_dim supported by every kernel
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Exact split of an fp32 value into three bf16 terms: f = hi + mid + lo for
+// every normal f whose terms stay normal (8 + 8 + 8 significant bits).
+__device__ __forceinline__ void split3_bf16(float f, uint16_t &hi, uint16_t &mid, uint16_t &lo) {
+    hi = f32_to_bf16_bits(f);
+    float r1 = f - bf16_bits_to_f32(hi);
+    mid = f32_to_bf16_bits(r1);
+    float r2 = r1 - bf16_bits_to_f32(mid);
+    lo = f32_to_bf16_bits(r2);
+}
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(const u16x8_t &a, const u16x8_t &b,
+                                                 const f32x16_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(const u16x8_t &a, const u16x8_t &b,
+                                                const f32x4_t &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+    f32x16_t z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+__device__ __forceinline__ f32x4_t zero4() {
+    f32x4_t z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = 0.f;
+    return z;
+}
+
+// Reductions over the 32 lanes of one half of a wave64 (xor offsets < 32 never
+// cross halves).
+__device__ __forceinline__ float half_max(float v) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace milo

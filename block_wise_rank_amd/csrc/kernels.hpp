@@ -1,0 +1,87 @@
+// Host-side launchers of the libmilo kernels (one translation unit per kernel
+// family; each launcher lives next to its kernel).  All launches are
+// asynchronous on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace milo {
+
+enum ElemType : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
+
+// G_b = X_b^T X_b, written as `splits` partial sums per block:
+// gpart[(b * splits + s) * 128 * 128 + i * 128 + j].
+hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
+                       int block_len, int n_blocks, int splits, float *gpart, hipStream_t st);
+
+// Symmetric eigensolve of G_b (sum of the partials) by parallel-order cyclic
+// Jacobi in LDS.  vt[b][i][:] = eigenvector i (unsorted); sweeps[b] = sweeps
+// used (negative when max_sweeps was hit).  sweeps may be null.
+hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt,
+                         int32_t *sweeps, int max_sweeps, float tol, hipStream_t st);
+
+// sigma_i = ||X_b v_i|| in fp32-accurate arithmetic, then eigenvectors sorted
+// by descending sigma (in place in vt) with the largest-magnitude entry of each
+// made positive; sigma[b][0..128) descending.
+hipError_t launch_refine(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
+                         int block_len, int n_blocks, float *vt, float *sigma, hipStream_t st);
+
+// Rank allocation for pools [pool_lo, pool_lo + n_pools) of the device pool
+// tables: ranks of blocks, per-pool objective (may be null), and when a_off is
+// non-null the arena offsets (pool_base[p] + prefix of rank * (T + d) * elem).
+hipError_t launch_alloc(const float *sigma, int sigma_pitch, int max_rank,
+                        const int32_t *pool_ptr, const int64_t *budget, const int64_t *pool_base,
+                        int pool_lo, int n_pools, int blk_lo, float eps2, int32_t *rank,
+                        double *objective, int64_t *a_off, int64_t *b_off, int block_len,
+                        int elem_bytes, hipStream_t st);
+
+// Factor pairs from sorted eigenvectors and ranks: A_b^T (rank-major) and B_b
+// rows into the arena, plus INT8 scales.
+hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
+                          int block_len, int n_blocks, const float *vt, const int32_t *rank,
+                          const int64_t *a_off, const int64_t *b_off, void *arena,
+                          int out_type, float *a_scale, float *b_scale, hipStream_t st);
+
+// X_hat = A B for the listed blocks.
+hipError_t launch_reconstruct(const void *arena, int f_type, const int32_t *rank,
+                              const int64_t *a_off, const int64_t *b_off, const float *a_scale,
+                              const float *b_scale, int block_len, const int32_t *ids, int n_ids,
+                              void *out, int out_type, hipStream_t st);
+
+struct DecodeParams {
+    const void *q;
+    int q_type;
+    const int64_t *q_pos;
+    int batch, n_q_heads, n_kv_heads, group;
+    // factor sets (same storage type)
+    int f_type;
+    int block_len, blocks_per_seq;
+    const int32_t *k_rank, *v_rank;
+    const int64_t *k_aoff, *k_boff, *v_aoff, *v_boff;
+    const uint8_t *k_arena, *v_arena;
+    const float *k_ascale, *k_bscale, *v_ascale, *v_bscale;
+    // selection
+    const int32_t *sel_ptr, *sel_blk;
+    int n_sel;  // splits-per-block slots reserved per sequence (sel_max or blocks_per_seq)
+    // tail
+    const void *tail_k, *tail_v;
+    int tail_type, tail_cap;
+    const int32_t *tail_len;
+    const int64_t *tail_pos0;
+    double rope_base;
+    float softmax_scale;
+    void *out;
+    int out_type;
+    int split_len;
+    int block_splits;  // block_len / split_len
+    int tail_splits;   // tail_cap / split_len (0 without tail)
+    int n_splits;      // n_sel * block_splits + tail_splits
+    float *part_ml;    // [batch][Hkv][n_splits][group][2]  (m, l) in log2 units
+    float *part_o;     // [batch][Hkv][n_splits][group][128]
+};
+
+size_t decode_workspace_bytes(const DecodeParams &p);
+hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
+
+}  // namespace milo

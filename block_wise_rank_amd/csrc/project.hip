@@ -1,0 +1,242 @@
+// Factor pairs of each block from its sorted right singular vectors:
+//   B_b = V_r^T (r_b x d rows), stored in the factor dtype;
+//   A_b = X_b B~_b^T with B~_b the STORED (rounded or quantised) B_b, so that the
+//         rebuilt block A_b B~_b is X_b projected on the stored basis;
+//   A_b is written transposed (rank-major, r_b rows of T tokens).
+// INT8: every row of B_b (one per rank) and every row of A_b (one per token)
+// gets an absmax scale s = max|row| / 127 and codes rint(x / s) clamped to
+// +-127, decided in fp32.
+//
+// A^T = B~ X^T runs on bf16 MFMA (M = rank, N = token, K = feature): the
+// fragments of B~ stay in registers (one 32-rank tile per wave) while 32-token
+// tiles of X stream in as 16-byte loads of 8 consecutive features.  fp32
+// storage splits V (and fp32 X) into three bf16 terms for fp32-accurate
+// products.  Grid: (block, 256-token part).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace milo {
+namespace {
+
+constexpr int kTokensPerWG = 256;
+
+template <int NX, int OUT>
+__global__ __launch_bounds__(256) void project_kernel(
+    const void *__restrict__ x, const int64_t *__restrict__ row0, int64_t row_stride, int T,
+    const float *__restrict__ vt, const int32_t *__restrict__ rank,
+    const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off,
+    uint8_t *__restrict__ arena, float *__restrict__ a_scale, float *__restrict__ b_scale) {
+    constexpr int NS = (OUT == kF32) ? 3 : 1;  // bf16 terms of the B operand
+    __shared__ float sB_rows[kD];
+    __shared__ float tmax[4][32];
+
+    const int blk = blockIdx.x, part = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = rank[blk];
+    const int t_begin = part * kTokensPerWG;
+    const int t_end = min(T, t_begin + kTokensPerWG);
+    if (r == 0) {
+        if constexpr (OUT == kI8)
+            for (int t = t_begin + tid; t < t_end; t += 256) a_scale[static_cast<int64_t>(blk) * T + t] = 0.f;
+        return;
+    }
+    const int ebytes = OUT == kF32 ? 4 : (OUT == kBF16 ? 2 : 1);
+    uint8_t *Ab = arena + a_off[blk];
+    uint8_t *Bb = arena + b_off[blk];
+
+    // ---- B fragments: row i = 32 wave + lane % 32, k slots j = 16 ks + 8 (lane / 32) + e.
+    const int i = 32 * wave + (lane & 31);
+    const bool row_ok = i < r;
+    const float *vrow = vt + static_cast<int64_t>(blk) * kD * kD + static_cast<int64_t>(i) * kD;
+    float v[8][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        if (row_ok) {
+            const float4 a = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5));
+            const float4 b = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5) + 4);
+            v[ks][0] = a.x; v[ks][1] = a.y; v[ks][2] = a.z; v[ks][3] = a.w;
+            v[ks][4] = b.x; v[ks][5] = b.y; v[ks][6] = b.z; v[ks][7] = b.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[ks][e] = 0.f;
+        }
+    }
+    float sB = 1.f;
+    if constexpr (OUT == kI8) {
+        float m = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[ks][e]));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        sB = __fdiv_rn(m, 127.f);
+    }
+    u16x8_t fa[NS][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (OUT == kF32) {
+                uint16_t h, mm, l;
+                split3_bf16(v[ks][e], h, mm, l);
+                fa[0][ks][e] = h;
+                fa[1 % NS][ks][e] = mm;
+                fa[2 % NS][ks][e] = l;
+            } else if constexpr (OUT == kBF16) {
+                fa[0][ks][e] = f32_to_bf16_bits(v[ks][e]);
+            } else {
+                float q = sB > 0.f ? rintf(__fdiv_rn(v[ks][e], sB)) : 0.f;
+                q = fminf(fmaxf(q, -127.f), 127.f);
+                v[ks][e] = q;  // keep the code for the B store
+                fa[0][ks][e] = f32_to_bf16_bits(q);  // |q| <= 127 is exact in bf16
+            }
+        }
+
+    // ---- B rows (first part only) and B scales.
+    if (part == 0 && row_ok) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int j0 = 16 * ks + 8 * (lane >> 5);
+            uint8_t *dst = Bb + (static_cast<int64_t>(i) * kD + j0) * ebytes;
+            if constexpr (OUT == kF32) {
+                float4 *d4 = reinterpret_cast<float4 *>(dst);
+                d4[0] = make_float4(v[ks][0], v[ks][1], v[ks][2], v[ks][3]);
+                d4[1] = make_float4(v[ks][4], v[ks][5], v[ks][6], v[ks][7]);
+            } else if constexpr (OUT == kBF16) {
+                *reinterpret_cast<u16x8_t *>(dst) = fa[0][ks];
+            } else {
+                uint2 w;
+                w.x = (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][0])))) |
+                      (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][1]))) << 8) |
+                      (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][2]))) << 16) |
+                      (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][3]))) << 24);
+                w.y = (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][4])))) |
+                      (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][5]))) << 8) |
+                      (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][6]))) << 16) |
+                      (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][7]))) << 24);
+                *reinterpret_cast<uint2 *>(dst) = w;
+            }
+        }
+        if constexpr (OUT == kI8)
+            if (lane < 32) b_scale[static_cast<int64_t>(blk) * kD + i] = sB;
+    }
+    if constexpr (OUT == kI8) {
+        if (lane < 32) sB_rows[i] = row_ok ? sB : 0.f;
+        __syncthreads();
+    }
+
+    const int64_t base = row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride;
+    const bool wave_active = 32 * wave < r;
+    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+        const int t = t0 + (lane & 31);
+        f32x16_t acc = zero16();
+        if (wave_active) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int j0 = 16 * ks + 8 * (lane >> 5);
+                if constexpr (NX == 1) {
+                    const u16x8_t fb = *reinterpret_cast<const u16x8_t *>(
+                        static_cast<const uint16_t *>(x) + base + static_cast<int64_t>(t) * row_stride + j0);
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) acc = mfma32x32x16(fa[s][ks], fb, acc);
+                } else {
+                    const float *xr = static_cast<const float *>(x) + base +
+                                      static_cast<int64_t>(t) * row_stride + j0;
+                    const float4 a = reinterpret_cast<const float4 *>(xr)[0];
+                    const float4 b = reinterpret_cast<const float4 *>(xr)[1];
+                    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                    u16x8_t fb[3];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        uint16_t h, mm, l;
+                        split3_bf16(f[e], h, mm, l);
+                        fb[0][e] = h;
+                        fb[1][e] = mm;
+                        fb[2][e] = l;
+                    }
+#pragma unroll
+                    for (int sa = 0; sa < NS; ++sa)
+#pragma unroll
+                        for (int sb = 0; sb < 3; ++sb)
+                            if (sa + sb <= 2) acc = mfma32x32x16(fa[sa][ks], fb[sb], acc);
+                }
+            }
+        }
+        // acc[q]: rank row i' = 32 wave + 8 (q / 4) + 4 (lane / 32) + q % 4, token t.
+        if constexpr (OUT != kI8) {
+            if (wave_active) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int ir = 32 * wave + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    if (ir < r) {
+                        if constexpr (OUT == kF32)
+                            reinterpret_cast<float *>(Ab)[static_cast<int64_t>(ir) * T + t] = acc[q];
+                        else
+                            reinterpret_cast<uint16_t *>(Ab)[static_cast<int64_t>(ir) * T + t] =
+                                f32_to_bf16_bits(acc[q]);
+                    }
+                }
+            }
+        } else {
+            float val[16];
+            float m = 0.f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int ir = 32 * wave + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                val[q] = (ir < r) ? acc[q] * sB_rows[ir] : 0.f;
+                m = fmaxf(m, fabsf(val[q]));
+            }
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            if (lane < 32) tmax[wave][lane] = m;
+            __syncthreads();
+            const int tl = lane & 31;
+            const float mt = fmaxf(fmaxf(tmax[0][tl], tmax[1][tl]), fmaxf(tmax[2][tl], tmax[3][tl]));
+            const float sA = __fdiv_rn(mt, 127.f);
+            if (wave_active) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int ir = 32 * wave + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    if (ir < r) {
+                        float c = sA > 0.f ? rintf(__fdiv_rn(val[q], sA)) : 0.f;
+                        c = fminf(fmaxf(c, -127.f), 127.f);
+                        reinterpret_cast<int8_t *>(Ab)[static_cast<int64_t>(ir) * T + t] =
+                            static_cast<int8_t>(c);
+                    }
+                }
+            }
+            if (wave == 0 && lane < 32) a_scale[static_cast<int64_t>(blk) * T + t] = sA;
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
+                          int block_len, int n_blocks, const float *vt, const int32_t *rank,
+                          const int64_t *a_off, const int64_t *b_off, void *arena, int out_type,
+                          float *a_scale, float *b_scale, hipStream_t st) {
+    if (n_blocks <= 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(n_blocks),
+                    static_cast<unsigned>((block_len + kTokensPerWG - 1) / kTokensPerWG));
+    uint8_t *ar = static_cast<uint8_t *>(arena);
+#define MILO_PROJECT(NX, OUT)                                                                     \
+    hipLaunchKernelGGL((project_kernel<NX, OUT>), grid, dim3(256), 0, st, x, row0, row_stride,    \
+                       block_len, vt, rank, a_off, b_off, ar, a_scale, b_scale)
+    if (x_type == kF32 && out_type == kF32)
+        MILO_PROJECT(3, kF32);
+    else if (x_type == kBF16 && out_type == kBF16)
+        MILO_PROJECT(1, kBF16);
+    else if (x_type == kBF16 && out_type == kI8)
+        MILO_PROJECT(1, kI8);
+    else if (x_type == kBF16 && out_type == kF32)
+        MILO_PROJECT(1, kF32);
+    else if (x_type == kF32 && out_type == kBF16)
+        MILO_PROJECT(3, kBF16);
+    else
+        MILO_PROJECT(3, kI8);
+#undef MILO_PROJECT
+    return hipGetLastError();
+}
+
+}  // namespace milo

@@ -1,0 +1,167 @@
+// Singular values as sigma_i = ||X_b v_i||, then the eigenvectors sorted by
+// descending sigma with a sign convention (largest-magnitude entry positive).
+//
+// The eigenvalues of an fp32 Gram are only accurate to about u * ||G||, which
+// is too coarse for the small singular values (sigma^2 ~ 1e-5 next to
+// sigma_0^2 ~ 1).  The norm ||X v_i|| is a Rayleigh quotient: its error is
+// second order in the eigenvector error, so recomputing it directly from X
+// gives singular values accurate to a few fp32 ulps of sigma_0.
+//
+// Y^T = V^T X^T runs on bf16 MFMA with V^T (fp32) split exactly into three
+// bf16 terms (and X too when it is fp32), keeping the products whose term
+// orders sum to <= 2; fp32 accumulation.  One workgroup (4 waves) per block;
+// wave w owns eigenvectors 32w .. 32w + 31 and keeps their fragments in
+// registers while it streams every 32-token tile of X straight from memory
+// (8 consecutive features per lane = one 16-byte load for bf16).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace milo {
+namespace {
+
+template <int NX>
+__global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
+                                                     const int64_t *__restrict__ row0,
+                                                     int64_t row_stride, int T,
+                                                     float *__restrict__ vt,
+                                                     float *__restrict__ sigma) {
+    __shared__ float Vs[kD * kD];  // 64 KiB, row i = eigenvector i
+    __shared__ float ss[kD];       // sum of squares per eigenvector
+    __shared__ float sig[kD];
+    __shared__ int perm[kD];
+    __shared__ float sgn[kD];
+
+    const int blk = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float *vblk = vt + static_cast<int64_t>(blk) * kD * kD;
+    for (int e = tid; e < kD * kD / 4; e += 256)
+        reinterpret_cast<float4 *>(Vs)[e] = reinterpret_cast<const float4 *>(vblk)[e];
+    __syncthreads();
+
+    // A fragments: row i = 32 * wave + lane % 32, k slots j = 16 ks + 8 (lane / 32) + e.
+    u16x8_t fa[3][8];
+    {
+        const int i = 32 * wave + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = Vs[i * kD + 16 * ks + 8 * (lane >> 5) + e];
+                uint16_t h, m, l;
+                split3_bf16(v, h, m, l);
+                fa[0][ks][e] = h;
+                fa[1][ks][e] = m;
+                fa[2][ks][e] = l;
+            }
+    }
+
+    const int64_t base = row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride;
+    float acc2[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc2[r] = 0.f;
+
+    for (int t0 = 0; t0 < T; t0 += 32) {
+        const int t = t0 + (lane & 31);
+        f32x16_t acc = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int j0 = 16 * ks + 8 * (lane >> 5);
+            if constexpr (NX == 1) {
+                const uint16_t *xr = static_cast<const uint16_t *>(x) + base +
+                                     static_cast<int64_t>(t) * row_stride + j0;
+                const u16x8_t fb = *reinterpret_cast<const u16x8_t *>(xr);
+                acc = mfma32x32x16(fa[0][ks], fb, acc);
+                acc = mfma32x32x16(fa[1][ks], fb, acc);
+                acc = mfma32x32x16(fa[2][ks], fb, acc);
+            } else {
+                const float *xr = static_cast<const float *>(x) + base +
+                                  static_cast<int64_t>(t) * row_stride + j0;
+                const float4 v0 = reinterpret_cast<const float4 *>(xr)[0];
+                const float4 v1 = reinterpret_cast<const float4 *>(xr)[1];
+                const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                u16x8_t fb[3];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint16_t h, m, l;
+                    split3_bf16(f[e], h, m, l);
+                    fb[0][e] = h;
+                    fb[1][e] = m;
+                    fb[2][e] = l;
+                }
+#pragma unroll
+                for (int sa = 0; sa < 3; ++sa)
+#pragma unroll
+                    for (int sb = 0; sb < 3; ++sb)
+                        if (sa + sb <= 2) acc = mfma32x32x16(fa[sa][ks], fb[sb], acc);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc2[r] += acc[r] * acc[r];
+    }
+    // acc2[r] belongs to row i = 32 wave + 8 (r / 4) + 4 (lane / 32) + r % 4, token lane % 32.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float tot = half_sum(acc2[r]);
+        if ((lane & 31) == 0) ss[32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] = tot;
+    }
+    __syncthreads();
+
+    // Sort descending (rank by counting; ties keep index order) and fix signs.
+    if (tid < kD) {
+        const float si = sqrtf(ss[tid]);
+        int pos = 0;
+        for (int j = 0; j < kD; ++j) {
+            const float sj = sqrtf(ss[j]);
+            pos += (sj > si) || (sj == si && j < tid);
+        }
+        perm[pos] = tid;
+        sig[pos] = si;
+    }
+    // Sign of eigenvector i: its largest-magnitude entry (first one on ties) positive.
+    for (int i = wave; i < kD; i += 4) {
+        const float a = Vs[i * kD + lane], b = Vs[i * kD + 64 + lane];
+        float best = fabsf(a);
+        int bidx = lane;
+        float bval = a;
+        if (fabsf(b) > best) {
+            best = fabsf(b);
+            bidx = 64 + lane;
+            bval = b;
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float ob = __shfl_xor(best, o, 64);
+            const int oi = __shfl_xor(bidx, o, 64);
+            const float ov = __shfl_xor(bval, o, 64);
+            if (ob > best || (ob == best && oi < bidx)) {
+                best = ob;
+                bidx = oi;
+                bval = ov;
+            }
+        }
+        if (lane == 0) sgn[i] = (bval < 0.f) ? -1.f : 1.f;
+    }
+    __syncthreads();
+    if (tid < kD) sigma[static_cast<int64_t>(blk) * kD + tid] = sig[tid];
+    for (int e = tid; e < kD * kD; e += 256) {
+        const int pos = e >> 7, j = e & 127;
+        const int src = perm[pos];
+        vblk[e] = sgn[src] * Vs[src * kD + j];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_refine(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
+                         int block_len, int n_blocks, float *vt, float *sigma, hipStream_t st) {
+    if (n_blocks <= 0) return hipSuccess;
+    if (x_type == kBF16)
+        hipLaunchKernelGGL(refine_kernel<1>, dim3(static_cast<unsigned>(n_blocks)), dim3(256), 0,
+                           st, x, row0, row_stride, block_len, vt, sigma);
+    else
+        hipLaunchKernelGGL(refine_kernel<3>, dim3(static_cast<unsigned>(n_blocks)), dim3(256), 0,
+                           st, x, row0, row_stride, block_len, vt, sigma);
+    return hipGetLastError();
+}
+
+}  // namespace milo

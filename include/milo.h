@@ -1,0 +1,239 @@
+/*
+ * milo.h -- C ABI of libmilo: block-wise low-rank compression of a KV cache and
+ * decode attention over the compressed blocks (the MILO method), for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method sources, cited by page and section:
+ *   [REV] evolve.pub AI review of "MILO: Efficient Many-shot In-Context Learning
+ *         with Block-wise Low-rank Compression" (arXiv 2609.29913): Summary,
+ *         Strengths (rank allocation, Eqs 5-7), FAQ.
+ *   [ABS] shd-paper.top digest of the paper: English abstract; method section
+ *         ("technical framework": blocking, block-level low-rank compression,
+ *         dynamic rank-budget allocation).
+ *   [DIG] ai4snews digest: arXivInterpretation; Figure 1 caption (pre-RoPE keys).
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers unless the comment says "host".
+ *     Sizes are element counts unless they say "bytes".
+ *   - The caller owns every buffer.  The library never allocates device memory,
+ *     never frees, and never synchronises; it enqueues kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream) and returns.
+ *     Outputs are valid once the stream has reached that point; inputs must
+ *     stay alive until then.  Small host arrays (pool tables) are copied to the
+ *     device inside the call, so they may be freed when the call returns.
+ *   - Every argument is validated on the host before anything is enqueued, so a
+ *     call that returns an error has written nothing.  Errors are status codes;
+ *     nothing is thrown across the ABI.  milo_last_error() gives a
+ *     human-readable reason for the last failure on the calling thread.
+ *   - head_dim must be 128 and block_len a multiple of 64 with block_len >= 128
+ *     (MILO_E_UNSUPPORTED otherwise).
+ *   - Calls on the same stream are ordered; calls on different streams that
+ *     share an output or workspace buffer race.
+ */
+#ifndef MILO_H
+#define MILO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MILO_ABI_VERSION 1
+
+typedef enum milo_status {
+    MILO_OK = 0,
+    MILO_E_INVALID = 1,     /* null pointer, negative or inconsistent size, bad CSR       */
+    MILO_E_UNSUPPORTED = 2, /* head_dim != 128, block_len not a multiple of 64 or < 128, */
+                            /* or an unsupported dtype combination                        */
+    MILO_E_WORKSPACE = 3,   /* workspace missing or too small; *_bytes holds the need   */
+    MILO_E_HIP = 4          /* a HIP runtime call or a kernel launch failed              */
+} milo_status;
+
+typedef enum milo_dtype {
+    MILO_F32 = 0,
+    MILO_BF16 = 1,
+    MILO_I8 = 2 /* factor storage only: per-row absmax INT8 with fp32 scales */
+} milo_dtype;
+
+/*
+ * A batch of KV blocks to compress (the cache cut into fixed-size blocks of
+ * block_len tokens, each holding several in-context examples: [DIG]
+ * arXivInterpretation; [ABS] abstract).  Block b is the block_len x head_dim
+ * matrix X_b whose token row t starts at element row0[b] + t * row_stride of x.
+ * K blocks must hold keys BEFORE rotary embedding ([REV] Summary; [DIG] Fig. 1).
+ */
+typedef struct milo_blocks {
+    const void *x;         /* device, element type `dtype` (MILO_F32 or MILO_BF16)       */
+    milo_dtype dtype;
+    const int64_t *row0;   /* device [n_blocks] element offsets, or NULL meaning          */
+                           /* row0[b] = b * block_len * row_stride (blocks back to back)  */
+    int64_t row_stride;    /* elements between consecutive token rows, >= head_dim        */
+    int32_t n_blocks;
+    int32_t block_len;     /* T */
+    int32_t head_dim;      /* d, must be 128 */
+} milo_blocks;
+
+/*
+ * Compressed blocks: X_b ~= A_b B_b with A_b = X_b V_r (T x r_b) and
+ * B_b = V_r^T (r_b x d), V_r the leading r_b right singular vectors of X_b
+ * ([REV] Summary and FAQ: a per-block SVD, the cache kept per block in
+ * low-rank form).  Layout in the arena, for block b:
+ *   A_b is stored TRANSPOSED, rank-major: r_b rows of block_len elements,
+ *       row i = column i of A_b, at byte offset a_off[b];
+ *   B_b is stored as r_b rows of head_dim elements at byte offset b_off[b].
+ * Element type `dtype`: MILO_F32, MILO_BF16, or MILO_I8 (codes).  For MILO_I8
+ * every row of A_b (one per token) has a scale a_scale[b*block_len + t] and
+ * every row of B_b (one per rank) a scale b_scale[b*head_dim + i]; the decoded
+ * value is code * scale.
+ * milo_compress_blocks writes rank, a_off, b_off, the arena and the scales;
+ * the caller sizes the arena with milo_arena_bytes().
+ */
+typedef struct milo_factors {
+    milo_dtype dtype;
+    int32_t n_blocks;
+    int32_t block_len;
+    int32_t head_dim;
+    int32_t *rank;         /* device [n_blocks]                                  */
+    int64_t *a_off;        /* device [n_blocks], bytes from arena                */
+    int64_t *b_off;        /* device [n_blocks], bytes from arena                */
+    void *arena;           /* device, 256-byte aligned                           */
+    size_t arena_bytes;
+    float *a_scale;        /* device [n_blocks * block_len], MILO_I8 only, else NULL */
+    float *b_scale;        /* device [n_blocks * head_dim],  MILO_I8 only, else NULL */
+} milo_factors;
+
+/*
+ * milo_compress_blocks -- per-block SVD of every block, global rank allocation
+ * per pool, and the factor pairs ([REV] Summary; [ABS] method section).
+ *
+ *  in          blocks to compress (K blocks pre-RoPE, or V blocks).
+ *  pool_ptr    host [n_pools + 1], CSR over blocks: pool p is the run of blocks
+ *              [pool_ptr[p], pool_ptr[p+1]); pool_ptr[0] = 0,
+ *              pool_ptr[n_pools] = n_blocks, non-decreasing.
+ *  budget      host [n_pools], the global rank budget R_p of each pool (>= 0).
+ *  eps2        eps^2 of the gain log(1 + sigma^2/eps^2) ([REV] Summary and
+ *              Strengths, Eqs 5-7); > 0.  The ranks do not depend on it, only
+ *              the reported objective does.
+ *  sigma_out   device [n_blocks][head_dim] fp32: singular values of each block,
+ *              descending.
+ *  objective_out device [n_pools] fp64 (may be NULL): sum over the pool of the
+ *              gains of the ranks handed out.
+ *  out         factor set: dtype, n_blocks, block_len, head_dim must match `in`;
+ *              rank/a_off/b_off/arena (and scales for MILO_I8) must be set.
+ *              Within each pool exactly min(R_p, n_p * min(T, d)) ranks are
+ *              handed out: the R_p largest singular values of the pool in the
+ *              order (sigma desc, block asc, index asc), which is what the
+ *              greedy on the gains selects.
+ *  sweeps_out  device [n_blocks] int32 (may be NULL): Jacobi sweeps used per
+ *              block; negative if the eigensolver hit its sweep cap.
+ *  workspace   device scratch; *workspace_bytes its size.  With workspace ==
+ *              NULL or a size below what one pool needs, returns
+ *              MILO_E_WORKSPACE and sets *workspace_bytes to the size that
+ *              processes every block in one pass.  Any size >= the largest
+ *              pool's need works: pools are then processed in chunks.
+ * Supported dtype pairs (in -> factors): F32 -> F32, BF16 -> BF16, BF16 -> I8.
+ */
+milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr, int32_t n_pools,
+                                 const int64_t *budget, float eps2, float *sigma_out,
+                                 double *objective_out, milo_factors *out, int32_t *sweeps_out,
+                                 void *workspace, size_t *workspace_bytes, void *stream);
+
+/*
+ * milo_allocate_ranks -- the rank allocation alone ([REV] Strengths, Eqs 5-7),
+ * on caller-supplied singular values.
+ *  sigma       device [n_blocks][head_dim] fp32, every row non-increasing and
+ *              >= 0 (results are unspecified otherwise).
+ *  max_rank    k = ranks a block can hold (1..head_dim); only sigma[b][0..k) count.
+ *  pool_ptr, budget, eps2  as for milo_compress_blocks (host arrays).
+ *  rank_out    device [n_blocks] int32.
+ *  objective_out device [n_pools] fp64 or NULL.
+ *  workspace   device scratch for the pool tables; with NULL or too small a
+ *              size returns MILO_E_WORKSPACE and sets *workspace_bytes.
+ */
+milo_status milo_allocate_ranks(const float *sigma, int32_t n_blocks, int32_t head_dim,
+                                int32_t max_rank, const int32_t *pool_ptr, int32_t n_pools,
+                                const int64_t *budget, float eps2, int32_t *rank_out,
+                                double *objective_out, void *workspace, size_t *workspace_bytes,
+                                void *stream);
+
+/*
+ * milo_reconstruct -- rebuild X_hat_b = A_b B_b (decoded) for the listed blocks
+ * only ([REV] FAQ: only the blocks a query needs are rebuilt).
+ *  block_ids   device [n_ids], each in [0, f->n_blocks).
+ *  x_out       device [n_ids][block_len][head_dim], MILO_F32 or MILO_BF16.
+ */
+milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, int32_t n_ids,
+                             void *x_out, milo_dtype out_dtype, void *stream);
+
+/*
+ * Decode attention over compressed blocks for one layer ([REV] Summary: the
+ * retrieved blocks' low-rank factors are rebuilt before sparse attention).
+ * Sequence s, query head hq uses KV head h = hq / (n_q_heads / n_kv_heads).
+ * Factor block id of block b of sequence s and KV head h:
+ *      (s * n_kv_heads + h) * blocks_per_seq + b.
+ * Token t of block b is at absolute position b * block_len + t; tail token i of
+ * sequence s at tail_pos0[s] + i.  RoPE (half-split pairs, angle
+ * pos * rope_base^(-2j/d)) is applied to the query at q_pos[s] and to every
+ * rebuilt key at its position; logits are scaled by softmax_scale.
+ */
+typedef struct milo_decode_args {
+    const void *q;            /* device [batch][n_q_heads][head_dim], pre-RoPE          */
+    milo_dtype q_dtype;       /* MILO_F32 or MILO_BF16                                  */
+    const int64_t *q_pos;     /* device [batch]                                         */
+    int32_t batch;
+    int32_t n_q_heads;        /* multiple of n_kv_heads; at most 16 per KV head        */
+    int32_t n_kv_heads;
+    int32_t head_dim;         /* 128                                                    */
+    const milo_factors *k;    /* host struct describing the K factor set               */
+    const milo_factors *v;    /* host struct describing the V factor set (same blocks) */
+    int32_t blocks_per_seq;
+    const int32_t *sel_ptr;   /* device CSR [batch + 1] over sel_blk, or NULL = every   */
+    const int32_t *sel_blk;   /* block; entries of a sequence ascending and distinct,   */
+    int32_t sel_max;          /* in [0, blocks_per_seq).  sel_max (host) bounds the     */
+                              /* entries per sequence; ignored when sel_ptr is NULL.    */
+    const void *tail_k;       /* device [batch][n_kv_heads][tail_cap][head_dim], keys   */
+    const void *tail_v;       /* pre-RoPE, or NULL for no uncompressed tail             */
+    milo_dtype tail_dtype;    /* MILO_F32 or MILO_BF16                                  */
+    int32_t tail_cap;         /* multiple of 64 when tail_k != NULL                     */
+    const int32_t *tail_len;  /* device [batch], 0..tail_cap                            */
+    const int64_t *tail_pos0; /* device [batch]                                         */
+    double rope_base;         /* > 1, e.g. 1e6                                           */
+    float softmax_scale;      /* e.g. 1/sqrt(head_dim)                                   */
+    void *out;                /* device [batch][n_q_heads][head_dim]                    */
+    milo_dtype out_dtype;     /* MILO_F32 or MILO_BF16                                  */
+    int32_t split_len;        /* tokens per work split: multiple of 64 dividing          */
+                              /* block_len (and tail_cap); 0 picks one                  */
+    void *workspace;          /* device scratch for the per-split partial results       */
+    size_t workspace_bytes;
+} milo_decode_args;
+
+/*
+ * milo_decode_attention -- one decode step of one layer.  With
+ * a->workspace == NULL or a->workspace_bytes too small it returns
+ * MILO_E_WORKSPACE and stores the size needed in *workspace_needed (may be NULL).
+ * K and V factor sets must use the same storage dtype (F32, BF16 or I8).
+ */
+milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_needed,
+                                  void *stream);
+
+/* Arena bytes for a factor set: sum over pools of min(R_p, n_p * min(T, d))
+ * ranks, each costing (block_len + head_dim) elements of dtype.  Host only.
+ * Returns 0 and sets the last error on invalid input. */
+size_t milo_arena_bytes(milo_dtype dtype, int32_t block_len, int32_t head_dim,
+                        const int32_t *pool_ptr, int32_t n_pools, const int64_t *budget);
+
+/* Workspace bytes milo_compress_blocks needs to process `n_blocks` blocks of
+ * the given geometry in one pass (host only). */
+size_t milo_compress_workspace_bytes(int32_t n_blocks, int32_t block_len, int32_t head_dim);
+
+const char *milo_status_string(milo_status s);
+const char *milo_last_error(void);
+int milo_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MILO_H */

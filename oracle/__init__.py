@@ -261,12 +261,14 @@ class Compressed:
     sweeps: np.ndarray | None = None
 
 
-def compress(X, pool_ptr, budgets, eps2: float, storage: str, max_sweeps: int = 60) -> Compressed:
+def compress(X, pool_ptr, budgets, eps2: float, storage: str, max_sweeps: int = 60,
+             svd=None) -> Compressed:
     """Steps 1-3 for every block.  pool_ptr is the CSR over blocks: pool p holds
-    blocks [pool_ptr[p], pool_ptr[p+1]) and gets budget budgets[p]."""
+    blocks [pool_ptr[p], pool_ptr[p+1]) and gets budget budgets[p].  ``svd`` may
+    pass the result of an earlier ``svd_blocks(X)`` to avoid recomputing it."""
     X = _f64(X)
     n, T, d = X.shape
-    sigma, V, sweeps = svd_blocks(X, max_sweeps=max_sweeps)
+    sigma, V, sweeps = svd if svd is not None else svd_blocks(X, max_sweeps=max_sweeps)
     k = min(T, d)
     rank = np.zeros(n, dtype=np.int32)
     objs = []
