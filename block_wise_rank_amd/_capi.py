@@ -46,9 +46,9 @@ class milo_decode_args(ctypes.Structure):
 # Every symbol include/milo.h declares, with its ctypes signature.
 SIGNATURES = {
     "milo_compress_blocks": (ctypes.c_int, [ctypes.POINTER(milo_blocks), _vp, _i32, _vp,
-                                            ctypes.c_float, _vp, _vp, ctypes.POINTER(milo_factors),
+                                            ctypes.c_double, _vp, _vp, ctypes.POINTER(milo_factors),
                                             _vp, _vp, ctypes.POINTER(ctypes.c_size_t), _vp]),
-    "milo_allocate_ranks": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _i32, _vp, ctypes.c_float,
+    "milo_allocate_ranks": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _i32, _vp, ctypes.c_double,
                                            _vp, _vp, _vp, ctypes.POINTER(ctypes.c_size_t), _vp]),
     "milo_reconstruct": (ctypes.c_int, [ctypes.POINTER(milo_factors), _vp, _i32, _vp,
                                         ctypes.c_int, _vp]),

@@ -70,7 +70,7 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t *buf) {
 __global__ __launch_bounds__(256) void alloc_kernel(
     const float *__restrict__ sigma, int pitch, int k, const int32_t *__restrict__ pool_ptr,
     const int64_t *__restrict__ budget, const int64_t *__restrict__ pool_base, int pool_lo,
-    int blk_lo, float eps2, int32_t *__restrict__ rank, double *__restrict__ objective,
+    int blk_lo, double eps2, int32_t *__restrict__ rank, double *__restrict__ objective,
     int64_t *__restrict__ a_off, int64_t *__restrict__ b_off, int T, int elem_bytes) {
     __shared__ int64_t red64[4];
     __shared__ double redd[4];
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void alloc_kernel(
         rank_sum += r;
         for (int i = 0; i < r; ++i) {
             const double s = static_cast<double>(row[i]);
-            obj += log1p(s * s / static_cast<double>(eps2));
+            obj += log1p(s * s / eps2);
         }
     }
     // Objective (reduction order is fixed by the thread layout: deterministic).
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void alloc_kernel(
 
 hipError_t launch_alloc(const float *sigma, int sigma_pitch, int max_rank, const int32_t *pool_ptr,
                         const int64_t *budget, const int64_t *pool_base, int pool_lo, int n_pools,
-                        int blk_lo, float eps2, int32_t *rank, double *objective, int64_t *a_off,
+                        int blk_lo, double eps2, int32_t *rank, double *objective, int64_t *a_off,
                         int64_t *b_off, int block_len, int elem_bytes, hipStream_t st) {
     if (n_pools <= 0) return hipSuccess;
     hipLaunchKernelGGL(alloc_kernel, dim3(static_cast<unsigned>(n_pools)), dim3(256), 0, st, sigma,

@@ -142,7 +142,7 @@ size_t milo_compress_workspace_bytes(int32_t n_blocks, int32_t block_len, int32_
 }
 
 milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr, int32_t n_pools,
-                                 const int64_t *budget, float eps2, float *sigma_out,
+                                 const int64_t *budget, double eps2, float *sigma_out,
                                  double *objective_out, milo_factors *out, int32_t *sweeps_out,
                                  void *workspace, size_t *workspace_bytes, void *stream) {
     if (!in) return fail(MILO_E_INVALID, "in is NULL");
@@ -163,7 +163,7 @@ milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr,
         return fail(MILO_E_INVALID, "row_stride must keep rows 16-byte aligned");
     if (in->n_blocks > 0 && (!in->x || !aligned(in->x, 16)))
         return fail(MILO_E_INVALID, "x must be a non-NULL 16-byte aligned device pointer");
-    if (!(eps2 > 0.f) || !std::isfinite(eps2)) return fail(MILO_E_INVALID, "eps2 must be finite and > 0");
+    if (!(eps2 > 0.0) || !std::isfinite(eps2)) return fail(MILO_E_INVALID, "eps2 must be finite and > 0");
     milo_status st = check_pools(pool_ptr, n_pools, budget, in->n_blocks);
     if (st != MILO_OK) return st;
     if (in->n_blocks > 0 && !sigma_out) return fail(MILO_E_INVALID, "sigma_out is NULL");
@@ -282,7 +282,7 @@ milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr,
 
 milo_status milo_allocate_ranks(const float *sigma, int32_t n_blocks, int32_t head_dim,
                                 int32_t max_rank, const int32_t *pool_ptr, int32_t n_pools,
-                                const int64_t *budget, float eps2, int32_t *rank_out,
+                                const int64_t *budget, double eps2, int32_t *rank_out,
                                 double *objective_out, void *workspace, size_t *workspace_bytes,
                                 void *stream) {
     if (head_dim <= 0) return fail(MILO_E_INVALID, "head_dim must be > 0");
@@ -290,7 +290,7 @@ milo_status milo_allocate_ranks(const float *sigma, int32_t n_blocks, int32_t he
         return fail(MILO_E_INVALID, "max_rank must be in [1, head_dim] (got %d)", max_rank);
     if (n_blocks < 0) return fail(MILO_E_INVALID, "n_blocks must be >= 0");
     if (n_blocks > 0 && (!sigma || !rank_out)) return fail(MILO_E_INVALID, "sigma and rank_out must be set");
-    if (!(eps2 > 0.f) || !std::isfinite(eps2)) return fail(MILO_E_INVALID, "eps2 must be finite and > 0");
+    if (!(eps2 > 0.0) || !std::isfinite(eps2)) return fail(MILO_E_INVALID, "eps2 must be finite and > 0");
     if (!workspace_bytes) return fail(MILO_E_INVALID, "workspace_bytes is NULL");
     milo_status st = check_pools(pool_ptr, n_pools, budget, n_blocks);
     if (st != MILO_OK) return st;
@@ -343,8 +343,101 @@ milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, in
 
 milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_needed,
                                   void *stream) {
-    (void)a; (void)workspace_needed; (void)stream;
-    return fail(MILO_E_UNSUPPORTED, "decode attention is not available in this build");
+    if (!a) return fail(MILO_E_INVALID, "args is NULL");
+    if (a->head_dim != kD) return fail(MILO_E_UNSUPPORTED, "head_dim must be 128 (got %d)", a->head_dim);
+    if (a->batch < 0) return fail(MILO_E_INVALID, "batch must be >= 0");
+    if (a->n_kv_heads < 1 || a->n_q_heads < 1 || a->n_q_heads % a->n_kv_heads != 0)
+        return fail(MILO_E_INVALID, "n_q_heads must be a positive multiple of n_kv_heads");
+    const int G = a->n_q_heads / a->n_kv_heads;
+    if (G > 16) return fail(MILO_E_UNSUPPORTED, "at most 16 query heads per KV head (got %d)", G);
+    if (!a->k || !a->v) return fail(MILO_E_INVALID, "k and v factor sets must be given");
+    const milo_factors *k = a->k, *v = a->v;
+    if (k->dtype != v->dtype) return fail(MILO_E_UNSUPPORTED, "K and V factors must share a dtype");
+    if (k->dtype != MILO_F32 && k->dtype != MILO_BF16 && k->dtype != MILO_I8)
+        return fail(MILO_E_INVALID, "unknown factor dtype");
+    if (k->head_dim != kD || v->head_dim != kD) return fail(MILO_E_UNSUPPORTED, "factor head_dim must be 128");
+    if (k->block_len != v->block_len) return fail(MILO_E_INVALID, "K and V block_len differ");
+    const int T = k->block_len;
+    if (T < 128 || T % 64 != 0) return fail(MILO_E_UNSUPPORTED, "block_len must be a multiple of 64 and >= 128");
+    if (a->blocks_per_seq < 0) return fail(MILO_E_INVALID, "blocks_per_seq must be >= 0");
+    const int64_t need_blocks = static_cast<int64_t>(a->batch) * a->n_kv_heads * a->blocks_per_seq;
+    if (k->n_blocks < need_blocks || v->n_blocks < need_blocks)
+        return fail(MILO_E_INVALID, "factor sets hold fewer than batch * n_kv_heads * blocks_per_seq blocks");
+    if (need_blocks > 0) {
+        if (!k->rank || !k->a_off || !k->b_off || !k->arena || !v->rank || !v->a_off || !v->b_off || !v->arena)
+            return fail(MILO_E_INVALID, "factor set pointers must be set");
+        if (k->dtype == MILO_I8 && (!k->a_scale || !k->b_scale || !v->a_scale || !v->b_scale))
+            return fail(MILO_E_INVALID, "MILO_I8 factors need scales");
+    }
+    if (a->q_dtype != MILO_F32 && a->q_dtype != MILO_BF16) return fail(MILO_E_UNSUPPORTED, "q_dtype must be F32 or BF16");
+    if (a->out_dtype != MILO_F32 && a->out_dtype != MILO_BF16) return fail(MILO_E_UNSUPPORTED, "out_dtype must be F32 or BF16");
+    if (a->batch > 0 && (!a->q || !a->q_pos || !a->out)) return fail(MILO_E_INVALID, "q, q_pos and out must be set");
+    if (a->sel_ptr) {
+        if (!a->sel_blk && a->sel_max > 0) return fail(MILO_E_INVALID, "sel_blk is NULL");
+        if (a->sel_max < 0 || a->sel_max > a->blocks_per_seq)
+            return fail(MILO_E_INVALID, "sel_max must be in [0, blocks_per_seq]");
+    }
+    const bool tail = a->tail_k != nullptr;
+    if (tail) {
+        if (!a->tail_v || !a->tail_len || !a->tail_pos0) return fail(MILO_E_INVALID, "tail_v, tail_len and tail_pos0 must be set");
+        if (a->tail_cap <= 0 || a->tail_cap % 64 != 0) return fail(MILO_E_UNSUPPORTED, "tail_cap must be a positive multiple of 64");
+        if (a->tail_dtype != MILO_F32 && a->tail_dtype != MILO_BF16) return fail(MILO_E_UNSUPPORTED, "tail_dtype must be F32 or BF16");
+        const int te = elem_bytes(a->tail_dtype);
+        if (!aligned(a->tail_k, 16) || !aligned(a->tail_v, 16) || te == 0)
+            return fail(MILO_E_INVALID, "tail buffers must be 16-byte aligned");
+    }
+    if (!(a->rope_base > 1.0) || !std::isfinite(a->rope_base)) return fail(MILO_E_INVALID, "rope_base must be finite and > 1");
+    if (!std::isfinite(a->softmax_scale)) return fail(MILO_E_INVALID, "softmax_scale must be finite");
+    int split = a->split_len;
+    if (split == 0) split = (T % 256 == 0) ? 256 : 128;
+    if (split < 128 || split % 128 != 0 || T % split != 0 || split > 1024)
+        return fail(MILO_E_UNSUPPORTED, "split_len must be a multiple of 128, at most 1024, dividing block_len");
+
+    milo::DecodeParams p{};
+    p.q = a->q;
+    p.q_type = a->q_dtype == MILO_F32 ? milo::kF32 : milo::kBF16;
+    p.q_pos = a->q_pos;
+    p.batch = a->batch;
+    p.n_q_heads = a->n_q_heads;
+    p.n_kv_heads = a->n_kv_heads;
+    p.group = G;
+    p.f_type = k->dtype == MILO_F32 ? milo::kF32 : (k->dtype == MILO_BF16 ? milo::kBF16 : milo::kI8);
+    p.block_len = T;
+    p.blocks_per_seq = a->blocks_per_seq;
+    p.k_rank = k->rank; p.v_rank = v->rank;
+    p.k_aoff = k->a_off; p.k_boff = k->b_off; p.v_aoff = v->a_off; p.v_boff = v->b_off;
+    p.k_arena = static_cast<const uint8_t *>(k->arena);
+    p.v_arena = static_cast<const uint8_t *>(v->arena);
+    p.k_ascale = k->a_scale; p.k_bscale = k->b_scale; p.v_ascale = v->a_scale; p.v_bscale = v->b_scale;
+    p.sel_ptr = a->sel_ptr;
+    p.sel_blk = a->sel_blk;
+    p.n_sel = a->sel_ptr ? a->sel_max : a->blocks_per_seq;
+    p.tail_k = a->tail_k;
+    p.tail_v = a->tail_v;
+    p.tail_type = a->tail_dtype == MILO_F32 ? milo::kF32 : milo::kBF16;
+    p.tail_cap = tail ? a->tail_cap : 0;
+    p.tail_len = a->tail_len;
+    p.tail_pos0 = a->tail_pos0;
+    p.rope_base = a->rope_base;
+    p.softmax_scale = a->softmax_scale;
+    p.out = a->out;
+    p.out_type = a->out_dtype == MILO_F32 ? milo::kF32 : milo::kBF16;
+    p.split_len = split;
+    p.block_splits = T / split;
+    p.tail_splits = tail ? (a->tail_cap + split - 1) / split : 0;
+    p.n_splits = p.n_sel * p.block_splits + p.tail_splits;
+
+    const size_t need = milo::decode_workspace_bytes(p);
+    if (workspace_needed) *workspace_needed = need;
+    if (!a->workspace || a->workspace_bytes < need)
+        return fail(MILO_E_WORKSPACE, "workspace of %zu bytes needed", need);
+    if (!aligned(a->workspace, 256)) return fail(MILO_E_INVALID, "workspace must be 256-byte aligned");
+    const size_t n = static_cast<size_t>(p.batch) * p.n_kv_heads * p.n_splits * G;
+    p.part_ml = static_cast<float *>(a->workspace);
+    p.part_o = reinterpret_cast<float *>(static_cast<uint8_t *>(a->workspace) + align_up(n * 2 * sizeof(float), 256));
+    hipError_t e = milo::launch_decode(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
 }
 
 }  // extern "C"

@@ -32,7 +32,7 @@ hipError_t launch_refine(const void *x, int x_type, const int64_t *row0, int64_t
 // non-null the arena offsets (pool_base[p] + prefix of rank * (T + d) * elem).
 hipError_t launch_alloc(const float *sigma, int sigma_pitch, int max_rank,
                         const int32_t *pool_ptr, const int64_t *budget, const int64_t *pool_base,
-                        int pool_lo, int n_pools, int blk_lo, float eps2, int32_t *rank,
+                        int pool_lo, int n_pools, int blk_lo, double eps2, int32_t *rank,
                         double *objective, int64_t *a_off, int64_t *b_off, int block_len,
                         int elem_bytes, hipStream_t st);
 

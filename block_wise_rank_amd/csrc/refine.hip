@@ -37,6 +37,16 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     for (int e = tid; e < kD * kD / 4; e += 256)
         reinterpret_cast<float4 *>(Vs)[e] = reinterpret_cast<const float4 *>(vblk)[e];
     __syncthreads();
+    // Thousands of fp32 rotations leave each eigenvector's norm off by ~1e-5;
+    // rescale to unit norm so ||X v|| measures sigma and B = V_r^T is orthonormal.
+    for (int i = wave; i < kD; i += 4) {
+        const float a = Vs[i * kD + lane], b = Vs[i * kD + 64 + lane];
+        const float nrm = sqrtf(wave_sum(a * a + b * b));
+        const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
+        Vs[i * kD + lane] = a * inv;
+        Vs[i * kD + 64 + lane] = b * inv;
+    }
+    __syncthreads();
 
     // A fragments: row i = 32 * wave + lane % 32, k slots j = 16 ks + 8 (lane / 32) + e.
     u16x8_t fa[3][8];

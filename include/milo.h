@@ -136,7 +136,7 @@ typedef struct milo_factors {
  * Supported dtype pairs (in -> factors): F32 -> F32, BF16 -> BF16, BF16 -> I8.
  */
 milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr, int32_t n_pools,
-                                 const int64_t *budget, float eps2, float *sigma_out,
+                                 const int64_t *budget, double eps2, float *sigma_out,
                                  double *objective_out, milo_factors *out, int32_t *sweeps_out,
                                  void *workspace, size_t *workspace_bytes, void *stream);
 
@@ -154,7 +154,7 @@ milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr,
  */
 milo_status milo_allocate_ranks(const float *sigma, int32_t n_blocks, int32_t head_dim,
                                 int32_t max_rank, const int32_t *pool_ptr, int32_t n_pools,
-                                const int64_t *budget, float eps2, int32_t *rank_out,
+                                const int64_t *budget, double eps2, int32_t *rank_out,
                                 double *objective_out, void *workspace, size_t *workspace_bytes,
                                 void *stream);
 

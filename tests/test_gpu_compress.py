@@ -7,8 +7,8 @@ import torch
 import oracle
 from block_wise_rank_amd import milo_allocate_ranks
 from synthetic import CONFIGS, layer_inputs
-from _parity import (check_ranks, check_reconstruction, check_sigma, layer_pools,
-                     reconstruct_all, run_gpu_compress)
+from _parity import (check_objective, check_ranks, check_reconstruction, check_sigma,
+                     layer_pools, reconstruct_all, run_gpu_compress)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,10 +44,8 @@ def test_config0_fp32(kind):
     nd = check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
     xh = reconstruct_all(f).cpu().numpy()
     rec = check_reconstruction(X64, comp, r_gpu, xh, "f32")
-    o = obj.cpu().numpy()
-    for p in range(len(pp) - 1):
-        tol = 1e-9 if nd == 0 else 1e-4
-        assert abs(o[p] - comp.objective[p]) <= tol * abs(comp.objective[p])
+    check_objective(obj.cpu().numpy(), sig.cpu().numpy(), r_gpu, comp.objective, comp.sigma, comp.rank, pp,
+                    cfg.eps2)
     print(f"[cfg0 {kind}] sigma worst/bound {worst:.3g}, rank diffs {nd}, recon rel-F {rec:.3g}")
 
 
@@ -62,6 +60,8 @@ def test_config1_bf16(kind):
     nd = check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
     xh = reconstruct_all(f).cpu().numpy()
     rec = check_reconstruction(X64, comp, r_gpu, xh, "bf16")
+    check_objective(obj.cpu().numpy(), sig.cpu().numpy(), r_gpu, comp.objective, comp.sigma, comp.rank, pp,
+                    cfg.eps2)
     print(f"[cfg1 {kind}] sigma worst/bound {worst:.3g}, rank diffs {nd}, recon rel-F {rec:.3g}")
 
 

@@ -1,0 +1,154 @@
+"""GPU parity of decode attention over compressed blocks against the fp64 oracle.
+
+Two kinds of cases:
+  * kernel level: seeded random factor sets in the arena layout (synthetic.factors)
+    feed both the kernels and the oracle, so the decode is tested on its own,
+    including ranks 0 and 128, INT8 rows with zero scale, block selections with
+    an empty selection, a ragged uncompressed tail, and several split lengths;
+  * end to end: GPU compression + GPU decode against oracle compression + oracle
+    decode on the same planted caches and queries.
+
+Tolerances (derived in the design doc): the kernels round the rebuilt keys, the
+rotated queries and the softmax weights to bf16 MFMA operands (fp32 factors:
+split into two bf16 terms), so errors scale with max|v|: 2e-2 * max|v| for bf16
+and INT8 factors, 1e-4 * max|v| for fp32 factors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_wise_rank_amd import Factors, milo_decode_attention
+from synthetic import CONFIGS, layer_inputs, queries, selection
+from synthetic.factors import random_factor_set
+from synthetic.planted import tail_inputs
+from _parity import layer_pools, run_gpu_compress
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"bf16": 2e-2, "i8": 2e-2, "f32": 1e-4}
+
+
+def _factors_on_gpu(tensors, storage, n_blocks, T, d=128):
+    f = Factors(storage, n_blocks, T, d, rank=tensors["rank"].to(DEV), a_off=tensors["a_off"].to(DEV),
+                b_off=tensors["b_off"].to(DEV), arena=tensors["arena"].to(DEV))
+    if storage == "i8":
+        f.a_scale = tensors["a_scale"].to(DEV)
+        f.b_scale = tensors["b_scale"].to(DEV)
+    return f
+
+
+def _run(q, q_pos, kf, vf, bps, hkv, out_dtype=torch.float32, **kw):
+    out = torch.empty(q.shape, dtype=out_dtype, device=DEV)
+    milo_decode_attention(q, q_pos, kf, vf, bps, hkv, out, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _recon(A_dec, B_dec):
+    return [a @ b for a, b in zip(A_dec, B_dec)]
+
+
+def _check(got, ref, vmax, storage, label):
+    err = np.abs(got - ref).max()
+    bound = TOL[storage] * vmax
+    print(f"  [{label}] max|err| {err:.3g}  bound {bound:.3g}  max|ref| {np.abs(ref).max():.3g}")
+    assert err <= bound, f"{label}: {err} > {bound}"
+
+
+@pytest.mark.parametrize("storage", ["bf16", "f32", "i8"])
+@pytest.mark.parametrize("q_scale", [1.0, 10.0])
+def test_kernel_level_all_blocks(storage, q_scale):
+    batch, hkv, hq, T, bps, d = 2, 2, 16, 256, 6, 128
+    n = batch * hkv * bps
+    ranks = np.random.default_rng(1).integers(1, 129, size=n)
+    ranks[0], ranks[1], ranks[2] = 0, 128, 17
+    kt, kA, kB = random_factor_set(n, T, d, storage, seed=11, ranks=ranks)
+    vt, vA, vB = random_factor_set(n, T, d, storage, seed=12, ranks=ranks[::-1].copy())
+    kf, vf = _factors_on_gpu(kt, storage, n, T), _factors_on_gpu(vt, storage, n, T)
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn((batch, hq, d), generator=g, dtype=torch.float64) * q_scale
+    qdt = torch.float32 if storage == "f32" else torch.bfloat16
+    qd = q.to(qdt)
+    q_pos = torch.tensor([bps * T, bps * T + 77], dtype=torch.int64)
+    Kh, Vh = _recon(kA, kB), _recon(vA, vB)
+    ref = oracle.decode(qd.to(torch.float64).numpy(), q_pos.numpy(), Kh, Vh, T, hkv, bps)
+    vmax = max(np.abs(v).max() for v in Vh)
+    for split in [0, 128]:
+        got = _run(qd.to(DEV), q_pos.to(DEV), kf, vf, bps, hkv, split_len=split).cpu().numpy()
+        _check(got, ref, vmax, storage, f"{storage} q*{q_scale} split {split}")
+
+
+@pytest.mark.parametrize("storage", ["bf16", "i8"])
+def test_kernel_level_selection_and_tail(storage):
+    """GQA 7:1, a per-sequence block selection (one sequence selects nothing),
+    and an uncompressed tail of different lengths per sequence."""
+    batch, hkv, hq, T, bps, d, cap = 3, 2, 14, 1024, 12, 128, 256
+    n = batch * hkv * bps
+    kt, kA, kB = random_factor_set(n, T, d, storage, seed=21, rank_range=(8, 100))
+    vt, vA, vB = random_factor_set(n, T, d, storage, seed=22, rank_range=(8, 100))
+    kf, vf = _factors_on_gpu(kt, storage, n, T), _factors_on_gpu(vt, storage, n, T)
+    sel = [[0, 3, 7, 11], [], [5, 6]]
+    sel_ptr = torch.tensor(np.cumsum([0] + [len(x) for x in sel]), dtype=torch.int32)
+    sel_blk = torch.tensor(sum(sel, []), dtype=torch.int32)
+    rng = np.random.default_rng(3)
+    tail_k = torch.from_numpy(rng.standard_normal((batch, hkv, cap, d)) * 0.3).to(torch.bfloat16)
+    tail_v = torch.from_numpy(rng.standard_normal((batch, hkv, cap, d))).to(torch.bfloat16)
+    tail_len = torch.tensor([256, 100, 0], dtype=torch.int32)
+    tail_pos0 = torch.tensor([bps * T] * batch, dtype=torch.int64)
+    q_pos = tail_pos0 + tail_len.to(torch.int64)
+    q = (torch.randn((batch, hq, d), generator=torch.Generator().manual_seed(9)) * 4).to(torch.bfloat16)
+    Kh, Vh = _recon(kA, kB), _recon(vA, vB)
+    ref = oracle.decode(q.to(torch.float64).numpy(), q_pos.numpy(), Kh, Vh, T, hkv, bps, sel=sel,
+                        tail_k=tail_k.to(torch.float64).numpy(), tail_v=tail_v.to(torch.float64).numpy(),
+                        tail_len=tail_len.numpy(), tail_pos0=tail_pos0.numpy())
+    vmax = max(max(np.abs(v).max() for v in Vh), float(tail_v.abs().max()))
+    for split in [0, 512]:
+        got = _run(q.to(DEV), q_pos.to(DEV), kf, vf, bps, hkv, sel_ptr=sel_ptr.to(DEV),
+                   sel_blk=sel_blk.to(DEV), sel_max=4, tail_k=tail_k.to(DEV), tail_v=tail_v.to(DEV),
+                   tail_len=tail_len.to(DEV), tail_pos0=tail_pos0.to(DEV), split_len=split,
+                   out_dtype=torch.bfloat16).float().cpu().numpy()
+        _check(got, ref, vmax, storage, f"sel+tail {storage} split {split}")
+
+
+def test_decode_is_deterministic():
+    batch, hkv, hq, T, bps, d = 1, 2, 16, 512, 4, 128
+    n = batch * hkv * bps
+    kt, _, _ = random_factor_set(n, T, d, "bf16", seed=31)
+    vt, _, _ = random_factor_set(n, T, d, "bf16", seed=32)
+    kf, vf = _factors_on_gpu(kt, "bf16", n, T), _factors_on_gpu(vt, "bf16", n, T)
+    q = torch.randn((batch, hq, d), generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).to(DEV)
+    q_pos = torch.tensor([bps * T], dtype=torch.int64, device=DEV)
+    a = _run(q, q_pos, kf, vf, bps, hkv)
+    for _ in range(5):
+        assert torch.equal(a, _run(q, q_pos, kf, vf, bps, hkv))
+
+
+@pytest.mark.parametrize("cfg_idx", [0, 1])
+@pytest.mark.parametrize("q_scale", [1.0, 300.0])
+def test_end_to_end(cfg_idx, q_scale):
+    """Compress K and V of one layer and decode one step, GPU vs oracle.  The literal
+    bound of 2e-2 max-abs holds trivially at the planted scale (|o| ~ 1e-4 for
+    N(0,1) queries), so the sharp variant (queries x300, logit spread of a few
+    units) carries the real check, scale-aware: 2e-2 * max|v|."""
+    cfg = CONFIGS[cfg_idx]
+    st = cfg.storage
+    pp, bud = layer_pools(cfg)
+    Xk = layer_inputs(cfg, 0, "k")
+    Xv = layer_inputs(cfg, 0, "v")
+    kf, _, _, _ = run_gpu_compress(Xk.to(DEV), pp, bud, cfg.eps2, st)
+    vf, _, _, _ = run_gpu_compress(Xv.to(DEV), pp, bud, cfg.eps2, st)
+    q = queries(cfg, 0, scale=q_scale)
+    q_pos = torch.full((cfg.batch,), cfg.context_len, dtype=torch.int64)
+    got = _run(q.to(DEV), q_pos.to(DEV), kf, vf, cfg.blocks_per_seq, cfg.n_kv_heads).cpu().numpy()
+    ck = oracle.compress(Xk.to(torch.float64).numpy(), pp, bud, cfg.eps2, st)
+    cv = oracle.compress(Xv.to(torch.float64).numpy(), pp, bud, cfg.eps2, st)
+    Kh = oracle.reconstruct_blocks(ck)
+    Vh = oracle.reconstruct_blocks(cv)
+    ref = oracle.decode(q.to(torch.float64).numpy(), q_pos.numpy(), Kh, Vh, cfg.block_len,
+                        cfg.n_kv_heads, cfg.blocks_per_seq, rope_base=cfg.rope_base)
+    err = np.abs(got - ref).max()
+    vmax = np.abs(Vh).max()
+    print(f"  [cfg{cfg_idx} q*{q_scale}] max|err| {err:.3g} max|ref| {np.abs(ref).max():.3g} max|v| {vmax:.3g}")
+    assert err <= 2e-2
+    assert err <= 2e-2 * vmax
