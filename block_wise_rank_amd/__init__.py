@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     milo_compress_blocks,
     milo_compress_workspace_bytes,
     milo_decode_attention,
+    milo_profile_enable,
+    milo_profile_read,
     milo_reconstruct,
 )
 from . import _capi  # noqa: F401
@@ -23,5 +25,5 @@ from . import _capi  # noqa: F401
 __all__ = [
     "Factors", "MiloError", "decode_workspace_bytes", "milo_abi_version", "milo_allocate_ranks",
     "milo_arena_bytes", "milo_compress_blocks", "milo_compress_workspace_bytes",
-    "milo_decode_attention", "milo_reconstruct",
+    "milo_decode_attention", "milo_profile_enable", "milo_profile_read", "milo_reconstruct",
 ]

@@ -56,6 +56,9 @@ SIGNATURES = {
                                              ctypes.POINTER(ctypes.c_size_t), _vp]),
     "milo_arena_bytes": (ctypes.c_size_t, [ctypes.c_int, _i32, _i32, _vp, _i32, _vp]),
     "milo_compress_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
+    "milo_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "milo_profile_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_i32),
+                                         ctypes.POINTER(ctypes.c_double), ctypes.c_int]),
     "milo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "milo_last_error": (ctypes.c_char_p, []),
     "milo_abi_version": (ctypes.c_int, []),

@@ -98,6 +98,15 @@ class Factors:
                               _p(self.arena), self.arena.numel(), _p(self.a_scale),
                               _p(self.b_scale))
 
+    def view(self, lo: int, n: int) -> "Factors":
+        """Blocks [lo, lo + n) of this set, sharing its arena (offsets are arena-relative)."""
+        return Factors(self.dtype, n, self.block_len, self.head_dim, rank=self.rank[lo:lo + n],
+                       a_off=self.a_off[lo:lo + n], b_off=self.b_off[lo:lo + n], arena=self.arena,
+                       a_scale=None if self.a_scale is None else
+                       self.a_scale[lo * self.block_len:(lo + n) * self.block_len],
+                       b_scale=None if self.b_scale is None else
+                       self.b_scale[lo * self.head_dim:(lo + n) * self.head_dim])
+
     def nbytes(self) -> int:
         """Bytes the factors occupy (arena payload + INT8 scales actually used)."""
         used = int(self.rank.sum().item()) * (self.block_len + self.head_dim) * \
@@ -105,6 +114,22 @@ class Factors:
         if self.dtype == "i8":
             used += 4 * (self.n_blocks * self.block_len + int(self.rank.sum().item()))
         return used
+
+
+def milo_profile_enable(on: bool) -> bool:
+    return bool(lib().milo_profile_enable(1 if on else 0))
+
+
+def milo_profile_read() -> dict:
+    """{kernel name: (launches, total milliseconds)} since the last read (waits)."""
+    cap = 32
+    names = (ctypes.c_char_p * cap)()
+    cnt = (ctypes.c_int32 * cap)()
+    ms = (ctypes.c_double * cap)()
+    n = lib().milo_profile_read(names, cnt, ms, cap)
+    if n < 0:
+        _check(C.MILO_E_HIP)
+    return {names[i].decode(): (int(cnt[i]), float(ms[i])) for i in range(min(n, cap))}
 
 
 def milo_abi_version() -> int:

@@ -17,6 +17,42 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Measurement aid: while enabled on a thread, every kernel launched by that
+// thread's calls is bracketed by HIP events on the call's stream.
+struct ProfRecord {
+    const char *name;
+    hipEvent_t start, stop;
+};
+struct ProfState {
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    size_t next = 0;
+    std::vector<ProfRecord> recs;
+};
+thread_local ProfState g_prof;
+
+hipEvent_t prof_event() {
+    if (g_prof.next < g_prof.pool.size()) return g_prof.pool[g_prof.next++];
+    hipEvent_t ev = nullptr;
+    if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+    g_prof.pool.push_back(ev);
+    g_prof.next = g_prof.pool.size();
+    return ev;
+}
+
+// Run a launcher (returning hipError_t) with optional event brackets.
+template <typename Fn>
+hipError_t timed(const char *name, hipStream_t s, Fn &&fn) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (g_prof.on && (a = prof_event())) hipEventRecord(a, s);
+    hipError_t e = fn();
+    if (g_prof.on && a && (b = prof_event())) {
+        hipEventRecord(b, s);
+        g_prof.recs.push_back({name, a, b});
+    }
+    return e;
+}
+
 milo_status fail(milo_status s, const char *fmt, ...) {
     char buf[512];
     va_list ap;
@@ -252,22 +288,28 @@ milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr,
             const void *xc = in->row0 ? static_cast<const void *>(xb)
                                       : static_cast<const void *>(xb + static_cast<size_t>(b0) * T * in->row_stride * xe);
             float *sig = sigma_out + static_cast<size_t>(b0) * kD;
-            if ((e = milo::launch_gram(xc, x_type, row0, in->row_stride, T, nb, splits, gpart, s)) != hipSuccess)
+            if ((e = timed("gram", s, [&] { return milo::launch_gram(xc, x_type, row0, in->row_stride, T, nb, splits, gpart, s); })) != hipSuccess)
                 return hip_fail(e, "gram launch");
-            if ((e = milo::launch_jacobi(gpart, splits, nb, vt, sweeps_out ? sweeps_out + b0 : nullptr,
-                                         kMaxSweeps, kJacobiTol, s)) != hipSuccess)
+            if ((e = timed("jacobi", s, [&] {
+                     return milo::launch_jacobi(gpart, splits, nb, vt, sweeps_out ? sweeps_out + b0 : nullptr,
+                                                kMaxSweeps, kJacobiTol, s);
+                 })) != hipSuccess)
                 return hip_fail(e, "jacobi launch");
-            if ((e = milo::launch_refine(xc, x_type, row0, in->row_stride, T, nb, vt, sig, s)) != hipSuccess)
+            if ((e = timed("refine", s, [&] { return milo::launch_refine(xc, x_type, row0, in->row_stride, T, nb, vt, sig, s); })) != hipSuccess)
                 return hip_fail(e, "refine launch");
-            if ((e = milo::launch_alloc(sig, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
-                                        eps2, out->rank, objective_out, out->a_off, out->b_off, T, fe,
-                                        s)) != hipSuccess)
+            if ((e = timed("alloc", s, [&] {
+                     return milo::launch_alloc(sig, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
+                                               eps2, out->rank, objective_out, out->a_off, out->b_off, T,
+                                               fe, s);
+                 })) != hipSuccess)
                 return hip_fail(e, "alloc launch");
-            if ((e = milo::launch_project(xc, x_type, row0, in->row_stride, T, nb, vt, out->rank + b0,
-                                          out->a_off + b0, out->b_off + b0, out->arena, f_type,
-                                          out->a_scale ? out->a_scale + static_cast<size_t>(b0) * T : nullptr,
-                                          out->b_scale ? out->b_scale + static_cast<size_t>(b0) * kD : nullptr,
-                                          s)) != hipSuccess)
+            if ((e = timed("project", s, [&] {
+                     return milo::launch_project(
+                         xc, x_type, row0, in->row_stride, T, nb, vt, out->rank + b0, out->a_off + b0,
+                         out->b_off + b0, out->arena, f_type,
+                         out->a_scale ? out->a_scale + static_cast<size_t>(b0) * T : nullptr,
+                         out->b_scale ? out->b_scale + static_cast<size_t>(b0) * kD : nullptr, s);
+                 })) != hipSuccess)
                 return hip_fail(e, "project launch");
         } else {
             if ((e = milo::launch_alloc(sigma_out, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
@@ -309,8 +351,10 @@ milo_status milo_allocate_ranks(const float *sigma, int32_t n_blocks, int32_t he
     if ((e = hipMemcpyAsync(d_pool_ptr, pool_ptr, sizeof(int32_t) * (n_pools + 1), hipMemcpyHostToDevice, s)) != hipSuccess ||
         (e = hipMemcpyAsync(d_budget, budget, sizeof(int64_t) * n_pools, hipMemcpyHostToDevice, s)) != hipSuccess)
         return hip_fail(e, "pool table upload");
-    e = milo::launch_alloc(sigma, head_dim, max_rank, d_pool_ptr, d_budget, nullptr, 0, n_pools, 0, eps2,
-                           rank_out, objective_out, nullptr, nullptr, 0, 0, s);
+    e = timed("alloc", s, [&] {
+        return milo::launch_alloc(sigma, head_dim, max_rank, d_pool_ptr, d_budget, nullptr, 0, n_pools, 0,
+                                  eps2, rank_out, objective_out, nullptr, nullptr, 0, 0, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "alloc launch");
     return ok();
 }
@@ -333,10 +377,12 @@ milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, in
     if (f->dtype == MILO_I8 && (!f->a_scale || !f->b_scale))
         return fail(MILO_E_INVALID, "MILO_I8 factors need scales");
     const int ft = f->dtype == MILO_F32 ? milo::kF32 : (f->dtype == MILO_BF16 ? milo::kBF16 : milo::kI8);
-    hipError_t e = milo::launch_reconstruct(f->arena, ft, f->rank, f->a_off, f->b_off, f->a_scale,
-                                            f->b_scale, f->block_len, block_ids, n_ids, x_out,
-                                            out_dtype == MILO_F32 ? milo::kF32 : milo::kBF16,
-                                            static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("reconstruct", s, [&] {
+        return milo::launch_reconstruct(f->arena, ft, f->rank, f->a_off, f->b_off, f->a_scale,
+                                        f->b_scale, f->block_len, block_ids, n_ids, x_out,
+                                        out_dtype == MILO_F32 ? milo::kF32 : milo::kBF16, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "reconstruct launch");
     return ok();
 }
@@ -435,9 +481,57 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
     const size_t n = static_cast<size_t>(p.batch) * p.n_kv_heads * p.n_splits * G;
     p.part_ml = static_cast<float *>(a->workspace);
     p.part_o = reinterpret_cast<float *>(static_cast<uint8_t *>(a->workspace) + align_up(n * 2 * sizeof(float), 256));
-    hipError_t e = milo::launch_decode(p, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.batch == 0) return ok();
+    hipError_t e = hipSuccess;
+    if (p.n_sel * p.block_splits > 0 &&
+        (e = timed("decode_blocks", s, [&] { return milo::launch_decode_blocks(p, s); })) != hipSuccess)
+        return hip_fail(e, "decode launch");
+    if (p.tail_splits > 0 &&
+        (e = timed("decode_tail", s, [&] { return milo::launch_decode_tail(p, s); })) != hipSuccess)
+        return hip_fail(e, "decode tail launch");
+    if ((e = timed("decode_combine", s, [&] { return milo::launch_decode_combine(p, s); })) != hipSuccess)
+        return hip_fail(e, "decode combine launch");
     return ok();
+}
+
+int milo_profile_enable(int on) {
+    const int prev = g_prof.on ? 1 : 0;
+    g_prof.on = on != 0;
+    return prev;
+}
+
+int milo_profile_read(const char **names, int32_t *launches, double *total_ms, int cap) {
+    std::vector<const char *> keys;
+    std::vector<int32_t> cnt;
+    std::vector<double> ms;
+    for (const ProfRecord &r : g_prof.recs) {
+        float t = 0.f;
+        if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) {
+            fail(MILO_E_HIP, "profile event failed");
+            g_prof.recs.clear();
+            g_prof.next = 0;
+            return -1;
+        }
+        size_t i = 0;
+        while (i < keys.size() && std::strcmp(keys[i], r.name) != 0) ++i;
+        if (i == keys.size()) {
+            keys.push_back(r.name);
+            cnt.push_back(0);
+            ms.push_back(0.0);
+        }
+        cnt[i] += 1;
+        ms[i] += t;
+    }
+    g_prof.recs.clear();
+    g_prof.next = 0;
+    const int n = static_cast<int>(keys.size());
+    for (int i = 0; i < n && i < cap; ++i) {
+        if (names) names[i] = keys[i];
+        if (launches) launches[i] = cnt[i];
+        if (total_ms) total_ms[i] = ms[i];
+    }
+    return n;
 }
 
 }  // extern "C"

@@ -505,36 +505,28 @@ hipError_t launch_partial(const DecodeParams &p, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
-size_t decode_lds_bytes(const DecodeParams &p, bool tail, int type) {
-    const int ns = type == kF32 ? 2 : 1;
-    return static_cast<size_t>(lds_layout(ns, p.split_len / kTile, p.group, tail).total);
-}
-
 size_t decode_workspace_bytes(const DecodeParams &p) {
     const size_t n = static_cast<size_t>(p.batch) * p.n_kv_heads * p.n_splits * p.group;
     const size_t ml = (n * 2 * sizeof(float) + 255) / 256 * 256;
     return ml + n * kD * sizeof(float);
 }
 
-hipError_t launch_decode(const DecodeParams &p, hipStream_t st) {
-    if (p.batch <= 0) return hipSuccess;
-    hipError_t e = hipSuccess;
-    const int nb = p.n_sel * p.block_splits;
-    if (nb > 0) {
-        const dim3 grid(static_cast<unsigned>(nb), static_cast<unsigned>(p.n_kv_heads),
-                        static_cast<unsigned>(p.batch));
-        if (p.f_type == kBF16) e = launch_partial<kBF16, false>(p, grid, st);
-        else if (p.f_type == kI8) e = launch_partial<kI8, false>(p, grid, st);
-        else e = launch_partial<kF32, false>(p, grid, st);
-        if (e != hipSuccess) return e;
-    }
-    if (p.tail_splits > 0) {
-        const dim3 grid(static_cast<unsigned>(p.tail_splits), static_cast<unsigned>(p.n_kv_heads),
-                        static_cast<unsigned>(p.batch));
-        if (p.tail_type == kBF16) e = launch_partial<kBF16, true>(p, grid, st);
-        else e = launch_partial<kF32, true>(p, grid, st);
-        if (e != hipSuccess) return e;
-    }
+hipError_t launch_decode_blocks(const DecodeParams &p, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(p.n_sel * p.block_splits), static_cast<unsigned>(p.n_kv_heads),
+                    static_cast<unsigned>(p.batch));
+    if (p.f_type == kBF16) return launch_partial<kBF16, false>(p, grid, st);
+    if (p.f_type == kI8) return launch_partial<kI8, false>(p, grid, st);
+    return launch_partial<kF32, false>(p, grid, st);
+}
+
+hipError_t launch_decode_tail(const DecodeParams &p, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(p.tail_splits), static_cast<unsigned>(p.n_kv_heads),
+                    static_cast<unsigned>(p.batch));
+    if (p.tail_type == kBF16) return launch_partial<kBF16, true>(p, grid, st);
+    return launch_partial<kF32, true>(p, grid, st);
+}
+
+hipError_t launch_decode_combine(const DecodeParams &p, hipStream_t st) {
     const dim3 cgrid(static_cast<unsigned>(p.n_q_heads), static_cast<unsigned>(p.batch));
     if (p.out_type == kF32)
         hipLaunchKernelGGL(decode_combine_kernel<kF32>, cgrid, dim3(128), 0, st, p);

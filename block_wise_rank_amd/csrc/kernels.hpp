@@ -82,6 +82,10 @@ struct DecodeParams {
 };
 
 size_t decode_workspace_bytes(const DecodeParams &p);
-hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
+// Partial results of the compressed-block splits, of the tail splits, and the
+// log-sum-exp merge into the output.
+hipError_t launch_decode_blocks(const DecodeParams &p, hipStream_t st);
+hipError_t launch_decode_tail(const DecodeParams &p, hipStream_t st);
+hipError_t launch_decode_combine(const DecodeParams &p, hipStream_t st);
 
 }  // namespace milo

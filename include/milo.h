@@ -228,6 +228,19 @@ size_t milo_arena_bytes(milo_dtype dtype, int32_t block_len, int32_t head_dim,
  * the given geometry in one pass (host only). */
 size_t milo_compress_workspace_bytes(int32_t n_blocks, int32_t block_len, int32_t head_dim);
 
+/*
+ * Measurement aid (not part of the method): while enabled, every kernel that
+ * the calling thread's libmilo calls launch is bracketed by a pair of HIP
+ * events recorded on the call's stream.  milo_profile_read waits for the
+ * recorded kernels, fills up to `cap` entries (kernel name -- a static string
+ * --, launch count, total milliseconds; any output pointer may be NULL),
+ * clears the record and returns the number of distinct kernels, or -1 if an
+ * event failed.  State is per thread; events are created on first use and
+ * reused.  milo_profile_enable returns the previous setting.
+ */
+int milo_profile_enable(int on);
+int milo_profile_read(const char **names, int32_t *launches, double *total_ms, int cap);
+
 const char *milo_status_string(milo_status s);
 const char *milo_last_error(void);
 int milo_abi_version(void);
