@@ -466,26 +466,46 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
     }
 }
 
+// One workgroup per (sequence, query head): the split maxima and weights are
+// computed by all threads in parallel, then thread j sums its output column.
 template <int OT>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeParams p) {
-    const int hq = blockIdx.x, s = blockIdx.y, j = threadIdx.x;
+    __shared__ float coef[1024];
+    __shared__ float red[2];
+    const int hq = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
     const int G = p.group;
     const int h = hq / G, g = hq - h * G;
     const int64_t base = static_cast<int64_t>(s * p.n_kv_heads + h) * p.n_splits;
+    float num = 0.f, den_part = 0.f;
+    // chunks of up to 1024 splits (the weights of one chunk fit in LDS)
     float M = -INFINITY;
-    for (int sp = 0; sp < p.n_splits; ++sp) M = fmaxf(M, p.part_ml[((base + sp) * G + g) * 2]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-        for (int sp = 0; sp < p.n_splits; ++sp) {
-            const float m = p.part_ml[((base + sp) * G + g) * 2];
-            if (m == -INFINITY) continue;
-            const float c = exp2f(m - M);
-            den += c * p.part_ml[((base + sp) * G + g) * 2 + 1];
-            num += c * p.part_o[((base + sp) * G + g) * kD + j];
+    for (int sp = tid; sp < p.n_splits; sp += 128) M = fmaxf(M, p.part_ml[((base + sp) * G + g) * 2]);
+    M = wave_max(M);
+    if ((tid & 63) == 0) red[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(red[0], red[1]);
+    __syncthreads();
+    for (int c0 = 0; c0 < p.n_splits; c0 += 1024) {
+        const int cn = min(1024, p.n_splits - c0);
+        for (int i = tid; i < cn; i += 128) {
+            const float m = p.part_ml[((base + c0 + i) * G + g) * 2];
+            const float c = (m == -INFINITY || M == -INFINITY) ? 0.f : exp2f(m - M);
+            coef[i] = c;
+            den_part += c * p.part_ml[((base + c0 + i) * G + g) * 2 + 1];
         }
+        __syncthreads();
+        for (int i = 0; i < cn; ++i) {
+            const float c = coef[i];
+            if (c != 0.f) num += c * p.part_o[((base + c0 + i) * G + g) * kD + tid];
+        }
+        __syncthreads();
     }
+    den_part = wave_sum(den_part);
+    if ((tid & 63) == 0) red[tid >> 6] = den_part;
+    __syncthreads();
+    const float den = red[0] + red[1];
     const float o = den > 0.f ? num / den : 0.f;
-    const int64_t oi = (static_cast<int64_t>(s) * p.n_q_heads + hq) * kD + j;
+    const int64_t oi = (static_cast<int64_t>(s) * p.n_q_heads + hq) * kD + tid;
     if constexpr (OT == kF32)
         static_cast<float *>(p.out)[oi] = o;
     else

@@ -1,5 +1,5 @@
 // Batched symmetric eigensolve of 128 x 128 Gram matrices by cyclic two-sided
-// Jacobi, held entirely in LDS (one workgroup of 8 waves per block).
+// Jacobi, held entirely in LDS (one workgroup of 16 waves per block).
 //
 // A Jacobi rotation of the pair (p, q) of G = X^T X is the same rotation a
 // one-sided (Hestenes) Jacobi step applies to columns p, q of X, computed from
@@ -11,7 +11,7 @@
 // rounds of 64 disjoint pairs per sweep, so one round's rotations commute and
 // are applied together.  Per round:
 //   A  wave 0 computes the 64 rotations and updates the 2 x 2 diagonal blocks,
-//      while waves 1..7 apply the previous round's rotations to the
+//      while waves 1..15 apply the previous round's rotations to the
 //      eigenvector rows;
 //   B  all waves update the 2016 off-diagonal 2 x 2 blocks of the upper
 //      triangle (G_PQ <- J_P^T G_PQ J_Q).
@@ -36,26 +36,50 @@ __device__ __forceinline__ int gidx(int a, int b) {
     return a < b ? a * kGP + b : b * kGP + a;
 }
 
-// Rotate eigenvector rows p, q for the pairs first, first + stride, ... of one round.
+constexpr int kThreads = 1024;  // 16 waves
+constexpr int kNW = kThreads / 64;
+
+// Rotate eigenvector rows p, q for the pairs first, first + stride, ... (< 64) of
+// one round.  All loads of the batch are issued before any store, so the wave
+// keeps up to 2 * NP LDS requests in flight instead of one dependent chain.
+template <int NP>
 __device__ __forceinline__ void rotate_vectors(float *V, const float *rc, const float *rs,
                                                const int *rp, const int *rq, int first,
                                                int stride, int lane) {
-    for (int P = first; P < 64; P += stride) {
-        const float s = rs[P];
-        if (s == 0.f) continue;  // uniform over the wave
-        const float c = rc[P];
-        float2 *vp = reinterpret_cast<float2 *>(V + rp[P] * kD) + lane;
-        float2 *vq = reinterpret_cast<float2 *>(V + rq[P] * kD) + lane;
-        const float2 a = *vp, b = *vq;
-        *vp = make_float2(c * a.x - s * b.x, c * a.y - s * b.y);
-        *vq = make_float2(s * a.x + c * b.x, s * a.y + c * b.y);
+    float c[NP], sn[NP];
+    int p[NP], q[NP];
+    bool act[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const int P = first + i * stride;
+        act[i] = P < 64;
+        const int Pc = act[i] ? P : 0;
+        c[i] = rc[Pc];
+        sn[i] = rs[Pc];
+        p[i] = rp[Pc];
+        q[i] = rq[Pc];
+        act[i] = act[i] && sn[i] != 0.f;  // uniform over the wave
     }
+    float2 a[NP], b[NP];
+    float2 *V2 = reinterpret_cast<float2 *>(V);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+        if (act[i]) {
+            a[i] = V2[p[i] * (kD / 2) + lane];
+            b[i] = V2[q[i] * (kD / 2) + lane];
+        }
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+        if (act[i]) {
+            V2[p[i] * (kD / 2) + lane] = make_float2(c[i] * a[i].x - sn[i] * b[i].x, c[i] * a[i].y - sn[i] * b[i].y);
+            V2[q[i] * (kD / 2) + lane] = make_float2(sn[i] * a[i].x + c[i] * b[i].x, sn[i] * a[i].y + c[i] * b[i].y);
+        }
 }
 
-__global__ __launch_bounds__(512) void jacobi_kernel(const float *__restrict__ gpart, int splits,
-                                                     float *__restrict__ vt_out,
-                                                     int32_t *__restrict__ sweeps_out,
-                                                     int max_sweeps, float tol) {
+__global__ __launch_bounds__(kThreads) void jacobi_kernel(const float *__restrict__ gpart, int splits,
+                                                          float *__restrict__ vt_out,
+                                                          int32_t *__restrict__ sweeps_out,
+                                                          int max_sweeps, float tol) {
     extern __shared__ float smem[];
     float *G = smem;            // 128 x 129
     float *V = smem + kD * kGP; // 128 x 128, row i = eigenvector i
@@ -66,7 +90,7 @@ __global__ __launch_bounds__(512) void jacobi_kernel(const float *__restrict__ g
     const int blk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float *src = gpart + static_cast<int64_t>(blk) * splits * kD * kD;
-    for (int e = tid; e < kD * kD; e += 512) {
+    for (int e = tid; e < kD * kD; e += kThreads) {
         float s = 0.f;
         for (int p = 0; p < splits; ++p) s += src[static_cast<int64_t>(p) * kD * kD + e];
         const int i = e >> 7, j = e & 127;
@@ -81,17 +105,20 @@ __global__ __launch_bounds__(512) void jacobi_kernel(const float *__restrict__ g
         for (int k = 0; k < 127; ++k) {
             const int buf = k & 1;
             if (wave == 0) {
+                // Phase A: the 64 rotations of this round (one pair per lane).
                 const int P = lane;
                 const int p = tournament_player(P, k), q = tournament_player(127 - P, k);
                 const int pq = gidx(p, q);
                 const float a = G[p * kGP + p], b = G[q * kGP + q], g = G[pq];
                 float c = 1.f, s = 0.f;
                 if (fabsf(g) > tol * sqrtf(fabsf(a) * fabsf(b))) {
-                    const float zeta = (b - a) / (2.f * g);
-                    const float t = fabsf(zeta) > 1e18f
-                                        ? 0.5f / zeta
-                                        : copysignf(1.f, zeta) / (fabsf(zeta) + sqrtf(1.f + zeta * zeta));
-                    c = 1.f / sqrtf(1.f + t * t);
+                    // Any (c, s) with c^2 + s^2 = 1 to working precision keeps the
+                    // transform orthogonal, so 1-ulp reciprocals are enough here.
+                    const float zeta = 0.5f * (b - a) * __builtin_amdgcn_rcpf(g);
+                    const float az = fabsf(zeta);
+                    const float t = az > 1e18f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
+                                               : copysignf(__builtin_amdgcn_rcpf(az + sqrtf(1.f + zeta * zeta)), zeta);
+                    c = __builtin_amdgcn_rsqf(1.f + t * t);
                     s = c * t;
                     G[p * kGP + p] = a - t * g;
                     G[q * kGP + q] = b + t * g;
@@ -103,48 +130,75 @@ __global__ __launch_bounds__(512) void jacobi_kernel(const float *__restrict__ g
                 rp[buf][P] = p;
                 rq[buf][P] = q;
             } else if (k > 0) {
-                rotate_vectors(V, rc[buf ^ 1], rs[buf ^ 1], rp[buf ^ 1], rq[buf ^ 1], wave - 1, 7,
-                               lane);
+                // Meanwhile waves 1..15 apply the previous round to the eigenvectors.
+                rotate_vectors<5>(V, rc[buf ^ 1], rs[buf ^ 1], rp[buf ^ 1], rq[buf ^ 1], wave - 1,
+                                  kNW - 1, lane);
             }
             __syncthreads();
 
-            // Off-diagonal 2 x 2 blocks (P < Q).  Wave-row wr pairs block-row wr
-            // (63 - wr blocks) with block-row 62 - wr (wr + 1 blocks): 64 lanes.
-            for (int wr = wave; wr < 32; wr += 8) {
-                int P, Q;
+            // Phase B: off-diagonal 2 x 2 blocks (P < Q).  Wave-row wr pairs block-row
+            // wr (63 - wr blocks) with block-row 62 - wr (wr + 1 blocks): 64 lanes.
+            // Each wave owns wave-rows wave and wave + 16, loaded as one batch.
+            int P[2], Q[2];
+            bool act[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int wr = wave + kNW * i;
+                act[i] = true;
                 if (wr < 31) {
                     if (lane < 63 - wr) {
-                        P = wr;
-                        Q = wr + 1 + lane;
+                        P[i] = wr;
+                        Q[i] = wr + 1 + lane;
                     } else {
-                        P = 62 - wr;
-                        Q = lane;
+                        P[i] = 62 - wr;
+                        Q[i] = lane;
                     }
                 } else {
-                    if (lane >= 32) continue;
-                    P = 31;
-                    Q = 32 + lane;
+                    act[i] = lane < 32;
+                    P[i] = 31;
+                    Q[i] = 32 + (lane & 31);
                 }
-                const float s1 = rs[buf][P], s2 = rs[buf][Q];
-                if (s1 == 0.f && s2 == 0.f) continue;
-                const float c1 = rc[buf][P], c2 = rc[buf][Q];
-                const int p1 = rp[buf][P], q1 = rq[buf][P];
-                const int p2 = rp[buf][Q], q2 = rq[buf][Q];
-                const int i11 = gidx(p1, p2), i12 = gidx(p1, q2);
-                const int i21 = gidx(q1, p2), i22 = gidx(q1, q2);
-                const float g11 = G[i11], g12 = G[i12], g21 = G[i21], g22 = G[i22];
-                // rows of pair P, then columns of pair Q
-                const float h11 = c1 * g11 - s1 * g21, h12 = c1 * g12 - s1 * g22;
-                const float h21 = s1 * g11 + c1 * g21, h22 = s1 * g12 + c1 * g22;
-                G[i11] = c2 * h11 - s2 * h12;
-                G[i12] = s2 * h11 + c2 * h12;
-                G[i21] = c2 * h21 - s2 * h22;
-                G[i22] = s2 * h21 + c2 * h22;
             }
+            float c1[2], s1[2], c2[2], s2[2];
+            int i11[2], i12[2], i21[2], i22[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                c1[i] = rc[buf][P[i]];
+                s1[i] = rs[buf][P[i]];
+                c2[i] = rc[buf][Q[i]];
+                s2[i] = rs[buf][Q[i]];
+                const int p1 = rp[buf][P[i]], q1 = rq[buf][P[i]];
+                const int p2 = rp[buf][Q[i]], q2 = rq[buf][Q[i]];
+                i11[i] = gidx(p1, p2);
+                i12[i] = gidx(p1, q2);
+                i21[i] = gidx(q1, p2);
+                i22[i] = gidx(q1, q2);
+                act[i] = act[i] && !(s1[i] == 0.f && s2[i] == 0.f);
+            }
+            float g11[2], g12[2], g21[2], g22[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                if (act[i]) {
+                    g11[i] = G[i11[i]];
+                    g12[i] = G[i12[i]];
+                    g21[i] = G[i21[i]];
+                    g22[i] = G[i22[i]];
+                }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                if (act[i]) {
+                    // rows of pair P, then columns of pair Q
+                    const float h11 = c1[i] * g11[i] - s1[i] * g21[i], h12 = c1[i] * g12[i] - s1[i] * g22[i];
+                    const float h21 = s1[i] * g11[i] + c1[i] * g21[i], h22 = s1[i] * g12[i] + c1[i] * g22[i];
+                    G[i11[i]] = c2[i] * h11 - s2[i] * h12;
+                    G[i12[i]] = s2[i] * h11 + c2[i] * h12;
+                    G[i21[i]] = c2[i] * h21 - s2[i] * h22;
+                    G[i22[i]] = s2[i] * h21 + c2[i] * h22;
+                }
             __syncthreads();
         }
         // The last round (126, buffer 0) still has to reach the eigenvectors.
-        rotate_vectors(V, rc[0], rs[0], rp[0], rq[0], wave, 8, lane);
+        rotate_vectors<4>(V, rc[0], rs[0], rp[0], rq[0], wave, kNW, lane);
         __syncthreads();
         const int rot = any_rot;
         __syncthreads();
@@ -156,7 +210,7 @@ __global__ __launch_bounds__(512) void jacobi_kernel(const float *__restrict__ g
     }
 
     float *dst = vt_out + static_cast<int64_t>(blk) * kD * kD;
-    for (int e = tid; e < kD * kD / 4; e += 512)
+    for (int e = tid; e < kD * kD / 4; e += kThreads)
         reinterpret_cast<float4 *>(dst)[e] = reinterpret_cast<const float4 *>(V)[e];
     if (tid == 0 && sweeps_out) sweeps_out[blk] = used;
 }
@@ -171,7 +225,7 @@ hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(512), lds, st,
+    hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), lds, st,
                        gpart, splits, vt, sweeps, max_sweeps, tol);
     return hipGetLastError();
 }

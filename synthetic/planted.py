@@ -29,10 +29,13 @@ _DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f64": torch.float64}
 def _thin_q(Gm: torch.Tensor) -> torch.Tensor:
     """Q of the thin QR of tall Gm [n, m, d] (m >= d) with R's diagonal positive,
     computed as G R^{-1} with R^T R = G^T G (Cholesky); fp64 keeps it orthonormal
-    to ~1e-15 for the well-conditioned tall Gaussians used here."""
+    to ~1e-15 for the well-conditioned tall Gaussians used here.  R^{-1} is
+    formed explicitly (d x d) so the large product is a plain batched matmul."""
     S = Gm.transpose(-1, -2) @ Gm
     L = torch.linalg.cholesky(S)
-    return torch.linalg.solve_triangular(L, Gm.transpose(-1, -2), upper=False).transpose(-1, -2)
+    eye = torch.eye(L.shape[-1], dtype=L.dtype, device=L.device).expand_as(L)
+    Linv = torch.linalg.solve_triangular(L, eye, upper=False)
+    return Gm @ Linv.transpose(-1, -2)
 
 
 def _square_q(Gm: torch.Tensor) -> torch.Tensor:
