@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void gram_kernel(const void *__restrict__ x,
                                                    const int64_t *__restrict__ row0,
                                                    int64_t row_stride, int T, int splits,
                                                    float *__restrict__ gpart) {
-    __shared__ uint16_t tile[NX][kTT * kPitch];
+    __shared__ __align__(16) uint16_t tile[NX][kTT * kPitch];
     const int blk = blockIdx.x / splits;
     const int sp = blockIdx.x - blk * splits;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

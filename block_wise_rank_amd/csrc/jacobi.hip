@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void jacobi_kernel(const float *__restric
                                                           float *__restrict__ vt_out,
                                                           int32_t *__restrict__ sweeps_out,
                                                           int max_sweeps, float tol) {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];
     float *G = smem;            // 128 x 129
     float *V = smem + kD * kGP; // 128 x 128, row i = eigenvector i
     __shared__ float rc[2][64], rs[2][64];

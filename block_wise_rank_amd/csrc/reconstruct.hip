@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off,
     const float *__restrict__ a_scale, const float *__restrict__ b_scale, int T,
     const int32_t *__restrict__ ids, void *__restrict__ out) {
-    __shared__ float Bs[kD * kD];
+    __shared__ __align__(16) float Bs[kD * kD];
     __shared__ float As[kD * 64];
     const int n = blockIdx.x;
     const int id = ids[n];

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
                                                      int64_t row_stride, int T,
                                                      float *__restrict__ vt,
                                                      float *__restrict__ sigma) {
-    __shared__ float Vs[kD * kD];  // 64 KiB, row i = eigenvector i
+    __shared__ __align__(16) float Vs[kD * kD];  // 64 KiB, row i = eigenvector i
     __shared__ float ss[kD];       // sum of squares per eigenvector
     __shared__ float sig[kD];
     __shared__ int perm[kD];
