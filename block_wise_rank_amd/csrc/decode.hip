@@ -43,27 +43,43 @@ constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct LdsLayout {
-    int bk, qf, scratch, pt, alpha, total;
+    int bk, qf, scratch, pt, alpha, kst, total;
 };
 
 __host__ __device__ inline int align16(int v) { return (v + 15) & ~15; }
 
+// Staging pitch (bytes) of one 32-token rank row of an A_k tile: the row plus 8
+// bytes, so rows 8 apart (the two lane halves of a transposed read) fall on
+// disjoint LDS banks.  fp32 factors bypass the staging buffer.
+__host__ __device__ inline int kst_pitch(int esize) { return esize == 4 ? 0 : 32 * esize + 8; }
+
 // All offsets in bytes.  scratch holds the prologue tables (RoPE table, the
 // queries, theta) and is reused for the end-of-split merge.
-__host__ __device__ inline LdsLayout lds_layout(int ns, int n_tiles, int G, bool tail) {
+__host__ __device__ inline LdsLayout lds_layout(int ns, int n_tiles, int G, bool tail, int esize) {
     LdsLayout L;
     const int bk = tail ? 0 : ns * 4 * 8 * 64 * 8 * 2;
     const int qf = ns * n_tiles * 8 * 2 * G * 8 * 2;
     const int prologue = 32 * 64 * 8 + G * 128 * 4 + 64 * 8;
     const int merge = kWaves * G * 128 * 4 + 2 * kWaves * 16 * 4;
     const int scratch = prologue > merge ? prologue : merge;
+    const int kst = tail ? 0 : kWaves * 128 * kst_pitch(esize);
     L.bk = 0;
     L.qf = align16(L.bk + bk);
     L.scratch = align16(L.qf + qf);
     L.pt = align16(L.scratch + scratch);
     L.alpha = align16(L.pt + kWaves * ns * 16 * 32 * 2);
-    L.total = align16(L.alpha + kWaves * 16 * 4);
+    L.kst = align16(L.alpha + kWaves * 16 * 4);
+    L.total = align16(L.kst + kst);
     return L;
+}
+
+// Order this wave's LDS writes before its later LDS reads of other lanes' data
+// (LDS executes a wave's operations in order; the fences stop the compiler from
+// reordering across this point).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int F>
@@ -87,7 +103,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
     const int G = p.group;
     const int n_tiles = p.split_len / kTile;
     const int tiles_per_wave = n_tiles / kWaves;
-    const LdsLayout L = lds_layout(NS, n_tiles, G, TAIL);
+    constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);
+    const LdsLayout L = lds_layout(NS, n_tiles, G, TAIL, ES);
     uint16_t *bk = reinterpret_cast<uint16_t *>(lds + L.bk);
     uint16_t *qf = reinterpret_cast<uint16_t *>(lds + L.qf);
     float2 *rope_tab = reinterpret_cast<float2 *>(lds + L.scratch);
@@ -156,18 +173,19 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
     __syncthreads();
     for (int e = tid; e < 32 * 64; e += 256) {
         const int t = e >> 6, j = e & 63;
-        double sn, cs;
-        sincos(static_cast<double>(t) * theta[j], &sn, &cs);
-        rope_tab[e] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+        float sn, cs;  // angle < 32 rad: fp32 sincos is accurate after its own reduction
+        sincosf(static_cast<float>(static_cast<double>(t) * theta[j]), &sn, &cs);
+        rope_tab[e] = make_float2(cs, sn);
     }
     const int qf_term = n_tiles * 8 * 2 * G * 8;  // elements per bf16 term
     const int64_t qpos = p.q_pos[s];
     for (int e = tid; e < n_tiles * 64; e += 256) {
         const int tl = e >> 6, j = e & 63;
         double a = static_cast<double>(qpos - (pos0 + tl * kTile)) * theta[j];
-        a -= kTwoPi * rint(a / kTwoPi);
-        double sn, cs;
-        sincos(a, &sn, &cs);
+        a -= kTwoPi * rint(a / kTwoPi);  // exact enough in fp64 for positions < 2^40
+        float snf, csf;
+        sincosf(static_cast<float>(a), &snf, &csf);
+        const double sn = snf, cs = csf;
 #pragma unroll 1
         for (int g = 0; g < G; ++g) {
             const double x1 = qs[g * kD + j], x2 = qs[g * kD + j + 64];
@@ -225,7 +243,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
             rsn[jt][i] = v.y;
         }
 
-    // ---- main loop over this wave's tiles
+    // ---- main loop over this wave's tiles (contiguous tiles per wave)
     float m_run[8], l_run[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -238,28 +256,112 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
     const int NTU = TAIL ? 8 : (rv + 15) >> 4;
     const float lscale = p.softmax_scale * kLog2e;
     uint16_t *my_pt = pt + wave * NS * 16 * 32;
+    const int tile0 = wave * tiles_per_wave;
+
+    // A_k tiles (bf16 / int8): 16-byte coalesced loads of LPR lanes per rank row,
+    // staged rank-major in this wave's LDS buffer and read back transposed
+    // (8 ranks of one token per lane).  Rows past rk reuse row rk - 1 (finite
+    // values; their B_k fragment rows are zero).
+    constexpr int RB = 32 * ES;                 // bytes of one rank row of a tile
+    constexpr int LPR = RB / 16 > 0 ? RB / 16 : 1;
+    constexpr int RPI = 64 / LPR;               // rank rows per load instruction
+    constexpr int NI = 128 / RPI;               // load instructions for 128 ranks
+    constexpr int KP = (F == kF32) ? 16 : 32 * ES + 8;  // staging pitch (bytes)
+    uint8_t *kst = lds + L.kst + wave * 128 * KP;
+    const int rk_pad = KS * 16;
+    uint4 kraw[F == kF32 ? 1 : NI];
+    auto load_k = [&](int tl) {
+        if constexpr (F != kF32 && !TAIL) {
+            const int tt0 = tok0 + tl * kTile;
+#pragma unroll
+            for (int c = 0; c < NI; ++c)
+                if (c * RPI < rk_pad) {
+                    const int r = min(c * RPI + lane / LPR, rk - 1);
+                    kraw[c] = *reinterpret_cast<const uint4 *>(
+                        Ak + (static_cast<int64_t>(r) * T + tt0) * ES + (lane % LPR) * 16);
+                }
+        }
+    };
+    // A_v fragments for P A_v (16x16x32 B operand): rank column 16 n + lane % 16,
+    // tokens tb .. tb + 7.  bf16: one 16-byte load; int8: 8 bytes; fp32: 32 bytes.
+    u16x8_t vraw[F == kF32 ? 1 : 8];
+    auto load_v = [&](int tl) {
+        if constexpr (F != kF32 && !TAIL) {
+            const int tb = tok0 + tl * kTile + 8 * (lane >> 4);
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+                if (n < NTU) {
+                    const int col = min(16 * n + (lane & 15), rv - 1);
+                    if constexpr (F == kBF16) {
+                        vraw[n] = *reinterpret_cast<const u16x8_t *>(
+                            reinterpret_cast<const uint16_t *>(Av) + static_cast<int64_t>(col) * T + tb);
+                    } else {
+                        const uint2 w = *reinterpret_cast<const uint2 *>(Av + static_cast<int64_t>(col) * T + tb);
+                        vraw[n][0] = static_cast<uint16_t>(w.x & 0xffff);
+                        vraw[n][1] = static_cast<uint16_t>(w.x >> 16);
+                        vraw[n][2] = static_cast<uint16_t>(w.y & 0xffff);
+                        vraw[n][3] = static_cast<uint16_t>(w.y >> 16);
+                    }
+                }
+        }
+    };
+    // Pipeline: the staging buffer holds tile it while its keys are rebuilt; the
+    // A_k registers already hold tile it + 1 and A_v registers tile it.  Each
+    // wait therefore covers loads issued a whole tile earlier.
+    auto stage_k = [&]() {
+        if constexpr (F != kF32 && !TAIL) {
+#pragma unroll
+            for (int c = 0; c < NI; ++c)
+                if (c * RPI < rk_pad) {
+                    uint8_t *dst = kst + (c * RPI + lane / LPR) * KP + (lane % LPR) * 16;
+                    reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[c].x, kraw[c].y);
+                    reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[c].z, kraw[c].w);
+                }
+            wave_lds_sync();
+        }
+    };
+    load_k(tile0);
+    stage_k();
+    load_v(tile0);
+    if (tiles_per_wave > 1) load_k(tile0 + 1);
 
     for (int it = 0; it < tiles_per_wave; ++it) {
-        const int tl = wave * tiles_per_wave + it;
+        const int tl = tile0 + it;
         const int tloc = tl * kTile;           // offset within the split
         const int t = tok0 + tloc + tl_;       // this lane's token (block- or tail-local)
         const bool tok_ok = tloc + tl_ < valid;
 
-        // K^T tile: kacc[jt][i] = k_hat[t][32 jt + 8 (i/4) + 4 hf + i%4]
+        // ---- K^T tile: kacc[jt][i] = k_hat[t][32 jt + 8 (i/4) + 4 hf + i%4]
         f32x16_t kacc[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) kacc[jt] = zero16();
         if constexpr (!TAIL) {
             for (int ks = 0; ks < KS; ++ks) {
                 u16x8_t af[NS];
+                if constexpr (F == kBF16) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = 16 * ks + 8 * hf_ + e;
-                    const float v = r < rk ? load_elem<F>(Ak, static_cast<int64_t>(r) * T + t) : 0.f;
-                    uint16_t tv[2];
-                    to_terms<NS>(v, tv);
+                    for (int e = 0; e < 8; ++e)
+                        af[0][e] = *reinterpret_cast<const uint16_t *>(kst + (16 * ks + 8 * hf_ + e) * KP + tl_ * 2);
+                } else if constexpr (F == kI8) {
 #pragma unroll
-                    for (int st = 0; st < NS; ++st) af[st][e] = tv[st];
+                    for (int e = 0; e < 8; ++e)
+                        af[0][e] = f32_to_bf16_bits(static_cast<float>(
+                            *reinterpret_cast<const int8_t *>(kst + (16 * ks + 8 * hf_ + e) * KP + tl_)));
+                } else {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int r = 16 * ks + 8 * hf_ + e;
+                        v[e] = load_elem<F>(Ak, static_cast<int64_t>(min(r, rk - 1)) * T + t);
+                        if (r >= rk) v[e] = 0.f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        uint16_t tv[2];
+                        to_terms<NS>(v[e], tv);
+#pragma unroll
+                        for (int st = 0; st < NS; ++st) af[st][e] = tv[st];
+                    }
                 }
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) {
@@ -274,18 +376,18 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
                 }
             }
         } else {
-            if (tok_ok) {
-                const int64_t row = ((static_cast<int64_t>(s) * Hkv + h) * p.tail_cap + t) * kD;
+            const int tc = min(t, tok0 + valid - 1);  // clamped: masked lanes read a valid row
+            const int64_t row = ((static_cast<int64_t>(s) * Hkv + h) * p.tail_cap + tc) * kD;
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt)
+            for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int j0 = 32 * jt + 8 * q4 + 4 * hf_;
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int j0 = 32 * jt + 8 * q4 + 4 * hf_;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            kacc[jt][4 * q4 + e] = load_elem<F>(static_cast<const uint8_t *>(p.tail_k), row + j0 + e);
-                    }
-            }
+                    for (int e = 0; e < 4; ++e)
+                        kacc[jt][4 * q4 + e] =
+                            load_elem<F>(static_cast<const uint8_t *>(p.tail_k), row + j0 + e);
+                }
         }
         // RoPE by the in-tile offset (pairs j, j + 64 sit in kacc[jt], kacc[jt + 2])
 #pragma unroll
@@ -326,11 +428,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
         }
         // online softmax (log2 domain); S[i] holds head g = 8 (i/4) + 4 hf + i%4, token tl_
         float tscale = lscale;
-        if constexpr (F == kI8 && !TAIL)
-            tscale *= tok_ok ? p.k_ascale[static_cast<int64_t>(fid) * T + t] : 0.f;
         float vscale = 1.f;
-        if constexpr (F == kI8 && !TAIL)
-            vscale = tok_ok ? p.v_ascale[static_cast<int64_t>(fid) * T + t] : 0.f;
+        if constexpr (F == kI8 && !TAIL) {
+            tscale *= p.k_ascale[static_cast<int64_t>(fid) * T + t];
+            vscale = p.v_ascale[static_cast<int64_t>(fid) * T + t];
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int g = 8 * (i >> 2) + 4 * hf_ + (i & 3);
@@ -350,7 +452,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
                 if (tl_ == 0) alpha_s[wave * 16 + g] = alpha;
             }
         }
-        __syncthreads();
+        wave_lds_sync();
         // u = u * alpha + P A_v   (u rows: g = 4 (lane/16) + i, columns: rank 16 n + lane%16)
         {
             const int g0 = 4 * (lane >> 4);
@@ -369,34 +471,35 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
                     for (int i = 0; i < 4; ++i) u[n][i] *= al[i];
                     const int col = 16 * n + (lane & 15);
                     u16x8_t vf[NS];
-                    if constexpr (!TAIL) {
-                        if (col < rv) {
-                            if constexpr (F == kBF16) {
-                                vf[0] = *reinterpret_cast<const u16x8_t *>(
-                                    reinterpret_cast<const uint16_t *>(Av) + static_cast<int64_t>(col) * T + tb);
-                            } else {
+                    if constexpr (!TAIL && F == kBF16) {
+                        vf[0] = vraw[n];
+                        if (col >= rv)
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) {
-                                    uint16_t tv[2];
-                                    to_terms<NS>(load_elem<F>(Av, static_cast<int64_t>(col) * T + tb + e), tv);
+                            for (int e = 0; e < 8; ++e) vf[0][e] = 0;
+                    } else if constexpr (!TAIL && F == kI8) {
 #pragma unroll
-                                    for (int st = 0; st < NS; ++st) vf[st][e] = tv[st];
-                                }
-                            }
-                        } else {
+                        for (int e = 0; e < 8; ++e) {
+                            const int8_t c8 = static_cast<int8_t>((vraw[n][e >> 1] >> (8 * (e & 1))) & 0xff);
+                            vf[0][e] = col < rv ? f32_to_bf16_bits(static_cast<float>(c8)) : 0;
+                        }
+                    } else if constexpr (!TAIL) {
+                        const int cc = min(col, rv - 1);
 #pragma unroll
-                            for (int st = 0; st < NS; ++st)
+                        for (int e = 0; e < 8; ++e) {
+                            uint16_t tv[2];
+                            const float v = col < rv ? load_elem<F>(Av, static_cast<int64_t>(cc) * T + tb + e) : 0.f;
+                            to_terms<NS>(v, tv);
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) vf[st][e] = 0;
+                            for (int st = 0; st < NS; ++st) vf[st][e] = tv[st];
                         }
                     } else {
                         const int64_t rowb = (static_cast<int64_t>(s) * Hkv + h) * p.tail_cap;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const bool ok = tb + e - tok0 < valid;
-                            const float v = ok ? load_elem<F>(static_cast<const uint8_t *>(p.tail_v),
-                                                              (rowb + tb + e) * kD + col)
-                                               : 0.f;
+                            const int te = ok ? tb + e : tok0;
+                            float v = load_elem<F>(static_cast<const uint8_t *>(p.tail_v), (rowb + te) * kD + col);
+                            if (!ok) v = 0.f;
                             uint16_t tv[2];
                             to_terms<NS>(v, tv);
 #pragma unroll
@@ -410,6 +513,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
                             if (sa + sb < NS) u[n] = mfma16x16x32(pf[sa], vf[sb], u[n]);
                 }
             }
+        }
+        if (it + 1 < tiles_per_wave) {
+            wave_lds_sync();  // this tile's staged keys have been read
+            stage_k();
+            load_v(tl + 1);
+            if (it + 2 < tiles_per_wave) load_k(tl + 2);
         }
     }
 
@@ -515,7 +624,8 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeParams 
 template <int F, bool TAIL>
 hipError_t launch_partial(const DecodeParams &p, dim3 grid, hipStream_t st) {
     constexpr int NS = (F == kF32) ? 2 : 1;
-    const LdsLayout L = lds_layout(NS, p.split_len / kTile, p.group, TAIL);
+    constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);
+    const LdsLayout L = lds_layout(NS, p.split_len / kTile, p.group, TAIL, ES);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_partial_kernel<F, TAIL>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
