@@ -68,7 +68,7 @@ __host__ __device__ inline LdsLayout lds_layout(int ns, int n_tiles, int G, bool
     L.scratch = align16(L.qf + qf);
     L.pt = align16(L.scratch + scratch);
     L.alpha = align16(L.pt + kWaves * ns * 16 * 32 * 2);
-    L.kst = align16(L.alpha + kWaves * 16 * 4);
+    L.kst = align16(L.alpha + 128 * 4);  // alpha per wave (64 floats), or 128 B-row scales
     L.total = align16(L.kst + kst);
     return L;
 }
@@ -80,6 +80,23 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Copy nbytes (a multiple of 16) from global memory to LDS in rounds of 4 KiB
+// per 4 chunks per thread: each round issues all its loads before any store.
+__device__ __forceinline__ void copy_to_lds(uint8_t *dst, const uint8_t *src, int nbytes) {
+    const int n = nbytes >> 4;
+    for (int base = 0; base < n; base += 1024) {
+        uint4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = reinterpret_cast<const uint4 *>(src)[min(base + static_cast<int>(threadIdx.x) + 256 * i, n - 1)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = base + threadIdx.x + 256 * i;
+            if (c < n) reinterpret_cast<uint4 *>(dst)[c] = v[i];
+        }
+    }
 }
 
 template <int F>
@@ -164,11 +181,19 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
 
     // ---- prologue: theta, queries, in-tile RoPE table, rotated query fragments
     if (tid < 64) theta[tid] = exp2(-(2.0 * tid / 128.0) * log2(p.rope_base));
-    for (int e = tid; e < G * kD; e += 256) {
-        const int g = e >> 7, j = e & 127;
-        const int64_t qi = (static_cast<int64_t>(s) * p.n_q_heads + h * G + g) * kD + j;
-        qs[e] = p.q_type == kF32 ? static_cast<const float *>(p.q)[qi]
-                                 : bf16_bits_to_f32(static_cast<const uint16_t *>(p.q)[qi]);
+    {
+        // the G query heads of this KV head are consecutive rows of q
+        const int64_t q0 = (static_cast<int64_t>(s) * p.n_q_heads + h * G) * kD;
+        float qv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = min(tid + 256 * i, G * kD - 1);
+            qv[i] = p.q_type == kF32 ? static_cast<const float *>(p.q)[q0 + e]
+                                     : bf16_bits_to_f32(static_cast<const uint16_t *>(p.q)[q0 + e]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (tid + 256 * i < G * kD) qs[tid + 256 * i] = qv[i];
     }
     __syncthreads();
     for (int e = tid; e < 32 * 64; e += 256) {
@@ -214,19 +239,45 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
         Av = p.v_arena + p.v_aoff[fid];
         Bv = p.v_arena + p.v_boff[fid];
         const uint8_t *Bk = p.k_arena + p.k_boff[fid];
-        for (int e = tid; e < KS * 16 * kD; e += 256) {
-            const int r = e >> 7, j = e & 127;
-            float v = 0.f;
-            if (r < rk) {
-                v = load_elem<F>(Bk, e);
-                if constexpr (F == kI8) v *= p.k_bscale[static_cast<int64_t>(fid) * kD + r];
-            }
-            const int jt = j >> 5, ln = (j & 31) + 32 * ((r >> 3) & 1);
-            const int idx = ((jt * 8 + (r >> 4)) * 64 + ln) * 8 + (r & 7);
-            uint16_t tv[2];
-            to_terms<NS>(v, tv);
+        if constexpr (F != kF32) {
+            // rows of B_k (and their INT8 scales) -> LDS, then into MFMA fragment order
+            uint8_t *tmp = lds + L.kst;
+            float *bsc = reinterpret_cast<float *>(lds + L.alpha);  // free until the main loop
+            copy_to_lds(tmp, Bk, rk * kD * ES);
+            if constexpr (F == kI8)
+                if (tid < rk) bsc[tid] = p.k_bscale[static_cast<int64_t>(fid) * kD + tid];
+            __syncthreads();
+            for (int q = tid; q < 4 * 8 * 64; q += 256) {
+                const int ln = q & 63, ks = (q >> 6) & 7, jt = q >> 9;
+                if (ks >= KS) continue;
+                const int j = 32 * jt + (ln & 31), r0 = 16 * ks + 8 * (ln >> 5);
+                u16x8_t ch;
 #pragma unroll
-            for (int st = 0; st < NS; ++st) bk[st * (4 * 8 * 64 * 8) + idx] = tv[st];
+                for (int e = 0; e < 8; ++e) {
+                    const int r = r0 + e;
+                    float v = 0.f;
+                    if (r < rk) {
+                        if constexpr (F == kBF16)
+                            v = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(tmp)[r * kD + j]);
+                        else
+                            v = static_cast<float>(reinterpret_cast<const int8_t *>(tmp)[r * kD + j]) * bsc[r];
+                    }
+                    ch[e] = f32_to_bf16_bits(v);
+                }
+                *reinterpret_cast<u16x8_t *>(bk + q * 8) = ch;
+            }
+            __syncthreads();  // the staging area is reused for A_k tiles
+        } else {
+            for (int e = tid; e < KS * 16 * kD; e += 256) {
+                const int r = e >> 7, j = e & 127;
+                const float v = r < rk ? load_elem<F>(Bk, e) : 0.f;
+                const int jt = j >> 5, ln = (j & 31) + 32 * ((r >> 3) & 1);
+                const int idx = ((jt * 8 + (r >> 4)) * 64 + ln) * 8 + (r & 7);
+                uint16_t tv[2];
+                to_terms<NS>(v, tv);
+#pragma unroll
+                for (int st = 0; st < NS; ++st) bk[st * (4 * 8 * 64 * 8) + idx] = tv[st];
+            }
         }
     }
     // P^T staging rows g >= G stay zero for the whole split.
@@ -539,6 +590,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
             const int g = 4 * (lane >> 4) + i;
             if (n < NTU && g < G) us[(wave * G + g) * kD + 16 * n + (lane & 15)] = u[n][i];
         }
+    const uint8_t *bv_src = Bv;
+    if constexpr (!TAIL && F != kF32) {
+        // B_v rows (and INT8 scales) -> LDS; the A_k staging area is free now
+        copy_to_lds(lds + L.kst, Bv, rv * kD * ES);
+        if constexpr (F == kI8)
+            if (tid < rv) reinterpret_cast<float *>(lds + L.alpha)[tid] = p.v_bscale[static_cast<int64_t>(fid) * kD + tid];
+        bv_src = lds + L.kst;
+    }
     __syncthreads();
     for (int e = tid; e < G * kD; e += 256) {
         const int g = e >> 7, j = e & 127;
@@ -559,8 +618,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
                 float uw = 0.f;
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) uw += coef[w] * us[(w * G + g) * kD + r];
-                float bv = load_elem<F>(Bv, static_cast<int64_t>(r) * kD + j);
-                if constexpr (F == kI8) bv *= p.v_bscale[static_cast<int64_t>(fid) * kD + r];
+                float bv = load_elem<F>(bv_src, static_cast<int64_t>(r) * kD + j);
+                if constexpr (F == kI8) bv *= reinterpret_cast<const float *>(lds + L.alpha)[r];
                 o += uw * bv;
             }
         } else {
