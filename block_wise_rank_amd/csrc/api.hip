@@ -434,10 +434,26 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
     }
     if (!(a->rope_base > 1.0) || !std::isfinite(a->rope_base)) return fail(MILO_E_INVALID, "rope_base must be finite and > 1");
     if (!std::isfinite(a->softmax_scale)) return fail(MILO_E_INVALID, "softmax_scale must be finite");
+    const int ftype = k->dtype == MILO_F32 ? milo::kF32 : (k->dtype == MILO_BF16 ? milo::kBF16 : milo::kI8);
+    const int ttype = a->tail_dtype == MILO_F32 ? milo::kF32 : milo::kBF16;
     int split = a->split_len;
-    if (split == 0) split = (T % 256 == 0) ? 256 : 128;
+    if (split == 0) {
+        // The longest split that still gives >= 1024 workgroups (four per CU):
+        // each split pays a prologue (B_k fragments, rotated queries) and a merge.
+        const int64_t units = static_cast<int64_t>(a->batch) * a->n_kv_heads *
+                              (a->sel_ptr ? a->sel_max : a->blocks_per_seq);
+        split = 128;
+        for (int c = 1024; c > 128; c /= 2)
+            if (T % c == 0 && units * (T / c) >= 1024 &&
+                milo::decode_split_fits(ftype, ttype, tail, G, c)) {
+                split = c;
+                break;
+            }
+    }
     if (split < 128 || split % 128 != 0 || T % split != 0 || split > 1024)
         return fail(MILO_E_UNSUPPORTED, "split_len must be a multiple of 128, at most 1024, dividing block_len");
+    if (!milo::decode_split_fits(ftype, ttype, tail, G, split))
+        return fail(MILO_E_UNSUPPORTED, "split_len %d needs more LDS than a workgroup has for %d query heads per KV head", split, G);
 
     milo::DecodeParams p{};
     p.q = a->q;

@@ -28,12 +28,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN): one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two values in one conversion: low half = a, high half = b.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+    const f2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2_t));
 }
 
 // Exact split of an fp32 value into three bf16 terms: f = hi + mid + lo for

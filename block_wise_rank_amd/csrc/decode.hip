@@ -694,6 +694,18 @@ hipError_t launch_partial(const DecodeParams &p, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
+bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int split) {
+    constexpr int kMaxLds = 160 * 1024;
+    const int esz = f_type == kF32 ? 4 : (f_type == kBF16 ? 2 : 1);
+    const int ns = f_type == kF32 ? 2 : 1;
+    if (lds_layout(ns, split / kTile, G, false, esz).total > kMaxLds) return false;
+    if (has_tail) {
+        const int tns = tail_type == kF32 ? 2 : 1;
+        if (lds_layout(tns, split / kTile, G, true, tail_type == kF32 ? 4 : 2).total > kMaxLds) return false;
+    }
+    return true;
+}
+
 size_t decode_workspace_bytes(const DecodeParams &p) {
     const size_t n = static_cast<size_t>(p.batch) * p.n_kv_heads * p.n_splits * p.group;
     const size_t ml = (n * 2 * sizeof(float) + 255) / 256 * 256;

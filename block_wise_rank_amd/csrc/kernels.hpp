@@ -81,6 +81,8 @@ struct DecodeParams {
     float *part_o;     // [batch][Hkv][n_splits][group][128]
 };
 
+// Whether a split of `split` tokens fits the decode kernels' LDS budget.
+bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int split);
 size_t decode_workspace_bytes(const DecodeParams &p);
 // Partial results of the compressed-block splits, of the tail splits, and the
 // log-sum-exp merge into the output.

@@ -203,8 +203,9 @@ typedef struct milo_decode_args {
     float softmax_scale;      /* e.g. 1/sqrt(head_dim)                                   */
     void *out;                /* device [batch][n_q_heads][head_dim]                    */
     milo_dtype out_dtype;     /* MILO_F32 or MILO_BF16                                  */
-    int32_t split_len;        /* tokens per work split: multiple of 64 dividing          */
-                              /* block_len (and tail_cap); 0 picks one                  */
+    int32_t split_len;        /* tokens per work split: multiple of 128, at most 1024,   */
+                              /* dividing block_len; 0 picks the longest split that     */
+                              /* still gives >= 1024 workgroups (else 128)              */
     void *workspace;          /* device scratch for the per-split partial results       */
     size_t workspace_bytes;
 } milo_decode_args;
