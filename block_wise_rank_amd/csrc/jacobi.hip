@@ -1,217 +1,327 @@
 // Batched symmetric eigensolve of 128 x 128 Gram matrices by cyclic two-sided
-// Jacobi, held entirely in LDS (one workgroup of 16 waves per block).
+// Jacobi; the matrix lives in LDS and the eigenvectors in registers.
 //
 // A Jacobi rotation of the pair (p, q) of G = X^T X is the same rotation a
 // one-sided (Hestenes) Jacobi step applies to columns p, q of X, computed from
 // alpha = G_pp, beta = G_qq, gamma = G_pq (Golub & Van Loan, Matrix
 // Computations, sec. 8.5 and 8.6): zeta = (beta - alpha) / (2 gamma),
-// t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), c = 1/sqrt(1 + t^2), s = c t.
+// t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), c = 1/sqrt(1 + t^2), s = c t;
+// afterwards G_pp = alpha - t gamma, G_qq = beta + t gamma, G_pq = 0.
 //
-// Ordering: the round-robin ("circle") tournament on 128 indices gives 127
-// rounds of 64 disjoint pairs per sweep, so one round's rotations commute and
-// are applied together.  Per round:
-//   A  wave 0 computes the 64 rotations and updates the 2 x 2 diagonal blocks,
-//      while waves 1..15 apply the previous round's rotations to the
-//      eigenvector rows;
-//   B  all waves update the 2016 off-diagonal 2 x 2 blocks of the upper
-//      triangle (G_PQ <- J_P^T G_PQ J_Q).
-// G is kept as its upper triangle inside a 128 x 129 array (pitch 129 puts
-// G[a][b] on bank (a + b) mod 32 whichever triangle is addressed); the
-// eigenvectors are rows of a 128 x 128 array.  Pairs whose rotation is the
-// identity (already orthogonal to tolerance) skip their LDS traffic, so late
-// sweeps cost little.  A sweep without any rotation ends the solve.
+// Ordering: the round-robin ("circle") tournament.  Positions 0..127 form 64
+// slots, slot P = positions (P, 127 - P); in round k position 0 holds index 0
+// and position i >= 1 holds index 1 + (i - 1 + k) mod 127.  One round's 64
+// pairs are disjoint, so their rotations commute and are applied together;
+// 127 rounds make a sweep.  From one round to the next every index except 0
+// moves to the neighbouring position, which is what the layout exploits:
+//
+//  * Eigenvectors: wave w holds slots 8w .. 8w + 7, both rows of each slot, two
+//    components per lane.  A rotation is lane-local; between rounds the rows
+//    shift one slot along the ring (first rows down, second rows up), inside
+//    the registers except for the 14 rows that cross a wave boundary, which go
+//    through a small double-buffered LDS exchange area.
+//  * Off-diagonal 2 x 2 blocks (slot P, slot Q), P < Q, of G: 2016 per round.
+//    G's upper triangle is indexed by matrix index (pitch 129 puts G[a][b] on
+//    bank (a + b) mod 32 whichever triangle is addressed).
+//  * Rotation parameters: the two indices of round k + 1's pair P' sit in
+//    slots P' + 1 (first row) and P' - 1 (second row) of round k (the ends of
+//    the ring differ slightly), so their off-diagonal entry is an
+//    element of block (P' - 1, P' + 1) and their new diagonal entries come from
+//    the rotations of pairs P' - 1 and P' + 1.  The lane that rotates that block
+//    in round k therefore has everything round k + 1's rotation P' needs and
+//    computes it at once; parameters and new diagonal entries of every pair are
+//    double-buffered in LDS.  One barrier per round.
+//
+// Pairs whose rotation is the identity (already orthogonal to tolerance) skip
+// their LDS traffic, so late sweeps cost little; a sweep without any rotation
+// ends the solve.  Diagonal entries are never stored in G.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace milo {
 namespace {
 
-constexpr int kGP = 129;  // LDS pitch of G (floats)
+constexpr int kGP = 129;              // LDS pitch of G (floats)
+constexpr int kThreads = 512;         // 8 waves
+constexpr int kNW = kThreads / 64;
+constexpr int kGWords = 16384;        // G's upper triangle ends at 126 * 129 + 127
+constexpr int kPrmBytes = 2 * 64 * 16;
+constexpr int kXchBytes = 2 * 2 * (kNW - 1) * 64 * 8;
+constexpr int kLdsBytes = kGWords * 4 + kPrmBytes + kXchBytes;  // 80 KiB: two blocks per CU
+constexpr int kGeneric = 2016 - 64;   // off-diagonal blocks not needed for the next round's rotations
+constexpr int kPerLane = (kGeneric + kThreads - 1) / kThreads;
+static_assert(kLdsBytes == 80 * 1024, "two workgroups per CU");
+static_assert(kPerLane == 4, "generic block slots per lane");
 
-__device__ __forceinline__ int tournament_player(int pos, int round) {
-    return pos == 0 ? 0 : 1 + (pos - 1 + round) % 127;
+// Block (P, Q) holds the next round's pair iff Q == P + 2, or it is (0, 1) or (62, 63).
+constexpr bool next_pair_block(int P, int Q) {
+    return Q == P + 2 || (P == 0 && Q == 1) || (P == 62 && Q == 63);
+}
+
+struct BlockTable {
+    uint16_t pq[kGeneric];  // P | Q << 8, row-major over P < Q
+};
+
+constexpr BlockTable make_block_table() {
+    BlockTable t{};
+    int n = 0;
+    for (int P = 0; P < 64; ++P)
+        for (int Q = P + 1; Q < 64; ++Q)
+            if (!next_pair_block(P, Q)) t.pq[n++] = static_cast<uint16_t>(P | (Q << 8));
+    return t;
+}
+
+__constant__ BlockTable kBlocks = make_block_table();
+
+// Matrix index at position `pos` in round k (0 <= k < 127).
+__device__ __forceinline__ int index_at(int pos, int k) {
+    if (pos == 0) return 0;
+    const unsigned u = static_cast<unsigned>(pos - 1 + k);
+    return static_cast<int>(min(u, u - 127u)) + 1;
 }
 
 __device__ __forceinline__ int gidx(int a, int b) {
-    return a < b ? a * kGP + b : b * kGP + a;
+    return static_cast<int>(__umul24(static_cast<unsigned>(min(a, b)), kGP)) + max(a, b);
 }
 
-constexpr int kThreads = 1024;  // 16 waves
-constexpr int kNW = kThreads / 64;
+struct Rot {
+    float c, s, na, nb;
+    bool rot;
+};
 
-// Rotate eigenvector rows p, q for the pairs first, first + stride, ... (< 64) of
-// one round.  All loads of the batch are issued before any store, so the wave
-// keeps up to 2 * NP LDS requests in flight instead of one dependent chain.
-template <int NP>
-__device__ __forceinline__ void rotate_vectors(float *V, const float *rc, const float *rs,
-                                               const int *rp, const int *rq, int first,
-                                               int stride, int lane) {
-    float c[NP], sn[NP];
-    int p[NP], q[NP];
-    bool act[NP];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        const int P = first + i * stride;
-        act[i] = P < 64;
-        const int Pc = act[i] ? P : 0;
-        c[i] = rc[Pc];
-        sn[i] = rs[Pc];
-        p[i] = rp[Pc];
-        q[i] = rq[Pc];
-        act[i] = act[i] && sn[i] != 0.f;  // uniform over the wave
+// Rotation annihilating g of the 2 x 2 block [a g; g b] (identity below tolerance).
+__device__ __forceinline__ Rot jacobi_rotation(float a, float b, float g, float tol) {
+    Rot r{1.f, 0.f, a, b, false};
+    if (g != 0.f && g * g > tol * tol * fabsf(a * b)) {
+        // Any (c, s) with c^2 + s^2 = 1 to working precision keeps the transform
+        // orthogonal, so 1-ulp reciprocals are enough here.
+        const float zeta = 0.5f * (b - a) * __builtin_amdgcn_rcpf(g);
+        const float az = fabsf(zeta);
+        const float t = az > 1e18f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
+                                   : copysignf(__builtin_amdgcn_rcpf(az + sqrtf(1.f + zeta * zeta)), zeta);
+        r.c = __builtin_amdgcn_rsqf(1.f + t * t);
+        r.s = r.c * t;
+        r.na = a - t * g;
+        r.nb = b + t * g;
+        r.rot = true;
     }
-    float2 a[NP], b[NP];
-    float2 *V2 = reinterpret_cast<float2 *>(V);
-#pragma unroll
-    for (int i = 0; i < NP; ++i)
-        if (act[i]) {
-            a[i] = V2[p[i] * (kD / 2) + lane];
-            b[i] = V2[q[i] * (kD / 2) + lane];
-        }
-#pragma unroll
-    for (int i = 0; i < NP; ++i)
-        if (act[i]) {
-            V2[p[i] * (kD / 2) + lane] = make_float2(c[i] * a[i].x - sn[i] * b[i].x, c[i] * a[i].y - sn[i] * b[i].y);
-            V2[q[i] * (kD / 2) + lane] = make_float2(sn[i] * a[i].x + c[i] * b[i].x, sn[i] * a[i].y + c[i] * b[i].y);
-        }
+    return r;
 }
 
-__global__ __launch_bounds__(kThreads) void jacobi_kernel(const float *__restrict__ gpart, int splits,
-                                                          float *__restrict__ vt_out,
-                                                          int32_t *__restrict__ sweeps_out,
-                                                          int max_sweeps, float tol) {
+__global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__restrict__ gpart, int splits,
+                                                             float *__restrict__ vt_out,
+                                                             int32_t *__restrict__ sweeps_out,
+                                                             int max_sweeps, float tol) {
     extern __shared__ __align__(16) float smem[];
-    float *G = smem;            // 128 x 129
-    float *V = smem + kD * kGP; // 128 x 128, row i = eigenvector i
-    __shared__ float rc[2][64], rs[2][64];
-    __shared__ int rp[2][64], rq[2][64];
-    __shared__ int any_rot;
+    float *G = smem;
+    int *flags = reinterpret_cast<int *>(smem);  // at diagonal slots 0 and 130 (unused by G)
+    float4 *prm = reinterpret_cast<float4 *>(smem + kGWords);                 // [2][64] (c, s, na, nb)
+    float2 *xch = reinterpret_cast<float2 *>(smem + kGWords + kPrmBytes / 4);  // [2][2][7][64]
 
     const int blk = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const float *src = gpart + static_cast<int64_t>(blk) * splits * kD * kD;
     for (int e = tid; e < kD * kD; e += kThreads) {
-        float s = 0.f;
-        for (int p = 0; p < splits; ++p) s += src[static_cast<int64_t>(p) * kD * kD + e];
         const int i = e >> 7, j = e & 127;
-        G[i * kGP + j] = s;
-        V[e] = (i == j) ? 1.f : 0.f;
+        if (i < j) {
+            float s = 0.f;
+            for (int p = 0; p < splits; ++p) s += src[static_cast<int64_t>(p) * kD * kD + e];
+            G[i * kGP + j] = s;
+        }
     }
-    if (tid == 0) any_rot = 0;
+    if (tid == 0) {
+        flags[0] = 0;
+        flags[130] = 0;
+    }
+    __syncthreads();
+
+    // Round 0 of sweep 0: pair P = (P, 127 - P).
+    if (wave == kNW - 1) {
+        const int x = lane, y = 127 - lane;
+        float a = 0.f, b = 0.f;
+        for (int p = 0; p < splits; ++p) {
+            a += src[static_cast<int64_t>(p) * kD * kD + x * kD + x];
+            b += src[static_cast<int64_t>(p) * kD * kD + y * kD + y];
+        }
+        const float g = G[x * kGP + y];
+        const Rot r = jacobi_rotation(a, b, g, tol);
+        prm[lane] = make_float4(r.c, r.s, r.na, r.nb);
+        if (r.rot) {
+            G[x * kGP + y] = 0.f;
+            flags[0] = 1;
+        }
+    }
+
+    // Eigenvector rows of this wave's slots: F = first rows, S = second rows
+    // (components 2 lane, 2 lane + 1); initially slot P holds indices P, 127 - P.
+    float2 F[8], S[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int P = 8 * wave + j, c0 = 2 * lane;
+        F[j] = make_float2(c0 == P ? 1.f : 0.f, c0 + 1 == P ? 1.f : 0.f);
+        S[j] = make_float2(c0 == 127 - P ? 1.f : 0.f, c0 + 1 == 127 - P ? 1.f : 0.f);
+    }
+    // Generic blocks of this lane: table entries tid, tid + 512, ...
+    int bq[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const int i = tid + kThreads * j;
+        bq[j] = i < kGeneric ? kBlocks.pq[i] : -1;
+    }
+    // The next-pair block of this lane (wave 7 only): lane = next round's pair P'.
+    const int Pn = lane;
+    const int Pa = Pn == 0 ? 0 : (Pn == 63 ? 62 : Pn - 1);
+    const int Pb = Pn == 0 ? 1 : (Pn == 63 ? 63 : Pn + 1);
+    const int sel = Pn == 0 ? 0 : (Pn == 63 ? 3 : 2);  // element (p1 p2) / (q1 q2) / (q1 p2)
     __syncthreads();
 
     int used = -max_sweeps;
+    int gk = 0;  // rounds done so far (parity selects the buffers)
     for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-        for (int k = 0; k < 127; ++k) {
-            const int buf = k & 1;
-            if (wave == 0) {
-                // Phase A: the 64 rotations of this round (one pair per lane).
-                const int P = lane;
-                const int p = tournament_player(P, k), q = tournament_player(127 - P, k);
-                const int pq = gidx(p, q);
-                const float a = G[p * kGP + p], b = G[q * kGP + q], g = G[pq];
-                float c = 1.f, s = 0.f;
-                if (fabsf(g) > tol * sqrtf(fabsf(a) * fabsf(b))) {
-                    // Any (c, s) with c^2 + s^2 = 1 to working precision keeps the
-                    // transform orthogonal, so 1-ulp reciprocals are enough here.
-                    const float zeta = 0.5f * (b - a) * __builtin_amdgcn_rcpf(g);
-                    const float az = fabsf(zeta);
-                    const float t = az > 1e18f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
-                                               : copysignf(__builtin_amdgcn_rcpf(az + sqrtf(1.f + zeta * zeta)), zeta);
-                    c = __builtin_amdgcn_rsqf(1.f + t * t);
-                    s = c * t;
-                    G[p * kGP + p] = a - t * g;
-                    G[q * kGP + q] = b + t * g;
-                    G[pq] = 0.f;
-                    any_rot = 1;
+        for (int kr = 0; kr < 127; ++kr, ++gk) {
+            // Opaque copy of the round: recomputing the indices each round keeps
+            // them out of per-index induction registers.
+            int k = kr;
+            asm volatile("" : "+s"(k));
+            const int cb = gk & 1;
+            const float4 *pc = prm + cb * 64;
+
+            // ---- eigenvector rows: rotate, shift along the ring, send the ends
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float2 cs = *reinterpret_cast<const float2 *>(pc + 8 * wave + j);
+                if (cs.y != 0.f) {  // uniform over the wave
+                    const float2 f = F[j], s = S[j];
+                    F[j] = make_float2(cs.x * f.x - cs.y * s.x, cs.x * f.y - cs.y * s.y);
+                    S[j] = make_float2(cs.y * f.x + cs.x * s.x, cs.y * f.y + cs.x * s.y);
                 }
-                rc[buf][P] = c;
-                rs[buf][P] = s;
-                rp[buf][P] = p;
-                rq[buf][P] = q;
-            } else if (k > 0) {
-                // Meanwhile waves 1..15 apply the previous round to the eigenvectors.
-                rotate_vectors<5>(V, rc[buf ^ 1], rs[buf ^ 1], rp[buf ^ 1], rq[buf ^ 1], wave - 1,
-                                  kNW - 1, lane);
             }
+            // Round k + 1's position i holds round k's position i + 1 (127 -> 1 wraps
+            // to 1 -> 127): first rows move down one slot, second rows up one slot.
+            float2 *xo = xch + cb * 2 * (kNW - 1) * 64;
+            if (wave > 0) xo[(wave - 1) * 64 + lane] = F[0];
+            if (wave < kNW - 1) xo[((kNW - 1) + wave) * 64 + lane] = S[7];
+            {
+                const float2 f1 = F[1], s7 = S[7];
+#pragma unroll
+                for (int j = 0; j < 7; ++j)
+                    if (j > 0 || wave > 0) F[j] = F[j + 1];  // index 0 never moves
+                if (wave == kNW - 1) F[7] = s7;
+#pragma unroll
+                for (int j = 7; j >= 1; --j) S[j] = S[j - 1];
+                if (wave == 0) S[0] = f1;
+            }
+
+            // ---- next round's rotations (wave 7): rotate block (Pa, Pb), then the
+            // pair of round k + 1 formed by one of its elements
+            const bool last_round = (k == 126);
+            if (wave == kNW - 1) {
+                const float4 A = pc[Pa], B = pc[Pb];
+                const int p1 = index_at(Pa, k), q1 = index_at(127 - Pa, k);
+                const int p2 = index_at(Pb, k), q2 = index_at(127 - Pb, k);
+                const int sa[4] = {gidx(p1, p2), gidx(p1, q2), gidx(q1, p2), gidx(q1, q2)};
+                const int asel = sel == 0 ? sa[0] : (sel == 2 ? sa[2] : sa[3]);
+                const bool sact = A.y != 0.f || B.y != 0.f;
+                float h[4];
+                if (sact) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[e] = G[sa[e]];
+                    const float r11 = A.x * h[0] - A.y * h[2], r12 = A.x * h[1] - A.y * h[3];
+                    const float r21 = A.y * h[0] + A.x * h[2], r22 = A.y * h[1] + A.x * h[3];
+                    h[0] = B.x * r11 - B.y * r12;
+                    h[1] = B.y * r11 + B.x * r12;
+                    h[2] = B.x * r21 - B.y * r22;
+                    h[3] = B.y * r21 + B.x * r22;
+                } else {
+                    const float v = G[asel];
+                    h[0] = h[2] = h[3] = v;
+                    h[1] = 0.f;
+                }
+                const float gn = sel == 0 ? h[0] : (sel == 2 ? h[2] : h[3]);
+                // new diagonal entries of the pair's first and second index
+                const float an = Pn == 0 ? A.z : (Pn == 63 ? B.w : B.z);
+                const float bn = Pn == 0 ? B.z : A.w;
+                const Rot r = jacobi_rotation(an, bn, gn, tol);
+                prm[(cb ^ 1) * 64 + Pn] = make_float4(r.c, r.s, r.na, r.nb);
+                const float gw = r.rot ? 0.f : gn;
+                if (sel == 0) h[0] = gw;
+                else if (sel == 2) h[2] = gw;
+                else h[3] = gw;
+                if (sact) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) G[sa[e]] = h[e];
+                } else if (r.rot) {
+                    G[asel] = 0.f;
+                }
+                if (r.rot) flags[((sweep + (last_round ? 1 : 0)) & 1) * 130] = 1;
+            }
+
+
+            // ---- generic off-diagonal blocks, two at a time: loads first, then stores
+#pragma unroll
+            for (int j0 = 0; j0 < kPerLane; j0 += 2) {
+                int ad[2][4];
+                float gv[2][4];
+                float2 c1[2], c2[2];
+                bool act[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int code = bq[j0 + i];
+                    act[i] = code >= 0;
+                    const int P = act[i] ? (code & 0xff) : 0, Q = act[i] ? (code >> 8) : 1;
+                    c1[i] = *reinterpret_cast<const float2 *>(pc + P);
+                    c2[i] = *reinterpret_cast<const float2 *>(pc + Q);
+                    act[i] = act[i] && (c1[i].y != 0.f || c2[i].y != 0.f);
+                    const int p1 = index_at(P, k), q1 = index_at(127 - P, k);
+                    const int p2 = index_at(Q, k), q2 = index_at(127 - Q, k);
+                    ad[i][0] = gidx(p1, p2);
+                    ad[i][1] = gidx(p1, q2);
+                    ad[i][2] = gidx(q1, p2);
+                    ad[i][3] = gidx(q1, q2);
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    if (act[i]) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) gv[i][e] = G[ad[i][e]];
+                    }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    if (act[i]) {
+                        // rows of pair P, then columns of pair Q
+                        const float s1 = c1[i].y, k1 = c1[i].x, s2 = c2[i].y, k2 = c2[i].x;
+                        const float h11 = k1 * gv[i][0] - s1 * gv[i][2], h12 = k1 * gv[i][1] - s1 * gv[i][3];
+                        const float h21 = s1 * gv[i][0] + k1 * gv[i][2], h22 = s1 * gv[i][1] + k1 * gv[i][3];
+                        G[ad[i][0]] = k2 * h11 - s2 * h12;
+                        G[ad[i][1]] = s2 * h11 + k2 * h12;
+                        G[ad[i][2]] = k2 * h21 - s2 * h22;
+                        G[ad[i][3]] = s2 * h21 + k2 * h22;
+                    }
+            }
+            if (k == 1 && tid == 0) flags[((sweep + 1) & 1) * 130] = 0;
             __syncthreads();
 
-            // Phase B: off-diagonal 2 x 2 blocks (P < Q).  Wave-row wr pairs block-row
-            // wr (63 - wr blocks) with block-row 62 - wr (wr + 1 blocks): 64 lanes.
-            // Each wave owns wave-rows wave and wave + 16, loaded as one batch.
-            int P[2], Q[2];
-            bool act[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int wr = wave + kNW * i;
-                act[i] = true;
-                if (wr < 31) {
-                    if (lane < 63 - wr) {
-                        P[i] = wr;
-                        Q[i] = wr + 1 + lane;
-                    } else {
-                        P[i] = 62 - wr;
-                        Q[i] = lane;
-                    }
-                } else {
-                    act[i] = lane < 32;
-                    P[i] = 31;
-                    Q[i] = 32 + (lane & 31);
-                }
-            }
-            float c1[2], s1[2], c2[2], s2[2];
-            int i11[2], i12[2], i21[2], i22[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                c1[i] = rc[buf][P[i]];
-                s1[i] = rs[buf][P[i]];
-                c2[i] = rc[buf][Q[i]];
-                s2[i] = rs[buf][Q[i]];
-                const int p1 = rp[buf][P[i]], q1 = rq[buf][P[i]];
-                const int p2 = rp[buf][Q[i]], q2 = rq[buf][Q[i]];
-                i11[i] = gidx(p1, p2);
-                i12[i] = gidx(p1, q2);
-                i21[i] = gidx(q1, p2);
-                i22[i] = gidx(q1, q2);
-                act[i] = act[i] && !(s1[i] == 0.f && s2[i] == 0.f);
-            }
-            float g11[2], g12[2], g21[2], g22[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                if (act[i]) {
-                    g11[i] = G[i11[i]];
-                    g12[i] = G[i12[i]];
-                    g21[i] = G[i21[i]];
-                    g22[i] = G[i22[i]];
-                }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                if (act[i]) {
-                    // rows of pair P, then columns of pair Q
-                    const float h11 = c1[i] * g11[i] - s1[i] * g21[i], h12 = c1[i] * g12[i] - s1[i] * g22[i];
-                    const float h21 = s1[i] * g11[i] + c1[i] * g21[i], h22 = s1[i] * g12[i] + c1[i] * g22[i];
-                    G[i11[i]] = c2[i] * h11 - s2[i] * h12;
-                    G[i12[i]] = s2[i] * h11 + c2[i] * h12;
-                    G[i21[i]] = c2[i] * h21 - s2[i] * h22;
-                    G[i22[i]] = s2[i] * h21 + c2[i] * h22;
-                }
-            __syncthreads();
+            // ---- receive the rows that crossed a wave boundary
+            const float2 *xi = xch + cb * 2 * (kNW - 1) * 64;
+            if (wave < kNW - 1) F[7] = xi[wave * 64 + lane];
+            if (wave > 0) S[0] = xi[((kNW - 1) + wave - 1) * 64 + lane];
         }
-        // The last round (126, buffer 0) still has to reach the eigenvectors.
-        rotate_vectors<4>(V, rc[0], rs[0], rp[0], rq[0], wave, kNW, lane);
-        __syncthreads();
-        const int rot = any_rot;
-        __syncthreads();
-        if (tid == 0) any_rot = 0;
+        const int rot = flags[(sweep & 1) * 130];
         if (!rot) {
             used = sweep + 1;
             break;
         }
     }
 
-    float *dst = vt_out + static_cast<int64_t>(blk) * kD * kD;
-    for (int e = tid; e < kD * kD / 4; e += kThreads)
-        reinterpret_cast<float4 *>(dst)[e] = reinterpret_cast<const float4 *>(V)[e];
+    // 127 rounds per sweep: slot P again holds indices P and 127 - P.
+    float2 *dst = reinterpret_cast<float2 *>(vt_out + static_cast<int64_t>(blk) * kD * kD);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int P = 8 * wave + j;
+        dst[P * 64 + lane] = F[j];
+        dst[(127 - P) * 64 + lane] = S[j];
+    }
     if (tid == 0 && sweeps_out) sweeps_out[blk] = used;
 }
 
@@ -220,12 +330,10 @@ __global__ __launch_bounds__(kThreads) void jacobi_kernel(const float *__restric
 hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt, int32_t *sweeps,
                          int max_sweeps, float tol, hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
-    const size_t lds = sizeof(float) * (kD * kGP + kD * kD);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(jacobi_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), lds, st,
+    hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), kLdsBytes, st,
                        gpart, splits, vt, sweeps, max_sweeps, tol);
     return hipGetLastError();
 }
