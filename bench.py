@@ -47,7 +47,126 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--decode-only-steps", type=int, default=20,
                     help="extra decode-only passes after the timed steps (reported separately)")
+    ap.add_argument("--ingest-stats", metavar="CSV",
+                    help="rocprofv3 kernel_stats.csv -> profiles/kernel_stats_<workload>.txt (no GPU)")
+    ap.add_argument("--ingest-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 counter_collection.csv of the bench (FETCH_SIZE, WRITE_SIZE) and of "
+                         "--calibrate-copy -> profiles/<kernel>_traffic.json (no GPU)")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --ingest-*: the command(s) that produced the CSV files")
     return ap.parse_args()
+
+
+# kernel -> the sources that define it (the traffic records are tied to their hash)
+KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "jacobi": ["jacobi.hip"],
+                  "refine": ["refine.hip", "common.hpp"], "alloc": ["alloc.hip"],
+                  "project": ["project.hip", "common.hpp"], "reconstruct": ["reconstruct.hip", "common.hpp"],
+                  "decode_blocks": ["decode.hip", "common.hpp"], "decode_tail": ["decode.hip", "common.hpp"],
+                  "decode_combine": ["decode.hip", "common.hpp"]}
+
+
+def kernel_key(name):
+    """libmilo kernel name (as rocprofv3 prints it) -> bench kernel key."""
+    for frag, key in (("gram_kernel", "gram"), ("jacobi_kernel", "jacobi"), ("refine_kernel", "refine"),
+                      ("alloc_kernel", "alloc"), ("project_kernel", "project"),
+                      ("reconstruct_kernel", "reconstruct"), ("decode_combine_kernel", "decode_combine")):
+        if frag in name:
+            return key
+    if "decode_partial_kernel" in name:
+        return "decode_tail" if "true>" in name else "decode_blocks"
+    return None
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def workload_slug(cfg):
+    return (f"{cfg.layers}L_b{cfg.batch}_kv{cfg.n_kv_heads}_q{cfg.n_q_heads}_"
+            f"{cfg.attended_blocks}x{cfg.block_len}")
+
+
+def ingest_stats(args):
+    from synthetic import CONFIGS
+    cfg = CONFIGS[args.config]
+    rows = _read_csv(args.ingest_stats)
+    lines = [f"# rocprofv3 kernel statistics: {cfg.workload}", ""]
+    for c in args.command:
+        lines.append(f"command: {c}")
+    lines += ["", f"{'kernel':16s} {'calls':>7s} {'avg_us':>12s} {'total_ms':>11s} {'share':>7s}  name"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        key = kernel_key(r["Name"]) or "-"
+        lines.append(f"{key:16s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:12.2f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:11.2f} {float(r['Percentage']):6.2f}%  {r['Name'][:110]}")
+    out = os.path.join(ROOT, "profiles", f"kernel_stats_{workload_slug(cfg)}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
+def _per_dispatch(rows, counter):
+    """{dispatch id: (kernel name, value)} for one counter (summed over its instances)."""
+    acc = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        d = r["Dispatch_Id"]
+        name, v = acc.get(d, (r["Kernel_Name"], 0.0))
+        acc[d] = (name, v + float(r["Counter_Value"]))
+    return acc
+
+
+def ingest_traffic(args):
+    from synthetic import CONFIGS
+    cfg = CONFIGS[args.config]
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.ingest_traffic
+    copy_bytes = 1 << 30
+
+    def copy_factor(path, counter):
+        d = _per_dispatch(_read_csv(path), counter)
+        vals = [v * 1024 for n, v in d.values() if "bitwise_not" in n.lower()]
+        if not vals:
+            vals = [v * 1024 for n, v in list(d.values())[-3:]]
+        vals.sort()
+        return vals[len(vals) // 2] / copy_bytes
+
+    f_fetch = copy_factor(cfetch_csv, "FETCH_SIZE")
+    f_write = copy_factor(cwrite_csv, "WRITE_SIZE")
+    per = {}
+    for path, counter, fac, slot in ((fetch_csv, "FETCH_SIZE", f_fetch, 0), (write_csv, "WRITE_SIZE", f_write, 1)):
+        for name, v in _per_dispatch(_read_csv(path), counter).values():
+            key = kernel_key(name)
+            if key is None:
+                continue
+            rec = per.setdefault(key, [[], []])
+            rec[slot].append(v * 1024 / fac)
+    lines = [f"# HBM traffic per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE): {cfg.workload}", "",
+             f"calibration: a plain {copy_bytes} B device copy reads {f_fetch:.4f} x and writes "
+             f"{f_write:.4f} x its size by these counters; values below are divided by that factor", ""]
+    for c in args.command:
+        lines.append(f"command: {c}")
+    lines += ["", f"{'kernel':16s} {'dispatches':>10s} {'fetch_MB':>12s} {'write_MB':>12s} {'total_MB':>12s}"]
+    for key, (fv, wv) in sorted(per.items()):
+        if not fv or not wv:
+            continue
+        fb, wb = sum(fv) / len(fv), sum(wv) / len(wv)
+        h = hashlib.sha256()
+        for n in KERNEL_SOURCES[key]:
+            with open(os.path.join(ROOT, "block_wise_rank_amd", "csrc", n), "rb") as f:
+                h.update(f.read())
+        rec = {"kernel": key, "workload": cfg.workload, "source_hash": h.hexdigest()[:16],
+               "bytes_per_launch": fb + wb, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+               "dispatches": len(fv), "copy_calibration": {"fetch": f_fetch, "write": f_write},
+               "commands": args.command}
+        with open(os.path.join(ROOT, "profiles", f"{key}_traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        lines.append(f"{key:16s} {len(fv):10d} {fb / 1e6:12.2f} {wb / 1e6:12.2f} {(fb + wb) / 1e6:12.2f}")
+    out = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_slug(cfg)}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
 
 
 def log(msg):
@@ -64,7 +183,9 @@ def calibrate_copy():
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     for _ in range(3):
-        b.copy_(a)
+        # an elementwise kernel that reads and writes n bytes (a plain copy_ may
+        # go to a DMA engine, which the counters do not see)
+        torch.bitwise_not(a, out=b)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
 
@@ -94,6 +215,12 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return 0
+    if args.ingest_stats:
+        ingest_stats(args)
+        return 0
+    if args.ingest_traffic:
+        ingest_traffic(args)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -261,10 +388,7 @@ def main():
         "decode_tail": (tail_bytes_all, "GB/s", "hbm", PEAK_HBM_GBS),
         "decode_combine": (L * cfg.batch * Hq * d * 4, "GB/s", "hbm", PEAK_HBM_GBS),
     }
-    hashes = {"gram": ["gram.hip", "common.hpp"], "jacobi": ["jacobi.hip"], "refine": ["refine.hip", "common.hpp"],
-              "alloc": ["alloc.hip"], "project": ["project.hip", "common.hpp"],
-              "decode_blocks": ["decode.hip", "common.hpp"], "decode_tail": ["decode.hip", "common.hpp"],
-              "decode_combine": ["decode.hip"]}
+    hashes = KERNEL_SOURCES
     rooflines = {}
     for name, (launches, tot_ms) in prof.items():
         if name not in work:
@@ -274,7 +398,7 @@ def main():
         avg_s = tot_ms / launches / 1e3
         achieved = per_launch / avg_s / (1e9 if unit == "GB/s" else 1e12)
         src = source_hash(*hashes[name])
-        traffic = load_traffic(name, src) if bound == "hbm" else None
+        traffic = load_traffic(name, src)
         rooflines[name] = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                            "frac": round(achieved / peak, 4), "traffic": traffic,
                            "launches_per_step": launches / args.steps,
