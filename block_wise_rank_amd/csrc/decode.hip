@@ -9,26 +9,38 @@
 // review of arXiv 2609.29913, Summary; FAQ); keys were compressed before RoPE
 // (ai4snews digest, Figure 1 caption), so RoPE is applied to rebuilt keys.
 //
-// Work split (flash-decoding style): one workgroup per (sequence, KV head,
-// selected block, token split); the partial (max, sum, unnormalised output)
-// triples are merged by decode_combine_kernel with log-sum-exp weights.  The
-// uncompressed recent tail runs through the same code with identity factors
-// (keys and values read directly, token-major).
+// Work split (flash-decoding style): one workgroup of 8 waves per (sequence,
+// KV head, selected block, token split); wave w takes the 32-token tiles
+// w, w + 8, ... of the split, so the 8 waves read neighbouring stretches of
+// every factor row at once.  The partial (max, sum, unnormalised output)
+// triples of the splits are merged by decode_combine_kernel with log-sum-exp
+// weights.  The uncompressed recent tail runs through the same code with the
+// keys and values read directly (token-major) and B_v = I.
 //
 // RoPE: logit_t = (R_{pq} q) . (R_{p0+t} k_t) = (R_{pq-p0} q) . (R_t k_t) for a
-// 32-token tile starting at position p0.  Each tile's rotated queries are
-// precomputed per workgroup (angles reduced in fp64), and R_t for t < 32 is a
-// per-lane register table, so per token only the key rotation by R_t remains.
+// tile starting at position p0.  A table of (cos, sin)((pq - p0) theta_j) per
+// tile (angles reduced in fp64) rotates the queries, which stay in registers,
+// at the start of each tile; a 32 x 64 table of (cos, sin)(t theta_j) rotates
+// the rebuilt keys.
 //
-// MFMA usage (bf16 in, fp32 accumulate; fp32 factors are split into two bf16
-// terms, three products):
-//   K^T tile   v_mfma_f32_32x32x16_bf16, M = head dim j, N = token, K = rank;
-//              B_k fragments live in LDS, A_k^T (rank-major in the arena) is
-//              gathered 8 ranks x 1 token per lane straight from memory;
-//   logits     32x32x16, M = query head (G <= 16 rows used), N = token,
-//              K = head dim, in a k-order that matches the K^T accumulator;
-//   P A_v      v_mfma_f32_16x16x32_bf16, M = query head, N = rank, K = token,
-//              A_v^T read as 16-byte rows of 8 consecutive tokens.
+// MFMA usage: v_mfma_f32_16x16x32_bf16 throughout (bf16 in, fp32 accumulate;
+// fp32 factors are split into two bf16 terms, three products).  Lane l = 16 c
+// + n of a wave holds, in every accumulator, row 4 c + i (i < 4) of column n.
+//   K^T tile  M = head dim, N = token, K = rank: B_k^T fragments were built in
+//             LDS once per workgroup; A_k^T (rank-major in the arena) is staged
+//             per wave in LDS (XOR-swizzled 16-byte chunks) and read back
+//             8 ranks x 1 token per lane.
+//   logits^T  M = token, N = query head, K = head dim.  The K^T accumulators
+//             feed the A operand in place: k-slot e < 4 of k-step kk is head
+//             dim 16 kk + 4 c + e, slot e >= 4 is dim 64 + 16 kk + 4 c + e - 4,
+//             which also keeps each RoPE pair (j, j + 64) inside one lane.
+//   u^T       M = rank, N = query head, K = token: the probabilities feed the
+//             B operand in place (k-slot e < 4 is token 4 c + e, e >= 4 is
+//             token 16 + 4 c + e - 4) and A_v^T rows are read as two 8-byte
+//             pieces in the same token order.
+// Every lane owns one query head (its column n) in the logits, the softmax
+// state and u, so rescaling needs no communication; the tile maximum is
+// reduced over the four lane groups with two shuffles.
 #include <math.h>
 
 #include "common.hpp"
@@ -38,65 +50,55 @@ namespace milo {
 namespace {
 
 constexpr int kTile = 32;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxLds = 160 * 1024;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr float kLog2e = 1.4426950408889634f;
-
-struct LdsLayout {
-    int bk, qf, scratch, pt, alpha, kst, total;
-};
+constexpr int kUP = 132;   // pitch (floats) of per-head u rows in the merge
+constexpr int kBVP = 260;  // pitch (bytes) of staged B_v rows: rows 8 apart on distinct banks
+constexpr int kTVP = 264;  // pitch (bytes) of staged tail V rows (32 tokens x 128 dims)
 
 __host__ __device__ inline int align16(int v) { return (v + 15) & ~15; }
 
-// Staging pitch (bytes) of one 32-token rank row of an A_k tile: the row plus 8
-// bytes, so rows 8 apart (the two lane halves of a transposed read) fall on
-// disjoint LDS banks.  fp32 factors bypass the staging buffer.
-__host__ __device__ inline int kst_pitch(int esize) { return esize == 4 ? 0 : 32 * esize + 8; }
+// A_k staging pitch per rank row of a 32-token tile (bytes); fp32 factors are
+// read straight from memory.
+__host__ __device__ inline int stage_pitch(int f) { return f == kBF16 ? 72 : (f == kI8 ? 40 : 0); }
 
-// All offsets in bytes.  scratch holds the prologue tables (RoPE table, the
-// queries, theta) and is reused for the end-of-split merge.
-__host__ __device__ inline LdsLayout lds_layout(int ns, int n_tiles, int G, bool tail, int esize) {
+struct LdsLayout {
+    int theta, qs, bk, rope, base, stage, loop_end;    // loop phase
+    int uw, mlw, uacc, bv, merge_end;                   // merge phase (aliases the loop phase)
+    int total;
+};
+
+__host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool tail) {
     LdsLayout L;
-    const int bk = tail ? 0 : ns * 4 * 8 * 64 * 8 * 2;
-    const int qf = ns * n_tiles * 8 * 2 * G * 8 * 2;
-    const int prologue = 32 * 64 * 8 + G * 128 * 4 + 64 * 8;
-    const int merge = kWaves * G * 128 * 4 + 2 * kWaves * 16 * 4;
-    const int scratch = prologue > merge ? prologue : merge;
-    const int kst = tail ? 0 : kWaves * 128 * kst_pitch(esize);
-    L.bk = 0;
-    L.qf = align16(L.bk + bk);
-    L.scratch = align16(L.qf + qf);
-    L.pt = align16(L.scratch + scratch);
-    L.alpha = align16(L.pt + kWaves * ns * 16 * 32 * 2);
-    L.kst = align16(L.alpha + 128 * 4);  // alpha per wave (64 floats), or 128 B-row scales
-    L.total = align16(L.kst + kst);
+    L.theta = 0;
+    L.qs = align16(L.theta + 64 * 8);
+    L.bk = align16(L.qs + 16 * kD * 4);
+    L.rope = align16(L.bk + (tail ? 0 : ns * 8 * 4 * 64 * 16));
+    L.base = align16(L.rope + 32 * 64 * 8);
+    L.stage = align16(L.base + n_tiles * 64 * 8);
+    int stage = 0;
+    if (!tail) stage = kWaves * 128 * stage_pitch(f);
+    else if (f == kBF16) stage = kWaves * 32 * kTVP;
+    // the B_k rows for the fragment build are staged in this area too
+    const int bk_rows = (tail || f == kF32) ? 0 : 128 * kD * (f == kBF16 ? 2 : 1);
+    if (stage < bk_rows) stage = bk_rows;
+    L.loop_end = align16(L.stage + stage);
+    L.uw = 0;
+    L.mlw = align16(L.uw + kWaves * 16 * kUP * 4);
+    L.uacc = align16(L.mlw + kWaves * 16 * 2 * 4);
+    L.bv = align16(L.uacc + 16 * kUP * 4);
+    L.merge_end = align16(L.bv + (tail ? 0 : ns * 128 * kBVP));
+    L.total = L.loop_end > L.merge_end ? L.loop_end : L.merge_end;
     return L;
 }
 
-// Order this wave's LDS writes before its later LDS reads of other lanes' data
-// (LDS executes a wave's operations in order; the fences stop the compiler from
-// reordering across this point).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Copy nbytes (a multiple of 16) from global memory to LDS in rounds of 4 KiB
-// per 4 chunks per thread: each round issues all its loads before any store.
-__device__ __forceinline__ void copy_to_lds(uint8_t *dst, const uint8_t *src, int nbytes) {
-    const int n = nbytes >> 4;
-    for (int base = 0; base < n; base += 1024) {
-        uint4 v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            v[i] = reinterpret_cast<const uint4 *>(src)[min(base + static_cast<int>(threadIdx.x) + 256 * i, n - 1)];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = base + threadIdx.x + 256 * i;
-            if (c < n) reinterpret_cast<uint4 *>(dst)[c] = v[i];
-        }
-    }
 }
 
 template <int F>
@@ -113,28 +115,53 @@ __device__ __forceinline__ void to_terms(float v, uint16_t (&t)[2]) {
     if constexpr (NS == 2) t[1] = f32_to_bf16_bits(v - bf16_bits_to_f32(t[0]));
 }
 
+// 8 floats -> NS bf16 fragments
+template <int NS>
+__device__ __forceinline__ void frag_terms(const float (&v)[8], u16x8_t (&f)[NS]) {
+    if constexpr (NS == 1) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const uint32_t w = f32x2_to_bf16x2_bits(v[e], v[e + 1]);
+            f[0][e] = static_cast<uint16_t>(w & 0xffff);
+            f[0][e + 1] = static_cast<uint16_t>(w >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint16_t t[2];
+            to_terms<NS>(v[e], t);
+            f[0][e] = t[0];
+            f[1][e] = t[1];
+        }
+    }
+}
+
+// Byte offset of (rank row r, token t) in a bf16 A_k staging tile: 16-byte
+// chunks of a row are swapped in pairs for rows with bit 4 set, so the four
+// lane groups (rows 8 apart) of a transposed read hit four distinct 32-byte
+// bank windows.
+__device__ __forceinline__ int stage_off_bf16(int r, int t) {
+    return r * 72 + ((((t >> 3) ^ (2 * ((r >> 4) & 1)))) << 4) + ((t & 7) << 1);
+}
+__device__ __forceinline__ int stage_off_i8(int r, int t) {
+    return r * 40 + ((((t >> 4) ^ ((r >> 4) & 1))) << 4) + (t & 15);
+}
+
 template <int F, bool TAIL>
-__global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
     constexpr int NS = (F == kF32) ? 2 : 1;
+    constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);
     extern __shared__ __align__(16) uint8_t lds[];
     const int G = p.group;
     const int n_tiles = p.split_len / kTile;
-    const int tiles_per_wave = n_tiles / kWaves;
-    constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);
-    const LdsLayout L = lds_layout(NS, n_tiles, G, TAIL, ES);
-    uint16_t *bk = reinterpret_cast<uint16_t *>(lds + L.bk);
-    uint16_t *qf = reinterpret_cast<uint16_t *>(lds + L.qf);
-    float2 *rope_tab = reinterpret_cast<float2 *>(lds + L.scratch);
-    float *qs = reinterpret_cast<float *>(lds + L.scratch + 32 * 64 * 8);
-    double *theta = reinterpret_cast<double *>(lds + L.scratch + 32 * 64 * 8 + G * 128 * 4);
-    float *us = reinterpret_cast<float *>(lds + L.scratch);            // merge (aliases the tables)
-    float *wm = us + kWaves * G * 128;
-    float *wl = wm + kWaves * 16;
-    uint16_t *pt = reinterpret_cast<uint16_t *>(lds + L.pt);
-    float *alpha_s = reinterpret_cast<float *>(lds + L.alpha);
+    const LdsLayout L = lds_layout(F, NS, n_tiles, TAIL);
+    double *theta = reinterpret_cast<double *>(lds + L.theta);
+    const float2 *rope = reinterpret_cast<const float2 *>(lds + L.rope);
+    const float2 *basetab = reinterpret_cast<const float2 *>(lds + L.base);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tl_ = lane & 31, hf_ = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c4 = lane >> 4, ln = lane & 15;
     const int s = blockIdx.z, h = blockIdx.y, sp = blockIdx.x;
     const int Hkv = p.n_kv_heads;
     const int T = p.block_len;
@@ -167,6 +194,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
         const int len = min(p.tail_len[s], p.tail_cap);  // never read past the tail buffer
         valid = min(max(len - tok0, 0), p.split_len);
         pos0 = p.tail_pos0[s] + tok0;
+        rk = rv = kD;
     }
     const int64_t pidx = static_cast<int64_t>(s * Hkv + h) * p.n_splits + split_index;
     float *ml = p.part_ml + pidx * G * 2;
@@ -178,458 +206,553 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeParams 
         }
         return;
     }
+    const int tiles_valid = (valid + kTile - 1) / kTile;
+    const int KS = (rk + 31) >> 5;    // 32-rank k-steps of the key rebuild
+    const int NTU = (rv + 15) >> 4;   // 16-rank row tiles of u
 
-    // ---- prologue: theta, queries, in-tile RoPE table, rotated query fragments
-    if (tid < 64) theta[tid] = exp2(-(2.0 * tid / 128.0) * log2(p.rope_base));
-    {
-        // the G query heads of this KV head are consecutive rows of q
-        const int64_t q0 = (static_cast<int64_t>(s) * p.n_q_heads + h * G) * kD;
-        float qv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = min(tid + 256 * i, G * kD - 1);
-            qv[i] = p.q_type == kF32 ? static_cast<const float *>(p.q)[q0 + e]
-                                     : bf16_bits_to_f32(static_cast<const uint16_t *>(p.q)[q0 + e]);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (tid + 256 * i < G * kD) qs[tid + 256 * i] = qv[i];
-    }
-    __syncthreads();
-    for (int e = tid; e < 32 * 64; e += 256) {
-        const int t = e >> 6, j = e & 63;
-        float sn, cs;  // angle < 32 rad: fp32 sincos is accurate after its own reduction
-        sincosf(static_cast<float>(static_cast<double>(t) * theta[j]), &sn, &cs);
-        rope_tab[e] = make_float2(cs, sn);
-    }
-    const int qf_term = n_tiles * 8 * 2 * G * 8;  // elements per bf16 term
-    const int64_t qpos = p.q_pos[s];
-    for (int e = tid; e < n_tiles * 64; e += 256) {
-        const int tl = e >> 6, j = e & 63;
-        double a = static_cast<double>(qpos - (pos0 + tl * kTile)) * theta[j];
-        a -= kTwoPi * rint(a / kTwoPi);  // exact enough in fp64 for positions < 2^40
-        float snf, csf;
-        sincosf(static_cast<float>(a), &snf, &csf);
-        const double sn = snf, cs = csf;
-#pragma unroll 1
-        for (int g = 0; g < G; ++g) {
-            const double x1 = qs[g * kD + j], x2 = qs[g * kD + j + 64];
-            const float y[2] = {static_cast<float>(x1 * cs - x2 * sn),
-                                static_cast<float>(x1 * sn + x2 * cs)};
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int jj = j + 64 * half;
-                const int jt = jj >> 5, rem = jj & 31;
-                const int kk = 2 * jt + (rem >> 4);
-                const int hf = (rem >> 2) & 1;
-                const int slot = 4 * ((rem >> 3) & 1) + (rem & 3);
-                const int idx = (((tl * 8 + kk) * 2 + hf) * G + g) * 8 + slot;
-                uint16_t tv[2];
-                to_terms<NS>(y[half], tv);
-#pragma unroll
-                for (int st = 0; st < NS; ++st) qf[st * qf_term + idx] = tv[st];
-            }
-        }
-    }
-    int KS = 0;
+    // ---- prologue: RoPE tables; B_k^T fragments
+    if (tid < 64) theta[tid] = exp2(-(static_cast<double>(tid) / 64.0) * log2(p.rope_base));
     const uint8_t *Ak = nullptr, *Av = nullptr, *Bv = nullptr;
     if constexpr (!TAIL) {
-        KS = (rk + 15) >> 4;
         Ak = p.k_arena + p.k_aoff[fid];
         Av = p.v_arena + p.v_aoff[fid];
         Bv = p.v_arena + p.v_boff[fid];
         const uint8_t *Bk = p.k_arena + p.k_boff[fid];
+        uint16_t *bk = reinterpret_cast<uint16_t *>(lds + L.bk);
         if constexpr (F != kF32) {
-            // rows of B_k (and their INT8 scales) -> LDS, then into MFMA fragment order
-            uint8_t *tmp = lds + L.kst;
-            float *bsc = reinterpret_cast<float *>(lds + L.alpha);  // free until the main loop
-            copy_to_lds(tmp, Bk, rk * kD * ES);
+            // B_k rows -> LDS (the A_k staging area is free until the main loop)
+            uint8_t *tmp = lds + L.stage;
+            const int n16 = (rk * kD * ES) >> 4;
+            for (int i = tid; i < n16; i += kThreads)
+                reinterpret_cast<uint4 *>(tmp)[i] = reinterpret_cast<const uint4 *>(Bk)[i];
+            float *bsc = reinterpret_cast<float *>(lds + L.rope);  // free until the tables are built
             if constexpr (F == kI8)
                 if (tid < rk) bsc[tid] = p.k_bscale[static_cast<int64_t>(fid) * kD + tid];
             __syncthreads();
-            for (int q = tid; q < 4 * 8 * 64; q += 256) {
-                const int ln = q & 63, ks = (q >> 6) & 7, jt = q >> 9;
+            for (int q = tid; q < 8 * 4 * 64; q += kThreads) {
+                const int l2 = q & 63, ks = (q >> 6) & 3, mt = q >> 8;
                 if (ks >= KS) continue;
-                const int j = 32 * jt + (ln & 31), r0 = 16 * ks + 8 * (ln >> 5);
-                u16x8_t ch;
+                const int j = 16 * mt + (l2 & 15), r0 = 32 * ks + 8 * (l2 >> 4);
+                float v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int r = r0 + e;
-                    float v = 0.f;
+                    v[e] = 0.f;
                     if (r < rk) {
-                        if constexpr (F == kBF16)
-                            v = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(tmp)[r * kD + j]);
-                        else
-                            v = static_cast<float>(reinterpret_cast<const int8_t *>(tmp)[r * kD + j]) * bsc[r];
+                        if constexpr (F == kBF16) v[e] = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(tmp)[r * kD + j]);
+                        else v[e] = static_cast<float>(reinterpret_cast<const int8_t *>(tmp)[r * kD + j]) * bsc[r];
                     }
-                    ch[e] = f32_to_bf16_bits(v);
                 }
-                *reinterpret_cast<u16x8_t *>(bk + q * 8) = ch;
+                u16x8_t f[1];
+                frag_terms<1>(v, f);
+                *reinterpret_cast<u16x8_t *>(bk + q * 8) = f[0];
             }
-            __syncthreads();  // the staging area is reused for A_k tiles
+            __syncthreads();  // tmp and bsc are reused below
         } else {
-            for (int e = tid; e < KS * 16 * kD; e += 256) {
-                const int r = e >> 7, j = e & 127;
-                const float v = r < rk ? load_elem<F>(Bk, e) : 0.f;
-                const int jt = j >> 5, ln = (j & 31) + 32 * ((r >> 3) & 1);
-                const int idx = ((jt * 8 + (r >> 4)) * 64 + ln) * 8 + (r & 7);
-                uint16_t tv[2];
-                to_terms<NS>(v, tv);
+            for (int q = tid; q < 8 * 4 * 64; q += kThreads) {
+                const int l2 = q & 63, ks = (q >> 6) & 3, mt = q >> 8;
+                if (ks >= KS) continue;
+                const int j = 16 * mt + (l2 & 15), r0 = 32 * ks + 8 * (l2 >> 4);
+                float v[8];
 #pragma unroll
-                for (int st = 0; st < NS; ++st) bk[st * (4 * 8 * 64 * 8) + idx] = tv[st];
+                for (int e = 0; e < 8; ++e) {
+                    const int r = r0 + e;
+                    v[e] = r < rk ? load_elem<F>(Bk, static_cast<int64_t>(r) * kD + j) : 0.f;
+                }
+                u16x8_t f[NS];
+                frag_terms<NS>(v, f);
+#pragma unroll
+                for (int st = 0; st < NS; ++st) *reinterpret_cast<u16x8_t *>(bk + (st * 2048 + q) * 8) = f[st];
             }
         }
     }
-    // P^T staging rows g >= G stay zero for the whole split.
-    for (int e = tid; e < kWaves * NS * 16 * 32; e += 256) pt[e] = 0;
-    __syncthreads();
-    float rc[2][16], rsn[2][16];
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int j = 32 * jt + 8 * (i >> 2) + 4 * hf_ + (i & 3);
-            const float2 v = rope_tab[tl_ * 64 + j];
-            rc[jt][i] = v.x;
-            rsn[jt][i] = v.y;
+    __syncthreads();  // theta
+    {
+        float2 *rw = reinterpret_cast<float2 *>(lds + L.rope);
+        for (int e = tid; e < 32 * 64; e += kThreads) {
+            const int t = e >> 6, j = e & 63;
+            float sn, cs;  // angle < 32 rad: fp32 sincos is accurate after its own reduction
+            sincosf(static_cast<float>(static_cast<double>(t) * theta[j]), &sn, &cs);
+            rw[e] = make_float2(cs, sn);
         }
-
-    // ---- main loop over this wave's tiles (contiguous tiles per wave)
-    float m_run[8], l_run[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        m_run[i] = -INFINITY;
-        l_run[i] = 0.f;
+        float2 *bw = reinterpret_cast<float2 *>(lds + L.base);
+        const int64_t qpos = p.q_pos[s];
+        for (int e = tid; e < tiles_valid * 64; e += kThreads) {
+            const int tl = e >> 6, j = e & 63;
+            double a = static_cast<double>(qpos - (pos0 + tl * kTile)) * theta[j];
+            a -= kTwoPi * rint(a / kTwoPi);  // exact enough in fp64 for positions < 2^40
+            float sn, cs;
+            sincosf(static_cast<float>(a), &sn, &cs);
+            bw[e] = make_float2(cs, sn);
+        }
     }
-    f32x4_t u[8];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) u[n] = zero4();
-    const int NTU = TAIL ? 8 : (rv + 15) >> 4;
-    const float lscale = p.softmax_scale * kLog2e;
-    uint16_t *my_pt = pt + wave * NS * 16 * 32;
-    const int tile0 = wave * tiles_per_wave;
 
-    // A_k tiles (bf16 / int8): 16-byte coalesced loads of LPR lanes per rank row,
-    // staged rank-major in this wave's LDS buffer and read back transposed
-    // (8 ranks of one token per lane).  Rows past rk reuse row rk - 1 (finite
-    // values; their B_k fragment rows are zero).
-    constexpr int RB = 32 * ES;                 // bytes of one rank row of a tile
-    constexpr int LPR = RB / 16 > 0 ? RB / 16 : 1;
-    constexpr int RPI = 64 / LPR;               // rank rows per load instruction
-    constexpr int NI = 128 / RPI;               // load instructions for 128 ranks
-    constexpr int KP = (F == kF32) ? 16 : 32 * ES + 8;  // staging pitch (bytes)
-    uint8_t *kst = lds + L.kst + wave * 128 * KP;
-    const int rk_pad = KS * 16;
-    uint4 kraw[F == kF32 ? 1 : NI];
-    auto load_k = [&](int tl) {
+    // ---- the G query heads of this KV head -> LDS (fp32; rows >= G are zero).
+    // Lane (c, n) owns head n: column n of every accumulator.
+    const bool head_ok = ln < G;
+    {
+        float *qw = reinterpret_cast<float *>(lds + L.qs);
+        const int64_t q0 = (static_cast<int64_t>(s) * p.n_q_heads + h * G) * kD;
+        for (int e = tid; e < 16 * kD; e += kThreads) {
+            float v = 0.f;
+            if (e < G * kD)
+                v = p.q_type == kF32 ? static_cast<const float *>(p.q)[q0 + e]
+                                     : bf16_bits_to_f32(static_cast<const uint16_t *>(p.q)[q0 + e]);
+            qw[e] = v;
+        }
+    }
+    const float *qrow = reinterpret_cast<const float *>(lds + L.qs) + ln * kD;
+
+    // ---- per-wave A_k staging (bf16 / int8 blocks) and tail V staging
+    uint8_t *stg = lds + L.stage;
+    if constexpr (!TAIL) stg += wave * 128 * stage_pitch(F);
+    else stg += wave * 32 * kTVP;
+    const uint16_t *bkf = reinterpret_cast<const uint16_t *>(lds + L.bk);
+
+    // A_k tile loads: 16-byte pieces, LPR lanes per rank row; rows past rk
+    // repeat row rk - 1 (finite; their B_k fragment rows are zero).
+    constexpr int RB = kTile * ES;                  // bytes of one rank row of a tile
+    constexpr int LPR = RB / 16 > 0 ? RB / 16 : 1;  // lanes per row
+    constexpr int RPI = 64 / LPR;                   // rows per load instruction
+    constexpr int NI = 128 / RPI;                   // load instructions for 128 ranks
+    uint4 kraw[(F == kF32 || TAIL) ? 1 : NI];
+    const int rk_pad = KS * 32;
+    // Every load instruction is issued (rows clamped to rk - 1; identical
+    // addresses coalesce), which keeps the registers free of partial paths.
+    auto load_k = [&](int tile) {
         if constexpr (F != kF32 && !TAIL) {
-            const int tt0 = tok0 + tl * kTile;
+            if (rk > 0) {
+                const int tt0 = tok0 + tile * kTile;
 #pragma unroll
-            for (int c = 0; c < NI; ++c)
-                if (c * RPI < rk_pad) {
-                    const int r = min(c * RPI + lane / LPR, rk - 1);
-                    kraw[c] = *reinterpret_cast<const uint4 *>(
-                        Ak + (static_cast<int64_t>(r) * T + tt0) * ES + (lane % LPR) * 16);
+                for (int ci = 0; ci < NI; ++ci) {
+                    // 32-bit offsets from the block's (uniform) base keep each address in one register
+                    const int r = min(ci * RPI + lane / LPR, rk - 1);
+                    const uint32_t off = static_cast<uint32_t>((r * T + tt0) * ES + (lane % LPR) * 16);
+                    kraw[ci] = *reinterpret_cast<const uint4 *>(Ak + off);
                 }
+            }
         }
     };
-    // A_v fragments for P A_v (16x16x32 B operand): rank column 16 n + lane % 16,
-    // tokens tb .. tb + 7.  bf16: one 16-byte load; int8: 8 bytes; fp32: 32 bytes.
-    u16x8_t vraw[F == kF32 ? 1 : 8];
-    auto load_v = [&](int tl) {
-        if constexpr (F != kF32 && !TAIL) {
-            const int tb = tok0 + tl * kTile + 8 * (lane >> 4);
-#pragma unroll
-            for (int n = 0; n < 8; ++n)
-                if (n < NTU) {
-                    const int col = min(16 * n + (lane & 15), rv - 1);
-                    if constexpr (F == kBF16) {
-                        vraw[n] = *reinterpret_cast<const u16x8_t *>(
-                            reinterpret_cast<const uint16_t *>(Av) + static_cast<int64_t>(col) * T + tb);
-                    } else {
-                        const uint2 w = *reinterpret_cast<const uint2 *>(Av + static_cast<int64_t>(col) * T + tb);
-                        vraw[n][0] = static_cast<uint16_t>(w.x & 0xffff);
-                        vraw[n][1] = static_cast<uint16_t>(w.x >> 16);
-                        vraw[n][2] = static_cast<uint16_t>(w.y & 0xffff);
-                        vraw[n][3] = static_cast<uint16_t>(w.y >> 16);
-                    }
-                }
-        }
-    };
-    // Pipeline: the staging buffer holds tile it while its keys are rebuilt; the
-    // A_k registers already hold tile it + 1 and A_v registers tile it.  Each
-    // wait therefore covers loads issued a whole tile earlier.
     auto stage_k = [&]() {
         if constexpr (F != kF32 && !TAIL) {
 #pragma unroll
-            for (int c = 0; c < NI; ++c)
-                if (c * RPI < rk_pad) {
-                    uint8_t *dst = kst + (c * RPI + lane / LPR) * KP + (lane % LPR) * 16;
-                    reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[c].x, kraw[c].y);
-                    reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[c].z, kraw[c].w);
+            for (int ci = 0; ci < NI; ++ci)
+                if (ci * RPI < rk_pad) {  // uniform
+                    const int r = ci * RPI + lane / LPR;
+                    if constexpr (F == kBF16) {
+                        uint8_t *dst = stg + r * 72 + (((lane % LPR) ^ (2 * ((r >> 4) & 1))) << 4);
+                        reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
+                        reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[ci].z, kraw[ci].w);
+                    } else {
+                        uint8_t *dst = stg + r * 40 + (((lane % LPR) ^ ((r >> 4) & 1)) << 4);
+                        reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
+                        reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[ci].z, kraw[ci].w);
+                    }
                 }
             wave_lds_sync();
         }
     };
-    load_k(tile0);
-    stage_k();
-    load_v(tile0);
-    if (tiles_per_wave > 1) load_k(tile0 + 1);
+    // A_v^T pieces: rank 16 mr + ln, tokens 4 c .. 4 c + 3 and 16 + 4 c .. + 3
+    uint2 vraw[(F == kF32 || TAIL) ? 1 : 8][2];
+    auto load_v = [&](int tile) {
+        if constexpr (F != kF32 && !TAIL) {
+            const int tb = tok0 + tile * kTile + 4 * c4;
+            if (rv > 0) {
+#pragma unroll
+                for (int mr = 0; mr < 8; ++mr) {
+                    const int row = min(16 * mr + ln, rv - 1);
+                    const uint32_t off = static_cast<uint32_t>((row * T + tb) * ES);
+                    if constexpr (F == kBF16) {
+                        vraw[mr][0] = *reinterpret_cast<const uint2 *>(Av + off);
+                        vraw[mr][1] = *reinterpret_cast<const uint2 *>(Av + off + 32);
+                    } else {
+                        vraw[mr][0] = make_uint2(*reinterpret_cast<const uint32_t *>(Av + off), 0u);
+                        vraw[mr][1] = make_uint2(*reinterpret_cast<const uint32_t *>(Av + off + 16), 0u);
+                    }
+                }
+            }
+        }
+    };
 
-    for (int it = 0; it < tiles_per_wave; ++it) {
-        const int tl = tile0 + it;
-        const int tloc = tl * kTile;           // offset within the split
-        const int t = tok0 + tloc + tl_;       // this lane's token (block- or tail-local)
-        const bool tok_ok = tloc + tl_ < valid;
+    __syncthreads();  // tables, fragments
 
-        // ---- K^T tile: kacc[jt][i] = k_hat[t][32 jt + 8 (i/4) + 4 hf + i%4]
-        f32x16_t kacc[4];
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t u[8];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) kacc[jt] = zero16();
-        if constexpr (!TAIL) {
-            for (int ks = 0; ks < KS; ++ks) {
-                u16x8_t af[NS];
-                if constexpr (F == kBF16) {
+    for (int mr = 0; mr < 8; ++mr) u[mr] = zero4();
+    const float lscale = p.softmax_scale * kLog2e;
+
+    // Pipeline: the staging buffer holds this tile's A_k^T while its keys are
+    // rebuilt; the next tile's A_k^T is loaded once the rebuild is done (so the
+    // registers are free during it) and staged at the end of the tile; A_v^T
+    // pieces are loaded a whole tile ahead.
+    const int my_tiles = tiles_valid > wave ? (tiles_valid - 1 - wave) / kWaves + 1 : 0;
+    if (my_tiles > 0) {
+        load_k(wave);
+        stage_k();
+        load_v(wave);
+    }
+    for (int it = 0; it < my_tiles; ++it) {
+        const int tile = wave + kWaves * it;
+        const int tt0 = tok0 + tile * kTile;  // first token of the tile (block- or tail-local)
+
+        // ---- rotated query fragments for this tile (dims 16 kk + 4 c + i and + 64)
+        u16x8_t qf[NS][4];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        af[0][e] = *reinterpret_cast<const uint16_t *>(kst + (16 * ks + 8 * hf_ + e) * KP + tl_ * 2);
-                } else if constexpr (F == kI8) {
+        for (int kk = 0; kk < 4; ++kk) {
+            const float4 *bp = reinterpret_cast<const float4 *>(basetab + tile * 64 + 16 * kk + 4 * c4);
+            const float4 b01 = bp[0], b23 = bp[1];
+            const float cs[4] = {b01.x, b01.z, b23.x, b23.z}, sn[4] = {b01.y, b01.w, b23.y, b23.w};
+            const float4 qa = *reinterpret_cast<const float4 *>(qrow + 16 * kk + 4 * c4);
+            const float4 qb = *reinterpret_cast<const float4 *>(qrow + 64 + 16 * kk + 4 * c4);
+            const float q1[4] = {qa.x, qa.y, qa.z, qa.w}, q2[4] = {qb.x, qb.y, qb.z, qb.w};
+            float v[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        af[0][e] = f32_to_bf16_bits(static_cast<float>(
-                            *reinterpret_cast<const int8_t *>(kst + (16 * ks + 8 * hf_ + e) * KP + tl_)));
-                } else {
+            for (int i = 0; i < 4; ++i) {
+                const float x1 = q1[i], x2 = q2[i];
+                v[i] = x1 * cs[i] - x2 * sn[i];
+                v[4 + i] = x1 * sn[i] + x2 * cs[i];
+            }
+            u16x8_t f[NS];
+            frag_terms<NS>(v, f);
+#pragma unroll
+            for (int st = 0; st < NS; ++st) qf[st][kk] = f[st];
+        }
+
+        // ---- per 16-token half nt: K^T (acc[mt][i] = k_hat[token 16 nt + ln][dim 16 mt + 4 c + i]),
+        // RoPE by the in-tile offset, logits^T S[nt][i] = logit(token 16 nt + 4 c + i, head ln)
+        f32x4_t S[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int t = 16 * nt + ln;
+            f32x4_t acc[8];
+            if constexpr (!TAIL) {
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
+                for (int ks = 0; ks < KS; ++ks) {
+                    u16x8_t bfr[NS];
+                    if constexpr (F == kBF16) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            bfr[0][e] = *reinterpret_cast<const uint16_t *>(stg + stage_off_bf16(32 * ks + 8 * c4 + e, t));
+                    } else if constexpr (F == kI8) {
+                        float v[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            v[e] = static_cast<float>(*reinterpret_cast<const int8_t *>(stg + stage_off_i8(32 * ks + 8 * c4 + e, t)));
+                        frag_terms<1>(v, reinterpret_cast<u16x8_t(&)[1]>(bfr));
+                    } else {
+                        float v[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int r = 32 * ks + 8 * c4 + e;
+                            v[e] = r < rk ? load_elem<F>(Ak, static_cast<int64_t>(r) * T + tt0 + t) : 0.f;
+                        }
+                        frag_terms<NS>(v, bfr);
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+                        for (int sa = 0; sa < NS; ++sa) {
+                            const u16x8_t a = *reinterpret_cast<const u16x8_t *>(bkf + ((sa * 2048) + (mt * 4 + ks) * 64 + lane) * 8);
+#pragma unroll
+                            for (int sb = 0; sb < NS; ++sb)
+                                if (sa + sb < NS) acc[mt] = mfma16x16x32(a, bfr[sb], acc[mt]);
+                        }
+                    }
+                }
+            } else {
+                // tail keys straight from memory (rows past the valid length repeat the last one)
+                const int64_t rowb = (static_cast<int64_t>(s) * Hkv + h) * p.tail_cap;
+                const int tk = min(tt0 + t, tok0 + valid - 1);
+                const uint8_t *kp = static_cast<const uint8_t *>(p.tail_k) + (rowb + tk) * kD * ES;
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) {
+                    const int j0 = 16 * mt + 4 * c4;
+                    if constexpr (F == kF32) {
+                        const float4 w = *reinterpret_cast<const float4 *>(kp + j0 * 4);
+                        acc[mt][0] = w.x; acc[mt][1] = w.y; acc[mt][2] = w.z; acc[mt][3] = w.w;
+                    } else {
+                        const uint2 w = *reinterpret_cast<const uint2 *>(kp + j0 * 2);
+                        acc[mt][0] = bf16_bits_to_f32(w.x & 0xffff);
+                        acc[mt][1] = bf16_bits_to_f32(w.x >> 16);
+                        acc[mt][2] = bf16_bits_to_f32(w.y & 0xffff);
+                        acc[mt][3] = bf16_bits_to_f32(w.y >> 16);
+                    }
+                }
+            }
+            S[nt] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const float4 *rp = reinterpret_cast<const float4 *>(rope + t * 64 + 16 * kk + 4 * c4);
+                const float4 r01 = rp[0], r23 = rp[1];
+                const float cs[4] = {r01.x, r01.z, r23.x, r23.z}, sn[4] = {r01.y, r01.w, r23.y, r23.w};
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float k1 = acc[kk][i], k2 = acc[kk + 4][i];
+                    v[i] = k1 * cs[i] - k2 * sn[i];
+                    v[4 + i] = k1 * sn[i] + k2 * cs[i];
+                }
+                u16x8_t kf[NS];
+                frag_terms<NS>(v, kf);
+#pragma unroll
+                for (int sa = 0; sa < NS; ++sa)
+#pragma unroll
+                    for (int sb = 0; sb < NS; ++sb)
+                        if (sa + sb < NS) S[nt] = mfma16x16x32(kf[sa], qf[sb][kk], S[nt]);
+            }
+        }
+
+        if (it + 1 < my_tiles) load_k(tile + kWaves);
+
+        // ---- online softmax (log2 domain) for head ln over this tile's 32 tokens
+        float sc[2][4], vs[2][4];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc[nt][i] = lscale;
+                vs[nt][i] = 1.f;
+            }
+        if constexpr (F == kI8 && !TAIL) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int64_t ti = static_cast<int64_t>(fid) * T + tt0 + 16 * nt + 4 * c4;
+                const float4 ka = *reinterpret_cast<const float4 *>(p.k_ascale + ti);
+                const float4 va = *reinterpret_cast<const float4 *>(p.v_ascale + ti);
+                sc[nt][0] *= ka.x; sc[nt][1] *= ka.y; sc[nt][2] *= ka.z; sc[nt][3] *= ka.w;
+                vs[nt][0] = va.x; vs[nt][1] = va.y; vs[nt][2] = va.z; vs[nt][3] = va.w;
+            }
+        }
+        float x[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = tile * kTile + 16 * nt + 4 * c4 + i < valid;
+                x[nt][i] = ok ? S[nt][i] * sc[nt][i] : -INFINITY;
+                tmax = fmaxf(tmax, x[nt][i]);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(m_run, tmax);
+        const bool none = (mn == -INFINITY);
+        const float alpha = none ? 1.f : exp2f(m_run - mn);
+        float pv[8], psum = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pr = none ? 0.f : exp2f(x[nt][i] - mn);
+                psum += pr;
+                pv[4 * nt + i] = pr * vs[nt][i];
+            }
+        l_run = l_run * alpha + psum;
+        m_run = mn;
+
+        // ---- u^T = alpha u^T + A_v^T P^T
+        u16x8_t pf[NS];
+        frag_terms<NS>(pv, pf);
+        if constexpr (!TAIL && F != kF32) {
+#pragma unroll
+            for (int mr = 0; mr < 8; ++mr)
+                if (mr < NTU) {
+                    u[mr] *= alpha;
+                    u16x8_t af;
+                    if constexpr (F == kBF16) {
+                        af[0] = vraw[mr][0].x & 0xffff; af[1] = vraw[mr][0].x >> 16;
+                        af[2] = vraw[mr][0].y & 0xffff; af[3] = vraw[mr][0].y >> 16;
+                        af[4] = vraw[mr][1].x & 0xffff; af[5] = vraw[mr][1].x >> 16;
+                        af[6] = vraw[mr][1].y & 0xffff; af[7] = vraw[mr][1].y >> 16;
+                    } else {
+                        float v[8];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[e] = static_cast<float>(static_cast<int8_t>((vraw[mr][0].x >> (8 * e)) & 0xff));
+                            v[4 + e] = static_cast<float>(static_cast<int8_t>((vraw[mr][1].x >> (8 * e)) & 0xff));
+                        }
+                        u16x8_t f[1];
+                        frag_terms<1>(v, f);
+                        af = f[0];
+                    }
+                    u[mr] = mfma16x16x32(af, pf[0], u[mr]);
+                }
+        } else if constexpr (!TAIL) {
+            // fp32 factors: A_v^T pieces straight from memory, two terms
+#pragma unroll
+            for (int mr = 0; mr < 8; ++mr)
+                if (mr < NTU) {
+                    u[mr] *= alpha;
+                    const int row = min(16 * mr + ln, rv - 1);
                     float v[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int r = 16 * ks + 8 * hf_ + e;
-                        v[e] = load_elem<F>(Ak, static_cast<int64_t>(min(r, rk - 1)) * T + t);
-                        if (r >= rk) v[e] = 0.f;
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = load_elem<F>(Av, static_cast<int64_t>(row) * T + tt0 + 4 * c4 + e);
+                        v[4 + e] = load_elem<F>(Av, static_cast<int64_t>(row) * T + tt0 + 16 + 4 * c4 + e);
                     }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        uint16_t tv[2];
-                        to_terms<NS>(v[e], tv);
-#pragma unroll
-                        for (int st = 0; st < NS; ++st) af[st][e] = tv[st];
-                    }
-                }
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt) {
-#pragma unroll
-                    for (int sa = 0; sa < NS; ++sa) {
-                        const u16x8_t bf = *reinterpret_cast<const u16x8_t *>(
-                            bk + sa * (4 * 8 * 64 * 8) + ((jt * 8 + ks) * 64 + lane) * 8);
-#pragma unroll
-                        for (int sb = 0; sb < NS; ++sb)
-                            if (sa + sb < NS) kacc[jt] = mfma32x32x16(bf, af[sb], kacc[jt]);
-                    }
-                }
-            }
-        } else {
-            const int tc = min(t, tok0 + valid - 1);  // clamped: masked lanes read a valid row
-            const int64_t row = ((static_cast<int64_t>(s) * Hkv + h) * p.tail_cap + tc) * kD;
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int j0 = 32 * jt + 8 * q4 + 4 * hf_;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        kacc[jt][4 * q4 + e] =
-                            load_elem<F>(static_cast<const uint8_t *>(p.tail_k), row + j0 + e);
-                }
-        }
-        // RoPE by the in-tile offset (pairs j, j + 64 sit in kacc[jt], kacc[jt + 2])
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float k1 = kacc[jt][i], k2 = kacc[jt + 2][i];
-                kacc[jt][i] = k1 * rc[jt][i] - k2 * rsn[jt][i];
-                kacc[jt + 2][i] = k1 * rsn[jt][i] + k2 * rc[jt][i];
-            }
-        // logits S[g][t] over 8 k-steps of 16 head dims
-        f32x16_t S = zero16();
-        const bool q_lane = tl_ < G;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int jt = kk >> 1, h2 = kk & 1;
-            u16x8_t kf[NS];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint16_t tv[2];
-                to_terms<NS>(kacc[jt][8 * h2 + e], tv);
-#pragma unroll
-                for (int st = 0; st < NS; ++st) kf[st][e] = tv[st];
-            }
-#pragma unroll
-            for (int sa = 0; sa < NS; ++sa) {
-                u16x8_t qv;
-                if (q_lane)
-                    qv = *reinterpret_cast<const u16x8_t *>(
-                        qf + sa * qf_term + (((tl * 8 + kk) * 2 + hf_) * G + tl_) * 8);
-                else
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) qv[e] = 0;
-#pragma unroll
-                for (int sb = 0; sb < NS; ++sb)
-                    if (sa + sb < NS) S = mfma32x32x16(qv, kf[sb], S);
-            }
-        }
-        // online softmax (log2 domain); S[i] holds head g = 8 (i/4) + 4 hf + i%4, token tl_
-        float tscale = lscale;
-        float vscale = 1.f;
-        if constexpr (F == kI8 && !TAIL) {
-            tscale *= p.k_ascale[static_cast<int64_t>(fid) * T + t];
-            vscale = p.v_ascale[static_cast<int64_t>(fid) * T + t];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int g = 8 * (i >> 2) + 4 * hf_ + (i & 3);
-            const float x = tok_ok ? S[i] * tscale : -INFINITY;
-            const float mt = half_max(x);
-            const float mn = fmaxf(m_run[i], mt);
-            const bool none = (mn == -INFINITY);
-            const float alpha = none ? 1.f : exp2f(m_run[i] - mn);
-            const float pr = none ? 0.f : exp2f(x - mn);
-            l_run[i] = l_run[i] * alpha + half_sum(pr);
-            m_run[i] = mn;
-            if (g < G) {
-                uint16_t tv[2];
-                to_terms<NS>(pr * vscale, tv);
-#pragma unroll
-                for (int st = 0; st < NS; ++st) my_pt[(st * 16 + g) * 32 + tl_] = tv[st];
-                if (tl_ == 0) alpha_s[wave * 16 + g] = alpha;
-            }
-        }
-        wave_lds_sync();
-        // u = u * alpha + P A_v   (u rows: g = 4 (lane/16) + i, columns: rank 16 n + lane%16)
-        {
-            const int g0 = 4 * (lane >> 4);
-            float al[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = (g0 + i < G) ? alpha_s[wave * 16 + g0 + i] : 1.f;
-            u16x8_t pf[NS];
-#pragma unroll
-            for (int st = 0; st < NS; ++st)
-                pf[st] = *reinterpret_cast<const u16x8_t *>(my_pt + (st * 16 + (lane & 15)) * 32 + 8 * (lane >> 4));
-            const int tb = tok0 + tloc + 8 * (lane >> 4);  // first of this lane's 8 tokens
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                if (n < NTU) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) u[n][i] *= al[i];
-                    const int col = 16 * n + (lane & 15);
-                    u16x8_t vf[NS];
-                    if constexpr (!TAIL && F == kBF16) {
-                        vf[0] = vraw[n];
-                        if (col >= rv)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) vf[0][e] = 0;
-                    } else if constexpr (!TAIL && F == kI8) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int8_t c8 = static_cast<int8_t>((vraw[n][e >> 1] >> (8 * (e & 1))) & 0xff);
-                            vf[0][e] = col < rv ? f32_to_bf16_bits(static_cast<float>(c8)) : 0;
-                        }
-                    } else if constexpr (!TAIL) {
-                        const int cc = min(col, rv - 1);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            uint16_t tv[2];
-                            const float v = col < rv ? load_elem<F>(Av, static_cast<int64_t>(cc) * T + tb + e) : 0.f;
-                            to_terms<NS>(v, tv);
-#pragma unroll
-                            for (int st = 0; st < NS; ++st) vf[st][e] = tv[st];
-                        }
-                    } else {
-                        const int64_t rowb = (static_cast<int64_t>(s) * Hkv + h) * p.tail_cap;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const bool ok = tb + e - tok0 < valid;
-                            const int te = ok ? tb + e : tok0;
-                            float v = load_elem<F>(static_cast<const uint8_t *>(p.tail_v), (rowb + te) * kD + col);
-                            if (!ok) v = 0.f;
-                            uint16_t tv[2];
-                            to_terms<NS>(v, tv);
-#pragma unroll
-                            for (int st = 0; st < NS; ++st) vf[st][e] = tv[st];
-                        }
-                    }
+                    u16x8_t af[NS];
+                    frag_terms<NS>(v, af);
 #pragma unroll
                     for (int sa = 0; sa < NS; ++sa)
 #pragma unroll
                         for (int sb = 0; sb < NS; ++sb)
-                            if (sa + sb < NS) u[n] = mfma16x16x32(pf[sa], vf[sb], u[n]);
+                            if (sa + sb < NS) u[mr] = mfma16x16x32(af[sa], pf[sb], u[mr]);
                 }
+        } else {
+            // tail values: dims play the role of ranks (B_v = I)
+            const int64_t rowb = (static_cast<int64_t>(s) * Hkv + h) * p.tail_cap;
+            const int tlast = tok0 + valid - 1;
+            if constexpr (F == kBF16) {
+                // stage the 32 x 128 tile token-major, read 8 tokens of one dim per lane
+#pragma unroll
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    const int ch = lane + 64 * q4;  // 16-byte chunk: token ch / 16, dims 8 (ch % 16) ..
+                    const int t = min(tt0 + (ch >> 4), tlast);
+                    const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(p.tail_v) +
+                                                                     ((rowb + t) * kD + 8 * (ch & 15)) * 2);
+                    uint8_t *dst = stg + (ch >> 4) * kTVP + (ch & 15) * 16;
+                    reinterpret_cast<uint2 *>(dst)[0] = make_uint2(w.x, w.y);
+                    reinterpret_cast<uint2 *>(dst)[1] = make_uint2(w.z, w.w);
+                }
+                wave_lds_sync();
             }
+#pragma unroll
+            for (int mr = 0; mr < 8; ++mr) {
+                u[mr] *= alpha;
+                const int dim = 16 * mr + ln;
+                u16x8_t af[NS];
+                if constexpr (F == kBF16) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int tt = (e < 4) ? 4 * c4 + e : 16 + 4 * c4 + e - 4;
+                        af[0][e] = *reinterpret_cast<const uint16_t *>(stg + tt * kTVP + dim * 2);
+                    }
+                } else {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int tt = (e < 4) ? 4 * c4 + e : 16 + 4 * c4 + e - 4;
+                        const int t = min(tt0 + tt, tlast);
+                        v[e] = reinterpret_cast<const float *>(p.tail_v)[(rowb + t) * kD + dim];
+                    }
+                    frag_terms<NS>(v, af);
+                }
+#pragma unroll
+                for (int sa = 0; sa < NS; ++sa)
+#pragma unroll
+                    for (int sb = 0; sb < NS; ++sb)
+                        if (sa + sb < NS) u[mr] = mfma16x16x32(af[sa], pf[sb], u[mr]);
+            }
+            if constexpr (F == kBF16) wave_lds_sync();  // staging reused by the next tile
         }
-        if (it + 1 < tiles_per_wave) {
+
+        if (it + 1 < my_tiles) {
+            load_v(tile + kWaves);
             wave_lds_sync();  // this tile's staged keys have been read
             stage_k();
-            load_v(tl + 1);
-            if (it + 2 < tiles_per_wave) load_k(tl + 2);
         }
     }
 
-    // ---- merge the four waves and apply B_v
-    __syncthreads();  // the scratch region (RoPE table, queries) is dead from here on
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int g = 8 * (i >> 2) + 4 * hf_ + (i & 3);
-        if (g < G && tl_ == 0) {
-            wm[wave * 16 + g] = m_run[i];
-            wl[wave * 16 + g] = l_run[i];
-        }
+    // ---- merge the waves (log-sum-exp) and apply B_v
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    __syncthreads();  // loop-phase LDS is dead from here on
+    float *uw = reinterpret_cast<float *>(lds + L.uw);
+    float *mlw = reinterpret_cast<float *>(lds + L.mlw);
+    float *uacc = reinterpret_cast<float *>(lds + L.uacc);
+    if (c4 == 0) {
+        mlw[(wave * 16 + ln) * 2] = m_run;
+        mlw[(wave * 16 + ln) * 2 + 1] = l_run;
     }
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
+    for (int mr = 0; mr < 8; ++mr)
+        if (mr < NTU)
+            *reinterpret_cast<f32x4_t *>(uw + (wave * 16 + ln) * kUP + 16 * mr + 4 * c4) = u[mr];
+    const int KSV = (rv + 31) >> 5;  // 32-rank k-steps of u B_v
+    const int rpad = TAIL ? kD : KSV * 32;
+    if constexpr (!TAIL) {
+        // B_v rows (INT8 dequantised; fp32 as two bf16 terms) -> LDS, zero rows up to rpad
+        uint8_t *bv = lds + L.bv;
+        for (int e = tid; e < rpad * 64; e += kThreads) {
+            const int r = e >> 6, w2 = e & 63;  // dims 2 w2, 2 w2 + 1
+            float v0 = 0.f, v1 = 0.f;
+            if (r < rv) {
+                v0 = load_elem<F>(Bv, static_cast<int64_t>(r) * kD + 2 * w2);
+                v1 = load_elem<F>(Bv, static_cast<int64_t>(r) * kD + 2 * w2 + 1);
+                if constexpr (F == kI8) {
+                    const float sb = p.v_bscale[static_cast<int64_t>(fid) * kD + r];
+                    v0 *= sb;
+                    v1 *= sb;
+                }
+            }
+            uint16_t t0[2], t1[2];
+            to_terms<NS>(v0, t0);
+            to_terms<NS>(v1, t1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int g = 4 * (lane >> 4) + i;
-            if (n < NTU && g < G) us[(wave * G + g) * kD + 16 * n + (lane & 15)] = u[n][i];
+            for (int st = 0; st < NS; ++st)
+                *reinterpret_cast<uint32_t *>(bv + (st * 128 + r) * kBVP + w2 * 4) =
+                    static_cast<uint32_t>(t0[st]) | (static_cast<uint32_t>(t1[st]) << 16);
         }
-    const uint8_t *bv_src = Bv;
-    if constexpr (!TAIL && F != kF32) {
-        // B_v rows (and INT8 scales) -> LDS; the A_k staging area is free now
-        copy_to_lds(lds + L.kst, Bv, rv * kD * ES);
-        if constexpr (F == kI8)
-            if (tid < rv) reinterpret_cast<float *>(lds + L.alpha)[tid] = p.v_bscale[static_cast<int64_t>(fid) * kD + tid];
-        bv_src = lds + L.kst;
     }
     __syncthreads();
-    for (int e = tid; e < G * kD; e += 256) {
-        const int g = e >> 7, j = e & 127;
+    for (int e = tid; e < 16 * rpad; e += kThreads) {
+        const int g = e / rpad, r = e - g * rpad;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * 16 + g]);
-        float coef[kWaves];
-        float Lsum = 0.f;
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mlw[(w * 16 + g) * 2]);
+        float uvs = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float mw = wm[w * 16 + g];
-            coef[w] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-            Lsum += coef[w] * wl[w * 16 + g];
+            const float mw = mlw[(w * 16 + g) * 2];
+            const float cf = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+            if (cf != 0.f && r < rv) uvs += cf * uw[(w * 16 + g) * kUP + r];
         }
-        float o = 0.f;
-        if constexpr (!TAIL) {
-            for (int r = 0; r < rv; ++r) {
-                float uw = 0.f;
+        uacc[g * kUP + r] = uvs;
+    }
+    if (tid < G) {  // (max, sum) of every head, also when rpad == 0 (rank-0 values)
+        float M = -INFINITY, Ls = 0.f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) uw += coef[w] * us[(w * G + g) * kD + r];
-                float bv = load_elem<F>(bv_src, static_cast<int64_t>(r) * kD + j);
-                if constexpr (F == kI8) bv *= reinterpret_cast<const float *>(lds + L.alpha)[r];
-                o += uw * bv;
-            }
-        } else {
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mlw[(w * 16 + tid) * 2]);
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) o += coef[w] * us[(w * G + g) * kD + j];
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = mlw[(w * 16 + tid) * 2];
+            Ls += (mw == -INFINITY ? 0.f : exp2f(mw - M)) * mlw[(w * 16 + tid) * 2 + 1];
         }
-        po[g * kD + j] = o;
-        if (j == 0) {
-            ml[2 * g] = M;
-            ml[2 * g + 1] = Lsum;
+        ml[2 * tid] = M;
+        ml[2 * tid + 1] = Ls;
+    }
+    __syncthreads();
+    if constexpr (TAIL) {
+        for (int e = tid; e < G * kD; e += kThreads) po[e] = uacc[(e >> 7) * kUP + (e & 127)];
+    } else {
+        // o^T tile of wave w: dims 16 w .. 16 w + 15 = u (16 x rpad) B_v (rpad x 128)
+        const uint8_t *bv = lds + L.bv;
+        f32x4_t o = zero4();
+        for (int ks = 0; ks < KSV; ++ks) {
+            const float4 *up = reinterpret_cast<const float4 *>(uacc + ln * kUP + 32 * ks + 8 * c4);
+            const float4 ua = up[0], ub = up[1];
+            const float v[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+            u16x8_t af[NS], bf[NS];
+            frag_terms<NS>(v, af);
+            const int dim = 16 * wave + ln;
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    bf[st][e] = *reinterpret_cast<const uint16_t *>(bv + (st * 128 + 32 * ks + 8 * c4 + e) * kBVP + dim * 2);
+#pragma unroll
+            for (int sa = 0; sa < NS; ++sa)
+#pragma unroll
+                for (int sb = 0; sb < NS; ++sb)
+                    if (sa + sb < NS) o = mfma16x16x32(af[sa], bf[sb], o);
+        }
+        // o[i]: head 4 c + i, dim 16 w + ln
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int g = 4 * c4 + i;
+            if (g < G) po[g * kD + 16 * wave + ln] = o[i];
         }
     }
 }
@@ -683,25 +806,23 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeParams 
 template <int F, bool TAIL>
 hipError_t launch_partial(const DecodeParams &p, dim3 grid, hipStream_t st) {
     constexpr int NS = (F == kF32) ? 2 : 1;
-    constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);
-    const LdsLayout L = lds_layout(NS, p.split_len / kTile, p.group, TAIL, ES);
+    const LdsLayout L = lds_layout(F, NS, p.split_len / kTile, TAIL);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_partial_kernel<F, TAIL>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_partial_kernel<F, TAIL>), grid, dim3(256), L.total, st, p);
+    hipLaunchKernelGGL((decode_partial_kernel<F, TAIL>), grid, dim3(kThreads), L.total, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int split) {
-    constexpr int kMaxLds = 160 * 1024;
-    const int esz = f_type == kF32 ? 4 : (f_type == kBF16 ? 2 : 1);
+    (void)G;
     const int ns = f_type == kF32 ? 2 : 1;
-    if (lds_layout(ns, split / kTile, G, false, esz).total > kMaxLds) return false;
+    if (lds_layout(f_type, ns, split / kTile, false).total > kMaxLds) return false;
     if (has_tail) {
         const int tns = tail_type == kF32 ? 2 : 1;
-        if (lds_layout(tns, split / kTile, G, true, tail_type == kF32 ? 4 : 2).total > kMaxLds) return false;
+        if (lds_layout(tail_type, tns, split / kTile, true).total > kMaxLds) return false;
     }
     return true;
 }
