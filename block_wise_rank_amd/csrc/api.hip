@@ -418,6 +418,9 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
     if (a->q_dtype != MILO_F32 && a->q_dtype != MILO_BF16) return fail(MILO_E_UNSUPPORTED, "q_dtype must be F32 or BF16");
     if (a->out_dtype != MILO_F32 && a->out_dtype != MILO_BF16) return fail(MILO_E_UNSUPPORTED, "out_dtype must be F32 or BF16");
     if (a->batch > 0 && (!a->q || !a->q_pos || !a->out)) return fail(MILO_E_INVALID, "q, q_pos and out must be set");
+    if (a->batch > 0 && !aligned(a->q, 16)) return fail(MILO_E_INVALID, "q must be 16-byte aligned");
+    if (need_blocks > 0 && (!aligned(k->arena, 16) || !aligned(v->arena, 16)))
+        return fail(MILO_E_INVALID, "factor arenas must be 16-byte aligned");
     if (a->sel_ptr) {
         if (!a->sel_blk && a->sel_max > 0) return fail(MILO_E_INVALID, "sel_blk is NULL");
         if (a->sel_max < 0 || a->sel_max > a->blocks_per_seq)
@@ -497,9 +500,15 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
     const size_t n = static_cast<size_t>(p.batch) * p.n_kv_heads * p.n_splits * G;
     p.part_ml = static_cast<float *>(a->workspace);
     p.part_o = reinterpret_cast<float *>(static_cast<uint8_t *>(a->workspace) + align_up(n * 2 * sizeof(float), 256));
+    uint8_t *tabs = static_cast<uint8_t *>(a->workspace) + milo::decode_workspace_bytes(p) - milo::decode_table_bytes();
+    p.theta = reinterpret_cast<double *>(tabs);
+    p.rope_tab = reinterpret_cast<float2 *>(tabs + 64 * sizeof(double));
+    p.step_tab = p.rope_tab + 32 * 64;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.batch == 0) return ok();
     hipError_t e = hipSuccess;
+    if ((e = timed("decode_tables", s, [&] { return milo::launch_decode_tables(p, s); })) != hipSuccess)
+        return hip_fail(e, "decode table launch");
     if (p.n_sel * p.block_splits > 0 &&
         (e = timed("decode_blocks", s, [&] { return milo::launch_decode_blocks(p, s); })) != hipSuccess)
         return hip_fail(e, "decode launch");

@@ -56,8 +56,11 @@ constexpr int kMaxLds = 160 * 1024;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kUP = 132;   // pitch (floats) of per-head u rows in the merge
-constexpr int kBVP = 260;  // pitch (bytes) of staged B_v rows: rows 8 apart on distinct banks
 constexpr int kTVP = 264;  // pitch (bytes) of staged tail V rows (32 tokens x 128 dims)
+// Row pitches of the in-tile RoPE table (float2) and of the queries (float): 528
+// bytes, so the 16-byte reads of 8 consecutive rows fall on distinct banks.
+constexpr int kRP = 66;
+constexpr int kQP = 132;
 
 __host__ __device__ inline int align16(int v) { return (v + 15) & ~15; }
 
@@ -66,18 +69,18 @@ __host__ __device__ inline int align16(int v) { return (v + 15) & ~15; }
 __host__ __device__ inline int stage_pitch(int f) { return f == kBF16 ? 72 : (f == kI8 ? 40 : 0); }
 
 struct LdsLayout {
-    int theta, qs, bk, rope, base, stage, loop_end;    // loop phase
-    int uw, mlw, uacc, bv, merge_end;                   // merge phase (aliases the loop phase)
+    int ang, qs, bk, rope, base, stage, loop_end;      // loop phase
+    int uw, mlw, uacc, merge_end;                       // merge phase (aliases the loop phase)
     int total;
 };
 
 __host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool tail) {
     LdsLayout L;
-    L.theta = 0;
-    L.qs = align16(L.theta + 64 * 8);
-    L.bk = align16(L.qs + 16 * kD * 4);
+    L.ang = 0;
+    L.qs = align16(L.ang + 64 * 8);
+    L.bk = align16(L.qs + 16 * kQP * 4);
     L.rope = align16(L.bk + (tail ? 0 : ns * 8 * 4 * 64 * 16));
-    L.base = align16(L.rope + 32 * 64 * 8);
+    L.base = align16(L.rope + 32 * kRP * 8);
     L.stage = align16(L.base + n_tiles * 64 * 8);
     int stage = 0;
     if (!tail) stage = kWaves * 128 * stage_pitch(f);
@@ -89,8 +92,7 @@ __host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool
     L.uw = 0;
     L.mlw = align16(L.uw + kWaves * 16 * kUP * 4);
     L.uacc = align16(L.mlw + kWaves * 16 * 2 * 4);
-    L.bv = align16(L.uacc + 16 * kUP * 4);
-    L.merge_end = align16(L.bv + (tail ? 0 : ns * 128 * kBVP));
+    L.merge_end = align16(L.uacc + 16 * kUP * 4);
     L.total = L.loop_end > L.merge_end ? L.loop_end : L.merge_end;
     return L;
 }
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     const int G = p.group;
     const int n_tiles = p.split_len / kTile;
     const LdsLayout L = lds_layout(F, NS, n_tiles, TAIL);
-    double *theta = reinterpret_cast<double *>(lds + L.theta);
+    float2 *ang = reinterpret_cast<float2 *>(lds + L.ang);
     const float2 *rope = reinterpret_cast<const float2 *>(lds + L.rope);
     const float2 *basetab = reinterpret_cast<const float2 *>(lds + L.base);
 
@@ -210,99 +212,13 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     const int KS = (rk + 31) >> 5;    // 32-rank k-steps of the key rebuild
     const int NTU = (rv + 15) >> 4;   // 16-rank row tiles of u
 
-    // ---- prologue: RoPE tables; B_k^T fragments
-    if (tid < 64) theta[tid] = exp2(-(static_cast<double>(tid) / 64.0) * log2(p.rope_base));
-    const uint8_t *Ak = nullptr, *Av = nullptr, *Bv = nullptr;
+    const uint8_t *Ak = nullptr, *Av = nullptr, *Bv = nullptr, *Bk = nullptr;
     if constexpr (!TAIL) {
         Ak = p.k_arena + p.k_aoff[fid];
         Av = p.v_arena + p.v_aoff[fid];
         Bv = p.v_arena + p.v_boff[fid];
-        const uint8_t *Bk = p.k_arena + p.k_boff[fid];
-        uint16_t *bk = reinterpret_cast<uint16_t *>(lds + L.bk);
-        if constexpr (F != kF32) {
-            // B_k rows -> LDS (the A_k staging area is free until the main loop)
-            uint8_t *tmp = lds + L.stage;
-            const int n16 = (rk * kD * ES) >> 4;
-            for (int i = tid; i < n16; i += kThreads)
-                reinterpret_cast<uint4 *>(tmp)[i] = reinterpret_cast<const uint4 *>(Bk)[i];
-            float *bsc = reinterpret_cast<float *>(lds + L.rope);  // free until the tables are built
-            if constexpr (F == kI8)
-                if (tid < rk) bsc[tid] = p.k_bscale[static_cast<int64_t>(fid) * kD + tid];
-            __syncthreads();
-            for (int q = tid; q < 8 * 4 * 64; q += kThreads) {
-                const int l2 = q & 63, ks = (q >> 6) & 3, mt = q >> 8;
-                if (ks >= KS) continue;
-                const int j = 16 * mt + (l2 & 15), r0 = 32 * ks + 8 * (l2 >> 4);
-                float v[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = r0 + e;
-                    v[e] = 0.f;
-                    if (r < rk) {
-                        if constexpr (F == kBF16) v[e] = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(tmp)[r * kD + j]);
-                        else v[e] = static_cast<float>(reinterpret_cast<const int8_t *>(tmp)[r * kD + j]) * bsc[r];
-                    }
-                }
-                u16x8_t f[1];
-                frag_terms<1>(v, f);
-                *reinterpret_cast<u16x8_t *>(bk + q * 8) = f[0];
-            }
-            __syncthreads();  // tmp and bsc are reused below
-        } else {
-            for (int q = tid; q < 8 * 4 * 64; q += kThreads) {
-                const int l2 = q & 63, ks = (q >> 6) & 3, mt = q >> 8;
-                if (ks >= KS) continue;
-                const int j = 16 * mt + (l2 & 15), r0 = 32 * ks + 8 * (l2 >> 4);
-                float v[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = r0 + e;
-                    v[e] = r < rk ? load_elem<F>(Bk, static_cast<int64_t>(r) * kD + j) : 0.f;
-                }
-                u16x8_t f[NS];
-                frag_terms<NS>(v, f);
-#pragma unroll
-                for (int st = 0; st < NS; ++st) *reinterpret_cast<u16x8_t *>(bk + (st * 2048 + q) * 8) = f[st];
-            }
-        }
+        Bk = p.k_arena + p.k_boff[fid];
     }
-    __syncthreads();  // theta
-    {
-        float2 *rw = reinterpret_cast<float2 *>(lds + L.rope);
-        for (int e = tid; e < 32 * 64; e += kThreads) {
-            const int t = e >> 6, j = e & 63;
-            float sn, cs;  // angle < 32 rad: fp32 sincos is accurate after its own reduction
-            sincosf(static_cast<float>(static_cast<double>(t) * theta[j]), &sn, &cs);
-            rw[e] = make_float2(cs, sn);
-        }
-        float2 *bw = reinterpret_cast<float2 *>(lds + L.base);
-        const int64_t qpos = p.q_pos[s];
-        for (int e = tid; e < tiles_valid * 64; e += kThreads) {
-            const int tl = e >> 6, j = e & 63;
-            double a = static_cast<double>(qpos - (pos0 + tl * kTile)) * theta[j];
-            a -= kTwoPi * rint(a / kTwoPi);  // exact enough in fp64 for positions < 2^40
-            float sn, cs;
-            sincosf(static_cast<float>(a), &sn, &cs);
-            bw[e] = make_float2(cs, sn);
-        }
-    }
-
-    // ---- the G query heads of this KV head -> LDS (fp32; rows >= G are zero).
-    // Lane (c, n) owns head n: column n of every accumulator.
-    const bool head_ok = ln < G;
-    {
-        float *qw = reinterpret_cast<float *>(lds + L.qs);
-        const int64_t q0 = (static_cast<int64_t>(s) * p.n_q_heads + h * G) * kD;
-        for (int e = tid; e < 16 * kD; e += kThreads) {
-            float v = 0.f;
-            if (e < G * kD)
-                v = p.q_type == kF32 ? static_cast<const float *>(p.q)[q0 + e]
-                                     : bf16_bits_to_f32(static_cast<const uint16_t *>(p.q)[q0 + e]);
-            qw[e] = v;
-        }
-    }
-    const float *qrow = reinterpret_cast<const float *>(lds + L.qs) + ln * kD;
-
     // ---- per-wave A_k staging (bf16 / int8 blocks) and tail V staging
     uint8_t *stg = lds + L.stage;
     if constexpr (!TAIL) stg += wave * 128 * stage_pitch(F);
@@ -374,7 +290,123 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         }
     };
 
-    __syncthreads();  // tables, fragments
+    // ---- prologue.  Every global load of the prologue (B_k rows, queries, the
+    // RoPE tables, the first tile's factors) is issued before any is used.
+    const int wt0 = wave;  // first tile of this wave
+    const bool has_tile = wt0 < tiles_valid;
+    if (has_tile) {
+        load_k(wt0);
+        load_v(wt0);
+    }
+    constexpr int NBK = (F == kF32 || TAIL) ? 1 : (128 * kD * ES / 16 + kThreads - 1) / kThreads;
+    uint4 bkraw[NBK];
+    const int n16 = (F == kF32 || TAIL) ? 0 : (rk * kD * ES) >> 4;
+    if constexpr (F != kF32 && !TAIL) {
+        // rk = 0: the (discarded) loads read the first bytes of q instead
+        const uint4 *src = reinterpret_cast<const uint4 *>(n16 > 0 ? Bk : static_cast<const uint8_t *>(p.q));
+        const int last = n16 > 0 ? n16 - 1 : 0;
+#pragma unroll
+        for (int i = 0; i < NBK; ++i) bkraw[i] = src[min(tid + kThreads * i, last)];
+    }
+    float bsc_v = 0.f;
+    if constexpr (F == kI8 && !TAIL)
+        if (tid < rk) bsc_v = p.k_bscale[static_cast<int64_t>(fid) * kD + tid];
+    const float4 rope_v = reinterpret_cast<const float4 *>(p.rope_tab)[tid];      // entries 2 tid, 2 tid + 1
+    const float4 rope_w = reinterpret_cast<const float4 *>(p.rope_tab)[tid + kThreads];
+    constexpr int NST = kMaxTiles * 64 / 2 / kThreads;                               // float4 per thread
+    float4 step_v[NST];
+#pragma unroll
+    for (int i = 0; i < NST; ++i) step_v[i] = reinterpret_cast<const float4 *>(p.step_tab)[tid + kThreads * i];
+    float qv[4];
+    {
+        // G query heads: 4 consecutive values per thread (rows >= G are zero)
+        const int64_t q0 = (static_cast<int64_t>(s) * p.n_q_heads + h * G) * kD;
+        const int e0 = 4 * tid;  // < 16 * 128
+        if (e0 < G * kD) {
+            if (p.q_type == kF32) {
+                const float4 w = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.q) + q0 + e0);
+                qv[0] = w.x; qv[1] = w.y; qv[2] = w.z; qv[3] = w.w;
+            } else {
+                const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.q) + q0 + e0);
+                qv[0] = bf16_bits_to_f32(w.x & 0xffff); qv[1] = bf16_bits_to_f32(w.x >> 16);
+                qv[2] = bf16_bits_to_f32(w.y & 0xffff); qv[3] = bf16_bits_to_f32(w.y >> 16);
+            }
+        } else {
+            qv[0] = qv[1] = qv[2] = qv[3] = 0.f;
+        }
+    }
+    if (tid < 64) {
+        // rotation of the queries relative to the split's first token, (pq - p0) theta_j
+        double a = static_cast<double>(p.q_pos[s] - pos0) * p.theta[tid];
+        a -= kTwoPi * rint(a / kTwoPi);  // exact enough in fp64 for positions < 2^40
+        float sn, cs;
+        sincosf(static_cast<float>(a), &sn, &cs);
+        ang[tid] = make_float2(cs, sn);
+    }
+    {
+        float *qw = reinterpret_cast<float *>(lds + L.qs);
+        const int e0 = 4 * tid;
+        *reinterpret_cast<float4 *>(qw + (e0 >> 7) * kQP + (e0 & 127)) = make_float4(qv[0], qv[1], qv[2], qv[3]);
+        float2 *rw = reinterpret_cast<float2 *>(lds + L.rope);
+        const int r0 = 2 * tid, r1 = 2 * (tid + kThreads);
+        *reinterpret_cast<float4 *>(rw + (r0 >> 6) * kRP + (r0 & 63)) = rope_v;
+        *reinterpret_cast<float4 *>(rw + (r1 >> 6) * kRP + (r1 & 63)) = rope_w;
+    }
+    if constexpr (F != kF32 && !TAIL) {
+        // B_k rows -> the A_k staging area (free until the main loop)
+        uint8_t *tmp = lds + L.stage;
+#pragma unroll
+        for (int i = 0; i < NBK; ++i) {
+            const bool ok = tid + kThreads * i < n16;
+            if (ok) reinterpret_cast<uint4 *>(tmp)[tid + kThreads * i] = bkraw[i];
+        }
+        if constexpr (F == kI8)
+            if (tid < rk) reinterpret_cast<float *>(tmp + 128 * kD)[tid] = bsc_v;  // after the rows
+    }
+    __syncthreads();
+    // per-tile query rotation (pq - p0 - 32 tile) theta_j = angle difference
+    {
+        float2 *bw = reinterpret_cast<float2 *>(lds + L.base);
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int e = 2 * (tid + kThreads * i);  // entries e, e + 1 (same tile)
+            if (e < tiles_valid * 64) {
+                const float4 st = step_v[i];
+                const float2 a0 = ang[e & 63], a1 = ang[(e + 1) & 63];
+                // (cos, sin)(A - B) = (cA cB + sA sB, sA cB - cA sB)
+                bw[e] = make_float2(a0.x * st.x + a0.y * st.y, a0.y * st.x - a0.x * st.y);
+                bw[e + 1] = make_float2(a1.x * st.z + a1.y * st.w, a1.y * st.z - a1.x * st.w);
+            }
+        }
+    }
+    if constexpr (!TAIL) {
+        uint16_t *bk = reinterpret_cast<uint16_t *>(lds + L.bk);
+        const uint8_t *tmp = lds + L.stage;
+        const float *bsc = reinterpret_cast<const float *>(tmp + 128 * kD);  // int8 only
+        for (int q = tid; q < 8 * 4 * 64; q += kThreads) {
+            const int l2 = q & 63, ks = (q >> 6) & 3, mt = q >> 8;
+            if (ks >= KS) continue;
+            const int j = 16 * mt + (l2 & 15), r0 = 32 * ks + 8 * (l2 >> 4);
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = r0 + e;
+                v[e] = 0.f;
+                if (r < rk) {
+                    if constexpr (F == kBF16) v[e] = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(tmp)[r * kD + j]);
+                    else if constexpr (F == kI8) v[e] = static_cast<float>(reinterpret_cast<const int8_t *>(tmp)[r * kD + j]) * bsc[r];
+                    else v[e] = load_elem<F>(Bk, static_cast<int64_t>(r) * kD + j);
+                }
+            }
+            u16x8_t f[NS];
+            frag_terms<NS>(v, f);
+#pragma unroll
+            for (int st = 0; st < NS; ++st) *reinterpret_cast<u16x8_t *>(bk + (st * 2048 + q) * 8) = f[st];
+        }
+    }
+    __syncthreads();  // tables, fragments; the staging area is free again
+    // Lane (c, n) owns query head n: column n of every accumulator.
+    const float *qrow = reinterpret_cast<const float *>(lds + L.qs) + ln * kQP;
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4_t u[8];
@@ -387,16 +419,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     // registers are free during it) and staged at the end of the tile; A_v^T
     // pieces are loaded a whole tile ahead.
     const int my_tiles = tiles_valid > wave ? (tiles_valid - 1 - wave) / kWaves + 1 : 0;
-    if (my_tiles > 0) {
-        load_k(wave);
-        stage_k();
-        load_v(wave);
-    }
+    if (my_tiles > 0) stage_k();
     for (int it = 0; it < my_tiles; ++it) {
         const int tile = wave + kWaves * it;
         const int tt0 = tok0 + tile * kTile;  // first token of the tile (block- or tail-local)
 
-        // ---- rotated query fragments for this tile (dims 16 kk + 4 c + i and + 64)
+        if (it + 1 < my_tiles) load_k(tile + kWaves);  // a whole tile of latency cover
+
+        // ---- this tile's rotated query fragments, dims 16 kk + 4 c + i and + 64
         u16x8_t qf[NS][4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -409,9 +439,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             float v[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x1 = q1[i], x2 = q2[i];
-                v[i] = x1 * cs[i] - x2 * sn[i];
-                v[4 + i] = x1 * sn[i] + x2 * cs[i];
+                v[i] = q1[i] * cs[i] - q2[i] * sn[i];
+                v[4 + i] = q1[i] * sn[i] + q2[i] * cs[i];
             }
             u16x8_t f[NS];
             frag_terms<NS>(v, f);
@@ -425,11 +454,13 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const int t = 16 * nt + ln;
+            asm volatile("" ::: "memory");
             f32x4_t acc[8];
             if constexpr (!TAIL) {
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
                 for (int ks = 0; ks < KS; ++ks) {
+                    const bool first = ks == 0;  // zero accumulator input (inline constant)
                     u16x8_t bfr[NS];
                     if constexpr (F == kBF16) {
 #pragma unroll
@@ -451,14 +482,18 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                         frag_terms<NS>(v, bfr);
                     }
 #pragma unroll
-                    for (int mt = 0; mt < 8; ++mt) {
+                    for (int sa = 0; sa < NS; ++sa) {
+                        // all eight fragment reads in flight before the first product
+                        u16x8_t a[8];
 #pragma unroll
-                        for (int sa = 0; sa < NS; ++sa) {
-                            const u16x8_t a = *reinterpret_cast<const u16x8_t *>(bkf + ((sa * 2048) + (mt * 4 + ks) * 64 + lane) * 8);
+                        for (int mt = 0; mt < 8; ++mt)
+                            a[mt] = *reinterpret_cast<const u16x8_t *>(bkf + ((sa * 2048) + (mt * 4 + ks) * 64 + lane) * 8);
+#pragma unroll
+                        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                             for (int sb = 0; sb < NS; ++sb)
-                                if (sa + sb < NS) acc[mt] = mfma16x16x32(a, bfr[sb], acc[mt]);
-                        }
+                                if (sa + sb < NS)
+                                    acc[mt] = mfma16x16x32(a[mt], bfr[sb], (first && sa + sb == 0) ? zero4() : acc[mt]);
                     }
                 }
             } else {
@@ -481,10 +516,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                     }
                 }
             }
+            // keep the table reads below after the rebuild (registers)
+            asm volatile("" ::: "memory");
             S[nt] = zero4();
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const float4 *rp = reinterpret_cast<const float4 *>(rope + t * 64 + 16 * kk + 4 * c4);
+                const float4 *rp = reinterpret_cast<const float4 *>(rope + t * kRP + 16 * kk + 4 * c4);
                 const float4 r01 = rp[0], r23 = rp[1];
                 const float cs[4] = {r01.x, r01.z, r23.x, r23.z}, sn[4] = {r01.y, r01.w, r23.y, r23.w};
                 float v[8];
@@ -504,7 +541,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             }
         }
 
-        if (it + 1 < my_tiles) load_k(tile + kWaves);
 
         // ---- online softmax (log2 domain) for head ln over this tile's 32 tokens
         float sc[2][4], vs[2][4];
@@ -531,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = tile * kTile + 16 * nt + 4 * c4 + i < valid;
+                const bool ok = !TAIL || tile * kTile + 16 * nt + 4 * c4 + i < valid;
                 x[nt][i] = ok ? S[nt][i] * sc[nt][i] : -INFINITY;
                 tmax = fmaxf(tmax, x[nt][i]);
             }
@@ -552,20 +588,18 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         l_run = l_run * alpha + psum;
         m_run = mn;
 
-        // ---- u^T = alpha u^T + A_v^T P^T
+        // ---- u^T = alpha u^T + A_v^T P^T (the rescale is skipped when no head's maximum moved)
         u16x8_t pf[NS];
         frag_terms<NS>(pv, pf);
+        const bool rescale = __any(alpha != 1.f);
         if constexpr (!TAIL && F != kF32) {
 #pragma unroll
             for (int mr = 0; mr < 8; ++mr)
                 if (mr < NTU) {
-                    u[mr] *= alpha;
+                    if (rescale) u[mr] *= alpha;
                     u16x8_t af;
                     if constexpr (F == kBF16) {
-                        af[0] = vraw[mr][0].x & 0xffff; af[1] = vraw[mr][0].x >> 16;
-                        af[2] = vraw[mr][0].y & 0xffff; af[3] = vraw[mr][0].y >> 16;
-                        af[4] = vraw[mr][1].x & 0xffff; af[5] = vraw[mr][1].x >> 16;
-                        af[6] = vraw[mr][1].y & 0xffff; af[7] = vraw[mr][1].y >> 16;
+                        af = __builtin_bit_cast(u16x8_t, make_uint4(vraw[mr][0].x, vraw[mr][0].y, vraw[mr][1].x, vraw[mr][1].y));
                     } else {
                         float v[8];
 #pragma unroll
@@ -584,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 #pragma unroll
             for (int mr = 0; mr < 8; ++mr)
                 if (mr < NTU) {
-                    u[mr] *= alpha;
+                    if (rescale) u[mr] *= alpha;
                     const int row = min(16 * mr + ln, rv - 1);
                     float v[8];
 #pragma unroll
@@ -620,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             }
 #pragma unroll
             for (int mr = 0; mr < 8; ++mr) {
-                u[mr] *= alpha;
+                if (rescale) u[mr] *= alpha;
                 const int dim = 16 * mr + ln;
                 u16x8_t af[NS];
                 if constexpr (F == kBF16) {
@@ -672,28 +706,28 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             *reinterpret_cast<f32x4_t *>(uw + (wave * 16 + ln) * kUP + 16 * mr + 4 * c4) = u[mr];
     const int KSV = (rv + 31) >> 5;  // 32-rank k-steps of u B_v
     const int rpad = TAIL ? kD : KSV * 32;
+    // B_v fragments for o = u B_v (lane: dim 16 w + n, ranks 32 ks + 8 c + e), read
+    // straight from memory now so that their latency overlaps the merge
+    u16x8_t bvf[NS][4];
     if constexpr (!TAIL) {
-        // B_v rows (INT8 dequantised; fp32 as two bf16 terms) -> LDS, zero rows up to rpad
-        uint8_t *bv = lds + L.bv;
-        for (int e = tid; e < rpad * 64; e += kThreads) {
-            const int r = e >> 6, w2 = e & 63;  // dims 2 w2, 2 w2 + 1
-            float v0 = 0.f, v1 = 0.f;
-            if (r < rv) {
-                v0 = load_elem<F>(Bv, static_cast<int64_t>(r) * kD + 2 * w2);
-                v1 = load_elem<F>(Bv, static_cast<int64_t>(r) * kD + 2 * w2 + 1);
-                if constexpr (F == kI8) {
-                    const float sb = p.v_bscale[static_cast<int64_t>(fid) * kD + r];
-                    v0 *= sb;
-                    v1 *= sb;
-                }
-            }
-            uint16_t t0[2], t1[2];
-            to_terms<NS>(v0, t0);
-            to_terms<NS>(v1, t1);
+        if (rv > 0) {
+            const int dim = 16 * wave + ln;
 #pragma unroll
-            for (int st = 0; st < NS; ++st)
-                *reinterpret_cast<uint32_t *>(bv + (st * 128 + r) * kBVP + w2 * 4) =
-                    static_cast<uint32_t>(t0[st]) | (static_cast<uint32_t>(t1[st]) << 16);
+            for (int ks = 0; ks < 4; ++ks) {
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 32 * ks + 8 * c4 + e;
+                    const int rc = min(r, rv - 1);
+                    float x = load_elem<F>(Bv, static_cast<int64_t>(rc) * kD + dim);
+                    if constexpr (F == kI8) x *= p.v_bscale[static_cast<int64_t>(fid) * kD + rc];
+                    v[e] = r < rv ? x : 0.f;
+                }
+                u16x8_t f[NS];
+                frag_terms<NS>(v, f);
+#pragma unroll
+                for (int st = 0; st < NS; ++st) bvf[st][ks] = f[st];
+            }
         }
     }
     __syncthreads();
@@ -728,25 +762,21 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         for (int e = tid; e < G * kD; e += kThreads) po[e] = uacc[(e >> 7) * kUP + (e & 127)];
     } else {
         // o^T tile of wave w: dims 16 w .. 16 w + 15 = u (16 x rpad) B_v (rpad x 128)
-        const uint8_t *bv = lds + L.bv;
         f32x4_t o = zero4();
-        for (int ks = 0; ks < KSV; ++ks) {
-            const float4 *up = reinterpret_cast<const float4 *>(uacc + ln * kUP + 32 * ks + 8 * c4);
-            const float4 ua = up[0], ub = up[1];
-            const float v[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
-            u16x8_t af[NS], bf[NS];
-            frag_terms<NS>(v, af);
-            const int dim = 16 * wave + ln;
 #pragma unroll
-            for (int st = 0; st < NS; ++st)
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks < KSV) {
+                const float4 *up = reinterpret_cast<const float4 *>(uacc + ln * kUP + 32 * ks + 8 * c4);
+                const float4 ua = up[0], ub = up[1];
+                const float v[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+                u16x8_t af[NS];
+                frag_terms<NS>(v, af);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    bf[st][e] = *reinterpret_cast<const uint16_t *>(bv + (st * 128 + 32 * ks + 8 * c4 + e) * kBVP + dim * 2);
+                for (int sa = 0; sa < NS; ++sa)
 #pragma unroll
-            for (int sa = 0; sa < NS; ++sa)
-#pragma unroll
-                for (int sb = 0; sb < NS; ++sb)
-                    if (sa + sb < NS) o = mfma16x16x32(af[sa], bf[sb], o);
+                    for (int sb = 0; sb < NS; ++sb)
+                        if (sa + sb < NS) o = mfma16x16x32(af[sa], bvf[sb][ks], o);
+            }
         }
         // o[i]: head 4 c + i, dim 16 w + ln
 #pragma unroll
@@ -803,6 +833,29 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeParams 
         static_cast<uint16_t *>(p.out)[oi] = f32_to_bf16_bits(o);
 }
 
+// RoPE tables shared by every workgroup of one call: theta_j = base^(-2j/128),
+// (cos, sin)(t theta_j) for t < 32, and (cos, sin)(32 tile theta_j) for the
+// tile offsets of a split (angles reduced in fp64).
+__global__ __launch_bounds__(256) void decode_tables_kernel(double rope_base, double *theta, float2 *rope,
+                                                            float2 *step) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int j = i & 63;
+    const double th = exp2(-(static_cast<double>(j) / 64.0) * log2(rope_base));
+    if (i < 64) theta[i] = th;
+    if (i < 32 * 64) {
+        float sn, cs;  // angle < 32 rad: fp32 sincos is accurate after its own reduction
+        sincosf(static_cast<float>(static_cast<double>(i >> 6) * th), &sn, &cs);
+        rope[i] = make_float2(cs, sn);
+    }
+    if (i < kMaxTiles * 64) {
+        double a = 32.0 * static_cast<double>(i >> 6) * th;
+        a -= kTwoPi * rint(a / kTwoPi);
+        float sn, cs;
+        sincosf(static_cast<float>(a), &sn, &cs);
+        step[i] = make_float2(cs, sn);
+    }
+}
+
 template <int F, bool TAIL>
 hipError_t launch_partial(const DecodeParams &p, dim3 grid, hipStream_t st) {
     constexpr int NS = (F == kF32) ? 2 : 1;
@@ -827,10 +880,20 @@ bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int spli
     return true;
 }
 
+size_t decode_table_bytes() {
+    return (64 * sizeof(double) + (32 + kMaxTiles) * 64 * sizeof(float2) + 255) / 256 * 256;
+}
+
 size_t decode_workspace_bytes(const DecodeParams &p) {
     const size_t n = static_cast<size_t>(p.batch) * p.n_kv_heads * p.n_splits * p.group;
     const size_t ml = (n * 2 * sizeof(float) + 255) / 256 * 256;
-    return ml + n * kD * sizeof(float);
+    return (ml + n * kD * sizeof(float) + 255) / 256 * 256 + decode_table_bytes();
+}
+
+hipError_t launch_decode_tables(const DecodeParams &p, hipStream_t st) {
+    hipLaunchKernelGGL(decode_tables_kernel, dim3(kMaxTiles * 64 / 256), dim3(256), 0, st, p.rope_base, p.theta,
+                       p.rope_tab, p.step_tab);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_blocks(const DecodeParams &p, hipStream_t st) {

@@ -79,13 +79,20 @@ struct DecodeParams {
     int n_splits;      // n_sel * block_splits + tail_splits
     float *part_ml;    // [batch][Hkv][n_splits][group][2]  (m, l) in log2 units
     float *part_o;     // [batch][Hkv][n_splits][group][128]
+    // RoPE tables, rebuilt by launch_decode_tables each call (workspace):
+    double *theta;     // [64] base^(-2j/128)
+    float2 *rope_tab;  // [32][64] (cos, sin)(t theta_j), t < 32
+    float2 *step_tab;  // [kMaxTiles][64] (cos, sin)(32 tile theta_j)
 };
+constexpr int kMaxTiles = 64;  // 32-token tiles per split (split_len <= 2048)
 
 // Whether a split of `split` tokens fits the decode kernels' LDS budget.
 bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int split);
-size_t decode_workspace_bytes(const DecodeParams &p);
+size_t decode_workspace_bytes(const DecodeParams &p);  // partials, then the tables
+size_t decode_table_bytes();
 // Partial results of the compressed-block splits, of the tail splits, and the
 // log-sum-exp merge into the output.
+hipError_t launch_decode_tables(const DecodeParams &p, hipStream_t st);
 hipError_t launch_decode_blocks(const DecodeParams &p, hipStream_t st);
 hipError_t launch_decode_tail(const DecodeParams &p, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeParams &p, hipStream_t st);

@@ -179,7 +179,8 @@ milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, in
  * rebuilt key at its position; logits are scaled by softmax_scale.
  */
 typedef struct milo_decode_args {
-    const void *q;            /* device [batch][n_q_heads][head_dim], pre-RoPE          */
+    const void *q;            /* device [batch][n_q_heads][head_dim], pre-RoPE, 16-byte */
+                              /* aligned (the factor arenas must be 16-byte aligned too) */
     milo_dtype q_dtype;       /* MILO_F32 or MILO_BF16                                  */
     const int64_t *q_pos;     /* device [batch]                                         */
     int32_t batch;
@@ -206,7 +207,8 @@ typedef struct milo_decode_args {
     int32_t split_len;        /* tokens per work split: multiple of 128, at most 1024,   */
                               /* dividing block_len; 0 picks the longest split that     */
                               /* still gives >= 1024 workgroups (else 128)              */
-    void *workspace;          /* device scratch for the per-split partial results       */
+    void *workspace;          /* device scratch: per-split partial results and the     */
+                              /* RoPE tables of the call (256-byte aligned)             */
     size_t workspace_bytes;
 } milo_decode_args;
 
