@@ -62,14 +62,15 @@ KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "jacobi": ["jacobi.hip"],
                   "refine": ["refine.hip", "common.hpp"], "alloc": ["alloc.hip"],
                   "project": ["project.hip", "common.hpp"], "reconstruct": ["reconstruct.hip", "common.hpp"],
                   "decode_blocks": ["decode.hip", "common.hpp"], "decode_tail": ["decode.hip", "common.hpp"],
-                  "decode_combine": ["decode.hip", "common.hpp"]}
+                  "decode_combine": ["decode.hip", "common.hpp"], "decode_tables": ["decode.hip"]}
 
 
 def kernel_key(name):
     """libmilo kernel name (as rocprofv3 prints it) -> bench kernel key."""
     for frag, key in (("gram_kernel", "gram"), ("jacobi_kernel", "jacobi"), ("refine_kernel", "refine"),
                       ("alloc_kernel", "alloc"), ("project_kernel", "project"),
-                      ("reconstruct_kernel", "reconstruct"), ("decode_combine_kernel", "decode_combine")):
+                      ("reconstruct_kernel", "reconstruct"), ("decode_combine_kernel", "decode_combine"),
+                      ("decode_tables_kernel", "decode_tables")):
         if frag in name:
             return key
     if "decode_partial_kernel" in name:
