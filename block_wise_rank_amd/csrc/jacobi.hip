@@ -49,9 +49,10 @@ constexpr int kPrmBytes = 2 * 64 * 16;
 constexpr int kXchBytes = 2 * 2 * (kNW - 1) * 64 * 8;
 constexpr int kLdsBytes = kGWords * 4 + kPrmBytes + kXchBytes;  // 80 KiB: two blocks per CU
 constexpr int kGeneric = 2016 - 64;   // off-diagonal blocks not needed for the next round's rotations
-constexpr int kPerLane = (kGeneric + kThreads - 1) / kThreads;
+constexpr int kGenLanes = kThreads - 64;  // waves 0..6 (wave 7 computes the next round's rotations)
+constexpr int kPerLane = (kGeneric + kGenLanes - 1) / kGenLanes;
 static_assert(kLdsBytes == 80 * 1024, "two workgroups per CU");
-static_assert(kPerLane == 4, "generic block slots per lane");
+static_assert(kPerLane == 5, "generic block slots per lane");
 
 // Block (P, Q) holds the next round's pair iff Q == P + 2, or it is (0, 1) or (62, 63).
 constexpr bool next_pair_block(int P, int Q) {
@@ -162,12 +163,12 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
         F[j] = make_float2(c0 == P ? 1.f : 0.f, c0 + 1 == P ? 1.f : 0.f);
         S[j] = make_float2(c0 == 127 - P ? 1.f : 0.f, c0 + 1 == 127 - P ? 1.f : 0.f);
     }
-    // Generic blocks of this lane: table entries tid, tid + 512, ...
+    // Generic blocks of this lane (waves 0..6): table entries tid, tid + 448, ...
     int bq[kPerLane];
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
-        const int i = tid + kThreads * j;
-        bq[j] = i < kGeneric ? kBlocks.pq[i] : -1;
+        const int i = tid + kGenLanes * j;
+        bq[j] = (wave < kNW - 1 && i < kGeneric) ? kBlocks.pq[i] : -1;
     }
     // The next-pair block of this lane (wave 7 only): lane = next round's pair P'.
     const int Pn = lane;
@@ -258,16 +259,17 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
             }
 
 
-            // ---- generic off-diagonal blocks, two at a time: loads first, then stores
+            // ---- generic off-diagonal blocks (waves 0..6), two at a time: loads first, then stores
 #pragma unroll
             for (int j0 = 0; j0 < kPerLane; j0 += 2) {
+                if (wave == kNW - 1) break;  // uniform
                 int ad[2][4];
                 float gv[2][4];
                 float2 c1[2], c2[2];
                 bool act[2];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const int code = bq[j0 + i];
+                    const int code = j0 + i < kPerLane ? bq[j0 + i] : -1;
                     act[i] = code >= 0;
                     const int P = act[i] ? (code & 0xff) : 0, Q = act[i] ? (code >> 8) : 1;
                     c1[i] = *reinterpret_cast<const float2 *>(pc + P);
