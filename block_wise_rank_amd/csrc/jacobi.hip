@@ -85,6 +85,41 @@ __device__ __forceinline__ int gidx(int a, int b) {
     return static_cast<int>(__umul24(static_cast<unsigned>(min(a, b)), kGP)) + max(a, b);
 }
 
+// LDS byte offsets of G's elements for every generic block of every lane in
+// every round of a sweep: [round][lane][kPerLane blocks x 4 elements, padded to
+// 24].  The tournament's index arithmetic is the same for every matrix, so it is
+// tabulated once (2.7 MB, L2-resident) and each lane loads its 48 bytes a round
+// ahead.  Byte offsets of the upper triangle end below 64 KiB, so 16 bits hold them.
+constexpr int kAddrPad = 24;
+constexpr int kAddrVec = kAddrPad * 2 / 16;  // uint4 per lane and round
+static_assert(kGWords * 4 <= 65536, "16-bit LDS offsets");
+static_assert(4 * kPerLane <= kAddrPad, "table row");
+__device__ __align__(16) uint16_t g_gen_addr[127 * kGenLanes * kAddrPad];
+
+__global__ __launch_bounds__(256) void jacobi_table_kernel() {
+    const int i = blockIdx.x * 256 + threadIdx.x;  // (round, lane, block slot)
+    if (i >= 127 * kGenLanes * kPerLane) return;
+    const int j = i % kPerLane, g = (i / kPerLane) % kGenLanes, k = i / (kPerLane * kGenLanes);
+    uint16_t *out = g_gen_addr + (k * kGenLanes + g) * kAddrPad + 4 * j;
+    const int bi = g + kGenLanes * j;
+    if (bi >= kGeneric) {
+        out[0] = out[1] = out[2] = out[3] = 0;
+        return;
+    }
+    const int code = kBlocks.pq[bi];
+    const int P = code & 0xff, Q = code >> 8;
+    const int p1 = index_at(P, k), q1 = index_at(127 - P, k);
+    const int p2 = index_at(Q, k), q2 = index_at(127 - Q, k);
+    out[0] = static_cast<uint16_t>(4 * gidx(p1, p2));
+    out[1] = static_cast<uint16_t>(4 * gidx(p1, q2));
+    out[2] = static_cast<uint16_t>(4 * gidx(q1, p2));
+    out[3] = static_cast<uint16_t>(4 * gidx(q1, q2));
+}
+
+__device__ __forceinline__ float &lds_at(float *base, unsigned byte_off) {
+    return *reinterpret_cast<float *>(reinterpret_cast<char *>(base) + byte_off);
+}
+
 struct Rot {
     float c, s, na, nb;
     bool rot;
@@ -175,6 +210,11 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
     const int Pa = Pn == 0 ? 0 : (Pn == 63 ? 62 : Pn - 1);
     const int Pb = Pn == 0 ? 1 : (Pn == 63 ? 63 : Pn + 1);
     const int sel = Pn == 0 ? 0 : (Pn == 63 ? 3 : 2);  // element (p1 p2) / (q1 q2) / (q1 p2)
+    // This lane's row of the offset table (wave 7 reads a valid row it never uses).
+    const uint4 *arow = reinterpret_cast<const uint4 *>(g_gen_addr) + (tid < kGenLanes ? tid : tid - 64) * kAddrVec;
+    uint4 ta[kAddrVec];
+#pragma unroll
+    for (int v = 0; v < kAddrVec; ++v) ta[v] = arow[v];
     __syncthreads();
 
     int used = -max_sweeps;
@@ -223,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                 const int p2 = index_at(Pb, k), q2 = index_at(127 - Pb, k);
                 const int sa[4] = {gidx(p1, p2), gidx(p1, q2), gidx(q1, p2), gidx(q1, q2)};
                 const int asel = sel == 0 ? sa[0] : (sel == 2 ? sa[2] : sa[3]);
-                const bool sact = A.y != 0.f || B.y != 0.f;
+                const bool sact = (A.y != 0.f) | (B.y != 0.f);
                 float h[4];
                 if (sact) {
 #pragma unroll
@@ -260,46 +300,53 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
 
 
             // ---- generic off-diagonal blocks (waves 0..6), two at a time: loads first, then stores
+            {
+                // next round's offsets (round 0 after the sweep's last): each uint4
+                // of the table row is reloaded once its two blocks are done
+                const int kn = k == 126 ? 0 : k + 1;
+                const uint4 *anext = arow + kn * kGenLanes * kAddrVec;
 #pragma unroll
-            for (int j0 = 0; j0 < kPerLane; j0 += 2) {
-                if (wave == kNW - 1) break;  // uniform
-                int ad[2][4];
-                float gv[2][4];
-                float2 c1[2], c2[2];
-                bool act[2];
+                for (int j0 = 0; j0 < kPerLane; j0 += 2) {
+                    if (wave == kNW - 1) break;  // uniform
+                    const uint4 tv = ta[j0 / 2];
+                    const unsigned aw[4] = {tv.x, tv.y, tv.z, tv.w};
+                    unsigned ad[2][4];
+                    float gv[2][4];
+                    float2 c1[2], c2[2];
+                    bool act[2];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int code = j0 + i < kPerLane ? bq[j0 + i] : -1;
-                    act[i] = code >= 0;
-                    const int P = act[i] ? (code & 0xff) : 0, Q = act[i] ? (code >> 8) : 1;
-                    c1[i] = *reinterpret_cast<const float2 *>(pc + P);
-                    c2[i] = *reinterpret_cast<const float2 *>(pc + Q);
-                    act[i] = act[i] && (c1[i].y != 0.f || c2[i].y != 0.f);
-                    const int p1 = index_at(P, k), q1 = index_at(127 - P, k);
-                    const int p2 = index_at(Q, k), q2 = index_at(127 - Q, k);
-                    ad[i][0] = gidx(p1, p2);
-                    ad[i][1] = gidx(p1, q2);
-                    ad[i][2] = gidx(q1, p2);
-                    ad[i][3] = gidx(q1, q2);
+                    for (int i = 0; i < 2; ++i) {
+                        const int code = j0 + i < kPerLane ? bq[j0 + i] : -1;
+                        act[i] = code >= 0;
+                        const int P = act[i] ? (code & 0xff) : 0, Q = act[i] ? (code >> 8) : 1;
+                        c1[i] = *reinterpret_cast<const float2 *>(pc + P);
+                        c2[i] = *reinterpret_cast<const float2 *>(pc + Q);
+                        act[i] = act[i] & ((c1[i].y != 0.f) | (c2[i].y != 0.f));
+                        ad[i][0] = aw[2 * i] & 0xffffu;
+                        ad[i][1] = aw[2 * i] >> 16;
+                        ad[i][2] = aw[2 * i + 1] & 0xffffu;
+                        ad[i][3] = aw[2 * i + 1] >> 16;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        if (act[i]) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) gv[i][e] = lds_at(G, ad[i][e]);
+                        }
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        if (act[i]) {
+                            // rows of pair P, then columns of pair Q
+                            const float s1 = c1[i].y, k1 = c1[i].x, s2 = c2[i].y, k2 = c2[i].x;
+                            const float h11 = k1 * gv[i][0] - s1 * gv[i][2], h12 = k1 * gv[i][1] - s1 * gv[i][3];
+                            const float h21 = s1 * gv[i][0] + k1 * gv[i][2], h22 = s1 * gv[i][1] + k1 * gv[i][3];
+                            lds_at(G, ad[i][0]) = k2 * h11 - s2 * h12;
+                            lds_at(G, ad[i][1]) = s2 * h11 + k2 * h12;
+                            lds_at(G, ad[i][2]) = k2 * h21 - s2 * h22;
+                            lds_at(G, ad[i][3]) = s2 * h21 + k2 * h22;
+                        }
+                    ta[j0 / 2] = anext[j0 / 2];
                 }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    if (act[i]) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) gv[i][e] = G[ad[i][e]];
-                    }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    if (act[i]) {
-                        // rows of pair P, then columns of pair Q
-                        const float s1 = c1[i].y, k1 = c1[i].x, s2 = c2[i].y, k2 = c2[i].x;
-                        const float h11 = k1 * gv[i][0] - s1 * gv[i][2], h12 = k1 * gv[i][1] - s1 * gv[i][3];
-                        const float h21 = s1 * gv[i][0] + k1 * gv[i][2], h22 = s1 * gv[i][1] + k1 * gv[i][3];
-                        G[ad[i][0]] = k2 * h11 - s2 * h12;
-                        G[ad[i][1]] = s2 * h11 + k2 * h12;
-                        G[ad[i][2]] = k2 * h21 - s2 * h22;
-                        G[ad[i][3]] = s2 * h21 + k2 * h22;
-                    }
             }
             if (k == 1 && tid == 0) flags[((sweep + 1) & 1) * 130] = 0;
             __syncthreads();
@@ -335,6 +382,10 @@ hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(jacobi_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
+    // Refilled on the caller's stream before every solve, so the solve never
+    // depends on another stream's work; concurrent fills write identical values.
+    constexpr int kTabThreads = 127 * kGenLanes * kPerLane;
+    hipLaunchKernelGGL(jacobi_table_kernel, dim3((kTabThreads + 255) / 256), dim3(256), 0, st);
     hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), kLdsBytes, st,
                        gpart, splits, vt, sweeps, max_sweeps, tol);
     return hipGetLastError();
