@@ -31,7 +31,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
-PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA
 PEAK_FP32_VEC_TFLOPS = 157.3   # fp32 vector (packed)
 METRIC = ("compressed-KV decode context-tokens/s (+HBM %peak); blocks/s compressed (+MFMA %)")
 
@@ -381,7 +380,10 @@ def main():
         # kernel: (algorithmic amount for the whole step, unit, bound, peak)
         "gram": (n_blocks_step * T * d * xe, "GB/s", "hbm", PEAK_HBM_GBS),
         "jacobi": (n_blocks_step * sweeps_mean * 9 * d * d * (d - 1), "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
-        "refine": (n_blocks_step * 2.0 * T * d * d, "TFLOP/s", "mfma", PEAK_FP32_MFMA_TFLOPS),
+        # bf16 MFMA products executed: V^T split in 3 bf16 terms (and X too when fp32),
+        # term pairs of order <= 2 kept: 3 products per bf16 X, 6 per fp32 X
+        "refine": (n_blocks_step * 2.0 * T * d * d * (3 if xe == 2 else 6), "TFLOP/s", "mfma",
+                   PEAK_BF16_TFLOPS),
         "alloc": (n_blocks_step * d * 4, "GB/s", "hbm", PEAK_HBM_GBS),
         "project": (n_blocks_step * T * d * xe + tot_rank * (T + d) * fe + n_blocks_step * d * d * 4,
                     "GB/s", "hbm", PEAK_HBM_GBS),

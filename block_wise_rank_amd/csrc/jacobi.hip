@@ -32,6 +32,17 @@
 //    computes it at once; parameters and new diagonal entries of every pair are
 //    double-buffered in LDS.  One barrier per round.
 //
+// Scaled rotations (the square-root-free bookkeeping of "fast Givens", Golub &
+// Van Loan sec. 5.1.13, applied to both sides): row i of G and of V^T is stored
+// divided by a scale s_i.  The rotation (c, s = c t) of pair (p, q) then becomes
+// R_p <- R_p - alpha R_q, R_q <- beta R_p + R_q with alpha = t s_q / s_p,
+// beta = t s_p / s_q, and s_p, s_q <- c s_p, c s_q: two FMAs per element
+// instead of four products.  Scales only shrink (c >= 1/sqrt 2), so every 63 or
+// 64 rounds (at rounds 63 and 126 of a sweep) G and V^T are multiplied back by
+// them and the scales restart at 1; stored values stay within 2^32 of the true
+// ones.  Rotation parameters are computed from true values (diagonal entries
+// are tracked unscaled, g = s_p s_q G_pq).
+//
 // Pairs whose rotation is the identity (already orthogonal to tolerance) skip
 // their LDS traffic, so late sweeps cost little; a sweep without any rotation
 // ends the solve.  Diagonal entries are never stored in G.
@@ -45,14 +56,29 @@ constexpr int kGP = 129;              // LDS pitch of G (floats)
 constexpr int kThreads = 512;         // 8 waves
 constexpr int kNW = kThreads / 64;
 constexpr int kGWords = 16384;        // G's upper triangle ends at 126 * 129 + 127
-constexpr int kPrmBytes = 2 * 64 * 16;
+constexpr int kPrmBytes = 2 * 64 * 8;  // (alpha, beta) per pair, double-buffered
 constexpr int kXchBytes = 2 * 2 * (kNW - 1) * 64 * 8;
-constexpr int kLdsBytes = kGWords * 4 + kPrmBytes + kXchBytes;  // 80 KiB: two blocks per CU
+constexpr int kLdsBytes = kGWords * 4 + kPrmBytes + kXchBytes;  // <= 80 KiB: two blocks per CU
 constexpr int kGeneric = 2016 - 64;   // off-diagonal blocks not needed for the next round's rotations
 constexpr int kGenLanes = kThreads - 64;  // waves 0..6 (wave 7 computes the next round's rotations)
 constexpr int kPerLane = (kGeneric + kGenLanes - 1) / kGenLanes;
-static_assert(kLdsBytes == 80 * 1024, "two workgroups per CU");
+static_assert(kLdsBytes <= 80 * 1024, "two workgroups per CU");
 static_assert(kPerLane == 5, "generic block slots per lane");
+
+// G's cells below and on the diagonal are free and hold small tables:
+//  * the two convergence flags (by sweep parity) at row 2, columns 0 and 1;
+//  * the scales by matrix index, gathered at renormalisation, on the diagonal
+//    (index 127's diagonal cell lies past the triangle: row 3, column 0);
+//  * per pair and buffer, (new diagonal of the first and second index, their
+//    new scales), as float4 at rows 64..79, columns < 35 (16-byte aligned).
+constexpr int kFlagWord = 2 * kGP;
+__device__ __forceinline__ int scale_word(int i) { return i < 127 ? i * (kGP + 1) : 3 * kGP; }
+static_assert(126 * (kGP + 1) < kGWords, "diagonal cells of indices 0..126 lie inside G");
+__device__ __forceinline__ int rec_word(int buf, int P) {
+    const int e = buf * 64 + P, r = 64 + (e >> 3);
+    return ((r * kGP + 3) & ~3) + 4 * (e & 7);
+}
+static_assert(((79 * kGP + 3) & ~3) + 4 * 7 + 3 < 79 * kGP + 64, "records stay below the diagonal");
 
 // Block (P, Q) holds the next round's pair iff Q == P + 2, or it is (0, 1) or (62, 63).
 constexpr bool next_pair_block(int P, int Q) {
@@ -121,13 +147,13 @@ __device__ __forceinline__ float &lds_at(float *base, unsigned byte_off) {
 }
 
 struct Rot {
-    float c, s, na, nb;
+    float c, t, na, nb;
     bool rot;
 };
 
 // Rotation annihilating g of the 2 x 2 block [a g; g b] (identity below tolerance).
 __device__ __forceinline__ Rot jacobi_rotation(float a, float b, float g, float tol) {
-    Rot r{1.f, 0.f, a, b, false};
+    Rot r{1.f, 0.f, a, b, false};  // (c, t, new a, new b)
     if (g != 0.f && g * g > tol * tol * fabsf(a * b)) {
         // Any (c, s) with c^2 + s^2 = 1 to working precision keeps the transform
         // orthogonal, so 1-ulp reciprocals are enough here.
@@ -135,11 +161,13 @@ __device__ __forceinline__ Rot jacobi_rotation(float a, float b, float g, float 
         const float az = fabsf(zeta);
         const float t = az > 1e18f ? 0.5f * __builtin_amdgcn_rcpf(zeta)
                                    : copysignf(__builtin_amdgcn_rcpf(az + sqrtf(1.f + zeta * zeta)), zeta);
-        r.c = __builtin_amdgcn_rsqf(1.f + t * t);
-        r.s = r.c * t;
-        r.na = a - t * g;
-        r.nb = b + t * g;
-        r.rot = true;
+        if (t != 0.f) {  // an infinite zeta (g negligible next to b - a) needs no rotation
+            r.c = __builtin_amdgcn_rsqf(1.f + t * t);
+            r.t = t;
+            r.na = a - t * g;
+            r.nb = b + t * g;
+            r.rot = true;
+        }
     }
     return r;
 }
@@ -150,8 +178,8 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                                                              int max_sweeps, float tol) {
     extern __shared__ __align__(16) float smem[];
     float *G = smem;
-    int *flags = reinterpret_cast<int *>(smem);  // at diagonal slots 0 and 130 (unused by G)
-    float4 *prm = reinterpret_cast<float4 *>(smem + kGWords);                 // [2][64] (c, s, na, nb)
+    int *flags = reinterpret_cast<int *>(smem + kFlagWord);                   // [2] by sweep parity
+    float2 *prm = reinterpret_cast<float2 *>(smem + kGWords);                 // [2][64] (alpha, beta)
     float2 *xch = reinterpret_cast<float2 *>(smem + kGWords + kPrmBytes / 4);  // [2][2][7][64]
 
     const int blk = blockIdx.x;
@@ -168,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
     }
     if (tid == 0) {
         flags[0] = 0;
-        flags[130] = 0;
+        flags[1] = 0;
     }
     __syncthreads();
 
@@ -181,8 +209,9 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
             b += src[static_cast<int64_t>(p) * kD * kD + y * kD + y];
         }
         const float g = G[x * kGP + y];
-        const Rot r = jacobi_rotation(a, b, g, tol);
-        prm[lane] = make_float4(r.c, r.s, r.na, r.nb);
+        const Rot r = jacobi_rotation(a, b, g, tol);  // scales start at 1: alpha = beta = t
+        prm[lane] = make_float2(r.t, r.t);
+        *reinterpret_cast<float4 *>(G + rec_word(0, lane)) = make_float4(r.na, r.nb, r.c, r.c);
         if (r.rot) {
             G[x * kGP + y] = 0.f;
             flags[0] = 1;
@@ -226,17 +255,18 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
             int k = kr;
             asm volatile("" : "+s"(k));
             const int cb = gk & 1;
-            const float4 *pc = prm + cb * 64;
+            const float2 *pc = prm + cb * 64;
+            // rounds after which G and V^T are multiplied back by their scales
+            const bool renorm = (k == 63) | (k == 126);
 
-            // ---- eigenvector rows: rotate, shift along the ring, send the ends
+            // ---- eigenvector rows: rotate (identity when alpha = beta = 0), shift
+            // along the ring, send the ends
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float2 cs = *reinterpret_cast<const float2 *>(pc + 8 * wave + j);
-                if (cs.y != 0.f) {  // uniform over the wave
-                    const float2 f = F[j], s = S[j];
-                    F[j] = make_float2(cs.x * f.x - cs.y * s.x, cs.x * f.y - cs.y * s.y);
-                    S[j] = make_float2(cs.y * f.x + cs.x * s.x, cs.y * f.y + cs.x * s.y);
-                }
+                const float2 ab = pc[8 * wave + j];
+                const float2 f = F[j], s = S[j];
+                F[j] = make_float2(fmaf(-ab.x, s.x, f.x), fmaf(-ab.x, s.y, f.y));
+                S[j] = make_float2(fmaf(ab.y, f.x, s.x), fmaf(ab.y, f.y, s.y));
             }
             // Round k + 1's position i holds round k's position i + 1 (127 -> 1 wraps
             // to 1 -> 127): first rows move down one slot, second rows up one slot.
@@ -258,33 +288,51 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
             // pair of round k + 1 formed by one of its elements
             const bool last_round = (k == 126);
             if (wave == kNW - 1) {
-                const float4 A = pc[Pa], B = pc[Pb];
+                const float2 A = pc[Pa], B = pc[Pb];
+                const float4 DA = *reinterpret_cast<const float4 *>(G + rec_word(cb, Pa));
+                const float4 DB = *reinterpret_cast<const float4 *>(G + rec_word(cb, Pb));
                 const int p1 = index_at(Pa, k), q1 = index_at(127 - Pa, k);
                 const int p2 = index_at(Pb, k), q2 = index_at(127 - Pb, k);
                 const int sa[4] = {gidx(p1, p2), gidx(p1, q2), gidx(q1, p2), gidx(q1, q2)};
                 const int asel = sel == 0 ? sa[0] : (sel == 2 ? sa[2] : sa[3]);
-                const bool sact = (A.y != 0.f) | (B.y != 0.f);
+                const bool sact = (A.x != 0.f) | (B.x != 0.f);
                 float h[4];
                 if (sact) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) h[e] = G[sa[e]];
-                    const float r11 = A.x * h[0] - A.y * h[2], r12 = A.x * h[1] - A.y * h[3];
-                    const float r21 = A.y * h[0] + A.x * h[2], r22 = A.y * h[1] + A.x * h[3];
-                    h[0] = B.x * r11 - B.y * r12;
-                    h[1] = B.y * r11 + B.x * r12;
-                    h[2] = B.x * r21 - B.y * r22;
-                    h[3] = B.y * r21 + B.x * r22;
+                    const float r11 = fmaf(-A.x, h[2], h[0]), r12 = fmaf(-A.x, h[3], h[1]);
+                    const float r21 = fmaf(A.y, h[0], h[2]), r22 = fmaf(A.y, h[1], h[3]);
+                    h[0] = fmaf(-B.x, r12, r11);
+                    h[1] = fmaf(B.y, r11, r12);
+                    h[2] = fmaf(-B.x, r22, r21);
+                    h[3] = fmaf(B.y, r21, r22);
                 } else {
                     const float v = G[asel];
                     h[0] = h[2] = h[3] = v;
                     h[1] = 0.f;
                 }
                 const float gn = sel == 0 ? h[0] : (sel == 2 ? h[2] : h[3]);
-                // new diagonal entries of the pair's first and second index
-                const float an = Pn == 0 ? A.z : (Pn == 63 ? B.w : B.z);
-                const float bn = Pn == 0 ? B.z : A.w;
-                const Rot r = jacobi_rotation(an, bn, gn, tol);
-                prm[(cb ^ 1) * 64 + Pn] = make_float4(r.c, r.s, r.na, r.nb);
+                // new diagonal entries and scales of the pair's first and second index
+                const float an = Pn == 0 ? DA.x : (Pn == 63 ? DB.y : DB.x);
+                const float bn = Pn == 0 ? DB.x : DA.y;
+                const float sfa = Pn == 0 ? DA.z : (Pn == 63 ? DB.w : DB.z);
+                const float sfb = Pn == 0 ? DB.z : DA.w;
+                Rot r = jacobi_rotation(an, bn, gn * sfa * sfb, tol);
+                const int kn = last_round ? 0 : k + 1;
+                float s1 = sfa, s2 = sfb;
+                if (renorm) {  // uniform: the scales are gathered by index and restart at 1
+                    G[scale_word(index_at(Pn, kn))] = sfa;
+                    G[scale_word(index_at(127 - Pn, kn))] = sfb;
+                    s1 = s2 = 1.f;
+                }
+                const float ratio = s2 * __builtin_amdgcn_rcpf(s1);
+                float al = r.t * ratio, be = r.t * __builtin_amdgcn_rcpf(ratio);
+                if ((al == 0.f) | (be == 0.f)) {  // negligible rotation: none
+                    r = Rot{1.f, 0.f, an, bn, false};
+                    al = be = 0.f;
+                }
+                prm[(cb ^ 1) * 64 + Pn] = make_float2(al, be);
+                *reinterpret_cast<float4 *>(G + rec_word(cb ^ 1, Pn)) = make_float4(r.na, r.nb, s1 * r.c, s2 * r.c);
                 const float gw = r.rot ? 0.f : gn;
                 if (sel == 0) h[0] = gw;
                 else if (sel == 2) h[2] = gw;
@@ -295,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                 } else if (r.rot) {
                     G[asel] = 0.f;
                 }
-                if (r.rot) flags[((sweep + (last_round ? 1 : 0)) & 1) * 130] = 1;
+                if (r.rot) flags[(sweep + (last_round ? 1 : 0)) & 1] = 1;
             }
 
 
@@ -319,9 +367,9 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                         const int code = j0 + i < kPerLane ? bq[j0 + i] : -1;
                         act[i] = code >= 0;
                         const int P = act[i] ? (code & 0xff) : 0, Q = act[i] ? (code >> 8) : 1;
-                        c1[i] = *reinterpret_cast<const float2 *>(pc + P);
-                        c2[i] = *reinterpret_cast<const float2 *>(pc + Q);
-                        act[i] = act[i] & ((c1[i].y != 0.f) | (c2[i].y != 0.f));
+                        c1[i] = pc[P];
+                        c2[i] = pc[Q];
+                        act[i] = act[i] & ((c1[i].x != 0.f) | (c2[i].x != 0.f));
                         ad[i][0] = aw[2 * i] & 0xffffu;
                         ad[i][1] = aw[2 * i] >> 16;
                         ad[i][2] = aw[2 * i + 1] & 0xffffu;
@@ -337,26 +385,44 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                     for (int i = 0; i < 2; ++i)
                         if (act[i]) {
                             // rows of pair P, then columns of pair Q
-                            const float s1 = c1[i].y, k1 = c1[i].x, s2 = c2[i].y, k2 = c2[i].x;
-                            const float h11 = k1 * gv[i][0] - s1 * gv[i][2], h12 = k1 * gv[i][1] - s1 * gv[i][3];
-                            const float h21 = s1 * gv[i][0] + k1 * gv[i][2], h22 = s1 * gv[i][1] + k1 * gv[i][3];
-                            lds_at(G, ad[i][0]) = k2 * h11 - s2 * h12;
-                            lds_at(G, ad[i][1]) = s2 * h11 + k2 * h12;
-                            lds_at(G, ad[i][2]) = k2 * h21 - s2 * h22;
-                            lds_at(G, ad[i][3]) = s2 * h21 + k2 * h22;
+                            const float a1 = c1[i].x, b1 = c1[i].y, a2 = c2[i].x, b2 = c2[i].y;
+                            const float h11 = fmaf(-a1, gv[i][2], gv[i][0]), h12 = fmaf(-a1, gv[i][3], gv[i][1]);
+                            const float h21 = fmaf(b1, gv[i][0], gv[i][2]), h22 = fmaf(b1, gv[i][1], gv[i][3]);
+                            lds_at(G, ad[i][0]) = fmaf(-a2, h12, h11);
+                            lds_at(G, ad[i][1]) = fmaf(b2, h11, h12);
+                            lds_at(G, ad[i][2]) = fmaf(-a2, h22, h21);
+                            lds_at(G, ad[i][3]) = fmaf(b2, h21, h22);
                         }
                     ta[j0 / 2] = anext[j0 / 2];
                 }
             }
-            if (k == 1 && tid == 0) flags[((sweep + 1) & 1) * 130] = 0;
+            if (k == 1 && tid == 0) flags[(sweep + 1) & 1] = 0;
             __syncthreads();
 
             // ---- receive the rows that crossed a wave boundary
             const float2 *xi = xch + cb * 2 * (kNW - 1) * 64;
             if (wave < kNW - 1) F[7] = xi[wave * 64 + lane];
             if (wave > 0) S[0] = xi[((kNW - 1) + wave - 1) * 64 + lane];
+
+            // ---- multiply G and V^T back by the scales (gathered by index above)
+            if (renorm) {
+                const int kn = k == 126 ? 0 : k + 1;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float sf = G[scale_word(index_at(8 * wave + j, kn))];
+                    const float ss = G[scale_word(index_at(127 - 8 * wave - j, kn))];
+                    F[j] = make_float2(F[j].x * sf, F[j].y * sf);
+                    S[j] = make_float2(S[j].x * ss, S[j].y * ss);
+                }
+                const float sj = G[scale_word(tid & 127)];
+                for (int e = tid; e < kD * kD; e += kThreads) {
+                    const int i = e >> 7, j = e & 127;
+                    if (i < j) G[i * kGP + j] *= G[scale_word(i)] * sj;
+                }
+                __syncthreads();
+            }
         }
-        const int rot = flags[(sweep & 1) * 130];
+        const int rot = flags[sweep & 1];
         if (!rot) {
             used = sweep + 1;
             break;
