@@ -81,6 +81,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 constexpr int kD = 128;
 constexpr int kMaxSweeps = 30;
 constexpr float kJacobiTol = 1e-6f;
+constexpr float kJacobiStopTol = 1e-3f;  // sqrt(kJacobiTol): quadratic convergence
 constexpr size_t kMat = sizeof(float) * kD * kD;  // one 128 x 128 fp32 matrix
 
 // Split the token dimension of the Gram when there are too few blocks to fill
@@ -292,7 +293,7 @@ milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr,
                 return hip_fail(e, "gram launch");
             if ((e = timed("jacobi", s, [&] {
                      return milo::launch_jacobi(gpart, splits, nb, vt, sweeps_out ? sweeps_out + b0 : nullptr,
-                                                kMaxSweeps, kJacobiTol, s);
+                                                kMaxSweeps, kJacobiTol, kJacobiStopTol, s);
                  })) != hipSuccess)
                 return hip_fail(e, "jacobi launch");
             if ((e = timed("refine", s, [&] { return milo::launch_refine(xc, x_type, row0, in->row_stride, T, nb, vt, sig, s); })) != hipSuccess)

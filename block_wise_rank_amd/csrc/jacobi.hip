@@ -44,8 +44,12 @@
 // are tracked unscaled, g = s_p s_q G_pq).
 //
 // Pairs whose rotation is the identity (already orthogonal to tolerance) skip
-// their LDS traffic, so late sweeps cost little; a sweep without any rotation
-// ends the solve.  Diagonal entries are never stored in G.
+// their LDS traffic, so late sweeps cost little.  Cyclic Jacobi converges
+// quadratically once the off-diagonal part is small (Golub & Van Loan sec. 8.5.3):
+// a sweep whose every relative off-diagonal |g| / sqrt|a b| was at most
+// stop_tol leaves them near stop_tol^2, so with stop_tol = sqrt(tol) such a
+// sweep ends the solve without the sweep that would only confirm it.
+// Diagonal entries are never stored in G.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -66,7 +70,8 @@ static_assert(kLdsBytes <= 80 * 1024, "two workgroups per CU");
 static_assert(kPerLane == 5, "generic block slots per lane");
 
 // G's cells below and on the diagonal are free and hold small tables:
-//  * the two convergence flags (by sweep parity) at row 2, columns 0 and 1;
+//  * the two convergence flags (by sweep parity: a rotation above stop_tol
+//    happened) at row 2, columns 0 and 1;
 //  * the scales by matrix index, gathered at renormalisation, on the diagonal
 //    (index 127's diagonal cell lies past the triangle: row 3, column 0);
 //  * per pair and buffer, (new diagonal of the first and second index, their
@@ -175,7 +180,7 @@ __device__ __forceinline__ Rot jacobi_rotation(float a, float b, float g, float 
 __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__restrict__ gpart, int splits,
                                                              float *__restrict__ vt_out,
                                                              int32_t *__restrict__ sweeps_out,
-                                                             int max_sweeps, float tol) {
+                                                             int max_sweeps, float tol, float stop_tol) {
     extern __shared__ __align__(16) float smem[];
     float *G = smem;
     int *flags = reinterpret_cast<int *>(smem + kFlagWord);                   // [2] by sweep parity
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
         *reinterpret_cast<float4 *>(G + rec_word(0, lane)) = make_float4(r.na, r.nb, r.c, r.c);
         if (r.rot) {
             G[x * kGP + y] = 0.f;
-            flags[0] = 1;
+            if (g * g > stop_tol * stop_tol * fabsf(a * b)) flags[0] = 1;
         }
     }
 
@@ -317,7 +322,8 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                 const float bn = Pn == 0 ? DB.x : DA.y;
                 const float sfa = Pn == 0 ? DA.z : (Pn == 63 ? DB.w : DB.z);
                 const float sfb = Pn == 0 ? DB.z : DA.w;
-                Rot r = jacobi_rotation(an, bn, gn * sfa * sfb, tol);
+                const float gt = gn * sfa * sfb;
+                Rot r = jacobi_rotation(an, bn, gt, tol);
                 const int kn = last_round ? 0 : k + 1;
                 float s1 = sfa, s2 = sfb;
                 if (renorm) {  // uniform: the scales are gathered by index and restart at 1
@@ -343,7 +349,8 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                 } else if (r.rot) {
                     G[asel] = 0.f;
                 }
-                if (r.rot) flags[(sweep + (last_round ? 1 : 0)) & 1] = 1;
+                if (r.rot && gt * gt > stop_tol * stop_tol * fabsf(an * bn))
+                    flags[(sweep + (last_round ? 1 : 0)) & 1] = 1;
             }
 
 
@@ -443,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
 }  // namespace
 
 hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt, int32_t *sweeps,
-                         int max_sweeps, float tol, hipStream_t st) {
+                         int max_sweeps, float tol, float stop_tol, hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(jacobi_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
@@ -453,7 +460,7 @@ hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt
     constexpr int kTabThreads = 127 * kGenLanes * kPerLane;
     hipLaunchKernelGGL(jacobi_table_kernel, dim3((kTabThreads + 255) / 256), dim3(256), 0, st);
     hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), kLdsBytes, st,
-                       gpart, splits, vt, sweeps, max_sweeps, tol);
+                       gpart, splits, vt, sweeps, max_sweeps, tol, stop_tol);
     return hipGetLastError();
 }
 

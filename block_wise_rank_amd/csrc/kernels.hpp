@@ -16,10 +16,12 @@ hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t r
                        int block_len, int n_blocks, int splits, float *gpart, hipStream_t st);
 
 // Symmetric eigensolve of G_b (sum of the partials) by parallel-order cyclic
-// Jacobi in LDS.  vt[b][i][:] = eigenvector i (unsorted); sweeps[b] = sweeps
-// used (negative when max_sweeps was hit).  sweeps may be null.
+// Jacobi in LDS.  Pairs with |g| <= tol sqrt|a b| are not rotated; the solve
+// ends after a sweep with no rotation above stop_tol.  vt[b][i][:] = eigenvector
+// i (unsorted); sweeps[b] = sweeps used (negative when max_sweeps was hit).
+// sweeps may be null.
 hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt,
-                         int32_t *sweeps, int max_sweeps, float tol, hipStream_t st);
+                         int32_t *sweeps, int max_sweeps, float tol, float stop_tol, hipStream_t st);
 
 // sigma_i = ||X_b v_i|| in fp32-accurate arithmetic, then eigenvectors sorted
 // by descending sigma (in place in vt) with the largest-magnitude entry of each
