@@ -39,6 +39,25 @@ def _p(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name: str, dtype=None, numel: int | None = None, optional: bool = False,
+          contiguous: bool = True):
+    """Marshalling check of a device tensor handed to the library as a plain
+    pointer: on a GPU, contiguous, of the element type the C ABI reads, and
+    holding at least the elements the call will read or write."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {numel}")
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -162,6 +181,12 @@ def milo_compress_blocks(x: torch.Tensor, pool_ptr, budget, eps2: float, sigma_o
         n_blocks, block_len, d = x.shape
         row_stride = d
     d = factors.head_dim
+    _need(x, "x", contiguous=row0 is None)  # with row0 the rows are addressed explicitly
+    _need(row0, "row0", torch.int64, int(n_blocks), optional=True)
+    _need(sigma_out, "sigma_out", torch.float32, int(n_blocks) * d)
+    _need(objective_out, "objective_out", torch.float64, len(pool_ptr) - 1, optional=True)
+    _need(sweeps_out, "sweeps_out", torch.int32, int(n_blocks), optional=True)
+    _need(workspace, "workspace", torch.uint8, optional=True)
     blocks = C.milo_blocks(_p(x), _dtype_code(x.dtype), _p(row0), int(row_stride), int(n_blocks),
                            int(block_len), int(d))
     fs = factors.struct()
@@ -185,6 +210,10 @@ def milo_allocate_ranks(sigma: torch.Tensor, max_rank: int, pool_ptr, budget, ep
                         rank_out: torch.Tensor, objective_out: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, stream=None) -> None:
     n_blocks, d = sigma.shape
+    _need(sigma, "sigma", torch.float32)
+    _need(rank_out, "rank_out", torch.int32, n_blocks)
+    _need(objective_out, "objective_out", torch.float64, len(pool_ptr) - 1, optional=True)
+    _need(workspace, "workspace", torch.uint8, optional=True)
     pp = _host_i32(pool_ptr)
     bb = _host_i64(budget)
     wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel())
@@ -202,6 +231,8 @@ def milo_allocate_ranks(sigma: torch.Tensor, max_rank: int, pool_ptr, budget, ep
 
 def milo_reconstruct(factors: Factors, block_ids: torch.Tensor, out: torch.Tensor,
                      stream=None) -> None:
+    _need(block_ids, "block_ids", torch.int32)
+    _need(out, "out", None, block_ids.numel() * factors.block_len * factors.head_dim)
     fs = factors.struct()
     st = lib().milo_reconstruct(ctypes.byref(fs), _p(block_ids), int(block_ids.numel()), _p(out),
                                 _dtype_code(out.dtype), _stream(stream))
@@ -217,6 +248,16 @@ def milo_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: F
                           softmax_scale: float | None = None, split_len: int = 0,
                           workspace: torch.Tensor | None = None, stream=None) -> None:
     batch, n_q, d = q.shape
+    _need(q, "q")
+    _need(q_pos, "q_pos", torch.int64, batch)
+    _need(out, "out", None, batch * n_q * d)
+    _need(sel_ptr, "sel_ptr", torch.int32, batch + 1, optional=True)
+    _need(sel_blk, "sel_blk", torch.int32, optional=True)
+    _need(tail_k, "tail_k", None, optional=True)
+    _need(tail_v, "tail_v", None, optional=True)
+    _need(tail_len, "tail_len", torch.int32, batch, optional=tail_k is None)
+    _need(tail_pos0, "tail_pos0", torch.int64, batch, optional=tail_k is None)
+    _need(workspace, "workspace", torch.uint8, optional=True)
     ks, vs = k.struct(), v.struct()
     tail_cap = 0 if tail_k is None else int(tail_k.shape[2])
     args = C.milo_decode_args(
