@@ -447,15 +447,15 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
         const int64_t units = static_cast<int64_t>(a->batch) * a->n_kv_heads *
                               (a->sel_ptr ? a->sel_max : a->blocks_per_seq);
         split = 128;
-        for (int c = 1024; c > 128; c /= 2)
+        for (int c = 2048; c > 128; c /= 2)
             if (T % c == 0 && units * (T / c) >= 1024 &&
                 milo::decode_split_fits(ftype, ttype, tail, G, c)) {
                 split = c;
                 break;
             }
     }
-    if (split < 128 || split % 128 != 0 || T % split != 0 || split > 1024)
-        return fail(MILO_E_UNSUPPORTED, "split_len must be a multiple of 128, at most 1024, dividing block_len");
+    if (split < 128 || split % 128 != 0 || T % split != 0 || split > 32 * milo::kMaxTiles)
+        return fail(MILO_E_UNSUPPORTED, "split_len must be a multiple of 128, at most 2048, dividing block_len");
     if (!milo::decode_split_fits(ftype, ttype, tail, G, split))
         return fail(MILO_E_UNSUPPORTED, "split_len %d needs more LDS than a workgroup has for %d query heads per KV head", split, G);
 

@@ -74,11 +74,11 @@ struct LdsLayout {
     int total;
 };
 
-__host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool tail) {
+__host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool tail, int G) {
     LdsLayout L;
     L.ang = 0;
     L.qs = align16(L.ang + 64 * 8);
-    L.bk = align16(L.qs + 16 * kQP * 4);
+    L.bk = align16(L.qs + G * kQP * 4);  // the G query heads (lanes n >= G reuse head G - 1)
     L.rope = align16(L.bk + (tail ? 0 : ns * 8 * 4 * 64 * 16));
     L.base = align16(L.rope + 32 * kRP * 8);
     L.stage = align16(L.base + n_tiles * 64 * 8);
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     extern __shared__ __align__(16) uint8_t lds[];
     const int G = p.group;
     const int n_tiles = p.split_len / kTile;
-    const LdsLayout L = lds_layout(F, NS, n_tiles, TAIL);
+    const LdsLayout L = lds_layout(F, NS, n_tiles, TAIL, G);
     float2 *ang = reinterpret_cast<float2 *>(lds + L.ang);
     const float2 *rope = reinterpret_cast<const float2 *>(lds + L.rope);
     const float2 *basetab = reinterpret_cast<const float2 *>(lds + L.base);
@@ -346,7 +346,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     {
         float *qw = reinterpret_cast<float *>(lds + L.qs);
         const int e0 = 4 * tid;
-        *reinterpret_cast<float4 *>(qw + (e0 >> 7) * kQP + (e0 & 127)) = make_float4(qv[0], qv[1], qv[2], qv[3]);
+        if (e0 < G * kD)
+            *reinterpret_cast<float4 *>(qw + (e0 >> 7) * kQP + (e0 & 127)) = make_float4(qv[0], qv[1], qv[2], qv[3]);
         float2 *rw = reinterpret_cast<float2 *>(lds + L.rope);
         const int r0 = 2 * tid, r1 = 2 * (tid + kThreads);
         *reinterpret_cast<float4 *>(rw + (r0 >> 6) * kRP + (r0 & 63)) = rope_v;
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     }
     __syncthreads();  // tables, fragments; the staging area is free again
     // Lane (c, n) owns query head n: column n of every accumulator.
-    const float *qrow = reinterpret_cast<const float *>(lds + L.qs) + ln * kQP;
+    const float *qrow = reinterpret_cast<const float *>(lds + L.qs) + min(ln, G - 1) * kQP;
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4_t u[8];
@@ -859,7 +860,7 @@ __global__ __launch_bounds__(256) void decode_tables_kernel(double rope_base, do
 template <int F, bool TAIL>
 hipError_t launch_partial(const DecodeParams &p, dim3 grid, hipStream_t st) {
     constexpr int NS = (F == kF32) ? 2 : 1;
-    const LdsLayout L = lds_layout(F, NS, p.split_len / kTile, TAIL);
+    const LdsLayout L = lds_layout(F, NS, p.split_len / kTile, TAIL, p.group);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_partial_kernel<F, TAIL>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
     if (e != hipSuccess) return e;
@@ -870,12 +871,11 @@ hipError_t launch_partial(const DecodeParams &p, dim3 grid, hipStream_t st) {
 }  // namespace
 
 bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int split) {
-    (void)G;
     const int ns = f_type == kF32 ? 2 : 1;
-    if (lds_layout(f_type, ns, split / kTile, false).total > kMaxLds) return false;
+    if (lds_layout(f_type, ns, split / kTile, false, G).total > kMaxLds) return false;
     if (has_tail) {
         const int tns = tail_type == kF32 ? 2 : 1;
-        if (lds_layout(tail_type, tns, split / kTile, true).total > kMaxLds) return false;
+        if (lds_layout(tail_type, tns, split / kTile, true, G).total > kMaxLds) return false;
     }
     return true;
 }

@@ -204,9 +204,11 @@ typedef struct milo_decode_args {
     float softmax_scale;      /* e.g. 1/sqrt(head_dim)                                   */
     void *out;                /* device [batch][n_q_heads][head_dim]                    */
     milo_dtype out_dtype;     /* MILO_F32 or MILO_BF16                                  */
-    int32_t split_len;        /* tokens per work split: multiple of 128, at most 1024,   */
-                              /* dividing block_len; 0 picks the longest split that     */
-                              /* still gives >= 1024 workgroups (else 128)              */
+    int32_t split_len;        /* tokens per work split: multiple of 128, at most 2048,   */
+                              /* dividing block_len, whose workgroup fits the LDS for   */
+                              /* the call's query heads per KV head; 0 picks the        */
+                              /* longest such split that still gives >= 1024            */
+                              /* workgroups (else 128)                                  */
     void *workspace;          /* device scratch: per-split partial results and the     */
                               /* RoPE tables of the call (256-byte aligned)             */
     size_t workspace_bytes;

@@ -111,6 +111,47 @@ def test_kernel_level_selection_and_tail(storage):
         _check(got, ref, vmax, storage, f"sel+tail {storage} split {split}")
 
 
+@pytest.mark.parametrize("storage", ["bf16", "f32", "i8"])
+def test_kernel_level_long_blocks(storage):
+    """2048-token blocks with the longest split (one workgroup per block, 64 tiles)
+    and a shorter one; GQA 8:1, ranks 0, 128 and ragged."""
+    batch, hkv, hq, T, bps, d = 1, 2, 16, 2048, 3, 128
+    n = batch * hkv * bps
+    ranks = np.array([0, 128, 45, 96, 1, 77])
+    kt, kA, kB = random_factor_set(n, T, d, storage, seed=41, ranks=ranks)
+    vt, vA, vB = random_factor_set(n, T, d, storage, seed=42, ranks=ranks[::-1].copy())
+    kf, vf = _factors_on_gpu(kt, storage, n, T), _factors_on_gpu(vt, storage, n, T)
+    q = torch.randn((batch, hq, d), generator=torch.Generator().manual_seed(6), dtype=torch.float64) * 10
+    qd = q.to(torch.float32 if storage == "f32" else torch.bfloat16)
+    q_pos = torch.tensor([bps * T + 5], dtype=torch.int64)
+    Kh, Vh = _recon(kA, kB), _recon(vA, vB)
+    ref = oracle.decode(qd.to(torch.float64).numpy(), q_pos.numpy(), Kh, Vh, T, hkv, bps)
+    vmax = max(np.abs(v).max() for v in Vh)
+    for split in [2048, 1024, 0]:
+        got = _run(qd.to(DEV), q_pos.to(DEV), kf, vf, bps, hkv, split_len=split).cpu().numpy()
+        _check(got, ref, vmax, storage, f"{storage} T=2048 split {split}")
+
+
+def test_split_beyond_lds_is_rejected():
+    """16 query heads per KV head do not fit a 2048-token bf16 split: the call is
+    refused before anything is enqueued, and the default split still works."""
+    from block_wise_rank_amd import MiloError
+    T, d = 2048, 128
+    kt, _, _ = random_factor_set(1, T, d, "bf16", seed=51, ranks=np.array([64]))
+    vt, _, _ = random_factor_set(1, T, d, "bf16", seed=52, ranks=np.array([64]))
+    kf, vf = _factors_on_gpu(kt, "bf16", 1, T), _factors_on_gpu(vt, "bf16", 1, T)
+    q = torch.randn((1, 16, d), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).to(DEV)
+    q_pos = torch.tensor([T], dtype=torch.int64, device=DEV)
+    out = torch.full((1, 16, d), 7.0, device=DEV)
+    with pytest.raises(MiloError):
+        milo_decode_attention(q, q_pos, kf, vf, 1, 1, out, split_len=2048)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    milo_decode_attention(q, q_pos, kf, vf, 1, 1, out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+
+
 def test_decode_is_deterministic():
     batch, hkv, hq, T, bps, d = 1, 2, 16, 512, 4, 128
     n = batch * hkv * bps
