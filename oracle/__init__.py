@@ -69,6 +69,13 @@ def load(path: str):
     L.oracle_allocate.restype = ctypes.c_int64
     L.oracle_objective.argtypes = [_dp, ctypes.c_int, ctypes.c_int, _ip, ctypes.c_double]
     L.oracle_objective.restype = ctypes.c_double
+    L.oracle_allocate_uniform.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, _ip]
+    L.oracle_allocate_uniform.restype = ctypes.c_int64
+    L.oracle_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    L.oracle_splitmix64.restype = ctypes.c_uint64
+    L.oracle_allocate_random.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
+                                         ctypes.c_int, _ip]
+    L.oracle_allocate_random.restype = ctypes.c_int64
     L.oracle_project.argtypes = [_dp, ctypes.c_int, ctypes.c_int, _dp, ctypes.c_int, _dp, _dp]
     L.oracle_project.restype = None
     L.oracle_reconstruct.argtypes = [_dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp]
@@ -137,6 +144,36 @@ def allocate(sigma, R: int, eps2: float, k: int | None = None):
     given = lib().oracle_allocate(_ptr(sigma), n, kk, int(R), float(eps2), _ptr(rank, _ip),
                                   ctypes.byref(obj))
     return rank, float(obj.value), int(given)
+
+
+POLICIES = ("entropy", "uniform", "random")
+
+
+def allocate_policy(sigma, R: int, eps2: float, policy: str = "entropy", seed: int = 0,
+                    pool: int = 0):
+    """Allocation of one pool under `policy`: "entropy" is the greedy of
+    ``allocate``; "uniform" and "random" are the equal-budget comparisons
+    (oracle_allocate_uniform / oracle_allocate_random).  Returns (rank, objective)."""
+    sigma = _f64(sigma)
+    n, k = sigma.shape
+    if policy == "entropy":
+        r, obj, _ = allocate(sigma, R, eps2)
+        return r, obj
+    rank = np.zeros(n, dtype=np.int32)
+    if policy == "uniform":
+        lib().oracle_allocate_uniform(n, k, int(R), _ptr(rank, _ip))
+    elif policy == "random":
+        got = lib().oracle_allocate_random(n, k, int(R), ctypes.c_uint64(seed & (2**64 - 1)), int(pool),
+                                           _ptr(rank, _ip))
+        if got < 0:
+            raise MemoryError("oracle_allocate_random")
+    else:
+        raise ValueError(policy)
+    return rank, objective(sigma, rank, eps2)
+
+
+def splitmix64(seed: int, c: int) -> int:
+    return int(lib().oracle_splitmix64(ctypes.c_uint64(seed & (2**64 - 1)), ctypes.c_uint64(c)))
 
 
 def objective(sigma, rank, eps2: float) -> float:
@@ -262,7 +299,7 @@ class Compressed:
 
 
 def compress(X, pool_ptr, budgets, eps2: float, storage: str, max_sweeps: int = 60,
-             svd=None) -> Compressed:
+             svd=None, policy: str = "entropy", seed: int = 0) -> Compressed:
     """Steps 1-3 for every block.  pool_ptr is the CSR over blocks: pool p holds
     blocks [pool_ptr[p], pool_ptr[p+1]) and gets budget budgets[p].  ``svd`` may
     pass the result of an earlier ``svd_blocks(X)`` to avoid recomputing it."""
@@ -274,7 +311,7 @@ def compress(X, pool_ptr, budgets, eps2: float, storage: str, max_sweeps: int = 
     objs = []
     for p in range(len(pool_ptr) - 1):
         lo, hi = int(pool_ptr[p]), int(pool_ptr[p + 1])
-        r, obj, _ = allocate(sigma[lo:hi, :k], int(budgets[p]), eps2)
+        r, obj = allocate_policy(sigma[lo:hi, :k], int(budgets[p]), eps2, policy, seed, p)
         rank[lo:hi] = r
         objs.append(obj)
     out = Compressed(sigma=sigma, V=V, rank=rank, objective=objs, sweeps=sweeps)

@@ -28,6 +28,12 @@
  *                       singular value brings the largest marginal gain
  *                       log(1 + sigma^2 / eps^2), until the global rank budget
  *                       is spent.
+ *   oracle_allocate_uniform / oracle_allocate_random
+ *                       the equal-budget allocations the greedy is compared
+ *                       with ([REV] Strengths, on Fig. 5(d)): ranks spread
+ *                       evenly over the pool's blocks, or the budget's ranks
+ *                       placed on (block, index) slots drawn uniformly at
+ *                       random without replacement (keys from SplitMix64).
  *   oracle_project      the per-block factor pair A = X V_r, B = V_r^T: the cache
  *                       is kept per block in low-rank form ([REV] FAQ).
  *   oracle_round_bf16 / oracle_quant_int8_rows
@@ -242,6 +248,82 @@ double oracle_objective(const double *sigma, int n, int k, const int32_t *rank, 
             obj += log1p(s * s / eps2);
         }
     return obj;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Equal-budget comparison allocations ([REV] Strengths: Fig. 5(d) compares  */
+/* the greedy with uniform and random allocation at the same budget).  Both  */
+/* hand out R' = min(R, n*k) ranks.                                          */
+/*                                                                           */
+/* Uniform: block j gets floor(R'/n), and one more when j < R' mod n.        */
+/* ------------------------------------------------------------------------- */
+int64_t oracle_allocate_uniform(int n, int k, int64_t R, int32_t *rank)
+{
+    int64_t cap = (int64_t)n * k;
+    int64_t Rp = R < cap ? R : cap;
+    if (n == 0)
+        return 0;
+    for (int j = 0; j < n; ++j)
+        rank[j] = (int32_t)(Rp / n + (j < Rp % n ? 1 : 0));
+    return Rp;
+}
+
+/* SplitMix64 (Steele, Lea & Flood, OOPSLA 2014; the finaliser is Stafford's */
+/* "variant 13"): the c-th output (c >= 1) of the generator seeded with s is */
+/* mix(s + c * 0x9E3779B97F4A7C15).                                          */
+uint64_t oracle_splitmix64(uint64_t seed, uint64_t c)
+{
+    uint64_t z = seed + c * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* Random: slot (j, i) of pool p (block j of the pool, index i < k) has the  */
+/* key = high 32 bits of output number 1 + (p << 32 | j << 8 | i) of the     */
+/* generator seeded with `seed`.  The R' slots with the largest keys are     */
+/* taken (equal keys: smaller block, then smaller index, first); r_j counts  */
+/* block j's slots.  With distinct keys this is a uniformly random R'-subset */
+/* of the n*k slots.                                                         */
+typedef struct {
+    uint32_t key;
+    int32_t block, index;
+} oracle_slot;
+
+static int slot_order(const void *a, const void *b)
+{
+    const oracle_slot *x = (const oracle_slot *)a, *y = (const oracle_slot *)b;
+    if (x->key != y->key)
+        return x->key > y->key ? -1 : 1;
+    if (x->block != y->block)
+        return x->block < y->block ? -1 : 1;
+    return x->index < y->index ? -1 : (x->index > y->index);
+}
+
+int64_t oracle_allocate_random(int n, int k, int64_t R, uint64_t seed, int pool, int32_t *rank)
+{
+    int64_t cap = (int64_t)n * k;
+    int64_t Rp = R < cap ? R : cap;
+    for (int j = 0; j < n; ++j)
+        rank[j] = 0;
+    if (cap == 0)
+        return 0;
+    oracle_slot *slots = (oracle_slot *)malloc(sizeof(oracle_slot) * (size_t)cap);
+    if (!slots)
+        return -1;
+    for (int j = 0; j < n; ++j)
+        for (int i = 0; i < k; ++i) {
+            uint64_t c = ((uint64_t)(uint32_t)pool << 32) | ((uint64_t)j << 8) | (uint64_t)i;
+            oracle_slot *sl = &slots[(size_t)j * k + i];
+            sl->key = (uint32_t)(oracle_splitmix64(seed, c + 1) >> 32);
+            sl->block = j;
+            sl->index = i;
+        }
+    qsort(slots, (size_t)cap, sizeof(oracle_slot), slot_order);
+    for (int64_t t = 0; t < Rp; ++t)
+        rank[slots[t].block] += 1;
+    free(slots);
+    return Rp;
 }
 
 /* ------------------------------------------------------------------------- */

@@ -15,6 +15,7 @@ import oracle
 import test_oracle_alloc as PA
 import test_oracle_attention as PT
 import test_oracle_factors as PF
+import test_oracle_policies as PP
 import test_oracle_svd as PS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "milo_oracle.c")
@@ -59,6 +60,11 @@ MUTATIONS = [
      lambda: PT.test_attention_matches_torch_sdpa(oracle)),
     ("key rotated at the query position", "oracle_rope(kr, d, (double)pos[t], base);",
      "oracle_rope(kr, d, (double)q_pos, base);", lambda: PT.test_attention_matches_torch_sdpa(oracle)),
+    ("splitmix64 first shift", "z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;",
+     "z = (z ^ (z >> 31)) * 0xBF58476D1CE4E5B9ull;", lambda: PP.test_splitmix64_reference_output()),
+    ("uniform remainder to the last blocks", "rank[j] = (int32_t)(Rp / n + (j < Rp % n ? 1 : 0));",
+     "rank[j] = (int32_t)(Rp / n + (j >= n - Rp % n ? 1 : 0));",
+     lambda: PP.test_uniform_is_the_greedy_on_identical_spectra(5, 8, 17)),
 ]
 
 
