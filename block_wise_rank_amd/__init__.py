@@ -12,8 +12,10 @@ from .binding import (  # noqa: F401
     decode_workspace_bytes,
     milo_abi_version,
     milo_allocate_ranks,
+    milo_allocate_ranks_ex,
     milo_arena_bytes,
     milo_compress_blocks,
+    milo_compress_blocks_ex,
     milo_compress_workspace_bytes,
     milo_decode_attention,
     milo_profile_enable,
@@ -24,6 +26,7 @@ from . import _capi  # noqa: F401
 
 __all__ = [
     "Factors", "MiloError", "decode_workspace_bytes", "milo_abi_version", "milo_allocate_ranks",
-    "milo_arena_bytes", "milo_compress_blocks", "milo_compress_workspace_bytes",
+    "milo_allocate_ranks_ex", "milo_arena_bytes", "milo_compress_blocks", "milo_compress_blocks_ex",
+    "milo_compress_workspace_bytes",
     "milo_decode_attention", "milo_profile_enable", "milo_profile_read", "milo_reconstruct",
 ]

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmilo.so"
 
 MILO_OK, MILO_E_INVALID, MILO_E_UNSUPPORTED, MILO_E_WORKSPACE, MILO_E_HIP = range(5)
 MILO_F32, MILO_BF16, MILO_I8 = 0, 1, 2
+MILO_ALLOC_ENTROPY, MILO_ALLOC_UNIFORM, MILO_ALLOC_RANDOM = 0, 1, 2
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -29,6 +30,10 @@ class milo_factors(ctypes.Structure):
                 ("head_dim", _i32), ("rank", _vp), ("a_off", _vp), ("b_off", _vp),
                 ("arena", _vp), ("arena_bytes", ctypes.c_size_t), ("a_scale", _vp),
                 ("b_scale", _vp)]
+
+
+class milo_alloc_options(ctypes.Structure):
+    _fields_ = [("policy", ctypes.c_int), ("seed", ctypes.c_uint64)]
 
 
 class milo_decode_args(ctypes.Structure):
@@ -48,8 +53,15 @@ SIGNATURES = {
     "milo_compress_blocks": (ctypes.c_int, [ctypes.POINTER(milo_blocks), _vp, _i32, _vp,
                                             ctypes.c_double, _vp, _vp, ctypes.POINTER(milo_factors),
                                             _vp, _vp, ctypes.POINTER(ctypes.c_size_t), _vp]),
+    "milo_compress_blocks_ex": (ctypes.c_int, [ctypes.POINTER(milo_blocks), _vp, _i32, _vp,
+                                               ctypes.c_double, _vp, _vp, ctypes.POINTER(milo_factors),
+                                               _vp, ctypes.POINTER(milo_alloc_options), _vp,
+                                               ctypes.POINTER(ctypes.c_size_t), _vp]),
     "milo_allocate_ranks": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _i32, _vp, ctypes.c_double,
                                            _vp, _vp, _vp, ctypes.POINTER(ctypes.c_size_t), _vp]),
+    "milo_allocate_ranks_ex": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _i32, _vp, ctypes.c_double,
+                                              _vp, _vp, ctypes.POINTER(milo_alloc_options), _vp,
+                                              ctypes.POINTER(ctypes.c_size_t), _vp]),
     "milo_reconstruct": (ctypes.c_int, [ctypes.POINTER(milo_factors), _vp, _i32, _vp,
                                         ctypes.c_int, _vp]),
     "milo_decode_attention": (ctypes.c_int, [ctypes.POINTER(milo_decode_args),

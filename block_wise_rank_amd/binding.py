@@ -169,6 +169,14 @@ def milo_compress_workspace_bytes(n_blocks: int, block_len: int, head_dim: int =
     return int(lib().milo_compress_workspace_bytes(n_blocks, block_len, head_dim))
 
 
+_POLICY = {None: None, "entropy": 0, "uniform": 1, "random": 2}
+
+
+def _alloc_options(policy, seed):
+    code = _POLICY[policy]
+    return None if code is None else ctypes.byref(C.milo_alloc_options(code, int(seed) & (2**64 - 1)))
+
+
 def milo_compress_blocks(x: torch.Tensor, pool_ptr, budget, eps2: float, sigma_out: torch.Tensor,
                          factors: Factors, objective_out: torch.Tensor | None = None,
                          sweeps_out: torch.Tensor | None = None,
@@ -177,6 +185,19 @@ def milo_compress_blocks(x: torch.Tensor, pool_ptr, budget, eps2: float, sigma_o
                          block_len: int | None = None, stream=None) -> None:
     """Compress blocks of ``x``: a contiguous [n_blocks, T, d] tensor, or any tensor
     addressed through ``row0``/``row_stride`` (with n_blocks and block_len given)."""
+    milo_compress_blocks_ex(x, pool_ptr, budget, eps2, sigma_out, factors, objective_out, sweeps_out,
+                            None, 0, workspace, row0, row_stride, n_blocks, block_len, stream)
+
+
+def milo_compress_blocks_ex(x: torch.Tensor, pool_ptr, budget, eps2: float, sigma_out: torch.Tensor,
+                            factors: Factors, objective_out: torch.Tensor | None = None,
+                            sweeps_out: torch.Tensor | None = None, policy: str | None = None,
+                            seed: int = 0, workspace: torch.Tensor | None = None,
+                            row0: torch.Tensor | None = None, row_stride: int | None = None,
+                            n_blocks: int | None = None, block_len: int | None = None,
+                            stream=None) -> None:
+    """milo_compress_blocks with the rank allocation policy "entropy" (the
+    default), "uniform" or "random" (seeded)."""
     if row0 is None and row_stride is None:
         n_blocks, block_len, d = x.shape
         row_stride = d
@@ -193,22 +214,31 @@ def milo_compress_blocks(x: torch.Tensor, pool_ptr, budget, eps2: float, sigma_o
     pp = _host_i32(pool_ptr)
     bb = _host_i64(budget)
     wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel())
-    st = lib().milo_compress_blocks(ctypes.byref(blocks), ctypes.cast(pp, ctypes.c_void_p),
-                                    len(pool_ptr) - 1, ctypes.cast(bb, ctypes.c_void_p),
-                                    float(eps2), _p(sigma_out), _p(objective_out),
-                                    ctypes.byref(fs), _p(sweeps_out), _p(workspace),
-                                    ctypes.byref(wsb), _stream(stream))
+    st = lib().milo_compress_blocks_ex(ctypes.byref(blocks), ctypes.cast(pp, ctypes.c_void_p),
+                                       len(pool_ptr) - 1, ctypes.cast(bb, ctypes.c_void_p),
+                                       float(eps2), _p(sigma_out), _p(objective_out),
+                                       ctypes.byref(fs), _p(sweeps_out), _alloc_options(policy, seed),
+                                       _p(workspace), ctypes.byref(wsb), _stream(stream))
     if st == C.MILO_E_WORKSPACE and workspace is None:
         workspace = torch.empty(int(wsb.value), dtype=torch.uint8, device=x.device)
-        return milo_compress_blocks(x, pool_ptr, budget, eps2, sigma_out, factors, objective_out,
-                                    sweeps_out, workspace, row0, row_stride, n_blocks, block_len,
-                                    stream)
+        return milo_compress_blocks_ex(x, pool_ptr, budget, eps2, sigma_out, factors, objective_out,
+                                       sweeps_out, policy, seed, workspace, row0, row_stride,
+                                       n_blocks, block_len, stream)
     _check(st)
 
 
 def milo_allocate_ranks(sigma: torch.Tensor, max_rank: int, pool_ptr, budget, eps2: float,
                         rank_out: torch.Tensor, objective_out: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, stream=None) -> None:
+    milo_allocate_ranks_ex(sigma, max_rank, pool_ptr, budget, eps2, rank_out, objective_out, None, 0,
+                           workspace, stream)
+
+
+def milo_allocate_ranks_ex(sigma: torch.Tensor, max_rank: int, pool_ptr, budget, eps2: float,
+                           rank_out: torch.Tensor, objective_out: torch.Tensor | None = None,
+                           policy: str | None = None, seed: int = 0,
+                           workspace: torch.Tensor | None = None, stream=None) -> None:
+    """milo_allocate_ranks with the policy "entropy" (default), "uniform" or "random"."""
     n_blocks, d = sigma.shape
     _need(sigma, "sigma", torch.float32)
     _need(rank_out, "rank_out", torch.int32, n_blocks)
@@ -217,15 +247,15 @@ def milo_allocate_ranks(sigma: torch.Tensor, max_rank: int, pool_ptr, budget, ep
     pp = _host_i32(pool_ptr)
     bb = _host_i64(budget)
     wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel())
-    st = lib().milo_allocate_ranks(_p(sigma), n_blocks, d, int(max_rank),
-                                   ctypes.cast(pp, ctypes.c_void_p), len(pool_ptr) - 1,
-                                   ctypes.cast(bb, ctypes.c_void_p), float(eps2), _p(rank_out),
-                                   _p(objective_out), _p(workspace), ctypes.byref(wsb),
-                                   _stream(stream))
+    st = lib().milo_allocate_ranks_ex(_p(sigma), n_blocks, d, int(max_rank),
+                                      ctypes.cast(pp, ctypes.c_void_p), len(pool_ptr) - 1,
+                                      ctypes.cast(bb, ctypes.c_void_p), float(eps2), _p(rank_out),
+                                      _p(objective_out), _alloc_options(policy, seed), _p(workspace),
+                                      ctypes.byref(wsb), _stream(stream))
     if st == C.MILO_E_WORKSPACE and workspace is None:
         workspace = torch.empty(int(wsb.value), dtype=torch.uint8, device=sigma.device)
-        return milo_allocate_ranks(sigma, max_rank, pool_ptr, budget, eps2, rank_out,
-                                   objective_out, workspace, stream)
+        return milo_allocate_ranks_ex(sigma, max_rank, pool_ptr, budget, eps2, rank_out,
+                                      objective_out, policy, seed, workspace, stream)
     _check(st)
 
 

@@ -16,11 +16,41 @@
 // Exact integer work on fp32 keys: the ranks do not depend on eps, and equal
 // the greedy's bit for bit.  One workgroup of 256 threads per pool; thread t
 // owns a contiguous run of blocks so prefix sums follow block order.
+//
+// The same selection serves the equal-budget comparisons the greedy is ablated
+// against (same review, Strengths, on Fig. 5(d)):
+//   uniform  block j of the pool gets floor(R'/n) ranks, one more if j < R' mod n;
+//   random   the R' (block, index) slots with the largest 32-bit keys, key =
+//            high half of SplitMix64 output 1 + (pool << 32 | j << 8 | i) for the
+//            caller's seed (Steele, Lea & Flood 2014, Stafford's finaliser 13):
+//            a uniformly random R'-subset of the slots; a block's rank is the
+//            number of its slots taken.  Keys are not sorted within a block, so
+//            they are counted by a scan instead of a binary search.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace milo {
 namespace {
+
+__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t c) {
+    uint64_t z = seed + c * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ uint32_t random_key(uint64_t seed, int pool, int j, int i) {
+    const uint64_t c = (static_cast<uint64_t>(static_cast<uint32_t>(pool)) << 32) |
+                       (static_cast<uint64_t>(j) << 8) | static_cast<uint64_t>(i);
+    return static_cast<uint32_t>(splitmix64(seed, c + 1) >> 32);
+}
+
+// Number of block j's random keys that are >= c.
+__device__ __forceinline__ int count_ge_random(uint64_t seed, int pool, int j, int k, uint32_t c) {
+    int n = 0;
+    for (int i = 0; i < k; ++i) n += random_key(seed, pool, j, i) >= c;
+    return n;
+}
 
 __device__ __forceinline__ uint32_t key_bits(float s) {
     const uint32_t u = __float_as_uint(s);
@@ -71,7 +101,8 @@ __global__ __launch_bounds__(256) void alloc_kernel(
     const float *__restrict__ sigma, int pitch, int k, const int32_t *__restrict__ pool_ptr,
     const int64_t *__restrict__ budget, const int64_t *__restrict__ pool_base, int pool_lo,
     int blk_lo, double eps2, int32_t *__restrict__ rank, double *__restrict__ objective,
-    int64_t *__restrict__ a_off, int64_t *__restrict__ b_off, int T, int elem_bytes) {
+    int64_t *__restrict__ a_off, int64_t *__restrict__ b_off, int T, int elem_bytes, int policy,
+    uint64_t seed) {
     __shared__ int64_t red64[4];
     __shared__ double redd[4];
     __shared__ int64_t scan_buf[256];
@@ -86,15 +117,21 @@ __global__ __launch_bounds__(256) void alloc_kernel(
     const int64_t cap = static_cast<int64_t>(n) * k;
     const int64_t R = budget[pool] < cap ? budget[pool] : cap;
 
+    const bool rnd = policy == kAllocRandom;
+    // keys of block b that are >= c
+    auto count = [&](int b, uint32_t c) {
+        return rnd ? count_ge_random(seed, pool, b - b_lo, k, c)
+                   : count_ge(sigma + static_cast<int64_t>(b - blk_lo) * pitch, k, c);
+    };
+
     // 1. tau = key of the R-th largest value (only needed when 0 < R < cap).
     uint32_t tau = 0;
-    const bool partial = R > 0 && R < cap;
+    const bool partial = R > 0 && R < cap && policy != kAllocUniform;
     if (partial) {
-        for (int bit = 30; bit >= 0; --bit) {
+        for (int bit = rnd ? 31 : 30; bit >= 0; --bit) {  // sigma keys have a clear sign bit
             const uint32_t cand = tau | (1u << bit);
             int64_t cnt = 0;
-            for (int b = my_lo; b < my_hi; ++b)
-                cnt += count_ge(sigma + static_cast<int64_t>(b - blk_lo) * pitch, k, cand);
+            for (int b = my_lo; b < my_hi; ++b) cnt += count(b, cand);
             cnt = block_sum<int64_t>(cnt, red64);
             if (cnt >= R) tau = cand;  // uniform decision
         }
@@ -103,10 +140,9 @@ __global__ __launch_bounds__(256) void alloc_kernel(
     // 2. ranks: strictly greater values, then ties in block order.
     int64_t gt_sum = 0, eq_sum = 0;
     for (int b = my_lo; b < my_hi; ++b) {
-        const float *row = sigma + static_cast<int64_t>(b - blk_lo) * pitch;
         if (partial) {
-            const int ge = count_ge(row, k, tau);
-            const int gt = tau == 0xffffffffu ? 0 : count_ge(row, k, tau + 1);
+            const int ge = count(b, tau);
+            const int gt = tau == 0xffffffffu ? 0 : count(b, tau + 1);
             gt_sum += gt;
             eq_sum += ge - gt;
         }
@@ -122,11 +158,14 @@ __global__ __launch_bounds__(256) void alloc_kernel(
     for (int b = my_lo; b < my_hi; ++b) {
         const float *row = sigma + static_cast<int64_t>(b - blk_lo) * pitch;
         int r;
-        if (!partial) {
+        if (policy == kAllocUniform) {
+            const int j = b - b_lo;
+            r = static_cast<int>(R / n + (j < R % n ? 1 : 0));
+        } else if (!partial) {
             r = R == 0 ? 0 : k;
         } else {
-            const int ge = count_ge(row, k, tau);
-            const int gt = tau == 0xffffffffu ? 0 : count_ge(row, k, tau + 1);
+            const int ge = count(b, tau);
+            const int gt = tau == 0xffffffffu ? 0 : count(b, tau + 1);
             int64_t extra = need - eq_before;
             extra = extra < 0 ? 0 : (extra > ge - gt ? ge - gt : extra);
             eq_before += ge - gt;
@@ -169,11 +208,12 @@ __global__ __launch_bounds__(256) void alloc_kernel(
 hipError_t launch_alloc(const float *sigma, int sigma_pitch, int max_rank, const int32_t *pool_ptr,
                         const int64_t *budget, const int64_t *pool_base, int pool_lo, int n_pools,
                         int blk_lo, double eps2, int32_t *rank, double *objective, int64_t *a_off,
-                        int64_t *b_off, int block_len, int elem_bytes, hipStream_t st) {
+                        int64_t *b_off, int block_len, int elem_bytes, int policy, uint64_t seed,
+                        hipStream_t st) {
     if (n_pools <= 0) return hipSuccess;
     hipLaunchKernelGGL(alloc_kernel, dim3(static_cast<unsigned>(n_pools)), dim3(256), 0, st, sigma,
                        sigma_pitch, max_rank, pool_ptr, budget, pool_base, pool_lo, blk_lo, eps2,
-                       rank, objective, a_off, b_off, block_len, elem_bytes);
+                       rank, objective, a_off, b_off, block_len, elem_bytes, policy, seed);
     return hipGetLastError();
 }
 

@@ -178,10 +178,32 @@ size_t milo_compress_workspace_bytes(int32_t n_blocks, int32_t block_len, int32_
     return tables_bytes(n_blocks) + chunk_bytes(n_blocks, block_len);
 }
 
+static milo_status read_policy(const milo_alloc_options *alloc, int *policy, uint64_t *seed) {
+    if (!alloc) return MILO_OK;
+    if (alloc->policy != MILO_ALLOC_ENTROPY && alloc->policy != MILO_ALLOC_UNIFORM &&
+        alloc->policy != MILO_ALLOC_RANDOM)
+        return fail(MILO_E_INVALID, "unknown allocation policy %d", static_cast<int>(alloc->policy));
+    *policy = static_cast<int>(alloc->policy);
+    *seed = alloc->seed;
+    return MILO_OK;
+}
+
 milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr, int32_t n_pools,
                                  const int64_t *budget, double eps2, float *sigma_out,
                                  double *objective_out, milo_factors *out, int32_t *sweeps_out,
                                  void *workspace, size_t *workspace_bytes, void *stream) {
+    return milo_compress_blocks_ex(in, pool_ptr, n_pools, budget, eps2, sigma_out, objective_out, out,
+                                   sweeps_out, nullptr, workspace, workspace_bytes, stream);
+}
+
+milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_ptr, int32_t n_pools,
+                                    const int64_t *budget, double eps2, float *sigma_out,
+                                    double *objective_out, milo_factors *out, int32_t *sweeps_out,
+                                    const milo_alloc_options *alloc, void *workspace,
+                                    size_t *workspace_bytes, void *stream) {
+    int policy = milo::kAllocEntropy;
+    uint64_t seed = 0;
+    if (milo_status st = read_policy(alloc, &policy, &seed); st != MILO_OK) return st;
     if (!in) return fail(MILO_E_INVALID, "in is NULL");
     if (!out) return fail(MILO_E_INVALID, "out is NULL");
     if (!workspace_bytes) return fail(MILO_E_INVALID, "workspace_bytes is NULL");
@@ -301,7 +323,7 @@ milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr,
             if ((e = timed("alloc", s, [&] {
                      return milo::launch_alloc(sig, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
                                                eps2, out->rank, objective_out, out->a_off, out->b_off, T,
-                                               fe, s);
+                                               fe, policy, seed, s);
                  })) != hipSuccess)
                 return hip_fail(e, "alloc launch");
             if ((e = timed("project", s, [&] {
@@ -315,7 +337,7 @@ milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr,
         } else {
             if ((e = milo::launch_alloc(sigma_out, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
                                         eps2, out->rank, objective_out, out->a_off, out->b_off, T, fe,
-                                        s)) != hipSuccess)
+                                        policy, seed, s)) != hipSuccess)
                 return hip_fail(e, "alloc launch");
         }
         p0 = p1;
@@ -328,6 +350,18 @@ milo_status milo_allocate_ranks(const float *sigma, int32_t n_blocks, int32_t he
                                 const int64_t *budget, double eps2, int32_t *rank_out,
                                 double *objective_out, void *workspace, size_t *workspace_bytes,
                                 void *stream) {
+    return milo_allocate_ranks_ex(sigma, n_blocks, head_dim, max_rank, pool_ptr, n_pools, budget, eps2,
+                                  rank_out, objective_out, nullptr, workspace, workspace_bytes, stream);
+}
+
+milo_status milo_allocate_ranks_ex(const float *sigma, int32_t n_blocks, int32_t head_dim,
+                                   int32_t max_rank, const int32_t *pool_ptr, int32_t n_pools,
+                                   const int64_t *budget, double eps2, int32_t *rank_out,
+                                   double *objective_out, const milo_alloc_options *alloc,
+                                   void *workspace, size_t *workspace_bytes, void *stream) {
+    int policy = milo::kAllocEntropy;
+    uint64_t seed = 0;
+    if (milo_status st = read_policy(alloc, &policy, &seed); st != MILO_OK) return st;
     if (head_dim <= 0) return fail(MILO_E_INVALID, "head_dim must be > 0");
     if (max_rank < 1 || max_rank > head_dim)
         return fail(MILO_E_INVALID, "max_rank must be in [1, head_dim] (got %d)", max_rank);
@@ -354,7 +388,7 @@ milo_status milo_allocate_ranks(const float *sigma, int32_t n_blocks, int32_t he
         return hip_fail(e, "pool table upload");
     e = timed("alloc", s, [&] {
         return milo::launch_alloc(sigma, head_dim, max_rank, d_pool_ptr, d_budget, nullptr, 0, n_pools, 0,
-                                  eps2, rank_out, objective_out, nullptr, nullptr, 0, 0, s);
+                                  eps2, rank_out, objective_out, nullptr, nullptr, 0, 0, policy, seed, s);
     });
     if (e != hipSuccess) return hip_fail(e, "alloc launch");
     return ok();

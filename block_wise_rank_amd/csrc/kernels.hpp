@@ -9,6 +9,8 @@
 namespace milo {
 
 enum ElemType : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
+// Rank allocation policies (values of milo_alloc_policy).
+enum AllocPolicy : int { kAllocEntropy = 0, kAllocUniform = 1, kAllocRandom = 2 };
 
 // G_b = X_b^T X_b, written as `splits` partial sums per block:
 // gpart[(b * splits + s) * 128 * 128 + i * 128 + j].
@@ -30,13 +32,14 @@ hipError_t launch_refine(const void *x, int x_type, const int64_t *row0, int64_t
                          int block_len, int n_blocks, float *vt, float *sigma, hipStream_t st);
 
 // Rank allocation for pools [pool_lo, pool_lo + n_pools) of the device pool
-// tables: ranks of blocks, per-pool objective (may be null), and when a_off is
-// non-null the arena offsets (pool_base[p] + prefix of rank * (T + d) * elem).
+// tables under `policy` (seed: the random policy's generator seed): ranks of
+// blocks, per-pool objective (may be null), and when a_off is non-null the
+// arena offsets (pool_base[p] + prefix of rank * (T + d) * elem).
 hipError_t launch_alloc(const float *sigma, int sigma_pitch, int max_rank,
                         const int32_t *pool_ptr, const int64_t *budget, const int64_t *pool_base,
                         int pool_lo, int n_pools, int blk_lo, double eps2, int32_t *rank,
                         double *objective, int64_t *a_off, int64_t *b_off, int block_len,
-                        int elem_bytes, hipStream_t st);
+                        int elem_bytes, int policy, uint64_t seed, hipStream_t st);
 
 // Factor pairs from sorted eigenvectors and ranks: A_b^T (rank-major) and B_b
 // rows into the arena, plus INT8 scales.

@@ -141,6 +141,40 @@ milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr,
                                  void *workspace, size_t *workspace_bytes, void *stream);
 
 /*
+ * Rank allocation policies.  MILO_ALLOC_ENTROPY is the method's allocation (the
+ * greedy on the gains, above).  The other two are the equal-budget allocations
+ * the method is compared with ([REV] Strengths, on Fig. 5(d)); both hand out
+ * exactly R' = min(R_p, n_p * k) ranks per pool, k = min(block_len, head_dim):
+ *  MILO_ALLOC_UNIFORM  block j of the pool (j = 0 .. n_p - 1) gets
+ *                      floor(R'/n_p) ranks, one more when j < R' mod n_p;
+ *  MILO_ALLOC_RANDOM   the R' (block, index) slots with the largest keys, key of
+ *                      slot (j, i) of pool p = the high 32 bits of output number
+ *                      1 + (p << 32 | j << 8 | i) of SplitMix64 seeded with
+ *                      `seed` (Steele, Lea & Flood 2014; Stafford's finaliser
+ *                      13), equal keys to the smaller block, then the smaller
+ *                      index: a uniformly random R'-subset of the pool's slots;
+ *                      block j's rank is the number of its slots taken.
+ * Every policy takes each block's leading singular vectors and reports the same
+ * objective: the sum of log(1 + sigma^2/eps^2) over the ranks handed out.
+ */
+typedef enum { MILO_ALLOC_ENTROPY = 0, MILO_ALLOC_UNIFORM = 1, MILO_ALLOC_RANDOM = 2 } milo_alloc_policy;
+typedef struct {
+    milo_alloc_policy policy;
+    uint64_t seed;  /* MILO_ALLOC_RANDOM only */
+} milo_alloc_options;
+
+/*
+ * milo_compress_blocks_ex -- milo_compress_blocks with the allocation policy
+ * chosen by `alloc` (NULL: MILO_ALLOC_ENTROPY, identical to
+ * milo_compress_blocks).  Returns MILO_E_INVALID for an unknown policy.
+ */
+milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_ptr, int32_t n_pools,
+                                    const int64_t *budget, double eps2, float *sigma_out,
+                                    double *objective_out, milo_factors *out, int32_t *sweeps_out,
+                                    const milo_alloc_options *alloc, void *workspace,
+                                    size_t *workspace_bytes, void *stream);
+
+/*
  * milo_allocate_ranks -- the rank allocation alone ([REV] Strengths, Eqs 5-7),
  * on caller-supplied singular values.
  *  sigma       device [n_blocks][head_dim] fp32, every row non-increasing and
@@ -157,6 +191,15 @@ milo_status milo_allocate_ranks(const float *sigma, int32_t n_blocks, int32_t he
                                 const int64_t *budget, double eps2, int32_t *rank_out,
                                 double *objective_out, void *workspace, size_t *workspace_bytes,
                                 void *stream);
+
+/* milo_allocate_ranks under the policy chosen by `alloc` (NULL: entropy).  The
+ * uniform and random policies do not read sigma for the ranks, only for the
+ * objective; k = max_rank. */
+milo_status milo_allocate_ranks_ex(const float *sigma, int32_t n_blocks, int32_t head_dim,
+                                   int32_t max_rank, const int32_t *pool_ptr, int32_t n_pools,
+                                   const int64_t *budget, double eps2, int32_t *rank_out,
+                                   double *objective_out, const milo_alloc_options *alloc,
+                                   void *workspace, size_t *workspace_bytes, void *stream);
 
 /*
  * milo_reconstruct -- rebuild X_hat_b = A_b B_b (decoded) for the listed blocks

@@ -158,6 +158,31 @@ def test_allocate_validation(L):
     assert size.value > 0
 
 
+def test_unknown_allocation_policy_is_rejected(L):
+    """The policy is validated before anything else, on the host."""
+    from block_wise_rank_amd import _capi
+    opts = _capi.milo_alloc_options(7, 0)
+    pp = (ctypes.c_int32 * 2)(0, 4)
+    bb = (ctypes.c_int64 * 1)(8)
+    size = ctypes.c_size_t(0)
+    st = L.milo_allocate_ranks_ex(0x1000, 4, 128, 128, ctypes.cast(pp, ctypes.c_void_p), 1,
+                                  ctypes.cast(bb, ctypes.c_void_p), 1e-4, 0x2000, None,
+                                  ctypes.byref(opts), None, ctypes.byref(size), None)
+    assert st == _capi.MILO_E_INVALID and b"policy" in L.milo_last_error()
+    blocks, f = _blocks(), _factors()
+    st = L.milo_compress_blocks_ex(ctypes.byref(blocks), ctypes.cast(pp, ctypes.c_void_p), 1,
+                                   ctypes.cast(bb, ctypes.c_void_p), 1e-4, 0x3000, None,
+                                   ctypes.byref(f), None, ctypes.byref(opts), None,
+                                   ctypes.byref(size), None)
+    assert st == _capi.MILO_E_INVALID and b"policy" in L.milo_last_error()
+    # a known policy passes this check and reaches the workspace size query
+    ok = _capi.milo_alloc_options(_capi.MILO_ALLOC_RANDOM, 5)
+    st = L.milo_allocate_ranks_ex(0x1000, 4, 128, 128, ctypes.cast(pp, ctypes.c_void_p), 1,
+                                  ctypes.cast(bb, ctypes.c_void_p), 1e-4, 0x2000, None,
+                                  ctypes.byref(ok), None, ctypes.byref(size), None)
+    assert st == _capi.MILO_E_WORKSPACE and size.value > 0
+
+
 def test_reconstruct_validation(L):
     f = _factors()
     assert L.milo_reconstruct(ctypes.byref(f), 0x10, 1, 0x20, 2, None) == 2   # int8 output
