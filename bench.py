@@ -348,6 +348,37 @@ def main():
     prof_dec = milo.milo_profile_read()
     milo.milo_profile_enable(False)
 
+    # the unfused alternative: rebuild every attended block into a staging cache,
+    # then attend over it as an uncompressed cache (one pass over all layers)
+    rebuild = None
+    if sel is None and not cfg.tail_len:
+        stg = [torch.empty((cfg.batch, H, cfg.blocks_per_seq * T, d), dtype=torch.bfloat16, device=dev)
+               for _ in range(2)]
+        outs2 = torch.empty((cfg.batch, Hq, d), dtype=xdt, device=dev)
+
+        def rebuild_layer(layer):
+            milo.reconstruct_then_attend(Q[layer], q_pos, F["k"].view(layer * nb_layer, nb_layer),
+                                         F["v"].view(layer * nb_layer, nb_layer), cfg.blocks_per_seq, H,
+                                         outs2, staging_k=stg[0], staging_v=stg[1])
+        rebuild_layer(0)
+        torch.cuda.synchronize()
+        milo.milo_profile_read()
+        milo.milo_profile_enable(True)
+        e0.record()
+        for layer in range(L):
+            rebuild_layer(layer)
+        e1.record()
+        torch.cuda.synchronize()
+        rb_ms = e0.elapsed_time(e1)
+        prof_rb = milo.milo_profile_read()
+        milo.milo_profile_enable(False)
+        rebuild = {"ms_per_step": round(rb_ms, 3), "fused_decode_ms_per_step": round(dec_only_ms, 3),
+                   "slowdown_vs_fused": round(rb_ms / dec_only_ms, 3),
+                   "kernels_ms_per_step": {n: round(v[1], 3) for n, v in prof_rb.items()},
+                   "staging_bytes_per_layer": 2 * stg[0].numel() * stg[0].element_size()}
+        del stg
+        log(f"reconstruct-then-attend: {rb_ms:.2f} ms per step vs fused decode {dec_only_ms:.2f} ms")
+
     # ---------------- algorithmic work per kernel launch ----------------
     ranks = {k: F[k].rank.to(torch.int64) for k in ("k", "v")}
     sw = torch.cat([sweeps["k"], sweeps["v"]]).to(torch.float64)
@@ -391,6 +422,10 @@ def main():
         "decode_tail": (tail_bytes_all, "GB/s", "hbm", PEAK_HBM_GBS),
         "decode_combine": (L * cfg.batch * Hq * d * 4, "GB/s", "hbm", PEAK_HBM_GBS),
     }
+    if rebuild is not None:
+        # fused: the factors once; unfused: the factors, the staging write, the staging read
+        rebuild["bytes_per_step"] = dec_bytes_all_layers + 2 * L * rebuild["staging_bytes_per_layer"]
+        rebuild["fused_bytes_per_step"] = dec_bytes_all_layers
     hashes = KERNEL_SOURCES
     rooflines = {}
     for name, (launches, tot_ms) in prof.items():
@@ -463,6 +498,7 @@ def main():
         "roofline": roof,
         "rooflines": rooflines,
         "decode_only_rooflines": dec_only,
+        "reconstruct_then_attend": rebuild,
         "memory": {"full_kv_bf16_bytes": full_kv, "factor_bytes": factor_bytes,
                    "ratio": round(factor_bytes / full_kv, 4)},
         "cpu_baseline": cpu,

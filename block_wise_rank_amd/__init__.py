@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     milo_profile_enable,
     milo_profile_read,
     milo_reconstruct,
+    reconstruct_then_attend,
 )
 from . import _capi  # noqa: F401
 
@@ -29,4 +30,5 @@ __all__ = [
     "milo_allocate_ranks_ex", "milo_arena_bytes", "milo_compress_blocks", "milo_compress_blocks_ex",
     "milo_compress_workspace_bytes",
     "milo_decode_attention", "milo_profile_enable", "milo_profile_read", "milo_reconstruct",
+    "reconstruct_then_attend",
 ]

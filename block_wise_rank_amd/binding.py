@@ -309,6 +309,39 @@ def milo_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: F
     _check(st)
 
 
+def reconstruct_then_attend(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: Factors,
+                            blocks_per_seq: int, n_kv_heads: int, out: torch.Tensor,
+                            staging_k: torch.Tensor | None = None,
+                            staging_v: torch.Tensor | None = None, staging_dtype=torch.bfloat16,
+                            rope_base: float = 1e6, softmax_scale: float | None = None,
+                            split_len: int = 0, stream=None):
+    """The unfused decode over every block of every sequence: milo_reconstruct
+    rebuilds the blocks into token-major staging caches [batch][n_kv_heads]
+    [blocks_per_seq * block_len][head_dim] (block b of sequence s, KV head h is
+    factor block (s * n_kv_heads + h) * blocks_per_seq + b, so positions stay
+    b * block_len + t), then milo_decode_attention attends over them as an
+    uncompressed cache (no factor blocks).  Returns (staging_k, staging_v)."""
+    batch = q.shape[0]
+    T, d = k.block_len, k.head_dim
+    shape = (batch, n_kv_heads, blocks_per_seq * T, d)
+    if staging_k is None:
+        staging_k = torch.empty(shape, dtype=staging_dtype, device=q.device)
+    if staging_v is None:
+        staging_v = torch.empty(shape, dtype=staging_dtype, device=q.device)
+    _need(staging_k, "staging_k", None, batch * n_kv_heads * blocks_per_seq * T * d)
+    _need(staging_v, "staging_v", staging_k.dtype, staging_k.numel())
+    ids = torch.arange(batch * n_kv_heads * blocks_per_seq, dtype=torch.int32, device=q.device)
+    milo_reconstruct(k, ids, staging_k, stream)
+    milo_reconstruct(v, ids, staging_v, stream)
+    tail_len = torch.full((batch,), blocks_per_seq * T, dtype=torch.int32, device=q.device)
+    tail_pos0 = torch.zeros((batch,), dtype=torch.int64, device=q.device)
+    milo_decode_attention(q, q_pos, k, v, 0, n_kv_heads, out, tail_k=staging_k.view(shape),
+                          tail_v=staging_v.view(shape), tail_len=tail_len, tail_pos0=tail_pos0,
+                          rope_base=rope_base, softmax_scale=softmax_scale, split_len=split_len,
+                          stream=stream)
+    return staging_k, staging_v
+
+
 def decode_workspace_bytes(q: torch.Tensor, k: Factors, v: Factors, blocks_per_seq: int,
                            n_kv_heads: int, out: torch.Tensor, **kw) -> int:
     """Size query for milo_decode_attention (no work is enqueued)."""

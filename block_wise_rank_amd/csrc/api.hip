@@ -476,13 +476,15 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
     const int ttype = a->tail_dtype == MILO_F32 ? milo::kF32 : milo::kBF16;
     int split = a->split_len;
     if (split == 0) {
-        // The longest split that still gives >= 1024 workgroups (four per CU):
-        // each split pays a prologue (B_k fragments, rotated queries) and a merge.
+        // The longest split that still gives >= 1024 workgroups (four per CU),
+        // counting the tail's: each split pays a prologue (B_k fragments,
+        // rotated queries) and a merge.
         const int64_t units = static_cast<int64_t>(a->batch) * a->n_kv_heads *
                               (a->sel_ptr ? a->sel_max : a->blocks_per_seq);
+        const int64_t tail_units = tail ? static_cast<int64_t>(a->batch) * a->n_kv_heads : 0;
         split = 128;
         for (int c = 2048; c > 128; c /= 2)
-            if (T % c == 0 && units * (T / c) >= 1024 &&
+            if (T % c == 0 && units * (T / c) + tail_units * ((a->tail_cap + c - 1) / c) >= 1024 &&
                 milo::decode_split_fits(ftype, ttype, tail, G, c)) {
                 split = c;
                 break;

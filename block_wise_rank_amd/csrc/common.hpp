@@ -64,6 +64,23 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const u16x8_t &a, const u16x8_t 
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// LDS transpose read of 16-bit data (ds_read_b64_tr_b16, gfx950).  Within each
+// group of 16 lanes, lane j receives element j % 4 of the 8-byte chunks that
+// lanes 4e + j / 4 (e = 0..3) of its group address.  So if lane j of a group
+// addresses row r0 + j / 4, columns 4 (j % 4) .. 4 (j % 4) + 3 of a row-major
+// 16-bit matrix, lane j receives column j, rows r0 .. r0 + 3: four consecutive
+// k values of one column of an MFMA operand, read from a k-major layout.
+__device__ __forceinline__ u16x4_t lds_read_tr16(const void *p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(p));
+    return __builtin_bit_cast(u16x4_t, v);
+}
+
+__device__ __forceinline__ u16x8_t cat8(const u16x4_t &a, const u16x4_t &b) {
+    return u16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 __device__ __forceinline__ f32x16_t zero16() {
     f32x16_t z;
 #pragma unroll

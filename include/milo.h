@@ -251,7 +251,7 @@ typedef struct milo_decode_args {
                               /* dividing block_len, whose workgroup fits the LDS for   */
                               /* the call's query heads per KV head; 0 picks the        */
                               /* longest such split that still gives >= 1024            */
-                              /* workgroups (else 128)                                  */
+                              /* workgroups, the tail's included (else 128)             */
     void *workspace;          /* device scratch: per-split partial results and the     */
                               /* RoPE tables of the call (256-byte aligned)             */
     size_t workspace_bytes;

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle
-from block_wise_rank_amd import Factors, milo_decode_attention
+from block_wise_rank_amd import Factors, milo_decode_attention, reconstruct_then_attend
 from synthetic import CONFIGS, layer_inputs, queries, selection
 from synthetic.factors import random_factor_set
 from synthetic.planted import tail_inputs
@@ -193,3 +193,12 @@ def test_end_to_end(cfg_idx, q_scale):
     print(f"  [cfg{cfg_idx} q*{q_scale}] max|err| {err:.3g} max|ref| {np.abs(ref).max():.3g} max|v| {vmax:.3g}")
     assert err <= 2e-2
     assert err <= 2e-2 * vmax
+    # the unfused path: rebuild the blocks into a staging cache, then attend over it
+    out2 = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    sdt = torch.float32 if st == "f32" else torch.bfloat16
+    reconstruct_then_attend(q.to(DEV), q_pos.to(DEV), kf, vf, cfg.blocks_per_seq, cfg.n_kv_heads, out2,
+                            staging_dtype=sdt, rope_base=cfg.rope_base)
+    torch.cuda.synchronize()
+    err2 = np.abs(out2.cpu().numpy() - ref).max()
+    print(f"  [cfg{cfg_idx} q*{q_scale}] reconstruct-then-attend max|err| {err2:.3g}")
+    assert err2 <= 2e-2 and err2 <= 2e-2 * vmax
