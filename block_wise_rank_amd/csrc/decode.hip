@@ -66,7 +66,7 @@ __host__ __device__ inline int align16(int v) { return (v + 15) & ~15; }
 
 // A_k staging pitch per rank row of a 32-token tile (bytes); fp32 factors are
 // read straight from memory.
-__host__ __device__ inline int stage_pitch(int f) { return f == kBF16 ? 72 : (f == kI8 ? 40 : 0); }
+__host__ __device__ inline int stage_pitch(int f) { return f == kBF16 ? 64 : (f == kI8 ? 40 : 0); }
 
 struct LdsLayout {
     int ang, qs, bk, rope, base, stage, loop_end;      // loop phase
@@ -138,12 +138,13 @@ __device__ __forceinline__ void frag_terms(const float (&v)[8], u16x8_t (&f)[NS]
     }
 }
 
-// Byte offset of (rank row r, token t) in a bf16 A_k staging tile: 16-byte
-// chunks of a row are swapped in pairs for rows with bit 4 set, so the four
-// lane groups (rows 8 apart) of a transposed read hit four distinct 32-byte
-// bank windows.
+// Byte offset of (rank row r, token t) in a bf16 A_k staging tile (64-byte
+// rows): the two 16-token halves of a row swap places in rows with bit 1 set.
+// A transposing read of one half-wave touches rows r0 .. r0 + 3 and r0 + 8 ..
+// r0 + 11 (r0 a multiple of 4) x 32 bytes of one half; the swap spreads them
+// over all 32 banks twice, the minimum for 256 bytes.
 __device__ __forceinline__ int stage_off_bf16(int r, int t) {
-    return r * 72 + ((((t >> 3) ^ (2 * ((r >> 4) & 1)))) << 4) + ((t & 7) << 1);
+    return r * 64 + ((((t >> 4) ^ ((r >> 1) & 1))) << 5) + ((t & 15) << 1);
 }
 __device__ __forceinline__ int stage_off_i8(int r, int t) {
     return r * 40 + ((((t >> 4) ^ ((r >> 4) & 1))) << 4) + (t & 15);
@@ -256,7 +257,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                 if (ci * RPI < rk_pad) {  // uniform
                     const int r = ci * RPI + lane / LPR;
                     if constexpr (F == kBF16) {
-                        uint8_t *dst = stg + r * 72 + (((lane % LPR) ^ (2 * ((r >> 4) & 1))) << 4);
+                        // 16-byte piece lane % LPR = tokens 8 (lane % LPR) .. + 7
+                        uint8_t *dst = stg + stage_off_bf16(r, 8 * (lane % LPR));
                         reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
                         reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[ci].z, kraw[ci].w);
                     } else {
@@ -464,9 +466,11 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                     const bool first = ks == 0;  // zero accumulator input (inline constant)
                     u16x8_t bfr[NS];
                     if constexpr (F == kBF16) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            bfr[0][e] = *reinterpret_cast<const uint16_t *>(stg + stage_off_bf16(32 * ks + 8 * c4 + e, t));
+                        // ranks 32 ks + 8 c .. + 7 of token t by two transposing reads: lane
+                        // (c, j) addresses rank row 32 ks + 8 c + j / 4 (+ 4), tokens 4 (j % 4) ..
+                        const int row = 32 * ks + 8 * c4 + (ln >> 2);
+                        const uint8_t *p0 = stg + stage_off_bf16(row, 16 * nt + 4 * (ln & 3));
+                        bfr[0] = cat8(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * 64));
                     } else if constexpr (F == kI8) {
                         float v[8];
 #pragma unroll

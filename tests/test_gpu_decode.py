@@ -132,9 +132,10 @@ def test_kernel_level_long_blocks(storage):
         _check(got, ref, vmax, storage, f"{storage} T=2048 split {split}")
 
 
-def test_split_beyond_lds_is_rejected():
-    """16 query heads per KV head do not fit a 2048-token bf16 split: the call is
-    refused before anything is enqueued, and the default split still works."""
+def test_invalid_split_is_rejected_and_16_heads_fit_2048():
+    """Split lengths that are not multiples of 128, exceed 2048 or do not divide
+    the block are refused before anything is enqueued; 16 query heads per KV head
+    fit a 2048-token bf16 split and agree with the default split."""
     from block_wise_rank_amd import MiloError
     T, d = 2048, 128
     kt, _, _ = random_factor_set(1, T, d, "bf16", seed=51, ranks=np.array([64]))
@@ -143,13 +144,18 @@ def test_split_beyond_lds_is_rejected():
     q = torch.randn((1, 16, d), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).to(DEV)
     q_pos = torch.tensor([T], dtype=torch.int64, device=DEV)
     out = torch.full((1, 16, d), 7.0, device=DEV)
-    with pytest.raises(MiloError):
-        milo_decode_attention(q, q_pos, kf, vf, 1, 1, out, split_len=2048)
+    for bad in (192, 4096, 768):
+        with pytest.raises(MiloError):
+            milo_decode_attention(q, q_pos, kf, vf, 1, 1, out, split_len=bad)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
-    milo_decode_attention(q, q_pos, kf, vf, 1, 1, out)
+    milo_decode_attention(q, q_pos, kf, vf, 1, 1, out, split_len=2048)
+    ref = torch.empty_like(out)
+    milo_decode_attention(q, q_pos, kf, vf, 1, 1, ref)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all())
+    # both round the softmax weights to bf16 relative to their own split's maximum
+    assert float((out - ref).abs().max()) <= 1e-2 * float(ref.abs().max())
 
 
 def test_decode_is_deterministic():
