@@ -9,146 +9,150 @@
 // afterwards G_pp = alpha - t gamma, G_qq = beta + t gamma, G_pq = 0.
 //
 // Ordering: the round-robin ("circle") tournament.  Positions 0..127 form 64
-// slots, slot P = positions (P, 127 - P); in round k position 0 holds index 0
-// and position i >= 1 holds index 1 + (i - 1 + k) mod 127.  One round's 64
-// pairs are disjoint, so their rotations commute and are applied together;
-// 127 rounds make a sweep.  From one round to the next every index except 0
-// moves to the neighbouring position, which is what the layout exploits:
+// slots, slot P = positions (P, 127 - P) (its first and second row); in round
+// k position 0 holds index 0 and position i >= 1 holds index
+// 1 + (i - 1 + k) mod 127.  One round's 64 pairs are disjoint, so their
+// rotations commute and are applied together; 127 rounds make a sweep, after
+// which every index is back at its starting position.  Between rounds the
+// index at position i >= 2 moves to position i - 1, the one at position 1 to
+// position 127, and index 0 stays.
 //
+// Everything is kept in position space, where that movement is the same in
+// every round:
 //  * Eigenvectors: wave w holds slots 8w .. 8w + 7, both rows of each slot, two
 //    components per lane.  A rotation is lane-local; between rounds the rows
 //    shift one slot along the ring (first rows down, second rows up), inside
 //    the registers except for the 14 rows that cross a wave boundary, which go
 //    through a small double-buffered LDS exchange area.
-//  * Off-diagonal 2 x 2 blocks (slot P, slot Q), P < Q, of G: 2016 per round.
-//    G's upper triangle is indexed by matrix index (pitch 129 puts G[a][b] on
-//    bank (a + b) mod 32 whichever triangle is addressed).
-//  * Rotation parameters: the two indices of round k + 1's pair P' sit in
-//    slots P' + 1 (first row) and P' - 1 (second row) of round k (the ends of
-//    the ring differ slightly), so their off-diagonal entry is an
-//    element of block (P' - 1, P' + 1) and their new diagonal entries come from
-//    the rotations of pairs P' - 1 and P' + 1.  The lane that rotates that block
-//    in round k therefore has everything round k + 1's rotation P' needs and
-//    computes it at once; parameters and new diagonal entries of every pair are
-//    double-buffered in LDS.  One barrier per round.
+//  * Off-diagonal 2 x 2 blocks of G between slots P < Q (2016 of them): four
+//    role arrays (first-first, first-second, second-first, second-second), each
+//    indexed by block, double-buffered.  After a round's rotation every element
+//    moves to the block and role its two positions have in the next round: a
+//    fixed permutation, tabulated at compile time.  A lane reads its blocks and
+//    writes the rotated elements to their next places in the other buffer;
+//    neighbouring lanes own neighbouring blocks, so both sides are consecutive
+//    words (no bank conflicts) and no address depends on the round.
+//  * Each pair's own element G_pq (positions P and 127 - P) is not in a block:
+//    it is kept in a register of the lane that computes that pair's rotation.
+//  * Rotation parameters: the element of the pair that slot P' holds in round
+//    k + 1 is the second-first element of block (P' - 1, P' + 1) of round k (the
+//    ends of the ring differ slightly), and its new diagonal entries come from
+//    the rotations of pairs P' - 1 and P' + 1.  Wave 7's lane P' rotates that
+//    block in round k and immediately computes round k + 1's rotation of pair
+//    P'; parameters are double-buffered in LDS, the other per-pair state stays
+//    in wave 7's registers.  One barrier per round.
 //
 // Scaled rotations (the square-root-free bookkeeping of "fast Givens", Golub &
-// Van Loan sec. 5.1.13, applied to both sides): row i of G and of V^T is stored
-// divided by a scale s_i.  The rotation (c, s = c t) of pair (p, q) then becomes
-// R_p <- R_p - alpha R_q, R_q <- beta R_p + R_q with alpha = t s_q / s_p,
-// beta = t s_p / s_q, and s_p, s_q <- c s_p, c s_q: two FMAs per element
-// instead of four products.  Scales only shrink (c >= 1/sqrt 2), so every 63 or
-// 64 rounds (at rounds 63 and 126 of a sweep) G and V^T are multiplied back by
-// them and the scales restart at 1; stored values stay within 2^32 of the true
-// ones.  Rotation parameters are computed from true values (diagonal entries
-// are tracked unscaled, g = s_p s_q G_pq).
+// Van Loan sec. 5.1.13, applied to both sides): the row and column of G and
+// the row of V^T at a position are stored divided by a scale s.  The rotation
+// (c, s = c t) of pair (p, q) then becomes R_p <- R_p - alpha R_q,
+// R_q <- beta R_p + R_q with alpha = t s_q / s_p, beta = t s_p / s_q, and
+// s_p, s_q <- c s_p, c s_q: two FMAs per element instead of four products.
+// Scales only shrink (c >= 1/sqrt 2), so after rounds 63 and 126 of a sweep G
+// and V^T are multiplied back by them and the scales restart at 1; stored
+// values stay within 2^32 of the true ones.  Rotation parameters are computed
+// from true values (diagonal entries are tracked unscaled, g = s_p s_q G_pq).
 //
-// Pairs whose rotation is the identity (already orthogonal to tolerance) skip
-// their LDS traffic, so late sweeps cost little.  Cyclic Jacobi converges
-// quadratically once the off-diagonal part is small (Golub & Van Loan sec. 8.5.3):
-// a sweep whose every relative off-diagonal |g| / sqrt|a b| was at most
-// stop_tol leaves them near stop_tol^2, so with stop_tol = sqrt(tol) such a
-// sweep ends the solve without the sweep that would only confirm it.
-// Diagonal entries are never stored in G.
+// A pair whose rotation is the identity has alpha = beta = 0, which moves its
+// rows unchanged.  Cyclic Jacobi converges quadratically once the off-diagonal
+// part is small (Golub & Van Loan sec. 8.5.3): a sweep whose every relative
+// off-diagonal |g| / sqrt|a b| was at most stop_tol leaves them near
+// stop_tol^2, so with stop_tol = sqrt(tol) such a sweep ends the solve without
+// the sweep that would only confirm it.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace milo {
 namespace {
 
-constexpr int kGP = 129;              // LDS pitch of G (floats)
-constexpr int kThreads = 512;         // 8 waves
+constexpr int kThreads = 512;                     // 8 waves
 constexpr int kNW = kThreads / 64;
-constexpr int kGWords = 16384;        // G's upper triangle ends at 126 * 129 + 127
-constexpr int kPrmBytes = 2 * 64 * 8;  // (alpha, beta) per pair, double-buffered
-constexpr int kXchBytes = 2 * 2 * (kNW - 1) * 64 * 8;
-constexpr int kLdsBytes = kGWords * 4 + kPrmBytes + kXchBytes;  // <= 80 KiB: two blocks per CU
-constexpr int kGeneric = 2016 - 64;   // off-diagonal blocks not needed for the next round's rotations
-constexpr int kGenLanes = kThreads - 64;  // waves 0..6 (wave 7 computes the next round's rotations)
+constexpr int kBlocks = 64 * 63 / 2;              // 2016 off-diagonal 2 x 2 blocks
+constexpr int kGeneric = kBlocks - 64;            // blocks not feeding the next round's rotations
+constexpr int kGenLanes = kThreads - 64;          // waves 0..6 (wave 7 computes the next round's rotations)
 constexpr int kPerLane = (kGeneric + kGenLanes - 1) / kGenLanes;
+constexpr int kRoleWords = kBlocks;               // one role array
+constexpr int kBufWords = 4 * kRoleWords;         // one buffer of G
+constexpr int kGBytes = 2 * kBufWords * 4;
+constexpr int kPrmBytes = 2 * 64 * 8;             // (alpha, beta) per pair, double-buffered
+constexpr int kXchBytes = 2 * 2 * (kNW - 1) * 64 * 8;
+constexpr int kStabBytes = 128 * 4;               // scales by position at renormalisation
+constexpr int kLdsBytes = kGBytes + kPrmBytes + kXchBytes + kStabBytes + 16;  // + flags
 static_assert(kLdsBytes <= 80 * 1024, "two workgroups per CU");
 static_assert(kPerLane == 5, "generic block slots per lane");
+static_assert(kBufWords * 4 < 65536, "16-bit byte offsets within a buffer");
 
-// G's cells below and on the diagonal are free and hold small tables:
-//  * the two convergence flags (by sweep parity: a rotation above stop_tol
-//    happened) at row 2, columns 0 and 1;
-//  * the scales by matrix index, gathered at renormalisation, on the diagonal
-//    (index 127's diagonal cell lies past the triangle: row 3, column 0);
-//  * per pair and buffer, (new diagonal of the first and second index, their
-//    new scales), as float4 at rows 64..79, columns < 35 (16-byte aligned).
-constexpr int kFlagWord = 2 * kGP;
-__device__ __forceinline__ int scale_word(int i) { return i < 127 ? i * (kGP + 1) : 3 * kGP; }
-static_assert(126 * (kGP + 1) < kGWords, "diagonal cells of indices 0..126 lie inside G");
-__device__ __forceinline__ int rec_word(int buf, int P) {
-    const int e = buf * 64 + P, r = 64 + (e >> 3);
-    return ((r * kGP + 3) & ~3) + 4 * (e & 7);
-}
-static_assert(((79 * kGP + 3) & ~3) + 4 * 7 + 3 < 79 * kGP + 64, "records stay below the diagonal");
-
-// Block (P, Q) holds the next round's pair iff Q == P + 2, or it is (0, 1) or (62, 63).
+// ---- the tournament in position space (compile time) ----
+constexpr int next_pos(int p) { return p == 0 ? 0 : (p == 1 ? 127 : p - 1); }
+constexpr int slot_of(int p) { return p <= 63 ? p : 127 - p; }
+constexpr int role_of(int p) { return p <= 63 ? 0 : 1; }  // 0: first row, 1: second row
+constexpr int pos_of(int slot, int role) { return role == 0 ? slot : 127 - slot; }
+constexpr int block_index(int P, int Q) { return P * 63 - P * (P - 1) / 2 + (Q - P - 1); }  // P < Q, row-major
+// The next round's pair P' lies in block (Pa, Pb) of this round, element role kSel.
+constexpr int next_pair_a(int Pn) { return Pn == 0 ? 0 : (Pn == 63 ? 62 : Pn - 1); }
+constexpr int next_pair_b(int Pn) { return Pn == 0 ? 1 : (Pn == 63 ? 63 : Pn + 1); }
+constexpr int next_pair_role(int Pn) { return Pn == 0 ? 0 : (Pn == 63 ? 3 : 2); }
 constexpr bool next_pair_block(int P, int Q) {
     return Q == P + 2 || (P == 0 && Q == 1) || (P == 62 && Q == 63);
 }
+// Word offset (role * kRoleWords + block) of the element at positions (a, b),
+// or -1 - slot when both positions are one slot's pair.
+constexpr int element_word(int a, int b) {
+    const int sa = slot_of(a), sb = slot_of(b);
+    if (sa == sb) return -1 - sa;
+    return sa < sb ? (2 * role_of(a) + role_of(b)) * kRoleWords + block_index(sa, sb)
+                   : (2 * role_of(b) + role_of(a)) * kRoleWords + block_index(sb, sa);
+}
 
-struct BlockTable {
-    uint16_t pq[kGeneric];  // P | Q << 8, row-major over P < Q
+struct Tables {
+    uint16_t pq[kBlocks];          // P | Q << 8 of block i
+    uint16_t gen[kGeneric];        // generic blocks, row-major
+    uint16_t dst[kBlocks][4];      // next-round byte offset (within a buffer) of each role
+    uint16_t pair_dst[64];         // next-round byte offset of pair P's own element
 };
 
-constexpr BlockTable make_block_table() {
-    BlockTable t{};
-    int n = 0;
+constexpr Tables make_tables() {
+    Tables t{};
+    int n = 0, g = 0;
     for (int P = 0; P < 64; ++P)
-        for (int Q = P + 1; Q < 64; ++Q)
-            if (!next_pair_block(P, Q)) t.pq[n++] = static_cast<uint16_t>(P | (Q << 8));
+        for (int Q = P + 1; Q < 64; ++Q) {
+            t.pq[n] = static_cast<uint16_t>(P | (Q << 8));
+            if (!next_pair_block(P, Q)) t.gen[g++] = static_cast<uint16_t>(n);
+            for (int r = 0; r < 4; ++r) {
+                const int w = element_word(next_pos(pos_of(P, r >> 1)), next_pos(pos_of(Q, r & 1)));
+                t.dst[n][r] = static_cast<uint16_t>(w >= 0 ? 4 * w : 0xffff);  // 0xffff: a pair's element
+            }
+            ++n;
+        }
+    for (int P = 0; P < 64; ++P)
+        t.pair_dst[P] = static_cast<uint16_t>(4 * element_word(next_pos(P), next_pos(127 - P)));
     return t;
 }
 
-__constant__ BlockTable kBlocks = make_block_table();
+__constant__ Tables kTab = make_tables();
 
-// Matrix index at position `pos` in round k (0 <= k < 127).
-__device__ __forceinline__ int index_at(int pos, int k) {
-    if (pos == 0) return 0;
-    const unsigned u = static_cast<unsigned>(pos - 1 + k);
-    return static_cast<int>(min(u, u - 127u)) + 1;
-}
-
-__device__ __forceinline__ int gidx(int a, int b) {
-    return static_cast<int>(__umul24(static_cast<unsigned>(min(a, b)), kGP)) + max(a, b);
-}
-
-// LDS byte offsets of G's elements for every generic block of every lane in
-// every round of a sweep: [round][lane][kPerLane blocks x 4 elements, padded to
-// 24].  The tournament's index arithmetic is the same for every matrix, so it is
-// tabulated once (2.7 MB, L2-resident) and each lane loads its 48 bytes a round
-// ahead.  Byte offsets of the upper triangle end below 64 KiB, so 16 bits hold them.
-constexpr int kAddrPad = 24;
-constexpr int kAddrVec = kAddrPad * 2 / 16;  // uint4 per lane and round
-static_assert(kGWords * 4 <= 65536, "16-bit LDS offsets");
-static_assert(4 * kPerLane <= kAddrPad, "table row");
-__device__ __align__(16) uint16_t g_gen_addr[127 * kGenLanes * kAddrPad];
-
-__global__ __launch_bounds__(256) void jacobi_table_kernel() {
-    const int i = blockIdx.x * 256 + threadIdx.x;  // (round, lane, block slot)
-    if (i >= 127 * kGenLanes * kPerLane) return;
-    const int j = i % kPerLane, g = (i / kPerLane) % kGenLanes, k = i / (kPerLane * kGenLanes);
-    uint16_t *out = g_gen_addr + (k * kGenLanes + g) * kAddrPad + 4 * j;
-    const int bi = g + kGenLanes * j;
-    if (bi >= kGeneric) {
-        out[0] = out[1] = out[2] = out[3] = 0;
-        return;
+// Compile-time checks of the move map: the pair elements of round k + 1 come
+// exactly from the next-pair blocks' selected roles, generic blocks only move
+// into blocks, and every pair element moves into a block.
+constexpr bool check_tables() {
+    const Tables t = make_tables();
+    for (int Pn = 0; Pn < 64; ++Pn) {
+        const int b = block_index(next_pair_a(Pn), next_pair_b(Pn));
+        if (element_word(next_pos(pos_of(next_pair_a(Pn), next_pair_role(Pn) >> 1)),
+                         next_pos(pos_of(next_pair_b(Pn), next_pair_role(Pn) & 1))) != -1 - Pn)
+            return false;
+        if (t.dst[b][next_pair_role(Pn)] != 0xffff) return false;
+        if (element_word(next_pos(Pn), next_pos(127 - Pn)) < 0) return false;
     }
-    const int code = kBlocks.pq[bi];
-    const int P = code & 0xff, Q = code >> 8;
-    const int p1 = index_at(P, k), q1 = index_at(127 - P, k);
-    const int p2 = index_at(Q, k), q2 = index_at(127 - Q, k);
-    out[0] = static_cast<uint16_t>(4 * gidx(p1, p2));
-    out[1] = static_cast<uint16_t>(4 * gidx(p1, q2));
-    out[2] = static_cast<uint16_t>(4 * gidx(q1, p2));
-    out[3] = static_cast<uint16_t>(4 * gidx(q1, q2));
+    for (int i = 0; i < kGeneric; ++i)
+        for (int r = 0; r < 4; ++r)
+            if (t.dst[t.gen[i]][r] == 0xffff) return false;
+    return true;
 }
+static_assert(check_tables(), "position-space move map");
 
-__device__ __forceinline__ float &lds_at(float *base, unsigned byte_off) {
-    return *reinterpret_cast<float *>(reinterpret_cast<char *>(base) + byte_off);
+__device__ __forceinline__ float &lds_at(uint8_t *base, unsigned byte_off) {
+    return *reinterpret_cast<float *>(base + byte_off);
 }
 
 struct Rot {
@@ -177,50 +181,66 @@ __device__ __forceinline__ Rot jacobi_rotation(float a, float b, float g, float 
     return r;
 }
 
+// (g0, g1, g2, g3) = (first-first, first-second, second-first, second-second)
+// of block (P, Q): rows by pair P's (alpha, beta), then columns by pair Q's.
+__device__ __forceinline__ void rotate_block(float (&g)[4], float2 p, float2 q) {
+    const float h11 = fmaf(-p.x, g[2], g[0]), h12 = fmaf(-p.x, g[3], g[1]);
+    const float h21 = fmaf(p.y, g[0], g[2]), h22 = fmaf(p.y, g[1], g[3]);
+    g[0] = fmaf(-q.x, h12, h11);
+    g[1] = fmaf(q.y, h11, h12);
+    g[2] = fmaf(-q.x, h22, h21);
+    g[3] = fmaf(q.y, h21, h22);
+}
+
 __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__restrict__ gpart, int splits,
                                                              float *__restrict__ vt_out,
                                                              int32_t *__restrict__ sweeps_out,
                                                              int max_sweeps, float tol, float stop_tol) {
-    extern __shared__ __align__(16) float smem[];
-    float *G = smem;
-    int *flags = reinterpret_cast<int *>(smem + kFlagWord);                   // [2] by sweep parity
-    float2 *prm = reinterpret_cast<float2 *>(smem + kGWords);                 // [2][64] (alpha, beta)
-    float2 *xch = reinterpret_cast<float2 *>(smem + kGWords + kPrmBytes / 4);  // [2][2][7][64]
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint8_t *G = smem;                                                        // [2][4][kBlocks]
+    float2 *prm = reinterpret_cast<float2 *>(smem + kGBytes);                 // [2][64] (alpha, beta)
+    float2 *xch = reinterpret_cast<float2 *>(smem + kGBytes + kPrmBytes);     // [2][2][7][64]
+    float *stab = reinterpret_cast<float *>(smem + kGBytes + kPrmBytes + kXchBytes);  // [128]
+    int *flags = reinterpret_cast<int *>(smem + kGBytes + kPrmBytes + kXchBytes + kStabBytes);
 
     const int blk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const float *src = gpart + static_cast<int64_t>(blk) * splits * kD * kD;
-    for (int e = tid; e < kD * kD; e += kThreads) {
-        const int i = e >> 7, j = e & 127;
-        if (i < j) {
-            float s = 0.f;
-            for (int p = 0; p < splits; ++p) s += src[static_cast<int64_t>(p) * kD * kD + e];
-            G[i * kGP + j] = s;
-        }
+    auto gram = [&](int a, int b) {
+        float s = 0.f;
+        for (int p = 0; p < splits; ++p) s += src[static_cast<int64_t>(p) * kD * kD + a * kD + b];
+        return s;
+    };
+    // Round 0: position = index, so block (P, Q) role r holds G[pos(P)][pos(Q)].
+    for (int e = tid; e < kBufWords; e += kThreads) {
+        const int r = e / kRoleWords, b = e - r * kRoleWords;
+        const int code = kTab.pq[b];
+        reinterpret_cast<float *>(G)[e] = gram(pos_of(code & 0xff, r >> 1), pos_of(code >> 8, r & 1));
     }
     if (tid == 0) {
         flags[0] = 0;
         flags[1] = 0;
     }
-    __syncthreads();
 
-    // Round 0 of sweep 0: pair P = (P, 127 - P).
+    // Wave 7 state of pair Pn = lane: its own element (stored form, before this
+    // round's rotation), whether this round rotates it, and after this round's
+    // rotation the diagonal entries (true) and scales of its first and second row.
+    const int Pn = lane;
+    const int Pa = next_pair_a(Pn), Pb = next_pair_b(Pn), sel = next_pair_role(Pn);
+    const int sblk = block_index(Pa, Pb);
+    float gp = 0.f, rna = 0.f, rnb = 0.f, rsa = 1.f, rsb = 1.f;
+    bool rotp = false;
     if (wave == kNW - 1) {
-        const int x = lane, y = 127 - lane;
-        float a = 0.f, b = 0.f;
-        for (int p = 0; p < splits; ++p) {
-            a += src[static_cast<int64_t>(p) * kD * kD + x * kD + x];
-            b += src[static_cast<int64_t>(p) * kD * kD + y * kD + y];
-        }
-        const float g = G[x * kGP + y];
-        const Rot r = jacobi_rotation(a, b, g, tol);  // scales start at 1: alpha = beta = t
-        prm[lane] = make_float2(r.t, r.t);
-        *reinterpret_cast<float4 *>(G + rec_word(0, lane)) = make_float4(r.na, r.nb, r.c, r.c);
-        if (r.rot) {
-            G[x * kGP + y] = 0.f;
-            if (g * g > stop_tol * stop_tol * fabsf(a * b)) flags[0] = 1;
-        }
+        const float a = gram(Pn, Pn), b = gram(127 - Pn, 127 - Pn);
+        gp = gram(Pn, 127 - Pn);
+        const Rot r = jacobi_rotation(a, b, gp, tol);  // scales start at 1: alpha = beta = t
+        prm[Pn] = make_float2(r.t, r.t);
+        rna = r.na;
+        rnb = r.nb;
+        rsa = rsb = r.c;
+        rotp = r.rot;
+        if (r.rot && gp * gp > stop_tol * stop_tol * fabsf(a * b)) flags[0] = 1;
     }
 
     // Eigenvector rows of this wave's slots: F = first rows, S = second rows
@@ -232,37 +252,42 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
         F[j] = make_float2(c0 == P ? 1.f : 0.f, c0 + 1 == P ? 1.f : 0.f);
         S[j] = make_float2(c0 == 127 - P ? 1.f : 0.f, c0 + 1 == 127 - P ? 1.f : 0.f);
     }
-    // Generic blocks of this lane (waves 0..6): table entries tid, tid + 448, ...
-    int bq[kPerLane];
+    // Generic blocks of this lane (waves 0..6): entries tid, tid + 448, ... of the
+    // generic list.  code = P | Q << 6 | block << 12; dst = next byte offsets of
+    // the four roles, two per word.
+    int code[kPerLane];
+    uint32_t dst[kPerLane][2];
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
         const int i = tid + kGenLanes * j;
-        bq[j] = (wave < kNW - 1 && i < kGeneric) ? kBlocks.pq[i] : -1;
+        const bool has = wave < kNW - 1 && i < kGeneric;
+        const int b = has ? kTab.gen[i] : 0;
+        const int pq = kTab.pq[b];
+        code[j] = (pq & 0xff) | ((pq >> 8) << 6) | (b << 12);
+        dst[j][0] = kTab.dst[b][0] | (static_cast<uint32_t>(kTab.dst[b][1]) << 16);
+        dst[j][1] = kTab.dst[b][2] | (static_cast<uint32_t>(kTab.dst[b][3]) << 16);
     }
-    // The next-pair block of this lane (wave 7 only): lane = next round's pair P'.
-    const int Pn = lane;
-    const int Pa = Pn == 0 ? 0 : (Pn == 63 ? 62 : Pn - 1);
-    const int Pb = Pn == 0 ? 1 : (Pn == 63 ? 63 : Pn + 1);
-    const int sel = Pn == 0 ? 0 : (Pn == 63 ? 3 : 2);  // element (p1 p2) / (q1 q2) / (q1 p2)
-    // This lane's row of the offset table (wave 7 reads a valid row it never uses).
-    const uint4 *arow = reinterpret_cast<const uint4 *>(g_gen_addr) + (tid < kGenLanes ? tid : tid - 64) * kAddrVec;
-    uint4 ta[kAddrVec];
-#pragma unroll
-    for (int v = 0; v < kAddrVec; ++v) ta[v] = arow[v];
+    const bool has4 = wave < kNW - 1 && tid + kGenLanes * (kPerLane - 1) < kGeneric;  // slot 4 is partial
+    // wave 7: next places of the special block's three other roles and of the
+    // pair's own element
+    const uint32_t sdst0 = kTab.dst[sblk][0] | (static_cast<uint32_t>(kTab.dst[sblk][1]) << 16);
+    const uint32_t sdst1 = kTab.dst[sblk][2] | (static_cast<uint32_t>(kTab.dst[sblk][3]) << 16);
+    const uint32_t pdst = kTab.pair_dst[Pn];
     __syncthreads();
 
     int used = -max_sweeps;
     int gk = 0;  // rounds done so far (parity selects the buffers)
     for (int sweep = 0; sweep < max_sweeps; ++sweep) {
         for (int kr = 0; kr < 127; ++kr, ++gk) {
-            // Opaque copy of the round: recomputing the indices each round keeps
-            // them out of per-index induction registers.
             int k = kr;
             asm volatile("" : "+s"(k));
             const int cb = gk & 1;
             const float2 *pc = prm + cb * 64;
+            uint8_t *cur = G + cb * (kBufWords * 4);
+            uint8_t *nxt = G + (cb ^ 1) * (kBufWords * 4);
             // rounds after which G and V^T are multiplied back by their scales
             const bool renorm = (k == 63) | (k == 126);
+            const bool last_round = (k == 126);
 
             // ---- eigenvector rows: rotate (identity when alpha = beta = 0), shift
             // along the ring, send the ends
@@ -289,47 +314,41 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                 if (wave == 0) S[0] = f1;
             }
 
-            // ---- next round's rotations (wave 7): rotate block (Pa, Pb), then the
-            // pair of round k + 1 formed by one of its elements
-            const bool last_round = (k == 126);
             if (wave == kNW - 1) {
+                // ---- wave 7: this pair's own element moves into a block; block
+                // (Pa, Pb) is rotated, its selected element becomes the element of
+                // round k + 1's pair Pn, whose rotation is computed here.
+                lds_at(nxt, pdst) = rotp ? 0.f : gp;
                 const float2 A = pc[Pa], B = pc[Pb];
-                const float4 DA = *reinterpret_cast<const float4 *>(G + rec_word(cb, Pa));
-                const float4 DB = *reinterpret_cast<const float4 *>(G + rec_word(cb, Pb));
-                const int p1 = index_at(Pa, k), q1 = index_at(127 - Pa, k);
-                const int p2 = index_at(Pb, k), q2 = index_at(127 - Pb, k);
-                const int sa[4] = {gidx(p1, p2), gidx(p1, q2), gidx(q1, p2), gidx(q1, q2)};
-                const int asel = sel == 0 ? sa[0] : (sel == 2 ? sa[2] : sa[3]);
-                const bool sact = (A.x != 0.f) | (B.x != 0.f);
                 float h[4];
-                if (sact) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) h[e] = G[sa[e]];
-                    const float r11 = fmaf(-A.x, h[2], h[0]), r12 = fmaf(-A.x, h[3], h[1]);
-                    const float r21 = fmaf(A.y, h[0], h[2]), r22 = fmaf(A.y, h[1], h[3]);
-                    h[0] = fmaf(-B.x, r12, r11);
-                    h[1] = fmaf(B.y, r11, r12);
-                    h[2] = fmaf(-B.x, r22, r21);
-                    h[3] = fmaf(B.y, r21, r22);
-                } else {
-                    const float v = G[asel];
-                    h[0] = h[2] = h[3] = v;
-                    h[1] = 0.f;
-                }
+                for (int e = 0; e < 4; ++e) h[e] = lds_at(cur, (e * kRoleWords + sblk) * 4);
+                rotate_block(h, A, B);
+                // the other three roles move on (the selected one's slot is unused)
                 const float gn = sel == 0 ? h[0] : (sel == 2 ? h[2] : h[3]);
-                // new diagonal entries and scales of the pair's first and second index
-                const float an = Pn == 0 ? DA.x : (Pn == 63 ? DB.y : DB.x);
-                const float bn = Pn == 0 ? DB.x : DA.y;
-                const float sfa = Pn == 0 ? DA.z : (Pn == 63 ? DB.w : DB.z);
-                const float sfb = Pn == 0 ? DB.z : DA.w;
+                if (sel != 0) lds_at(nxt, sdst0 & 0xffffu) = h[0];
+                lds_at(nxt, sdst0 >> 16) = h[1];
+                if (sel != 2) lds_at(nxt, sdst1 & 0xffffu) = h[2];
+                if (sel != 3) lds_at(nxt, sdst1 >> 16) = h[3];
+                // new diagonal entries and scales of the rows that form pair Pn next
+                // round (pair Pa's second row and pair Pb's first row; ends differ)
+                const float a_na = __shfl(rna, Pa, 64), a_nb = __shfl(rnb, Pa, 64);
+                const float a_sa = __shfl(rsa, Pa, 64), a_sb = __shfl(rsb, Pa, 64);
+                const float b_na = __shfl(rna, Pb, 64), b_nb = __shfl(rnb, Pb, 64);
+                const float b_sa = __shfl(rsa, Pb, 64), b_sb = __shfl(rsb, Pb, 64);
+                const float an = Pn == 0 ? a_na : (Pn == 63 ? b_nb : b_na);
+                const float bn = Pn == 0 ? b_na : a_nb;
+                const float sfa = Pn == 0 ? a_sa : (Pn == 63 ? b_sb : b_sa);
+                const float sfb = Pn == 0 ? b_sa : a_sb;
                 const float gt = gn * sfa * sfb;
                 Rot r = jacobi_rotation(an, bn, gt, tol);
-                const int kn = last_round ? 0 : k + 1;
                 float s1 = sfa, s2 = sfb;
-                if (renorm) {  // uniform: the scales are gathered by index and restart at 1
-                    G[scale_word(index_at(Pn, kn))] = sfa;
-                    G[scale_word(index_at(127 - Pn, kn))] = sfb;
+                gp = gn;
+                if (renorm) {  // uniform: scales gathered by next-round position, restart at 1
+                    stab[Pn] = sfa;
+                    stab[127 - Pn] = sfb;
                     s1 = s2 = 1.f;
+                    gp = gn * sfa * sfb;
                 }
                 const float ratio = s2 * __builtin_amdgcn_rcpf(s1);
                 float al = r.t * ratio, be = r.t * __builtin_amdgcn_rcpf(ratio);
@@ -338,69 +357,41 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                     al = be = 0.f;
                 }
                 prm[(cb ^ 1) * 64 + Pn] = make_float2(al, be);
-                *reinterpret_cast<float4 *>(G + rec_word(cb ^ 1, Pn)) = make_float4(r.na, r.nb, s1 * r.c, s2 * r.c);
-                const float gw = r.rot ? 0.f : gn;
-                if (sel == 0) h[0] = gw;
-                else if (sel == 2) h[2] = gw;
-                else h[3] = gw;
-                if (sact) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) G[sa[e]] = h[e];
-                } else if (r.rot) {
-                    G[asel] = 0.f;
-                }
+                rna = r.na;
+                rnb = r.nb;
+                rsa = s1 * r.c;
+                rsb = s2 * r.c;
+                rotp = r.rot;
                 if (r.rot && gt * gt > stop_tol * stop_tol * fabsf(an * bn))
                     flags[(sweep + (last_round ? 1 : 0)) & 1] = 1;
-            }
-
-
-            // ---- generic off-diagonal blocks (waves 0..6), two at a time: loads first, then stores
-            {
-                // next round's offsets (round 0 after the sweep's last): each uint4
-                // of the table row is reloaded once its two blocks are done
-                const int kn = k == 126 ? 0 : k + 1;
-                const uint4 *anext = arow + kn * kGenLanes * kAddrVec;
+            } else {
+                // ---- waves 0..6: generic blocks, two at a time (loads, then stores)
 #pragma unroll
                 for (int j0 = 0; j0 < kPerLane; j0 += 2) {
-                    if (wave == kNW - 1) break;  // uniform
-                    const uint4 tv = ta[j0 / 2];
-                    const unsigned aw[4] = {tv.x, tv.y, tv.z, tv.w};
-                    unsigned ad[2][4];
-                    float gv[2][4];
-                    float2 c1[2], c2[2];
-                    bool act[2];
+                    const int nb = j0 + 2 <= kPerLane ? 2 : kPerLane - j0;
+                    float g[2][4];
+                    float2 cp[2], cq[2];
+                    bool on[2];
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const int code = j0 + i < kPerLane ? bq[j0 + i] : -1;
-                        act[i] = code >= 0;
-                        const int P = act[i] ? (code & 0xff) : 0, Q = act[i] ? (code >> 8) : 1;
-                        c1[i] = pc[P];
-                        c2[i] = pc[Q];
-                        act[i] = act[i] & ((c1[i].x != 0.f) | (c2[i].x != 0.f));
-                        ad[i][0] = aw[2 * i] & 0xffffu;
-                        ad[i][1] = aw[2 * i] >> 16;
-                        ad[i][2] = aw[2 * i + 1] & 0xffffu;
-                        ad[i][3] = aw[2 * i + 1] >> 16;
+                    for (int i = 0; i < nb; ++i) {
+                        const int c = code[j0 + i];
+                        on[i] = j0 + i < kPerLane - 1 || has4;
+                        cp[i] = pc[c & 63];
+                        cq[i] = pc[(c >> 6) & 63];
+                        if (on[i]) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) g[i][e] = lds_at(cur, (e * kRoleWords + (c >> 12)) * 4);
+                        }
                     }
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        if (act[i]) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) gv[i][e] = lds_at(G, ad[i][e]);
+                    for (int i = 0; i < nb; ++i)
+                        if (on[i]) {
+                            rotate_block(g[i], cp[i], cq[i]);
+                            lds_at(nxt, dst[j0 + i][0] & 0xffffu) = g[i][0];
+                            lds_at(nxt, dst[j0 + i][0] >> 16) = g[i][1];
+                            lds_at(nxt, dst[j0 + i][1] & 0xffffu) = g[i][2];
+                            lds_at(nxt, dst[j0 + i][1] >> 16) = g[i][3];
                         }
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        if (act[i]) {
-                            // rows of pair P, then columns of pair Q
-                            const float a1 = c1[i].x, b1 = c1[i].y, a2 = c2[i].x, b2 = c2[i].y;
-                            const float h11 = fmaf(-a1, gv[i][2], gv[i][0]), h12 = fmaf(-a1, gv[i][3], gv[i][1]);
-                            const float h21 = fmaf(b1, gv[i][0], gv[i][2]), h22 = fmaf(b1, gv[i][1], gv[i][3]);
-                            lds_at(G, ad[i][0]) = fmaf(-a2, h12, h11);
-                            lds_at(G, ad[i][1]) = fmaf(b2, h11, h12);
-                            lds_at(G, ad[i][2]) = fmaf(-a2, h22, h21);
-                            lds_at(G, ad[i][3]) = fmaf(b2, h21, h22);
-                        }
-                    ta[j0 / 2] = anext[j0 / 2];
                 }
             }
             if (k == 1 && tid == 0) flags[(sweep + 1) & 1] = 0;
@@ -411,20 +402,19 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
             if (wave < kNW - 1) F[7] = xi[wave * 64 + lane];
             if (wave > 0) S[0] = xi[((kNW - 1) + wave - 1) * 64 + lane];
 
-            // ---- multiply G and V^T back by the scales (gathered by index above)
+            // ---- multiply G and V^T back by the scales (gathered by position above)
             if (renorm) {
-                const int kn = k == 126 ? 0 : k + 1;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float sf = G[scale_word(index_at(8 * wave + j, kn))];
-                    const float ss = G[scale_word(index_at(127 - 8 * wave - j, kn))];
+                    const float sf = stab[8 * wave + j], ss = stab[127 - 8 * wave - j];
                     F[j] = make_float2(F[j].x * sf, F[j].y * sf);
                     S[j] = make_float2(S[j].x * ss, S[j].y * ss);
                 }
-                const float sj = G[scale_word(tid & 127)];
-                for (int e = tid; e < kD * kD; e += kThreads) {
-                    const int i = e >> 7, j = e & 127;
-                    if (i < j) G[i * kGP + j] *= G[scale_word(i)] * sj;
+                float *gn = reinterpret_cast<float *>(nxt);
+                for (int e = tid; e < kBufWords; e += kThreads) {
+                    const int r = e / kRoleWords, b = e - r * kRoleWords;
+                    const int pq = kTab.pq[b];
+                    gn[e] *= stab[pos_of(pq & 0xff, r >> 1)] * stab[pos_of(pq >> 8, r & 1)];
                 }
                 __syncthreads();
             }
@@ -437,12 +427,12 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
     }
 
     // 127 rounds per sweep: slot P again holds indices P and 127 - P.
-    float2 *dst = reinterpret_cast<float2 *>(vt_out + static_cast<int64_t>(blk) * kD * kD);
+    float2 *dstv = reinterpret_cast<float2 *>(vt_out + static_cast<int64_t>(blk) * kD * kD);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int P = 8 * wave + j;
-        dst[P * 64 + lane] = F[j];
-        dst[(127 - P) * 64 + lane] = S[j];
+        dstv[P * 64 + lane] = F[j];
+        dstv[(127 - P) * 64 + lane] = S[j];
     }
     if (tid == 0 && sweeps_out) sweeps_out[blk] = used;
 }
@@ -455,10 +445,6 @@ hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(jacobi_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
-    // Refilled on the caller's stream before every solve, so the solve never
-    // depends on another stream's work; concurrent fills write identical values.
-    constexpr int kTabThreads = 127 * kGenLanes * kPerLane;
-    hipLaunchKernelGGL(jacobi_table_kernel, dim3((kTabThreads + 255) / 256), dim3(256), 0, st);
     hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), kLdsBytes, st,
                        gpart, splits, vt, sweeps, max_sweeps, tol, stop_tol);
     return hipGetLastError();
