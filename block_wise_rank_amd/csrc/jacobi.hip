@@ -315,6 +315,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
             }
 
             if (wave == kNW - 1) {
+                __builtin_amdgcn_s_setprio(2);  // the round's longest chain goes first on its SIMD
                 // ---- wave 7: this pair's own element moves into a block; block
                 // (Pa, Pb) is rotated, its selected element becomes the element of
                 // round k + 1's pair Pn, whose rotation is computed here.
@@ -350,8 +351,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                     s1 = s2 = 1.f;
                     gp = gn * sfa * sfb;
                 }
-                const float ratio = s2 * __builtin_amdgcn_rcpf(s1);
-                float al = r.t * ratio, be = r.t * __builtin_amdgcn_rcpf(ratio);
+                float al = r.t * (s2 * __builtin_amdgcn_rcpf(s1)), be = r.t * (s1 * __builtin_amdgcn_rcpf(s2));
                 if ((al == 0.f) | (be == 0.f)) {  // negligible rotation: none
                     r = Rot{1.f, 0.f, an, bn, false};
                     al = be = 0.f;
@@ -364,6 +364,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                 rotp = r.rot;
                 if (r.rot && gt * gt > stop_tol * stop_tol * fabsf(an * bn))
                     flags[(sweep + (last_round ? 1 : 0)) & 1] = 1;
+                __builtin_amdgcn_s_setprio(0);
             } else {
                 // ---- waves 0..6: generic blocks, two at a time (loads, then stores)
 #pragma unroll
