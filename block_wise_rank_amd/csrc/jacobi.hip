@@ -77,7 +77,8 @@ constexpr int kGBytes = 2 * kBufWords * 4;
 constexpr int kPrmBytes = 2 * 64 * 8;             // (alpha, beta) per pair, double-buffered
 constexpr int kXchBytes = 2 * 2 * (kNW - 1) * 64 * 8;
 constexpr int kStabBytes = 128 * 4;               // scales by position at renormalisation
-constexpr int kLdsBytes = kGBytes + kPrmBytes + kXchBytes + kStabBytes + 16;  // + flags
+constexpr int kRecBytes = 64 * 16;                // per pair (new a, new b, scale a, scale b)
+constexpr int kLdsBytes = kGBytes + kPrmBytes + kXchBytes + kStabBytes + 16 + kRecBytes;  // + flags
 static_assert(kLdsBytes <= 80 * 1024, "two workgroups per CU");
 static_assert(kPerLane == 5, "generic block slots per lane");
 static_assert(kBufWords * 4 < 65536, "16-bit byte offsets within a buffer");
@@ -87,13 +88,23 @@ constexpr int next_pos(int p) { return p == 0 ? 0 : (p == 1 ? 127 : p - 1); }
 constexpr int slot_of(int p) { return p <= 63 ? p : 127 - p; }
 constexpr int role_of(int p) { return p <= 63 ? 0 : 1; }  // 0: first row, 1: second row
 constexpr int pos_of(int slot, int role) { return role == 0 ? slot : 127 - slot; }
-constexpr int block_index(int P, int Q) { return P * 63 - P * (P - 1) / 2 + (Q - P - 1); }  // P < Q, row-major
+constexpr int rowmajor_index(int P, int Q) { return P * 63 - P * (P - 1) / 2 + (Q - P - 1); }  // P < Q
 // The next round's pair P' lies in block (Pa, Pb) of this round, element role kSel.
 constexpr int next_pair_a(int Pn) { return Pn == 0 ? 0 : (Pn == 63 ? 62 : Pn - 1); }
 constexpr int next_pair_b(int Pn) { return Pn == 0 ? 1 : (Pn == 63 ? 63 : Pn + 1); }
 constexpr int next_pair_role(int Pn) { return Pn == 0 ? 0 : (Pn == 63 ? 3 : 2); }
 constexpr bool next_pair_block(int P, int Q) {
     return Q == P + 2 || (P == 0 && Q == 1) || (P == 62 && Q == 63);
+}
+// Storage index of block (P, Q), P < Q: the 64 next-pair blocks first, in the
+// order of the pair they feed (so wave 7's lanes read consecutive words), then
+// the generic blocks in row-major order.
+constexpr int block_index(int P, int Q) {
+    if (next_pair_block(P, Q)) return P == 0 && Q == 1 ? 0 : (P == 62 && Q == 63 ? 63 : P + 1);
+    // next-pair blocks before (P, Q) in row-major order: (0, 1), (p, p + 2) for
+    // p < P, and (P, P + 2) when it precedes Q
+    const int before = 1 + (P < 62 ? P : 62) + (P <= 61 && P + 2 < Q ? 1 : 0);
+    return 64 + rowmajor_index(P, Q) - before;
 }
 // Word offset (role * kRoleWords + block) of the element at positions (a, b),
 // or -1 - slot when both positions are one slot's pair.
@@ -116,11 +127,12 @@ constexpr Tables make_tables() {
     int n = 0, g = 0;
     for (int P = 0; P < 64; ++P)
         for (int Q = P + 1; Q < 64; ++Q) {
-            t.pq[n] = static_cast<uint16_t>(P | (Q << 8));
-            if (!next_pair_block(P, Q)) t.gen[g++] = static_cast<uint16_t>(n);
+            const int b = block_index(P, Q);
+            t.pq[b] = static_cast<uint16_t>(P | (Q << 8));
+            if (!next_pair_block(P, Q)) t.gen[g++] = static_cast<uint16_t>(b);
             for (int r = 0; r < 4; ++r) {
                 const int w = element_word(next_pos(pos_of(P, r >> 1)), next_pos(pos_of(Q, r & 1)));
-                t.dst[n][r] = static_cast<uint16_t>(w >= 0 ? 4 * w : 0xffff);  // 0xffff: a pair's element
+                t.dst[b][r] = static_cast<uint16_t>(w >= 0 ? 4 * w : 0xffff);  // 0xffff: a pair's element
             }
             ++n;
         }
@@ -138,15 +150,18 @@ constexpr bool check_tables() {
     const Tables t = make_tables();
     for (int Pn = 0; Pn < 64; ++Pn) {
         const int b = block_index(next_pair_a(Pn), next_pair_b(Pn));
+        if (b != Pn) return false;
         if (element_word(next_pos(pos_of(next_pair_a(Pn), next_pair_role(Pn) >> 1)),
                          next_pos(pos_of(next_pair_b(Pn), next_pair_role(Pn) & 1))) != -1 - Pn)
             return false;
         if (t.dst[b][next_pair_role(Pn)] != 0xffff) return false;
         if (element_word(next_pos(Pn), next_pos(127 - Pn)) < 0) return false;
     }
-    for (int i = 0; i < kGeneric; ++i)
+    for (int i = 0; i < kGeneric; ++i) {
+        if (t.gen[i] != 64 + i) return false;
         for (int r = 0; r < 4; ++r)
             if (t.dst[t.gen[i]][r] == 0xffff) return false;
+    }
     return true;
 }
 static_assert(check_tables(), "position-space move map");
@@ -202,6 +217,11 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
     float2 *xch = reinterpret_cast<float2 *>(smem + kGBytes + kPrmBytes);     // [2][2][7][64]
     float *stab = reinterpret_cast<float *>(smem + kGBytes + kPrmBytes + kXchBytes);  // [128]
     int *flags = reinterpret_cast<int *>(smem + kGBytes + kPrmBytes + kXchBytes + kStabBytes);
+    // Per pair, after the current round's rotation: its diagonal entries (true)
+    // and the scales of its first and second row.  Only wave 7 touches it; a
+    // round reads its neighbours' entries before any lane rewrites its own, so
+    // one buffer suffices.
+    float4 *rec = reinterpret_cast<float4 *>(smem + kGBytes + kPrmBytes + kXchBytes + kStabBytes + 16);
 
     const int blk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -224,21 +244,18 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
     }
 
     // Wave 7 state of pair Pn = lane: its own element (stored form, before this
-    // round's rotation), whether this round rotates it, and after this round's
-    // rotation the diagonal entries (true) and scales of its first and second row.
+    // round's rotation) and whether this round rotates it.
     const int Pn = lane;
     const int Pa = next_pair_a(Pn), Pb = next_pair_b(Pn), sel = next_pair_role(Pn);
-    const int sblk = block_index(Pa, Pb);
-    float gp = 0.f, rna = 0.f, rnb = 0.f, rsa = 1.f, rsb = 1.f;
+    const int sblk = block_index(Pa, Pb);  // = Pn
+    float gp = 0.f;
     bool rotp = false;
     if (wave == kNW - 1) {
         const float a = gram(Pn, Pn), b = gram(127 - Pn, 127 - Pn);
         gp = gram(Pn, 127 - Pn);
         const Rot r = jacobi_rotation(a, b, gp, tol);  // scales start at 1: alpha = beta = t
         prm[Pn] = make_float2(r.t, r.t);
-        rna = r.na;
-        rnb = r.nb;
-        rsa = rsb = r.c;
+        rec[Pn] = make_float4(r.na, r.nb, r.c, r.c);
         rotp = r.rot;
         if (r.rot && gp * gp > stop_tol * stop_tol * fabsf(a * b)) flags[0] = 1;
     }
@@ -321,6 +338,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                 // round k + 1's pair Pn, whose rotation is computed here.
                 lds_at(nxt, pdst) = rotp ? 0.f : gp;
                 const float2 A = pc[Pa], B = pc[Pb];
+                const float4 RA = rec[Pa], RB = rec[Pb];
                 float h[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) h[e] = lds_at(cur, (e * kRoleWords + sblk) * 4);
@@ -333,14 +351,10 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                 if (sel != 3) lds_at(nxt, sdst1 >> 16) = h[3];
                 // new diagonal entries and scales of the rows that form pair Pn next
                 // round (pair Pa's second row and pair Pb's first row; ends differ)
-                const float a_na = __shfl(rna, Pa, 64), a_nb = __shfl(rnb, Pa, 64);
-                const float a_sa = __shfl(rsa, Pa, 64), a_sb = __shfl(rsb, Pa, 64);
-                const float b_na = __shfl(rna, Pb, 64), b_nb = __shfl(rnb, Pb, 64);
-                const float b_sa = __shfl(rsa, Pb, 64), b_sb = __shfl(rsb, Pb, 64);
-                const float an = Pn == 0 ? a_na : (Pn == 63 ? b_nb : b_na);
-                const float bn = Pn == 0 ? b_na : a_nb;
-                const float sfa = Pn == 0 ? a_sa : (Pn == 63 ? b_sb : b_sa);
-                const float sfb = Pn == 0 ? b_sa : a_sb;
+                const float an = Pn == 0 ? RA.x : (Pn == 63 ? RB.y : RB.x);
+                const float bn = Pn == 0 ? RB.x : RA.y;
+                const float sfa = Pn == 0 ? RA.z : (Pn == 63 ? RB.w : RB.z);
+                const float sfb = Pn == 0 ? RB.z : RA.w;
                 const float gt = gn * sfa * sfb;
                 Rot r = jacobi_rotation(an, bn, gt, tol);
                 float s1 = sfa, s2 = sfb;
@@ -357,10 +371,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
                     al = be = 0.f;
                 }
                 prm[(cb ^ 1) * 64 + Pn] = make_float2(al, be);
-                rna = r.na;
-                rnb = r.nb;
-                rsa = s1 * r.c;
-                rsb = s2 * r.c;
+                rec[Pn] = make_float4(r.na, r.nb, s1 * r.c, s2 * r.c);
                 rotp = r.rot;
                 if (r.rot && gt * gt > stop_tol * stop_tol * fabsf(an * bn))
                     flags[(sweep + (last_round ? 1 : 0)) & 1] = 1;
