@@ -70,19 +70,38 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc2[r] = 0.f;
 
+    // bf16 X: the next 32-token tile's fragments are loaded while this tile's
+    // products run (one tile of latency cover).
+    u16x8_t xb[NX == 1 ? 8 : 1];
+    auto load_x = [&](int t0) {
+        if constexpr (NX == 1) {
+            const uint16_t *xr = static_cast<const uint16_t *>(x) + base +
+                                 static_cast<int64_t>(t0 + (lane & 31)) * row_stride + 8 * (lane >> 5);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) xb[ks] = *reinterpret_cast<const u16x8_t *>(xr + 16 * ks);
+        }
+    };
+    load_x(0);
     for (int t0 = 0; t0 < T; t0 += 32) {
         const int t = t0 + (lane & 31);
-        f32x16_t acc = zero16();
+        f32x16_t acc = zero16(), acc1 = zero16();
+        u16x8_t cur[NX == 1 ? 8 : 1];
+        if constexpr (NX == 1) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) cur[ks] = xb[ks];
+            load_x(t0 + 32 < T ? t0 + 32 : t0);  // the last tile reloads itself (unused)
+            // keep the scheduler from sinking those loads back between the products
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int j0 = 16 * ks + 8 * (lane >> 5);
             if constexpr (NX == 1) {
-                const uint16_t *xr = static_cast<const uint16_t *>(x) + base +
-                                     static_cast<int64_t>(t) * row_stride + j0;
-                const u16x8_t fb = *reinterpret_cast<const u16x8_t *>(xr);
-                acc = mfma32x32x16(fa[0][ks], fb, acc);
-                acc = mfma32x32x16(fa[1][ks], fb, acc);
-                acc = mfma32x32x16(fa[2][ks], fb, acc);
+                // two independent accumulation chains (even / odd k-steps)
+                f32x16_t &a = (ks & 1) ? acc1 : acc;
+                a = mfma32x32x16(fa[0][ks], cur[ks], a);
+                a = mfma32x32x16(fa[1][ks], cur[ks], a);
+                a = mfma32x32x16(fa[2][ks], cur[ks], a);
             } else {
                 const float *xr = static_cast<const float *>(x) + base +
                                   static_cast<int64_t>(t) * row_stride + j0;
@@ -105,6 +124,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
                         if (sa + sb <= 2) acc = mfma32x32x16(fa[sa][ks], fb[sb], acc);
             }
         }
+        if constexpr (NX == 1) acc += acc1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc2[r] += acc[r] * acc[r];
     }
@@ -117,15 +137,17 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     __syncthreads();
 
     // Sort descending (rank by counting; ties keep index order) and fix signs.
+    if (tid < kD) sig[tid] = sqrtf(ss[tid]);
+    __syncthreads();
     if (tid < kD) {
-        const float si = sqrtf(ss[tid]);
+        const float si = sig[tid];
         int pos = 0;
         for (int j = 0; j < kD; ++j) {
-            const float sj = sqrtf(ss[j]);
+            const float sj = sig[j];
             pos += (sj > si) || (sj == si && j < tid);
         }
         perm[pos] = tid;
-        sig[pos] = si;
+        ss[pos] = si;  // sorted values (ss is free again)
     }
     // Sign of eigenvector i: its largest-magnitude entry (first one on ties) positive.
     for (int i = wave; i < kD; i += 4) {
@@ -152,7 +174,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
         if (lane == 0) sgn[i] = (bval < 0.f) ? -1.f : 1.f;
     }
     __syncthreads();
-    if (tid < kD) sigma[static_cast<int64_t>(blk) * kD + tid] = sig[tid];
+    if (tid < kD) sigma[static_cast<int64_t>(blk) * kD + tid] = ss[tid];
     for (int e = tid; e < kD * kD; e += 256) {
         const int pos = e >> 7, j = e & 127;
         const int src = perm[pos];
