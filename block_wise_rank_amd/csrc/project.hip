@@ -12,6 +12,12 @@
 // tiles of X stream in as 16-byte loads of 8 consecutive features.  fp32
 // storage splits V (and fp32 X) into three bf16 terms for fp32-accurate
 // products.  Grid: (block, 256-token part).
+//
+// bf16 X -> bf16 factors (the storage the method runs on) has its own kernel:
+// 1024-token parts (B fragments built twice per 2048-token block instead of
+// eight times), the next X tile loaded while the current one's products run,
+// and each wave's 32 rank rows collected for 128 tokens in LDS so that A^T is
+// written as whole 256-byte row pieces with 16-byte stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -210,6 +216,95 @@ __global__ __launch_bounds__(256) void project_kernel(
     }
 }
 
+constexpr int kPartBF = 1024;   // tokens per workgroup (bf16 path)
+constexpr int kStageT = 128;    // tokens collected per flush
+constexpr int kStageP = 264;    // LDS pitch (bytes) of a staged rank row (256 B + 8)
+
+__global__ __launch_bounds__(256) void project_bf16_kernel(
+    const uint16_t *__restrict__ x, const int64_t *__restrict__ row0, int64_t row_stride, int T,
+    const float *__restrict__ vt, const int32_t *__restrict__ rank,
+    const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off, uint8_t *__restrict__ arena) {
+    __shared__ __align__(16) uint8_t stage[4][32 * kStageP];
+    const int blk = blockIdx.x, part = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = rank[blk];
+    if (32 * wave >= r) return;  // no rank rows for this wave (waves are independent)
+    const int t_begin = part * kPartBF;
+    const int t_end = min(T, t_begin + kPartBF);
+    uint16_t *Ab = reinterpret_cast<uint16_t *>(arena + a_off[blk]);
+    uint16_t *Bb = reinterpret_cast<uint16_t *>(arena + b_off[blk]);
+
+    // B~ fragments: rank row i = 32 wave + lane % 32, features 16 ks + 8 (lane / 32) + e
+    const int i = 32 * wave + (lane & 31);
+    const bool row_ok = i < r;
+    const float *vrow = vt + static_cast<int64_t>(blk) * kD * kD + static_cast<int64_t>(i) * kD;
+    u16x8_t fa[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (row_ok) {
+            a = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5));
+            b = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5) + 4);
+        }
+        const uint32_t w0 = f32x2_to_bf16x2_bits(a.x, a.y), w1 = f32x2_to_bf16x2_bits(a.z, a.w);
+        const uint32_t w2 = f32x2_to_bf16x2_bits(b.x, b.y), w3 = f32x2_to_bf16x2_bits(b.z, b.w);
+        fa[ks] = __builtin_bit_cast(u16x8_t, make_uint4(w0, w1, w2, w3));
+        if (part == 0 && row_ok)  // B row i, features 16 ks + 8 (lane / 32) ..
+            *reinterpret_cast<uint4 *>(Bb + i * kD + 16 * ks + 8 * (lane >> 5)) = make_uint4(w0, w1, w2, w3);
+    }
+
+    const uint16_t *xb = x + (row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride) + 8 * (lane >> 5);
+    u16x8_t xn[8];
+    auto load_x = [&](int t0) {
+        const uint16_t *xr = xb + static_cast<int64_t>(t0 + (lane & 31)) * row_stride;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) xn[ks] = *reinterpret_cast<const u16x8_t *>(xr + 16 * ks);
+    };
+    uint8_t *stg = stage[wave];
+    load_x(t_begin);
+    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+        u16x8_t xc[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) xc[ks] = xn[ks];
+        load_x(t0 + 32 < t_end ? t0 + 32 : t0);  // the last tile reloads itself (unused)
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16_t acc = zero16(), acc1 = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ks += 2) {
+            acc = mfma32x32x16(fa[ks], xc[ks], acc);
+            acc1 = mfma32x32x16(fa[ks + 1], xc[ks + 1], acc1);
+        }
+        acc += acc1;
+        // acc[q]: rank row 8 (q / 4) + 4 (lane / 32) + q % 4 of this wave, token lane % 32
+        const int tt = (t0 - t_begin) & (kStageT - 1);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+            *reinterpret_cast<uint16_t *>(stg + row * kStageP + (tt + (lane & 31)) * 2) = f32_to_bf16_bits(acc[q]);
+        }
+        if (tt + 32 == kStageT || t0 + 32 >= t_end) {
+            // flush: 32 rows x (tt + 32) tokens; 16 lanes per row, 16 bytes each
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int n16 = (tt + 32) / 8;  // 16-byte pieces per row
+            const int tok0 = t0 + 32 - (tt + 32);
+#pragma unroll
+            for (int rr = 0; rr < 32; rr += 4) {
+                const int row = rr + (lane >> 4), piece = lane & 15;
+                const int ir = 32 * wave + row;
+                if (ir < r && piece < n16)
+                    *reinterpret_cast<uint4 *>(Ab + static_cast<int64_t>(ir) * T + tok0 + 8 * piece) =
+                        *reinterpret_cast<const uint4 *>(stg + row * kStageP + piece * 16);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
@@ -217,6 +312,12 @@ hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_
                           const int64_t *a_off, const int64_t *b_off, void *arena, int out_type,
                           float *a_scale, float *b_scale, hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
+    if (x_type == kBF16 && out_type == kBF16) {
+        const dim3 g(static_cast<unsigned>(n_blocks), static_cast<unsigned>((block_len + kPartBF - 1) / kPartBF));
+        hipLaunchKernelGGL(project_bf16_kernel, g, dim3(256), 0, st, static_cast<const uint16_t *>(x), row0,
+                           row_stride, block_len, vt, rank, a_off, b_off, static_cast<uint8_t *>(arena));
+        return hipGetLastError();
+    }
     const dim3 grid(static_cast<unsigned>(n_blocks),
                     static_cast<unsigned>((block_len + kTokensPerWG - 1) / kTokensPerWG));
     uint8_t *ar = static_cast<uint8_t *>(arena);
