@@ -10,6 +10,13 @@
 //
 // One workgroup (4 waves) per (block, token split); wave w owns the 64 x 64
 // quadrant (w / 2, w % 2) of G as 2 x 2 tiles of 32 x 32.
+//
+// bf16 inputs (the method's cache) have their own kernel: tiles are
+// double-buffered in LDS with the next tile's loads in flight during the
+// current tile's products, and the fragments are read with transposing LDS
+// loads (two per fragment instead of eight 16-bit reads), from rows of 288
+// bytes so that the 4 rows x 64 bytes of a half-wave's read cover every bank
+// exactly twice.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -116,6 +123,83 @@ __global__ __launch_bounds__(256) void gram_kernel(const void *__restrict__ x,
             }
 }
 
+constexpr int kBP = 288;  // LDS row pitch in bytes (bf16 kernel)
+
+__global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t *__restrict__ x,
+                                                        const int64_t *__restrict__ row0,
+                                                        int64_t row_stride, int T, int splits,
+                                                        float *__restrict__ gpart) {
+    __shared__ __align__(16) uint8_t tile[2][kTT * kBP];
+    const int blk = blockIdx.x / splits;
+    const int sp = blockIdx.x - blk * splits;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int span = T / splits;
+    const int t_begin = sp * span;
+    const uint16_t *xb = x + (row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride);
+    const int mb = wave >> 1, nb = wave & 1;
+    const int g = lane >> 4, j = lane & 15;  // 16-lane group, lane within it
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = zero16();
+
+    // tile loads: token row c >> 4, 16-byte piece c & 15 for c = tid + 256 u
+    const int64_t off0 = static_cast<int64_t>(tid >> 4) * row_stride + (tid & 15) * 8;
+    const int64_t rstep = 16 * row_stride;  // c + 256 is 16 token rows further
+    const int so = (tid >> 4) * kBP + (tid & 15) * 16;
+    uint4 x0, x1, x2, x3;
+    auto load = [&](int t0) {
+        const uint16_t *p = xb + static_cast<int64_t>(t0) * row_stride + off0;
+        x0 = *reinterpret_cast<const uint4 *>(p);
+        x1 = *reinterpret_cast<const uint4 *>(p + rstep);
+        x2 = *reinterpret_cast<const uint4 *>(p + 2 * rstep);
+        x3 = *reinterpret_cast<const uint4 *>(p + 3 * rstep);
+    };
+    const int n_tiles = span / kTT;
+    load(t_begin);
+    for (int it = 0; it < n_tiles; ++it) {
+        uint8_t *tb = tile[it & 1];
+        *reinterpret_cast<uint4 *>(tb + so) = x0;
+        *reinterpret_cast<uint4 *>(tb + so + 16 * kBP) = x1;
+        *reinterpret_cast<uint4 *>(tb + so + 32 * kBP) = x2;
+        *reinterpret_cast<uint4 *>(tb + so + 48 * kBP) = x3;
+        if (it + 1 < n_tiles) load(t_begin + (it + 1) * kTT);
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < kTT; ks += 16) {
+            // lane (g, j): features base + 16 (g % 2) + j, tokens ks + 8 (g / 2) + 4 h + 0..3
+            const uint8_t *rowp = tb + (ks + 8 * (g >> 1) + (j >> 2)) * kBP + (16 * (g & 1) + 4 * (j & 3)) * 2;
+            u16x8_t fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint8_t *pa = rowp + (64 * mb + 32 * i) * 2;
+                const uint8_t *pb = rowp + (64 * nb + 32 * i) * 2;
+                fa[i] = cat8(lds_read_tr16(pa), lds_read_tr16(pa + 4 * kBP));
+                fb[i] = cat8(lds_read_tr16(pb), lds_read_tr16(pb + 4 * kBP));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mfma32x32x16(fa[i], fb[jj], acc[i][jj]);
+        }
+    }
+
+    float *gp = gpart + (static_cast<int64_t>(blk) * splits + sp) * kD * kD;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 64 * mb + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int col = 64 * nb + 32 * jj + (lane & 31);
+                gp[row * kD + col] = acc[i][jj][r];
+            }
+}
+
 }  // namespace
 
 hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
@@ -123,8 +207,8 @@ hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t r
     if (n_blocks <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(n_blocks * splits));
     if (x_type == kBF16)
-        hipLaunchKernelGGL(gram_kernel<1>, grid, dim3(256), 0, st, x, row0, row_stride, block_len,
-                           splits, gpart);
+        hipLaunchKernelGGL(gram_bf16_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t *>(x), row0,
+                           row_stride, block_len, splits, gpart);
     else
         hipLaunchKernelGGL(gram_kernel<3>, grid, dim3(256), 0, st, x, row0, row_stride, block_len,
                            splits, gpart);
