@@ -66,9 +66,10 @@ KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "jacobi": ["jacobi.hip"],
 
 def kernel_key(name):
     """libmilo kernel name (as rocprofv3 prints it) -> bench kernel key."""
-    for frag, key in (("gram_kernel", "gram"), ("jacobi_kernel", "jacobi"), ("refine_kernel", "refine"),
-                      ("alloc_kernel", "alloc"), ("project_kernel", "project"),
-                      ("reconstruct_kernel", "reconstruct"), ("decode_combine_kernel", "decode_combine"),
+    for frag, key in (("gram_kernel", "gram"), ("gram_bf16_kernel", "gram"), ("jacobi_kernel", "jacobi"),
+                      ("refine_kernel", "refine"), ("alloc_kernel", "alloc"), ("project_kernel", "project"),
+                      ("project_bf16_kernel", "project"), ("reconstruct_kernel", "reconstruct"),
+                      ("reconstruct_bf16_kernel", "reconstruct"), ("decode_combine_kernel", "decode_combine"),
                       ("decode_tables_kernel", "decode_tables")):
         if frag in name:
             return key
