@@ -81,6 +81,7 @@ constexpr int kRecBytes = 64 * 16;                // per pair (new a, new b, sca
 constexpr int kLdsBytes = kGBytes + kPrmBytes + kXchBytes + kStabBytes + 16 + kRecBytes;  // + flags
 static_assert(kLdsBytes <= 80 * 1024, "two workgroups per CU");
 static_assert(kPerLane == 5, "generic block slots per lane");
+constexpr int kBatch = 2;                         // generic blocks whose loads are issued together
 static_assert(kBufWords * 4 < 65536, "16-bit byte offsets within a buffer");
 
 // ---- the tournament in position space (compile time) ----
@@ -164,11 +165,8 @@ constexpr bool check_tables() {
     }
     return true;
 }
-static_assert(check_tables(), "position-space move map");
+static_assert(check_tables(), "position-space move map");  // includes gen[i] == 64 + i
 
-__device__ __forceinline__ float &lds_at(uint8_t *base, unsigned byte_off) {
-    return *reinterpret_cast<float *>(base + byte_off);
-}
 
 struct Rot {
     float c, t, na, nb;
@@ -207,22 +205,271 @@ __device__ __forceinline__ void rotate_block(float (&g)[4], float2 p, float2 q) 
     g[3] = fmaf(q.y, h21, h22);
 }
 
+// LDS of one workgroup; static, so that its address is known and every offset
+// below folds into the LDS instructions' immediate field.
+__shared__ __align__(16) uint8_t g_lds[kLdsBytes];
+constexpr int kPrmOff = kGBytes;                                   // [2][64] (alpha, beta)
+constexpr int kXchOff = kPrmOff + kPrmBytes;                       // [2][2][7][64] rows crossing waves
+constexpr int kStabOff = kXchOff + kXchBytes;                      // [128] scales by position
+constexpr int kFlagOff = kStabOff + kStabBytes;                    // [2] "a sweep rotated" flags
+// Per pair, after the current round's rotation: its diagonal entries (true) and
+// the scales of its first and second row.  Only wave 7 touches it; a round reads
+// its neighbours' entries before any lane rewrites its own, so one buffer suffices.
+constexpr int kRecOff = kFlagOff + 16;
+__device__ __forceinline__ float &lds_f(uint32_t byte_off) { return *reinterpret_cast<float *>(g_lds + byte_off); }
+__device__ __forceinline__ float2 &lds_f2(uint32_t byte_off) { return *reinterpret_cast<float2 *>(g_lds + byte_off); }
+__device__ __forceinline__ float4 &lds_f4(uint32_t byte_off) { return *reinterpret_cast<float4 *>(g_lds + byte_off); }
+__device__ __forceinline__ int &lds_i(uint32_t byte_off) { return *reinterpret_cast<int *>(g_lds + byte_off); }
+
+// Registers of one lane for the whole solve.
+struct LaneState {
+    // Eigenvector rows of this wave's slots (components 2 lane, 2 lane + 1): F =
+    // first rows, S = second rows.  The rows of a wave move one slot per round
+    // along its F and S rings; the rings are renamed instead of moved: in phase
+    // ph (= rounds done mod 8) logical first-row slot j lives in F[(j + ph) & 7]
+    // and logical second-row slot j in S[(j - ph) & 7].
+    float2 F[8], S[8];
+    // Byte offsets of this lane's blocks, kept unpacked so that every LDS access
+    // of a round is one register plus an immediate (the buffer's offset).
+    // Waves 0..6, generic slot j = entry tid + 448 j of the generic list, i.e.
+    // block 64 + tid + 448 j: gb = slot 0's read offset (slot j's is gb + 1792 j),
+    // pq = the (alpha, beta) offsets of P and Q (low and high half), d = the
+    // next-round offsets of its four roles (two per word).  Wave 7 (no generic
+    // blocks) keeps in gb and d[0] the special block's read offset and next-round
+    // role offsets, in pq[1] the pair element's next-round offset, and in d[1],
+    // d[2] and d[3] its pair's (alpha, beta) and record (see the round below).
+    uint32_t gb, pq[kPerLane], d[kPerLane][2];
+    float gp;    // wave 7: this pair's own element (stored form, before this round's rotation)
+    bool rotp;   // wave 7: whether this round rotates it
+    bool has4;   // generic slot 4 is in use (it is partial)
+};
+
+struct Solve {
+    int k, sweep, used;     // round within the sweep, sweeps done, result
+    int wave, lane, tid, sel, blk, max_sweeps;
+    float tol, stop_tol;
+    float *vt_out;
+    int32_t *sweeps_out;
+};
+
+// V^T rows out: after 127 rounds slot P again holds indices P and 127 - P.
+template <int NPH>
+__device__ __forceinline__ void write_rows(const LaneState &L, const Solve &C, int ln) {
+    float2 *dstv = reinterpret_cast<float2 *>(C.vt_out + static_cast<int64_t>(C.blk) * kD * kD) + ln;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int P = 8 * C.wave + j;
+        dstv[P * 64] = L.F[(j + NPH) & 7];
+        dstv[(127 - P) * 64] = L.S[(j - NPH) & 7];
+    }
+}
+
+// Eigenvector rows of one round: rotate (identity when alpha = beta = 0), shift
+// along the ring, send the ends.  pc = this round's (alpha, beta) table.
+template <int PH>
+__device__ __forceinline__ void rotate_rows(LaneState &L, uint32_t pc, int wave, int ln, uint32_t xb) {
+    constexpr int f0 = PH & 7, f1 = (PH + 1) & 7, s7 = (7 - PH) & 7;
+    float4 ab[4];  // this wave's eight pairs, as broadcast reads
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ab[j] = lds_f4(pc + 64 * wave + 16 * j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float al = (j & 1) ? ab[j >> 1].z : ab[j >> 1].x;
+        const float be = (j & 1) ? ab[j >> 1].w : ab[j >> 1].y;
+        float2 &fr = L.F[(j + PH) & 7], &sr = L.S[(j - PH) & 7];
+        const float2 f = fr, s = sr;
+        fr = make_float2(fmaf(-al, s.x, f.x), fmaf(-al, s.y, f.y));
+        sr = make_float2(fmaf(be, f.x, s.x), fmaf(be, f.y, s.y));
+    }
+    // computed here (not sunk past the barrier, where they would cost copies)
+    asm volatile("" : "+v"(L.F[0]), "+v"(L.F[1]), "+v"(L.F[2]), "+v"(L.F[3]), "+v"(L.F[4]), "+v"(L.F[5]),
+                      "+v"(L.F[6]), "+v"(L.F[7]));
+    asm volatile("" : "+v"(L.S[0]), "+v"(L.S[1]), "+v"(L.S[2]), "+v"(L.S[3]), "+v"(L.S[4]), "+v"(L.S[5]),
+                      "+v"(L.S[6]), "+v"(L.S[7]));
+    // Round k + 1's position i holds round k's position i + 1 (127 -> 1 wraps to
+    // 1 -> 127): first rows move down one slot, second rows up one slot.  After
+    // the renaming, F[f0] is logical slot 7 and S[s7] logical slot 0.
+    if (wave > 0) lds_f2(xb + 8 * ((wave - 1) * 64 + ln)) = L.F[f0];
+    if (wave < kNW - 1) lds_f2(xb + 8 * (((kNW - 1) + wave) * 64 + ln)) = L.S[s7];
+    if (wave == 0) {  // position 0 stays, position 1 wraps to 127 (this wave's S slot 0)
+        const float2 p1 = L.F[f1];
+        L.F[f1] = L.F[f0];
+        L.S[s7] = p1;
+    }
+    if (wave == kNW - 1) L.F[f0] = L.S[s7];  // position 64 -> 63
+}
+
+// Lane l of wave 7 receives the value of lane l - 1 (shr) or l + 1 (shl); the
+// end lane keeps its own, which is what pairs 0 and 63 need.
+__device__ __forceinline__ float lane_prev(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x138, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_next(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x130, 0xf, 0xf, false));
+}
+
+// One round of the tournament in phase PH; true once the solve has ended (the
+// rows are then written out).
+template <int PH>
+__device__ __forceinline__ bool jacobi_round(LaneState &L, Solve &C) {
+    constexpr int cb = PH & 1;                        // buffer parity
+    constexpr uint32_t cur = cb * (kBufWords * 4), nxt = (cb ^ 1) * (kBufWords * 4);
+    constexpr uint32_t pc = kPrmOff + cb * 512, pn = kPrmOff + (cb ^ 1) * 512;
+    constexpr uint32_t xb = kXchOff + cb * (2 * (kNW - 1) * 64 * 8);
+    constexpr int f0 = PH & 7, f1 = (PH + 1) & 7, s7 = (7 - PH) & 7;
+    const int wave = C.wave;
+    int k = C.k;
+    asm volatile("" : "+s"(k));
+    int ln = C.lane;
+    asm volatile("" : "+v"(ln));
+    // unpacked in every round: hoisted out of the loop the halves would take
+    // registers the round needs
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) asm volatile("" : "+v"(L.pq[j]), "+v"(L.d[j][0]), "+v"(L.d[j][1]));
+    // rounds after which G and V^T are multiplied back by their scales
+    const bool renorm = (k == 63) | (k == 126);
+    const bool last_round = (k == 126);
+
+    if (wave == kNW - 1) {
+        __builtin_amdgcn_s_setprio(2);  // the round's longest chain goes first on its SIMD
+        // ---- wave 7: this pair's own element moves into a block; block (Pa, Pb)
+        // is rotated, its selected element becomes the element of round k + 1's
+        // pair Pn = lane, whose rotation is computed here.
+        const int sel = C.sel;
+        // the special block, written last round by the lanes that moved its elements
+        float h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = lds_f(cur + L.gb + e * kRoleWords * 4);
+        lds_f(nxt + L.pq[1]) = L.rotp ? 0.f : L.gp;
+        // this round's (alpha, beta) and records of pairs Pa = lane - 1 and Pb =
+        // lane + 1, computed last round by those lanes (held in unused slot registers)
+        const float wal = __uint_as_float(L.d[1][0]), wbe = __uint_as_float(L.d[1][1]);
+        const float4 wrc = make_float4(__uint_as_float(L.d[2][0]), __uint_as_float(L.d[2][1]),
+                                       __uint_as_float(L.d[3][0]), __uint_as_float(L.d[3][1]));
+        // this wave's rows (pairs 56 .. 63) while the block is in flight
+        rotate_rows<PH>(L, pc, wave, ln, xb);
+        const float2 A = make_float2(lane_prev(wal), lane_prev(wbe)), B = make_float2(lane_next(wal), lane_next(wbe));
+        rotate_block(h, A, B);
+        const float4 RA = make_float4(lane_prev(wrc.x), lane_prev(wrc.y), lane_prev(wrc.z), lane_prev(wrc.w));
+        const float4 RB = make_float4(lane_next(wrc.x), lane_next(wrc.y), lane_next(wrc.z), lane_next(wrc.w));
+        // the other three roles move on (the selected one's slot is unused)
+        const float gn = sel == 0 ? h[0] : (sel == 2 ? h[2] : h[3]);
+        if (sel != 0) lds_f(nxt + (L.d[0][0] & 0xffffu)) = h[0];
+        lds_f(nxt + (L.d[0][0] >> 16)) = h[1];
+        if (sel != 2) lds_f(nxt + (L.d[0][1] & 0xffffu)) = h[2];
+        if (sel != 3) lds_f(nxt + (L.d[0][1] >> 16)) = h[3];
+        // new diagonal entries and scales of the rows that form pair Pn next round
+        // (pair Pa's second row and pair Pb's first row; the ends differ)
+        const bool first = ln == 0, last = ln == 63;
+        const float an = first ? RA.x : (last ? RB.y : RB.x);
+        const float bn = first ? RB.x : RA.y;
+        const float sfa = first ? RA.z : (last ? RB.w : RB.z);
+        const float sfb = first ? RB.z : RA.w;
+        const float gt = gn * sfa * sfb;
+        Rot r = jacobi_rotation(an, bn, gt, C.tol);
+        float s1 = sfa, s2 = sfb;
+        L.gp = gn;
+        if (renorm) {  // uniform: scales gathered by next-round position, restart at 1
+            lds_f(kStabOff + 4 * ln) = sfa;
+            lds_f(kStabOff + 4 * (127 - ln)) = sfb;
+            s1 = s2 = 1.f;
+            L.gp = gn * sfa * sfb;
+        }
+        float al = r.t * (s2 * __builtin_amdgcn_rcpf(s1)), be = r.t * (s1 * __builtin_amdgcn_rcpf(s2));
+        if ((al == 0.f) | (be == 0.f)) {  // negligible rotation: none
+            r = Rot{1.f, 0.f, an, bn, false};
+            al = be = 0.f;
+        }
+        lds_f2(pn + 8 * ln) = make_float2(al, be);
+        L.d[1][0] = __float_as_uint(al);
+        L.d[1][1] = __float_as_uint(be);
+        L.d[2][0] = __float_as_uint(r.na);
+        L.d[2][1] = __float_as_uint(r.nb);
+        L.d[3][0] = __float_as_uint(s1 * r.c);
+        L.d[3][1] = __float_as_uint(s2 * r.c);
+        L.rotp = r.rot;
+        if (r.rot && gt * gt > C.stop_tol * C.stop_tol * fabsf(an * bn))
+            lds_i(kFlagOff + 4 * ((C.sweep + (last_round ? 1 : 0)) & 1)) = 1;
+        __builtin_amdgcn_s_setprio(0);
+    } else {
+        rotate_rows<PH>(L, pc, wave, ln, xb);
+        // ---- waves 0..6: generic blocks, kBatch at a time (loads, then stores)
+#pragma unroll
+        for (int j0 = 0; j0 < kPerLane; j0 += kBatch) {
+            const int nb = j0 + kBatch <= kPerLane ? kBatch : kPerLane - j0;
+            float g[kBatch][4];
+            float2 cp[kBatch], cq[kBatch];
+            bool on[kBatch];
+#pragma unroll
+            for (int i = 0; i < nb; ++i) {
+                const int j = j0 + i;
+                on[i] = j < kPerLane - 1 || L.has4;
+                cp[i] = lds_f2(pc + (L.pq[j] & 0xffffu));
+                cq[i] = lds_f2(pc + (L.pq[j] >> 16));
+                if (on[i]) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        g[i][e] = lds_f(cur + L.gb + 4 * kGenLanes * j + e * kRoleWords * 4);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < nb; ++i)
+                if (on[i]) {
+                    rotate_block(g[i], cp[i], cq[i]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t w = L.d[j0 + i][e >> 1];
+                        lds_f(nxt + ((e & 1) ? w >> 16 : w & 0xffffu)) = g[i][e];
+                    }
+                }
+        }
+    }
+    if (k == 1 && C.tid == 0) lds_i(kFlagOff + 4 * ((C.sweep + 1) & 1)) = 0;
+    __syncthreads();
+
+    // ---- receive the rows that crossed a wave boundary
+    if (wave < kNW - 1) L.F[f0] = lds_f2(xb + 8 * (wave * 64 + ln));
+    if (wave > 0) L.S[s7] = lds_f2(xb + 8 * (((kNW - 1) + wave - 1) * 64 + ln));
+
+    // ---- multiply G and V^T back by the scales (gathered by position above)
+    if (renorm) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float sf = lds_f(kStabOff + 4 * (8 * wave + j)), ss = lds_f(kStabOff + 4 * (127 - 8 * wave - j));
+            float2 &fr = L.F[(j + PH + 1) & 7], &sr = L.S[(j - PH - 1) & 7];
+            fr = make_float2(fr.x * sf, fr.y * sf);
+            sr = make_float2(sr.x * ss, sr.y * ss);
+        }
+        for (int e = C.tid; e < kBufWords; e += kThreads) {
+            const int r = e / kRoleWords, b = e - r * kRoleWords;
+            const int c = kTab.pq[b];
+            lds_f(nxt + 4 * e) *= lds_f(kStabOff + 4 * pos_of(c & 0xff, r >> 1)) *
+                                  lds_f(kStabOff + 4 * pos_of(c >> 8, r & 1));
+        }
+        __syncthreads();
+    }
+
+    // ---- end of a sweep
+    if (last_round) {
+        const int rot = lds_i(kFlagOff + 4 * (C.sweep & 1));
+        ++C.sweep;
+        if (!rot || C.sweep == C.max_sweeps) {
+            if (!rot) C.used = C.sweep;
+            write_rows<(PH + 1) & 7>(L, C, ln);
+            if (C.tid == 0 && C.sweeps_out) C.sweeps_out[C.blk] = C.used;
+            return true;
+        }
+        C.k = 0;
+    } else {
+        C.k = k + 1;
+    }
+    return false;
+}
+
 __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__restrict__ gpart, int splits,
                                                              float *__restrict__ vt_out,
                                                              int32_t *__restrict__ sweeps_out,
                                                              int max_sweeps, float tol, float stop_tol) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t *G = smem;                                                        // [2][4][kBlocks]
-    float2 *prm = reinterpret_cast<float2 *>(smem + kGBytes);                 // [2][64] (alpha, beta)
-    float2 *xch = reinterpret_cast<float2 *>(smem + kGBytes + kPrmBytes);     // [2][2][7][64]
-    float *stab = reinterpret_cast<float *>(smem + kGBytes + kPrmBytes + kXchBytes);  // [128]
-    int *flags = reinterpret_cast<int *>(smem + kGBytes + kPrmBytes + kXchBytes + kStabBytes);
-    // Per pair, after the current round's rotation: its diagonal entries (true)
-    // and the scales of its first and second row.  Only wave 7 touches it; a
-    // round reads its neighbours' entries before any lane rewrites its own, so
-    // one buffer suffices.
-    float4 *rec = reinterpret_cast<float4 *>(smem + kGBytes + kPrmBytes + kXchBytes + kStabBytes + 16);
-
     const int blk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -236,217 +483,76 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
     for (int e = tid; e < kBufWords; e += kThreads) {
         const int r = e / kRoleWords, b = e - r * kRoleWords;
         const int code = kTab.pq[b];
-        reinterpret_cast<float *>(G)[e] = gram(pos_of(code & 0xff, r >> 1), pos_of(code >> 8, r & 1));
+        lds_f(4 * e) = gram(pos_of(code & 0xff, r >> 1), pos_of(code >> 8, r & 1));
     }
     if (tid == 0) {
-        flags[0] = 0;
-        flags[1] = 0;
+        lds_i(kFlagOff) = 0;
+        lds_i(kFlagOff + 4) = 0;
     }
 
-    // Wave 7 state of pair Pn = lane: its own element (stored form, before this
-    // round's rotation) and whether this round rotates it.
+    LaneState L;
     const int Pn = lane;
     const int Pa = next_pair_a(Pn), Pb = next_pair_b(Pn), sel = next_pair_role(Pn);
     const int sblk = block_index(Pa, Pb);  // = Pn
-    float gp = 0.f;
-    bool rotp = false;
-    if (wave == kNW - 1) {
-        const float a = gram(Pn, Pn), b = gram(127 - Pn, 127 - Pn);
-        gp = gram(Pn, 127 - Pn);
-        const Rot r = jacobi_rotation(a, b, gp, tol);  // scales start at 1: alpha = beta = t
-        prm[Pn] = make_float2(r.t, r.t);
-        rec[Pn] = make_float4(r.na, r.nb, r.c, r.c);
-        rotp = r.rot;
-        if (r.rot && gp * gp > stop_tol * stop_tol * fabsf(a * b)) flags[0] = 1;
-    }
-
-    // Eigenvector rows of this wave's slots: F = first rows, S = second rows
-    // (components 2 lane, 2 lane + 1); initially slot P holds indices P, 127 - P.
-    float2 F[8], S[8];
+    // initially slot P holds indices P, 127 - P
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int P = 8 * wave + j, c0 = 2 * lane;
-        F[j] = make_float2(c0 == P ? 1.f : 0.f, c0 + 1 == P ? 1.f : 0.f);
-        S[j] = make_float2(c0 == 127 - P ? 1.f : 0.f, c0 + 1 == 127 - P ? 1.f : 0.f);
+        L.F[j] = make_float2(c0 == P ? 1.f : 0.f, c0 + 1 == P ? 1.f : 0.f);
+        L.S[j] = make_float2(c0 == 127 - P ? 1.f : 0.f, c0 + 1 == 127 - P ? 1.f : 0.f);
     }
-    // Generic blocks of this lane (waves 0..6): entries tid, tid + 448, ... of the
-    // generic list.  code = P | Q << 6 | block << 12; dst = next byte offsets of
-    // the four roles, two per word.
-    int code[kPerLane];
-    uint32_t dst[kPerLane][2];
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
         const int i = tid + kGenLanes * j;
         const bool has = wave < kNW - 1 && i < kGeneric;
-        const int b = has ? kTab.gen[i] : 0;
-        const int pq = kTab.pq[b];
-        code[j] = (pq & 0xff) | ((pq >> 8) << 6) | (b << 12);
-        dst[j][0] = kTab.dst[b][0] | (static_cast<uint32_t>(kTab.dst[b][1]) << 16);
-        dst[j][1] = kTab.dst[b][2] | (static_cast<uint32_t>(kTab.dst[b][3]) << 16);
+        const int b = wave == kNW - 1 ? (j == 0 ? sblk : 0) : (has ? kTab.gen[i] : 0);
+        const int c = kTab.pq[b];
+        if (j == 0) L.gb = 4u * b;
+        L.pq[j] = 8u * (c & 0xff) | (8u * (c >> 8)) << 16;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) L.d[j][e] = kTab.dst[b][2 * e] | static_cast<uint32_t>(kTab.dst[b][2 * e + 1]) << 16;
     }
-    const bool has4 = wave < kNW - 1 && tid + kGenLanes * (kPerLane - 1) < kGeneric;  // slot 4 is partial
-    // wave 7: next places of the special block's three other roles and of the
-    // pair's own element
-    const uint32_t sdst0 = kTab.dst[sblk][0] | (static_cast<uint32_t>(kTab.dst[sblk][1]) << 16);
-    const uint32_t sdst1 = kTab.dst[sblk][2] | (static_cast<uint32_t>(kTab.dst[sblk][3]) << 16);
-    const uint32_t pdst = kTab.pair_dst[Pn];
+    if (wave == kNW - 1) L.pq[1] = kTab.pair_dst[Pn];
+    // Wave 7: the rotation of pair Pn = lane for round 0; its (alpha, beta) and
+    // record stay in slot registers this wave does not use otherwise.
+    L.gp = 0.f;
+    L.rotp = false;
+    if (wave == kNW - 1) {
+        const float a = gram(Pn, Pn), b = gram(127 - Pn, 127 - Pn);
+        L.gp = gram(Pn, 127 - Pn);
+        const Rot r = jacobi_rotation(a, b, L.gp, tol);  // scales start at 1: alpha = beta = t
+        lds_f2(kPrmOff + 8 * Pn) = make_float2(r.t, r.t);
+        L.d[1][0] = L.d[1][1] = __float_as_uint(r.t);
+        L.d[2][0] = __float_as_uint(r.na);
+        L.d[2][1] = __float_as_uint(r.nb);
+        L.d[3][0] = L.d[3][1] = __float_as_uint(r.c);
+        L.rotp = r.rot;
+        if (r.rot && L.gp * L.gp > stop_tol * stop_tol * fabsf(a * b)) lds_i(kFlagOff) = 1;
+    }
+    // opaque from here on: kept as whole registers, not repacked
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+        asm volatile("" : "+v"(L.pq[j]), "+v"(L.d[j][0]), "+v"(L.d[j][1]));
+    asm volatile("" : "+v"(L.gb));
+    L.has4 = wave < kNW - 1 && tid + kGenLanes * (kPerLane - 1) < kGeneric;  // slot 4 is partial
     __syncthreads();
 
-    int used = -max_sweeps;
-    int gk = 0;  // rounds done so far (parity selects the buffers)
-    for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-        for (int kr = 0; kr < 127; ++kr, ++gk) {
-            int k = kr;
-            asm volatile("" : "+s"(k));
-            const int cb = gk & 1;
-            const float2 *pc = prm + cb * 64;
-            uint8_t *cur = G + cb * (kBufWords * 4);
-            uint8_t *nxt = G + (cb ^ 1) * (kBufWords * 4);
-            // rounds after which G and V^T are multiplied back by their scales
-            const bool renorm = (k == 63) | (k == 126);
-            const bool last_round = (k == 126);
-
-            // ---- eigenvector rows: rotate (identity when alpha = beta = 0), shift
-            // along the ring, send the ends
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float2 ab = pc[8 * wave + j];
-                const float2 f = F[j], s = S[j];
-                F[j] = make_float2(fmaf(-ab.x, s.x, f.x), fmaf(-ab.x, s.y, f.y));
-                S[j] = make_float2(fmaf(ab.y, f.x, s.x), fmaf(ab.y, f.y, s.y));
-            }
-            // Round k + 1's position i holds round k's position i + 1 (127 -> 1 wraps
-            // to 1 -> 127): first rows move down one slot, second rows up one slot.
-            float2 *xo = xch + cb * 2 * (kNW - 1) * 64;
-            if (wave > 0) xo[(wave - 1) * 64 + lane] = F[0];
-            if (wave < kNW - 1) xo[((kNW - 1) + wave) * 64 + lane] = S[7];
-            {
-                const float2 f1 = F[1], s7 = S[7];
-#pragma unroll
-                for (int j = 0; j < 7; ++j)
-                    if (j > 0 || wave > 0) F[j] = F[j + 1];  // index 0 never moves
-                if (wave == kNW - 1) F[7] = s7;
-#pragma unroll
-                for (int j = 7; j >= 1; --j) S[j] = S[j - 1];
-                if (wave == 0) S[0] = f1;
-            }
-
-            if (wave == kNW - 1) {
-                __builtin_amdgcn_s_setprio(2);  // the round's longest chain goes first on its SIMD
-                // ---- wave 7: this pair's own element moves into a block; block
-                // (Pa, Pb) is rotated, its selected element becomes the element of
-                // round k + 1's pair Pn, whose rotation is computed here.
-                lds_at(nxt, pdst) = rotp ? 0.f : gp;
-                const float2 A = pc[Pa], B = pc[Pb];
-                const float4 RA = rec[Pa], RB = rec[Pb];
-                float h[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = lds_at(cur, (e * kRoleWords + sblk) * 4);
-                rotate_block(h, A, B);
-                // the other three roles move on (the selected one's slot is unused)
-                const float gn = sel == 0 ? h[0] : (sel == 2 ? h[2] : h[3]);
-                if (sel != 0) lds_at(nxt, sdst0 & 0xffffu) = h[0];
-                lds_at(nxt, sdst0 >> 16) = h[1];
-                if (sel != 2) lds_at(nxt, sdst1 & 0xffffu) = h[2];
-                if (sel != 3) lds_at(nxt, sdst1 >> 16) = h[3];
-                // new diagonal entries and scales of the rows that form pair Pn next
-                // round (pair Pa's second row and pair Pb's first row; ends differ)
-                const float an = Pn == 0 ? RA.x : (Pn == 63 ? RB.y : RB.x);
-                const float bn = Pn == 0 ? RB.x : RA.y;
-                const float sfa = Pn == 0 ? RA.z : (Pn == 63 ? RB.w : RB.z);
-                const float sfb = Pn == 0 ? RB.z : RA.w;
-                const float gt = gn * sfa * sfb;
-                Rot r = jacobi_rotation(an, bn, gt, tol);
-                float s1 = sfa, s2 = sfb;
-                gp = gn;
-                if (renorm) {  // uniform: scales gathered by next-round position, restart at 1
-                    stab[Pn] = sfa;
-                    stab[127 - Pn] = sfb;
-                    s1 = s2 = 1.f;
-                    gp = gn * sfa * sfb;
-                }
-                float al = r.t * (s2 * __builtin_amdgcn_rcpf(s1)), be = r.t * (s1 * __builtin_amdgcn_rcpf(s2));
-                if ((al == 0.f) | (be == 0.f)) {  // negligible rotation: none
-                    r = Rot{1.f, 0.f, an, bn, false};
-                    al = be = 0.f;
-                }
-                prm[(cb ^ 1) * 64 + Pn] = make_float2(al, be);
-                rec[Pn] = make_float4(r.na, r.nb, s1 * r.c, s2 * r.c);
-                rotp = r.rot;
-                if (r.rot && gt * gt > stop_tol * stop_tol * fabsf(an * bn))
-                    flags[(sweep + (last_round ? 1 : 0)) & 1] = 1;
-                __builtin_amdgcn_s_setprio(0);
-            } else {
-                // ---- waves 0..6: generic blocks, two at a time (loads, then stores)
-#pragma unroll
-                for (int j0 = 0; j0 < kPerLane; j0 += 2) {
-                    const int nb = j0 + 2 <= kPerLane ? 2 : kPerLane - j0;
-                    float g[2][4];
-                    float2 cp[2], cq[2];
-                    bool on[2];
-#pragma unroll
-                    for (int i = 0; i < nb; ++i) {
-                        const int c = code[j0 + i];
-                        on[i] = j0 + i < kPerLane - 1 || has4;
-                        cp[i] = pc[c & 63];
-                        cq[i] = pc[(c >> 6) & 63];
-                        if (on[i]) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) g[i][e] = lds_at(cur, (e * kRoleWords + (c >> 12)) * 4);
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < nb; ++i)
-                        if (on[i]) {
-                            rotate_block(g[i], cp[i], cq[i]);
-                            lds_at(nxt, dst[j0 + i][0] & 0xffffu) = g[i][0];
-                            lds_at(nxt, dst[j0 + i][0] >> 16) = g[i][1];
-                            lds_at(nxt, dst[j0 + i][1] & 0xffffu) = g[i][2];
-                            lds_at(nxt, dst[j0 + i][1] >> 16) = g[i][3];
-                        }
-                }
-            }
-            if (k == 1 && tid == 0) flags[(sweep + 1) & 1] = 0;
-            __syncthreads();
-
-            // ---- receive the rows that crossed a wave boundary
-            const float2 *xi = xch + cb * 2 * (kNW - 1) * 64;
-            if (wave < kNW - 1) F[7] = xi[wave * 64 + lane];
-            if (wave > 0) S[0] = xi[((kNW - 1) + wave - 1) * 64 + lane];
-
-            // ---- multiply G and V^T back by the scales (gathered by position above)
-            if (renorm) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float sf = stab[8 * wave + j], ss = stab[127 - 8 * wave - j];
-                    F[j] = make_float2(F[j].x * sf, F[j].y * sf);
-                    S[j] = make_float2(S[j].x * ss, S[j].y * ss);
-                }
-                float *gn = reinterpret_cast<float *>(nxt);
-                for (int e = tid; e < kBufWords; e += kThreads) {
-                    const int r = e / kRoleWords, b = e - r * kRoleWords;
-                    const int pq = kTab.pq[b];
-                    gn[e] *= stab[pos_of(pq & 0xff, r >> 1)] * stab[pos_of(pq >> 8, r & 1)];
-                }
-                __syncthreads();
-            }
-        }
-        const int rot = flags[sweep & 1];
-        if (!rot) {
-            used = sweep + 1;
-            break;
-        }
+    Solve C{0, 0, -max_sweeps, wave, lane, tid, sel, blk, max_sweeps, tol, stop_tol, vt_out, sweeps_out};
+    if (max_sweeps <= 0) {
+        write_rows<0>(L, C, lane);
+        if (tid == 0 && sweeps_out) sweeps_out[blk] = C.used;
+        return;
     }
-
-    // 127 rounds per sweep: slot P again holds indices P and 127 - P.
-    float2 *dstv = reinterpret_cast<float2 *>(vt_out + static_cast<int64_t>(blk) * kD * kD);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int P = 8 * wave + j;
-        dstv[P * 64 + lane] = F[j];
-        dstv[(127 - P) * 64 + lane] = S[j];
+    for (;;) {
+        if (jacobi_round<0>(L, C)) return;
+        if (jacobi_round<1>(L, C)) return;
+        if (jacobi_round<2>(L, C)) return;
+        if (jacobi_round<3>(L, C)) return;
+        if (jacobi_round<4>(L, C)) return;
+        if (jacobi_round<5>(L, C)) return;
+        if (jacobi_round<6>(L, C)) return;
+        if (jacobi_round<7>(L, C)) return;
     }
-    if (tid == 0 && sweeps_out) sweeps_out[blk] = used;
 }
 
 }  // namespace
@@ -454,10 +560,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
 hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt, int32_t *sweeps,
                          int max_sweeps, float tol, float stop_tol, hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(jacobi_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), kLdsBytes, st,
+    hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), 0, st,
                        gpart, splits, vt, sweeps, max_sweeps, tol, stop_tol);
     return hipGetLastError();
 }
