@@ -7,9 +7,13 @@
 // second order in the eigenvector error, so recomputing it directly from X
 // gives singular values accurate to a few fp32 ulps of sigma_0.
 //
-// Y^T = V^T X^T runs on bf16 MFMA with V^T (fp32) split exactly into three
-// bf16 terms (and X too when it is fp32), keeping the products whose term
-// orders sum to <= 2; fp32 accumulation.  One workgroup (4 waves) per block;
+// Y^T = V^T X^T runs on bf16 MFMA with fp32 accumulation.  For fp32 X both
+// operands are split exactly into three bf16 terms, keeping the products whose
+// term orders sum to <= 2.  For bf16 X (exact as it stands) V is split into two
+// terms, which leaves a perturbation delta of V with |delta| <= 2^-17 |v|; its
+// effect on ||X v|| is first order only through v . delta (relative 2^-17) and
+// otherwise second order (||X delta||^2 / 2 sigma <= sigma_0^2 2^-35 / sigma),
+// far inside the singular values' tolerance.  One workgroup (4 waves) per block;
 // wave w owns eigenvectors 32w .. 32w + 31 and keeps their fragments in
 // registers while it streams every 32-token tile of X straight from memory
 // (8 consecutive features per lane = one 16-byte load for bf16).
@@ -49,7 +53,8 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     __syncthreads();
 
     // A fragments: row i = 32 * wave + lane % 32, k slots j = 16 ks + 8 (lane / 32) + e.
-    u16x8_t fa[3][8];
+    constexpr int NT = NX == 1 ? 2 : 3;  // terms of V
+    u16x8_t fa[NT][8];
     {
         const int i = 32 * wave + (lane & 31);
 #pragma unroll
@@ -61,7 +66,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
                 split3_bf16(v, h, m, l);
                 fa[0][ks][e] = h;
                 fa[1][ks][e] = m;
-                fa[2][ks][e] = l;
+                if constexpr (NT == 3) fa[NT - 1][ks][e] = l;
             }
     }
 
@@ -101,7 +106,6 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
                 f32x16_t &a = (ks & 1) ? acc1 : acc;
                 a = mfma32x32x16(fa[0][ks], cur[ks], a);
                 a = mfma32x32x16(fa[1][ks], cur[ks], a);
-                a = mfma32x32x16(fa[2][ks], cur[ks], a);
             } else {
                 const float *xr = static_cast<const float *>(x) + base +
                                   static_cast<int64_t>(t) * row_stride + j0;
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
                 for (int sa = 0; sa < 3; ++sa)
 #pragma unroll
                     for (int sb = 0; sb < 3; ++sb)
-                        if (sa + sb <= 2) acc = mfma32x32x16(fa[sa][ks], fb[sb], acc);
+                        if (sa + sb <= 2) acc = mfma32x32x16(fa[sa < NT ? sa : 0][ks], fb[sb], acc);
             }
         }
         if constexpr (NX == 1) acc += acc1;
