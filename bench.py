@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--factor-dtype", default=None, help="bf16 | i8 (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the host-offloaded cache measurement (compressed vs full KV over PCIe)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--decode-only-steps", type=int, default=20,
                     help="extra decode-only passes after the timed steps (reported separately)")
@@ -380,6 +382,14 @@ def main():
         del stg
         log(f"reconstruct-then-attend: {rb_ms:.2f} ms per step vs fused decode {dec_only_ms:.2f} ms")
 
+    # host-offloaded cache (the pages' throughput setting): per decode step every
+    # layer's attended blocks cross PCIe from pinned host memory into HBM, layer
+    # l + 1's copies overlapping layer l's attention; against offloading the full
+    # bf16 KV cache the same way
+    offload = None
+    if not args.no_offload:
+        offload = offload_measure(milo, torch, np, cfg, F, X, Q, q_pos, sel, nb_layer, fdt, xdt, dev)
+
     # ---------------- algorithmic work per kernel launch ----------------
     ranks = {k: F[k].rank.to(torch.int64) for k in ("k", "v")}
     sw = torch.cat([sweeps["k"], sweeps["v"]]).to(torch.float64)
@@ -412,9 +422,9 @@ def main():
         # kernel: (algorithmic amount for the whole step, unit, bound, peak)
         "gram": (n_blocks_step * T * d * xe, "GB/s", "hbm", PEAK_HBM_GBS),
         "jacobi": (n_blocks_step * sweeps_mean * 9 * d * d * (d - 1), "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
-        # bf16 MFMA products executed: V^T split in 3 bf16 terms (and X too when fp32),
-        # term pairs of order <= 2 kept: 3 products per bf16 X, 6 per fp32 X
-        "refine": (n_blocks_step * 2.0 * T * d * d * (3 if xe == 2 else 6), "TFLOP/s", "mfma",
+        # bf16 MFMA products executed: for bf16 X, V^T split in 2 bf16 terms (2
+        # products); for fp32 X both in 3 terms, term pairs of order <= 2 kept (6)
+        "refine": (n_blocks_step * 2.0 * T * d * d * (2 if xe == 2 else 6), "TFLOP/s", "mfma",
                    PEAK_BF16_TFLOPS),
         "alloc": (n_blocks_step * d * 4, "GB/s", "hbm", PEAK_HBM_GBS),
         "project": (n_blocks_step * T * d * xe + tot_rank * (T + d) * fe + n_blocks_step * d * d * 4,
@@ -500,12 +510,144 @@ def main():
         "rooflines": rooflines,
         "decode_only_rooflines": dec_only,
         "reconstruct_then_attend": rebuild,
+        "offload": offload,
         "memory": {"full_kv_bf16_bytes": full_kv, "factor_bytes": factor_bytes,
                    "ratio": round(factor_bytes / full_kv, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
     return 0
+
+
+def offload_measure(milo, torch, np, cfg, F, X, Q, q_pos, sel, nb_layer, fdt, xdt, dev, n_src=2):
+    """Decode over all layers with the cache in pinned host memory.  n_src
+    distinct layers are held on the host and cycled through (the copies do not
+    depend on the bytes); two device buffers alternate, the copy stream filling
+    one while the compute stream attends over the other."""
+    T, d, L, H, Hq = cfg.block_len, cfg.head_dim, cfg.layers, cfg.n_kv_heads, cfg.n_q_heads
+    bps = cfg.blocks_per_seq
+    n_src = min(n_src, L)
+    if sel is None:
+        ids = list(range(nb_layer))
+        sel_kw = {}
+    else:
+        ids = [(s_ * H + h) * bps + b for s_ in range(cfg.batch) for h in range(H) for b in sel[s_]]
+        sel_kw = dict(sel_ptr=torch.tensor(np.cumsum([0] + [len(x) for x in sel]), dtype=torch.int32, device=dev),
+                      sel_blk=torch.tensor(sum(sel, []), dtype=torch.int32, device=dev), sel_max=cfg.sel_blocks)
+    ids_t = torch.tensor(ids, dtype=torch.int32)
+    es = {"f32": 4, "bf16": 2, "i8": 1}[fdt]
+
+    def layer_host_set(f, layer):
+        """A compact pinned-host copy of one layer's factor set (offsets rebased)."""
+        v = f.view(layer * nb_layer, nb_layer)
+        lo = int(v.a_off.min())
+        hi = int((v.b_off + v.rank.to(torch.int64) * d * es).max())
+        h = milo.Factors(fdt, nb_layer, T, d, rank=v.rank.cpu().pin_memory(), a_off=(v.a_off - lo).cpu().pin_memory(),
+                         b_off=(v.b_off - lo).cpu().pin_memory(), arena=v.arena[lo:hi].cpu().pin_memory())
+        if fdt == "i8":
+            h.a_scale, h.b_scale = v.a_scale.cpu().pin_memory(), v.b_scale.cpu().pin_memory()
+        return h
+
+    out = torch.empty((cfg.batch, Hq, d), dtype=xdt, device=dev)
+    cs = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def run(fetch, attend):
+        fetched = [torch.cuda.Event() for _ in range(2)]
+        used = [torch.cuda.Event() for _ in range(2)]
+        for layer in range(L):
+            j = layer % 2
+            with torch.cuda.stream(cs):
+                if layer >= 2:
+                    cs.wait_event(used[j])
+                fetch(layer, j)
+                fetched[j].record(cs)
+            main.wait_event(fetched[j])
+            attend(layer, j)
+            used[j].record(main)
+
+    def timed(fetch, attend):
+        run(fetch, attend)  # warm
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run(fetch, attend)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    # compressed: the factor sets of n_src layers on the host (each with its own
+    # layout, whose device copy of the metadata the device buffer takes on)
+    hk = [layer_host_set(F["k"], l) for l in range(n_src)]
+    hv = [layer_host_set(F["v"], l) for l in range(n_src)]
+    meta = [(hk[i].like(dev), hv[i].like(dev)) for i in range(n_src)]
+    cap_k = max(h.arena.numel() for h in hk)
+    cap_v = max(h.arena.numel() for h in hv)
+    dk = [milo.Factors.alloc(fdt, nb_layer, T, d, cap_k, device=dev) for _ in range(2)]
+    dv = [milo.Factors.alloc(fdt, nb_layer, T, d, cap_v, device=dev) for _ in range(2)]
+    for m in meta:  # the metadata sets need no arenas of their own
+        m[0].arena = m[1].arena = None
+
+    def fetch_c(layer, j):
+        i = layer % n_src
+        dk[j].rank, dk[j].a_off, dk[j].b_off = meta[i][0].rank, meta[i][0].a_off, meta[i][0].b_off
+        dv[j].rank, dv[j].a_off, dv[j].b_off = meta[i][1].rank, meta[i][1].a_off, meta[i][1].b_off
+        milo.milo_fetch_blocks(hk[i], dk[j], ids_t, stream=cs)
+        milo.milo_fetch_blocks(hv[i], dv[j], ids_t, stream=cs)
+
+    def attend_c(layer, j):
+        milo.milo_decode_attention(Q[layer], q_pos, dk[j], dv[j], bps, H, out, **sel_kw)
+
+    comp_ms = timed(fetch_c, attend_c)
+    comp_bytes = 0
+    for i in range(n_src):
+        for h in (hk[i], hv[i]):
+            r = h.rank.to(torch.int64)[ids_t.long()]
+            comp_bytes += int(r.sum()) * (T + d) * es + (4 * len(ids) * (T + d) if fdt == "i8" else 0)
+    comp_bytes = comp_bytes * L / n_src
+    del hk, hv, dk, dv, meta
+
+    # full KV: the attended blocks' bf16 keys (pre-RoPE) and values on the host,
+    # attended as an uncompressed cache (positions b * T + t as for the blocks)
+    nsel = len(sel[0]) if sel is not None else bps
+    if sel is not None and any(len(x) != nsel for x in sel):
+        return {"compressed_ms_per_step": round(comp_ms, 3), "note": "ragged selections: full-KV side skipped"}
+
+    def host_cache(kind, layer):
+        xs = X[kind][layer * nb_layer:(layer + 1) * nb_layer].view(cfg.batch, H, bps, T, d)
+        if sel is not None:
+            xs = torch.stack([xs[s_][:, sel[s_]] for s_ in range(cfg.batch)])
+        return xs.reshape(cfg.batch, H, nsel * T, d).to(torch.bfloat16).cpu().pin_memory()
+
+    fk = [host_cache("k", l) for l in range(n_src)]
+    fv = [host_cache("v", l) for l in range(n_src)]
+    sk = [torch.empty(fk[0].shape, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    sv = [torch.empty(fv[0].shape, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    tl = torch.full((cfg.batch,), nsel * T, dtype=torch.int32, device=dev)
+    tp = torch.zeros(cfg.batch, dtype=torch.int64, device=dev)
+    empty = milo.Factors.alloc(fdt, 1, T, d, 256, device=dev)
+
+    def fetch_f(layer, j):
+        i = layer % n_src
+        sk[j].copy_(fk[i], non_blocking=True)
+        sv[j].copy_(fv[i], non_blocking=True)
+
+    def attend_f(layer, j):
+        milo.milo_decode_attention(Q[layer], q_pos, empty, empty, 0, H, out, tail_k=sk[j], tail_v=sv[j],
+                                   tail_len=tl, tail_pos0=tp)
+
+    full_ms = timed(fetch_f, attend_f)
+    full_bytes = 2 * L * fk[0].numel() * 2
+    del fk, fv, sk, sv
+    ctx = cfg.context_tokens_per_step
+    return {"compressed_ms_per_step": round(comp_ms, 3), "full_kv_ms_per_step": round(full_ms, 3),
+            "speedup_vs_full_kv": round(full_ms / comp_ms, 3),
+            "compressed_bytes_per_step": comp_bytes, "full_kv_bytes_per_step": full_bytes,
+            "compressed_host_to_device_GBs": round(comp_bytes / comp_ms / 1e6, 1),
+            "full_kv_host_to_device_GBs": round(full_bytes / full_ms / 1e6, 1),
+            "compressed_context_tokens_per_s": ctx / (comp_ms / 1e3),
+            "full_kv_context_tokens_per_s": ctx / (full_ms / 1e3),
+            "host_layers_cycled": n_src}
 
 
 def cpu_baseline(cfg, fdt, X, Q, q_pos, sel, tails, nb_layer, L, ctx_tokens):

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     milo_compress_blocks_ex,
     milo_compress_workspace_bytes,
     milo_decode_attention,
+    milo_fetch_blocks,
     milo_profile_enable,
     milo_profile_read,
     milo_reconstruct,
@@ -29,6 +30,6 @@ __all__ = [
     "Factors", "MiloError", "decode_workspace_bytes", "milo_abi_version", "milo_allocate_ranks",
     "milo_allocate_ranks_ex", "milo_arena_bytes", "milo_compress_blocks", "milo_compress_blocks_ex",
     "milo_compress_workspace_bytes",
-    "milo_decode_attention", "milo_profile_enable", "milo_profile_read", "milo_reconstruct",
+    "milo_decode_attention", "milo_fetch_blocks", "milo_profile_enable", "milo_profile_read", "milo_reconstruct",
     "reconstruct_then_attend",
 ]

@@ -64,6 +64,8 @@ SIGNATURES = {
                                               ctypes.POINTER(ctypes.c_size_t), _vp]),
     "milo_reconstruct": (ctypes.c_int, [ctypes.POINTER(milo_factors), _vp, _i32, _vp,
                                         ctypes.c_int, _vp]),
+    "milo_fetch_blocks": (ctypes.c_int, [ctypes.POINTER(milo_factors), ctypes.POINTER(milo_factors), _vp,
+                                         _i32, _vp]),
     "milo_decode_attention": (ctypes.c_int, [ctypes.POINTER(milo_decode_args),
                                              ctypes.POINTER(ctypes.c_size_t), _vp]),
     "milo_arena_bytes": (ctypes.c_size_t, [ctypes.c_int, _i32, _i32, _vp, _i32, _vp]),

@@ -126,6 +126,30 @@ class Factors:
                        b_scale=None if self.b_scale is None else
                        self.b_scale[lo * self.head_dim:(lo + n) * self.head_dim])
 
+    def to_host(self) -> "Factors":
+        """A copy of this set in pinned host memory (arena, scales and metadata):
+        the offloaded form milo_fetch_blocks reads from."""
+        def pin(t):
+            if t is None:
+                return None
+            h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+            h.copy_(t)
+            return h
+        return Factors(self.dtype, self.n_blocks, self.block_len, self.head_dim, rank=pin(self.rank),
+                       a_off=pin(self.a_off), b_off=pin(self.b_off), arena=pin(self.arena),
+                       a_scale=pin(self.a_scale), b_scale=pin(self.b_scale))
+
+    def like(self, device="cuda") -> "Factors":
+        """A set on `device` with this set's layout (metadata copied) and an empty
+        arena and scales: the destination of milo_fetch_blocks."""
+        dev = torch.device(device)
+        f = Factors.alloc(self.dtype, self.n_blocks, self.block_len, self.head_dim, self.arena.numel(),
+                          device=dev)
+        f.rank.copy_(self.rank)
+        f.a_off.copy_(self.a_off)
+        f.b_off.copy_(self.b_off)
+        return f
+
     def nbytes(self) -> int:
         """Bytes the factors occupy (arena payload + INT8 scales actually used)."""
         used = int(self.rank.sum().item()) * (self.block_len + self.head_dim) * \
@@ -266,6 +290,23 @@ def milo_reconstruct(factors: Factors, block_ids: torch.Tensor, out: torch.Tenso
     fs = factors.struct()
     st = lib().milo_reconstruct(ctypes.byref(fs), _p(block_ids), int(block_ids.numel()), _p(out),
                                 _dtype_code(out.dtype), _stream(stream))
+    _check(st)
+
+
+def milo_fetch_blocks(host: Factors, dev: Factors, blocks, stream=None) -> None:
+    """Copy the listed blocks' factors from the host-resident set `host` into the
+    device set `dev` (same layout); asynchronous on `stream`."""
+    for t, name in ((host.rank, "host.rank"), (host.a_off, "host.a_off"), (host.b_off, "host.b_off"),
+                    (host.arena, "host.arena")):
+        if t.device.type != "cpu":
+            raise ValueError(f"{name} must be in host memory")
+    if dev.arena.device.type != "cuda":
+        raise ValueError("dev.arena must be device memory")
+    ids = torch.as_tensor(blocks, dtype=torch.int32).contiguous()
+    if ids.device.type != "cpu":
+        raise ValueError("blocks must be a host array")
+    hs, ds = host.struct(), dev.struct()
+    st = lib().milo_fetch_blocks(ctypes.byref(hs), ctypes.byref(ds), _p(ids), int(ids.numel()), _stream(stream))
     _check(st)
 
 

@@ -422,6 +422,68 @@ milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, in
     return ok();
 }
 
+milo_status milo_fetch_blocks(const milo_factors *host, const milo_factors *dev, const int32_t *blocks,
+                              int32_t n, void *stream) {
+    if (!host || !dev) return fail(MILO_E_INVALID, "host and dev factor sets must be given");
+    if (host->dtype != dev->dtype) return fail(MILO_E_INVALID, "host and dev dtypes differ");
+    if (host->dtype != MILO_F32 && host->dtype != MILO_BF16 && host->dtype != MILO_I8)
+        return fail(MILO_E_INVALID, "unknown factor dtype");
+    if (host->n_blocks != dev->n_blocks || host->block_len != dev->block_len || host->head_dim != dev->head_dim)
+        return fail(MILO_E_INVALID, "host and dev geometries differ");
+    if (host->n_blocks < 0 || host->block_len < 1 || host->head_dim < 1) return fail(MILO_E_INVALID, "bad geometry");
+    if (dev->arena_bytes < host->arena_bytes) return fail(MILO_E_INVALID, "dev arena smaller than host arena");
+    if (n < 0) return fail(MILO_E_INVALID, "n must be >= 0");
+    if (n == 0) return ok();
+    if (!blocks) return fail(MILO_E_INVALID, "blocks must be set");
+    if (!host->rank || !host->a_off || !host->b_off || !host->arena || !dev->arena)
+        return fail(MILO_E_INVALID, "factor set pointers must be set");
+    const bool i8 = host->dtype == MILO_I8;
+    if (i8 && (!host->a_scale || !host->b_scale || !dev->a_scale || !dev->b_scale))
+        return fail(MILO_E_INVALID, "MILO_I8 factors need scales");
+    const int64_t es = host->dtype == MILO_F32 ? 4 : (host->dtype == MILO_BF16 ? 2 : 1);
+    const int64_t T = host->block_len, d = host->head_dim, cap = static_cast<int64_t>(host->arena_bytes);
+    // byte runs [begin, end) of the arena, and of the two scale arrays, in list order
+    struct Run { int64_t b, e; };
+    std::vector<Run> arena, sa, sb;
+    auto add = [](std::vector<Run> &v, int64_t b, int64_t e) {
+        if (e <= b) return;
+        if (!v.empty() && v.back().e == b) v.back().e = e;
+        else v.push_back({b, e});
+    };
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t id = blocks[i];
+        if (id < 0 || id >= host->n_blocks) return fail(MILO_E_INVALID, "block id %d out of range", id);
+        const int64_t r = host->rank[id];
+        if (r < 0 || r > (T < d ? T : d)) return fail(MILO_E_INVALID, "block %d has rank %lld", id, (long long)r);
+        const int64_t a0 = host->a_off[id], b0 = host->b_off[id];
+        if (a0 < 0 || b0 < 0 || a0 + r * T * es > cap || b0 + r * d * es > cap)
+            return fail(MILO_E_INVALID, "block %d reaches past the arena", id);
+        add(arena, a0, a0 + r * T * es);
+        add(arena, b0, b0 + r * d * es);
+        if (i8) {
+            add(sa, static_cast<int64_t>(id) * T * 4, (static_cast<int64_t>(id) + 1) * T * 4);
+            add(sb, static_cast<int64_t>(id) * d * 4, (static_cast<int64_t>(id) + 1) * d * 4);
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("fetch", s, [&] {
+        auto copy = [&](const std::vector<Run> &v, const void *src, void *dst) {
+            for (const Run &q : v) {
+                hipError_t r = hipMemcpyAsync(static_cast<uint8_t *>(dst) + q.b, static_cast<const uint8_t *>(src) + q.b,
+                                              static_cast<size_t>(q.e - q.b), hipMemcpyHostToDevice, s);
+                if (r != hipSuccess) return r;
+            }
+            return hipSuccess;
+        };
+        hipError_t r = copy(arena, host->arena, dev->arena);
+        if (r == hipSuccess && i8) r = copy(sa, host->a_scale, dev->a_scale);
+        if (r == hipSuccess && i8) r = copy(sb, host->b_scale, dev->b_scale);
+        return r;
+    });
+    if (e != hipSuccess) return hip_fail(e, "fetch copies");
+    return ok();
+}
+
 milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_needed,
                                   void *stream) {
     if (!a) return fail(MILO_E_INVALID, "args is NULL");

@@ -211,6 +211,34 @@ milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, in
                              void *x_out, milo_dtype out_dtype, void *stream);
 
 /*
+ * milo_fetch_blocks -- host-offloaded compressed cache: bring the factors of
+ * the listed blocks from a factor set kept in host memory into a device factor
+ * set of the same layout ([REV] Summary and FAQ: the compressed cache is
+ * offloaded to CPU memory, on one L4 GPU, and only the blocks a query needs are
+ * brought back and rebuilt; the throughput figures are measured against
+ * offloading the full cache).
+ *  host    factor set whose arena (and, for MILO_I8, a_scale / b_scale) is in
+ *          pinned host memory (hipHostMalloc; pageable memory works, but the
+ *          copies then do not overlap other work), and whose rank / a_off /
+ *          b_off are HOST arrays.  Only read.
+ *  dev     factor set with the same dtype, n_blocks, block_len and head_dim and
+ *          arena_bytes >= host's; its arena (and scales) are device memory.
+ *          Its metadata arrays are not touched and must hold host's values: the
+ *          layout is shared, so a fetched block sits at the same arena offsets
+ *          (and scale rows) in both sets, and decode over dev reads exactly the
+ *          fetched blocks.
+ *  blocks  host [n]: block ids, each in [0, n_blocks); any order, repeats
+ *          allowed.  Ranges that continue the previous block's in the list are
+ *          fetched with one copy (a whole pool in id order is one copy).
+ *  stream  the copies are asynchronous DMA on this stream; the host arrays are
+ *          read during the call only.
+ * Errors (nothing copied): MILO_E_INVALID for missing pointers, mismatched
+ * geometry, ids out of range or offsets reaching past arena_bytes.
+ */
+milo_status milo_fetch_blocks(const milo_factors *host, const milo_factors *dev, const int32_t *blocks,
+                              int32_t n, void *stream);
+
+/*
  * Decode attention over compressed blocks for one layer ([REV] Summary: the
  * retrieved blocks' low-rank factors are rebuilt before sparse attention).
  * Sequence s, query head hq uses KV head h = hq / (n_q_heads / n_kv_heads).

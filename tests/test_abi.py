@@ -190,3 +190,47 @@ def test_reconstruct_validation(L):
     assert L.milo_reconstruct(ctypes.byref(f), 0x10, 0, 0x20, 0, None) == 0   # nothing to do
     f.head_dim = 64
     assert L.milo_reconstruct(ctypes.byref(f), 0x10, 1, 0x20, 0, None) == 2
+
+
+def _host_set(n=4, T=256, d=128, ranks=(8, 0, 128, 5), dtype=1):
+    """A factor set whose metadata are host arrays (milo_fetch_blocks reads them
+    on the host and rejects bad inputs before any HIP call)."""
+    from block_wise_rank_amd import _capi
+    rk = (ctypes.c_int32 * n)(*ranks)
+    e = 2 if dtype == 1 else (4 if dtype == 0 else 1)
+    sizes = [r * (T + d) * e for r in ranks]
+    ao = [sum(sizes[:i]) for i in range(n)]
+    bo = [ao[i] + ranks[i] * T * e for i in range(n)]
+    aoff = (ctypes.c_int64 * n)(*ao)
+    boff = (ctypes.c_int64 * n)(*bo)
+    keep = (rk, aoff, boff)
+    f = _capi.milo_factors(dtype, n, T, d, ctypes.cast(rk, ctypes.c_void_p), ctypes.cast(aoff, ctypes.c_void_p),
+                           ctypes.cast(boff, ctypes.c_void_p), 0x1000, sum(sizes), None, None)
+    return f, keep
+
+
+def test_fetch_validation(L):
+    """milo_fetch_blocks checks ids, geometry and offsets on the host."""
+    host, keep = _host_set()
+    dev, _ = _host_set()
+    dev.arena = 0x2000
+    ids = lambda *v: ((ctypes.c_int32 * len(v))(*v), len(v))
+
+    def call(h, dv, v):
+        arr, n = v
+        return L.milo_fetch_blocks(ctypes.byref(h), ctypes.byref(dv), ctypes.cast(arr, ctypes.c_void_p), n, None)
+
+    assert L.milo_fetch_blocks(ctypes.byref(host), ctypes.byref(dev), None, 0, None) == 0  # nothing to do
+    assert call(host, dev, ids(4)) == 1 and b"out of range" in L.milo_last_error()
+    assert call(host, dev, ids(-1)) == 1
+    dev.block_len = 512
+    assert call(host, dev, ids(0)) == 1 and b"geometr" in L.milo_last_error()
+    dev.block_len = 256
+    dev.arena_bytes = host.arena_bytes - 1
+    assert call(host, dev, ids(0)) == 1 and b"smaller" in L.milo_last_error()
+    dev.arena_bytes = host.arena_bytes
+    host.arena_bytes -= 1  # block 3 now reaches past the arena
+    dev.arena_bytes = host.arena_bytes
+    assert call(host, dev, ids(3)) == 1 and b"past the arena" in L.milo_last_error()
+    dev.dtype = 2
+    assert call(host, dev, ids(0)) == 1 and b"dtype" in L.milo_last_error()
