@@ -86,6 +86,8 @@ def load(path: str):
     L.oracle_round_f32.restype = None
     L.oracle_quant_int8_rows.argtypes = [_dp, ctypes.c_int, ctypes.c_int, _dp, _i8p, _dp]
     L.oracle_quant_int8_rows.restype = None
+    L.oracle_quant_int4_groups.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _i8p, _dp]
+    L.oracle_quant_int4_groups.restype = None
     L.oracle_rope.argtypes = [_dp, ctypes.c_int, ctypes.c_double, ctypes.c_double]
     L.oracle_rope.restype = None
     L.oracle_attention.argtypes = [_dp, ctypes.c_int, ctypes.c_int64, _dp, _dp, _i64p,
@@ -238,11 +240,33 @@ def quant_int8_rows(M):
     return scale, codes, deq
 
 
+I4_GROUP = 32  # elements per 4-bit scale group (tokens of an A row, dims of a B row)
+
+
+def quant_int4_groups(M, group: int = I4_GROUP):
+    """Symmetric 4-bit codes per run of `group` elements of each row.  Returns
+    (scale [rows, cols/group], codes int8 in [-7, 7] [rows, cols], dequant fp64)."""
+    M = _f64(M)
+    if M.ndim != 2:
+        raise ValueError("quant_int4_groups expects a 2-D array")
+    rows, cols = M.shape
+    if cols % group:
+        raise ValueError(f"row length {cols} is not a multiple of the group {group}")
+    scale = np.zeros((rows, cols // group))
+    codes = np.zeros((rows, cols), dtype=np.int8)
+    deq = np.zeros((rows, cols))
+    if rows and cols:
+        lib().oracle_quant_int4_groups(_ptr(M), rows, cols, group, _ptr(scale), _ptr(codes, _i8p), _ptr(deq))
+    return scale, codes, deq
+
+
 def store(A, B, storage: str):
     """Apply the storage encoding to a factor pair; returns the decoded (A, B) in fp64.
 
-    storage: "f32" | "bf16" | "i8".  For "i8" every row of A (one per token) and
-    every row of B (one per rank) gets its own absmax scale.
+    storage: "f32" | "bf16" | "i8" | "i4".  For "i8" every row of A (one per
+    token) and every row of B (one per rank) gets its own absmax scale.  For "i4"
+    the rank rows of A^T (T tokens) and of B (d dims) are cut into groups of
+    I4_GROUP consecutive elements with a scale each.
     """
     if storage == "f32":
         return round_f32(A), round_f32(B)
@@ -254,6 +278,12 @@ def store(A, B, storage: str):
         if A.shape[1] == 0:
             return A.copy(), B.copy()
         return quant_int8_rows(A)[2], quant_int8_rows(B)[2]
+    if storage == "i4":
+        A = _f64(A)
+        B = _f64(B)
+        if A.shape[1] == 0:
+            return A.copy(), B.copy()
+        return quant_int4_groups(A.T)[2].T.copy(), quant_int4_groups(B)[2]
     raise ValueError(f"unknown storage {storage!r}")
 
 

@@ -40,6 +40,14 @@
  *                       storage encodings.  INT8 with per-row absmax scales is
  *                       the composition with INT8 quantisation that [REV]
  *                       Summary and Key claims report.
+ *   oracle_quant_int4_groups
+ *                       4-bit storage beyond INT8 (the composition with
+ *                       low-bit KV quantisation such as KIVI that [REV] Key
+ *                       claims and FAQ report, up to 5.3x): every run of
+ *                       `group` consecutive elements of a row gets its own
+ *                       absmax scale s = max|x| / 7 and codes rint(x / s) in
+ *                       [-7, 7].  The quantiser itself is this project's own
+ *                       (the pages do not specify one).
  *   oracle_rope / oracle_attention
  *                       exact softmax attention of a rotary-embedded query over
  *                       rotary-embedded reconstructed keys: keys are compressed
@@ -48,8 +56,8 @@
  *                       their absolute positions.
  *
  * All arithmetic is IEEE fp64 except where a storage format forces a narrower
- * decision (the INT8 code decision is taken in fp32, the precision the GPU
- * kernel takes it in).
+ * decision (the INT8 and 4-bit code decisions are taken in fp32, the precision
+ * the GPU kernel takes them in).
  */
 #include <float.h>
 #include <math.h>
@@ -416,6 +424,42 @@ void oracle_quant_int8_rows(const double *M, int rows, int cols, double *scale,
             codes[(size_t)r * cols + c] = (int8_t)q;
             if (dequant)
                 dequant[(size_t)r * cols + c] = (double)((float)q * s);
+        }
+    }
+}
+
+/* Symmetric 4-bit codes per group of `group` consecutive elements of each   */
+/* row (cols a multiple of group): s = max|x| / 7, q = rint(x / s) clamped   */
+/* to [-7, 7], x~ = q s.  The code is decided in fp32 (round half to even),  */
+/* the precision the GPU kernel decides it in.  scale is [rows][cols/group]. */
+void oracle_quant_int4_groups(const double *M, int rows, int cols, int group, double *scale,
+                              int8_t *codes, double *dequant)
+{
+    const int ng = cols / group;
+    for (int r = 0; r < rows; ++r) {
+        for (int g = 0; g < ng; ++g) {
+            const double *x = M + (size_t)r * cols + (size_t)g * group;
+            float m = 0.0f;
+            for (int c = 0; c < group; ++c) {
+                float a = fabsf((float)x[c]);
+                if (a > m)
+                    m = a;
+            }
+            float s = m / 7.0f;
+            scale[(size_t)r * ng + g] = (double)s;
+            for (int c = 0; c < group; ++c) {
+                int q = 0;
+                if (s > 0.0f) {
+                    float v = nearbyintf((float)x[c] / s);
+                    if (v > 7.0f) v = 7.0f;
+                    if (v < -7.0f) v = -7.0f;
+                    q = (int)v;
+                }
+                const size_t i = (size_t)r * cols + (size_t)g * group + c;
+                codes[i] = (int8_t)q;
+                if (dequant)
+                    dequant[i] = (double)((float)q * s);
+            }
         }
     }
 }

@@ -118,12 +118,52 @@ def test_int8_error_bound(oracle_lib):
     assert (np.abs(deq - M) <= bound).all()
 
 
+def test_int4_hand_values(oracle_lib):
+    """Groups of 4 for hand values (the group length is a parameter): s = max|x|/7,
+    codes rint(x/s) with ties to even, each group on its own."""
+    M = np.array([[7.0, -3.5, 0.5, 0.0, 14.0, 1.0, 3.0, -14.0],
+                  [0.0, 0.0, 0.0, 0.0, -1.0, 0.25, 0.5, 0.0]])
+    scale, codes, deq = oracle_lib.quant_int4_groups(M, group=4)
+    assert scale[0].tolist() == [1.0, 2.0]
+    assert list(codes[0]) == [7, -4, 0, 0, 7, 0, 2, -7]
+    assert scale[1][0] == 0.0 and list(codes[1][:4]) == [0, 0, 0, 0] and (deq[1][:4] == 0).all()
+    s = np.float32(1.0) / np.float32(7.0)
+    assert scale[1][1] == float(s)
+    assert list(codes[1][4:]) == [-7] + [int(np.rint(np.float32(v) / s)) for v in (0.25, 0.5, 0.0)]
+    assert deq[0][1] == -4.0 and deq[0][6] == 4.0
+
+
+def test_int4_error_bound_and_groups(oracle_lib):
+    rng = np.random.default_rng(5)
+    M = rng.standard_normal((48, 256)) * np.exp(2 * rng.standard_normal((48, 8))).repeat(32, axis=1)
+    scale, codes, deq = oracle_lib.quant_int4_groups(M)
+    assert scale.shape == (48, 8)
+    assert (np.abs(codes.astype(int)) <= 7).all()
+    # every group reaches +-7 at its largest element
+    assert (np.abs(codes.reshape(48, 8, 32)).max(axis=2) == 7).all()
+    # |x - q s| <= s/2 plus the fp32 rounding of x and of s
+    bound = np.repeat(scale, 32, axis=1) * (0.5 + 1e-5) + np.abs(M) * 2e-7
+    assert (np.abs(deq - M) <= bound).all()
+    # groups are independent: changing one group changes nothing else
+    M2 = M.copy()
+    M2[3, 64:96] *= 100.0
+    s2, c2, _ = oracle_lib.quant_int4_groups(M2)
+    keep = np.ones((48, 8), dtype=bool)
+    keep[3, 2] = False
+    assert np.array_equal(s2[keep], scale[keep])
+    assert np.array_equal(c2.reshape(48, 8, 32)[keep], codes.reshape(48, 8, 32)[keep])
+    # the dequantised values quantise to themselves
+    s3, c3, d3 = oracle_lib.quant_int4_groups(deq)
+    assert np.array_equal(c3, codes) and np.allclose(d3, deq, rtol=1e-6, atol=0)
+
+
 def test_store_roundtrip_shapes(oracle_lib, block):
     X, sigma, V = block
     A, B = oracle_lib.project(X, V, 50)
-    for st in ("f32", "bf16", "i8"):
+    for st in ("f32", "bf16", "i8", "i4"):
         As, Bs = oracle_lib.store(A, B, st)
         assert As.shape == A.shape and Bs.shape == B.shape
         rel = np.linalg.norm(oracle_lib.reconstruct(As, Bs) - oracle_lib.reconstruct(A, B)) / \
             np.linalg.norm(oracle_lib.reconstruct(A, B))
-        assert rel <= {"f32": 1e-6, "bf16": 1e-2, "i8": 3e-2}[st]
+        # 4-bit: each element moves by at most s/2 = max|group|/14
+        assert rel <= {"f32": 1e-6, "bf16": 1e-2, "i8": 3e-2, "i4": 0.2}[st]

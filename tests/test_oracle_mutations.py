@@ -50,6 +50,11 @@ MUTATIONS = [
      "double r = round(x / quantum) * quantum;", lambda: PF.test_round_bf16_hand_values(oracle)),
     ("int8 truncates", "float v = nearbyintf((float)row[c] / s);",
      "float v = truncf((float)row[c] / s);", lambda: PF.test_int8_hand_values(oracle)),
+    ("int4 scale over 8 levels", "float s = m / 7.0f;", "float s = m / 8.0f;",
+     lambda: PF.test_int4_hand_values(oracle)),
+    ("int4 groups overlap", "const double *x = M + (size_t)r * cols + (size_t)g * group;",
+     "const double *x = M + (size_t)r * cols + (size_t)g;",
+     lambda: PF.test_int4_hand_values(oracle)),
     ("rope second component sign", "x[j + h] = a * s + b * c;", "x[j + h] = a * s - b * c;",
      lambda: PT.test_rope_matches_complex_form(oracle)),
     ("rope frequency exponent", "pow(base, -2.0 * j / (double)d)", "pow(base, -1.0 * j / (double)d)",
