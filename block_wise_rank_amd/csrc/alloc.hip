@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void alloc_kernel(
     const float *__restrict__ sigma, int pitch, int k, const int32_t *__restrict__ pool_ptr,
     const int64_t *__restrict__ budget, const int64_t *__restrict__ pool_base, int pool_lo,
     int blk_lo, double eps2, int32_t *__restrict__ rank, double *__restrict__ objective,
-    int64_t *__restrict__ a_off, int64_t *__restrict__ b_off, int T, int elem_bytes, int policy,
+    int64_t *__restrict__ a_off, int64_t *__restrict__ b_off, int a_bpr, int b_bpr, int policy,
     uint64_t seed) {
     __shared__ int64_t red64[4];
     __shared__ double redd[4];
@@ -190,15 +190,16 @@ __global__ __launch_bounds__(256) void alloc_kernel(
         if (tid == 0 && objective) objective[pool] = ((redd[0] + redd[1]) + redd[2]) + redd[3];
     }
     // Arena offsets: the pool's blocks are laid out back to back in block order,
-    // each as A^T (r x T) followed by B (r x d).
+    // each as A^T (r x T) followed by B (r x d); a rank takes a_bpr bytes of A
+    // and b_bpr bytes of B.
     if (a_off) {
         const int64_t before = block_exclusive_scan(rank_sum, scan_buf);
-        int64_t off = pool_base[pool] + before * (T + kD) * elem_bytes;
+        int64_t off = pool_base[pool] + before * (a_bpr + b_bpr);
         for (int b = my_lo; b < my_hi; ++b) {
             const int r = rank[b];
             a_off[b] = off;
-            b_off[b] = off + static_cast<int64_t>(r) * T * elem_bytes;
-            off += static_cast<int64_t>(r) * (T + kD) * elem_bytes;
+            b_off[b] = off + static_cast<int64_t>(r) * a_bpr;
+            off += static_cast<int64_t>(r) * (a_bpr + b_bpr);
         }
     }
 }
@@ -208,12 +209,12 @@ __global__ __launch_bounds__(256) void alloc_kernel(
 hipError_t launch_alloc(const float *sigma, int sigma_pitch, int max_rank, const int32_t *pool_ptr,
                         const int64_t *budget, const int64_t *pool_base, int pool_lo, int n_pools,
                         int blk_lo, double eps2, int32_t *rank, double *objective, int64_t *a_off,
-                        int64_t *b_off, int block_len, int elem_bytes, int policy, uint64_t seed,
+                        int64_t *b_off, int a_bpr, int b_bpr, int policy, uint64_t seed,
                         hipStream_t st) {
     if (n_pools <= 0) return hipSuccess;
     hipLaunchKernelGGL(alloc_kernel, dim3(static_cast<unsigned>(n_pools)), dim3(256), 0, st, sigma,
                        sigma_pitch, max_rank, pool_ptr, budget, pool_base, pool_lo, blk_lo, eps2,
-                       rank, objective, a_off, b_off, block_len, elem_bytes, policy, seed);
+                       rank, objective, a_off, b_off, a_bpr, b_bpr, policy, seed);
     return hipGetLastError();
 }
 

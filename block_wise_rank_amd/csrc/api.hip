@@ -73,6 +73,14 @@ milo_status hip_fail(hipError_t e, const char *what) {
 }
 
 int elem_bytes(milo_dtype t) { return t == MILO_F32 ? 4 : (t == MILO_BF16 ? 2 : 1); }
+bool factor_dtype_ok(milo_dtype t) { return t == MILO_F32 || t == MILO_BF16 || t == MILO_I8 || t == MILO_I4; }
+int kernel_type(milo_dtype t) {
+    return t == MILO_F32 ? milo::kF32 : (t == MILO_BF16 ? milo::kBF16 : (t == MILO_I8 ? milo::kI8 : milo::kI4));
+}
+// Bytes one rank takes in a block's A part (T elements) and B part (d elements):
+// MILO_I4 holds half a byte per element and an fp32 scale per 32 elements.
+int64_t a_rank_bytes(milo_dtype t, int T) { return t == MILO_I4 ? T / 2 + 4 * (T / 32) : static_cast<int64_t>(T) * elem_bytes(t); }
+int64_t b_rank_bytes(milo_dtype t, int d) { return t == MILO_I4 ? d / 2 + 4 * (d / 32) : static_cast<int64_t>(d) * elem_bytes(t); }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -145,7 +153,7 @@ const char *milo_status_string(milo_status s) {
 
 size_t milo_arena_bytes(milo_dtype dtype, int32_t block_len, int32_t head_dim,
                         const int32_t *pool_ptr, int32_t n_pools, const int64_t *budget) {
-    if (dtype != MILO_F32 && dtype != MILO_BF16 && dtype != MILO_I8) {
+    if (!factor_dtype_ok(dtype)) {
         fail(MILO_E_INVALID, "unknown dtype %d", static_cast<int>(dtype));
         return 0;
     }
@@ -165,7 +173,7 @@ size_t milo_arena_bytes(milo_dtype dtype, int32_t block_len, int32_t head_dim,
             return 0;
         }
         total += static_cast<size_t>(pool_ranks(pool_ptr, budget, p, k)) *
-                 static_cast<size_t>(block_len + head_dim) * elem_bytes(dtype);
+                 static_cast<size_t>(a_rank_bytes(dtype, block_len) + b_rank_bytes(dtype, head_dim));
     }
     g_last_error.clear();
     return total;
@@ -227,11 +235,10 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
     if (st != MILO_OK) return st;
     if (in->n_blocks > 0 && !sigma_out) return fail(MILO_E_INVALID, "sigma_out is NULL");
     // factor set
-    const bool pair_ok = (in->dtype == MILO_F32 && out->dtype == MILO_F32) ||
-                         (in->dtype == MILO_BF16 && out->dtype == MILO_BF16) ||
-                         (in->dtype == MILO_BF16 && out->dtype == MILO_I8);
-    if (!pair_ok) return fail(MILO_E_UNSUPPORTED, "unsupported dtype pair (in %d -> factors %d)",
-                              static_cast<int>(in->dtype), static_cast<int>(out->dtype));
+    if (!factor_dtype_ok(out->dtype))
+        return fail(MILO_E_UNSUPPORTED, "unsupported factor dtype %d", static_cast<int>(out->dtype));
+    if (out->dtype == MILO_I4 && in->block_len % 128 != 0)
+        return fail(MILO_E_UNSUPPORTED, "MILO_I4 factors need block_len a multiple of 128");
     if (out->n_blocks != in->n_blocks || out->block_len != in->block_len || out->head_dim != in->head_dim)
         return fail(MILO_E_INVALID, "factor set geometry does not match the blocks");
     const size_t need_arena = milo_arena_bytes(out->dtype, in->block_len, in->head_dim, pool_ptr, n_pools, budget);
@@ -262,9 +269,9 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int T = in->block_len;
     const int k = T < kD ? T : kD;
-    const int fe = elem_bytes(out->dtype);
+    const int a_bpr = static_cast<int>(a_rank_bytes(out->dtype, T)), b_bpr = static_cast<int>(b_rank_bytes(out->dtype, kD));
     const int x_type = in->dtype == MILO_F32 ? milo::kF32 : milo::kBF16;
-    const int f_type = out->dtype == MILO_F32 ? milo::kF32 : (out->dtype == MILO_BF16 ? milo::kBF16 : milo::kI8);
+    const int f_type = kernel_type(out->dtype);
 
     // pool tables -> device
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -276,7 +283,7 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
     int64_t acc = 0;
     for (int p = 0; p < n_pools; ++p) {
         base[p] = acc;
-        acc += pool_ranks(pool_ptr, budget, p, k) * static_cast<int64_t>(T + kD) * fe;
+        acc += pool_ranks(pool_ptr, budget, p, k) * static_cast<int64_t>(a_bpr + b_bpr);
     }
     hipError_t e;
     if (n_pools > 0) {
@@ -322,8 +329,8 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
                 return hip_fail(e, "refine launch");
             if ((e = timed("alloc", s, [&] {
                      return milo::launch_alloc(sig, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
-                                               eps2, out->rank, objective_out, out->a_off, out->b_off, T,
-                                               fe, policy, seed, s);
+                                               eps2, out->rank, objective_out, out->a_off, out->b_off, a_bpr,
+                                               b_bpr, policy, seed, s);
                  })) != hipSuccess)
                 return hip_fail(e, "alloc launch");
             if ((e = timed("project", s, [&] {
@@ -336,8 +343,8 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
                 return hip_fail(e, "project launch");
         } else {
             if ((e = milo::launch_alloc(sigma_out, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
-                                        eps2, out->rank, objective_out, out->a_off, out->b_off, T, fe,
-                                        policy, seed, s)) != hipSuccess)
+                                        eps2, out->rank, objective_out, out->a_off, out->b_off, a_bpr,
+                                        b_bpr, policy, seed, s)) != hipSuccess)
                 return hip_fail(e, "alloc launch");
         }
         p0 = p1;
@@ -400,8 +407,9 @@ milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, in
     if (f->head_dim != kD) return fail(MILO_E_UNSUPPORTED, "head_dim must be 128");
     if (f->block_len < 128 || f->block_len % 64 != 0)
         return fail(MILO_E_UNSUPPORTED, "block_len must be a multiple of 64 and >= 128");
-    if (f->dtype != MILO_F32 && f->dtype != MILO_BF16 && f->dtype != MILO_I8)
-        return fail(MILO_E_INVALID, "unknown factor dtype");
+    if (!factor_dtype_ok(f->dtype)) return fail(MILO_E_INVALID, "unknown factor dtype");
+    if (f->dtype == MILO_I4 && f->block_len % 128 != 0)
+        return fail(MILO_E_UNSUPPORTED, "MILO_I4 factors need block_len a multiple of 128");
     if (out_dtype != MILO_F32 && out_dtype != MILO_BF16)
         return fail(MILO_E_UNSUPPORTED, "out_dtype must be MILO_F32 or MILO_BF16");
     if (n_ids < 0) return fail(MILO_E_INVALID, "n_ids must be >= 0");
@@ -411,7 +419,7 @@ milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, in
         return fail(MILO_E_INVALID, "factor set pointers must be set");
     if (f->dtype == MILO_I8 && (!f->a_scale || !f->b_scale))
         return fail(MILO_E_INVALID, "MILO_I8 factors need scales");
-    const int ft = f->dtype == MILO_F32 ? milo::kF32 : (f->dtype == MILO_BF16 ? milo::kBF16 : milo::kI8);
+    const int ft = kernel_type(f->dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed("reconstruct", s, [&] {
         return milo::launch_reconstruct(f->arena, ft, f->rank, f->a_off, f->b_off, f->a_scale,
@@ -426,8 +434,7 @@ milo_status milo_fetch_blocks(const milo_factors *host, const milo_factors *dev,
                               int32_t n, void *stream) {
     if (!host || !dev) return fail(MILO_E_INVALID, "host and dev factor sets must be given");
     if (host->dtype != dev->dtype) return fail(MILO_E_INVALID, "host and dev dtypes differ");
-    if (host->dtype != MILO_F32 && host->dtype != MILO_BF16 && host->dtype != MILO_I8)
-        return fail(MILO_E_INVALID, "unknown factor dtype");
+    if (!factor_dtype_ok(host->dtype)) return fail(MILO_E_INVALID, "unknown factor dtype");
     if (host->n_blocks != dev->n_blocks || host->block_len != dev->block_len || host->head_dim != dev->head_dim)
         return fail(MILO_E_INVALID, "host and dev geometries differ");
     if (host->n_blocks < 0 || host->block_len < 1 || host->head_dim < 1) return fail(MILO_E_INVALID, "bad geometry");
@@ -440,8 +447,10 @@ milo_status milo_fetch_blocks(const milo_factors *host, const milo_factors *dev,
     const bool i8 = host->dtype == MILO_I8;
     if (i8 && (!host->a_scale || !host->b_scale || !dev->a_scale || !dev->b_scale))
         return fail(MILO_E_INVALID, "MILO_I8 factors need scales");
-    const int64_t es = host->dtype == MILO_F32 ? 4 : (host->dtype == MILO_BF16 ? 2 : 1);
     const int64_t T = host->block_len, d = host->head_dim, cap = static_cast<int64_t>(host->arena_bytes);
+    if (host->dtype == MILO_I4 && (T % 32 != 0 || d % 32 != 0))
+        return fail(MILO_E_INVALID, "MILO_I4 geometry must hold whole 32-element groups");
+    const int64_t abpr = a_rank_bytes(host->dtype, static_cast<int>(T)), bbpr = b_rank_bytes(host->dtype, static_cast<int>(d));
     // byte runs [begin, end) of the arena, and of the two scale arrays, in list order
     struct Run { int64_t b, e; };
     std::vector<Run> arena, sa, sb;
@@ -456,10 +465,10 @@ milo_status milo_fetch_blocks(const milo_factors *host, const milo_factors *dev,
         const int64_t r = host->rank[id];
         if (r < 0 || r > (T < d ? T : d)) return fail(MILO_E_INVALID, "block %d has rank %lld", id, (long long)r);
         const int64_t a0 = host->a_off[id], b0 = host->b_off[id];
-        if (a0 < 0 || b0 < 0 || a0 + r * T * es > cap || b0 + r * d * es > cap)
+        if (a0 < 0 || b0 < 0 || a0 + r * abpr > cap || b0 + r * bbpr > cap)
             return fail(MILO_E_INVALID, "block %d reaches past the arena", id);
-        add(arena, a0, a0 + r * T * es);
-        add(arena, b0, b0 + r * d * es);
+        add(arena, a0, a0 + r * abpr);
+        add(arena, b0, b0 + r * bbpr);
         if (i8) {
             add(sa, static_cast<int64_t>(id) * T * 4, (static_cast<int64_t>(id) + 1) * T * 4);
             add(sb, static_cast<int64_t>(id) * d * 4, (static_cast<int64_t>(id) + 1) * d * 4);
@@ -496,12 +505,13 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
     if (!a->k || !a->v) return fail(MILO_E_INVALID, "k and v factor sets must be given");
     const milo_factors *k = a->k, *v = a->v;
     if (k->dtype != v->dtype) return fail(MILO_E_UNSUPPORTED, "K and V factors must share a dtype");
-    if (k->dtype != MILO_F32 && k->dtype != MILO_BF16 && k->dtype != MILO_I8)
-        return fail(MILO_E_INVALID, "unknown factor dtype");
+    if (!factor_dtype_ok(k->dtype)) return fail(MILO_E_INVALID, "unknown factor dtype");
     if (k->head_dim != kD || v->head_dim != kD) return fail(MILO_E_UNSUPPORTED, "factor head_dim must be 128");
     if (k->block_len != v->block_len) return fail(MILO_E_INVALID, "K and V block_len differ");
     const int T = k->block_len;
     if (T < 128 || T % 64 != 0) return fail(MILO_E_UNSUPPORTED, "block_len must be a multiple of 64 and >= 128");
+    if (k->dtype == MILO_I4 && T % 128 != 0)
+        return fail(MILO_E_UNSUPPORTED, "MILO_I4 factors need block_len a multiple of 128");
     if (a->blocks_per_seq < 0) return fail(MILO_E_INVALID, "blocks_per_seq must be >= 0");
     const int64_t need_blocks = static_cast<int64_t>(a->batch) * a->n_kv_heads * a->blocks_per_seq;
     if (k->n_blocks < need_blocks || v->n_blocks < need_blocks)
@@ -534,7 +544,7 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
     }
     if (!(a->rope_base > 1.0) || !std::isfinite(a->rope_base)) return fail(MILO_E_INVALID, "rope_base must be finite and > 1");
     if (!std::isfinite(a->softmax_scale)) return fail(MILO_E_INVALID, "softmax_scale must be finite");
-    const int ftype = k->dtype == MILO_F32 ? milo::kF32 : (k->dtype == MILO_BF16 ? milo::kBF16 : milo::kI8);
+    const int ftype = kernel_type(k->dtype);
     const int ttype = a->tail_dtype == MILO_F32 ? milo::kF32 : milo::kBF16;
     int split = a->split_len;
     if (split == 0) {
@@ -565,7 +575,7 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
     p.n_q_heads = a->n_q_heads;
     p.n_kv_heads = a->n_kv_heads;
     p.group = G;
-    p.f_type = k->dtype == MILO_F32 ? milo::kF32 : (k->dtype == MILO_BF16 ? milo::kBF16 : milo::kI8);
+    p.f_type = kernel_type(k->dtype);
     p.block_len = T;
     p.blocks_per_seq = a->blocks_per_seq;
     p.k_rank = k->rank; p.v_rank = v->rank;

@@ -66,7 +66,8 @@ __host__ __device__ inline int align16(int v) { return (v + 15) & ~15; }
 
 // A_k staging pitch per rank row of a 32-token tile (bytes); fp32 factors are
 // read straight from memory.
-__host__ __device__ inline int stage_pitch(int f) { return f == kBF16 ? 64 : (f == kI8 ? 40 : 0); }
+// 4-bit factors are dequantised into the bf16 layout as they are staged.
+__host__ __device__ inline int stage_pitch(int f) { return (f == kBF16 || f == kI4) ? 64 : (f == kI8 ? 40 : 0); }
 
 struct LdsLayout {
     int ang, qs, bk, rope, base, stage, loop_end;      // loop phase
@@ -86,7 +87,7 @@ __host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool
     if (!tail) stage = kWaves * 128 * stage_pitch(f);
     else if (f == kBF16) stage = kWaves * 32 * kTVP;
     // the B_k rows for the fragment build are staged in this area too
-    const int bk_rows = (tail || f == kF32) ? 0 : 128 * kD * (f == kBF16 ? 2 : 1);
+    const int bk_rows = (tail || f == kF32) ? 0 : (f == kI4 ? 128 * (kD / 2 + 4 * (kD / kI4Group)) : 128 * kD * (f == kBF16 ? 2 : 1));
     if (stage < bk_rows) stage = bk_rows;
     L.loop_end = align16(L.stage + stage);
     L.uw = 0;
@@ -101,6 +102,11 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Signed value of nibble k (0..7) of a word of eight 4-bit codes.
+__device__ __forceinline__ float nib(uint32_t w, int k) {
+    return static_cast<float>(static_cast<int32_t>(w << (28 - 4 * k)) >> 28);
 }
 
 template <int F>
@@ -153,7 +159,7 @@ __device__ __forceinline__ int stage_off_i8(int r, int t) {
 template <int F, bool TAIL>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
     constexpr int NS = (F == kF32) ? 2 : 1;
-    constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);
+    constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);  // kI4: half a byte, see below
     extern __shared__ __align__(16) uint8_t lds[];
     const int G = p.group;
     const int n_tiles = p.split_len / kTile;
@@ -228,11 +234,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 
     // A_k tile loads: 16-byte pieces, LPR lanes per rank row; rows past rk
     // repeat row rk - 1 (finite; their B_k fragment rows are zero).
-    constexpr int RB = kTile * ES;                  // bytes of one rank row of a tile
+    constexpr int RB = F == kI4 ? kTile / 2 : kTile * ES;  // bytes of one rank row of a tile
     constexpr int LPR = RB / 16 > 0 ? RB / 16 : 1;  // lanes per row
     constexpr int RPI = 64 / LPR;                   // rows per load instruction
     constexpr int NI = 128 / RPI;                   // load instructions for 128 ranks
     uint4 kraw[(F == kF32 || TAIL) ? 1 : NI];
+    float kscl[(F == kI4 && !TAIL) ? NI : 1];  // 4-bit: the tile's scale of each loaded row
     const int rk_pad = KS * 32;
     // Every load instruction is issued (rows clamped to rk - 1; identical
     // addresses coalesce), which keeps the registers free of partial paths.
@@ -244,8 +251,15 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                 for (int ci = 0; ci < NI; ++ci) {
                     // 32-bit offsets from the block's (uniform) base keep each address in one register
                     const int r = min(ci * RPI + lane / LPR, rk - 1);
-                    const uint32_t off = static_cast<uint32_t>((r * T + tt0) * ES + (lane % LPR) * 16);
-                    kraw[ci] = *reinterpret_cast<const uint4 *>(Ak + off);
+                    if constexpr (F == kI4) {
+                        // codes of row r, tokens tt0 .. tt0 + 31; the scales follow the rk code rows
+                        kraw[ci] = *reinterpret_cast<const uint4 *>(Ak + static_cast<uint32_t>(r * (T / 2) + tt0 / 2));
+                        kscl[ci] = *reinterpret_cast<const float *>(
+                            Ak + static_cast<uint32_t>(rk * (T / 2) + (r * (T / kI4Group) + tt0 / kI4Group) * 4));
+                    } else {
+                        const uint32_t off = static_cast<uint32_t>((r * T + tt0) * ES + (lane % LPR) * 16);
+                        kraw[ci] = *reinterpret_cast<const uint4 *>(Ak + off);
+                    }
                 }
             }
         }
@@ -256,7 +270,20 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             for (int ci = 0; ci < NI; ++ci)
                 if (ci * RPI < rk_pad) {  // uniform
                     const int r = ci * RPI + lane / LPR;
-                    if constexpr (F == kBF16) {
+                    if constexpr (F == kI4) {
+                        // one row's 32 codes -> four 16-byte chunks of bf16 (tokens 8 c .. 8 c + 7)
+                        const uint32_t wv[4] = {kraw[ci].x, kraw[ci].y, kraw[ci].z, kraw[ci].w};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            uint32_t h[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                h[e] = f32x2_to_bf16x2_bits(nib(wv[c], 2 * e) * kscl[ci], nib(wv[c], 2 * e + 1) * kscl[ci]);
+                            uint8_t *dst = stg + stage_off_bf16(r, 8 * c);
+                            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(h[0], h[1]);
+                            reinterpret_cast<uint2 *>(dst)[1] = make_uint2(h[2], h[3]);
+                        }
+                    } else if constexpr (F == kBF16) {
                         // 16-byte piece lane % LPR = tokens 8 (lane % LPR) .. + 7
                         uint8_t *dst = stg + stage_off_bf16(r, 8 * (lane % LPR));
                         reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
@@ -280,7 +307,15 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                 for (int mr = 0; mr < 8; ++mr) {
                     const int row = min(16 * mr + ln, rv - 1);
                     const uint32_t off = static_cast<uint32_t>((row * T + tb) * ES);
-                    if constexpr (F == kBF16) {
+                    if constexpr (F == kI4) {
+                        // codes of tokens tb .. tb + 3 and tb + 16 .. + 19, and the tile's scale
+                        const uint32_t o4 = static_cast<uint32_t>(row * (T / 2) + tb / 2);
+                        const uint32_t lo = *reinterpret_cast<const uint16_t *>(Av + o4);
+                        const uint32_t hi = *reinterpret_cast<const uint16_t *>(Av + o4 + 8);
+                        const float sc = *reinterpret_cast<const float *>(
+                            Av + static_cast<uint32_t>(rv * (T / 2) + (row * (T / kI4Group) + (tb - 4 * c4) / kI4Group) * 4));
+                        vraw[mr][0] = make_uint2(lo | (hi << 16), __float_as_uint(sc));
+                    } else if constexpr (F == kBF16) {
                         vraw[mr][0] = *reinterpret_cast<const uint2 *>(Av + off);
                         vraw[mr][1] = *reinterpret_cast<const uint2 *>(Av + off + 32);
                     } else {
@@ -300,9 +335,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         load_k(wt0);
         load_v(wt0);
     }
-    constexpr int NBK = (F == kF32 || TAIL) ? 1 : (128 * kD * ES / 16 + kThreads - 1) / kThreads;
+    // B_k part of the arena as raw 16-byte chunks (4-bit: rk code rows of d/2
+    // bytes, then rk x d/32 fp32 scales)
+    constexpr int BKB = F == kI4 ? kD / 2 + 4 * (kD / kI4Group) : kD * ES;  // bytes per rank
+    constexpr int NBK = (F == kF32 || TAIL) ? 1 : (128 * BKB / 16 + kThreads - 1) / kThreads;
     uint4 bkraw[NBK];
-    const int n16 = (F == kF32 || TAIL) ? 0 : (rk * kD * ES) >> 4;
+    const int n16 = (F == kF32 || TAIL) ? 0 : (rk * BKB) >> 4;
     if constexpr (F != kF32 && !TAIL) {
         // rk = 0: the (discarded) loads read the first bytes of q instead
         const uint4 *src = reinterpret_cast<const uint4 *>(n16 > 0 ? Bk : static_cast<const uint8_t *>(p.q));
@@ -398,6 +436,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                 if (r < rk) {
                     if constexpr (F == kBF16) v[e] = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(tmp)[r * kD + j]);
                     else if constexpr (F == kI8) v[e] = static_cast<float>(reinterpret_cast<const int8_t *>(tmp)[r * kD + j]) * bsc[r];
+                    else if constexpr (F == kI4) {
+                        const int byte = tmp[r * (kD / 2) + (j >> 1)];
+                        const int n = (j & 1) ? (byte >> 4) : (byte & 15);
+                        v[e] = static_cast<float>(n >= 8 ? n - 16 : n) *
+                               reinterpret_cast<const float *>(tmp + rk * (kD / 2))[r * (kD / kI4Group) + j / kI4Group];
+                    }
                     else v[e] = load_elem<F>(Bk, static_cast<int64_t>(r) * kD + j);
                 }
             }
@@ -465,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                 for (int ks = 0; ks < KS; ++ks) {
                     const bool first = ks == 0;  // zero accumulator input (inline constant)
                     u16x8_t bfr[NS];
-                    if constexpr (F == kBF16) {
+                    if constexpr (F == kBF16 || F == kI4) {
                         // ranks 32 ks + 8 c .. + 7 of token t by two transposing reads: lane
                         // (c, j) addresses rank row 32 ks + 8 c + j / 4 (+ 4), tokens 4 (j % 4) ..
                         const int row = 32 * ks + 8 * c4 + (ln >> 2);
@@ -605,6 +649,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                     u16x8_t af;
                     if constexpr (F == kBF16) {
                         af = __builtin_bit_cast(u16x8_t, make_uint4(vraw[mr][0].x, vraw[mr][0].y, vraw[mr][1].x, vraw[mr][1].y));
+                    } else if constexpr (F == kI4) {
+                        const float sc = __uint_as_float(vraw[mr][0].y);
+                        float v[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = nib(vraw[mr][0].x, e) * sc;
+                        u16x8_t f[1];
+                        frag_terms<1>(v, f);
+                        af = f[0];
                     } else {
                         float v[8];
 #pragma unroll
@@ -724,7 +776,15 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                 for (int e = 0; e < 8; ++e) {
                     const int r = 32 * ks + 8 * c4 + e;
                     const int rc = min(r, rv - 1);
-                    float x = load_elem<F>(Bv, static_cast<int64_t>(rc) * kD + dim);
+                    float x;
+                    if constexpr (F == kI4) {
+                        const int byte = Bv[rc * (kD / 2) + (dim >> 1)];
+                        const int n = (dim & 1) ? (byte >> 4) : (byte & 15);
+                        x = static_cast<float>(n >= 8 ? n - 16 : n) *
+                            reinterpret_cast<const float *>(Bv + rv * (kD / 2))[rc * (kD / kI4Group) + dim / kI4Group];
+                    } else {
+                        x = load_elem<F>(Bv, static_cast<int64_t>(rc) * kD + dim);
+                    }
                     if constexpr (F == kI8) x *= p.v_bscale[static_cast<int64_t>(fid) * kD + rc];
                     v[e] = r < rv ? x : 0.f;
                 }
@@ -905,6 +965,7 @@ hipError_t launch_decode_blocks(const DecodeParams &p, hipStream_t st) {
                     static_cast<unsigned>(p.batch));
     if (p.f_type == kBF16) return launch_partial<kBF16, false>(p, grid, st);
     if (p.f_type == kI8) return launch_partial<kI8, false>(p, grid, st);
+    if (p.f_type == kI4) return launch_partial<kI4, false>(p, grid, st);
     return launch_partial<kF32, false>(p, grid, st);
 }
 

@@ -8,7 +8,10 @@
 
 namespace milo {
 
-enum ElemType : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
+enum ElemType : int { kF32 = 0, kBF16 = 1, kI8 = 2, kI4 = 3 };
+// 4-bit factors: symmetric codes in [-7, 7], two per byte (element 2k in the low
+// nibble), one fp32 scale per kI4Group consecutive elements of a row.
+constexpr int kI4Group = 32;
 // Rank allocation policies (values of milo_alloc_policy).
 enum AllocPolicy : int { kAllocEntropy = 0, kAllocUniform = 1, kAllocRandom = 2 };
 
@@ -34,12 +37,13 @@ hipError_t launch_refine(const void *x, int x_type, const int64_t *row0, int64_t
 // Rank allocation for pools [pool_lo, pool_lo + n_pools) of the device pool
 // tables under `policy` (seed: the random policy's generator seed): ranks of
 // blocks, per-pool objective (may be null), and when a_off is non-null the
-// arena offsets (pool_base[p] + prefix of rank * (T + d) * elem).
+// arena offsets (pool_base[p] + prefix of rank * (a_bpr + b_bpr): a rank's
+// bytes in the A and in the B part of a block).
 hipError_t launch_alloc(const float *sigma, int sigma_pitch, int max_rank,
                         const int32_t *pool_ptr, const int64_t *budget, const int64_t *pool_base,
                         int pool_lo, int n_pools, int blk_lo, double eps2, int32_t *rank,
-                        double *objective, int64_t *a_off, int64_t *b_off, int block_len,
-                        int elem_bytes, int policy, uint64_t seed, hipStream_t st);
+                        double *objective, int64_t *a_off, int64_t *b_off, int a_bpr,
+                        int b_bpr, int policy, uint64_t seed, hipStream_t st);
 
 // Factor pairs from sorted eigenvectors and ranks: A_b^T (rank-major) and B_b
 // rows into the arena, plus INT8 scales.

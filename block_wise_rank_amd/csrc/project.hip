@@ -6,6 +6,10 @@
 // INT8: every row of B_b (one per rank) and every row of A_b (one per token)
 // gets an absmax scale s = max|row| / 127 and codes rint(x / s) clamped to
 // +-127, decided in fp32.
+// 4-bit: A_b = X_b B_b^T with the fp32-accurate B_b (the products are the
+// fp32 storage's, bit for bit), then every run of 32 consecutive elements of a
+// rank row of A^T (tokens) and of B (features) gets s = max|run| / 7 and codes
+// rint(x / s) in [-7, 7], decided in fp32.
 //
 // A^T = B~ X^T runs on bf16 MFMA (M = rank, N = token, K = feature): the
 // fragments of B~ stay in registers (one 32-rank tile per wave) while 32-token
@@ -32,7 +36,7 @@ __global__ __launch_bounds__(256) void project_kernel(
     const float *__restrict__ vt, const int32_t *__restrict__ rank,
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off,
     uint8_t *__restrict__ arena, float *__restrict__ a_scale, float *__restrict__ b_scale) {
-    constexpr int NS = (OUT == kF32) ? 3 : 1;  // bf16 terms of the B operand
+    constexpr int NS = (OUT == kF32 || OUT == kI4) ? 3 : 1;  // bf16 terms of the B operand
     __shared__ float sB_rows[kD];
     __shared__ float tmax[4][32];
 
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(256) void project_kernel(
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            if constexpr (OUT == kF32) {
+            if constexpr (OUT == kF32 || OUT == kI4) {
                 uint16_t h, mm, l;
                 split3_bf16(v[ks][e], h, mm, l);
                 fa[0][ks][e] = h;
@@ -98,6 +102,19 @@ __global__ __launch_bounds__(256) void project_kernel(
             }
         }
 
+    // 4-bit B: scale of each 32-feature run g of row i (features 32 g .. 32 g + 31
+    // sit in k-steps 2 g and 2 g + 1 of this lane and of lane ^ 32)
+    float sB4[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (OUT == kI4) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float m = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fmaxf(fabsf(v[2 * g][e]), fabsf(v[2 * g + 1][e])));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            sB4[g] = __fdiv_rn(m, 7.f);
+        }
+    }
     // ---- B rows (first part only) and B scales.
     if (part == 0 && row_ok) {
 #pragma unroll
@@ -110,6 +127,16 @@ __global__ __launch_bounds__(256) void project_kernel(
                 d4[1] = make_float4(v[ks][4], v[ks][5], v[ks][6], v[ks][7]);
             } else if constexpr (OUT == kBF16) {
                 *reinterpret_cast<u16x8_t *>(dst) = fa[0][ks];
+            } else if constexpr (OUT == kI4) {
+                const float sg = sB4[ks >> 1];
+                uint32_t w = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float c = sg > 0.f ? rintf(__fdiv_rn(v[ks][e], sg)) : 0.f;
+                    c = fminf(fmaxf(c, -7.f), 7.f);
+                    w |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xfu) << (4 * e);
+                }
+                *reinterpret_cast<uint32_t *>(Bb + static_cast<int64_t>(i) * (kD / 2) + 8 * ks + 4 * (lane >> 5)) = w;
             } else {
                 uint2 w;
                 w.x = (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][0])))) |
@@ -125,6 +152,10 @@ __global__ __launch_bounds__(256) void project_kernel(
         }
         if constexpr (OUT == kI8)
             if (lane < 32) b_scale[static_cast<int64_t>(blk) * kD + i] = sB;
+        if constexpr (OUT == kI4)
+            if (lane < 32)
+                *reinterpret_cast<float4 *>(Bb + static_cast<int64_t>(r) * (kD / 2) + 16 * i) =
+                    make_float4(sB4[0], sB4[1], sB4[2], sB4[3]);
     }
     if constexpr (OUT == kI8) {
         if (lane < 32) sB_rows[i] = row_ok ? sB : 0.f;
@@ -169,7 +200,33 @@ __global__ __launch_bounds__(256) void project_kernel(
             }
         }
         // acc[q]: rank row i' = 32 wave + 8 (q / 4) + 4 (lane / 32) + q % 4, token t.
-        if constexpr (OUT != kI8) {
+        if constexpr (OUT == kI4) {
+            // 32-token run of row i' = this tile: lanes of one half hold it
+            if (wave_active) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int ir = 32 * wave + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    float m = fabsf(acc[q]);
+#pragma unroll
+                    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                    const float sA = __fdiv_rn(m, 7.f);
+                    float c = sA > 0.f ? rintf(__fdiv_rn(acc[q], sA)) : 0.f;
+                    c = fminf(fmaxf(c, -7.f), 7.f);
+                    // eight tokens' nibbles into one word (token t0 + 8k + e at bits 4e)
+                    uint32_t w = (static_cast<uint32_t>(static_cast<int>(c)) & 0xfu) << (4 * (lane & 7));
+                    w |= __shfl_xor(w, 1, 64);
+                    w |= __shfl_xor(w, 2, 64);
+                    w |= __shfl_xor(w, 4, 64);
+                    if (ir < r) {
+                        if ((lane & 7) == 0)
+                            *reinterpret_cast<uint32_t *>(Ab + static_cast<int64_t>(ir) * (T / 2) + t / 2) = w;
+                        if ((lane & 31) == 0)
+                            *reinterpret_cast<float *>(Ab + static_cast<int64_t>(r) * (T / 2) +
+                                                       (static_cast<int64_t>(ir) * (T / kI4Group) + t0 / kI4Group) * 4) = sA;
+                    }
+                }
+            }
+        } else if constexpr (OUT != kI8) {
             if (wave_active) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
@@ -334,6 +391,10 @@ hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_
         MILO_PROJECT(1, kF32);
     else if (x_type == kF32 && out_type == kBF16)
         MILO_PROJECT(3, kBF16);
+    else if (x_type == kBF16 && out_type == kI4)
+        MILO_PROJECT(1, kI4);
+    else if (x_type == kF32 && out_type == kI4)
+        MILO_PROJECT(3, kI4);
     else
         MILO_PROJECT(3, kI8);
 #undef MILO_PROJECT

@@ -27,6 +27,14 @@ __device__ __forceinline__ float load_code(const uint8_t *p, int64_t idx) {
     else return static_cast<float>(reinterpret_cast<const int8_t *>(p)[idx]);
 }
 
+// Element idx of a 4-bit code row starting at p (two's-complement nibbles,
+// element 2k in the low nibble of byte k).
+__device__ __forceinline__ float i4_code(const uint8_t *p, int64_t idx) {
+    const int byte = p[idx >> 1];
+    const int n = (idx & 1) ? (byte >> 4) : (byte & 15);
+    return static_cast<float>(n >= 8 ? n - 16 : n);
+}
+
 template <int F, int OUT>
 __global__ __launch_bounds__(256) void reconstruct_kernel(
     const uint8_t *__restrict__ arena, const int32_t *__restrict__ rank,
@@ -43,14 +51,28 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(
     const uint8_t *Ab = arena + a_off[id];
     const uint8_t *Bb = arena + b_off[id];
     for (int e = tid; e < r * kD; e += 256) {
-        float v = load_code<F>(Bb, e);
-        if constexpr (F == kI8) v *= b_scale[static_cast<int64_t>(id) * kD + e / kD];
+        float v;
+        if constexpr (F == kI4) {
+            // code row i at Bb + i * d / 2, scales (r x d / 32) after the r code rows
+            const float *bs = reinterpret_cast<const float *>(Bb + static_cast<int64_t>(r) * (kD / 2));
+            v = i4_code(Bb, e) * bs[e / kI4Group];
+        } else {
+            v = load_code<F>(Bb, e);
+            if constexpr (F == kI8) v *= b_scale[static_cast<int64_t>(id) * kD + e / kD];
+        }
         Bs[e] = v;
     }
     for (int e = tid; e < r * 64; e += 256) {
         const int i = e >> 6, tt = e & 63;
-        float v = load_code<F>(Ab, static_cast<int64_t>(i) * T + t0 + tt);
-        if constexpr (F == kI8) v *= a_scale[static_cast<int64_t>(id) * T + t0 + tt];
+        float v;
+        if constexpr (F == kI4) {
+            const float *as = reinterpret_cast<const float *>(Ab + static_cast<int64_t>(r) * (T / 2));
+            const int64_t idx = static_cast<int64_t>(i) * T + t0 + tt;
+            v = i4_code(Ab, idx) * as[idx / kI4Group];
+        } else {
+            v = load_code<F>(Ab, static_cast<int64_t>(i) * T + t0 + tt);
+            if constexpr (F == kI8) v *= a_scale[static_cast<int64_t>(id) * T + t0 + tt];
+        }
         As[e] = v;
     }
     __syncthreads();
@@ -224,6 +246,8 @@ hipError_t launch_reconstruct(const void *arena, int f_type, const int32_t *rank
                        b_off, a_scale, b_scale, block_len, ids, out)
     if (f_type == kF32) {
         if (out_type == kF32) MILO_RECON(kF32, kF32); else MILO_RECON(kF32, kBF16);
+    } else if (f_type == kI4) {
+        if (out_type == kF32) MILO_RECON(kI4, kF32); else MILO_RECON(kI4, kBF16);
     } else {
         if (out_type == kF32) MILO_RECON(kI8, kF32); else MILO_RECON(kI8, kBF16);
     }

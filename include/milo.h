@@ -54,7 +54,8 @@ typedef enum milo_status {
 typedef enum milo_dtype {
     MILO_F32 = 0,
     MILO_BF16 = 1,
-    MILO_I8 = 2 /* factor storage only: per-row absmax INT8 with fp32 scales */
+    MILO_I8 = 2, /* factor storage only: per-row absmax INT8 with fp32 scales */
+    MILO_I4 = 3  /* factor storage only: 4-bit codes, an fp32 scale per 32 elements */
 } milo_dtype;
 
 /*
@@ -83,10 +84,20 @@ typedef struct milo_blocks {
  *   A_b is stored TRANSPOSED, rank-major: r_b rows of block_len elements,
  *       row i = column i of A_b, at byte offset a_off[b];
  *   B_b is stored as r_b rows of head_dim elements at byte offset b_off[b].
- * Element type `dtype`: MILO_F32, MILO_BF16, or MILO_I8 (codes).  For MILO_I8
+ * Element type `dtype`: MILO_F32, MILO_BF16, MILO_I8 or MILO_I4 (codes).  For MILO_I8
  * every row of A_b (one per token) has a scale a_scale[b*block_len + t] and
  * every row of B_b (one per rank) a scale b_scale[b*head_dim + i]; the decoded
  * value is code * scale.
+ * MILO_I4 (block_len a multiple of 128; the composition with low-bit KV
+ * quantisation of [REV] Key claims and FAQ, with this library's own group-wise
+ * quantiser): each row is cut into runs of 32 consecutive elements, each with
+ * an fp32 scale s = max|run| / 7 and codes rint(x / s) in [-7, 7] (decided in
+ * fp32), decoded value code * s.  Codes are two's-complement nibbles, two per
+ * byte, element 2k in the low nibble.  A_b's part at a_off[b]: the r_b code rows
+ * (block_len / 2 bytes each), then the r_b x (block_len / 32) scales.  B_b's
+ * part at b_off[b]: the r_b code rows (head_dim / 2 bytes each), then the
+ * r_b x (head_dim / 32) scales.  a_scale / b_scale are not used (NULL).  A_b
+ * is computed from the fp32-accurate B_b before either is quantised.
  * milo_compress_blocks writes rank, a_off, b_off, the arena and the scales;
  * the caller sizes the arena with milo_arena_bytes().
  */
@@ -133,7 +144,7 @@ typedef struct milo_factors {
  *              MILO_E_WORKSPACE and sets *workspace_bytes to the size that
  *              processes every block in one pass.  Any size >= the largest
  *              pool's need works: pools are then processed in chunks.
- * Supported dtype pairs (in -> factors): F32 -> F32, BF16 -> BF16, BF16 -> I8.
+ * Supported dtype pairs (in -> factors): F32 or BF16 -> any of F32, BF16, I8, I4.
  */
 milo_status milo_compress_blocks(const milo_blocks *in, const int32_t *pool_ptr, int32_t n_pools,
                                  const int64_t *budget, double eps2, float *sigma_out,

@@ -13,6 +13,41 @@ import numpy as np
 import torch
 
 _ELEM = {"f32": 4, "bf16": 2, "i8": 1}
+I4_GROUP = 32
+
+
+def pack_i4(codes: np.ndarray) -> np.ndarray:
+    """Rows of 4-bit codes in [-8, 7] -> bytes, element 2k in the low nibble of
+    byte k (the arena's nibble order)."""
+    c = (codes.astype(np.int16) & 0xF).astype(np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_i4(raw: np.ndarray, n: int) -> np.ndarray:
+    """Inverse of pack_i4 for rows of n codes."""
+    raw = raw.astype(np.uint8)
+    lo = (raw & 0xF).astype(np.int16)
+    hi = (raw >> 4).astype(np.int16)
+    out = np.empty(raw.shape[:-1] + (n,), dtype=np.int16)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return np.where(out >= 8, out - 16, out).astype(np.int8)
+
+
+def i4_rank_bytes(T: int, d: int):
+    """Bytes one rank takes in a block's A part and B part (codes + fp32 scales)."""
+    return T // 2 + 4 * (T // I4_GROUP), d // 2 + 4 * (d // I4_GROUP)
+
+
+def read_i4_block(arena: np.ndarray, a_off: int, b_off: int, r: int, T: int, d: int):
+    """(A codes [r, T], A scales [r, T/32], B codes [r, d], B scales [r, d/32]) of a block."""
+    a_codes = unpack_i4(arena[a_off:a_off + r * T // 2].reshape(r, T // 2), T)
+    o = a_off + r * T // 2
+    a_sc = arena[o:o + 4 * r * (T // I4_GROUP)].view(np.float32).reshape(r, T // I4_GROUP)
+    b_codes = unpack_i4(arena[b_off:b_off + r * d // 2].reshape(r, d // 2), d)
+    o = b_off + r * d // 2
+    b_sc = arena[o:o + 4 * r * (d // I4_GROUP)].view(np.float32).reshape(r, d // I4_GROUP)
+    return a_codes, a_sc, b_codes, b_sc
 
 
 def random_factor_set(n_blocks: int, T: int, d: int, storage: str, seed: int,
@@ -24,10 +59,13 @@ def random_factor_set(n_blocks: int, T: int, d: int, storage: str, seed: int,
     if ranks is None:
         ranks = rng.integers(rank_range[0], rank_range[1] + 1, size=n_blocks)
     ranks = np.asarray(ranks, dtype=np.int32)
-    e = _ELEM[storage]
-    sizes = ranks.astype(np.int64) * (T + d) * e
+    if storage == "i4":
+        abpr, bbpr = i4_rank_bytes(T, d)
+    else:
+        abpr, bbpr = T * _ELEM[storage], d * _ELEM[storage]
+    sizes = ranks.astype(np.int64) * (abpr + bbpr)
     a_off = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int64)
-    b_off = a_off + ranks.astype(np.int64) * T * e
+    b_off = a_off + ranks.astype(np.int64) * abpr
     total = int(sizes.sum())
     arena = np.zeros(max(total, 256), dtype=np.uint8)
     a_scale = np.zeros(n_blocks * T, dtype=np.float32) if storage == "i8" else None
@@ -49,6 +87,21 @@ def random_factor_set(n_blocks: int, T: int, d: int, storage: str, seed: int,
             raw_b = Bt.view(torch.int16).numpy().view(np.uint8)
             A_dec.append(At.to(torch.float64).numpy().T.copy())
             B_dec.append(Bt.to(torch.float64).numpy())
+        elif storage == "i4":
+            # codes in [-7, 7], one positive scale per 32 elements of a row (some
+            # runs all zero with a zero scale, as the quantiser leaves them)
+            ca = rng.integers(-7, 8, size=(r, T)).astype(np.int8)
+            cb = rng.integers(-7, 8, size=(r, d)).astype(np.int8)
+            sa = (rng.uniform(0.5, 1.5, size=(r, T // I4_GROUP)) * a_std * 3 / 7).astype(np.float32)
+            sb = (rng.uniform(0.5, 1.5, size=(r, d // I4_GROUP)) * 3 / np.sqrt(max(r, 1)) / 7).astype(np.float32)
+            if r > 0:
+                i, g = rng.integers(0, r), rng.integers(0, T // I4_GROUP)
+                ca[i, g * I4_GROUP:(g + 1) * I4_GROUP] = 0
+                sa[i, g] = 0.0
+            raw_a = np.concatenate([pack_i4(ca).reshape(-1), sa.reshape(-1).view(np.uint8)])
+            raw_b = np.concatenate([pack_i4(cb).reshape(-1), sb.reshape(-1).view(np.uint8)])
+            A_dec.append((ca.astype(np.float32) * np.repeat(sa, I4_GROUP, axis=1)).astype(np.float64).T.copy())
+            B_dec.append((cb.astype(np.float32) * np.repeat(sb, I4_GROUP, axis=1)).astype(np.float64))
         else:
             qa = rng.integers(-127, 128, size=(T, r)).astype(np.int8)
             qb = rng.integers(-127, 128, size=(r, d)).astype(np.int8)

@@ -41,6 +41,16 @@ def _arr(typ, vals):
     return (typ * len(vals))(*vals)
 
 
+def test_arena_bytes_formula_i4(L):
+    """4-bit: per rank T/2 + T/8 bytes of A (codes, fp32 scales per 32 tokens)
+    and d/2 + d/8 bytes of B."""
+    pp = _arr(ctypes.c_int32, [0, 8, 8, 20])
+    bud = _arr(ctypes.c_int64, [512, 5, 10 ** 6])
+    n = L.milo_arena_bytes(3, 256, 128, ctypes.cast(pp, ctypes.c_void_p), 3,
+                           ctypes.cast(bud, ctypes.c_void_p))
+    assert n == (512 + 0 + 12 * 128) * ((128 + 32) + (64 + 16))
+
+
 def test_arena_bytes_formula(L):
     pp = _arr(ctypes.c_int32, [0, 8, 8, 20])
     bud = _arr(ctypes.c_int64, [512, 5, 10 ** 6])
@@ -94,6 +104,7 @@ def _compress(L, blocks, factors, pp=(0, 8), bud=(512,), eps2=1e-4, ws=None, wsb
 
 @pytest.mark.parametrize("case,expect", [
     ("head_dim", 2), ("block_len", 2), ("block_len_small", 2), ("in_dtype", 2), ("pair", 2),
+    ("i4_block_len", 2),
     ("pool0", 1), ("pool_end", 1), ("pool_order", 1), ("budget_neg", 1), ("eps", 1),
     ("stride", 1), ("align", 1), ("geometry", 1), ("arena_small", 1), ("i8_scales", 1),
 ])
@@ -110,7 +121,10 @@ def test_compress_validation(L, case, expect):
     elif case == "in_dtype":
         b.dtype = 2
     elif case == "pair":
-        b.dtype, f.dtype = 0, 1
+        f.dtype = 9  # no such factor dtype
+    elif case == "i4_block_len":
+        b.block_len = f.block_len = 192  # 4-bit factors need whole 128-token multiples
+        f.dtype = 3
     elif case == "pool0":
         kw["pp"] = (1, 8)
     elif case == "pool_end":

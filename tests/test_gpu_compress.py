@@ -124,3 +124,56 @@ def test_config3_budget_precision_sweep(frac, storage):
         # INT8 invariants: every non-empty row of B reaches +-127; scales >= 0
         bs = f.b_scale.cpu().numpy()
         assert (bs >= 0).all() and (f.a_scale.cpu().numpy() >= 0).all()
+
+
+@pytest.mark.parametrize("kind", ["k", "v"])
+def test_int4_factors(kind):
+    """4-bit factors on the config-1 shapes (1024-token bf16 blocks, 50% budget).
+
+    The 4-bit path computes its factors as the fp32 storage does (the same
+    products), then quantises them.  So every code and scale must equal the
+    oracle's quantiser applied to the fp32 factors of a call on the same blocks
+    (the code decided in fp32 on both sides): exact parity.  The quantised
+    factors themselves differ from the oracle's by the eigenvector differences
+    the fp32 parity allows, which move codes at rounding boundaries; the rebuilt
+    blocks are therefore compared with X against the oracle's own 4-bit error."""
+    from synthetic.factors import read_i4_block
+
+    cfg = CONFIGS[1]
+    X = layer_inputs(cfg, 0, kind, device="cpu")
+    pp, bud = layer_pools(cfg)
+    Xg = X.to(DEV)
+    f32, s32, _, _ = run_gpu_compress(Xg, pp, bud, cfg.eps2, "f32")
+    f4, s4, _, _ = run_gpu_compress(Xg, pp, bud, cfg.eps2, "i4")
+    assert torch.equal(f32.rank, f4.rank) and torch.equal(s32, s4)
+    n, T, d = X.shape
+    ar32, ar4 = f32.arena.cpu().numpy(), f4.arena.cpu().numpy()
+    rk = f4.rank.cpu().numpy()
+    for b in range(n):
+        r = int(rk[b])
+        if r == 0:
+            continue
+        ao, bo = int(f32.a_off[b]), int(f32.b_off[b])
+        A32 = ar32[ao:ao + 4 * r * T].view(np.float32).reshape(r, T)
+        B32 = ar32[bo:bo + 4 * r * d].view(np.float32).reshape(r, d)
+        sa, ca, _ = oracle.quant_int4_groups(A32)
+        sb, cb, _ = oracle.quant_int4_groups(B32)
+        ac, asc, bc, bsc = read_i4_block(ar4, int(f4.a_off[b]), int(f4.b_off[b]), r, T, d)
+        assert np.array_equal(ac, ca), f"block {b}: A codes"
+        assert np.array_equal(bc, cb), f"block {b}: B codes"
+        assert np.array_equal(asc, sa.astype(np.float32)) and np.array_equal(bsc, sb.astype(np.float32)), b
+
+    X64 = X.to(torch.float64).numpy()
+    key = (1, kind, n)
+    if key not in _SVD:
+        _SVD[key] = oracle.svd_blocks(X64)
+    comp = oracle.compress(X64, pp, bud, cfg.eps2, "i4", svd=_SVD[key])
+    xh = reconstruct_all(f4).cpu().numpy()
+    e_gpu = np.array([np.linalg.norm(xh[b] - X64[b]) / np.linalg.norm(X64[b]) for b in range(n)])
+    e_ora = np.array([np.linalg.norm(oracle.reconstruct(comp.A[b], comp.B[b]) - X64[b]) / np.linalg.norm(X64[b])
+                      for b in range(n)])
+    print(f"\n[i4 {kind}] rel-F to X: gpu mean {e_gpu.mean():.4f} max {e_gpu.max():.4f}; "
+          f"oracle mean {e_ora.mean():.4f} max {e_ora.max():.4f}; memory ratio "
+          f"{f4.nbytes() / (n * T * d * 2):.4f}")
+    assert (e_gpu <= 1.1 * e_ora + 2e-3).all(), np.max(e_gpu - 1.1 * e_ora)
+    assert abs(e_gpu.mean() - e_ora.mean()) <= 0.05 * e_ora.mean()

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from block_wise_rank_amd import Factors, MiloError, milo_decode_attention, milo_fetch_blocks
-from synthetic.factors import random_factor_set
+from synthetic.factors import i4_rank_bytes, random_factor_set
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -33,7 +33,7 @@ def _decode(q, q_pos, kf, vf, bps, hkv, sel_ptr, sel_blk, sel_max):
     return out
 
 
-@pytest.mark.parametrize("storage", ["bf16", "i8", "f32"])
+@pytest.mark.parametrize("storage", ["bf16", "i8", "i4", "f32"])
 def test_fetch_then_decode_equals_resident(storage):
     batch, hkv, hq, T, bps = 2, 2, 16, 512, 8
     n = batch * hkv * bps
@@ -60,13 +60,17 @@ def test_fetch_then_decode_equals_resident(storage):
         milo_fetch_blocks(v_host, v_dev, listed, stream=st)
     st.synchronize()
 
-    e = {"f32": 4, "bf16": 2, "i8": 1}[storage]
+    if storage == "i4":
+        abpr, bbpr = i4_rank_bytes(T, 128)
+    else:
+        e = {"f32": 4, "bf16": 2, "i8": 1}[storage]
+        abpr, bbpr = T * e, 128 * e
     for host, dev in ((k_host, k_dev), (v_host, v_dev)):
         arena_h, arena_d = host.arena, dev.arena.cpu()
         touched = np.zeros(arena_h.numel(), dtype=bool)
         for b in ids:
             r = int(host.rank[b])
-            for off, ln in ((int(host.a_off[b]), r * T * e), (int(host.b_off[b]), r * 128 * e)):
+            for off, ln in ((int(host.a_off[b]), r * abpr), (int(host.b_off[b]), r * bbpr)):
                 assert torch.equal(arena_d[off:off + ln], arena_h[off:off + ln]), f"block {b}"
                 touched[off:off + ln] = True
         assert bool((arena_d.numpy()[~touched] == 0x5A).all()), "bytes outside the listed blocks changed"

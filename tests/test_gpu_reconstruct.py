@@ -1,7 +1,7 @@
 """GPU parity of milo_reconstruct on seeded factor sets in the arena layout
 against the oracle's X_hat = A B (fp64), for the listed blocks only: ranks 0, 1,
 around the 32-rank steps and 128; block lists in any order with repeats; fp32
-and bf16 output; bf16 (MFMA path), INT8 and fp32 factors."""
+and bf16 output; bf16 (MFMA path), INT8, 4-bit and fp32 factors."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.mark.parametrize("storage", ["bf16", "i8", "f32"])
+@pytest.mark.parametrize("storage", ["bf16", "i8", "i4", "f32"])
 @pytest.mark.parametrize("T", [256, 2048])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_reconstruct_listed_blocks(storage, T, out_dtype):
