@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--factor-dtype", default=None, help="bf16 | i8 (default: the config's)")
+    ap.add_argument("--factor-dtype", default=None, help="bf16 | i8 | i4 (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-offloaded cache measurement (compressed vs full KV over PCIe)")
@@ -394,7 +394,8 @@ def main():
     ranks = {k: F[k].rank.to(torch.int64) for k in ("k", "v")}
     sw = torch.cat([sweeps["k"], sweeps["v"]]).to(torch.float64)
     sweeps_mean = float(sw.abs().mean())
-    fe = {"f32": 4, "bf16": 2, "i8": 1}[fdt]
+    # bytes per factor element (4-bit: half a byte + an fp32 scale per 32 elements)
+    fe = {"f32": 4, "bf16": 2, "i8": 1, "i4": 5 / 8}[fdt]
     xe = 4 if cfg.storage == "f32" else 2
     tot_rank = int(ranks["k"].sum() + ranks["v"].sum())
     ctx_tokens = cfg.context_tokens_per_step
@@ -412,7 +413,7 @@ def main():
                         ids.append(layer * nb_layer + (s_ * H + h) * cfg.blocks_per_seq + b)
         att = torch.tensor(ids, device=dev)
     att_rank = int(ranks["k"][att].sum() + ranks["v"][att].sum())
-    dec_bytes_all_layers = att_rank * (T + d) * fe
+    dec_bytes_all_layers = int(att_rank * (T + d) * fe)
     if fdt == "i8":
         dec_bytes_all_layers += 4 * (2 * att.numel() * T + att_rank)
     tail_bytes_all = 2 * L * cfg.batch * H * cfg.tail_len * d * xe
@@ -470,7 +471,7 @@ def main():
         roof["kernel"] = dominant
 
     full_kv = 2 * n_all * T * d * 2
-    factor_bytes = tot_rank * (T + d) * fe + (4 * (2 * n_all * T + tot_rank) if fdt == "i8" else 0)
+    factor_bytes = int(tot_rank * (T + d) * fe) + (4 * (2 * n_all * T + tot_rank) if fdt == "i8" else 0)
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
     cpu = None
@@ -535,13 +536,13 @@ def offload_measure(milo, torch, np, cfg, F, X, Q, q_pos, sel, nb_layer, fdt, xd
         sel_kw = dict(sel_ptr=torch.tensor(np.cumsum([0] + [len(x) for x in sel]), dtype=torch.int32, device=dev),
                       sel_blk=torch.tensor(sum(sel, []), dtype=torch.int32, device=dev), sel_max=cfg.sel_blocks)
     ids_t = torch.tensor(ids, dtype=torch.int32)
-    es = {"f32": 4, "bf16": 2, "i8": 1}[fdt]
+    es = {"f32": 4, "bf16": 2, "i8": 1, "i4": 5 / 8}[fdt]
 
     def layer_host_set(f, layer):
         """A compact pinned-host copy of one layer's factor set (offsets rebased)."""
         v = f.view(layer * nb_layer, nb_layer)
         lo = int(v.a_off.min())
-        hi = int((v.b_off + v.rank.to(torch.int64) * d * es).max())
+        hi = int((v.b_off + (v.rank.to(torch.int64) * int(d * es))).max())
         h = milo.Factors(fdt, nb_layer, T, d, rank=v.rank.cpu().pin_memory(), a_off=(v.a_off - lo).cpu().pin_memory(),
                          b_off=(v.b_off - lo).cpu().pin_memory(), arena=v.arena[lo:hi].cpu().pin_memory())
         if fdt == "i8":
@@ -603,7 +604,7 @@ def offload_measure(milo, torch, np, cfg, F, X, Q, q_pos, sel, nb_layer, fdt, xd
     for i in range(n_src):
         for h in (hk[i], hv[i]):
             r = h.rank.to(torch.int64)[ids_t.long()]
-            comp_bytes += int(r.sum()) * (T + d) * es + (4 * len(ids) * (T + d) if fdt == "i8" else 0)
+            comp_bytes += int(int(r.sum()) * (T + d) * es) + (4 * len(ids) * (T + d) if fdt == "i8" else 0)
     comp_bytes = comp_bytes * L / n_src
     del hk, hv, dk, dv, meta
 

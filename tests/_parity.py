@@ -14,7 +14,10 @@ from synthetic import pool_layout
 # for every singular value above eps (all the ones the allocation can pick),
 # absolute 1e-3 * eps below it, where log(1 + sigma^2/eps^2) is flat.
 SIGMA_REL = 1e-3
-RECON_TOL = {"f32": 1e-3, "bf16": 2e-2, "i8": 2e-2}
+# 4-bit: the factors agree with the oracle's to ~1e-3, and an entry that close
+# to a rounding boundary moves by a whole step s = max|run| / 7 (about a third
+# of the run's rms): at most ~1.4% of entries, ~4% rel-Frobenius.
+RECON_TOL = {"f32": 1e-3, "bf16": 2e-2, "i8": 2e-2, "i4": 5e-2}
 
 
 def run_gpu_compress(X: torch.Tensor, pool_ptr, budgets, eps2: float, storage: str):

@@ -110,7 +110,7 @@ def test_ranks_bit_exact_given_oracle_sigma():
 
 
 @pytest.mark.parametrize("frac", [0.25, 0.5, 0.75])
-@pytest.mark.parametrize("storage", ["bf16", "i8"])
+@pytest.mark.parametrize("storage", ["bf16", "i8", "i4"])
 def test_config3_budget_precision_sweep(frac, storage):
     cfg, X64, pp, bud, f, sig, obj, sweeps, comp = _case(3, "k", storage=storage, frac=frac)
     r_gpu = f.rank.cpu().numpy()
