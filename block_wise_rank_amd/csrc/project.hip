@@ -30,6 +30,38 @@ namespace {
 
 constexpr int kTokensPerWG = 256;
 
+// 4-bit B row i: this lane holds features 16 ks + 8 (lane / 32) + e of it, so
+// the 32-feature run g sits in k-steps 2 g and 2 g + 1 of this lane and of
+// lane ^ 32.  Every lane takes part (cross-lane max); `store` picks the writers.
+__device__ __forceinline__ void store_b_i4(const float (&v)[8][8], int i, int r, int lane, bool store,
+                                           uint8_t *Bb) {
+    float sB4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fmaxf(fabsf(v[2 * g][e]), fabsf(v[2 * g + 1][e])));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        sB4[g] = __fdiv_rn(m, 7.f);
+    }
+    if (!store) return;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const float sg = sB4[ks >> 1];
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float c = sg > 0.f ? rintf(__fdiv_rn(v[ks][e], sg)) : 0.f;
+            c = fminf(fmaxf(c, -7.f), 7.f);
+            w |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xfu) << (4 * e);
+        }
+        *reinterpret_cast<uint32_t *>(Bb + static_cast<int64_t>(i) * (kD / 2) + 8 * ks + 4 * (lane >> 5)) = w;
+    }
+    if (lane < 32)
+        *reinterpret_cast<float4 *>(Bb + static_cast<int64_t>(r) * (kD / 2) + 16 * i) =
+            make_float4(sB4[0], sB4[1], sB4[2], sB4[3]);
+}
+
 template <int NX, int OUT>
 __global__ __launch_bounds__(256) void project_kernel(
     const void *__restrict__ x, const int64_t *__restrict__ row0, int64_t row_stride, int T,
@@ -102,21 +134,9 @@ __global__ __launch_bounds__(256) void project_kernel(
             }
         }
 
-    // 4-bit B: scale of each 32-feature run g of row i (features 32 g .. 32 g + 31
-    // sit in k-steps 2 g and 2 g + 1 of this lane and of lane ^ 32)
-    float sB4[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (OUT == kI4) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float m = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m = fmaxf(m, fmaxf(fabsf(v[2 * g][e]), fabsf(v[2 * g + 1][e])));
-            m = fmaxf(m, __shfl_xor(m, 32, 64));
-            sB4[g] = __fdiv_rn(m, 7.f);
-        }
-    }
     // ---- B rows (first part only) and B scales.
-    if (part == 0 && row_ok) {
+    if constexpr (OUT == kI4) store_b_i4(v, i, r, lane, part == 0 && row_ok, Bb);
+    if (OUT != kI4 && part == 0 && row_ok) {
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int j0 = 16 * ks + 8 * (lane >> 5);
@@ -127,16 +147,6 @@ __global__ __launch_bounds__(256) void project_kernel(
                 d4[1] = make_float4(v[ks][4], v[ks][5], v[ks][6], v[ks][7]);
             } else if constexpr (OUT == kBF16) {
                 *reinterpret_cast<u16x8_t *>(dst) = fa[0][ks];
-            } else if constexpr (OUT == kI4) {
-                const float sg = sB4[ks >> 1];
-                uint32_t w = 0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float c = sg > 0.f ? rintf(__fdiv_rn(v[ks][e], sg)) : 0.f;
-                    c = fminf(fmaxf(c, -7.f), 7.f);
-                    w |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xfu) << (4 * e);
-                }
-                *reinterpret_cast<uint32_t *>(Bb + static_cast<int64_t>(i) * (kD / 2) + 8 * ks + 4 * (lane >> 5)) = w;
             } else {
                 uint2 w;
                 w.x = (static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(v[ks][0])))) |
@@ -152,10 +162,6 @@ __global__ __launch_bounds__(256) void project_kernel(
         }
         if constexpr (OUT == kI8)
             if (lane < 32) b_scale[static_cast<int64_t>(blk) * kD + i] = sB;
-        if constexpr (OUT == kI4)
-            if (lane < 32)
-                *reinterpret_cast<float4 *>(Bb + static_cast<int64_t>(r) * (kD / 2) + 16 * i) =
-                    make_float4(sB4[0], sB4[1], sB4[2], sB4[3]);
     }
     if constexpr (OUT == kI8) {
         if (lane < 32) sB_rows[i] = row_ok ? sB : 0.f;
@@ -362,6 +368,153 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(
     }
 }
 
+// bf16 X -> fp32 or 4-bit factors: the B operand in three bf16 terms (the
+// products are fp32-accurate and identical for both storages, so the 4-bit
+// codes are those of the fp32 factors), 1024-token parts with the next X tile
+// loaded while the current one's products run.  Each wave's 32 rank rows are
+// collected in LDS as fp32 for 128 tokens; the flush writes fp32 rows as whole
+// pieces, or quantises each 32-token run (one run per lane: max, scale, codes)
+// and writes its 16 code bytes and its scale.
+constexpr int kRunP = 36;           // LDS floats per staged 32-token run (16-byte aligned pieces)
+constexpr int kRowP = 4 * kRunP;    // LDS floats per staged rank row (128 tokens)
+
+template <int OUT>
+__global__ __launch_bounds__(256, 2) void project_split_kernel(
+    const uint16_t *__restrict__ x, const int64_t *__restrict__ row0, int64_t row_stride, int T,
+    const float *__restrict__ vt, const int32_t *__restrict__ rank,
+    const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off, uint8_t *__restrict__ arena) {
+    __shared__ __align__(16) float stage[4][32 * kRowP];
+    const int blk = blockIdx.x, part = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = rank[blk];
+    if (32 * wave >= r) return;  // no rank rows for this wave (waves are independent)
+    const int t_begin = part * kPartBF;
+    const int t_end = min(T, t_begin + kPartBF);
+    uint8_t *Ab = arena + a_off[blk];
+    uint8_t *Bb = arena + b_off[blk];
+
+    // B fragments: rank row i = 32 wave + lane % 32, features 16 ks + 8 (lane / 32) + e
+    const int i = 32 * wave + (lane & 31);
+    const bool row_ok = i < r;
+    const float *vrow = vt + static_cast<int64_t>(blk) * kD * kD + static_cast<int64_t>(i) * kD;
+    float v[8][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (row_ok) {
+            a = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5));
+            b = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5) + 4);
+        }
+        v[ks][0] = a.x; v[ks][1] = a.y; v[ks][2] = a.z; v[ks][3] = a.w;
+        v[ks][4] = b.x; v[ks][5] = b.y; v[ks][6] = b.z; v[ks][7] = b.w;
+        if constexpr (OUT == kF32)
+            if (part == 0 && row_ok) {
+                float4 *d4 = reinterpret_cast<float4 *>(Bb + (static_cast<int64_t>(i) * kD + 16 * ks + 8 * (lane >> 5)) * 4);
+                d4[0] = a;
+                d4[1] = b;
+            }
+    }
+    if constexpr (OUT == kI4) store_b_i4(v, i, r, lane, part == 0 && row_ok, Bb);
+    u16x8_t fa[3][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint16_t h, mm, l;
+            split3_bf16(v[ks][e], h, mm, l);
+            fa[0][ks][e] = h;
+            fa[1][ks][e] = mm;
+            fa[2][ks][e] = l;
+        }
+
+    const uint16_t *xb = x + (row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride) + 8 * (lane >> 5);
+    u16x8_t xn[8];
+    auto load_x = [&](int t0) {
+        const uint16_t *xr = xb + static_cast<int64_t>(t0 + (lane & 31)) * row_stride;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) xn[ks] = *reinterpret_cast<const u16x8_t *>(xr + 16 * ks);
+    };
+    float *stg = stage[wave];
+    load_x(t_begin);
+    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+        u16x8_t xc[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) xc[ks] = xn[ks];
+        load_x(t0 + 32 < t_end ? t0 + 32 : t0);  // the last tile reloads itself (unused)
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16_t acc = zero16(), acc1 = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ks += 2)
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                acc = mfma32x32x16(fa[s][ks], xc[ks], acc);
+                acc1 = mfma32x32x16(fa[s][ks + 1], xc[ks + 1], acc1);
+            }
+        acc += acc1;
+        // acc[q]: rank row 8 (q / 4) + 4 (lane / 32) + q % 4 of this wave, token lane % 32
+        const int g = ((t0 - t_begin) & 127) >> 5;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+            stg[row * kRowP + g * kRunP + (lane & 31)] = acc[q];
+        }
+        if (g == 3 || t0 + 32 >= t_end) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int tok0 = t0 - 32 * g;  // first token of the flush
+            if constexpr (OUT == kF32) {
+                // (g + 1) runs of 32 tokens per row, as 16-byte pieces of 4 tokens
+#pragma unroll
+                for (int rr = 0; rr < 32; rr += 2) {
+                    const int row = rr + (lane >> 5), piece = lane & 31;
+                    const int ir = 32 * wave + row;
+                    if (ir < r && piece < 8 * (g + 1))
+                        *reinterpret_cast<float4 *>(Ab + (static_cast<int64_t>(ir) * T + tok0 + 4 * piece) * 4) =
+                            *reinterpret_cast<const float4 *>(stg + row * kRowP + (piece >> 3) * kRunP + 4 * (piece & 7));
+                }
+            } else {
+                // 128 runs (32 rows x 4), two per lane; block_len % 128 == 0, so g == 3 here
+#pragma unroll
+                for (int j0 = 0; j0 < 128; j0 += 64) {
+                    const int j = j0 + lane, row = j >> 2, gg = j & 3;
+                    const int ir = 32 * wave + row;
+                    const float4 *src = reinterpret_cast<const float4 *>(stg + row * kRowP + gg * kRunP);
+                    float m = 0.f;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float4 a = src[k];
+                        m = fmaxf(fmaxf(m, fmaxf(fabsf(a.x), fabsf(a.y))), fmaxf(fabsf(a.z), fabsf(a.w)));
+                    }
+                    const float sA = __fdiv_rn(m, 7.f);
+                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float4 a = src[k];
+                        const float f[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float c = sA > 0.f ? rintf(__fdiv_rn(f[e], sA)) : 0.f;
+                            c = fminf(fmaxf(c, -7.f), 7.f);
+                            w[k >> 1] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xfu) << (4 * (4 * (k & 1) + e));
+                        }
+                    }
+                    if (ir < r) {
+                        *reinterpret_cast<uint4 *>(Ab + static_cast<int64_t>(ir) * (T / 2) + (tok0 + 32 * gg) / 2) =
+                            make_uint4(w[0], w[1], w[2], w[3]);
+                        *reinterpret_cast<float *>(Ab + static_cast<int64_t>(r) * (T / 2) +
+                                                   (static_cast<int64_t>(ir) * (T / kI4Group) + tok0 / kI4Group + gg) * 4) = sA;
+                    }
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
@@ -375,6 +528,16 @@ hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_
                            row_stride, block_len, vt, rank, a_off, b_off, static_cast<uint8_t *>(arena));
         return hipGetLastError();
     }
+    if (x_type == kBF16 && (out_type == kF32 || out_type == kI4)) {
+        const dim3 g(static_cast<unsigned>(n_blocks), static_cast<unsigned>((block_len + kPartBF - 1) / kPartBF));
+        if (out_type == kF32)
+            hipLaunchKernelGGL(project_split_kernel<kF32>, g, dim3(256), 0, st, static_cast<const uint16_t *>(x), row0,
+                               row_stride, block_len, vt, rank, a_off, b_off, static_cast<uint8_t *>(arena));
+        else
+            hipLaunchKernelGGL(project_split_kernel<kI4>, g, dim3(256), 0, st, static_cast<const uint16_t *>(x), row0,
+                               row_stride, block_len, vt, rank, a_off, b_off, static_cast<uint8_t *>(arena));
+        return hipGetLastError();
+    }
     const dim3 grid(static_cast<unsigned>(n_blocks),
                     static_cast<unsigned>((block_len + kTokensPerWG - 1) / kTokensPerWG));
     uint8_t *ar = static_cast<uint8_t *>(arena);
@@ -383,16 +546,10 @@ hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_
                        block_len, vt, rank, a_off, b_off, ar, a_scale, b_scale)
     if (x_type == kF32 && out_type == kF32)
         MILO_PROJECT(3, kF32);
-    else if (x_type == kBF16 && out_type == kBF16)
-        MILO_PROJECT(1, kBF16);
     else if (x_type == kBF16 && out_type == kI8)
         MILO_PROJECT(1, kI8);
-    else if (x_type == kBF16 && out_type == kF32)
-        MILO_PROJECT(1, kF32);
     else if (x_type == kF32 && out_type == kBF16)
         MILO_PROJECT(3, kBF16);
-    else if (x_type == kBF16 && out_type == kI4)
-        MILO_PROJECT(1, kI4);
     else if (x_type == kF32 && out_type == kI4)
         MILO_PROJECT(3, kI4);
     else
