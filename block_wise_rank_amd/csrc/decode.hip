@@ -104,6 +104,10 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 // Signed value of nibble k (0..7) of a word of eight 4-bit codes.
 __device__ __forceinline__ float nib(uint32_t w, int k) {
     return static_cast<float>(static_cast<int32_t>(w << (28 - 4 * k)) >> 28);
@@ -165,8 +169,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     const int n_tiles = p.split_len / kTile;
     const LdsLayout L = lds_layout(F, NS, n_tiles, TAIL, G);
     float2 *ang = reinterpret_cast<float2 *>(lds + L.ang);
-    const float2 *rope = reinterpret_cast<const float2 *>(lds + L.rope);
-    const float2 *basetab = reinterpret_cast<const float2 *>(lds + L.base);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -230,7 +232,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     uint8_t *stg = lds + L.stage;
     if constexpr (!TAIL) stg += wave * 128 * stage_pitch(F);
     else stg += wave * 32 * kTVP;
-    const uint16_t *bkf = reinterpret_cast<const uint16_t *>(lds + L.bk);
 
     // A_k tile loads: 16-byte pieces, LPR lanes per rank row; rows past rk
     // repeat row rk - 1 (finite; their B_k fragment rows are zero).
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             }
         }
     };
-    auto stage_k = [&]() {
+    auto stage_k = [&](uint8_t *sdst) {
         if constexpr (F != kF32 && !TAIL) {
 #pragma unroll
             for (int ci = 0; ci < NI; ++ci)
@@ -279,17 +280,17 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
                                 h[e] = f32x2_to_bf16x2_bits(nib(wv[c], 2 * e) * kscl[ci], nib(wv[c], 2 * e + 1) * kscl[ci]);
-                            uint8_t *dst = stg + stage_off_bf16(r, 8 * c);
+                            uint8_t *dst = sdst + stage_off_bf16(r, 8 * c);
                             reinterpret_cast<uint2 *>(dst)[0] = make_uint2(h[0], h[1]);
                             reinterpret_cast<uint2 *>(dst)[1] = make_uint2(h[2], h[3]);
                         }
                     } else if constexpr (F == kBF16) {
                         // 16-byte piece lane % LPR = tokens 8 (lane % LPR) .. + 7
-                        uint8_t *dst = stg + stage_off_bf16(r, 8 * (lane % LPR));
+                        uint8_t *dst = sdst + stage_off_bf16(r, 8 * (lane % LPR));
                         reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
                         reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[ci].z, kraw[ci].w);
                     } else {
-                        uint8_t *dst = stg + r * 40 + (((lane % LPR) ^ ((r >> 4) & 1)) << 4);
+                        uint8_t *dst = sdst + r * 40 + (((lane % LPR) ^ ((r >> 4) & 1)) << 4);
                         reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
                         reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[ci].z, kraw[ci].w);
                     }
@@ -297,12 +298,44 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             wave_lds_sync();
         }
     };
+    // bf16 blocks, tiles after the first: the tile's A_k^T goes from memory
+    // straight into this wave's staging rows (LDS DMA, 16 bytes per lane, no
+    // registers).  Instruction ci fills rows 16 ci .. 16 ci + 15; lane L writes
+    // bytes 16 L of them, i.e. row 16 ci + L / 4 at 16 (L % 4), which is where
+    // stage_off_bf16 puts the row's tokens 8 pc .. 8 pc + 7 for the pc below.
+    // All eight instructions are always issued (rows past rk repeat row rk - 1;
+    // rk = 0 reads the first bytes of q), so that the number of memory
+    // operations in flight after them is the same on every path.
+    auto dma_k = [&](int tile, uint8_t *sdst) {
+        if constexpr (F == kBF16 && !TAIL) {
+            const int tt0 = tok0 + tile * kTile;
+            const int hh = (lane >> 1) & 1, lo = lane & 1;
+            const uint8_t *base = rk > 0 ? Ak : static_cast<const uint8_t *>(p.q);
+#pragma unroll
+            for (int ci = 0; ci < 8; ++ci) {
+                const int r = 16 * ci + (lane >> 2);
+                const int pc = ((hh ^ ((r >> 1) & 1)) << 1) | lo;
+                const uint32_t off = rk > 0 ? static_cast<uint32_t>((min(r, rk - 1) * T + tt0 + 8 * pc) * 2) : 0u;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
+                                                 (__attribute__((address_space(3))) void *)(sdst + 1024 * ci), 16, 0, 0);
+            }
+        }
+    };
     // A_v^T pieces: rank 16 mr + ln, tokens 4 c .. 4 c + 3 and 16 + 4 c .. + 3
     uint2 vraw[(F == kF32 || TAIL) ? 1 : 8][2];
     auto load_v = [&](int tile) {
         if constexpr (F != kF32 && !TAIL) {
             const int tb = tok0 + tile * kTile + 4 * c4;
-            if (rv > 0) {
+            if constexpr (F == kBF16) {
+                // always 16 loads (rv = 0 reads the first bytes of q), see dma_k
+                const uint8_t *base = rv > 0 ? Av : static_cast<const uint8_t *>(p.q);
+#pragma unroll
+                for (int mr = 0; mr < 8; ++mr) {
+                    const uint32_t off = rv > 0 ? static_cast<uint32_t>((min(16 * mr + ln, rv - 1) * T + tb) * 2) : 0u;
+                    vraw[mr][0] = *reinterpret_cast<const uint2 *>(base + off);
+                    vraw[mr][1] = *reinterpret_cast<const uint2 *>(base + off + (rv > 0 ? 32 : 0));
+                }
+            } else if (rv > 0) {
 #pragma unroll
                 for (int mr = 0; mr < 8; ++mr) {
                     const int row = min(16 * mr + ln, rv - 1);
@@ -315,9 +348,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                         const float sc = *reinterpret_cast<const float *>(
                             Av + static_cast<uint32_t>(rv * (T / 2) + (row * (T / kI4Group) + (tb - 4 * c4) / kI4Group) * 4));
                         vraw[mr][0] = make_uint2(lo | (hi << 16), __float_as_uint(sc));
-                    } else if constexpr (F == kBF16) {
-                        vraw[mr][0] = *reinterpret_cast<const uint2 *>(Av + off);
-                        vraw[mr][1] = *reinterpret_cast<const uint2 *>(Av + off + 32);
                     } else {
                         vraw[mr][0] = make_uint2(*reinterpret_cast<const uint32_t *>(Av + off), 0u);
                         vraw[mr][1] = make_uint2(*reinterpret_cast<const uint32_t *>(Av + off + 16), 0u);
@@ -453,7 +483,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     }
     __syncthreads();  // tables, fragments; the staging area is free again
     // Lane (c, n) owns query head n: column n of every accumulator.
-    const float *qrow = reinterpret_cast<const float *>(lds + L.qs) + min(ln, G - 1) * kQP;
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4_t u[8];
@@ -462,16 +491,35 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     const float lscale = p.softmax_scale * kLog2e;
 
     // Pipeline: the staging buffer holds this tile's A_k^T while its keys are
-    // rebuilt; the next tile's A_k^T is loaded once the rebuild is done (so the
-    // registers are free during it) and staged at the end of the tile; A_v^T
-    // pieces are loaded a whole tile ahead.
+    // rebuilt; A_v^T pieces are loaded a whole tile ahead.  bf16: the next
+    // tile's A_k^T is DMA'd into the staging rows as soon as the rebuild has
+    // read them.  Other formats: it is loaded into registers at the start of
+    // the tile and staged at its end.
     const int my_tiles = tiles_valid > wave ? (tiles_valid - 1 - wave) / kWaves + 1 : 0;
-    if (my_tiles > 0) stage_k();
+    if (my_tiles > 0) stage_k(stg);
+    // The loop reaches LDS through two restrict pointers, the staging rows and
+    // the tables (disjoint regions), so that the compiler knows the staging DMA
+    // does not write what the table reads load.
+    auto main_loop = [&](uint8_t *__restrict__ sg, const uint8_t *__restrict__ tb) {
+    const float2 *rope = reinterpret_cast<const float2 *>(tb + L.rope);
+    const float2 *basetab = reinterpret_cast<const float2 *>(tb + L.base);
+    const uint16_t *bkf = reinterpret_cast<const uint16_t *>(tb + L.bk);
+    const float *qrow = reinterpret_cast<const float *>(tb + L.qs) + min(ln, G - 1) * kQP;
+    uint8_t *stg = sg;
     for (int it = 0; it < my_tiles; ++it) {
         const int tile = wave + kWaves * it;
         const int tt0 = tok0 + tile * kTile;  // first token of the tile (block- or tail-local)
 
-        if (it + 1 < my_tiles) load_k(tile + kWaves);  // a whole tile of latency cover
+        if constexpr (F == kBF16 && !TAIL) {
+            // this tile's DMA was issued just before the previous iteration's
+            // 16 A_v loads: wait for it
+            if (it > 0) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+                asm volatile("" ::: "memory");
+            }
+        } else if (it + 1 < my_tiles) {
+            load_k(tile + kWaves);  // a whole tile of latency cover
+        }
 
         // ---- this tile's rotated query fragments, dims 16 kk + 4 c + i and + 64
         u16x8_t qf[NS][4];
@@ -537,6 +585,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 #pragma unroll
                         for (int mt = 0; mt < 8; ++mt)
                             a[mt] = *reinterpret_cast<const u16x8_t *>(bkf + ((sa * 2048) + (mt * 4 + ks) * 64 + lane) * 8);
+                        // (the scheduler would otherwise interleave reads and products
+                        // two at a time, serialising the LDS round trips)
+                        if constexpr (NS == 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -563,6 +614,15 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                         acc[mt][2] = bf16_bits_to_f32(w.y & 0xffff);
                         acc[mt][3] = bf16_bits_to_f32(w.y >> 16);
                     }
+                }
+            }
+            if constexpr (F == kBF16 && !TAIL) {
+                if (nt == 1) {
+                    // both halves have read the staged tile: the next one may land
+                    // (the last tile reloads itself, which keeps the counts uniform)
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    asm volatile("" ::: "memory");
+                    dma_k(it + 1 < my_tiles ? tile + kWaves : tile, stg);
                 }
             }
             // keep the table reads below after the rebuild (registers)
@@ -624,13 +684,13 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float mn = fmaxf(m_run, tmax);
         const bool none = (mn == -INFINITY);
-        const float alpha = none ? 1.f : exp2f(m_run - mn);
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
         float pv[8], psum = 0.f;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pr = none ? 0.f : exp2f(x[nt][i] - mn);
+                const float pr = none ? 0.f : __builtin_amdgcn_exp2f(x[nt][i] - mn);
                 psum += pr;
                 pv[4 * nt + i] = pr * vs[nt][i];
             }
@@ -739,11 +799,20 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             if constexpr (F == kBF16) wave_lds_sync();  // staging reused by the next tile
         }
 
-        if (it + 1 < my_tiles) {
+        if constexpr (F == kBF16 && !TAIL) {
+            load_v(it + 1 < my_tiles ? tile + kWaves : tile);
+        } else if (it + 1 < my_tiles) {
             load_v(tile + kWaves);
             wave_lds_sync();  // this tile's staged keys have been read
-            stage_k();
+            stage_k(stg);
         }
+    }
+    };
+    main_loop(stg, lds);
+    if constexpr (F == kBF16 && !TAIL) {
+        // the last DMA lands in LDS that the merge reuses
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("" ::: "memory");
     }
 
     // ---- merge the waves (log-sum-exp) and apply B_v
