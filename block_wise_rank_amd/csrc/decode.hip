@@ -321,36 +321,33 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             }
         }
     };
-    // A_v^T pieces: rank 16 mr + ln, tokens 4 c .. 4 c + 3 and 16 + 4 c .. + 3
-    uint2 vraw[(F == kF32 || TAIL) ? 1 : 8][2];
+    // A_v^T pieces: rank 16 mr + ln, tokens 8 c .. 8 c + 7 of the tile (the
+    // token order of the tiles below makes them the lane's eight P slots)
+    uint4 vraw[(F == kF32 || TAIL) ? 1 : 8];
     auto load_v = [&](int tile) {
         if constexpr (F != kF32 && !TAIL) {
-            const int tb = tok0 + tile * kTile + 4 * c4;
+            const int t0 = tok0 + tile * kTile, tb = t0 + 8 * c4;
             if constexpr (F == kBF16) {
-                // always 16 loads (rv = 0 reads the first bytes of q), see dma_k
+                // always 8 loads (rv = 0 reads the first bytes of q), see dma_k
                 const uint8_t *base = rv > 0 ? Av : static_cast<const uint8_t *>(p.q);
 #pragma unroll
                 for (int mr = 0; mr < 8; ++mr) {
                     const uint32_t off = rv > 0 ? static_cast<uint32_t>((min(16 * mr + ln, rv - 1) * T + tb) * 2) : 0u;
-                    vraw[mr][0] = *reinterpret_cast<const uint2 *>(base + off);
-                    vraw[mr][1] = *reinterpret_cast<const uint2 *>(base + off + (rv > 0 ? 32 : 0));
+                    vraw[mr] = *reinterpret_cast<const uint4 *>(base + off);
                 }
             } else if (rv > 0) {
 #pragma unroll
                 for (int mr = 0; mr < 8; ++mr) {
                     const int row = min(16 * mr + ln, rv - 1);
-                    const uint32_t off = static_cast<uint32_t>((row * T + tb) * ES);
                     if constexpr (F == kI4) {
-                        // codes of tokens tb .. tb + 3 and tb + 16 .. + 19, and the tile's scale
-                        const uint32_t o4 = static_cast<uint32_t>(row * (T / 2) + tb / 2);
-                        const uint32_t lo = *reinterpret_cast<const uint16_t *>(Av + o4);
-                        const uint32_t hi = *reinterpret_cast<const uint16_t *>(Av + o4 + 8);
+                        // codes of tokens tb .. tb + 7, and the scale of the tile's run
+                        const uint32_t w = *reinterpret_cast<const uint32_t *>(Av + static_cast<uint32_t>(row * (T / 2) + tb / 2));
                         const float sc = *reinterpret_cast<const float *>(
-                            Av + static_cast<uint32_t>(rv * (T / 2) + (row * (T / kI4Group) + (tb - 4 * c4) / kI4Group) * 4));
-                        vraw[mr][0] = make_uint2(lo | (hi << 16), __float_as_uint(sc));
+                            Av + static_cast<uint32_t>(rv * (T / 2) + (row * (T / kI4Group) + t0 / kI4Group) * 4));
+                        vraw[mr] = make_uint4(w, __float_as_uint(sc), 0u, 0u);
                     } else {
-                        vraw[mr][0] = make_uint2(*reinterpret_cast<const uint32_t *>(Av + off), 0u);
-                        vraw[mr][1] = make_uint2(*reinterpret_cast<const uint32_t *>(Av + off + 16), 0u);
+                        const uint2 w = *reinterpret_cast<const uint2 *>(Av + static_cast<uint32_t>(row * T + tb));
+                        vraw[mr] = make_uint4(w.x, w.y, 0u, 0u);
                     }
                 }
             }
@@ -512,9 +509,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 
         if constexpr (F == kBF16 && !TAIL) {
             // this tile's DMA was issued just before the previous iteration's
-            // 16 A_v loads: wait for it
+            // 8 A_v loads: wait for it
             if (it > 0) {
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
                 asm volatile("" ::: "memory");
             }
         } else if (it + 1 < my_tiles) {
@@ -543,12 +540,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             for (int st = 0; st < NS; ++st) qf[st][kk] = f[st];
         }
 
-        // ---- per 16-token half nt: K^T (acc[mt][i] = k_hat[token 16 nt + ln][dim 16 mt + 4 c + i]),
-        // RoPE by the in-tile offset, logits^T S[nt][i] = logit(token 16 nt + 4 c + i, head ln)
+        // ---- per half nt: K^T (acc[mt][i] = k_hat[token tk(nt, ln)][dim 16 mt + 4 c + i]),
+        // RoPE by the in-tile offset, logits^T S[nt][i] = logit(token tk(nt, 4 c + i), head ln),
+        // where tk(nt, 4 c + i) = 8 c + 4 nt + i: lane (c, n)'s eight P values are then
+        // tokens 8 c .. 8 c + 7 (slot 4 nt + i), which one 16-byte A_v load holds
         f32x4_t S[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const int t = 16 * nt + ln;
+            const int t = 8 * (ln >> 2) + 4 * nt + (ln & 3);
             asm volatile("" ::: "memory");
             f32x4_t acc[8];
             if constexpr (!TAIL) {
@@ -559,9 +558,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                     u16x8_t bfr[NS];
                     if constexpr (F == kBF16 || F == kI4) {
                         // ranks 32 ks + 8 c .. + 7 of token t by two transposing reads: lane
-                        // (c, j) addresses rank row 32 ks + 8 c + j / 4 (+ 4), tokens 4 (j % 4) ..
+                        // (c, j) addresses rank row 32 ks + 8 c + j / 4 (+ 4), tokens
+                        // 8 (j % 4) + 4 nt .. + 3, and lane (c, j) receives token tk(nt, j)
                         const int row = 32 * ks + 8 * c4 + (ln >> 2);
-                        const uint8_t *p0 = stg + stage_off_bf16(row, 16 * nt + 4 * (ln & 3));
+                        const uint8_t *p0 = stg + stage_off_bf16(row, 8 * (ln & 3) + 4 * nt);
                         bfr[0] = cat8(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * 64));
                     } else if constexpr (F == kI8) {
                         float v[8];
@@ -663,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         if constexpr (F == kI8 && !TAIL) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const int64_t ti = static_cast<int64_t>(fid) * T + tt0 + 16 * nt + 4 * c4;
+                const int64_t ti = static_cast<int64_t>(fid) * T + tt0 + 8 * c4 + 4 * nt;
                 const float4 ka = *reinterpret_cast<const float4 *>(p.k_ascale + ti);
                 const float4 va = *reinterpret_cast<const float4 *>(p.v_ascale + ti);
                 sc[nt][0] *= ka.x; sc[nt][1] *= ka.y; sc[nt][2] *= ka.z; sc[nt][3] *= ka.w;
@@ -676,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = !TAIL || tile * kTile + 16 * nt + 4 * c4 + i < valid;
+                const bool ok = !TAIL || tile * kTile + 8 * c4 + 4 * nt + i < valid;
                 x[nt][i] = ok ? S[nt][i] * sc[nt][i] : -INFINITY;
                 tmax = fmaxf(tmax, x[nt][i]);
             }
@@ -708,12 +708,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                     if (rescale) u[mr] *= alpha;
                     u16x8_t af;
                     if constexpr (F == kBF16) {
-                        af = __builtin_bit_cast(u16x8_t, make_uint4(vraw[mr][0].x, vraw[mr][0].y, vraw[mr][1].x, vraw[mr][1].y));
+                        af = __builtin_bit_cast(u16x8_t, vraw[mr]);
                     } else if constexpr (F == kI4) {
-                        const float sc = __uint_as_float(vraw[mr][0].y);
+                        const float sc = __uint_as_float(vraw[mr].y);
                         float v[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] = nib(vraw[mr][0].x, e) * sc;
+                        for (int e = 0; e < 8; ++e) v[e] = nib(vraw[mr].x, e) * sc;
                         u16x8_t f[1];
                         frag_terms<1>(v, f);
                         af = f[0];
@@ -721,8 +721,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                         float v[8];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            v[e] = static_cast<float>(static_cast<int8_t>((vraw[mr][0].x >> (8 * e)) & 0xff));
-                            v[4 + e] = static_cast<float>(static_cast<int8_t>((vraw[mr][1].x >> (8 * e)) & 0xff));
+                            v[e] = static_cast<float>(static_cast<int8_t>((vraw[mr].x >> (8 * e)) & 0xff));
+                            v[4 + e] = static_cast<float>(static_cast<int8_t>((vraw[mr].y >> (8 * e)) & 0xff));
                         }
                         u16x8_t f[1];
                         frag_terms<1>(v, f);
@@ -740,8 +740,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                     float v[8];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        v[e] = load_elem<F>(Av, static_cast<int64_t>(row) * T + tt0 + 4 * c4 + e);
-                        v[4 + e] = load_elem<F>(Av, static_cast<int64_t>(row) * T + tt0 + 16 + 4 * c4 + e);
+                        v[e] = load_elem<F>(Av, static_cast<int64_t>(row) * T + tt0 + 8 * c4 + e);
+                        v[4 + e] = load_elem<F>(Av, static_cast<int64_t>(row) * T + tt0 + 8 * c4 + 4 + e);
                     }
                     u16x8_t af[NS];
                     frag_terms<NS>(v, af);
@@ -777,14 +777,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                 if constexpr (F == kBF16) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const int tt = (e < 4) ? 4 * c4 + e : 16 + 4 * c4 + e - 4;
+                        const int tt = 8 * c4 + e;
                         af[0][e] = *reinterpret_cast<const uint16_t *>(stg + tt * kTVP + dim * 2);
                     }
                 } else {
                     float v[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const int tt = (e < 4) ? 4 * c4 + e : 16 + 4 * c4 + e - 4;
+                        const int tt = 8 * c4 + e;
                         const int t = min(tt0 + tt, tlast);
                         v[e] = reinterpret_cast<const float *>(p.tail_v)[(rowb + t) * kD + dim];
                     }
