@@ -321,6 +321,22 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             }
         }
     };
+    // bf16 blocks: B_v rows (256 bytes each) DMA'd into the staging rows of
+    // waves 4..7 once their last rebuild is done (wave w: rows 32 (w - 4) ..
+    // + 31, four rows per instruction), for the o = u B_v product of the merge.
+    // That half of the staging lies past the merge's own LDS areas.
+    auto dma_bv = [&](uint8_t *sdst) {
+        if constexpr (F == kBF16 && !TAIL) {
+            const uint8_t *base = rv > 0 ? Bv : static_cast<const uint8_t *>(p.q);
+#pragma unroll
+            for (int ci = 0; ci < 8; ++ci) {
+                const int row = 32 * (wave - 4) + 4 * ci + (lane >> 4);
+                const uint32_t off = rv > 0 ? static_cast<uint32_t>(min(row, rv - 1) * (kD * 2) + 16 * (lane & 15)) : 0u;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
+                                                 (__attribute__((address_space(3))) void *)(sdst + 1024 * ci), 16, 0, 0);
+            }
+        }
+    };
     // A_v^T pieces: rank 16 mr + ln, tokens 8 c .. 8 c + 7 of the tile (the
     // token order of the tiles below makes them the lane's eight P slots)
     uint4 vraw[(F == kF32 || TAIL) ? 1 : 8];
@@ -619,10 +635,11 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             if constexpr (F == kBF16 && !TAIL) {
                 if (nt == 1) {
                     // both halves have read the staged tile: the next one may land
-                    // (the last tile reloads itself, which keeps the counts uniform)
                     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
                     asm volatile("" ::: "memory");
-                    dma_k(it + 1 < my_tiles ? tile + kWaves : tile, stg);
+                    if (it + 1 < my_tiles) dma_k(tile + kWaves, stg);
+                    else if (wave >= 4) dma_bv(stg);
+                    else dma_k(tile, stg);  // reloads itself (keeps the counts uniform)
                 }
             }
             // keep the table reads below after the rebuild (registers)
@@ -810,7 +827,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     };
     main_loop(stg, lds);
     if constexpr (F == kBF16 && !TAIL) {
-        // the last DMA lands in LDS that the merge reuses
+        if (my_tiles == 0 && wave >= 4) dma_bv(stg);
+        // the DMAs land before the barrier that starts the merge
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         asm volatile("" ::: "memory");
     }
@@ -835,7 +853,19 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     // B_v fragments for o = u B_v (lane: dim 16 w + n, ranks 32 ks + 8 c + e), read
     // straight from memory now so that their latency overlaps the merge
     u16x8_t bvf[NS][4];
-    if constexpr (!TAIL) {
+    if constexpr (F == kBF16 && !TAIL) {
+        // lane (c, j): ranks 32 ks + 8 c .. + 7 of dim 16 w + j by two transposing
+        // reads of the staged rows (lane (c, j) addresses row 32 ks + 8 c + j / 4
+        // (+ 4), dims 16 w + 4 (j % 4) .. + 3); rows past rv repeat row rv - 1,
+        // and u is zero there
+        const uint8_t *bvl = lds + L.stage + 4 * 128 * stage_pitch(F);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            if (ks < KSV) {
+                const uint8_t *p0 = bvl + (32 * ks + 8 * c4 + (ln >> 2)) * (kD * 2) + (16 * wave + 4 * (ln & 3)) * 2;
+                bvf[0][ks] = cat8(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * kD * 2));
+            }
+    } else if constexpr (!TAIL) {
         if (rv > 0) {
             const int dim = 16 * wave + ln;
 #pragma unroll
@@ -1005,7 +1035,10 @@ hipError_t launch_partial(const DecodeParams &p, dim3 grid, hipStream_t st) {
 
 bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int split) {
     const int ns = f_type == kF32 ? 2 : 1;
-    if (lds_layout(f_type, ns, split / kTile, false, G).total > kMaxLds) return false;
+    const LdsLayout L = lds_layout(f_type, ns, split / kTile, false, G);
+    if (L.total > kMaxLds) return false;
+    // bf16: B_v is staged in the upper half of the staging rows during the merge
+    if (f_type == kBF16 && L.merge_end > L.stage + kWaves / 2 * 128 * stage_pitch(kBF16)) return false;
     if (has_tail) {
         const int tns = tail_type == kF32 ? 2 : 1;
         if (lds_layout(tail_type, tns, split / kTile, true, G).total > kMaxLds) return false;
