@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 
     // ---- which tokens this workgroup covers
     int split_index, tok0 = 0, valid = 0, fid = -1, rk = 0, rv = 0;
-    int64_t pos0 = 0;
+    int64_t pos0 = 0, ka_off = 0, va_off = 0, kb_off = 0, vb_off = 0;
     if constexpr (!TAIL) {
         const int e = sp / p.block_splits, c = sp - e * p.block_splits;
         split_index = sp;
@@ -191,10 +191,18 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             if (ok) b = p.sel_blk[beg + e];
             ok = ok && b >= 0 && b < p.blocks_per_seq;
         }
+        // every metadata load is issued at once (index 0 stands in when the
+        // selection entry is invalid; nothing is read through it then)
+        const int fs = ok ? (s * Hkv + h) * p.blocks_per_seq + b : 0;
+        const int rk_s = p.k_rank[fs], rv_s = p.v_rank[fs];
+        ka_off = p.k_aoff[fs];
+        va_off = p.v_aoff[fs];
+        kb_off = p.k_boff[fs];
+        vb_off = p.v_boff[fs];
         if (ok) {
-            fid = (s * Hkv + h) * p.blocks_per_seq + b;
-            rk = p.k_rank[fid];
-            rv = p.v_rank[fid];
+            fid = fs;
+            rk = rk_s;
+            rv = rv_s;
             tok0 = c * p.split_len;
             pos0 = static_cast<int64_t>(b) * T + tok0;
             valid = p.split_len;
@@ -223,10 +231,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 
     const uint8_t *Ak = nullptr, *Av = nullptr, *Bv = nullptr, *Bk = nullptr;
     if constexpr (!TAIL) {
-        Ak = p.k_arena + p.k_aoff[fid];
-        Av = p.v_arena + p.v_aoff[fid];
-        Bv = p.v_arena + p.v_boff[fid];
-        Bk = p.k_arena + p.k_boff[fid];
+        Ak = p.k_arena + ka_off;
+        Av = p.v_arena + va_off;
+        Bv = p.v_arena + vb_off;
+        Bk = p.k_arena + kb_off;
     }
     // ---- per-wave A_k staging (bf16 / int8 blocks) and tail V staging
     uint8_t *stg = lds + L.stage;
@@ -391,61 +399,62 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 #pragma unroll
         for (int i = 0; i < NBK; ++i) bkraw[i] = src[min(tid + kThreads * i, last)];
     }
+    // The remaining loads are issued unconditionally (indices clamped) so that
+    // none is sunk into the branch that uses it, and used in issue order.
     float bsc_v = 0.f;
-    if constexpr (F == kI8 && !TAIL)
-        if (tid < rk) bsc_v = p.k_bscale[static_cast<int64_t>(fid) * kD + tid];
+    if constexpr (F == kI8 && !TAIL) bsc_v = p.k_bscale[static_cast<int64_t>(fid) * kD + (tid & (kD - 1))];
     const float4 rope_v = reinterpret_cast<const float4 *>(p.rope_tab)[tid];      // entries 2 tid, 2 tid + 1
     const float4 rope_w = reinterpret_cast<const float4 *>(p.rope_tab)[tid + kThreads];
     constexpr int NST = kMaxTiles * 64 / 2 / kThreads;                               // float4 per thread
     float4 step_v[NST];
 #pragma unroll
     for (int i = 0; i < NST; ++i) step_v[i] = reinterpret_cast<const float4 *>(p.step_tab)[tid + kThreads * i];
-    float qv[4];
-    {
-        // G query heads: 4 consecutive values per thread (rows >= G are zero)
-        const int64_t q0 = (static_cast<int64_t>(s) * p.n_q_heads + h * G) * kD;
-        const int e0 = 4 * tid;  // < 16 * 128
-        if (e0 < G * kD) {
-            if (p.q_type == kF32) {
-                const float4 w = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.q) + q0 + e0);
-                qv[0] = w.x; qv[1] = w.y; qv[2] = w.z; qv[3] = w.w;
-            } else {
-                const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.q) + q0 + e0);
-                qv[0] = bf16_bits_to_f32(w.x & 0xffff); qv[1] = bf16_bits_to_f32(w.x >> 16);
-                qv[2] = bf16_bits_to_f32(w.y & 0xffff); qv[3] = bf16_bits_to_f32(w.y >> 16);
-            }
-        } else {
-            qv[0] = qv[1] = qv[2] = qv[3] = 0.f;
-        }
-    }
-    if (tid < 64) {
-        // rotation of the queries relative to the split's first token, (pq - p0) theta_j
-        double a = static_cast<double>(p.q_pos[s] - pos0) * p.theta[tid];
-        a -= kTwoPi * rint(a / kTwoPi);  // exact enough in fp64 for positions < 2^40
-        float sn, cs;
-        sincosf(static_cast<float>(a), &sn, &cs);
-        ang[tid] = make_float2(cs, sn);
+    // G query heads: 4 consecutive values per thread (rows >= G are zero)
+    const int64_t q0 = (static_cast<int64_t>(s) * p.n_q_heads + h * G) * kD;
+    const int qe0 = 4 * tid;  // < 16 * 128
+    const int64_t qi = q0 + min(qe0, G * kD - 4);
+    const bool q32 = p.q_type == kF32;
+    const uint8_t *qb = static_cast<const uint8_t *>(p.q) + qi * (q32 ? 4 : 2);
+    const uint2 qlo = *reinterpret_cast<const uint2 *>(qb), qhi = *reinterpret_cast<const uint2 *>(qb + (q32 ? 8 : 0));
+    const uint4 qraw = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
+    const double theta_v = p.theta[tid & 63];
+    const int64_t qpos = p.q_pos[s];
+
+    if constexpr (F != kF32 && !TAIL) {
+        // B_k rows -> the A_k staging area (free until the main loop); chunks past
+        // the rows repeat the last one and are never read
+        uint8_t *tmp = lds + L.stage;
+#pragma unroll
+        for (int i = 0; i < NBK; ++i) reinterpret_cast<uint4 *>(tmp)[tid + kThreads * i] = bkraw[i];
+        if constexpr (F == kI8)
+            if (tid < rk) reinterpret_cast<float *>(tmp + 128 * kD)[tid] = bsc_v;  // after the rows
     }
     {
-        float *qw = reinterpret_cast<float *>(lds + L.qs);
-        const int e0 = 4 * tid;
-        if (e0 < G * kD)
-            *reinterpret_cast<float4 *>(qw + (e0 >> 7) * kQP + (e0 & 127)) = make_float4(qv[0], qv[1], qv[2], qv[3]);
         float2 *rw = reinterpret_cast<float2 *>(lds + L.rope);
         const int r0 = 2 * tid, r1 = 2 * (tid + kThreads);
         *reinterpret_cast<float4 *>(rw + (r0 >> 6) * kRP + (r0 & 63)) = rope_v;
         *reinterpret_cast<float4 *>(rw + (r1 >> 6) * kRP + (r1 & 63)) = rope_w;
     }
-    if constexpr (F != kF32 && !TAIL) {
-        // B_k rows -> the A_k staging area (free until the main loop)
-        uint8_t *tmp = lds + L.stage;
-#pragma unroll
-        for (int i = 0; i < NBK; ++i) {
-            const bool ok = tid + kThreads * i < n16;
-            if (ok) reinterpret_cast<uint4 *>(tmp)[tid + kThreads * i] = bkraw[i];
+    {
+        float qv[4];
+        if (q32) {
+            qv[0] = __uint_as_float(qraw.x); qv[1] = __uint_as_float(qraw.y);
+            qv[2] = __uint_as_float(qraw.z); qv[3] = __uint_as_float(qraw.w);
+        } else {
+            qv[0] = bf16_bits_to_f32(qraw.x & 0xffff); qv[1] = bf16_bits_to_f32(qraw.x >> 16);
+            qv[2] = bf16_bits_to_f32(qraw.y & 0xffff); qv[3] = bf16_bits_to_f32(qraw.y >> 16);
         }
-        if constexpr (F == kI8)
-            if (tid < rk) reinterpret_cast<float *>(tmp + 128 * kD)[tid] = bsc_v;  // after the rows
+        float *qw = reinterpret_cast<float *>(lds + L.qs);
+        if (qe0 < G * kD)
+            *reinterpret_cast<float4 *>(qw + (qe0 >> 7) * kQP + (qe0 & 127)) = make_float4(qv[0], qv[1], qv[2], qv[3]);
+    }
+    if (tid < 64) {
+        // rotation of the queries relative to the split's first token, (pq - p0) theta_j
+        double a = static_cast<double>(qpos - pos0) * theta_v;
+        a -= kTwoPi * rint(a / kTwoPi);  // exact enough in fp64 for positions < 2^40
+        float sn, cs;
+        sincosf(static_cast<float>(a), &sn, &cs);
+        ang[tid] = make_float2(cs, sn);
     }
     __syncthreads();
     // per-tile query rotation (pq - p0 - 32 tile) theta_j = angle difference
@@ -523,6 +532,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         const int tile = wave + kWaves * it;
         const int tt0 = tok0 + tile * kTile;  // first token of the tile (block- or tail-local)
 
+        // The two waves of a SIMD (w, w + 4) take turns at the higher issue
+        // priority, tile by tile, so that they finish together.
+        if ((it + (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         if constexpr (F == kBF16 && !TAIL) {
             // this tile's DMA was issued just before the previous iteration's
             // 8 A_v loads: wait for it
@@ -826,6 +839,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     }
     };
     main_loop(stg, lds);
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (F == kBF16 && !TAIL) {
         if (my_tiles == 0 && wave >= 4) dma_bv(stg);
         // the DMAs land before the barrier that starts the merge
