@@ -34,40 +34,67 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     __shared__ float sig[kD];
     __shared__ int perm[kD];
     __shared__ float sgn[kD];
+    __shared__ float ninv[kD];     // 1 / ||v_i||
 
     const int blk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float *vblk = vt + static_cast<int64_t>(blk) * kD * kD;
-    for (int e = tid; e < kD * kD / 4; e += 256)
-        reinterpret_cast<float4 *>(Vs)[e] = reinterpret_cast<const float4 *>(vblk)[e];
-    __syncthreads();
-    // Thousands of fp32 rotations leave each eigenvector's norm off by ~1e-5;
-    // rescale to unit norm so ||X v|| measures sigma and B = V_r^T is orthonormal.
-    for (int i = wave; i < kD; i += 4) {
-        const float a = Vs[i * kD + lane], b = Vs[i * kD + 64 + lane];
-        const float nrm = sqrtf(wave_sum(a * a + b * b));
-        const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
-        Vs[i * kD + lane] = a * inv;
-        Vs[i * kD + 64 + lane] = b * inv;
-    }
+    constexpr int NV = kD * kD / 4 / 256;  // float4 of V per thread
+    float4 vr[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) vr[k] = reinterpret_cast<const float4 *>(vblk)[tid + 256 * k];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) reinterpret_cast<float4 *>(Vs)[tid + 256 * k] = vr[k];
     __syncthreads();
 
     // A fragments: row i = 32 * wave + lane % 32, k slots j = 16 ks + 8 (lane / 32) + e.
+    // Thousands of fp32 rotations leave each eigenvector's norm off by ~1e-5: the
+    // fragments are built from v_i / ||v_i|| (so that ||X v|| measures sigma and
+    // B = V_r^T is orthonormal), and the same pass finds the row's sign: its
+    // largest-magnitude entry (first one on ties) is made positive.
     constexpr int NT = NX == 1 ? 2 : 3;  // terms of V
     u16x8_t fa[NT][8];
     {
-        const int i = 32 * wave + (lane & 31);
+        const int i = 32 * wave + (lane & 31), h = lane >> 5;
+        float v[8][8];
+        float ssq = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const float4 p0 = *reinterpret_cast<const float4 *>(Vs + i * kD + 16 * ks + 8 * h);
+            const float4 p1 = *reinterpret_cast<const float4 *>(Vs + i * kD + 16 * ks + 8 * h + 4);
+            v[ks][0] = p0.x; v[ks][1] = p0.y; v[ks][2] = p0.z; v[ks][3] = p0.w;
+            v[ks][4] = p1.x; v[ks][5] = p1.y; v[ks][6] = p1.z; v[ks][7] = p1.w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ssq = fmaf(v[ks][e], v[ks][e], ssq);
+        }
+        ssq += __shfl_xor(ssq, 32, 64);
+        const float nrm = sqrtf(ssq);
+        const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
+        float best = -1.f, bval = 0.f;
+        int bidx = 0;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float v = Vs[i * kD + 16 * ks + 8 * (lane >> 5) + e];
-                uint16_t h, m, l;
-                split3_bf16(v, h, m, l);
-                fa[0][ks][e] = h;
-                fa[1][ks][e] = m;
-                if constexpr (NT == 3) fa[NT - 1][ks][e] = l;
+                const float a = v[ks][e] * inv;
+                if (fabsf(a) > best) {  // indices increase along the lane's slots
+                    best = fabsf(a);
+                    bidx = 16 * ks + 8 * h + e;
+                    bval = a;
+                }
+                uint16_t hi, mi, lo;
+                split3_bf16(a, hi, mi, lo);
+                fa[0][ks][e] = hi;
+                fa[1][ks][e] = mi;
+                if constexpr (NT == 3) fa[NT - 1][ks][e] = lo;
             }
+        const float ob = __shfl_xor(best, 32, 64), ov = __shfl_xor(bval, 32, 64);
+        const int oi = __shfl_xor(bidx, 32, 64);
+        if (ob > best || (ob == best && oi < bidx)) bval = ov;
+        if (h == 0) {
+            ninv[i] = inv;
+            sgn[i] = (bval < 0.f) ? -1.f : 1.f;
+        }
     }
 
     const int64_t base = row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride;
@@ -153,36 +180,14 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
         perm[pos] = tid;
         ss[pos] = si;  // sorted values (ss is free again)
     }
-    // Sign of eigenvector i: its largest-magnitude entry (first one on ties) positive.
-    for (int i = wave; i < kD; i += 4) {
-        const float a = Vs[i * kD + lane], b = Vs[i * kD + 64 + lane];
-        float best = fabsf(a);
-        int bidx = lane;
-        float bval = a;
-        if (fabsf(b) > best) {
-            best = fabsf(b);
-            bidx = 64 + lane;
-            bval = b;
-        }
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float ob = __shfl_xor(best, o, 64);
-            const int oi = __shfl_xor(bidx, o, 64);
-            const float ov = __shfl_xor(bval, o, 64);
-            if (ob > best || (ob == best && oi < bidx)) {
-                best = ob;
-                bidx = oi;
-                bval = ov;
-            }
-        }
-        if (lane == 0) sgn[i] = (bval < 0.f) ? -1.f : 1.f;
-    }
     __syncthreads();
     if (tid < kD) sigma[static_cast<int64_t>(blk) * kD + tid] = ss[tid];
-    for (int e = tid; e < kD * kD; e += 256) {
-        const int pos = e >> 7, j = e & 127;
+    for (int e4 = tid; e4 < kD * kD / 4; e4 += 256) {
+        const int pos = e4 >> 5, j = 4 * (e4 & 31);
         const int src = perm[pos];
-        vblk[e] = sgn[src] * Vs[src * kD + j];
+        const float g = sgn[src], iv = ninv[src];
+        const float4 a = *reinterpret_cast<const float4 *>(Vs + src * kD + j);
+        reinterpret_cast<float4 *>(vblk)[e4] = make_float4(g * (a.x * iv), g * (a.y * iv), g * (a.z * iv), g * (a.w * iv));
     }
 }
 
