@@ -102,40 +102,87 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc2[r] = 0.f;
 
-    // bf16 X: the next 32-token tile's fragments are loaded while this tile's
-    // products run (one tile of latency cover).
-    u16x8_t xb[NX == 1 ? 8 : 1];
-    auto load_x = [&](int t0) {
-        if constexpr (NX == 1) {
-            const uint16_t *xr = static_cast<const uint16_t *>(x) + base +
-                                 static_cast<int64_t>(t0 + (lane & 31)) * row_stride + 8 * (lane >> 5);
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) xb[ks] = *reinterpret_cast<const u16x8_t *>(xr + 16 * ks);
+    if constexpr (NX == 1) {
+        // bf16 X streams through a ring of four 32-token tiles in LDS (the V
+        // area, free once the fragments are built).  Each wave loads a quarter of
+        // a tile (rows 8 w .. 8 w + 7, two 16-byte loads per lane) four tiles
+        // ahead, so that the workgroup keeps four distinct tiles in flight
+        // instead of every wave loading every tile.  Rows are padded to 272
+        // bytes: the 16-byte fragment reads of 32 consecutive rows fall on
+        // distinct banks.
+        constexpr int kRowB = kD * 2 + 16;
+        constexpr int kSlot = 32 * kRowB;
+        static_assert(4 * kSlot <= kD * kD * 4, "the ring fits in the V area");
+        uint8_t *ring = reinterpret_cast<uint8_t *>(Vs);
+        const int n_tiles = T / 32;
+        const uint8_t *xg = static_cast<const uint8_t *>(x) + base * 2;
+        const int lr = 8 * wave + (lane >> 4);  // rows lr and lr + 4 of a tile
+        const uint8_t *xl = xg + static_cast<int64_t>(lr) * row_stride * 2 + 16 * (lane & 15);
+        const int64_t x4 = static_cast<int64_t>(4) * row_stride * 2, x32 = static_cast<int64_t>(32) * row_stride * 2;
+        auto load_q = [&](uint4 &ra, uint4 &rb, int tile) __attribute__((always_inline)) {
+            const int tt = tile < n_tiles ? tile : n_tiles - 1;  // past the end: the last tile again
+            const uint8_t *p0 = xl + tt * x32;
+            ra = *reinterpret_cast<const uint4 *>(p0);
+            rb = *reinterpret_cast<const uint4 *>(p0 + x4);
+        };
+        auto store_q = [&](const uint4 &ra, const uint4 &rb, int tile) __attribute__((always_inline)) {
+            uint8_t *p0 = ring + (tile & 3) * kSlot + lr * kRowB + 16 * (lane & 15);
+            *reinterpret_cast<uint4 *>(p0) = ra;
+            *reinterpret_cast<uint4 *>(p0 + 4 * kRowB) = rb;
+        };
+        // tile k waits in (qka, qkb), k = tile % 4, until it is stored, one tile before its use
+        uint4 q0a, q0b, q1a, q1b, q2a, q2b, q3a, q3b;
+        __syncthreads();  // every wave has read V: its LDS is free
+        {
+            uint4 ra, rb;
+            load_q(ra, rb, 0);
+            load_q(q1a, q1b, 1);
+            load_q(q2a, q2b, 2);
+            load_q(q3a, q3b, 3);
+            load_q(q0a, q0b, 4);
+            store_q(ra, rb, 0);
         }
-    };
-    load_x(0);
-    for (int t0 = 0; t0 < T; t0 += 32) {
-        const int t = t0 + (lane & 31);
-        f32x16_t acc = zero16(), acc1 = zero16();
-        u16x8_t cur[NX == 1 ? 8 : 1];
-        if constexpr (NX == 1) {
+        __syncthreads();
+        auto step = [&](uint4 &na, uint4 &nb, int t) __attribute__((always_inline)) {
+            // B fragments of tile t: token lane % 32, features 16 ks + 8 (lane / 32) ..
+            const uint8_t *src = ring + (t & 3) * kSlot + (lane & 31) * kRowB + 16 * (lane >> 5);
+            u16x8_t cur[8];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) cur[ks] = xb[ks];
-            load_x(t0 + 32 < T ? t0 + 32 : t0);  // the last tile reloads itself (unused)
-            // keep the scheduler from sinking those loads back between the products
-            __builtin_amdgcn_sched_barrier(0);
-        }
+            for (int ks = 0; ks < 8; ++ks) cur[ks] = *reinterpret_cast<const u16x8_t *>(src + 32 * ks);
+            f32x16_t acc = zero16(), acc1 = zero16();
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int j0 = 16 * ks + 8 * (lane >> 5);
-            if constexpr (NX == 1) {
+            for (int ks = 0; ks < 8; ++ks) {
                 // two independent accumulation chains (even / odd k-steps)
                 f32x16_t &a = (ks & 1) ? acc1 : acc;
                 a = mfma32x32x16(fa[0][ks], cur[ks], a);
                 a = mfma32x32x16(fa[1][ks], cur[ks], a);
-            } else {
-                const float *xr = static_cast<const float *>(x) + base +
-                                  static_cast<int64_t>(t) * row_stride + j0;
+            }
+            store_q(na, nb, t + 1);  // its slot was last read in tile t - 3
+            load_q(na, nb, t + 5);
+            acc += acc1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc2[r] += acc[r] * acc[r];
+            __syncthreads();
+        };
+        int t = 0;
+        for (; t + 4 <= n_tiles; t += 4) {
+            step(q1a, q1b, t);
+            step(q2a, q2b, t + 1);
+            step(q3a, q3b, t + 2);
+            step(q0a, q0b, t + 3);
+        }
+        if (t < n_tiles) {  // block_len % 64 == 0: an even number of tiles, so two remain
+            step(q1a, q1b, t);
+            step(q2a, q2b, t + 1);
+        }
+    } else {
+        for (int t0 = 0; t0 < T; t0 += 32) {
+            const int t = t0 + (lane & 31);
+            f32x16_t acc = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int j0 = 16 * ks + 8 * (lane >> 5);
+                const float *xr = static_cast<const float *>(x) + base + static_cast<int64_t>(t) * row_stride + j0;
                 const float4 v0 = reinterpret_cast<const float4 *>(xr)[0];
                 const float4 v1 = reinterpret_cast<const float4 *>(xr)[1];
                 const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -154,10 +201,9 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
                     for (int sb = 0; sb < 3; ++sb)
                         if (sa + sb <= 2) acc = mfma32x32x16(fa[sa < NT ? sa : 0][ks], fb[sb], acc);
             }
-        }
-        if constexpr (NX == 1) acc += acc1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc2[r] += acc[r] * acc[r];
+            for (int r = 0; r < 16; ++r) acc2[r] += acc[r] * acc[r];
+        }
     }
     // acc2[r] belongs to row i = 32 wave + 8 (r / 4) + 4 (lane / 32) + r % 4, token lane % 32.
 #pragma unroll
@@ -182,13 +228,20 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     }
     __syncthreads();
     if (tid < kD) sigma[static_cast<int64_t>(blk) * kD + tid] = ss[tid];
-    for (int e4 = tid; e4 < kD * kD / 4; e4 += 256) {
-        const int pos = e4 >> 5, j = 4 * (e4 & 31);
+    // sorted, signed, unit-norm rows, read again from memory (the V area of LDS
+    // held the X ring): every thread holds its rows before any is overwritten
+    float4 w[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int e4 = tid + 256 * k, pos = e4 >> 5, j = 4 * (e4 & 31);
         const int src = perm[pos];
         const float g = sgn[src], iv = ninv[src];
-        const float4 a = *reinterpret_cast<const float4 *>(Vs + src * kD + j);
-        reinterpret_cast<float4 *>(vblk)[e4] = make_float4(g * (a.x * iv), g * (a.y * iv), g * (a.z * iv), g * (a.w * iv));
+        const float4 a = *reinterpret_cast<const float4 *>(vblk + src * kD + j);
+        w[k] = make_float4(g * (a.x * iv), g * (a.y * iv), g * (a.z * iv), g * (a.w * iv));
     }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NV; ++k) reinterpret_cast<float4 *>(vblk)[tid + 256 * k] = w[k];
 }
 
 }  // namespace
