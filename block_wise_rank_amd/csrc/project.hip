@@ -283,16 +283,82 @@ constexpr int kPartBF = 1024;   // tokens per workgroup (bf16 path)
 constexpr int kStageT = 128;    // tokens collected per flush
 constexpr int kStageP = 264;    // LDS pitch (bytes) of a staged rank row (256 B + 8)
 
+// Cooperative stream of a block part's bf16 rows through LDS: four 32-token
+// slots of 272-byte rows (the 16-byte reads of 32 consecutive rows fall on
+// distinct banks).  Wave w loads rows 8 w .. 8 w + 7 of a tile (two 16-byte
+// loads per lane) four tiles ahead of its use, so that the workgroup keeps four
+// distinct tiles in flight instead of every wave loading every tile.
+// compute(t, cur) receives tile t's B fragments (token lane % 32, features
+// 16 ks + 8 (lane / 32) + e).  Every wave of the workgroup must take part;
+// n_tiles is even.
+constexpr int kXRowB = kD * 2 + 16;
+constexpr int kXSlot = 32 * kXRowB;
+
+template <typename F>
+__device__ __forceinline__ void stream_x_ring(uint8_t *ring, const uint16_t *xrow0, int64_t row_stride,
+                                              int n_tiles, int wave, int lane, F &&compute) {
+    const int lr = 8 * wave + (lane >> 4);  // rows lr and lr + 4 of a tile
+    const uint8_t *xl = reinterpret_cast<const uint8_t *>(xrow0) + static_cast<int64_t>(lr) * row_stride * 2 +
+                        16 * (lane & 15);
+    const int64_t x4 = 8 * row_stride, x32 = 64 * row_stride;  // bytes of 4 and of 32 rows
+    auto load_q = [&](uint4 &ra, uint4 &rb, int tile) __attribute__((always_inline)) {
+        const int tt = tile < n_tiles ? tile : n_tiles - 1;  // past the end: the last tile again
+        const uint8_t *p0 = xl + tt * x32;
+        ra = *reinterpret_cast<const uint4 *>(p0);
+        rb = *reinterpret_cast<const uint4 *>(p0 + x4);
+    };
+    auto store_q = [&](const uint4 &ra, const uint4 &rb, int tile) __attribute__((always_inline)) {
+        uint8_t *p0 = ring + (tile & 3) * kXSlot + lr * kXRowB + 16 * (lane & 15);
+        *reinterpret_cast<uint4 *>(p0) = ra;
+        *reinterpret_cast<uint4 *>(p0 + 4 * kXRowB) = rb;
+    };
+    auto step = [&](uint4 &na, uint4 &nb, int t) __attribute__((always_inline)) {
+        const uint8_t *src = ring + (t & 3) * kXSlot + (lane & 31) * kXRowB + 16 * (lane >> 5);
+        u16x8_t cur[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) cur[ks] = *reinterpret_cast<const u16x8_t *>(src + 32 * ks);
+        compute(t, cur);
+        store_q(na, nb, t + 1);  // its slot was last read in tile t - 3
+        load_q(na, nb, t + 5);
+        __syncthreads();
+    };
+    // tile k waits in (qka, qkb), k = tile % 4, until it is stored, one tile before its use
+    uint4 q0a, q0b, q1a, q1b, q2a, q2b, q3a, q3b;
+    {
+        uint4 ra, rb;
+        load_q(ra, rb, 0);
+        load_q(q1a, q1b, 1);
+        load_q(q2a, q2b, 2);
+        load_q(q3a, q3b, 3);
+        load_q(q0a, q0b, 4);
+        store_q(ra, rb, 0);
+    }
+    __syncthreads();
+    int t = 0;
+    for (; t + 4 <= n_tiles; t += 4) {
+        step(q1a, q1b, t);
+        step(q2a, q2b, t + 1);
+        step(q3a, q3b, t + 2);
+        step(q0a, q0b, t + 3);
+    }
+    if (t < n_tiles) {  // an even number of tiles: two remain
+        step(q1a, q1b, t);
+        step(q2a, q2b, t + 1);
+    }
+}
+
 __global__ __launch_bounds__(256) void project_bf16_kernel(
     const uint16_t *__restrict__ x, const int64_t *__restrict__ row0, int64_t row_stride, int T,
     const float *__restrict__ vt, const int32_t *__restrict__ rank,
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off, uint8_t *__restrict__ arena) {
     __shared__ __align__(16) uint8_t stage[4][32 * kStageP];
+    __shared__ __align__(16) uint8_t xring[4 * kXSlot];
     const int blk = blockIdx.x, part = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = rank[blk];
-    if (32 * wave >= r) return;  // no rank rows for this wave (waves are independent)
+    if (r == 0) return;  // uniform over the workgroup
+    const bool active = 32 * wave < r;  // the wave has rank rows (all waves stream X)
     const int t_begin = part * kPartBF;
     const int t_end = min(T, t_begin + kPartBF);
     uint16_t *Ab = reinterpret_cast<uint16_t *>(arena + a_off[blk]);
@@ -317,21 +383,13 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(
             *reinterpret_cast<uint4 *>(Bb + i * kD + 16 * ks + 8 * (lane >> 5)) = make_uint4(w0, w1, w2, w3);
     }
 
-    const uint16_t *xb = x + (row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride) + 8 * (lane >> 5);
-    u16x8_t xn[8];
-    auto load_x = [&](int t0) {
-        const uint16_t *xr = xb + static_cast<int64_t>(t0 + (lane & 31)) * row_stride;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) xn[ks] = *reinterpret_cast<const u16x8_t *>(xr + 16 * ks);
-    };
+    const uint16_t *xp = x + (row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride) +
+                         static_cast<int64_t>(t_begin) * row_stride;
     uint8_t *stg = stage[wave];
-    load_x(t_begin);
-    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
-        u16x8_t xc[8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) xc[ks] = xn[ks];
-        load_x(t0 + 32 < t_end ? t0 + 32 : t0);  // the last tile reloads itself (unused)
-        __builtin_amdgcn_sched_barrier(0);
+    stream_x_ring(xring, xp, row_stride, (t_end - t_begin) / 32, wave, lane,
+                  [&](int t, const u16x8_t (&xc)[8]) __attribute__((always_inline)) {
+        if (!active) return;
+        const int t0 = t_begin + 32 * t;
         f32x16_t acc = zero16(), acc1 = zero16();
 #pragma unroll
         for (int ks = 0; ks < 8; ks += 2) {
@@ -365,7 +423,7 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-    }
+    });
 }
 
 // bf16 X -> fp32 or 4-bit factors: the B operand in three bf16 terms (the
