@@ -448,7 +448,8 @@ def main():
         avg_s = tot_ms / launches / 1e3
         achieved = per_launch / avg_s / (1e9 if unit == "GB/s" else 1e12)
         src = source_hash(*hashes[name])
-        traffic = load_traffic(name, src)
+        # the counters were taken on the workload's own factor dtype
+        traffic = load_traffic(name, src) if fdt == cfg.storage else None
         rooflines[name] = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                            "frac": round(achieved / peak, 4), "traffic": traffic,
                            "launches_per_step": launches / args.steps,
