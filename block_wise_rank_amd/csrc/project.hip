@@ -428,13 +428,13 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(
 
 // bf16 X -> fp32 or 4-bit factors: the B operand in three bf16 terms (the
 // products are fp32-accurate and identical for both storages, so the 4-bit
-// codes are those of the fp32 factors), 1024-token parts with the next X tile
-// loaded while the current one's products run.  Each wave's 32 rank rows are
-// collected in LDS as fp32 for 128 tokens; the flush writes fp32 rows as whole
-// pieces, or quantises each 32-token run (one run per lane: max, scale, codes)
-// and writes its 16 code bytes and its scale.
+// codes are those of the fp32 factors), 1024-token parts, X through the LDS
+// ring above.  Each wave's 32 rank rows are collected in LDS as fp32 for 64
+// tokens; the flush writes fp32 rows as whole pieces, or quantises each 32-token
+// run (one run per lane: max, scale, codes) and writes its 16 code bytes and its
+// scale.
 constexpr int kRunP = 36;           // LDS floats per staged 32-token run (16-byte aligned pieces)
-constexpr int kRowP = 4 * kRunP;    // LDS floats per staged rank row (128 tokens)
+constexpr int kRowP = 2 * kRunP;    // LDS floats per staged rank row (64 tokens)
 
 template <int OUT>
 __global__ __launch_bounds__(256, 2) void project_split_kernel(
@@ -442,11 +442,13 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
     const float *__restrict__ vt, const int32_t *__restrict__ rank,
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off, uint8_t *__restrict__ arena) {
     __shared__ __align__(16) float stage[4][32 * kRowP];
+    __shared__ __align__(16) uint8_t xring[4 * kXSlot];
     const int blk = blockIdx.x, part = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = rank[blk];
-    if (32 * wave >= r) return;  // no rank rows for this wave (waves are independent)
+    if (r == 0) return;  // uniform over the workgroup
+    const bool active = 32 * wave < r;  // the wave has rank rows (all waves stream X)
     const int t_begin = part * kPartBF;
     const int t_end = min(T, t_begin + kPartBF);
     uint8_t *Ab = arena + a_off[blk];
@@ -486,21 +488,13 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
             fa[2][ks][e] = l;
         }
 
-    const uint16_t *xb = x + (row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride) + 8 * (lane >> 5);
-    u16x8_t xn[8];
-    auto load_x = [&](int t0) {
-        const uint16_t *xr = xb + static_cast<int64_t>(t0 + (lane & 31)) * row_stride;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) xn[ks] = *reinterpret_cast<const u16x8_t *>(xr + 16 * ks);
-    };
+    const uint16_t *xp = x + (row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride) +
+                         static_cast<int64_t>(t_begin) * row_stride;
     float *stg = stage[wave];
-    load_x(t_begin);
-    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
-        u16x8_t xc[8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) xc[ks] = xn[ks];
-        load_x(t0 + 32 < t_end ? t0 + 32 : t0);  // the last tile reloads itself (unused)
-        __builtin_amdgcn_sched_barrier(0);
+    stream_x_ring(xring, xp, row_stride, (t_end - t_begin) / 32, wave, lane,
+                  [&](int t, const u16x8_t (&xc)[8]) __attribute__((always_inline)) {
+        if (!active) return;
+        const int t0 = t_begin + 32 * t;
         f32x16_t acc = zero16(), acc1 = zero16();
 #pragma unroll
         for (int ks = 0; ks < 8; ks += 2)
@@ -511,66 +505,70 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
             }
         acc += acc1;
         // acc[q]: rank row 8 (q / 4) + 4 (lane / 32) + q % 4 of this wave, token lane % 32
-        const int g = ((t0 - t_begin) & 127) >> 5;
+        const int g = t & 1;  // run of the 64-token flush (the part has an even number of tiles)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int row = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
             stg[row * kRowP + g * kRunP + (lane & 31)] = acc[q];
         }
-        if (g == 3 || t0 + 32 >= t_end) {
+        if (g == 1) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int tok0 = t0 - 32 * g;  // first token of the flush
+            const int tok0 = t0 - 32;  // first token of the flush
             if constexpr (OUT == kF32) {
-                // (g + 1) runs of 32 tokens per row, as 16-byte pieces of 4 tokens
+                // 32 rows x 64 tokens: 16 lanes per row, 16-byte pieces of 4 tokens
 #pragma unroll
-                for (int rr = 0; rr < 32; rr += 2) {
-                    const int row = rr + (lane >> 5), piece = lane & 31;
+                for (int rr = 0; rr < 32; rr += 4) {
+                    const int row = rr + (lane >> 4), piece = lane & 15;
                     const int ir = 32 * wave + row;
-                    if (ir < r && piece < 8 * (g + 1))
+                    if (ir < r)
                         *reinterpret_cast<float4 *>(Ab + (static_cast<int64_t>(ir) * T + tok0 + 4 * piece) * 4) =
                             *reinterpret_cast<const float4 *>(stg + row * kRowP + (piece >> 3) * kRunP + 4 * (piece & 7));
                 }
             } else {
-                // 128 runs (32 rows x 4), two per lane; block_len % 128 == 0, so g == 3 here
+                // 64 runs (32 rows x 2), one per lane
+                const int row = lane >> 1, gg = lane & 1;
+                const int ir = 32 * wave + row;
+                const float4 *src = reinterpret_cast<const float4 *>(stg + row * kRowP + gg * kRunP);
+                float m = 0.f;
 #pragma unroll
-                for (int j0 = 0; j0 < 128; j0 += 64) {
-                    const int j = j0 + lane, row = j >> 2, gg = j & 3;
-                    const int ir = 32 * wave + row;
-                    const float4 *src = reinterpret_cast<const float4 *>(stg + row * kRowP + gg * kRunP);
-                    float m = 0.f;
+                for (int k = 0; k < 8; ++k) {
+                    const float4 a = src[k];
+                    m = fmaxf(fmaxf(m, fmaxf(fabsf(a.x), fabsf(a.y))), fmaxf(fabsf(a.z), fabsf(a.w)));
+                }
+                const float sA = __fdiv_rn(m, 7.f);
+                // code = rint(x / s) with the IEEE quotient.  x * fl(1 / s) is within
+                // 1e-6 of x / s (|x / s| <= 7.5), and so is fl(x / s): unless x * (1 / s)
+                // lies within 1e-5 of a half-integer, both round to the same code.
+                // Near one, the quotient itself decides.
+                const float inv = sA > 0.f ? __fdiv_rn(1.f, sA) : 0.f;
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const float4 a = src[k];
-                        m = fmaxf(fmaxf(m, fmaxf(fabsf(a.x), fabsf(a.y))), fmaxf(fabsf(a.z), fabsf(a.w)));
+                for (int k = 0; k < 8; ++k) {
+                    const float4 a = src[k];
+                    const float f[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float qf = f[e] * inv;
+                        float c = rintf(qf);
+                        if (fabsf(qf - c) > 0.5f - 1e-5f) c = rintf(__fdiv_rn(f[e], sA));
+                        c = fminf(fmaxf(c, -7.f), 7.f);
+                        w[k >> 1] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xfu) << (4 * (4 * (k & 1) + e));
                     }
-                    const float sA = __fdiv_rn(m, 7.f);
-                    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const float4 a = src[k];
-                        const float f[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float c = sA > 0.f ? rintf(__fdiv_rn(f[e], sA)) : 0.f;
-                            c = fminf(fmaxf(c, -7.f), 7.f);
-                            w[k >> 1] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xfu) << (4 * (4 * (k & 1) + e));
-                        }
-                    }
-                    if (ir < r) {
-                        *reinterpret_cast<uint4 *>(Ab + static_cast<int64_t>(ir) * (T / 2) + (tok0 + 32 * gg) / 2) =
-                            make_uint4(w[0], w[1], w[2], w[3]);
-                        *reinterpret_cast<float *>(Ab + static_cast<int64_t>(r) * (T / 2) +
-                                                   (static_cast<int64_t>(ir) * (T / kI4Group) + tok0 / kI4Group + gg) * 4) = sA;
-                    }
+                }
+                if (ir < r) {
+                    *reinterpret_cast<uint4 *>(Ab + static_cast<int64_t>(ir) * (T / 2) + (tok0 + 32 * gg) / 2) =
+                        make_uint4(w[0], w[1], w[2], w[3]);
+                    *reinterpret_cast<float *>(Ab + static_cast<int64_t>(r) * (T / 2) +
+                                               (static_cast<int64_t>(ir) * (T / kI4Group) + tok0 / kI4Group + gg) * 4) = sA;
                 }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-    }
+    });
 }
 
 }  // namespace
