@@ -177,3 +177,25 @@ def test_int4_factors(kind):
           f"{f4.nbytes() / (n * T * d * 2):.4f}")
     assert (e_gpu <= 1.1 * e_ora + 2e-3).all(), np.max(e_gpu - 1.1 * e_ora)
     assert abs(e_gpu.mean() - e_ora.mean()) <= 0.05 * e_ora.mean()
+
+
+@pytest.mark.parametrize("T", [192, 1088])
+@pytest.mark.parametrize("storage", ["bf16", "f32", "i8"])
+def test_ragged_tile_counts(T, storage):
+    """Block lengths whose 32-token tile count per workgroup part is 2 mod 4
+    (192: 6 tiles; 1088: a 1024-token part and a 64-token part of 2 tiles), so
+    that the refine and projection tile rings run their two-tile tails."""
+    from synthetic import planted_blocks
+    n = 6
+    X = planted_blocks(n, T, 128, (4.0, 24.0), seed=7000 + T, out_dtype="bf16")
+    pp, bud = [0, n], [n * 64]
+    eps2 = 1e-4
+    f, sig, obj, sweeps = run_gpu_compress(X.to(DEV), pp, bud, eps2, storage)
+    X64 = X.to(torch.float64).numpy()
+    comp = oracle.compress(X64, pp, bud, eps2, storage)
+    worst = check_sigma(sig.cpu().numpy(), comp.sigma, np.sqrt(eps2))
+    r_gpu = f.rank.cpu().numpy()
+    nd = check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
+    xh = reconstruct_all(f).cpu().numpy()
+    rec = check_reconstruction(X64, comp, r_gpu, xh, storage)
+    print(f"\n[T={T} {storage}] sigma worst/bound {worst:.3g}, rank diffs {nd}, recon rel-F {rec:.3g}")
