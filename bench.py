@@ -226,8 +226,8 @@ def main():
         ingest_traffic(args)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the work would shard); rerun with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; "
+              "rerun with --gpus 1", file=sys.stderr)
         return 2
 
     import numpy as np

@@ -11,8 +11,7 @@ Method sources, cited by page and section (see the header of ``milo_oracle.c``):
   [ABS] shd-paper.top digest -- English abstract, method section.
   [DIG] ai4snews digest -- arXivInterpretation, Figure 1 caption.
 
-Readings of points the pages leave open are stated where they are used and
-listed together in the design doc.
+Readings of points the pages leave open are stated where they are used.
 """
 from __future__ import annotations
 

@@ -8,7 +8,7 @@ Two kinds of cases:
   * end to end: GPU compression + GPU decode against oracle compression + oracle
     decode on the same planted caches and queries.
 
-Tolerances (derived in the design doc): the kernels round the rebuilt keys, the
+Tolerances: the kernels round the rebuilt keys, the
 rotated queries and the softmax weights to bf16 MFMA operands (fp32 factors:
 split into two bf16 terms), so errors scale with max|v|: 2e-2 * max|v| for bf16
 and INT8 factors, 1e-4 * max|v| for fp32 factors, and 5e-2 * max|v| for 4-bit
