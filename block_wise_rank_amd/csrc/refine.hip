@@ -39,10 +39,49 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     const int blk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float *vblk = vt + static_cast<int64_t>(blk) * kD * kD;
+    const int64_t base = row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride;
+    // bf16 X streams through a ring of four 32-token tiles in LDS (the V
+    // area, free once the fragments are built).  Each wave loads a quarter of
+    // a tile (rows 8 w .. 8 w + 7, two 16-byte loads per lane) four tiles
+    // ahead, so that the workgroup keeps four distinct tiles in flight
+    // instead of every wave loading every tile.  Rows are padded to 272
+    // bytes: the 16-byte fragment reads of 32 consecutive rows fall on
+    // distinct banks.
+    constexpr int kRowB = kD * 2 + 16;
+    constexpr int kSlot = 32 * kRowB;
+    static_assert(4 * kSlot <= kD * kD * 4, "the ring fits in the V area");
+    uint8_t *ring = reinterpret_cast<uint8_t *>(Vs);
+    const int n_tiles = T / 32;
+    const uint8_t *xg = static_cast<const uint8_t *>(x) + base * 2;
+    const int lr = 8 * wave + (lane >> 4);  // rows lr and lr + 4 of a tile
+    const uint8_t *xl = xg + static_cast<int64_t>(lr) * row_stride * 2 + 16 * (lane & 15);
+    const int64_t x4 = static_cast<int64_t>(4) * row_stride * 2, x32 = static_cast<int64_t>(32) * row_stride * 2;
+    auto load_q = [&](uint4 &ra, uint4 &rb, int tile) __attribute__((always_inline)) {
+        const int tt = tile < n_tiles ? tile : n_tiles - 1;  // past the end: the last tile again
+        const uint8_t *p0 = xl + tt * x32;
+        ra = *reinterpret_cast<const uint4 *>(p0);
+        rb = *reinterpret_cast<const uint4 *>(p0 + x4);
+    };
+    auto store_q = [&](const uint4 &ra, const uint4 &rb, int tile) __attribute__((always_inline)) {
+        uint8_t *p0 = ring + (tile & 3) * kSlot + lr * kRowB + 16 * (lane & 15);
+        *reinterpret_cast<uint4 *>(p0) = ra;
+        *reinterpret_cast<uint4 *>(p0 + 4 * kRowB) = rb;
+    };
+    // tile k waits in (qka, qkb), k = tile % 4, until it is stored, one tile before its use
+    uint4 q0a, q0b, q1a, q1b, q2a, q2b, q3a, q3b;
     constexpr int NV = kD * kD / 4 / 256;  // float4 of V per thread
     float4 vr[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) vr[k] = reinterpret_cast<const float4 *>(vblk)[tid + 256 * k];
+    // the first five X tiles are in flight while V is prepared
+    uint4 ra, rb;
+    if constexpr (NX == 1) {
+        load_q(ra, rb, 0);
+        load_q(q1a, q1b, 1);
+        load_q(q2a, q2b, 2);
+        load_q(q3a, q3b, 3);
+        load_q(q0a, q0b, 4);
+    }
 #pragma unroll
     for (int k = 0; k < NV; ++k) reinterpret_cast<float4 *>(Vs)[tid + 256 * k] = vr[k];
     __syncthreads();
@@ -97,51 +136,13 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
         }
     }
 
-    const int64_t base = row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride;
     float acc2[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc2[r] = 0.f;
 
     if constexpr (NX == 1) {
-        // bf16 X streams through a ring of four 32-token tiles in LDS (the V
-        // area, free once the fragments are built).  Each wave loads a quarter of
-        // a tile (rows 8 w .. 8 w + 7, two 16-byte loads per lane) four tiles
-        // ahead, so that the workgroup keeps four distinct tiles in flight
-        // instead of every wave loading every tile.  Rows are padded to 272
-        // bytes: the 16-byte fragment reads of 32 consecutive rows fall on
-        // distinct banks.
-        constexpr int kRowB = kD * 2 + 16;
-        constexpr int kSlot = 32 * kRowB;
-        static_assert(4 * kSlot <= kD * kD * 4, "the ring fits in the V area");
-        uint8_t *ring = reinterpret_cast<uint8_t *>(Vs);
-        const int n_tiles = T / 32;
-        const uint8_t *xg = static_cast<const uint8_t *>(x) + base * 2;
-        const int lr = 8 * wave + (lane >> 4);  // rows lr and lr + 4 of a tile
-        const uint8_t *xl = xg + static_cast<int64_t>(lr) * row_stride * 2 + 16 * (lane & 15);
-        const int64_t x4 = static_cast<int64_t>(4) * row_stride * 2, x32 = static_cast<int64_t>(32) * row_stride * 2;
-        auto load_q = [&](uint4 &ra, uint4 &rb, int tile) __attribute__((always_inline)) {
-            const int tt = tile < n_tiles ? tile : n_tiles - 1;  // past the end: the last tile again
-            const uint8_t *p0 = xl + tt * x32;
-            ra = *reinterpret_cast<const uint4 *>(p0);
-            rb = *reinterpret_cast<const uint4 *>(p0 + x4);
-        };
-        auto store_q = [&](const uint4 &ra, const uint4 &rb, int tile) __attribute__((always_inline)) {
-            uint8_t *p0 = ring + (tile & 3) * kSlot + lr * kRowB + 16 * (lane & 15);
-            *reinterpret_cast<uint4 *>(p0) = ra;
-            *reinterpret_cast<uint4 *>(p0 + 4 * kRowB) = rb;
-        };
-        // tile k waits in (qka, qkb), k = tile % 4, until it is stored, one tile before its use
-        uint4 q0a, q0b, q1a, q1b, q2a, q2b, q3a, q3b;
         __syncthreads();  // every wave has read V: its LDS is free
-        {
-            uint4 ra, rb;
-            load_q(ra, rb, 0);
-            load_q(q1a, q1b, 1);
-            load_q(q2a, q2b, 2);
-            load_q(q3a, q3b, 3);
-            load_q(q0a, q0b, 4);
-            store_q(ra, rb, 0);
-        }
+        store_q(ra, rb, 0);
         __syncthreads();
         auto step = [&](uint4 &na, uint4 &nb, int t) __attribute__((always_inline)) {
             // B fragments of tile t: token lane % 32, features 16 ks + 8 (lane / 32) ..
@@ -205,6 +206,16 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
             for (int r = 0; r < 16; ++r) acc2[r] += acc[r] * acc[r];
         }
     }
+    // V again (the X ring overwrote its LDS copy): DMA'd from memory into the V
+    // area, 1 KiB per wave instruction, while the sums are reduced and sorted
+    // (every wave's last ring read is behind the loop's final barrier)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int m = 16 * wave + k;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(reinterpret_cast<const uint8_t *>(vblk) + 1024 * m + 16 * lane),
+            (__attribute__((address_space(3))) void *)(reinterpret_cast<uint8_t *>(Vs) + 1024 * m), 16, 0, 0);
+    }
     // acc2[r] belongs to row i = 32 wave + 8 (r / 4) + 4 (lane / 32) + r % 4, token lane % 32.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -228,20 +239,17 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     }
     __syncthreads();
     if (tid < kD) sigma[static_cast<int64_t>(blk) * kD + tid] = ss[tid];
-    // sorted, signed, unit-norm rows, read again from memory (the V area of LDS
-    // held the X ring): every thread holds its rows before any is overwritten
-    float4 w[NV];
+    // sorted, signed, unit-norm rows (the DMA of V has landed before the barrier)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         const int e4 = tid + 256 * k, pos = e4 >> 5, j = 4 * (e4 & 31);
         const int src = perm[pos];
         const float g = sgn[src], iv = ninv[src];
-        const float4 a = *reinterpret_cast<const float4 *>(vblk + src * kD + j);
-        w[k] = make_float4(g * (a.x * iv), g * (a.y * iv), g * (a.z * iv), g * (a.w * iv));
+        const float4 a = *reinterpret_cast<const float4 *>(Vs + src * kD + j);
+        reinterpret_cast<float4 *>(vblk)[e4] = make_float4(g * (a.x * iv), g * (a.y * iv), g * (a.z * iv), g * (a.w * iv));
     }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < NV; ++k) reinterpret_cast<float4 *>(vblk)[tid + 256 * k] = w[k];
 }
 
 }  // namespace
