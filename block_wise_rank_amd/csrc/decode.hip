@@ -480,6 +480,18 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             const int l2 = q & 63, ks = (q >> 6) & 3, mt = q >> 8;
             if (ks >= KS) continue;
             const int j = 16 * mt + (l2 & 15), r0 = 32 * ks + 8 * (l2 >> 4);
+            if constexpr (F == kBF16) {
+                // ranks r0 .. r0 + 7 of dim j by two transposing reads of the staged
+                // rows (lane (c, i) of a 16-lane group addresses row r0 + i / 4 (+ 4),
+                // dims 16 mt + 4 (i % 4) ..); rows past rk (repeats) become zero
+                const uint8_t *p0 = tmp + (r0 + ((l2 & 15) >> 2)) * (kD * 2) + (16 * mt + 4 * (l2 & 3)) * 2;
+                u16x8_t f0 = cat8(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * kD * 2));
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (r0 + e >= rk) f0[e] = 0;
+                *reinterpret_cast<u16x8_t *>(bk + q * 8) = f0;
+                continue;
+            }
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
