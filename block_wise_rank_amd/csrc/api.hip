@@ -89,7 +89,10 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 constexpr int kD = 128;
 constexpr int kMaxSweeps = 30;
 constexpr float kJacobiTol = 1e-6f;
-constexpr float kJacobiStopTol = 1e-3f;  // sqrt(kJacobiTol): quadratic convergence
+// A sweep whose relative off-diagonals all stay below 3e-3 leaves them near
+// 1e-5 (quadratic convergence); the singular values are Rayleigh quotients
+// ||X v||, second order in the eigenvector error, so that sweep ends the solve.
+constexpr float kJacobiStopTol = 3e-3f;
 constexpr size_t kMat = sizeof(float) * kD * kD;  // one 128 x 128 fp32 matrix
 
 // Split the token dimension of the Gram when there are too few blocks to fill

@@ -57,8 +57,8 @@
 // rows unchanged.  Cyclic Jacobi converges quadratically once the off-diagonal
 // part is small (Golub & Van Loan sec. 8.5.3): a sweep whose every relative
 // off-diagonal |g| / sqrt|a b| was at most stop_tol leaves them near
-// stop_tol^2, so with stop_tol = sqrt(tol) such a sweep ends the solve without
-// the sweep that would only confirm it.
+// stop_tol^2, so such a sweep ends the solve without the sweep that would only
+// confirm it.
 #include "common.hpp"
 #include "kernels.hpp"
 

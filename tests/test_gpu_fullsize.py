@@ -49,7 +49,8 @@ def _check_unit(cfg, s, h, X, comp_gpu, sig_gpu, obj_gpu, storage):
     sg = sig_gpu[lo:hi].double().cpu().numpy()
     rg = comp_gpu.rank[lo:hi].cpu().numpy()
     eps = float(np.sqrt(cfg.eps2))
-    check_sigma(sg, ora.sigma, eps)
+    worst = check_sigma(sg, ora.sigma, eps)
+    print(f"  unit ({s},{h}) sigma worst err/bound {worst:.3g}")
     n_swap = check_ranks(rg, ora.rank, ora.sigma, [0, hi - lo], [R])
     pool = s * cfg.n_kv_heads + h
     check_objective(obj_gpu[pool:pool + 1].cpu().numpy(), sg, rg, ora.objective, ora.sigma, ora.rank,
