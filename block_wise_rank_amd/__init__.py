@@ -9,6 +9,7 @@ the binding functions requires the built library; there is no fallback path.
 from .binding import (  # noqa: F401
     Factors,
     MiloError,
+    NotConvergedError,
     decode_workspace_bytes,
     milo_abi_version,
     milo_allocate_ranks,
@@ -27,7 +28,7 @@ from .binding import (  # noqa: F401
 from . import _capi  # noqa: F401
 
 __all__ = [
-    "Factors", "MiloError", "decode_workspace_bytes", "milo_abi_version", "milo_allocate_ranks",
+    "Factors", "MiloError", "NotConvergedError", "decode_workspace_bytes", "milo_abi_version", "milo_allocate_ranks",
     "milo_allocate_ranks_ex", "milo_arena_bytes", "milo_compress_blocks", "milo_compress_blocks_ex",
     "milo_compress_workspace_bytes",
     "milo_decode_attention", "milo_fetch_blocks", "milo_profile_enable", "milo_profile_read", "milo_reconstruct",

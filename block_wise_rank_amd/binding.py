@@ -24,6 +24,16 @@ class MiloError(RuntimeError):
         super().__init__(message)
 
 
+class NotConvergedError(MiloError):
+    """Raised by milo_compress_blocks(check_convergence=True) when the eigensolve
+    of some block reached the sweep cap (a negative entry of sweeps_out)."""
+
+    def __init__(self, blocks):
+        self.blocks = list(blocks)
+        super().__init__(C.MILO_OK, f"eigensolve reached its sweep cap on {len(self.blocks)} block(s): "
+                                    f"{self.blocks[:8]}")
+
+
 def lib():
     return C.load()
 
@@ -64,6 +74,23 @@ def _stream(stream):
     if isinstance(stream, torch.cuda.Stream):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def _torch_stream(stream, device) -> torch.cuda.Stream:
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _on_stream(stream, device, shape, dtype=torch.uint8) -> torch.Tensor:
+    """A scratch tensor for work enqueued on `stream`.  It is allocated with that
+    stream current, so torch's caching allocator hands its memory, once the
+    tensor is dropped, only to later work of the same stream (ordered after the
+    kernels that use it), never to another stream's."""
+    with torch.cuda.stream(_torch_stream(stream, device)):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _dtype_code(dtype) -> int:
@@ -208,11 +235,18 @@ def milo_compress_blocks(x: torch.Tensor, pool_ptr, budget, eps2: float, sigma_o
                          sweeps_out: torch.Tensor | None = None,
                          workspace: torch.Tensor | None = None, row0: torch.Tensor | None = None,
                          row_stride: int | None = None, n_blocks: int | None = None,
-                         block_len: int | None = None, stream=None) -> None:
+                         block_len: int | None = None, stream=None,
+                         check_convergence: bool = False) -> None:
     """Compress blocks of ``x``: a contiguous [n_blocks, T, d] tensor, or any tensor
-    addressed through ``row0``/``row_stride`` (with n_blocks and block_len given)."""
+    addressed through ``row0``/``row_stride`` (with n_blocks and block_len given).
+
+    The call is asynchronous, so a block whose eigensolve reached the sweep cap
+    shows only as a negative entry of ``sweeps_out``.  With
+    ``check_convergence=True`` the binding supplies ``sweeps_out`` if none is
+    given, waits for the stream and raises NotConvergedError naming such blocks."""
     milo_compress_blocks_ex(x, pool_ptr, budget, eps2, sigma_out, factors, objective_out, sweeps_out,
-                            None, 0, workspace, row0, row_stride, n_blocks, block_len, stream)
+                            None, 0, workspace, row0, row_stride, n_blocks, block_len, stream,
+                            check_convergence)
 
 
 def milo_compress_blocks_ex(x: torch.Tensor, pool_ptr, budget, eps2: float, sigma_out: torch.Tensor,
@@ -221,13 +255,15 @@ def milo_compress_blocks_ex(x: torch.Tensor, pool_ptr, budget, eps2: float, sigm
                             seed: int = 0, workspace: torch.Tensor | None = None,
                             row0: torch.Tensor | None = None, row_stride: int | None = None,
                             n_blocks: int | None = None, block_len: int | None = None,
-                            stream=None) -> None:
+                            stream=None, check_convergence: bool = False) -> None:
     """milo_compress_blocks with the rank allocation policy "entropy" (the
     default), "uniform" or "random" (seeded)."""
     if row0 is None and row_stride is None:
         n_blocks, block_len, d = x.shape
         row_stride = d
     d = factors.head_dim
+    if check_convergence and sweeps_out is None:
+        sweeps_out = _on_stream(stream, x.device, int(n_blocks), torch.int32)
     _need(x, "x", contiguous=row0 is None)  # with row0 the rows are addressed explicitly
     _need(row0, "row0", torch.int64, int(n_blocks), optional=True)
     _need(sigma_out, "sigma_out", torch.float32, int(n_blocks) * d)
@@ -246,11 +282,16 @@ def milo_compress_blocks_ex(x: torch.Tensor, pool_ptr, budget, eps2: float, sigm
                                        ctypes.byref(fs), _p(sweeps_out), _alloc_options(policy, seed),
                                        _p(workspace), ctypes.byref(wsb), _stream(stream))
     if st == C.MILO_E_WORKSPACE and workspace is None:
-        workspace = torch.empty(int(wsb.value), dtype=torch.uint8, device=x.device)
+        workspace = _on_stream(stream, x.device, int(wsb.value))
         return milo_compress_blocks_ex(x, pool_ptr, budget, eps2, sigma_out, factors, objective_out,
                                        sweeps_out, policy, seed, workspace, row0, row_stride,
-                                       n_blocks, block_len, stream)
+                                       n_blocks, block_len, stream, check_convergence)
     _check(st)
+    if check_convergence and int(n_blocks) > 0:
+        _torch_stream(stream, x.device).synchronize()
+        bad = torch.nonzero(sweeps_out[:int(n_blocks)] < 0).flatten().tolist()
+        if bad:
+            raise NotConvergedError(bad)
 
 
 def milo_allocate_ranks(sigma: torch.Tensor, max_rank: int, pool_ptr, budget, eps2: float,
@@ -279,7 +320,7 @@ def milo_allocate_ranks_ex(sigma: torch.Tensor, max_rank: int, pool_ptr, budget,
                                       _p(objective_out), _alloc_options(policy, seed), _p(workspace),
                                       ctypes.byref(wsb), _stream(stream))
     if st == C.MILO_E_WORKSPACE and workspace is None:
-        workspace = torch.empty(int(wsb.value), dtype=torch.uint8, device=sigma.device)
+        workspace = _on_stream(stream, sigma.device, int(wsb.value))
         return milo_allocate_ranks_ex(sigma, max_rank, pool_ptr, budget, eps2, rank_out,
                                       objective_out, policy, seed, workspace, stream)
     _check(st)
@@ -345,7 +386,7 @@ def milo_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: F
     need = ctypes.c_size_t(0)
     st = lib().milo_decode_attention(ctypes.byref(args), ctypes.byref(need), _stream(stream))
     if st == C.MILO_E_WORKSPACE and workspace is None:
-        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=q.device)
+        workspace = _on_stream(stream, q.device, int(need.value))
         return milo_decode_attention(q, q_pos, k, v, blocks_per_seq, n_kv_heads, out, sel_ptr,
                                      sel_blk, sel_max, tail_k, tail_v, tail_len, tail_pos0,
                                      rope_base, softmax_scale, split_len, workspace, stream)
@@ -368,16 +409,17 @@ def reconstruct_then_attend(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v:
     T, d = k.block_len, k.head_dim
     shape = (batch, n_kv_heads, blocks_per_seq * T, d)
     if staging_k is None:
-        staging_k = torch.empty(shape, dtype=staging_dtype, device=q.device)
+        staging_k = _on_stream(stream, q.device, shape, staging_dtype)
     if staging_v is None:
-        staging_v = torch.empty(shape, dtype=staging_dtype, device=q.device)
+        staging_v = _on_stream(stream, q.device, shape, staging_dtype)
     _need(staging_k, "staging_k", None, batch * n_kv_heads * blocks_per_seq * T * d)
     _need(staging_v, "staging_v", staging_k.dtype, staging_k.numel())
-    ids = torch.arange(batch * n_kv_heads * blocks_per_seq, dtype=torch.int32, device=q.device)
+    with torch.cuda.stream(_torch_stream(stream, q.device)):  # scratch of this stream (see _on_stream)
+        ids = torch.arange(batch * n_kv_heads * blocks_per_seq, dtype=torch.int32, device=q.device)
+        tail_len = torch.full((batch,), blocks_per_seq * T, dtype=torch.int32, device=q.device)
+        tail_pos0 = torch.zeros((batch,), dtype=torch.int64, device=q.device)
     milo_reconstruct(k, ids, staging_k, stream)
     milo_reconstruct(v, ids, staging_v, stream)
-    tail_len = torch.full((batch,), blocks_per_seq * T, dtype=torch.int32, device=q.device)
-    tail_pos0 = torch.zeros((batch,), dtype=torch.int64, device=q.device)
     milo_decode_attention(q, q_pos, k, v, 0, n_kv_heads, out, tail_k=staging_k.view(shape),
                           tail_v=staging_v.view(shape), tail_len=tail_len, tail_pos0=tail_pos0,
                           rope_base=rope_base, softmax_scale=softmax_scale, split_len=split_len,

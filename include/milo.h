@@ -138,7 +138,11 @@ typedef struct milo_factors {
  *              order (sigma desc, block asc, index asc), which is what the
  *              greedy on the gains selects.
  *  sweeps_out  device [n_blocks] int32 (may be NULL): Jacobi sweeps used per
- *              block; negative if the eigensolver hit its sweep cap.
+ *              block; -30 if the eigensolve of that block reached its cap of
+ *              30 sweeps (its results are then those of the last sweep).  The
+ *              call returns before its kernels run, so it cannot report this in
+ *              its status: a caller that must know passes sweeps_out and checks
+ *              it once the stream has reached the call.
  *  workspace   device scratch; *workspace_bytes its size.  With workspace ==
  *              NULL or a size below what one pool needs, returns
  *              MILO_E_WORKSPACE and sets *workspace_bytes to the size that

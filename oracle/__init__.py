@@ -94,6 +94,8 @@ def load(path: str):
     L.oracle_attention.restype = ctypes.c_int
     L.oracle_max_threads.argtypes = []
     L.oracle_max_threads.restype = ctypes.c_int
+    L.oracle_set_threads.argtypes = [ctypes.c_int]
+    L.oracle_set_threads.restype = ctypes.c_int
     return L
 
 
@@ -107,6 +109,11 @@ def _ptr(a: np.ndarray, typ=_dp):
 
 def max_threads() -> int:
     return int(lib().oracle_max_threads())
+
+
+def set_threads(n: int) -> int:
+    """Threads the block loops use from now on; returns the previous count."""
+    return int(lib().oracle_set_threads(int(n)))
 
 
 # --------------------------------------------------------------------------- #

@@ -80,6 +80,20 @@ int oracle_max_threads(void)
 #endif
 }
 
+/* Threads the block loop may use from now on (timing of the oracle as a
+ * baseline at one thread and at all host threads); returns the previous count. */
+int oracle_set_threads(int n)
+{
+    const int prev = oracle_max_threads();
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return prev;
+}
+
 /* ------------------------------------------------------------------------- */
 /* SVD of one block by one-sided cyclic Jacobi.                              */
 /*                                                                           */

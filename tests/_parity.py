@@ -11,8 +11,12 @@ from block_wise_rank_amd import (Factors, milo_arena_bytes, milo_compress_blocks
 from synthetic import pool_layout
 
 # |sigma_gpu - sigma_oracle| <= SIGMA_REL * max(sigma_oracle, eps): relative 1e-3
-# for every singular value above eps (all the ones the allocation can pick),
-# absolute 1e-3 * eps below it, where log(1 + sigma^2/eps^2) is flat.
+# for every singular value above eps, absolute 1e-3 * eps below it.  Below eps
+# the Gram-based solve in fp32 cannot promise 1e-3 relative: its backward error
+# is ~u * sigma_max^2 (u = 2^-24), which moves sigma by ~u sigma_max^2 / (2 sigma),
+# i.e. 1e-3 relative only for sigma above ~0.005 sigma_max.  Where a pool's
+# budget cutoff falls below eps (short blocks, whose noise singular values reach
+# below eps) the selected values under eps are reported, not asserted.
 SIGMA_REL = 1e-3
 # 4-bit: the factors agree with the oracle's to ~1e-3, and an entry that close
 # to a rounding boundary moves by a whole step s = max|run| / 7 (about a third
@@ -28,7 +32,8 @@ def run_gpu_compress(X: torch.Tensor, pool_ptr, budgets, eps2: float, storage: s
     sigma = torch.empty((n, d), dtype=torch.float32, device=X.device)
     obj = torch.empty(len(pool_ptr) - 1, dtype=torch.float64, device=X.device)
     sweeps = torch.empty(n, dtype=torch.int32, device=X.device)
-    milo_compress_blocks(X, pool_ptr, budgets, eps2, sigma, f, objective_out=obj, sweeps_out=sweeps)
+    milo_compress_blocks(X, pool_ptr, budgets, eps2, sigma, f, objective_out=obj, sweeps_out=sweeps,
+                         check_convergence=True)
     torch.cuda.synchronize()
     return f, sigma, obj, sweeps
 
@@ -41,16 +46,38 @@ def reconstruct_all(f: Factors, out_dtype=torch.float32):
     return out
 
 
-def check_sigma(sig_gpu: np.ndarray, sig_ora: np.ndarray, eps: float):
+def pool_cutoffs(sig_ora: np.ndarray, pool_ptr, r_ora) -> np.ndarray:
+    """Per block: the smallest singular value the oracle selects in its pool (inf
+    for a pool that selects none)."""
+    cut = np.full(sig_ora.shape[0], np.inf)
+    for p in range(len(pool_ptr) - 1):
+        lo, hi = int(pool_ptr[p]), int(pool_ptr[p + 1])
+        sel = [sig_ora[b, int(r_ora[b]) - 1] for b in range(lo, hi) if int(r_ora[b]) > 0]
+        if sel:
+            cut[lo:hi] = min(sel)
+    return cut
+
+
+def check_sigma(sig_gpu: np.ndarray, sig_ora: np.ndarray, eps: float, pool_ptr=None, r_ora=None):
+    """Every singular value within SIGMA_REL * max(sigma_oracle, eps) (see above).
+    With the pool table and the oracle's ranks, the relative error of the selected
+    values below eps is printed as well."""
     bound = SIGMA_REL * np.maximum(sig_ora, eps)
     err = np.abs(sig_gpu - sig_ora)
     worst = float((err / bound).max())
     rel = err / np.maximum(sig_ora, eps)
-    for lo, hi in [(0.1, 10.0), (eps, 0.1), (0.0, eps)]:
+    for lo, hi in [(0.1, np.inf), (eps, 0.1), (0.0, eps)]:
         m = (sig_ora >= lo) & (sig_ora < hi)
         if m.any():
             print(f"  sigma in [{lo:g},{hi:g}): n={int(m.sum())} max rel {rel[m].max():.3g} "
                   f"median rel {np.median(rel[m]):.3g}")
+    if pool_ptr is not None:
+        cut = pool_cutoffs(sig_ora, pool_ptr, r_ora)[:, None]
+        m = (sig_ora >= cut) & (sig_ora < eps) & (sig_ora > 0)
+        if m.any():
+            r = (err / sig_ora)[m]
+            print(f"  selected sigma below eps (cutoff {float(cut.min()):.3g}): n={int(m.sum())} "
+                  f"max rel {r.max():.3g} median rel {np.median(r):.3g}")
     assert worst <= 1.0, f"sigma parity: worst err/bound = {worst:.3g}"
     return worst
 

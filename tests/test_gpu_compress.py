@@ -39,7 +39,7 @@ def test_config0_fp32(kind):
     cfg, X64, pp, bud, f, sig, obj, sweeps, comp = _case(0, kind)
     print(f"\n[cfg0 {kind}] sweeps {sweeps.cpu().numpy()}")
     assert (sweeps.cpu().numpy() > 0).all()
-    worst = check_sigma(sig.cpu().numpy(), comp.sigma, np.sqrt(cfg.eps2))
+    worst = check_sigma(sig.cpu().numpy(), comp.sigma, np.sqrt(cfg.eps2), pp, comp.rank)
     r_gpu = f.rank.cpu().numpy()
     nd = check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
     xh = reconstruct_all(f).cpu().numpy()
@@ -55,7 +55,7 @@ def test_config1_bf16(kind):
     sw = sweeps.cpu().numpy()
     print(f"\n[cfg1 {kind}] sweeps min {sw.min()} max {sw.max()} mean {sw.mean():.2f}")
     assert (sw > 0).all()
-    worst = check_sigma(sig.cpu().numpy(), comp.sigma, np.sqrt(cfg.eps2))
+    worst = check_sigma(sig.cpu().numpy(), comp.sigma, np.sqrt(cfg.eps2), pp, comp.rank)
     r_gpu = f.rank.cpu().numpy()
     nd = check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
     xh = reconstruct_all(f).cpu().numpy()
@@ -109,21 +109,162 @@ def test_ranks_bit_exact_given_oracle_sigma():
         assert np.array_equal(rg[pp[p]:pp[p + 1]], r_o), p
 
 
+def _int8_invariants(f, T, d):
+    """The GPU's own INT8 factors: every row with a positive scale reaches the
+    code +-127 (the absmax element), every row with a zero scale is all zero."""
+    ar = f.arena.cpu().numpy()
+    a_sc, b_sc = f.a_scale.cpu().numpy(), f.b_scale.cpu().numpy()
+    rk = f.rank.cpu().numpy()
+    for b in range(f.n_blocks):
+        r = int(rk[b])
+        if r == 0:
+            continue
+        ao, bo = int(f.a_off[b]), int(f.b_off[b])
+        A8 = ar[ao:ao + r * T].view(np.int8).reshape(r, T).astype(np.int32)
+        B8 = ar[bo:bo + r * d].view(np.int8).reshape(r, d).astype(np.int32)
+        for codes, sc in ((A8.T, a_sc[b * T:(b + 1) * T]), (B8, b_sc[b * d:b * d + r])):
+            top = np.abs(codes).max(axis=1)
+            assert (sc >= 0).all(), b
+            assert (top[sc > 0] == 127).all(), f"block {b}: a row with a positive scale misses +-127"
+            assert (top[sc == 0] == 0).all(), f"block {b}: a zero-scale row holds codes"
+
+
 @pytest.mark.parametrize("frac", [0.25, 0.5, 0.75])
 @pytest.mark.parametrize("storage", ["bf16", "i8", "i4"])
 def test_config3_budget_precision_sweep(frac, storage):
     cfg, X64, pp, bud, f, sig, obj, sweeps, comp = _case(3, "k", storage=storage, frac=frac)
     r_gpu = f.rank.cpu().numpy()
+    check_sigma(sig.cpu().numpy(), comp.sigma, np.sqrt(cfg.eps2), pp, comp.rank)
     check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
     xh = reconstruct_all(f).cpu().numpy()
-    rec = check_reconstruction(X64, comp, r_gpu, xh, storage, blocks=range(0, f.n_blocks, 3))
+    rec = check_reconstruction(X64, comp, r_gpu, xh, storage)
     full = f.n_blocks * cfg.block_len * cfg.head_dim * 2
     ratio = f.nbytes() / full
     print(f"\n[cfg3 {storage} {frac:.2f}] memory ratio vs bf16 KV {ratio:.4f}, recon rel-F {rec:.3g}")
     if storage == "i8":
-        # INT8 invariants: every non-empty row of B reaches +-127; scales >= 0
-        bs = f.b_scale.cpu().numpy()
-        assert (bs >= 0).all() and (f.a_scale.cpu().numpy() >= 0).all()
+        _int8_invariants(f, cfg.block_len, cfg.head_dim)
+
+
+@pytest.mark.parametrize("kind", ["k", "v"])
+def test_int8_codes(kind):
+    """INT8 factors on the config-1 shapes (1024-token bf16 blocks, 50% budget)
+    against the oracle's quantiser, code by code.
+
+    B: the INT8 path quantises the same fp32 eigenvector rows the fp32 storage
+    stores, with the code decided in fp32 on both sides, so every B code and
+    scale must equal the oracle's quantiser applied to the fp32 factors of a call
+    on the same blocks.  A = X B~^T is formed from the dequantised B~ (codes x
+    scale): the oracle quantises the exact product (fp64) per token row; the GPU
+    sums in fp32, so a code may differ by one step where the product lies within
+    fp32 rounding of a rounding boundary, and the scales agree to fp32 accuracy."""
+    cfg = CONFIGS[1]
+    X = layer_inputs(cfg, 0, kind, device="cpu")
+    pp, bud = layer_pools(cfg)
+    Xg = X.to(DEV)
+    f32, s32, _, _ = run_gpu_compress(Xg, pp, bud, cfg.eps2, "f32")
+    f8, s8, _, _ = run_gpu_compress(Xg, pp, bud, cfg.eps2, "i8")
+    assert torch.equal(f32.rank, f8.rank) and torch.equal(s32, s8)
+    n, T, d = X.shape
+    X64 = X.to(torch.float64).numpy()
+    ar32, ar8 = f32.arena.cpu().numpy(), f8.arena.cpu().numpy()
+    a_sc, b_sc = f8.a_scale.cpu().numpy(), f8.b_scale.cpu().numpy()
+    rk = f8.rank.cpu().numpy()
+    n_off = n_codes = 0
+    worst_scale = 0.0
+    for b in range(n):
+        r = int(rk[b])
+        if r == 0:
+            continue
+        B32 = ar32[int(f32.b_off[b]):int(f32.b_off[b]) + 4 * r * d].view(np.float32).reshape(r, d)
+        sb, cb, _ = oracle.quant_int8_rows(B32)
+        bo = int(f8.b_off[b])
+        B8 = ar8[bo:bo + r * d].view(np.int8).reshape(r, d)
+        assert np.array_equal(B8, cb), f"block {b}: B codes"
+        assert np.array_equal(b_sc[b * d:b * d + r], sb.astype(np.float32)), f"block {b}: B scales"
+        A_ref = (X64[b] @ B8.T.astype(np.float64)) * b_sc[b * d:b * d + r].astype(np.float64)  # T x r
+        sa, ca, _ = oracle.quant_int8_rows(A_ref)
+        ao = int(f8.a_off[b])
+        A8 = ar8[ao:ao + r * T].view(np.int8).reshape(r, T).T
+        diff = np.abs(A8.astype(np.int32) - ca.astype(np.int32))
+        assert diff.max() <= 1, f"block {b}: A code off by {diff.max()}"
+        n_off += int((diff != 0).sum())
+        n_codes += diff.size
+        ga = a_sc[b * T:(b + 1) * T].astype(np.float64)
+        worst_scale = max(worst_scale, float((np.abs(ga - sa) / np.maximum(sa, 1e-30)).max()))
+    print(f"\n[i8 {kind}] A codes one step off: {n_off} of {n_codes}; worst A scale rel err {worst_scale:.3g}")
+    assert worst_scale <= 1e-5
+    assert n_off <= 1e-3 * n_codes
+    _int8_invariants(f8, T, d)
+
+
+def test_compress_edge_cases():
+    """Degenerate blocks through the whole compression, fp32 storage, against the
+    oracle: an all-zero block, a rank-1 block, a block with orthonormal columns
+    (every singular value 1, so the singular subspaces are not unique), and the
+    same planted blocks at x1e-3, x1 and x1e3 in pools of their own (the method
+    is scale-invariant: equal ranks, singular values and relative errors)."""
+    from synthetic import planted_blocks
+    T, d = 256, 128
+    P = planted_blocks(2, T, d, (4.0, 32.0), seed=8101, out_dtype="f64")
+    g = torch.Generator().manual_seed(8102)
+    a = torch.randn(T, generator=g, dtype=torch.float64)
+    v = torch.randn(d, generator=g, dtype=torch.float64)
+    rank1 = 0.7 * torch.outer(a / a.norm(), v / v.norm())
+    Q, _ = torch.linalg.qr(torch.randn(T, d, generator=g, dtype=torch.float64))
+    blocks = [torch.zeros(T, d, dtype=torch.float64), rank1, P[0], Q,
+              1e-3 * P[0], 1e-3 * P[1], 1e3 * P[0], 1e3 * P[1], P[0], P[1]]
+    scale = np.array([1, 1, 1, 1, 1e-3, 1e-3, 1e3, 1e3, 1, 1], dtype=np.float64)
+    X = torch.stack(blocks).to(torch.float32)
+    pp, bud = [0, 3, 4, 6, 8, 10], [100, 50, 128, 128, 128]
+    eps2 = 1e-4
+    f, sig, obj, sweeps = run_gpu_compress(X.to(DEV), pp, bud, eps2, "f32")
+    assert (sweeps.cpu().numpy() > 0).all()
+    X64 = X.to(torch.float64).numpy()
+    comp = oracle.compress(X64, pp, bud, eps2, "f32")
+    sg = sig.cpu().numpy().astype(np.float64)
+    worst = check_sigma(sg / scale[:, None], comp.sigma / scale[:, None], np.sqrt(eps2), pp, comp.rank)
+    assert (sg[0] == 0).all(), "zero block: singular values"
+    r_gpu = f.rank.cpu().numpy()
+    check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
+    assert list(r_gpu[:4]) == [0, 1, 99, 50]
+    assert np.array_equal(r_gpu[4:6], r_gpu[8:10]) and np.array_equal(r_gpu[6:8], r_gpu[8:10])
+    xh = reconstruct_all(f).cpu().numpy().astype(np.float64)
+    assert (xh[0] == 0).all()
+    rec = check_reconstruction(X64, comp, r_gpu, xh, "f32", blocks=[0, 1, 2, 4, 5, 6, 7, 8, 9])
+    # orthonormal columns: any 50 of the equal singular directions are a best
+    # rank-50 approximation; what is unique is the residual (78 of 128 unit
+    # values, Eckart-Young) and that the factors are X projected on an
+    # orthonormal basis (B B^T = I, A = X B^T)
+    res = np.sum((xh[3] - X64[3]) ** 2)
+    assert abs(res - np.sum(comp.sigma[3, 50:] ** 2)) <= 1e-4 * 128, res
+    ar = f.arena.cpu().numpy()
+    B = ar[int(f.b_off[3]):int(f.b_off[3]) + 4 * 50 * d].view(np.float32).reshape(50, d).astype(np.float64)
+    A = ar[int(f.a_off[3]):int(f.a_off[3]) + 4 * 50 * T].view(np.float32).reshape(50, T).T.astype(np.float64)
+    assert np.abs(B @ B.T - np.eye(50)).max() <= 1e-5
+    assert np.abs(A - X64[3] @ B.T).max() <= 1e-5
+    print(f"\n[edge] sigma worst/bound {worst:.3g}, ranks {list(r_gpu)}, recon rel-F {rec:.3g}, "
+          f"orthonormal-block residual {res:.4f}")
+
+
+def test_block_len_128():
+    """The smallest block length: 128 tokens, so k = min(T, d) = T = d."""
+    from synthetic import planted_blocks
+    n, T = 8, 128
+    X = planted_blocks(n, T, 128, (4.0, 24.0), seed=8201, out_dtype="bf16")
+    pp, bud = [0, 5, 8], [5 * 64, 3 * 64]
+    eps2 = 1e-4
+    for storage in ("bf16", "f32", "i8", "i4"):
+        f, sig, obj, sweeps = run_gpu_compress(X.to(DEV), pp, bud, eps2, storage)
+        X64 = X.to(torch.float64).numpy()
+        comp = oracle.compress(X64, pp, bud, eps2, storage)
+        worst = check_sigma(sig.cpu().numpy(), comp.sigma, np.sqrt(eps2), pp, comp.rank)
+        r_gpu = f.rank.cpu().numpy()
+        check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
+        xh = reconstruct_all(f).cpu().numpy()
+        rec = check_reconstruction(X64, comp, r_gpu, xh, storage)
+        check_objective(obj.cpu().numpy(), sig.cpu().numpy(), r_gpu, comp.objective, comp.sigma, comp.rank,
+                        pp, eps2)
+        print(f"\n[T=128 {storage}] sigma worst/bound {worst:.3g}, recon rel-F {rec:.3g}")
 
 
 @pytest.mark.parametrize("kind", ["k", "v"])
@@ -193,7 +334,7 @@ def test_ragged_tile_counts(T, storage):
     f, sig, obj, sweeps = run_gpu_compress(X.to(DEV), pp, bud, eps2, storage)
     X64 = X.to(torch.float64).numpy()
     comp = oracle.compress(X64, pp, bud, eps2, storage)
-    worst = check_sigma(sig.cpu().numpy(), comp.sigma, np.sqrt(eps2))
+    worst = check_sigma(sig.cpu().numpy(), comp.sigma, np.sqrt(eps2), pp, comp.rank)
     r_gpu = f.rank.cpu().numpy()
     nd = check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
     xh = reconstruct_all(f).cpu().numpy()

@@ -4,11 +4,15 @@ pinned host memory, the blocks a decode step attends brought to the device.
 The fetch is pure data movement, so its parity is equality: the fetched bytes
 equal the host bytes, blocks not listed are left untouched, and decode over the
 fetched set is bit-identical to decode over a device-resident set; the decode
-itself is checked against the oracle in test_gpu_decode.py.
+over the fetched set is also checked against the oracle's decode of the
+decoded factor values the generator wrote (the same tolerances as the resident
+decode tests).
 """
 import numpy as np
 import pytest
 import torch
+
+import oracle
 
 from block_wise_rank_amd import Factors, MiloError, milo_decode_attention, milo_fetch_blocks
 from synthetic.factors import i4_rank_bytes, random_factor_set
@@ -39,8 +43,8 @@ def test_fetch_then_decode_equals_resident(storage):
     n = batch * hkv * bps
     ranks = np.random.default_rng(4).integers(0, 129, size=n)
     ranks[3] = 0
-    kt, _, _ = random_factor_set(n, T, 128, storage, seed=31, ranks=ranks)
-    vt, _, _ = random_factor_set(n, T, 128, storage, seed=32, ranks=ranks[::-1].copy())
+    kt, kA, kB = random_factor_set(n, T, 128, storage, seed=31, ranks=ranks)
+    vt, vA, vB = random_factor_set(n, T, 128, storage, seed=32, ranks=ranks[::-1].copy())
     k_res, v_res = _set(kt, storage, n, T, DEV), _set(vt, storage, n, T, DEV)
     k_host, v_host = k_res.to_host(), v_res.to_host()
     assert k_host.arena.is_pinned() and k_host.rank.device.type == "cpu"
@@ -50,10 +54,11 @@ def test_fetch_then_decode_equals_resident(storage):
         if f.a_scale is not None:
             f.a_scale.fill_(7.0)
             f.b_scale.fill_(7.0)
-    # per sequence: blocks attended (sequence 1 in a scrambled order with a repeat)
-    sel = [[0, 1, 2, 5], [7, 3, 3, 4]]
+    # per sequence: blocks attended (ascending and distinct, as decode requires);
+    # the fetch list names them in a scrambled order with repeats
+    sel = [[0, 1, 2, 5], [3, 4, 7]]
     ids = sorted({(s * hkv + h) * bps + b for s in range(batch) for h in range(hkv) for b in sel[s]})
-    listed = ids[::-1] + ids[:3]  # any order, repeats allowed
+    listed = ids[::-1] + ids[:3]
     st = torch.cuda.Stream()
     with torch.cuda.stream(st):
         milo_fetch_blocks(k_host, k_dev, listed, stream=st)
@@ -88,6 +93,16 @@ def test_fetch_then_decode_equals_resident(storage):
     want = _decode(q, q_pos, k_res, v_res, bps, hkv, sel_ptr, sel_blk, 4)
     got = _decode(q, q_pos, k_dev, v_dev, bps, hkv, sel_ptr, sel_blk, 4)
     assert torch.equal(got, want), f"max diff {float((got - want).abs().max())}"
+    # the decode over the fetched set against the oracle on the decoded factors
+    Kh = [a @ b for a, b in zip(kA, kB)]
+    Vh = [a @ b for a, b in zip(vA, vB)]
+    ref = oracle.decode(q.to(torch.float64).cpu().numpy(), q_pos.cpu().numpy(), Kh, Vh, T, hkv, bps, sel=sel)
+    vmax = max(float(np.abs(Vh[(s * hkv + h) * bps + b]).max()) for s in range(batch) for h in range(hkv)
+               for b in sel[s])
+    err = float(np.abs(got.cpu().numpy() - ref).max())
+    tol = {"bf16": 2e-2, "i8": 2e-2, "i4": 5e-2, "f32": 1e-4}[storage]
+    print(f"\n[offload {storage}] max|err| vs oracle {err:.3g}, bound {tol * vmax:.3g}")
+    assert err <= tol * vmax
 
 
 def test_fetch_rejects_bad_ids_and_geometry():

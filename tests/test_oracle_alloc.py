@@ -124,3 +124,28 @@ def test_planted_pool_ranks_follow_tau(oracle_lib):
         for b in range(8):
             if t[a] > t[b] + 2.0:
                 assert rank[a] >= rank[b]
+
+
+def test_compress_several_pools(oracle_lib):
+    """oracle.compress over a pool table with pools of unequal sizes and budgets
+    (one pool empty, one budget zero): each pool's ranks are the greedy's closed
+    form on that pool's own singular values and budget, the objective per pool
+    is the sum of its selected gains, and every block's factors carry its own
+    rank (the Eckart-Young residual of that rank)."""
+    from synthetic import planted_blocks
+    X = planted_blocks(9, 128, 128, (4.0, 32.0), 91, out_dtype="f64").numpy()
+    pool_ptr, budgets, eps2 = [0, 2, 2, 6, 9], [100, 5, 300, 0], 1e-4
+    comp = oracle_lib.compress(X, pool_ptr, budgets, eps2, "f32")
+    assert len(comp.objective) == 4
+    for p in range(4):
+        lo, hi = pool_ptr[p], pool_ptr[p + 1]
+        want = _top_r(comp.sigma[lo:hi], budgets[p]) if hi > lo else np.zeros(0, dtype=np.int32)
+        assert np.array_equal(comp.rank[lo:hi], want), p
+        gains = sum(np.log1p(comp.sigma[b, :comp.rank[b]] ** 2 / eps2).sum() for b in range(lo, hi))
+        assert abs(comp.objective[p] - gains) <= 1e-9 * max(1.0, gains), p
+    assert comp.rank[6:].sum() == 0 and comp.rank[2:6].sum() == 300 and comp.rank[:2].sum() == 100
+    for b in range(9):
+        r = int(comp.rank[b])
+        assert comp.A[b].shape == (128, r) and comp.B[b].shape == (r, 128)
+        err2 = np.sum((X[b] - comp.A[b] @ comp.B[b]) ** 2)
+        assert abs(err2 - np.sum(comp.sigma[b, r:] ** 2)) <= 1e-6 * np.sum(comp.sigma[b] ** 2), b

@@ -120,3 +120,47 @@ def test_decode_selection_and_tail(oracle_lib):
     pos = np.concatenate([np.arange(T) + T, np.arange(T) + 3 * T, np.arange(10) + nblk * T])
     ref = oracle_lib.attention(q[0, 0], nblk * T + 10, Kc, Vc, pos, BASE, 1 / np.sqrt(d))
     assert np.abs(out[0, 0] - ref).max() <= 1e-15
+
+
+def _sdpa_reference(q, q_pos, K_all, V_all, sel, block_len):
+    """Decode by torch's fp64 attention with its own grouped-query mapping
+    (enable_gqa: query head j of a group of G reads KV head j // G).  The cache
+    is a [batch, Hkv, blocks, T, d] array; a sequence's attended blocks are
+    sliced out of it and concatenated in order, so nothing here repeats the
+    oracle's block-id arithmetic."""
+    batch, Hq, d = q.shape
+    out = np.zeros((batch, Hq, d))
+    for s in range(batch):
+        blocks = list(sel[s])
+        Kc = K_all[s][:, blocks].reshape(K_all.shape[1], -1, d)   # [Hkv, L, d]
+        Vc = V_all[s][:, blocks].reshape(V_all.shape[1], -1, d)
+        pos = np.concatenate([np.arange(block_len) + b * block_len for b in blocks]).astype(np.float64)
+        qr = torch.from_numpy(_rope_complex(q[s], np.float64(q_pos[s])))[None, :, None]   # [1, Hq, 1, d]
+        kr = torch.from_numpy(_rope_complex(Kc, pos))[None]
+        o = torch.nn.functional.scaled_dot_product_attention(qr, kr, torch.from_numpy(Vc)[None],
+                                                             enable_gqa=True)
+        out[s] = o[0, :, 0].numpy()
+    return out
+
+
+def test_decode_batches_kv_heads_and_groups(oracle_lib):
+    """Several sequences, KV heads and query-head groups: the oracle's decode
+    equals torch's grouped-query attention over the same cache laid out as
+    [sequence, KV head, block, token, dim], with the factor block list in that
+    order (block id = position in the flattened layout), per-sequence query
+    positions and per-sequence block selections."""
+    rng = np.random.default_rng(7)
+    batch, Hkv, G, bps, T, d = 2, 2, 4, 3, 16, 128
+    K_all = rng.standard_normal((batch, Hkv, bps, T, d))
+    V_all = rng.standard_normal((batch, Hkv, bps, T, d))
+    q = rng.standard_normal((batch, Hkv * G, d)) * 4
+    q_pos = [bps * T, bps * T + 5]
+    K_list = list(K_all.reshape(-1, T, d))
+    V_list = list(V_all.reshape(-1, T, d))
+    got = oracle_lib.decode(q, q_pos, K_list, V_list, T, Hkv, bps)
+    ref = _sdpa_reference(q, q_pos, K_all, V_all, [range(bps)] * batch, T)
+    assert np.abs(got - ref).max() <= 1e-12
+    sel = [[0, 2], [1]]
+    got = oracle_lib.decode(q, q_pos, K_list, V_list, T, Hkv, bps, sel=sel)
+    ref = _sdpa_reference(q, q_pos, K_all, V_all, sel, T)
+    assert np.abs(got - ref).max() <= 1e-12

@@ -96,3 +96,41 @@ def test_unmutated_pins_pass():
     """The same pin calls pass on the real oracle (so the failures above are the mutations')."""
     for _, _, _, pin in MUTATIONS:
         pin()
+
+
+# Mistakes planted in the oracle's Python layer (the loops over pools, sequences,
+# KV heads and query heads), each against the pin that must catch it.
+PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+PY_MUTATIONS = [
+    ("query heads interleaved over KV heads", "hq = h * G + g", "hq = g * n_kv_heads + h",
+     lambda m: PT.test_decode_batches_kv_heads_and_groups(m)),
+    ("block id with heads outermost", "fid = (s * n_kv_heads + h) * blocks_per_seq + b",
+     "fid = (h * batch + s) * blocks_per_seq + b", lambda m: PT.test_decode_batches_kv_heads_and_groups(m)),
+    ("first sequence's selection for every sequence", "else [int(b) for b in sel[s]]",
+     "else [int(b) for b in sel[0]]", lambda m: PT.test_decode_batches_kv_heads_and_groups(m)),
+    ("first pool's budget for every pool", "int(budgets[p]), eps2, policy, seed, p)",
+     "int(budgets[0]), eps2, policy, seed, p)", lambda m: PA.test_compress_several_pools(m)),
+]
+
+
+@pytest.mark.parametrize("name,old,new,pin", PY_MUTATIONS, ids=[m[0] for m in PY_MUTATIONS])
+def test_pin_catches_python_mutation(name, old, new, pin):
+    import importlib.util
+    import sys
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    spec = importlib.util.spec_from_loader("oracle_mutant", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__file__ = PY_SRC  # so that it loads the same liboracle.so
+    sys.modules["oracle_mutant"] = mod
+    try:
+        exec(compile(src.replace(old, new), PY_SRC, "exec"), mod.__dict__)
+        with pytest.raises(AssertionError):
+            pin(mod)
+    finally:
+        del sys.modules["oracle_mutant"]
+
+
+def test_unmutated_python_pins_pass():
+    for _, _, _, pin in PY_MUTATIONS:
+        pin(oracle)
