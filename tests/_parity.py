@@ -10,13 +10,15 @@ from block_wise_rank_amd import (Factors, milo_arena_bytes, milo_compress_blocks
                                  milo_reconstruct)
 from synthetic import pool_layout
 
-# |sigma_gpu - sigma_oracle| <= SIGMA_REL * max(sigma_oracle, eps): relative 1e-3
-# for every singular value above eps, absolute 1e-3 * eps below it.  Below eps
-# the Gram-based solve in fp32 cannot promise 1e-3 relative: its backward error
-# is ~u * sigma_max^2 (u = 2^-24), which moves sigma by ~u sigma_max^2 / (2 sigma),
-# i.e. 1e-3 relative only for sigma above ~0.005 sigma_max.  Where a pool's
-# budget cutoff falls below eps (short blocks, whose noise singular values reach
-# below eps) the selected values under eps are reported, not asserted.
+# Singular values: |sigma_gpu - sigma_oracle| <= SIGMA_REL * sigma_oracle for
+# every sigma >= eps (relative 1e-3); below eps, where the gain
+# log(1 + sigma^2/eps^2) ~ sigma^2/eps^2 is what the allocation reads, the bound
+# is on sigma^2: |sigma_gpu^2 - sigma_oracle^2| <= 2 SIGMA_REL eps^2 (the gain to
+# 2e-3; continuous with the relative bound at sigma = eps).  The eigensolve works
+# on the fp32 Gram, whose backward error ~u sigma_max^2 (u = 2^-24) moves sigma^2
+# by that much whatever sigma is, so no bound on sigma itself holds as sigma -> 0
+# (128-token blocks have noise singular values down to ~1e-4).  Where a pool's
+# budget cutoff falls below eps the selected values there are reported too.
 SIGMA_REL = 1e-3
 # 4-bit: the factors agree with the oracle's to ~1e-3, and an entry that close
 # to a rounding boundary moves by a whole step s = max|run| / 7 (about a third
@@ -59,12 +61,16 @@ def pool_cutoffs(sig_ora: np.ndarray, pool_ptr, r_ora) -> np.ndarray:
 
 
 def check_sigma(sig_gpu: np.ndarray, sig_ora: np.ndarray, eps: float, pool_ptr=None, r_ora=None):
-    """Every singular value within SIGMA_REL * max(sigma_oracle, eps) (see above).
+    """Every singular value within the bound above (relative 1e-3 from eps up, on
+    sigma^2 below).
     With the pool table and the oracle's ranks, the relative error of the selected
     values below eps is printed as well."""
-    bound = SIGMA_REL * np.maximum(sig_ora, eps)
+    sig_gpu = np.asarray(sig_gpu, dtype=np.float64)
     err = np.abs(sig_gpu - sig_ora)
-    worst = float((err / bound).max())
+    above = sig_ora >= eps
+    ratio = np.where(above, err / (SIGMA_REL * np.maximum(sig_ora, eps)),
+                     np.abs(sig_gpu ** 2 - sig_ora ** 2) / (2 * SIGMA_REL * eps * eps))
+    worst = float(ratio.max())
     rel = err / np.maximum(sig_ora, eps)
     for lo, hi in [(0.1, np.inf), (eps, 0.1), (0.0, eps)]:
         m = (sig_ora >= lo) & (sig_ora < hi)
@@ -86,8 +92,9 @@ def check_objective(obj_gpu, sig_gpu, r_gpu, obj_ora, sig_ora, r_ora, pool_ptr, 
     """The GPU objective is the sum of log(1 + sigma^2/eps^2) over the ranks it handed
     out (recomputed here from its own outputs), and it is within the bound the
     sigma tolerance implies of the oracle's objective: each gain moves by at most
-    2 |d sigma| sigma / (eps^2 + sigma^2) <= 2 SIGMA_REL, and a +-1 swap at the
-    cutoff trades two gains whose singular values agree to 2 SIGMA_REL."""
+    |d sigma^2| / (eps^2 + sigma^2) <= 2 SIGMA_REL max(sigma, eps)^2 / (eps^2 + sigma^2)
+    <= 2 SIGMA_REL, and a +-1 swap at the cutoff trades two gains whose singular
+    values agree to 2 SIGMA_REL."""
     eps = np.sqrt(eps2)
     for p in range(len(pool_ptr) - 1):
         lo, hi = pool_ptr[p], pool_ptr[p + 1]
@@ -97,7 +104,8 @@ def check_objective(obj_gpu, sig_gpu, r_gpu, obj_ora, sig_ora, r_ora, pool_ptr, 
         bound = 0.0
         for b in range(lo, hi):
             s = sig_ora[b, :int(r_gpu[b])]
-            bound += (2 * SIGMA_REL * np.maximum(s, eps) * s / (eps2 + s ** 2)).sum()
+            # |d sigma^2| <= 2 SIGMA_REL sigma^2 from eps up, 2 SIGMA_REL eps^2 below
+            bound += (2 * SIGMA_REL * np.maximum(s, eps) ** 2 / (eps2 + s ** 2)).sum()
         n_swap = int(np.abs(np.asarray(r_gpu[lo:hi]) - np.asarray(r_ora[lo:hi])).sum())
         bound += 4 * SIGMA_REL * n_swap
         assert abs(obj_gpu[p] - obj_ora[p]) <= bound + 1e-9 * abs(obj_ora[p]), \
