@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     milo_compress_blocks_ex,
     milo_compress_workspace_bytes,
     milo_decode_attention,
+    milo_decode_attention_noalloc,
     milo_fetch_blocks,
     milo_profile_enable,
     milo_profile_read,
@@ -31,6 +32,6 @@ __all__ = [
     "Factors", "MiloError", "NotConvergedError", "decode_workspace_bytes", "milo_abi_version", "milo_allocate_ranks",
     "milo_allocate_ranks_ex", "milo_arena_bytes", "milo_compress_blocks", "milo_compress_blocks_ex",
     "milo_compress_workspace_bytes",
-    "milo_decode_attention", "milo_fetch_blocks", "milo_profile_enable", "milo_profile_read", "milo_reconstruct",
+    "milo_decode_attention", "milo_decode_attention_noalloc", "milo_fetch_blocks", "milo_profile_enable", "milo_profile_read", "milo_reconstruct",
     "reconstruct_then_attend",
 ]

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmilo.so"
 MILO_OK, MILO_E_INVALID, MILO_E_UNSUPPORTED, MILO_E_WORKSPACE, MILO_E_HIP = range(5)
 MILO_F32, MILO_BF16, MILO_I8, MILO_I4 = 0, 1, 2, 3
 MILO_ALLOC_ENTROPY, MILO_ALLOC_UNIFORM, MILO_ALLOC_RANDOM = 0, 1, 2
+MILO_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -68,6 +69,7 @@ SIGNATURES = {
                                          _i32, _vp]),
     "milo_decode_attention": (ctypes.c_int, [ctypes.POINTER(milo_decode_args),
                                              ctypes.POINTER(ctypes.c_size_t), _vp]),
+    "milo_decode_attention_noalloc": (ctypes.c_int, [ctypes.POINTER(milo_decode_args), _vp]),
     "milo_arena_bytes": (ctypes.c_size_t, [ctypes.c_int, _i32, _i32, _vp, _i32, _vp]),
     "milo_compress_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
     "milo_profile_enable": (ctypes.c_int, [ctypes.c_int]),

@@ -393,6 +393,39 @@ def milo_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: F
     _check(st)
 
 
+def milo_decode_attention_noalloc(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: Factors,
+                                  blocks_per_seq: int, n_kv_heads: int, out: torch.Tensor,
+                                  sel_ptr: torch.Tensor | None = None, sel_blk: torch.Tensor | None = None,
+                                  sel_max: int = 0, tail_k: torch.Tensor | None = None,
+                                  tail_v: torch.Tensor | None = None, tail_len: torch.Tensor | None = None,
+                                  tail_pos0: torch.Tensor | None = None, rope_base: float = 1e6,
+                                  softmax_scale: float | None = None, split_len: int = 0,
+                                  stream=None) -> None:
+    """milo_decode_attention with the library's static per-GPU scratch instead of
+    a workspace: nothing is allocated (for callers that cannot allocate)."""
+    batch, n_q, d = q.shape
+    _need(q, "q")
+    _need(q_pos, "q_pos", torch.int64, batch)
+    _need(out, "out", None, batch * n_q * d)
+    _need(sel_ptr, "sel_ptr", torch.int32, batch + 1, optional=True)
+    _need(sel_blk, "sel_blk", torch.int32, optional=True)
+    _need(tail_k, "tail_k", None, optional=True)
+    _need(tail_v, "tail_v", None, optional=True)
+    _need(tail_len, "tail_len", torch.int32, batch, optional=tail_k is None)
+    _need(tail_pos0, "tail_pos0", torch.int64, batch, optional=tail_k is None)
+    ks, vs = k.struct(), v.struct()
+    tail_cap = 0 if tail_k is None else int(tail_k.shape[2])
+    args = C.milo_decode_args(
+        _p(q), _dtype_code(q.dtype), _p(q_pos), batch, n_q, int(n_kv_heads), d,
+        ctypes.pointer(ks), ctypes.pointer(vs), int(blocks_per_seq), _p(sel_ptr), _p(sel_blk),
+        int(sel_max), _p(tail_k), _p(tail_v),
+        _dtype_code(tail_k.dtype) if tail_k is not None else C.MILO_BF16, tail_cap,
+        _p(tail_len), _p(tail_pos0), float(rope_base),
+        float(softmax_scale if softmax_scale is not None else d ** -0.5), _p(out),
+        _dtype_code(out.dtype), int(split_len), None, 0)
+    _check(lib().milo_decode_attention_noalloc(ctypes.byref(args), _stream(stream)))
+
+
 def reconstruct_then_attend(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: Factors,
                             blocks_per_seq: int, n_kv_heads: int, out: torch.Tensor,
                             staging_k: torch.Tensor | None = None,

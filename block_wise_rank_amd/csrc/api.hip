@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -496,8 +497,14 @@ milo_status milo_fetch_blocks(const milo_factors *host, const milo_factors *dev,
     return ok();
 }
 
-milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_needed,
-                                  void *stream) {
+}  // extern "C"
+
+namespace {
+
+// milo_decode_attention's work with the scratch given explicitly: `ws` of
+// `ws_bytes` bytes (the caller's workspace, or this device's static scratch).
+milo_status decode_attention(const milo_decode_args *a, size_t *workspace_needed, void *ws, size_t ws_bytes,
+                             void *stream) {
     if (!a) return fail(MILO_E_INVALID, "args is NULL");
     if (a->head_dim != kD) return fail(MILO_E_UNSUPPORTED, "head_dim must be 128 (got %d)", a->head_dim);
     if (a->batch < 0) return fail(MILO_E_INVALID, "batch must be >= 0");
@@ -606,13 +613,13 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
 
     const size_t need = milo::decode_workspace_bytes(p);
     if (workspace_needed) *workspace_needed = need;
-    if (!a->workspace || a->workspace_bytes < need)
-        return fail(MILO_E_WORKSPACE, "workspace of %zu bytes needed", need);
-    if (!aligned(a->workspace, 256)) return fail(MILO_E_INVALID, "workspace must be 256-byte aligned");
+    if (!ws || ws_bytes < need)
+        return fail(MILO_E_WORKSPACE, "workspace of %zu bytes needed (%zu given)", need, ws ? ws_bytes : 0);
+    if (!aligned(ws, 256)) return fail(MILO_E_INVALID, "workspace must be 256-byte aligned");
     const size_t n = static_cast<size_t>(p.batch) * p.n_kv_heads * p.n_splits * G;
-    p.part_ml = static_cast<float *>(a->workspace);
-    p.part_o = reinterpret_cast<float *>(static_cast<uint8_t *>(a->workspace) + align_up(n * 2 * sizeof(float), 256));
-    uint8_t *tabs = static_cast<uint8_t *>(a->workspace) + milo::decode_workspace_bytes(p) - milo::decode_table_bytes();
+    p.part_ml = static_cast<float *>(ws);
+    p.part_o = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + align_up(n * 2 * sizeof(float), 256));
+    uint8_t *tabs = static_cast<uint8_t *>(ws) + milo::decode_workspace_bytes(p) - milo::decode_table_bytes();
     p.theta = reinterpret_cast<double *>(tabs);
     p.rope_tab = reinterpret_cast<float2 *>(tabs + 64 * sizeof(double));
     p.step_tab = p.rope_tab + 32 * 64;
@@ -630,6 +637,56 @@ milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_n
     if ((e = timed("decode_combine", s, [&] { return milo::launch_decode_combine(p, s); })) != hipSuccess)
         return hip_fail(e, "decode combine launch");
     return ok();
+}
+
+// Scratch of milo_decode_attention_noalloc: a static device array, so that the
+// entry point never allocates.  Every GPU the library runs on holds its own copy
+// for the life of the process.  In host code `scratch` only names the symbol;
+// its device address, per device, comes from hipGetSymbolAddress and is kept
+// here, set once per device on the first call there.
+constexpr size_t kScratchBytes = MILO_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+milo_status device_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MILO_E_UNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MILO_E_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MILO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_needed, void *stream) {
+    if (!a) return fail(MILO_E_INVALID, "args is NULL");
+    return decode_attention(a, workspace_needed, a->workspace, a->workspace_bytes, stream);
+}
+
+milo_status milo_decode_attention_noalloc(const milo_decode_args *a, void *stream) {
+    if (!a) return fail(MILO_E_INVALID, "args is NULL");
+    void *ws = nullptr;
+    if (milo_status st = device_scratch(&ws); st != MILO_OK) return st;
+    size_t need = 0;
+    const milo_status st = decode_attention(a, &need, ws, kScratchBytes, stream);
+    if (st == MILO_E_WORKSPACE)
+        return fail(MILO_E_WORKSPACE, "the call needs %zu bytes of scratch; milo_decode_attention_noalloc "
+                    "has %zu (MILO_NOALLOC_SCRATCH_BYTES)", need, kScratchBytes);
+    return st;
 }
 
 int milo_profile_enable(int on) {

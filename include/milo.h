@@ -309,6 +309,27 @@ typedef struct milo_decode_args {
 milo_status milo_decode_attention(const milo_decode_args *a, size_t *workspace_needed,
                                   void *stream);
 
+/*
+ * milo_decode_attention_noalloc -- milo_decode_attention for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, kernels and results
+ * as milo_decode_attention, except that a->workspace and a->workspace_bytes are
+ * ignored: the scratch (split partials and RoPE tables) is a static device
+ * array of MILO_NOALLOC_SCRATCH_BYTES per GPU, held by every GPU the library
+ * runs on until the process ends.  The call allocates nothing (its first call
+ * on a device looks up that device's array address, once).
+ *  - A call that needs more scratch than that returns MILO_E_WORKSPACE and
+ *    enqueues nothing; milo_last_error() gives the size it needs (the default
+ *    split of every supported geometry with up to 16 x 2 KV heads x 64 blocks
+ *    of 2048 tokens and 8 query heads per KV head needs about 8.5 MiB).
+ *  - Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *    GPU (different streams, or other host threads) race and must not be
+ *    issued; calls ordered on one stream are fine.  Nothing in the array needs
+ *    to start at zero: each call writes every partial it reads.
+ */
+#define MILO_NOALLOC_SCRATCH_BYTES (32u << 20)
+milo_status milo_decode_attention_noalloc(const milo_decode_args *a, void *stream);
+
 /* Arena bytes for a factor set: sum over pools of min(R_p, n_p * min(T, d))
  * ranks, each costing (block_len + head_dim) elements of dtype.  Host only.
  * Returns 0 and sets the last error on invalid input. */
