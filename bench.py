@@ -60,6 +60,10 @@ def parse():
                     help="rocprofv3 counter_collection.csv of the bench with SQ_INSTS_VALU_MFMA_MOPS_BF16, "
                          "SQ_INSTS_VALU_MFMA_MOPS_F32, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE -> "
                          "profiles/<kernel>_mfma.json (no GPU)")
+    ap.add_argument("--compress-streams", type=int, default=1,
+                    help="streams the compression calls of a step alternate between (1 or 2)")
+    ap.add_argument("--compress-chunks", type=int, default=1,
+                    help="compression calls per kind (runs of whole layers)")
     ap.add_argument("--extra", default="2,1",
                     help="other workloads measured after the main one (config indices, or 'none'): "
                          "multi-layer ones as whole steps, one-layer ones warm and cold")
@@ -342,7 +346,7 @@ def jacobi_executed_flops_per_sweep(d=128):
 
 
 def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=True, want_offload=True,
-                 want_cpu=True, counters=True):
+                 want_cpu=True, counters=True, compress_streams=1, compress_chunks=1):
     """Generate the workload's inputs in HBM, time `steps` whole steps (compress
     every K and V block of every layer, then one decode step of every layer) and
     price every kernel against its roofline.  Returns the result dict."""
@@ -397,9 +401,34 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     F = {k: milo.Factors.alloc(fdt, n_all, T, d, arena_bytes, device=dev) for k in ("k", "v")}
     sigma = {k: torch.empty((n_all, d), dtype=torch.float32, device=dev) for k in ("k", "v")}
     sweeps = {k: torch.empty(n_all, dtype=torch.int32, device=dev) for k in ("k", "v")}
-    ws_bytes = milo.milo_compress_workspace_bytes(n_all, T, d)
+    # Compression calls: one per kind over every layer, or `compress_chunks` calls
+    # per kind over runs of whole layers; with two streams, consecutive calls
+    # alternate between them (each stream its own workspace), so that one call's
+    # HBM-bound passes can share the chip with another's eigensolve.  A chunk's
+    # factors sit in its own slice of the arena (offsets relative to the slice).
+    chunks = max(1, min(compress_chunks, L))
+    bounds = [round(i * L / chunks) for i in range(chunks + 1)]
+    layer_bytes = arena_bytes // L  # pools are identical per layer
+    CF = {k: [] for k in ("k", "v")}
+    for k in ("k", "v"):
+        for c in range(chunks):
+            l0, l1 = bounds[c], bounds[c + 1]
+            f = F[k].view(l0 * nb_layer, (l1 - l0) * nb_layer)
+            f.arena = F[k].arena[l0 * layer_bytes:l1 * layer_bytes] if chunks > 1 else F[k].arena
+            CF[k].append((l0, l1, f))
+    calls = [(k, c) for c in range(chunks) for k in ("k", "v")]
+    side = torch.cuda.Stream() if compress_streams > 1 else None
+    ws_blocks = max((l1 - l0) for l0, l1, _ in CF["k"]) * nb_layer
+    ws_bytes = milo.milo_compress_workspace_bytes(ws_blocks, T, d)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if side is not None else None
     outs = [torch.empty((cfg.batch, Hq, d), dtype=xdt, device=dev) for _ in range(L)]
+
+    def layer_factors(kind, layer):
+        for l0, l1, f in CF[kind]:
+            if l0 <= layer < l1:
+                return f.view((layer - l0) * nb_layer, nb_layer)
+        raise IndexError(layer)
 
     def decode_kw(layer):
         kw = dict(sel_kw)
@@ -408,20 +437,34 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
         return kw
 
     def decode_layer(layer, dws):
-        milo.milo_decode_attention(Q[layer], q_pos, F["k"].view(layer * nb_layer, nb_layer),
-                                   F["v"].view(layer * nb_layer, nb_layer), cfg.blocks_per_seq, H,
-                                   outs[layer], workspace=dws, **decode_kw(layer))
+        milo.milo_decode_attention(Q[layer], q_pos, layer_factors("k", layer), layer_factors("v", layer),
+                                   cfg.blocks_per_seq, H, outs[layer], workspace=dws, **decode_kw(layer))
 
-    dws_bytes = milo.decode_workspace_bytes(Q[0], F["k"].view(0, nb_layer), F["v"].view(0, nb_layer),
+    dws_bytes = milo.decode_workspace_bytes(Q[0], layer_factors("k", 0), layer_factors("v", 0),
                                             cfg.blocks_per_seq, H, outs[0], q_pos=q_pos, **decode_kw(0))
     dws = torch.empty(dws_bytes, dtype=torch.uint8, device=dev)
+    main_stream = torch.cuda.current_stream()
+
+    def compress_all():
+        if side is not None:
+            side.wait_stream(main_stream)
+        for i, (kind, c) in enumerate(calls):
+            l0, l1, f = CF[kind][c]
+            lo, n = l0 * nb_layer, (l1 - l0) * nb_layer
+            p0 = l0 * len(bud1)
+            npl = (l1 - l0) * len(bud1)
+            ppc = [pp[p0 + j] - pp[p0] for j in range(npl + 1)]
+            st = main_stream if (side is None or i % 2 == 0) else side
+            milo.milo_compress_blocks(X[kind][lo:lo + n], ppc, bud[p0:p0 + npl], cfg.eps2,
+                                      sigma[kind][lo:lo + n], f, sweeps_out=sweeps[kind][lo:lo + n],
+                                      workspace=ws if st is main_stream else ws2, stream=st)
+        if side is not None:
+            main_stream.wait_stream(side)
 
     def step(record=None):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ev[0].record()
-        for kind in ("k", "v"):
-            milo.milo_compress_blocks(X[kind], pp, bud, cfg.eps2, sigma[kind], F[kind],
-                                      sweeps_out=sweeps[kind], workspace=ws)
+        compress_all()
         ev[1].record()
         for layer in range(L):
             decode_layer(layer, dws)
@@ -476,9 +519,8 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
         outs2 = torch.empty((cfg.batch, Hq, d), dtype=xdt, device=dev)
 
         def rebuild_layer(layer):
-            milo.reconstruct_then_attend(Q[layer], q_pos, F["k"].view(layer * nb_layer, nb_layer),
-                                         F["v"].view(layer * nb_layer, nb_layer), cfg.blocks_per_seq, H,
-                                         outs2, staging_k=stg[0], staging_v=stg[1])
+            milo.reconstruct_then_attend(Q[layer], q_pos, layer_factors("k", layer), layer_factors("v", layer),
+                                         cfg.blocks_per_seq, H, outs2, staging_k=stg[0], staging_v=stg[1])
         rebuild_layer(0)
         torch.cuda.synchronize()
         milo.milo_profile_read()
@@ -506,7 +548,8 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     # bf16 KV cache the same way
     offload = None
     if want_offload:
-        offload = offload_measure(milo, torch, np, cfg, F, X, Q, q_pos, sel, nb_layer, fdt, xdt, dev)
+        offload = offload_measure(milo, torch, np, cfg, layer_factors, X, Q, q_pos, sel, nb_layer, fdt, xdt,
+                                  dev)
 
     # ---------------- algorithmic work per kernel launch ----------------
     ranks = {k: F[k].rank.to(torch.int64) for k in ("k", "v")}
@@ -634,7 +677,8 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
                    "n_q_heads": Hq, "head_dim": d, "block_len": T, "blocks_per_seq": cfg.blocks_per_seq,
                    "batch": cfg.batch, "attended_blocks_per_seq": cfg.attended_blocks,
                    "tail_len": cfg.tail_len, "budget_frac": cfg.budget_fracs[0], "factor_dtype": fdt,
-                   "context_tokens_per_step": ctx_tokens, "blocks_compressed_per_step": n_blocks_step},
+                   "context_tokens_per_step": ctx_tokens, "blocks_compressed_per_step": n_blocks_step,
+                   "compress_calls_per_step": len(calls), "compress_streams": 1 if side is None else 2},
         "breakdown": {
             "compress_ms": round(comp_ms, 3), "decode_ms": round(dec_ms, 3),
             "blocks_per_s": n_blocks_step / (comp_ms / 1e3),
@@ -683,23 +727,37 @@ def run_warm_cold(cfg, fdt, iters=20, copies=16):
     xe = 4 if cfg.storage == "f32" else 2
     xname = "f32" if xe == 4 else "bf16"
 
+    ws2 = torch.empty_like(ws)
+    side = torch.cuda.Stream()
+    main_stream = torch.cuda.current_stream()
+    streams = {"k": main_stream, "v": main_stream}
+
     def comp(src):
+        if streams["v"] is not main_stream:
+            side.wait_stream(main_stream)
         for k in ("k", "v"):
-            milo.milo_compress_blocks(src[k], pp, bud, cfg.eps2, sig[k], F[k], workspace=ws)
+            milo.milo_compress_blocks(src[k], pp, bud, cfg.eps2, sig[k], F[k],
+                                      workspace=ws if streams[k] is main_stream else ws2, stream=streams[k])
+        if streams["v"] is not main_stream:
+            main_stream.wait_stream(side)
 
     res = {"workload": cfg.workload, "blocks_per_iteration": 2 * n, "iterations": iters,
            "input_bytes_per_iteration": 2 * X["k"].numel() * X["k"].element_size(),
            "cold_copies": copies, "cold_bytes": copies * 2 * X["k"].numel() * X["k"].element_size()}
-    for mode in ("warm", "cold"):
+    # warm / cold: K then V on one stream; warm_two_streams: the K and V calls on
+    # two streams, so that their eigensolves (one workgroup per block, far fewer
+    # blocks than CUs) run side by side
+    for mode in ("warm", "cold", "warm_two_streams"):
+        streams["v"] = side if mode == "warm_two_streams" else main_stream
         for i in range(3):
-            comp(X if mode == "warm" else {k: cold[k][i % copies] for k in ("k", "v")})
+            comp(X if mode != "cold" else {k: cold[k][i % copies] for k in ("k", "v")})
         torch.cuda.synchronize()
         milo.milo_profile_read()
         milo.milo_profile_enable(True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(iters):
-            comp(X if mode == "warm" else {k: cold[k][i % copies] for k in ("k", "v")})
+            comp(X if mode != "cold" else {k: cold[k][i % copies] for k in ("k", "v")})
         e1.record()
         torch.cuda.synchronize()
         prof = milo.milo_profile_read()
@@ -777,7 +835,8 @@ def main():
     cfg = CONFIGS[args.config]
     fdt = args.factor_dtype or cfg.storage
     main_res = run_workload(cfg, fdt, args.steps, args.warmup, decode_only_steps=args.decode_only_steps,
-                            want_offload=not args.no_offload, want_cpu=not args.no_cpu_baseline)
+                            want_offload=not args.no_offload, want_cpu=not args.no_cpu_baseline,
+                            compress_streams=args.compress_streams, compress_chunks=args.compress_chunks)
     torch.cuda.empty_cache()
     extra = {}
     for c in [int(x) for x in args.extra.split(",") if x.strip()] if args.extra != "none" else []:
@@ -820,7 +879,7 @@ def main():
     return 0
 
 
-def offload_measure(milo, torch, np, cfg, F, X, Q, q_pos, sel, nb_layer, fdt, xdt, dev, n_src=2):
+def offload_measure(milo, torch, np, cfg, layer_factors, X, Q, q_pos, sel, nb_layer, fdt, xdt, dev, n_src=2):
     """Decode over all layers with the cache in pinned host memory.  n_src
     distinct layers are held on the host and cycled through (the copies do not
     depend on the bytes); two device buffers alternate, the copy stream filling
@@ -838,9 +897,9 @@ def offload_measure(milo, torch, np, cfg, F, X, Q, q_pos, sel, nb_layer, fdt, xd
     ids_t = torch.tensor(ids, dtype=torch.int32)
     es = {"f32": 4, "bf16": 2, "i8": 1, "i4": 5 / 8}[fdt]
 
-    def layer_host_set(f, layer):
+    def layer_host_set(kind, layer):
         """A compact pinned-host copy of one layer's factor set (offsets rebased)."""
-        v = f.view(layer * nb_layer, nb_layer)
+        v = layer_factors(kind, layer)
         lo = int(v.a_off.min())
         hi = int((v.b_off + (v.rank.to(torch.int64) * int(d * es))).max())
         h = milo.Factors(fdt, nb_layer, T, d, rank=v.rank.cpu().pin_memory(), a_off=(v.a_off - lo).cpu().pin_memory(),
@@ -879,8 +938,8 @@ def offload_measure(milo, torch, np, cfg, F, X, Q, q_pos, sel, nb_layer, fdt, xd
 
     # compressed: the factor sets of n_src layers on the host (each with its own
     # layout, whose device copy of the metadata the device buffer takes on)
-    hk = [layer_host_set(F["k"], l) for l in range(n_src)]
-    hv = [layer_host_set(F["v"], l) for l in range(n_src)]
+    hk = [layer_host_set("k", l) for l in range(n_src)]
+    hv = [layer_host_set("v", l) for l in range(n_src)]
     meta = [(hk[i].like(dev), hv[i].like(dev)) for i in range(n_src)]
     cap_k = max(h.arena.numel() for h in hk)
     cap_v = max(h.arena.numel() for h in hv)

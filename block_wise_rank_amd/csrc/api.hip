@@ -109,9 +109,12 @@ size_t tables_bytes(int n_pools) {
     return align_up(sizeof(int32_t) * (n_pools + 1), 256) + align_up(sizeof(int64_t) * n_pools, 256) * 2;
 }
 
+// Per block: the sorted order of its eigenvectors and their scales (refine -> project).
+constexpr size_t kOrder = sizeof(int32_t) * kD + sizeof(float) * kD;
+
 size_t chunk_bytes(int n_blocks, int block_len) {
     const int s = gram_splits(n_blocks, block_len);
-    return static_cast<size_t>(n_blocks) * (s + 1) * kMat;
+    return static_cast<size_t>(n_blocks) * ((s + 1) * kMat + kOrder);
 }
 
 milo_status check_pools(const int32_t *pool_ptr, int32_t n_pools, const int64_t *budget,
@@ -261,8 +264,8 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
     const size_t full = tab + chunk_bytes(in->n_blocks, in->block_len);
     int max_pool = 0;
     for (int p = 0; p < n_pools; ++p) max_pool = std::max(max_pool, pool_ptr[p + 1] - pool_ptr[p]);
-    // a chunk needs at least one Gram partial and the eigenvectors per block
-    const size_t minimum = tab + static_cast<size_t>(max_pool) * 2 * kMat;
+    // a chunk needs at least one Gram partial, the eigenvectors and their order per block
+    const size_t minimum = tab + static_cast<size_t>(max_pool) * (2 * kMat + kOrder);
     if (!workspace || *workspace_bytes < minimum) {
         *workspace_bytes = full;
         return fail(MILO_E_WORKSPACE, "workspace of %zu bytes needed (minimum %zu)", full, minimum);
@@ -307,16 +310,19 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
         // grow the chunk while its workspace fits
         int p1 = p0 + 1;
         while (p1 < n_pools &&
-               static_cast<size_t>(pool_ptr[p1 + 1] - pool_ptr[p0]) * 2 * kMat <= chunk_cap)
+               static_cast<size_t>(pool_ptr[p1 + 1] - pool_ptr[p0]) * (2 * kMat + kOrder) <= chunk_cap)
             ++p1;
         const int b0 = pool_ptr[p0], nb = pool_ptr[p1] - b0;
         if (nb > 0) {
             // Gram token splits: enough workgroups to fill the chip, within the workspace.
-            const int fit = static_cast<int>(chunk_cap / (static_cast<size_t>(nb) * kMat)) - 1;
+            const int fit = static_cast<int>((chunk_cap - static_cast<size_t>(nb) * kOrder) /
+                                             (static_cast<size_t>(nb) * kMat)) - 1;
             int splits = gram_splits(nb, T);
             while (splits > 1 && splits > fit) splits /= 2;  // powers of two keep T / splits % 64 == 0
             float *gpart = reinterpret_cast<float *>(chunk_ws);
             float *vt = reinterpret_cast<float *>(chunk_ws + static_cast<size_t>(nb) * splits * kMat);
+            int32_t *vperm = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(vt) + static_cast<size_t>(nb) * kMat);
+            float *vscale = reinterpret_cast<float *>(vperm + static_cast<size_t>(nb) * kD);
             // block b of the chunk: row0 points into the caller's table, else blocks back to back
             const int64_t *row0 = in->row0 ? in->row0 + b0 : nullptr;
             const void *xc = in->row0 ? static_cast<const void *>(xb)
@@ -329,7 +335,7 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
                                                 kMaxSweeps, kJacobiTol, kJacobiStopTol, s);
                  })) != hipSuccess)
                 return hip_fail(e, "jacobi launch");
-            if ((e = timed("refine", s, [&] { return milo::launch_refine(xc, x_type, row0, in->row_stride, T, nb, vt, sig, s); })) != hipSuccess)
+            if ((e = timed("refine", s, [&] { return milo::launch_refine(xc, x_type, row0, in->row_stride, T, nb, vt, sig, vperm, vscale, s); })) != hipSuccess)
                 return hip_fail(e, "refine launch");
             if ((e = timed("alloc", s, [&] {
                      return milo::launch_alloc(sig, kD, k, d_pool_ptr, d_budget, d_base, p0, p1 - p0, b0,
@@ -339,7 +345,7 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
                 return hip_fail(e, "alloc launch");
             if ((e = timed("project", s, [&] {
                      return milo::launch_project(
-                         xc, x_type, row0, in->row_stride, T, nb, vt, out->rank + b0, out->a_off + b0,
+                         xc, x_type, row0, in->row_stride, T, nb, vt, vperm, vscale, out->rank + b0, out->a_off + b0,
                          out->b_off + b0, out->arena, f_type,
                          out->a_scale ? out->a_scale + static_cast<size_t>(b0) * T : nullptr,
                          out->b_scale ? out->b_scale + static_cast<size_t>(b0) * kD : nullptr, s);

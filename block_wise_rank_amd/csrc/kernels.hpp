@@ -28,11 +28,13 @@ hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t r
 hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt,
                          int32_t *sweeps, int max_sweeps, float tol, float stop_tol, hipStream_t st);
 
-// sigma_i = ||X_b v_i|| in fp32-accurate arithmetic, then eigenvectors sorted
-// by descending sigma (in place in vt) with the largest-magnitude entry of each
-// made positive; sigma[b][0..128) descending.
+// sigma_i = ||X_b v_i|| in fp32-accurate arithmetic, sorted descending into
+// sigma[b][0..128); perm[b][k] = the eigenvector (row of vt[b]) of sorted rank k
+// and scale[b][k] = its sign (largest-magnitude entry made positive) / ||v||:
+// sorted row k of V^T is scale[b][k] * vt[b][perm[b][k]][:].
 hipError_t launch_refine(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
-                         int block_len, int n_blocks, float *vt, float *sigma, hipStream_t st);
+                         int block_len, int n_blocks, const float *vt, float *sigma, int32_t *perm,
+                         float *scale, hipStream_t st);
 
 // Rank allocation for pools [pool_lo, pool_lo + n_pools) of the device pool
 // tables under `policy` (seed: the random policy's generator seed): ranks of
@@ -45,10 +47,12 @@ hipError_t launch_alloc(const float *sigma, int sigma_pitch, int max_rank,
                         double *objective, int64_t *a_off, int64_t *b_off, int a_bpr,
                         int b_bpr, int policy, uint64_t seed, hipStream_t st);
 
-// Factor pairs from sorted eigenvectors and ranks: A_b^T (rank-major) and B_b
+// Factor pairs from the eigenvectors (sorted rank k = scale[b][k] *
+// vt[b][perm[b][k]], see launch_refine) and ranks: A_b^T (rank-major) and B_b
 // rows into the arena, plus INT8 scales.
 hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
-                          int block_len, int n_blocks, const float *vt, const int32_t *rank,
+                          int block_len, int n_blocks, const float *vt, const int32_t *perm,
+                          const float *vscale, const int32_t *rank,
                           const int64_t *a_off, const int64_t *b_off, void *arena,
                           int out_type, float *a_scale, float *b_scale, hipStream_t st);
 

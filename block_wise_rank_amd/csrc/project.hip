@@ -65,7 +65,8 @@ __device__ __forceinline__ void store_b_i4(const float (&v)[8][8], int i, int r,
 template <int NX, int OUT>
 __global__ __launch_bounds__(256) void project_kernel(
     const void *__restrict__ x, const int64_t *__restrict__ row0, int64_t row_stride, int T,
-    const float *__restrict__ vt, const int32_t *__restrict__ rank,
+    const float *__restrict__ vt, const int32_t *__restrict__ perm, const float *__restrict__ vscale,
+    const int32_t *__restrict__ rank,
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off,
     uint8_t *__restrict__ arena, float *__restrict__ a_scale, float *__restrict__ b_scale) {
     constexpr int NS = (OUT == kF32 || OUT == kI4) ? 3 : 1;  // bf16 terms of the B operand
@@ -89,15 +90,18 @@ __global__ __launch_bounds__(256) void project_kernel(
     // ---- B fragments: row i = 32 wave + lane % 32, k slots j = 16 ks + 8 (lane / 32) + e.
     const int i = 32 * wave + (lane & 31);
     const bool row_ok = i < r;
-    const float *vrow = vt + static_cast<int64_t>(blk) * kD * kD + static_cast<int64_t>(i) * kD;
+    // sorted rank i: row perm[i] of the eigensolver's output times vscale[i]
+    const int vsrc = row_ok ? perm[static_cast<int64_t>(blk) * kD + i] : 0;
+    const float vsc = row_ok ? vscale[static_cast<int64_t>(blk) * kD + i] : 0.f;
+    const float *vrow = vt + static_cast<int64_t>(blk) * kD * kD + static_cast<int64_t>(vsrc) * kD;
     float v[8][8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
         if (row_ok) {
             const float4 a = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5));
             const float4 b = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5) + 4);
-            v[ks][0] = a.x; v[ks][1] = a.y; v[ks][2] = a.z; v[ks][3] = a.w;
-            v[ks][4] = b.x; v[ks][5] = b.y; v[ks][6] = b.z; v[ks][7] = b.w;
+            v[ks][0] = a.x * vsc; v[ks][1] = a.y * vsc; v[ks][2] = a.z * vsc; v[ks][3] = a.w * vsc;
+            v[ks][4] = b.x * vsc; v[ks][5] = b.y * vsc; v[ks][6] = b.z * vsc; v[ks][7] = b.w * vsc;
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[ks][e] = 0.f;
@@ -349,7 +353,8 @@ __device__ __forceinline__ void stream_x_ring(uint8_t *ring, const uint16_t *xro
 
 __global__ __launch_bounds__(256) void project_bf16_kernel(
     const uint16_t *__restrict__ x, const int64_t *__restrict__ row0, int64_t row_stride, int T,
-    const float *__restrict__ vt, const int32_t *__restrict__ rank,
+    const float *__restrict__ vt, const int32_t *__restrict__ perm, const float *__restrict__ vscale,
+    const int32_t *__restrict__ rank,
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off, uint8_t *__restrict__ arena) {
     __shared__ __align__(16) uint8_t stage[4][32 * kStageP];
     __shared__ __align__(16) uint8_t xring[4 * kXSlot];
@@ -367,7 +372,10 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(
     // B~ fragments: rank row i = 32 wave + lane % 32, features 16 ks + 8 (lane / 32) + e
     const int i = 32 * wave + (lane & 31);
     const bool row_ok = i < r;
-    const float *vrow = vt + static_cast<int64_t>(blk) * kD * kD + static_cast<int64_t>(i) * kD;
+    // sorted rank i: row perm[i] of the eigensolver's output times vscale[i]
+    const int vsrc = row_ok ? perm[static_cast<int64_t>(blk) * kD + i] : 0;
+    const float vsc = row_ok ? vscale[static_cast<int64_t>(blk) * kD + i] : 0.f;
+    const float *vrow = vt + static_cast<int64_t>(blk) * kD * kD + static_cast<int64_t>(vsrc) * kD;
     u16x8_t fa[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -375,6 +383,8 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(
         if (row_ok) {
             a = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5));
             b = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5) + 4);
+            a = make_float4(a.x * vsc, a.y * vsc, a.z * vsc, a.w * vsc);
+            b = make_float4(b.x * vsc, b.y * vsc, b.z * vsc, b.w * vsc);
         }
         const uint32_t w0 = f32x2_to_bf16x2_bits(a.x, a.y), w1 = f32x2_to_bf16x2_bits(a.z, a.w);
         const uint32_t w2 = f32x2_to_bf16x2_bits(b.x, b.y), w3 = f32x2_to_bf16x2_bits(b.z, b.w);
@@ -439,7 +449,8 @@ constexpr int kRowP = 2 * kRunP;    // LDS floats per staged rank row (64 tokens
 template <int OUT>
 __global__ __launch_bounds__(256, 2) void project_split_kernel(
     const uint16_t *__restrict__ x, const int64_t *__restrict__ row0, int64_t row_stride, int T,
-    const float *__restrict__ vt, const int32_t *__restrict__ rank,
+    const float *__restrict__ vt, const int32_t *__restrict__ perm, const float *__restrict__ vscale,
+    const int32_t *__restrict__ rank,
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off, uint8_t *__restrict__ arena) {
     __shared__ __align__(16) float stage[4][32 * kRowP];
     __shared__ __align__(16) uint8_t xring[4 * kXSlot];
@@ -457,7 +468,10 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
     // B fragments: rank row i = 32 wave + lane % 32, features 16 ks + 8 (lane / 32) + e
     const int i = 32 * wave + (lane & 31);
     const bool row_ok = i < r;
-    const float *vrow = vt + static_cast<int64_t>(blk) * kD * kD + static_cast<int64_t>(i) * kD;
+    // sorted rank i: row perm[i] of the eigensolver's output times vscale[i]
+    const int vsrc = row_ok ? perm[static_cast<int64_t>(blk) * kD + i] : 0;
+    const float vsc = row_ok ? vscale[static_cast<int64_t>(blk) * kD + i] : 0.f;
+    const float *vrow = vt + static_cast<int64_t>(blk) * kD * kD + static_cast<int64_t>(vsrc) * kD;
     float v[8][8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -465,6 +479,8 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
         if (row_ok) {
             a = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5));
             b = *reinterpret_cast<const float4 *>(vrow + 16 * ks + 8 * (lane >> 5) + 4);
+            a = make_float4(a.x * vsc, a.y * vsc, a.z * vsc, a.w * vsc);
+            b = make_float4(b.x * vsc, b.y * vsc, b.z * vsc, b.w * vsc);
         }
         v[ks][0] = a.x; v[ks][1] = a.y; v[ks][2] = a.z; v[ks][3] = a.w;
         v[ks][4] = b.x; v[ks][5] = b.y; v[ks][6] = b.z; v[ks][7] = b.w;
@@ -574,24 +590,25 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
 }  // namespace
 
 hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
-                          int block_len, int n_blocks, const float *vt, const int32_t *rank,
+                          int block_len, int n_blocks, const float *vt, const int32_t *perm,
+                          const float *vscale, const int32_t *rank,
                           const int64_t *a_off, const int64_t *b_off, void *arena, int out_type,
                           float *a_scale, float *b_scale, hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
     if (x_type == kBF16 && out_type == kBF16) {
         const dim3 g(static_cast<unsigned>(n_blocks), static_cast<unsigned>((block_len + kPartBF - 1) / kPartBF));
         hipLaunchKernelGGL(project_bf16_kernel, g, dim3(256), 0, st, static_cast<const uint16_t *>(x), row0,
-                           row_stride, block_len, vt, rank, a_off, b_off, static_cast<uint8_t *>(arena));
+                           row_stride, block_len, vt, perm, vscale, rank, a_off, b_off, static_cast<uint8_t *>(arena));
         return hipGetLastError();
     }
     if (x_type == kBF16 && (out_type == kF32 || out_type == kI4)) {
         const dim3 g(static_cast<unsigned>(n_blocks), static_cast<unsigned>((block_len + kPartBF - 1) / kPartBF));
         if (out_type == kF32)
             hipLaunchKernelGGL(project_split_kernel<kF32>, g, dim3(256), 0, st, static_cast<const uint16_t *>(x), row0,
-                               row_stride, block_len, vt, rank, a_off, b_off, static_cast<uint8_t *>(arena));
+                               row_stride, block_len, vt, perm, vscale, rank, a_off, b_off, static_cast<uint8_t *>(arena));
         else
             hipLaunchKernelGGL(project_split_kernel<kI4>, g, dim3(256), 0, st, static_cast<const uint16_t *>(x), row0,
-                               row_stride, block_len, vt, rank, a_off, b_off, static_cast<uint8_t *>(arena));
+                               row_stride, block_len, vt, perm, vscale, rank, a_off, b_off, static_cast<uint8_t *>(arena));
         return hipGetLastError();
     }
     const dim3 grid(static_cast<unsigned>(n_blocks),
@@ -599,7 +616,7 @@ hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_
     uint8_t *ar = static_cast<uint8_t *>(arena);
 #define MILO_PROJECT(NX, OUT)                                                                     \
     hipLaunchKernelGGL((project_kernel<NX, OUT>), grid, dim3(256), 0, st, x, row0, row_stride,    \
-                       block_len, vt, rank, a_off, b_off, ar, a_scale, b_scale)
+                       block_len, vt, perm, vscale, rank, a_off, b_off, ar, a_scale, b_scale)
     if (x_type == kF32 && out_type == kF32)
         MILO_PROJECT(3, kF32);
     else if (x_type == kBF16 && out_type == kI8)

@@ -1,5 +1,5 @@
-// Singular values as sigma_i = ||X_b v_i||, then the eigenvectors sorted by
-// descending sigma with a sign convention (largest-magnitude entry positive).
+// Singular values as sigma_i = ||X_b v_i||, sorted descending, with the order
+// and a per-row scale (sign and 1/||v_i||) written for the projection.
 //
 // The eigenvalues of an fp32 Gram are only accurate to about u * ||G||, which
 // is too coarse for the small singular values (sigma^2 ~ 1e-5 next to
@@ -14,79 +14,125 @@
 // effect on ||X v|| is first order only through v . delta (relative 2^-17) and
 // otherwise second order (||X delta||^2 / 2 sigma <= sigma_0^2 2^-35 / sigma),
 // far inside the singular values' tolerance.  One workgroup (4 waves) per block;
-// wave w owns eigenvectors 32w .. 32w + 31 and keeps their fragments in
-// registers while it streams every 32-token tile of X straight from memory
-// (8 consecutive features per lane = one 16-byte load for bf16).
+// wave w owns eigenvectors 32w .. 32w + 31 and builds their fragments straight
+// from memory, keeping them in registers for the whole block.
+//
+// The eigenvectors are not rewritten: the projection reads row perm[i] of the
+// eigensolver's output for sorted rank i and multiplies it by scale[i] = sign /
+// ||v||, the same value the sorted row would have held.
+//
+// bf16 X streams through an 8-slot ring of 32-token tiles in LDS, filled by LDS
+// DMA (global_load_lds, 16 bytes per lane, no registers) seven tiles ahead of
+// use, so that a workgroup keeps 56 KiB of loads in flight: at the latency of a
+// loaded HBM that is what streaming at full bandwidth needs with two
+// workgroups per CU.  A tile is 32 unpadded 256-byte rows; a row's 16-byte
+// chunk c sits at chunk c ^ (row % 16), so the fragment reads of 16 consecutive
+// rows cover every bank.  The DMA lane that writes physical chunk p of row r
+// loads logical chunk p ^ (r % 16).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace milo {
 namespace {
 
+constexpr int kRing = 8;                 // tiles in the ring
+constexpr int kAhead = kRing - 1;        // tiles loaded ahead of use
+constexpr int kTileB = 32 * kD * 2;      // bytes of one bf16 tile
+constexpr int kDmaPerWave = kTileB / 1024 / 4;  // 1 KiB DMA instructions per wave and tile
+
+// s_waitcnt immediate: at most n vector memory operations outstanding.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+
+// Eight 16-byte LDS reads at addr[k] + off, waited for inside the same asm block.
+__device__ __forceinline__ void read8_lds(u16x8_t (&out)[8], const uint32_t (&addr)[8], uint32_t off) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    v4i r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(addr[0] + off), "v"(addr[1] + off), "v"(addr[2] + off), "v"(addr[3] + off),
+          "v"(addr[4] + off), "v"(addr[5] + off), "v"(addr[6] + off), "v"(addr[7] + off)
+        : "memory");
+    out[0] = __builtin_bit_cast(u16x8_t, r0);
+    out[1] = __builtin_bit_cast(u16x8_t, r1);
+    out[2] = __builtin_bit_cast(u16x8_t, r2);
+    out[3] = __builtin_bit_cast(u16x8_t, r3);
+    out[4] = __builtin_bit_cast(u16x8_t, r4);
+    out[5] = __builtin_bit_cast(u16x8_t, r5);
+    out[6] = __builtin_bit_cast(u16x8_t, r6);
+    out[7] = __builtin_bit_cast(u16x8_t, r7);
+}
+
 template <int NX>
 __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
                                                      const int64_t *__restrict__ row0,
                                                      int64_t row_stride, int T,
-                                                     float *__restrict__ vt,
-                                                     float *__restrict__ sigma) {
-    __shared__ __align__(16) float Vs[kD * kD];  // 64 KiB, row i = eigenvector i
+                                                     const float *__restrict__ vt,
+                                                     float *__restrict__ sigma,
+                                                     int32_t *__restrict__ perm_out,
+                                                     float *__restrict__ scale_out) {
+    __shared__ __align__(16) uint8_t ring[NX == 1 ? kRing * kTileB : 16];
     __shared__ float ss[kD];       // sum of squares per eigenvector
     __shared__ float sig[kD];
-    __shared__ int perm[kD];
-    __shared__ float sgn[kD];
-    __shared__ float ninv[kD];     // 1 / ||v_i||
+    __shared__ float scl[kD];      // sign / ||v_i|| by original index
 
     const int blk = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    float *vblk = vt + static_cast<int64_t>(blk) * kD * kD;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const float *vblk = vt + static_cast<int64_t>(blk) * kD * kD;
     const int64_t base = row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride;
-    // bf16 X streams through a ring of four 32-token tiles in LDS (the V
-    // area, free once the fragments are built).  Each wave loads a quarter of
-    // a tile (rows 8 w .. 8 w + 7, two 16-byte loads per lane) four tiles
-    // ahead, so that the workgroup keeps four distinct tiles in flight
-    // instead of every wave loading every tile.  Rows are padded to 272
-    // bytes: the 16-byte fragment reads of 32 consecutive rows fall on
-    // distinct banks.
-    constexpr int kRowB = kD * 2 + 16;
-    constexpr int kSlot = 32 * kRowB;
-    static_assert(4 * kSlot <= kD * kD * 4, "the ring fits in the V area");
-    uint8_t *ring = reinterpret_cast<uint8_t *>(Vs);
     const int n_tiles = T / 32;
-    const uint8_t *xg = static_cast<const uint8_t *>(x) + base * 2;
-    const int lr = 8 * wave + (lane >> 4);  // rows lr and lr + 4 of a tile
-    const uint8_t *xl = xg + static_cast<int64_t>(lr) * row_stride * 2 + 16 * (lane & 15);
-    const int64_t x4 = static_cast<int64_t>(4) * row_stride * 2, x32 = static_cast<int64_t>(32) * row_stride * 2;
-    auto load_q = [&](uint4 &ra, uint4 &rb, int tile) __attribute__((always_inline)) {
-        const int tt = tile < n_tiles ? tile : n_tiles - 1;  // past the end: the last tile again
-        const uint8_t *p0 = xl + tt * x32;
-        ra = *reinterpret_cast<const uint4 *>(p0);
-        rb = *reinterpret_cast<const uint4 *>(p0 + x4);
-    };
-    auto store_q = [&](const uint4 &ra, const uint4 &rb, int tile) __attribute__((always_inline)) {
-        uint8_t *p0 = ring + (tile & 3) * kSlot + lr * kRowB + 16 * (lane & 15);
-        *reinterpret_cast<uint4 *>(p0) = ra;
-        *reinterpret_cast<uint4 *>(p0 + 4 * kRowB) = rb;
-    };
-    // tile k waits in (qka, qkb), k = tile % 4, until it is stored, one tile before its use
-    uint4 q0a, q0b, q1a, q1b, q2a, q2b, q3a, q3b;
-    constexpr int NV = kD * kD / 4 / 256;  // float4 of V per thread
-    float4 vr[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) vr[k] = reinterpret_cast<const float4 *>(vblk)[tid + 256 * k];
-    // the first five X tiles are in flight while V is prepared
-    uint4 ra, rb;
-    if constexpr (NX == 1) {
-        load_q(ra, rb, 0);
-        load_q(q1a, q1b, 1);
-        load_q(q2a, q2b, 2);
-        load_q(q3a, q3b, 3);
-        load_q(q0a, q0b, 4);
-    }
-#pragma unroll
-    for (int k = 0; k < NV; ++k) reinterpret_cast<float4 *>(Vs)[tid + 256 * k] = vr[k];
-    __syncthreads();
 
-    // A fragments: row i = 32 * wave + lane % 32, k slots j = 16 ks + 8 (lane / 32) + e.
+    // A fragments: row i = 32 * wave + lane % 32, k slots j = 16 ks + 8 (lane / 32) + e,
+    // loaded before the first tiles' DMA so that they arrive first.
+    const int i = 32 * wave + (lane & 31), h = lane >> 5;
+    float v[8][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const float4 p0 = *reinterpret_cast<const float4 *>(vblk + i * kD + 16 * ks + 8 * h);
+        const float4 p1 = *reinterpret_cast<const float4 *>(vblk + i * kD + 16 * ks + 8 * h + 4);
+        v[ks][0] = p0.x; v[ks][1] = p0.y; v[ks][2] = p0.z; v[ks][3] = p0.w;
+        v[ks][4] = p1.x; v[ks][5] = p1.y; v[ks][6] = p1.z; v[ks][7] = p1.w;
+    }
+
+    // DMA of tile tau (clamped to the last tile) into slot tau % kRing: wave w
+    // writes rows 8 w .. 8 w + 7 (two 1 KiB instructions of four rows each).
+    const uint8_t *xg = static_cast<const uint8_t *>(x) + base * 2;
+    const int dr = lane >> 4, dp = lane & 15;  // row within an instruction, physical chunk
+    auto dma = [&](int tau) __attribute__((always_inline)) {
+        if constexpr (NX == 1) {
+            const int tt = tau < n_tiles ? tau : n_tiles - 1;
+#pragma unroll
+            for (int k = 0; k < kDmaPerWave; ++k) {
+                const int j = kDmaPerWave * wave + k;       // instruction: rows 4 j .. 4 j + 3
+                const int r = 4 * j + dr;
+                const uint8_t *src = xg + (static_cast<int64_t>(32 * tt + r) * row_stride) * 2 + 16 * (dp ^ (r & 15));
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                                 (__attribute__((address_space(3))) void *)(ring + (tau % kRing) * kTileB + 1024 * j),
+                                                 16, 0, 0);
+            }
+        }
+    };
+    if constexpr (NX == 1) {
+#pragma unroll
+        for (int tau = 0; tau < kAhead; ++tau) dma(tau);
+        // every prologue DMA is issued before the fragment build waits for V
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
     // Thousands of fp32 rotations leave each eigenvector's norm off by ~1e-5: the
     // fragments are built from v_i / ||v_i|| (so that ||X v|| measures sigma and
     // B = V_r^T is orthonormal), and the same pass finds the row's sign: its
@@ -94,18 +140,11 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     constexpr int NT = NX == 1 ? 2 : 3;  // terms of V
     u16x8_t fa[NT][8];
     {
-        const int i = 32 * wave + (lane & 31), h = lane >> 5;
-        float v[8][8];
         float ssq = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const float4 p0 = *reinterpret_cast<const float4 *>(Vs + i * kD + 16 * ks + 8 * h);
-            const float4 p1 = *reinterpret_cast<const float4 *>(Vs + i * kD + 16 * ks + 8 * h + 4);
-            v[ks][0] = p0.x; v[ks][1] = p0.y; v[ks][2] = p0.z; v[ks][3] = p0.w;
-            v[ks][4] = p1.x; v[ks][5] = p1.y; v[ks][6] = p1.z; v[ks][7] = p1.w;
+        for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) ssq = fmaf(v[ks][e], v[ks][e], ssq);
-        }
         ssq += __shfl_xor(ssq, 32, 64);
         const float nrm = sqrtf(ssq);
         const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
@@ -130,10 +169,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
         const float ob = __shfl_xor(best, 32, 64), ov = __shfl_xor(bval, 32, 64);
         const int oi = __shfl_xor(bidx, 32, 64);
         if (ob > best || (ob == best && oi < bidx)) bval = ov;
-        if (h == 0) {
-            ninv[i] = inv;
-            sgn[i] = (bval < 0.f) ? -1.f : 1.f;
-        }
+        if (h == 0) scl[i] = (bval < 0.f) ? -inv : inv;
     }
 
     float acc2[16];
@@ -141,15 +177,25 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     for (int r = 0; r < 16; ++r) acc2[r] = 0.f;
 
     if constexpr (NX == 1) {
-        __syncthreads();  // every wave has read V: its LDS is free
-        store_q(ra, rb, 0);
-        __syncthreads();
-        auto step = [&](uint4 &na, uint4 &nb, int t) __attribute__((always_inline)) {
-            // B fragments of tile t: token lane % 32, features 16 ks + 8 (lane / 32) ..
-            const uint8_t *src = ring + (t & 3) * kSlot + (lane & 31) * kRowB + 16 * (lane >> 5);
-            u16x8_t cur[8];
+        // B fragments of a tile: token n = lane % 32, logical chunk 2 ks + h of its row
+        const int n = lane & 31;
+        uint32_t roff[8];  // LDS byte addresses in slot 0
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) cur[ks] = *reinterpret_cast<const u16x8_t *>(src + 32 * ks);
+        for (int ks = 0; ks < 8; ++ks) roff[ks] = lds_addr(ring) + n * (kD * 2) + 16 * ((2 * ks + h) ^ (n & 15));
+        for (int t = 0; t < n_tiles; ++t) {
+            // this wave's part of tile t has landed (each later tile added
+            // kDmaPerWave operations); the barrier makes every part visible and
+            // frees slot (t - 1) % kRing for the tile kAhead ahead
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((kAhead - 1) * kDmaPerWave));
+            __syncthreads();
+            dma(t + kAhead);
+            // The tile's fragments, read in one asm block that also waits for
+            // them: the compiler then sees no LDS read that the DMAs in flight
+            // might write (it would wait for all of them), and no result is
+            // used before it has arrived.
+            const uint32_t so = (t % kRing) * kTileB;
+            u16x8_t cur[8];
+            read8_lds(cur, roff, so);
             f32x16_t acc = zero16(), acc1 = zero16();
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
@@ -158,24 +204,11 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
                 a = mfma32x32x16(fa[0][ks], cur[ks], a);
                 a = mfma32x32x16(fa[1][ks], cur[ks], a);
             }
-            store_q(na, nb, t + 1);  // its slot was last read in tile t - 3
-            load_q(na, nb, t + 5);
             acc += acc1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc2[r] += acc[r] * acc[r];
-            __syncthreads();
-        };
-        int t = 0;
-        for (; t + 4 <= n_tiles; t += 4) {
-            step(q1a, q1b, t);
-            step(q2a, q2b, t + 1);
-            step(q3a, q3b, t + 2);
-            step(q0a, q0b, t + 3);
         }
-        if (t < n_tiles) {  // block_len % 64 == 0: an even number of tiles, so two remain
-            step(q1a, q1b, t);
-            step(q2a, q2b, t + 1);
-        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing (discarded) tiles have landed
     } else {
         for (int t0 = 0; t0 < T; t0 += 32) {
             const int t = t0 + (lane & 31);
@@ -190,9 +223,9 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
                 u16x8_t fb[3];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    uint16_t h, m, l;
-                    split3_bf16(f[e], h, m, l);
-                    fb[0][e] = h;
+                    uint16_t hh, m, l;
+                    split3_bf16(f[e], hh, m, l);
+                    fb[0][e] = hh;
                     fb[1][e] = m;
                     fb[2][e] = l;
                 }
@@ -206,16 +239,6 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
             for (int r = 0; r < 16; ++r) acc2[r] += acc[r] * acc[r];
         }
     }
-    // V again (the X ring overwrote its LDS copy): DMA'd from memory into the V
-    // area, 1 KiB per wave instruction, while the sums are reduced and sorted
-    // (every wave's last ring read is behind the loop's final barrier)
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int m = 16 * wave + k;
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void *)(reinterpret_cast<const uint8_t *>(vblk) + 1024 * m + 16 * lane),
-            (__attribute__((address_space(3))) void *)(reinterpret_cast<uint8_t *>(Vs) + 1024 * m), 16, 0, 0);
-    }
     // acc2[r] belongs to row i = 32 wave + 8 (r / 4) + 4 (lane / 32) + r % 4, token lane % 32.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -224,7 +247,7 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
     }
     __syncthreads();
 
-    // Sort descending (rank by counting; ties keep index order) and fix signs.
+    // Sort descending (rank by counting; ties keep index order).
     if (tid < kD) sig[tid] = sqrtf(ss[tid]);
     __syncthreads();
     if (tid < kD) {
@@ -234,35 +257,25 @@ __global__ __launch_bounds__(256) void refine_kernel(const void *__restrict__ x,
             const float sj = sig[j];
             pos += (sj > si) || (sj == si && j < tid);
         }
-        perm[pos] = tid;
-        ss[pos] = si;  // sorted values (ss is free again)
-    }
-    __syncthreads();
-    if (tid < kD) sigma[static_cast<int64_t>(blk) * kD + tid] = ss[tid];
-    // sorted, signed, unit-norm rows (the DMA of V has landed before the barrier)
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int e4 = tid + 256 * k, pos = e4 >> 5, j = 4 * (e4 & 31);
-        const int src = perm[pos];
-        const float g = sgn[src], iv = ninv[src];
-        const float4 a = *reinterpret_cast<const float4 *>(Vs + src * kD + j);
-        reinterpret_cast<float4 *>(vblk)[e4] = make_float4(g * (a.x * iv), g * (a.y * iv), g * (a.z * iv), g * (a.w * iv));
+        const int64_t o = static_cast<int64_t>(blk) * kD + pos;
+        sigma[o] = si;
+        perm_out[o] = tid;
+        scale_out[o] = scl[tid];
     }
 }
 
 }  // namespace
 
 hipError_t launch_refine(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
-                         int block_len, int n_blocks, float *vt, float *sigma, hipStream_t st) {
+                         int block_len, int n_blocks, const float *vt, float *sigma, int32_t *perm,
+                         float *scale, hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
     if (x_type == kBF16)
         hipLaunchKernelGGL(refine_kernel<1>, dim3(static_cast<unsigned>(n_blocks)), dim3(256), 0,
-                           st, x, row0, row_stride, block_len, vt, sigma);
+                           st, x, row0, row_stride, block_len, vt, sigma, perm, scale);
     else
         hipLaunchKernelGGL(refine_kernel<3>, dim3(static_cast<unsigned>(n_blocks)), dim3(256), 0,
-                           st, x, row0, row_stride, block_len, vt, sigma);
+                           st, x, row0, row_stride, block_len, vt, sigma, perm, scale);
     return hipGetLastError();
 }
 
