@@ -513,14 +513,24 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     # the unfused alternative: rebuild every attended block into a staging cache,
     # then attend over it as an uncompressed cache (one pass over all layers)
     rebuild = None
-    if want_rebuild and sel is None and not cfg.tail_len and dec_only_ms is not None:
-        stg = [torch.empty((cfg.batch, H, cfg.blocks_per_seq * T, d), dtype=torch.bfloat16, device=dev)
+    if want_rebuild and dec_only_ms is not None:
+        # staging rows: the attended blocks back to back, then (with a tail) a copy of the tail
+        n_att = cfg.blocks_per_seq if sel is None else max(len(x) for x in sel)
+        stg = [torch.empty((cfg.batch, H, n_att * T + cfg.tail_len, d), dtype=torch.bfloat16, device=dev)
                for _ in range(2)]
         outs2 = torch.empty((cfg.batch, Hq, d), dtype=xdt, device=dev)
+        rta_kw = {}
+        if sel is not None:
+            rta_kw["sel"] = sel
+        if cfg.tail_len:
+            rta_kw.update(tail_len=[cfg.tail_len] * cfg.batch, tail_pos0=[cfg.context_len] * cfg.batch)
 
         def rebuild_layer(layer):
+            kw = dict(rta_kw)
+            if cfg.tail_len:
+                kw.update(tail_k=tails[layer][0], tail_v=tails[layer][1])
             milo.reconstruct_then_attend(Q[layer], q_pos, layer_factors("k", layer), layer_factors("v", layer),
-                                         cfg.blocks_per_seq, H, outs2, staging_k=stg[0], staging_v=stg[1])
+                                         cfg.blocks_per_seq, H, outs2, staging_k=stg[0], staging_v=stg[1], **kw)
         rebuild_layer(0)
         torch.cuda.synchronize()
         milo.milo_profile_read()
@@ -603,9 +613,11 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
         "refine": (n_blocks_step * 2.0 * T * d * d, n_blocks_step * 2.0 * T * d * d * REFINE_TERMS[xe]),
     }
     if rebuild is not None:
-        # fused: the factors once; unfused: the factors, the staging write, the staging read
-        rebuild["bytes_per_step"] = dec_bytes_all_layers + 2 * L * rebuild["staging_bytes_per_layer"]
-        rebuild["fused_bytes_per_step"] = dec_bytes_all_layers
+        # fused: the factors (and tail) once; unfused: the factors, the staging write (tail copy
+        # included) and the staging read
+        rebuild["bytes_per_step"] = (dec_bytes_all_layers + tail_bytes_all
+                                     + 2 * L * rebuild["staging_bytes_per_layer"])
+        rebuild["fused_bytes_per_step"] = dec_bytes_all_layers + tail_bytes_all
     rooflines = {}
     for name, (launches, tot_ms) in prof.items():
         if name not in work:

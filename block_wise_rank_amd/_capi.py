@@ -46,7 +46,8 @@ class milo_decode_args(ctypes.Structure):
                 ("tail_cap", _i32), ("tail_len", _vp), ("tail_pos0", _vp),
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
                 ("out", _vp), ("out_dtype", ctypes.c_int), ("split_len", _i32),
-                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("tail_seg_pos", _vp), ("tail_seg_valid", _vp), ("tail_seg_len", _i32)]
 
 
 # Every symbol include/milo.h declares, with its ctypes signature.
@@ -65,6 +66,8 @@ SIGNATURES = {
                                               ctypes.POINTER(ctypes.c_size_t), _vp]),
     "milo_reconstruct": (ctypes.c_int, [ctypes.POINTER(milo_factors), _vp, _i32, _vp,
                                         ctypes.c_int, _vp]),
+    "milo_reconstruct_ex": (ctypes.c_int, [ctypes.POINTER(milo_factors), _vp, _i32, _vp, _vp,
+                                           ctypes.c_int, _vp]),
     "milo_fetch_blocks": (ctypes.c_int, [ctypes.POINTER(milo_factors), ctypes.POINTER(milo_factors), _vp,
                                          _i32, _vp]),
     "milo_decode_attention": (ctypes.c_int, [ctypes.POINTER(milo_decode_args),

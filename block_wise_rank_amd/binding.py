@@ -327,12 +327,20 @@ def milo_allocate_ranks_ex(sigma: torch.Tensor, max_rank: int, pool_ptr, budget,
 
 
 def milo_reconstruct(factors: Factors, block_ids: torch.Tensor, out: torch.Tensor,
-                     stream=None) -> None:
+                     stream=None, out_off: torch.Tensor | None = None) -> None:
+    """Rebuild the listed blocks into out: block i at element offset out_off[i]
+    (device int64) when given (milo_reconstruct_ex), else back to back."""
     _need(block_ids, "block_ids", torch.int32)
-    _need(out, "out", None, block_ids.numel() * factors.block_len * factors.head_dim)
+    n = block_ids.numel()
+    rows = factors.block_len * factors.head_dim
+    if out_off is None:
+        _need(out, "out", None, n * rows)
+    else:
+        _need(out_off, "out_off", torch.int64, n)
+        _need(out, "out", None)
     fs = factors.struct()
-    st = lib().milo_reconstruct(ctypes.byref(fs), _p(block_ids), int(block_ids.numel()), _p(out),
-                                _dtype_code(out.dtype), _stream(stream))
+    st = lib().milo_reconstruct_ex(ctypes.byref(fs), _p(block_ids), int(n), _p(out), _p(out_off),
+                                   _dtype_code(out.dtype), _stream(stream))
     _check(st)
 
 
@@ -360,7 +368,9 @@ def milo_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: F
                           tail_v: torch.Tensor | None = None, tail_len: torch.Tensor | None = None,
                           tail_pos0: torch.Tensor | None = None, rope_base: float = 1e6,
                           softmax_scale: float | None = None, split_len: int = 0,
-                          workspace: torch.Tensor | None = None, stream=None) -> None:
+                          workspace: torch.Tensor | None = None, stream=None,
+                          tail_seg_pos: torch.Tensor | None = None, tail_seg_valid: torch.Tensor | None = None,
+                          tail_seg_len: int = 0) -> None:
     batch, n_q, d = q.shape
     _need(q, "q")
     _need(q_pos, "q_pos", torch.int64, batch)
@@ -369,11 +379,16 @@ def milo_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: F
     _need(sel_blk, "sel_blk", torch.int32, optional=True)
     _need(tail_k, "tail_k", None, optional=True)
     _need(tail_v, "tail_v", None, optional=True)
-    _need(tail_len, "tail_len", torch.int32, batch, optional=tail_k is None)
-    _need(tail_pos0, "tail_pos0", torch.int64, batch, optional=tail_k is None)
+    segs = tail_seg_pos is not None
+    _need(tail_len, "tail_len", torch.int32, batch, optional=tail_k is None or segs)
+    _need(tail_pos0, "tail_pos0", torch.int64, batch, optional=tail_k is None or segs)
     _need(workspace, "workspace", torch.uint8, optional=True)
     ks, vs = k.struct(), v.struct()
     tail_cap = 0 if tail_k is None else int(tail_k.shape[2])
+    if segs:
+        nseg = tail_cap // max(int(tail_seg_len), 1)
+        _need(tail_seg_pos, "tail_seg_pos", torch.int64, batch * nseg)
+        _need(tail_seg_valid, "tail_seg_valid", torch.int32, batch * nseg)
     args = C.milo_decode_args(
         _p(q), _dtype_code(q.dtype), _p(q_pos), batch, n_q, int(n_kv_heads), d,
         ctypes.pointer(ks), ctypes.pointer(vs), int(blocks_per_seq), _p(sel_ptr), _p(sel_blk),
@@ -382,14 +397,16 @@ def milo_decode_attention(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v: F
         _p(tail_len), _p(tail_pos0), float(rope_base),
         float(softmax_scale if softmax_scale is not None else d ** -0.5), _p(out),
         _dtype_code(out.dtype), int(split_len), _p(workspace),
-        0 if workspace is None else workspace.numel())
+        0 if workspace is None else workspace.numel(), _p(tail_seg_pos), _p(tail_seg_valid),
+        int(tail_seg_len) if segs else 0)
     need = ctypes.c_size_t(0)
     st = lib().milo_decode_attention(ctypes.byref(args), ctypes.byref(need), _stream(stream))
     if st == C.MILO_E_WORKSPACE and workspace is None:
         workspace = _on_stream(stream, q.device, int(need.value))
         return milo_decode_attention(q, q_pos, k, v, blocks_per_seq, n_kv_heads, out, sel_ptr,
                                      sel_blk, sel_max, tail_k, tail_v, tail_len, tail_pos0,
-                                     rope_base, softmax_scale, split_len, workspace, stream)
+                                     rope_base, softmax_scale, split_len, workspace, stream,
+                                     tail_seg_pos, tail_seg_valid, tail_seg_len)
     _check(st)
 
 
@@ -431,32 +448,100 @@ def reconstruct_then_attend(q: torch.Tensor, q_pos: torch.Tensor, k: Factors, v:
                             staging_k: torch.Tensor | None = None,
                             staging_v: torch.Tensor | None = None, staging_dtype=torch.bfloat16,
                             rope_base: float = 1e6, softmax_scale: float | None = None,
-                            split_len: int = 0, stream=None):
-    """The unfused decode over every block of every sequence: milo_reconstruct
-    rebuilds the blocks into token-major staging caches [batch][n_kv_heads]
-    [blocks_per_seq * block_len][head_dim] (block b of sequence s, KV head h is
-    factor block (s * n_kv_heads + h) * blocks_per_seq + b, so positions stay
-    b * block_len + t), then milo_decode_attention attends over them as an
-    uncompressed cache (no factor blocks).  Returns (staging_k, staging_v)."""
+                            split_len: int = 0, stream=None, sel=None, tail_k: torch.Tensor | None = None,
+                            tail_v: torch.Tensor | None = None, tail_len=None, tail_pos0=None,
+                            seg_len: int | None = None):
+    """The unfused decode: milo_reconstruct rebuilds the attended blocks into
+    token-major staging caches, then milo_decode_attention attends over them as
+    an uncompressed cache (no factor blocks).  Returns (staging_k, staging_v).
+
+    Without ``sel`` or a tail every block is attended and the staging caches are
+    [batch][n_kv_heads][blocks_per_seq * block_len][head_dim] with block b of
+    sequence s, KV head h (factor block (s * n_kv_heads + h) * blocks_per_seq + b)
+    at positions b * block_len + t.  With ``sel`` (host lists of ascending,
+    distinct block indices per sequence) and/or an uncompressed tail (tail_k,
+    tail_v [batch][n_kv_heads][tail_cap][head_dim], host lists tail_len and
+    tail_pos0), sequence s's staging row holds its selected blocks in order,
+    then a copy of its tail, as segments of ``seg_len`` slots (default: the
+    largest multiple of 128 dividing both block_len and tail_cap) whose start
+    positions are the blocks' own (b * block_len) and the tail's (tail_pos0),
+    so that every key keeps its absolute position."""
     batch = q.shape[0]
     T, d = k.block_len, k.head_dim
-    shape = (batch, n_kv_heads, blocks_per_seq * T, d)
+    dev = q.device
+    if sel is None and tail_k is None:
+        shape = (batch, n_kv_heads, blocks_per_seq * T, d)
+        if staging_k is None:
+            staging_k = _on_stream(stream, dev, shape, staging_dtype)
+        if staging_v is None:
+            staging_v = _on_stream(stream, dev, shape, staging_dtype)
+        _need(staging_k, "staging_k", None, batch * n_kv_heads * blocks_per_seq * T * d)
+        _need(staging_v, "staging_v", staging_k.dtype, staging_k.numel())
+        with torch.cuda.stream(_torch_stream(stream, dev)):  # scratch of this stream (see _on_stream)
+            ids = torch.arange(batch * n_kv_heads * blocks_per_seq, dtype=torch.int32, device=dev)
+            tl = torch.full((batch,), blocks_per_seq * T, dtype=torch.int32, device=dev)
+            tp = torch.zeros((batch,), dtype=torch.int64, device=dev)
+        milo_reconstruct(k, ids, staging_k, stream)
+        milo_reconstruct(v, ids, staging_v, stream)
+        milo_decode_attention(q, q_pos, k, v, 0, n_kv_heads, out, tail_k=staging_k.view(shape),
+                              tail_v=staging_v.view(shape), tail_len=tl, tail_pos0=tp,
+                              rope_base=rope_base, softmax_scale=softmax_scale, split_len=split_len,
+                              stream=stream)
+        return staging_k, staging_v
+
+    sel = [list(range(blocks_per_seq))] * batch if sel is None else [[int(b) for b in x] for x in sel]
+    nmax = max((len(x) for x in sel), default=0)
+    tcap = 0 if tail_k is None else int(tail_k.shape[2])
+    if seg_len is None:
+        seg_len = 128
+        for c in (2048, 1024, 512, 256):
+            if T % c == 0 and tcap % c == 0:
+                seg_len = c
+                break
+    cap = nmax * T + tcap
+    shape = (batch, n_kv_heads, cap, d)
     if staging_k is None:
-        staging_k = _on_stream(stream, q.device, shape, staging_dtype)
+        staging_k = _on_stream(stream, dev, shape, staging_dtype)
     if staging_v is None:
-        staging_v = _on_stream(stream, q.device, shape, staging_dtype)
-    _need(staging_k, "staging_k", None, batch * n_kv_heads * blocks_per_seq * T * d)
+        staging_v = _on_stream(stream, dev, shape, staging_dtype)
+    _need(staging_k, "staging_k", None, batch * n_kv_heads * cap * d)
     _need(staging_v, "staging_v", staging_k.dtype, staging_k.numel())
-    with torch.cuda.stream(_torch_stream(stream, q.device)):  # scratch of this stream (see _on_stream)
-        ids = torch.arange(batch * n_kv_heads * blocks_per_seq, dtype=torch.int32, device=q.device)
-        tail_len = torch.full((batch,), blocks_per_seq * T, dtype=torch.int32, device=q.device)
-        tail_pos0 = torch.zeros((batch,), dtype=torch.int64, device=q.device)
-    milo_reconstruct(k, ids, staging_k, stream)
-    milo_reconstruct(v, ids, staging_v, stream)
-    milo_decode_attention(q, q_pos, k, v, 0, n_kv_heads, out, tail_k=staging_k.view(shape),
-                          tail_v=staging_v.view(shape), tail_len=tail_len, tail_pos0=tail_pos0,
+    staging_k, staging_v = staging_k.view(shape), staging_v.view(shape)
+    # host-side plan: which blocks land where, and the segment table
+    ids, offs = [], []
+    nseg = cap // seg_len
+    seg_pos = [[0] * nseg for _ in range(batch)]
+    seg_valid = [[0] * nseg for _ in range(batch)]
+    per_blk = T // seg_len
+    for s_, blocks in enumerate(sel):
+        for h in range(n_kv_heads):
+            for j, b in enumerate(blocks):
+                ids.append((s_ * n_kv_heads + h) * blocks_per_seq + b)
+                offs.append(((s_ * n_kv_heads + h) * cap + j * T) * d)
+        for j, b in enumerate(blocks):
+            for u in range(per_blk):
+                seg_pos[s_][j * per_blk + u] = b * T + u * seg_len
+                seg_valid[s_][j * per_blk + u] = seg_len
+        if tcap:
+            L = int(tail_len[s_])
+            for u in range(tcap // seg_len):
+                m = nmax * per_blk + u
+                seg_pos[s_][m] = int(tail_pos0[s_]) + u * seg_len
+                seg_valid[s_][m] = max(0, min(seg_len, L - u * seg_len))
+    with torch.cuda.stream(_torch_stream(stream, dev)):  # scratch of this stream (see _on_stream)
+        ids_t = torch.tensor(ids, dtype=torch.int32, device=dev)
+        offs_t = torch.tensor(offs, dtype=torch.int64, device=dev)
+        sp_t = torch.tensor(seg_pos, dtype=torch.int64, device=dev)
+        sv_t = torch.tensor(seg_valid, dtype=torch.int32, device=dev)
+        if tcap:  # the uncompressed tail joins the staging rows (data movement only)
+            staging_k[:, :, nmax * T:].copy_(tail_k)
+            staging_v[:, :, nmax * T:].copy_(tail_v)
+    if ids:
+        milo_reconstruct(k, ids_t, staging_k, stream, out_off=offs_t)
+        milo_reconstruct(v, ids_t, staging_v, stream, out_off=offs_t)
+    milo_decode_attention(q, q_pos, k, v, 0, n_kv_heads, out, tail_k=staging_k, tail_v=staging_v,
                           rope_base=rope_base, softmax_scale=softmax_scale, split_len=split_len,
-                          stream=stream)
+                          stream=stream, tail_seg_pos=sp_t, tail_seg_valid=sv_t, tail_seg_len=seg_len)
     return staging_k, staging_v
 
 

@@ -413,6 +413,11 @@ milo_status milo_allocate_ranks_ex(const float *sigma, int32_t n_blocks, int32_t
 
 milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, int32_t n_ids,
                              void *x_out, milo_dtype out_dtype, void *stream) {
+    return milo_reconstruct_ex(f, block_ids, n_ids, x_out, nullptr, out_dtype, stream);
+}
+
+milo_status milo_reconstruct_ex(const milo_factors *f, const int32_t *block_ids, int32_t n_ids,
+                                void *x_out, const int64_t *out_off, milo_dtype out_dtype, void *stream) {
     if (!f) return fail(MILO_E_INVALID, "factor set is NULL");
     if (f->head_dim != kD) return fail(MILO_E_UNSUPPORTED, "head_dim must be 128");
     if (f->block_len < 128 || f->block_len % 64 != 0)
@@ -433,7 +438,7 @@ milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, in
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed("reconstruct", s, [&] {
         return milo::launch_reconstruct(f->arena, ft, f->rank, f->a_off, f->b_off, f->a_scale,
-                                        f->b_scale, f->block_len, block_ids, n_ids, x_out,
+                                        f->b_scale, f->block_len, block_ids, n_ids, x_out, out_off,
                                         out_dtype == MILO_F32 ? milo::kF32 : milo::kBF16, s);
     });
     if (e != hipSuccess) return hip_fail(e, "reconstruct launch");
@@ -550,8 +555,17 @@ milo_status decode_attention(const milo_decode_args *a, size_t *workspace_needed
             return fail(MILO_E_INVALID, "sel_max must be in [0, blocks_per_seq]");
     }
     const bool tail = a->tail_k != nullptr;
+    const bool segs = a->tail_seg_pos != nullptr;
+    if (segs && !tail) return fail(MILO_E_INVALID, "tail_seg_pos needs tail_k");
     if (tail) {
-        if (!a->tail_v || !a->tail_len || !a->tail_pos0) return fail(MILO_E_INVALID, "tail_v, tail_len and tail_pos0 must be set");
+        if (!a->tail_v) return fail(MILO_E_INVALID, "tail_v must be set");
+        if (segs) {
+            if (!a->tail_seg_valid) return fail(MILO_E_INVALID, "tail_seg_valid must be set with tail_seg_pos");
+            if (a->tail_seg_len <= 0 || a->tail_seg_len % 128 != 0 || a->tail_cap % a->tail_seg_len != 0)
+                return fail(MILO_E_UNSUPPORTED, "tail_seg_len must be a positive multiple of 128 dividing tail_cap");
+        } else if (!a->tail_len || !a->tail_pos0) {
+            return fail(MILO_E_INVALID, "tail_len and tail_pos0 must be set");
+        }
         if (a->tail_cap <= 0 || a->tail_cap % 64 != 0) return fail(MILO_E_UNSUPPORTED, "tail_cap must be a positive multiple of 64");
         if (a->tail_dtype != MILO_F32 && a->tail_dtype != MILO_BF16) return fail(MILO_E_UNSUPPORTED, "tail_dtype must be F32 or BF16");
         const int te = elem_bytes(a->tail_dtype);
@@ -564,15 +578,17 @@ milo_status decode_attention(const milo_decode_args *a, size_t *workspace_needed
     const int ttype = a->tail_dtype == MILO_F32 ? milo::kF32 : milo::kBF16;
     int split = a->split_len;
     if (split == 0) {
-        // The longest split that still gives >= 1024 workgroups (four per CU),
+        // The longest split that still gives a workgroup to every CU (256),
         // counting the tail's: each split pays a prologue (B_k fragments,
-        // rotated queries) and a merge.
+        // rotated queries) and a merge, and one workgroup fills a CU (its LDS
+        // and registers), so more, shorter splits only add rounds of those.
         const int64_t units = static_cast<int64_t>(a->batch) * a->n_kv_heads *
                               (a->sel_ptr ? a->sel_max : a->blocks_per_seq);
         const int64_t tail_units = tail ? static_cast<int64_t>(a->batch) * a->n_kv_heads : 0;
         split = 128;
         for (int c = 2048; c > 128; c /= 2)
-            if (T % c == 0 && units * (T / c) + tail_units * ((a->tail_cap + c - 1) / c) >= 1024 &&
+            if (T % c == 0 && (!segs || a->tail_seg_len % c == 0) &&
+                units * (T / c) + tail_units * ((a->tail_cap + c - 1) / c) >= 256 &&
                 milo::decode_split_fits(ftype, ttype, tail, G, c)) {
                 split = c;
                 break;
@@ -580,6 +596,8 @@ milo_status decode_attention(const milo_decode_args *a, size_t *workspace_needed
     }
     if (split < 128 || split % 128 != 0 || T % split != 0 || split > 32 * milo::kMaxTiles)
         return fail(MILO_E_UNSUPPORTED, "split_len must be a multiple of 128, at most 2048, dividing block_len");
+    if (segs && a->tail_seg_len % split != 0)
+        return fail(MILO_E_UNSUPPORTED, "split_len %d must divide tail_seg_len %d", split, a->tail_seg_len);
     if (!milo::decode_split_fits(ftype, ttype, tail, G, split))
         return fail(MILO_E_UNSUPPORTED, "split_len %d needs more LDS than a workgroup has for %d query heads per KV head", split, G);
 
@@ -608,6 +626,9 @@ milo_status decode_attention(const milo_decode_args *a, size_t *workspace_needed
     p.tail_cap = tail ? a->tail_cap : 0;
     p.tail_len = a->tail_len;
     p.tail_pos0 = a->tail_pos0;
+    p.tail_seg_pos = segs ? a->tail_seg_pos : nullptr;
+    p.tail_seg_valid = segs ? a->tail_seg_valid : nullptr;
+    p.tail_seg_len = segs ? a->tail_seg_len : 0;
     p.rope_base = a->rope_base;
     p.softmax_scale = a->softmax_scale;
     p.out = a->out;

@@ -210,9 +210,19 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     } else {
         split_index = p.n_sel * p.block_splits + sp;
         tok0 = sp * p.split_len;
-        const int len = min(p.tail_len[s], p.tail_cap);  // never read past the tail buffer
-        valid = min(max(len - tok0, 0), p.split_len);
-        pos0 = p.tail_pos0[s] + tok0;
+        if (p.tail_seg_pos) {
+            // segment m holds its first tail_seg_valid tokens at tail_seg_pos + i;
+            // a split never straddles two segments (split_len divides tail_seg_len)
+            const int m = tok0 / p.tail_seg_len, off = tok0 - m * p.tail_seg_len;
+            const int64_t si = static_cast<int64_t>(s) * (p.tail_cap / p.tail_seg_len) + m;
+            const int sv = min(max(p.tail_seg_valid[si], 0), p.tail_seg_len);
+            valid = min(max(sv - off, 0), p.split_len);
+            pos0 = p.tail_seg_pos[si] + off;
+        } else {
+            const int len = min(p.tail_len[s], p.tail_cap);  // never read past the tail buffer
+            valid = min(max(len - tok0, 0), p.split_len);
+            pos0 = p.tail_pos0[s] + tok0;
+        }
         rk = rv = kD;
     }
     const int64_t pidx = static_cast<int64_t>(s * Hkv + h) * p.n_splits + split_index;

@@ -56,11 +56,12 @@ hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_
                           const int64_t *a_off, const int64_t *b_off, void *arena,
                           int out_type, float *a_scale, float *b_scale, hipStream_t st);
 
-// X_hat = A B for the listed blocks.
+// X_hat = A B for the listed blocks; block i's rows start at element out_off[i]
+// of out (out_off null: i * block_len * 128).
 hipError_t launch_reconstruct(const void *arena, int f_type, const int32_t *rank,
                               const int64_t *a_off, const int64_t *b_off, const float *a_scale,
                               const float *b_scale, int block_len, const int32_t *ids, int n_ids,
-                              void *out, int out_type, hipStream_t st);
+                              void *out, const int64_t *out_off, int out_type, hipStream_t st);
 
 struct DecodeParams {
     const void *q;
@@ -82,6 +83,11 @@ struct DecodeParams {
     int tail_type, tail_cap;
     const int32_t *tail_len;
     const int64_t *tail_pos0;
+    // segmented tail (tail_seg_pos non-null): [batch][tail_cap / tail_seg_len]
+    // start positions and valid token counts of segments of tail_seg_len slots
+    const int64_t *tail_seg_pos;
+    const int32_t *tail_seg_valid;
+    int tail_seg_len;
     double rope_base;
     float softmax_scale;
     void *out;

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(
     const uint8_t *__restrict__ arena, const int32_t *__restrict__ rank,
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off,
     const float *__restrict__ a_scale, const float *__restrict__ b_scale, int T,
-    const int32_t *__restrict__ ids, void *__restrict__ out) {
+    const int32_t *__restrict__ ids, void *__restrict__ out, const int64_t *__restrict__ out_off) {
     __shared__ __align__(16) float Bs[kD * kD];
     __shared__ float As[kD * 64];
     const int n = blockIdx.x;
@@ -86,13 +86,15 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(
 #pragma unroll
         for (int u = 0; u < 32; ++u) acc[u] = fmaf(a[u], b, acc[u]);
     }
-    const int64_t row = static_cast<int64_t>(n) * T + t0 + half * 32;
+    // element offset of this block's first output row
+    const int64_t obase = out_off ? out_off[n] : static_cast<int64_t>(n) * T * kD;
+    const int64_t row = t0 + half * 32;
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
         if constexpr (OUT == kF32)
-            static_cast<float *>(out)[(row + u) * kD + j] = acc[u];
+            static_cast<float *>(out)[obase + (row + u) * kD + j] = acc[u];
         else
-            static_cast<uint16_t *>(out)[(row + u) * kD + j] = f32_to_bf16_bits(acc[u]);
+            static_cast<uint16_t *>(out)[obase + (row + u) * kD + j] = f32_to_bf16_bits(acc[u]);
     }
 }
 
@@ -112,7 +114,7 @@ template <int OUT>
 __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(
     const uint8_t *__restrict__ arena, const int32_t *__restrict__ rank,
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off, int T,
-    const int32_t *__restrict__ ids, void *__restrict__ out) {
+    const int32_t *__restrict__ ids, void *__restrict__ out, const int64_t *__restrict__ out_off) {
     constexpr int OE = OUT == kF32 ? 4 : 2;  // output element bytes
     extern __shared__ __align__(16) uint8_t lds[];
     uint8_t *bst = lds;                      // B rows (prologue only)
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c4 = lane >> 4, j = lane & 15;
     const int r = rank[id];
-    uint8_t *ob = static_cast<uint8_t *>(out) + static_cast<int64_t>(n) * T * kD * OE;
+    uint8_t *ob = static_cast<uint8_t *>(out) + (out_off ? out_off[n] : static_cast<int64_t>(n) * T * kD) * OE;
     if (r == 0) {
         for (int64_t q = tid; q < static_cast<int64_t>(T) * kD * OE / 16; q += 256)
             reinterpret_cast<uint4 *>(ob)[q] = make_uint4(0u, 0u, 0u, 0u);
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(
 hipError_t launch_reconstruct(const void *arena, int f_type, const int32_t *rank,
                               const int64_t *a_off, const int64_t *b_off, const float *a_scale,
                               const float *b_scale, int block_len, const int32_t *ids, int n_ids,
-                              void *out, int out_type, hipStream_t st) {
+                              void *out, const int64_t *out_off, int out_type, hipStream_t st) {
     if (n_ids <= 0) return hipSuccess;
     if (f_type == kBF16) {
         const int lds = recon_bf16_lds(out_type == kF32 ? 4 : 2);
@@ -233,17 +235,17 @@ hipError_t launch_reconstruct(const void *arena, int f_type, const int32_t *rank
         const uint8_t *ar = static_cast<const uint8_t *>(arena);
         if (out_type == kF32)
             hipLaunchKernelGGL(reconstruct_bf16_kernel<kF32>, dim3(static_cast<unsigned>(n_ids)), dim3(256), lds,
-                               st, ar, rank, a_off, b_off, block_len, ids, out);
+                               st, ar, rank, a_off, b_off, block_len, ids, out, out_off);
         else
             hipLaunchKernelGGL(reconstruct_bf16_kernel<kBF16>, dim3(static_cast<unsigned>(n_ids)), dim3(256), lds,
-                               st, ar, rank, a_off, b_off, block_len, ids, out);
+                               st, ar, rank, a_off, b_off, block_len, ids, out, out_off);
         return hipGetLastError();
     }
     const dim3 grid(static_cast<unsigned>(n_ids), static_cast<unsigned>(block_len / 64));
     const uint8_t *ar = static_cast<const uint8_t *>(arena);
 #define MILO_RECON(F, O)                                                                         \
     hipLaunchKernelGGL((reconstruct_kernel<F, O>), grid, dim3(256), 0, st, ar, rank, a_off,      \
-                       b_off, a_scale, b_scale, block_len, ids, out)
+                       b_off, a_scale, b_scale, block_len, ids, out, out_off)
     if (f_type == kF32) {
         if (out_type == kF32) MILO_RECON(kF32, kF32); else MILO_RECON(kF32, kBF16);
     } else if (f_type == kI4) {

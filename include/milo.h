@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MILO_ABI_VERSION 1
+#define MILO_ABI_VERSION 2
 
 typedef enum milo_status {
     MILO_OK = 0,
@@ -226,6 +226,18 @@ milo_status milo_reconstruct(const milo_factors *f, const int32_t *block_ids, in
                              void *x_out, milo_dtype out_dtype, void *stream);
 
 /*
+ * milo_reconstruct_ex -- milo_reconstruct writing block i's block_len rows at
+ * element offset out_off[i] of x_out instead of i * block_len * head_dim, so
+ * that rebuilt blocks land where a staging cache keeps them (for example per
+ * sequence and KV head, next to an uncompressed tail).
+ *  out_off  device [n_ids] int64, or NULL (= milo_reconstruct).  Each offset
+ *           must be a multiple of 8 (16-byte aligned rows); the regions of
+ *           different ids must not overlap.  Device values are not validated.
+ */
+milo_status milo_reconstruct_ex(const milo_factors *f, const int32_t *block_ids, int32_t n_ids,
+                                void *x_out, const int64_t *out_off, milo_dtype out_dtype, void *stream);
+
+/*
  * milo_fetch_blocks -- host-offloaded compressed cache: bring the factors of
  * the listed blocks from a factor set kept in host memory into a device factor
  * set of the same layout ([REV] Summary and FAQ: the compressed cache is
@@ -293,11 +305,23 @@ typedef struct milo_decode_args {
     int32_t split_len;        /* tokens per work split: multiple of 128, at most 2048,   */
                               /* dividing block_len, whose workgroup fits the LDS for   */
                               /* the call's query heads per KV head; 0 picks the        */
-                              /* longest such split that still gives >= 1024            */
+                              /* longest such split that still gives >= 256             */
                               /* workgroups, the tail's included (else 128)             */
     void *workspace;          /* device scratch: per-split partial results and the     */
                               /* RoPE tables of the call (256-byte aligned)             */
     size_t workspace_bytes;
+    /* Segmented uncompressed part (ABI version 2), for caches that hold blocks
+     * rebuilt at their own positions next to the recent tail ([REV] FAQ: only
+     * the blocks a query needs are rebuilt, then attended sparsely).  With
+     * tail_seg_pos non-NULL, sequence s's tail_cap slots are tail_cap /
+     * tail_seg_len segments of tail_seg_len slots; segment m holds its first
+     * tail_seg_valid[s][m] tokens (0..tail_seg_len), token i of it at position
+     * tail_seg_pos[s][m] + i; tail_len and tail_pos0 are then not read (may be
+     * NULL).  tail_seg_len is a multiple of 128 dividing tail_cap, and the
+     * split must divide it (the default split does).                        */
+    const int64_t *tail_seg_pos;   /* device [batch][tail_cap / tail_seg_len] or NULL */
+    const int32_t *tail_seg_valid; /* device [batch][tail_cap / tail_seg_len]        */
+    int32_t tail_seg_len;
 } milo_decode_args;
 
 /*

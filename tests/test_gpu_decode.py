@@ -111,6 +111,48 @@ def test_kernel_level_selection_and_tail(storage):
                    tail_len=tail_len.to(DEV), tail_pos0=tail_pos0.to(DEV), split_len=split,
                    out_dtype=torch.bfloat16).float().cpu().numpy()
         _check(got, ref, vmax, storage, f"sel+tail {storage} split {split}")
+    # the unfused path over the same selection and tail: the selected blocks
+    # rebuilt into staging rows next to the tail, each at its own positions
+    out2 = torch.empty((batch, hq, d), dtype=torch.float32, device=DEV)
+    reconstruct_then_attend(q.to(DEV), q_pos.to(DEV), kf, vf, bps, hkv, out2, sel=sel, tail_k=tail_k.to(DEV),
+                            tail_v=tail_v.to(DEV), tail_len=tail_len.tolist(), tail_pos0=tail_pos0.tolist())
+    torch.cuda.synchronize()
+    _check(out2.cpu().numpy(), ref, vmax, storage, f"reconstruct-then-attend sel+tail {storage}")
+
+
+def test_segmented_tail_positions():
+    """An uncompressed part given as segments (start position and valid count
+    each, gaps left unattended) against exact attention over the valid tokens
+    at their positions (the oracle's attention)."""
+    batch, hkv, G, d, seg, nseg = 2, 2, 4, 128, 256, 5
+    cap = seg * nseg
+    rng = np.random.default_rng(13)
+    tk = (rng.standard_normal((batch, hkv, cap, d)) * 0.3).astype(np.float32)
+    tv = rng.standard_normal((batch, hkv, cap, d)).astype(np.float32)
+    pos = np.array([[40960, 0, 1024, 7000, 512], [3, 100000, 256, 9000, 12345]], dtype=np.int64)
+    valid = np.array([[256, 0, 100, 256, 1], [17, 256, 0, 255, 256]], dtype=np.int32)
+    q = (rng.standard_normal((batch, hkv * G, d)) * 4).astype(np.float32)
+    q_pos = np.array([200000, 300000], dtype=np.int64)
+    empty = Factors.alloc("bf16", 1, 1024, d, 256, device=DEV)
+    tkb = torch.from_numpy(tk).to(torch.bfloat16)
+    tvb = torch.from_numpy(tv).to(torch.bfloat16)
+    for split in (0, 128, 256):
+        got = _run(torch.from_numpy(q).to(DEV), torch.from_numpy(q_pos).to(DEV), empty, empty, 0, hkv,
+                   tail_k=tkb.to(DEV), tail_v=tvb.to(DEV), tail_seg_pos=torch.from_numpy(pos).to(DEV),
+                   tail_seg_valid=torch.from_numpy(valid).to(DEV), tail_seg_len=seg,
+                   split_len=split).cpu().numpy()
+        k64, v64 = tkb.double().numpy(), tvb.double().numpy()
+        worst, vmax = 0.0, float(np.abs(v64).max())
+        for s_ in range(batch):
+            for h in range(hkv):
+                idx = np.concatenate([np.arange(m * seg, m * seg + valid[s_, m]) for m in range(nseg)])
+                p_ = np.concatenate([pos[s_, m] + np.arange(valid[s_, m]) for m in range(nseg)])
+                for g in range(G):
+                    ref = oracle.attention(q[s_, h * G + g].astype(np.float64), int(q_pos[s_]), k64[s_, h, idx],
+                                           v64[s_, h, idx], p_, 1e6, d ** -0.5)
+                    worst = max(worst, float(np.abs(got[s_, h * G + g] - ref).max()))
+        print(f"  [segments split {split}] max|err| {worst:.3g}")
+        assert worst <= 2e-2 * vmax
 
 
 @pytest.mark.parametrize("storage", ["bf16", "f32", "i8", "i4"])

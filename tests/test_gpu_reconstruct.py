@@ -41,3 +41,30 @@ def test_reconstruct_listed_blocks(storage, T, out_dtype):
             assert err == 0.0, f"rank-0 block {b} not zero"
         else:
             assert err / den <= tol, f"{storage} T={T} block {b} (rank {ranks[b]}): rel-F {err / den:.3g}"
+
+
+@pytest.mark.parametrize("storage", ["bf16", "i8", "f32"])
+def test_reconstruct_at_offsets(storage):
+    """milo_reconstruct_ex: each listed block's rows land at its own element
+    offset of a larger buffer (gaps between them untouched), equal to the
+    back-to-back reconstruction of the same list."""
+    d, T = 128, 512
+    ranks = np.array([5, 0, 64, 128, 33])
+    n = len(ranks)
+    tens, _, _ = random_factor_set(n, T, d, storage, seed=71, ranks=ranks)
+    f = Factors(storage, n, T, d, rank=tens["rank"].to(DEV), a_off=tens["a_off"].to(DEV),
+                b_off=tens["b_off"].to(DEV), arena=tens["arena"].to(DEV))
+    if storage == "i8":
+        f.a_scale, f.b_scale = tens["a_scale"].to(DEV), tens["b_scale"].to(DEV)
+    ids = torch.tensor([3, 0, 4, 1, 2], dtype=torch.int32, device=DEV)
+    slots = [6, 1, 3, 0, 4]                      # where each listed block goes (in blocks of T rows)
+    dense = torch.empty((len(ids), T, d), dtype=torch.bfloat16, device=DEV)
+    milo_reconstruct(f, ids, dense)
+    big = torch.full((8, T, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    offs = torch.tensor([sl * T * d for sl in slots], dtype=torch.int64, device=DEV)
+    milo_reconstruct(f, ids, big, out_off=offs)
+    torch.cuda.synchronize()
+    for i, sl in enumerate(slots):
+        assert torch.equal(big[sl], dense[i]), (i, sl)
+    for sl in set(range(8)) - set(slots):
+        assert bool((big[sl] == 7.0).all()), sl
