@@ -76,8 +76,8 @@ def parse():
 KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "jacobi": ["jacobi.hip"],
                   "refine": ["refine.hip", "common.hpp"], "alloc": ["alloc.hip"],
                   "project": ["project.hip", "common.hpp"], "reconstruct": ["reconstruct.hip", "common.hpp"],
-                  "decode_blocks": ["decode.hip", "common.hpp"], "decode_tail": ["decode.hip", "common.hpp"],
-                  "decode_combine": ["decode.hip", "common.hpp"], "decode_tables": ["decode.hip"]}
+                  "decode": ["decode.hip", "common.hpp"], "decode_combine": ["decode.hip", "common.hpp"],
+                  "decode_tables": ["decode.hip"]}
 
 
 def kernel_key(name):
@@ -85,12 +85,10 @@ def kernel_key(name):
     for frag, key in (("gram_kernel", "gram"), ("gram_bf16_kernel", "gram"), ("jacobi_kernel", "jacobi"),
                       ("refine_kernel", "refine"), ("alloc_kernel", "alloc"), ("project_kernel", "project"),
                       ("project_bf16_kernel", "project"), ("reconstruct_kernel", "reconstruct"),
-                      ("reconstruct_bf16_kernel", "reconstruct"), ("decode_combine_kernel", "decode_combine"),
-                      ("decode_tables_kernel", "decode_tables")):
+                      ("reconstruct_bf16_kernel", "reconstruct"), ("decode_tables_kernel", "decode_tables"),
+                      ("decode_combine_kernel", "decode_combine"), ("decode_kernel", "decode")):
         if frag in name:
             return key
-    if "decode_partial_kernel" in name:
-        return "decode_tail" if "true>" in name else "decode_blocks"
     return None
 
 
@@ -602,8 +600,8 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
         "alloc": (n_blocks_step * d * 4, "GB/s", "hbm", PEAK_HBM_GBS),
         "project": (n_blocks_step * T * d * xe + tot_rank * (T + d) * fe + n_blocks_step * d * d * 4,
                     "GB/s", "hbm", PEAK_HBM_GBS),
-        "decode_blocks": (dec_bytes_all_layers, "GB/s", "hbm", PEAK_HBM_GBS),
-        "decode_tail": (tail_bytes_all, "GB/s", "hbm", PEAK_HBM_GBS),
+        # one launch per layer: the attended blocks' factors and the tail
+        "decode": (dec_bytes_all_layers + tail_bytes_all, "GB/s", "hbm", PEAK_HBM_GBS),
         "decode_combine": (L * cfg.batch * Hq * d * 4, "GB/s", "hbm", PEAK_HBM_GBS),
     }
     # MFMA work of the contractions, per step: (algorithmic flops, executed flops)

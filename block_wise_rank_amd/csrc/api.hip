@@ -644,9 +644,10 @@ milo_status decode_attention(const milo_decode_args *a, size_t *workspace_needed
         return fail(MILO_E_WORKSPACE, "workspace of %zu bytes needed (%zu given)", need, ws ? ws_bytes : 0);
     if (!aligned(ws, 256)) return fail(MILO_E_INVALID, "workspace must be 256-byte aligned");
     const size_t n = static_cast<size_t>(p.batch) * p.n_kv_heads * p.n_splits * G;
+    const size_t ml_bytes = align_up(n * 2 * sizeof(float), 256), po_bytes = align_up(n * kD * sizeof(float), 256);
     p.part_ml = static_cast<float *>(ws);
-    p.part_o = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + align_up(n * 2 * sizeof(float), 256));
-    uint8_t *tabs = static_cast<uint8_t *>(ws) + milo::decode_workspace_bytes(p) - milo::decode_table_bytes();
+    p.part_o = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + ml_bytes);
+    uint8_t *tabs = static_cast<uint8_t *>(ws) + ml_bytes + po_bytes;
     p.theta = reinterpret_cast<double *>(tabs);
     p.rope_tab = reinterpret_cast<float2 *>(tabs + 64 * sizeof(double));
     p.step_tab = p.rope_tab + 32 * 64;
@@ -655,12 +656,8 @@ milo_status decode_attention(const milo_decode_args *a, size_t *workspace_needed
     hipError_t e = hipSuccess;
     if ((e = timed("decode_tables", s, [&] { return milo::launch_decode_tables(p, s); })) != hipSuccess)
         return hip_fail(e, "decode table launch");
-    if (p.n_sel * p.block_splits > 0 &&
-        (e = timed("decode_blocks", s, [&] { return milo::launch_decode_blocks(p, s); })) != hipSuccess)
+    if ((e = timed("decode", s, [&] { return milo::launch_decode(p, s); })) != hipSuccess)
         return hip_fail(e, "decode launch");
-    if (p.tail_splits > 0 &&
-        (e = timed("decode_tail", s, [&] { return milo::launch_decode_tail(p, s); })) != hipSuccess)
-        return hip_fail(e, "decode tail launch");
     if ((e = timed("decode_combine", s, [&] { return milo::launch_decode_combine(p, s); })) != hipSuccess)
         return hip_fail(e, "decode combine launch");
     return ok();

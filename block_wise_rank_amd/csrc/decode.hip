@@ -160,11 +160,13 @@ __device__ __forceinline__ int stage_off_i8(int r, int t) {
     return r * 40 + ((((t >> 4) ^ ((r >> 4) & 1))) << 4) + (t & 15);
 }
 
+// One split's partial result (m, l, unnormalised o) of the G query heads of
+// (sequence blockIdx.z, KV head blockIdx.y): split sp of the selected blocks,
+// or of the uncompressed tail (TAIL; F is then the tail's element type).
 template <int F, bool TAIL>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
+__device__ __forceinline__ void decode_partial(const DecodeParams &p, const int sp, uint8_t *lds) {
     constexpr int NS = (F == kF32) ? 2 : 1;
     constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);  // kI4: half a byte, see below
-    extern __shared__ __align__(16) uint8_t lds[];
     const int G = p.group;
     const int n_tiles = p.split_len / kTile;
     const LdsLayout L = lds_layout(F, NS, n_tiles, TAIL, G);
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c4 = lane >> 4, ln = lane & 15;
-    const int s = blockIdx.z, h = blockIdx.y, sp = blockIdx.x;
+    const int s = blockIdx.z, h = blockIdx.y;
     const int Hkv = p.n_kv_heads;
     const int T = p.block_len;
 
@@ -1033,6 +1035,25 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeParams 
         static_cast<uint16_t *>(p.out)[oi] = f32_to_bf16_bits(o);
 }
 
+// One launch for every split of a call: workgroup x < n_sel * block_splits
+// runs split x of the selected blocks (factor type F), the rest run the
+// tail's splits (element type TF; TF < 0: no tail).  The partials are merged
+// by decode_combine_kernel, a launch of its own: a merge inside this kernel by
+// its last workgroup would need a device-scope release from every workgroup,
+// which writes back the issuing XCD's L2 each time.
+template <int F, int TF>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int nb = p.n_sel * p.block_splits;
+    const int x = blockIdx.x;
+    if constexpr (TF < 0) {
+        decode_partial<F, false>(p, x, lds);
+    } else {
+        if (x < nb) decode_partial<F, false>(p, x, lds);
+        else decode_partial<TF, true>(p, x - nb, lds);
+    }
+}
+
 // RoPE tables shared by every workgroup of one call: theta_j = base^(-2j/128),
 // (cos, sin)(t theta_j) for t < 32, and (cos, sin)(32 tile theta_j) for the
 // tile offsets of a split (angles reduced in fp64).
@@ -1056,15 +1077,29 @@ __global__ __launch_bounds__(256) void decode_tables_kernel(double rope_base, do
     }
 }
 
-template <int F, bool TAIL>
-hipError_t launch_partial(const DecodeParams &p, dim3 grid, hipStream_t st) {
+template <int F, int TF>
+hipError_t launch_decode_kernel(const DecodeParams &p, hipStream_t st) {
     constexpr int NS = (F == kF32) ? 2 : 1;
-    const LdsLayout L = lds_layout(F, NS, p.split_len / kTile, TAIL, p.group);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_partial_kernel<F, TAIL>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L.total);
+    const int n_tiles = p.split_len / kTile;
+    int lds = lds_layout(F, NS, n_tiles, false, p.group).total;
+    if constexpr (TF >= 0) {
+        const int tl = lds_layout(TF, TF == kF32 ? 2 : 1, n_tiles, true, p.group).total;
+        lds = lds > tl ? lds : tl;
+    }
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_kernel<F, TF>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_partial_kernel<F, TAIL>), grid, dim3(kThreads), L.total, st, p);
+    const dim3 grid(static_cast<unsigned>(p.n_splits), static_cast<unsigned>(p.n_kv_heads),
+                    static_cast<unsigned>(p.batch));
+    hipLaunchKernelGGL((decode_kernel<F, TF>), grid, dim3(kThreads), lds, st, p);
     return hipGetLastError();
+}
+
+template <int F>
+hipError_t launch_decode_f(const DecodeParams &p, hipStream_t st) {
+    if (p.tail_splits == 0) return launch_decode_kernel<F, -1>(p, st);
+    if (p.tail_type == kBF16) return launch_decode_kernel<F, kBF16>(p, st);
+    return launch_decode_kernel<F, kF32>(p, st);
 }
 
 }  // namespace
@@ -1089,29 +1124,14 @@ size_t decode_table_bytes() {
 size_t decode_workspace_bytes(const DecodeParams &p) {
     const size_t n = static_cast<size_t>(p.batch) * p.n_kv_heads * p.n_splits * p.group;
     const size_t ml = (n * 2 * sizeof(float) + 255) / 256 * 256;
-    return (ml + n * kD * sizeof(float) + 255) / 256 * 256 + decode_table_bytes();
+    const size_t po = (n * kD * sizeof(float) + 255) / 256 * 256;
+    return ml + po + decode_table_bytes();
 }
 
 hipError_t launch_decode_tables(const DecodeParams &p, hipStream_t st) {
     hipLaunchKernelGGL(decode_tables_kernel, dim3(kMaxTiles * 64 / 256), dim3(256), 0, st, p.rope_base, p.theta,
                        p.rope_tab, p.step_tab);
     return hipGetLastError();
-}
-
-hipError_t launch_decode_blocks(const DecodeParams &p, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(p.n_sel * p.block_splits), static_cast<unsigned>(p.n_kv_heads),
-                    static_cast<unsigned>(p.batch));
-    if (p.f_type == kBF16) return launch_partial<kBF16, false>(p, grid, st);
-    if (p.f_type == kI8) return launch_partial<kI8, false>(p, grid, st);
-    if (p.f_type == kI4) return launch_partial<kI4, false>(p, grid, st);
-    return launch_partial<kF32, false>(p, grid, st);
-}
-
-hipError_t launch_decode_tail(const DecodeParams &p, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(p.tail_splits), static_cast<unsigned>(p.n_kv_heads),
-                    static_cast<unsigned>(p.batch));
-    if (p.tail_type == kBF16) return launch_partial<kBF16, true>(p, grid, st);
-    return launch_partial<kF32, true>(p, grid, st);
 }
 
 hipError_t launch_decode_combine(const DecodeParams &p, hipStream_t st) {
@@ -1121,6 +1141,14 @@ hipError_t launch_decode_combine(const DecodeParams &p, hipStream_t st) {
     else
         hipLaunchKernelGGL(decode_combine_kernel<kBF16>, cgrid, dim3(128), 0, st, p);
     return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeParams &p, hipStream_t st) {
+    if (p.n_splits == 0) return hipSuccess;
+    if (p.n_sel * p.block_splits == 0 || p.f_type == kBF16) return launch_decode_f<kBF16>(p, st);
+    if (p.f_type == kI8) return launch_decode_f<kI8>(p, st);
+    if (p.f_type == kI4) return launch_decode_f<kI4>(p, st);
+    return launch_decode_f<kF32>(p, st);
 }
 
 }  // namespace milo

@@ -107,13 +107,13 @@ constexpr int kMaxTiles = 64;  // 32-token tiles per split (split_len <= 2048)
 
 // Whether a split of `split` tokens fits the decode kernels' LDS budget.
 bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int split);
-size_t decode_workspace_bytes(const DecodeParams &p);  // partials, then the tables
+// Workspace: the partials (m, l; then o), then the tables.
+size_t decode_workspace_bytes(const DecodeParams &p);
 size_t decode_table_bytes();
-// Partial results of the compressed-block splits, of the tail splits, and the
-// log-sum-exp merge into the output.
+// The RoPE tables; one launch for the partial results of the compressed-block
+// splits and of the tail splits; the log-sum-exp merge into the output.
 hipError_t launch_decode_tables(const DecodeParams &p, hipStream_t st);
-hipError_t launch_decode_blocks(const DecodeParams &p, hipStream_t st);
-hipError_t launch_decode_tail(const DecodeParams &p, hipStream_t st);
+hipError_t launch_decode(const DecodeParams &p, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeParams &p, hipStream_t st);
 
 }  // namespace milo
