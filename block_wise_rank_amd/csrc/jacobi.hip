@@ -558,9 +558,13 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
 }  // namespace
 
 hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt, int32_t *sweeps,
-                         int max_sweeps, float tol, float stop_tol, hipStream_t st) {
+                         int max_sweeps, float tol, float stop_tol, int n_cus, hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), 0, st,
+    // Fewer blocks than CUs: a little dynamic LDS puts each workgroup past half
+    // of a CU's LDS, so that no two share a CU (one alone runs its rounds faster,
+    // and concurrent calls on other streams spread over the idle CUs instead).
+    const size_t extra = n_blocks < n_cus ? 160 * 1024 / 2 - kLdsBytes + 1024 : 0;
+    hipLaunchKernelGGL(jacobi_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), extra, st,
                        gpart, splits, vt, sweeps, max_sweeps, tol, stop_tol);
     return hipGetLastError();
 }

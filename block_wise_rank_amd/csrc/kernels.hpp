@@ -26,7 +26,8 @@ hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t r
 // i (unsorted); sweeps[b] = sweeps used (negative when max_sweeps was hit).
 // sweeps may be null.
 hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt,
-                         int32_t *sweeps, int max_sweeps, float tol, float stop_tol, hipStream_t st);
+                         int32_t *sweeps, int max_sweeps, float tol, float stop_tol, int n_cus,
+                         hipStream_t st);
 
 // sigma_i = ||X_b v_i|| in fp32-accurate arithmetic, sorted descending into
 // sigma[b][0..128); perm[b][k] = the eigenvector (row of vt[b]) of sorted rank k
