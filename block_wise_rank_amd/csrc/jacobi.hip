@@ -54,11 +54,15 @@
 // from true values (diagonal entries are tracked unscaled, g = s_p s_q G_pq).
 //
 // A pair whose rotation is the identity has alpha = beta = 0, which moves its
-// rows unchanged.  Cyclic Jacobi converges quadratically once the off-diagonal
-// part is small (Golub & Van Loan sec. 8.5.3): a sweep whose every relative
-// off-diagonal |g| / sqrt|a b| was at most stop_tol leaves them near
-// stop_tol^2, so such a sweep ends the solve without the sweep that would only
-// confirm it.
+// rows unchanged.  The solve ends after a sweep whose every relative
+// off-diagonal |g| / sqrt|a b| was at most stop_tol, without the sweep that
+// would only confirm it: cyclic Jacobi converges quadratically once the
+// off-diagonal part is small (Golub & Van Loan sec. 8.5.3), but for clustered
+// eigenvalues that says little about each eigenvector.  The accuracy of the
+// singular values rests instead on the pass that follows, which recomputes
+// them as Rayleigh quotients ||X v|| (second order in the eigenvector error,
+// and within a cluster a mix of nearly equal values); stop_tol is chosen by
+// measurement against the oracle.
 #include "common.hpp"
 #include "kernels.hpp"
 
