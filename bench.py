@@ -64,6 +64,8 @@ def parse():
                     help="streams the compression calls of a step alternate between (1 or 2)")
     ap.add_argument("--compress-chunks", type=int, default=1,
                     help="compression calls per kind (runs of whole layers)")
+    ap.add_argument("--filter-csv", nargs=2, metavar=("IN", "OUT"),
+                    help="copy the rows of a rocprofv3 CSV that belong to libmilo's kernels (no GPU)")
     ap.add_argument("--extra", default="2,1",
                     help="other workloads measured after the main one (config indices, or 'none'): "
                          "multi-layer ones as whole steps, one-layer ones warm and cold")
@@ -76,7 +78,8 @@ def parse():
 KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "jacobi": ["jacobi.hip"],
                   "refine": ["refine.hip", "common.hpp"], "alloc": ["alloc.hip"],
                   "project": ["project.hip", "common.hpp"], "reconstruct": ["reconstruct.hip", "common.hpp"],
-                  "decode": ["decode.hip", "common.hpp"], "decode_combine": ["decode.hip", "common.hpp"],
+                  "decode": ["decode.hip", "common.hpp"], "decode_tail": ["decode.hip", "common.hpp"],
+                  "decode_combine": ["decode.hip", "common.hpp"],
                   "decode_tables": ["decode.hip"]}
 
 
@@ -86,9 +89,11 @@ def kernel_key(name):
                       ("refine_kernel", "refine"), ("alloc_kernel", "alloc"), ("project_kernel", "project"),
                       ("project_bf16_kernel", "project"), ("reconstruct_kernel", "reconstruct"),
                       ("reconstruct_bf16_kernel", "reconstruct"), ("decode_tables_kernel", "decode_tables"),
-                      ("decode_combine_kernel", "decode_combine"), ("decode_kernel", "decode")):
+                      ("decode_combine_kernel", "decode_combine")):
         if frag in name:
             return key
+    if "decode_kernel<" in name:  # <factor type, tail type>: -1 = no tail
+        return "decode" if ", -1>" in name else "decode_tail"
     return None
 
 
@@ -829,6 +834,17 @@ def main():
         return 0
     if args.ingest_mfma:
         ingest_mfma(args)
+        return 0
+    if args.filter_csv:
+        import csv
+        src, dst = args.filter_csv
+        with open(src, newline="") as f, open(dst, "w", newline="") as g:
+            rd = csv.DictReader(f)
+            wr = csv.DictWriter(g, fieldnames=rd.fieldnames)
+            wr.writeheader()
+            for row in rd:
+                if "milo::" in row.get("Kernel_Name", ""):
+                    wr.writerow(row)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path; "
