@@ -61,6 +61,9 @@ constexpr int kTVP = 264;  // pitch (bytes) of staged tail V rows (32 tokens x 1
 // bytes, so the 16-byte reads of 8 consecutive rows fall on distinct banks.
 constexpr int kRP = 66;
 constexpr int kQP = 132;
+// 4-bit B_k: offset of its decoded bf16 rows in the staging area, past the raw
+// codes and scales of up to 128 ranks (80 bytes each)
+constexpr int kBkRows4 = 128 * (kD / 2 + 4 * (kD / kI4Group));
 
 __host__ __device__ inline int align16(int v) { return (v + 15) & ~15; }
 
@@ -107,6 +110,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 // s_waitcnt immediate that waits until at most n vector memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// c ? a : b for a condition uniform over the wave, as one scalar select (a
+// select the compiler turned into branches would leave the number of memory
+// operations in flight unknown on the joined path, and it would then wait for
+// all of them).
+__device__ __forceinline__ const uint8_t *pick_uniform(bool c, const void *a, const void *b) {
+    const uint64_t x = c ? reinterpret_cast<uint64_t>(a) : reinterpret_cast<uint64_t>(b);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+    return reinterpret_cast<const uint8_t *>(static_cast<uint64_t>(hi) << 32 | lo);
+}
 
 // Signed value of nibble k (0..7) of a word of eight 4-bit codes.
 __device__ __forceinline__ float nib(uint32_t w, int k) {
@@ -259,8 +273,12 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     constexpr int LPR = RB / 16 > 0 ? RB / 16 : 1;  // lanes per row
     constexpr int RPI = 64 / LPR;                   // rows per load instruction
     constexpr int NI = 128 / RPI;                   // load instructions for 128 ranks
-    uint4 kraw[(F == kF32 || TAIL) ? 1 : NI];
-    float kscl[(F == kI4 && !TAIL) ? NI : 1];  // 4-bit: the tile's scale of each loaded row
+    uint4 kraw[(F == kF32 || F == kI4 || TAIL) ? 1 : NI];
+    // 4-bit: lane L stages, for ci = 0..7, the 16 bytes that the bf16 DMA would
+    // write (row 16 ci + L / 4, physical chunk L % 4): 8 codes and their row's
+    // scale for the tile.  Consecutive lanes then write consecutive 16 bytes.
+    uint32_t kcode[(F == kI4 && !TAIL) ? 8 : 1];
+    float kscl[(F == kI4 && !TAIL) ? 8 : 1];
     const int rk_pad = KS * 32;
     // Every load instruction is issued (rows clamped to rk - 1; identical
     // addresses coalesce), which keeps the registers free of partial paths.
@@ -268,16 +286,22 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         if constexpr (F != kF32 && !TAIL) {
             if (rk > 0) {
                 const int tt0 = tok0 + tile * kTile;
+                if constexpr (F == kI4) {
+                    const int pp = lane & 3;
 #pragma unroll
-                for (int ci = 0; ci < NI; ++ci) {
-                    // 32-bit offsets from the block's (uniform) base keep each address in one register
-                    const int r = min(ci * RPI + lane / LPR, rk - 1);
-                    if constexpr (F == kI4) {
-                        // codes of row r, tokens tt0 .. tt0 + 31; the scales follow the rk code rows
-                        kraw[ci] = *reinterpret_cast<const uint4 *>(Ak + static_cast<uint32_t>(r * (T / 2) + tt0 / 2));
+                    for (int ci = 0; ci < 8; ++ci) {
+                        const int rp = 16 * ci + (lane >> 2);  // staging row
+                        const int r = min(rp, rk - 1);         // rows past rk repeat the last
+                        const int pc = ((((pp >> 1) ^ ((rp >> 1) & 1))) << 1) | (pp & 1);  // logical chunk
+                        kcode[ci] = *reinterpret_cast<const uint32_t *>(Ak + static_cast<uint32_t>(r * (T / 2) + tt0 / 2 + 4 * pc));
                         kscl[ci] = *reinterpret_cast<const float *>(
                             Ak + static_cast<uint32_t>(rk * (T / 2) + (r * (T / kI4Group) + tt0 / kI4Group) * 4));
-                    } else {
+                    }
+                } else {
+#pragma unroll
+                    for (int ci = 0; ci < NI; ++ci) {
+                        // 32-bit offsets from the block's (uniform) base keep each address in one register
+                        const int r = min(ci * RPI + lane / LPR, rk - 1);
                         const uint32_t off = static_cast<uint32_t>((r * T + tt0) * ES + (lane % LPR) * 16);
                         kraw[ci] = *reinterpret_cast<const uint4 *>(Ak + off);
                     }
@@ -287,34 +311,33 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     };
     auto stage_k = [&](uint8_t *sdst) {
         if constexpr (F != kF32 && !TAIL) {
+            if constexpr (F == kI4) {
 #pragma unroll
-            for (int ci = 0; ci < NI; ++ci)
-                if (ci * RPI < rk_pad) {  // uniform
-                    const int r = ci * RPI + lane / LPR;
-                    if constexpr (F == kI4) {
-                        // one row's 32 codes -> four 16-byte chunks of bf16 (tokens 8 c .. 8 c + 7)
-                        const uint32_t wv[4] = {kraw[ci].x, kraw[ci].y, kraw[ci].z, kraw[ci].w};
+                for (int ci = 0; ci < 8; ++ci)
+                    if (16 * ci < rk_pad) {  // uniform
+                        uint32_t hw[4];
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            uint32_t h[4];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                h[e] = f32x2_to_bf16x2_bits(nib(wv[c], 2 * e) * kscl[ci], nib(wv[c], 2 * e + 1) * kscl[ci]);
-                            uint8_t *dst = sdst + stage_off_bf16(r, 8 * c);
-                            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(h[0], h[1]);
-                            reinterpret_cast<uint2 *>(dst)[1] = make_uint2(h[2], h[3]);
-                        }
-                    } else if constexpr (F == kBF16) {
-                        // 16-byte piece lane % LPR = tokens 8 (lane % LPR) .. + 7
-                        uint8_t *dst = sdst + stage_off_bf16(r, 8 * (lane % LPR));
-                        reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
-                        reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[ci].z, kraw[ci].w);
-                    } else {
-                        uint8_t *dst = sdst + r * 40 + (((lane % LPR) ^ ((r >> 4) & 1)) << 4);
-                        reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
-                        reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[ci].z, kraw[ci].w);
+                        for (int e = 0; e < 4; ++e)
+                            hw[e] = f32x2_to_bf16x2_bits(nib(kcode[ci], 2 * e) * kscl[ci], nib(kcode[ci], 2 * e + 1) * kscl[ci]);
+                        *reinterpret_cast<uint4 *>(sdst + 1024 * ci + 16 * lane) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
                     }
-                }
+            } else {
+#pragma unroll
+                for (int ci = 0; ci < NI; ++ci)
+                    if (ci * RPI < rk_pad) {  // uniform
+                        const int r = ci * RPI + lane / LPR;
+                        if constexpr (F == kBF16) {
+                            // 16-byte piece lane % LPR = tokens 8 (lane % LPR) .. + 7
+                            uint8_t *dst = sdst + stage_off_bf16(r, 8 * (lane % LPR));
+                            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
+                            reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[ci].z, kraw[ci].w);
+                        } else {
+                            uint8_t *dst = sdst + r * 40 + (((lane % LPR) ^ ((r >> 4) & 1)) << 4);
+                            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(kraw[ci].x, kraw[ci].y);
+                            reinterpret_cast<uint2 *>(dst)[1] = make_uint2(kraw[ci].z, kraw[ci].w);
+                        }
+                    }
+            }
             wave_lds_sync();
         }
     };
@@ -323,19 +346,19 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     // registers).  Instruction ci fills rows 16 ci .. 16 ci + 15; lane L writes
     // bytes 16 L of them, i.e. row 16 ci + L / 4 at 16 (L % 4), which is where
     // stage_off_bf16 puts the row's tokens 8 pc .. 8 pc + 7 for the pc below.
-    // All eight instructions are always issued (rows past rk repeat row rk - 1;
-    // rk = 0 reads the first bytes of q), so that the number of memory
-    // operations in flight after them is the same on every path.
+    // All eight instructions are issued without branches (rows past rk repeat
+    // row rk - 1; rk = 0 reads the first bytes of q).
     auto dma_k = [&](int tile, uint8_t *sdst) {
         if constexpr (F == kBF16 && !TAIL) {
             const int tt0 = tok0 + tile * kTile;
             const int hh = (lane >> 1) & 1, lo = lane & 1;
-            const uint8_t *base = rk > 0 ? Ak : static_cast<const uint8_t *>(p.q);
+            const uint8_t *base = pick_uniform(rk > 0, Ak, p.q);
+            const int rlast = max(rk - 1, 0), on = rk > 0 ? 2 : 0;  // rk = 0: offset 0
 #pragma unroll
             for (int ci = 0; ci < 8; ++ci) {
                 const int r = 16 * ci + (lane >> 2);
                 const int pc = ((hh ^ ((r >> 1) & 1)) << 1) | lo;
-                const uint32_t off = rk > 0 ? static_cast<uint32_t>((min(r, rk - 1) * T + tt0 + 8 * pc) * 2) : 0u;
+                const uint32_t off = static_cast<uint32_t>((min(r, rlast) * T + tt0 + 8 * pc) * on);
                 __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
                                                  (__attribute__((address_space(3))) void *)(sdst + 1024 * ci), 16, 0, 0);
             }
@@ -347,11 +370,12 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     // That half of the staging lies past the merge's own LDS areas.
     auto dma_bv = [&](uint8_t *sdst) {
         if constexpr (F == kBF16 && !TAIL) {
-            const uint8_t *base = rv > 0 ? Bv : static_cast<const uint8_t *>(p.q);
+            const uint8_t *base = pick_uniform(rv > 0, Bv, p.q);
+            const int rlast = max(rv - 1, 0), on = rv > 0 ? 1 : 0;  // rv = 0: offset 0
 #pragma unroll
             for (int ci = 0; ci < 8; ++ci) {
                 const int row = 32 * (wave - 4) + 4 * ci + (lane >> 4);
-                const uint32_t off = rv > 0 ? static_cast<uint32_t>(min(row, rv - 1) * (kD * 2) + 16 * (lane & 15)) : 0u;
+                const uint32_t off = static_cast<uint32_t>((min(row, rlast) * (kD * 2) + 16 * (lane & 15)) * on);
                 __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
                                                  (__attribute__((address_space(3))) void *)(sdst + 1024 * ci), 16, 0, 0);
             }
@@ -364,11 +388,12 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         if constexpr (F != kF32 && !TAIL) {
             const int t0 = tok0 + tile * kTile, tb = t0 + 8 * c4;
             if constexpr (F == kBF16) {
-                // always 8 loads (rv = 0 reads the first bytes of q), see dma_k
-                const uint8_t *base = rv > 0 ? Av : static_cast<const uint8_t *>(p.q);
+                // always 8 loads, without branches (rv = 0 reads the first bytes of q)
+                const uint8_t *base = pick_uniform(rv > 0, Av, p.q);
+                const int rlast = max(rv - 1, 0), on = rv > 0 ? 2 : 0;  // rv = 0: offset 0
 #pragma unroll
                 for (int mr = 0; mr < 8; ++mr) {
-                    const uint32_t off = rv > 0 ? static_cast<uint32_t>((min(16 * mr + ln, rv - 1) * T + tb) * 2) : 0u;
+                    const uint32_t off = static_cast<uint32_t>((min(16 * mr + ln, rlast) * T + tb) * on);
                     vraw[mr] = *reinterpret_cast<const uint4 *>(base + off);
                 }
             } else if (rv > 0) {
@@ -488,15 +513,40 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         uint16_t *bk = reinterpret_cast<uint16_t *>(lds + L.bk);
         const uint8_t *tmp = lds + L.stage;
         const float *bsc = reinterpret_cast<const float *>(tmp + 128 * kD);  // int8 only
+        // 4-bit: B_k's rows are first decoded into bf16 rows (row r at 256 r bytes,
+        // after the raw codes and scales), so that the fragments come from them by
+        // the bf16 path's transposing reads.  Thread t: row t / 4, dims 32 (t % 4) ..
+        uint8_t *rows4 = lds + L.stage + kBkRows4;
+        if constexpr (F == kI4) {
+            const int r = tid >> 2, qd = tid & 3;
+            uint32_t hw[16];
+            if (r < rk) {
+                const uint4 cw = *reinterpret_cast<const uint4 *>(tmp + r * (kD / 2) + 16 * qd);
+                const float sc = reinterpret_cast<const float *>(tmp + rk * (kD / 2))[r * (kD / kI4Group) + qd];
+                const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        hw[4 * c + e] = f32x2_to_bf16x2_bits(nib(w4[c], 2 * e) * sc, nib(w4[c], 2 * e + 1) * sc);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) hw[k] = 0u;
+            }
+            uint4 *dst = reinterpret_cast<uint4 *>(rows4 + r * (kD * 2) + 64 * qd);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dst[c] = make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]);
+            __syncthreads();
+        }
         for (int q = tid; q < 8 * 4 * 64; q += kThreads) {
             const int l2 = q & 63, ks = (q >> 6) & 3, mt = q >> 8;
             if (ks >= KS) continue;
             const int j = 16 * mt + (l2 & 15), r0 = 32 * ks + 8 * (l2 >> 4);
-            if constexpr (F == kBF16) {
+            if constexpr (F == kBF16 || F == kI4) {
                 // ranks r0 .. r0 + 7 of dim j by two transposing reads of the staged
                 // rows (lane (c, i) of a 16-lane group addresses row r0 + i / 4 (+ 4),
                 // dims 16 mt + 4 (i % 4) ..); rows past rk (repeats) become zero
-                const uint8_t *p0 = tmp + (r0 + ((l2 & 15) >> 2)) * (kD * 2) + (16 * mt + 4 * (l2 & 3)) * 2;
+                const uint8_t *p0 = (F == kI4 ? rows4 : tmp) + (r0 + ((l2 & 15) >> 2)) * (kD * 2) + (16 * mt + 4 * (l2 & 3)) * 2;
                 u16x8_t f0 = cat8(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * kD * 2));
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -510,14 +560,7 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
                 const int r = r0 + e;
                 v[e] = 0.f;
                 if (r < rk) {
-                    if constexpr (F == kBF16) v[e] = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(tmp)[r * kD + j]);
-                    else if constexpr (F == kI8) v[e] = static_cast<float>(reinterpret_cast<const int8_t *>(tmp)[r * kD + j]) * bsc[r];
-                    else if constexpr (F == kI4) {
-                        const int byte = tmp[r * (kD / 2) + (j >> 1)];
-                        const int n = (j & 1) ? (byte >> 4) : (byte & 15);
-                        v[e] = static_cast<float>(n >= 8 ? n - 16 : n) *
-                               reinterpret_cast<const float *>(tmp + rk * (kD / 2))[r * (kD / kI4Group) + j / kI4Group];
-                    }
+                    if constexpr (F == kI8) v[e] = static_cast<float>(reinterpret_cast<const int8_t *>(tmp)[r * kD + j]) * bsc[r];
                     else v[e] = load_elem<F>(Bk, static_cast<int64_t>(r) * kD + j);
                 }
             }
@@ -543,6 +586,33 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     // the tile and staged at its end.
     const int my_tiles = tiles_valid > wave ? (tiles_valid - 1 - wave) / kWaves + 1 : 0;
     if (my_tiles > 0) stage_k(stg);
+    if constexpr (F == kBF16 && !TAIL) {
+        // Every prologue load has landed by now (the first tile's A_v pieces
+        // included).  Some are used only inside branches (the query rows, the
+        // first wave's angles, part of the step table); left pending on the
+        // paths that skip them, they would be carried into the tile loop, where
+        // with LDS DMA in flight the compiler waits for all memory operations
+        // (vmcnt(0)) at the first reuse of their registers, in every tile.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("" ::: "memory");
+    }
+    // bf16 blocks: a tile's u update (u = alpha u + A_v^T P^T) runs at the top
+    // of the next tile, right after the wait for that tile's DMA.  While an LDS
+    // DMA is in flight the compiler waits for every memory operation (vmcnt(0))
+    // before any use of a loaded register, so the A_v pieces are used only
+    // where nothing newer is in flight: a tile's pieces are loaded at its top
+    // and used at the next top, and its softmax weights wait in pf_prev.
+    u16x8_t pf_prev = {};
+    float alpha_prev = 1.f;
+    bool rescale_prev = false;
+    auto u_update_bf16 = [&]() {
+#pragma unroll
+        for (int mr = 0; mr < 8; ++mr)
+            if (mr < NTU) {
+                if (rescale_prev) u[mr] *= alpha_prev;
+                u[mr] = mfma16x16x32(__builtin_bit_cast(u16x8_t, vraw[mr]), pf_prev, u[mr]);
+            }
+    };
     // The loop reaches LDS through two restrict pointers, the staging rows and
     // the tables (disjoint regions), so that the compiler knows the staging DMA
     // does not write what the table reads load.
@@ -561,11 +631,12 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         if ((it + (wave >> 2)) & 1) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
         if constexpr (F == kBF16 && !TAIL) {
-            // this tile's DMA was issued just before the previous iteration's
-            // 8 A_v loads: wait for it
             if (it > 0) {
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+                // this tile's DMA and the previous tile's A_v pieces have landed
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 asm volatile("" ::: "memory");
+                u_update_bf16();  // the previous tile's
+                load_v(tile);     // used at the next top (the first tile's came with the prologue)
             }
         } else if (it + 1 < my_tiles) {
             load_k(tile + kWaves);  // a whole tile of latency cover
@@ -676,7 +747,6 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
                     asm volatile("" ::: "memory");
                     if (it + 1 < my_tiles) dma_k(tile + kWaves, stg);
                     else if (wave >= 4) dma_bv(stg);
-                    else dma_k(tile, stg);  // reloads itself (keeps the counts uniform)
                 }
             }
             // keep the table reads below after the rebuild (registers)
@@ -755,15 +825,17 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         u16x8_t pf[NS];
         frag_terms<NS>(pv, pf);
         const bool rescale = __any(alpha != 1.f);
-        if constexpr (!TAIL && F != kF32) {
+        if constexpr (F == kBF16 && !TAIL) {
+            pf_prev = pf[0];
+            alpha_prev = alpha;
+            rescale_prev = rescale;
+        } else if constexpr (!TAIL && F != kF32) {
 #pragma unroll
             for (int mr = 0; mr < 8; ++mr)
                 if (mr < NTU) {
                     if (rescale) u[mr] *= alpha;
                     u16x8_t af;
-                    if constexpr (F == kBF16) {
-                        af = __builtin_bit_cast(u16x8_t, vraw[mr]);
-                    } else if constexpr (F == kI4) {
+                    if constexpr (F == kI4) {
                         const float sc = __uint_as_float(vraw[mr].y);
                         float v[8];
 #pragma unroll
@@ -854,7 +926,7 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         }
 
         if constexpr (F == kBF16 && !TAIL) {
-            load_v(it + 1 < my_tiles ? tile + kWaves : tile);
+            // (this tile's A_v pieces were loaded at its top)
         } else if (it + 1 < my_tiles) {
             load_v(tile + kWaves);
             wave_lds_sync();  // this tile's staged keys have been read
@@ -869,6 +941,29 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         // the DMAs land before the barrier that starts the merge
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         asm volatile("" ::: "memory");
+        if (my_tiles > 0) u_update_bf16();  // the last tile's
+    }
+    if constexpr (F == kI4 && !TAIL) {
+        // B_v's code rows and scales (rv x 80 bytes, at most 640 16-byte chunks)
+        // go by LDS DMA into the staging rows of waves 4 and 5, which lie past the
+        // merge's own areas: chunk c at byte 16 c from the start of wave 4's rows.
+        // A wave writes only its own rows, which it no longer reads: wave 4
+        // chunks 0 .. 511, wave 5 chunks 512 .. 639 (chunks past the last repeat it).
+        if (wave == 4 || wave == 5) {
+            const int n16v = rv * (kD / 2 + 4 * (kD / kI4Group)) / 16;
+            const uint8_t *base = pick_uniform(n16v > 0, Bv, p.q);
+            const int last = max(n16v - 1, 0), on = n16v > 0 ? 16 : 0;
+            uint8_t *dst = lds + L.stage + 4 * 128 * stage_pitch(F);
+            const int ninst = wave == 4 ? 8 : 2;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (k < ninst) {
+                    const int c0 = 512 * (wave - 4) + 64 * k;
+                    const uint32_t off = static_cast<uint32_t>(min(c0 + lane, last) * on);
+                    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
+                                                     (__attribute__((address_space(3))) void *)(dst + 16 * c0), 16, 0, 0);
+                }
+        }
     }
 
     // ---- merge the waves (log-sum-exp) and apply B_v
@@ -878,6 +973,7 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     float *uw = reinterpret_cast<float *>(lds + L.uw);
     float *mlw = reinterpret_cast<float *>(lds + L.mlw);
     float *uacc = reinterpret_cast<float *>(lds + L.uacc);
+    const uint8_t *bv4 = lds + L.stage + 4 * 128 * stage_pitch(F);  // 4-bit B_v (DMA'd after the loop)
     if (c4 == 0) {
         mlw[(wave * 16 + ln) * 2] = m_run;
         mlw[(wave * 16 + ln) * 2 + 1] = l_run;
@@ -903,7 +999,7 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
                 const uint8_t *p0 = bvl + (32 * ks + 8 * c4 + (ln >> 2)) * (kD * 2) + (16 * wave + 4 * (ln & 3)) * 2;
                 bvf[0][ks] = cat8(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * kD * 2));
             }
-    } else if constexpr (!TAIL) {
+    } else if constexpr (!TAIL && F != kI4) {
         if (rv > 0) {
             const int dim = 16 * wave + ln;
 #pragma unroll
@@ -913,15 +1009,7 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
                 for (int e = 0; e < 8; ++e) {
                     const int r = 32 * ks + 8 * c4 + e;
                     const int rc = min(r, rv - 1);
-                    float x;
-                    if constexpr (F == kI4) {
-                        const int byte = Bv[rc * (kD / 2) + (dim >> 1)];
-                        const int n = (dim & 1) ? (byte >> 4) : (byte & 15);
-                        x = static_cast<float>(n >= 8 ? n - 16 : n) *
-                            reinterpret_cast<const float *>(Bv + rv * (kD / 2))[rc * (kD / kI4Group) + dim / kI4Group];
-                    } else {
-                        x = load_elem<F>(Bv, static_cast<int64_t>(rc) * kD + dim);
-                    }
+                    float x = load_elem<F>(Bv, static_cast<int64_t>(rc) * kD + dim);
                     if constexpr (F == kI8) x *= p.v_bscale[static_cast<int64_t>(fid) * kD + rc];
                     v[e] = r < rv ? x : 0.f;
                 }
@@ -932,7 +1020,35 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
             }
         }
     }
+    if constexpr (F == kI4 && !TAIL) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the B_v DMA has landed (before the barrier)
+        asm volatile("" ::: "memory");
+    }
     __syncthreads();
+    if constexpr (F == kI4 && !TAIL) {
+        // 4-bit B_v fragments from the chunks DMA'd after the loop
+        if (rv > 0) {
+            const int dim = 16 * wave + ln;
+            const float *bsc = reinterpret_cast<const float *>(bv4 + rv * (kD / 2));
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                if (ks < KSV) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int r = 32 * ks + 8 * c4 + e;
+                        const int rc = min(r, rv - 1);
+                        const int byte = bv4[rc * (kD / 2) + (dim >> 1)];
+                        const int n = (dim & 1) ? (byte >> 4) : (byte & 15);
+                        const float x = static_cast<float>(n >= 8 ? n - 16 : n) * bsc[rc * (kD / kI4Group) + dim / kI4Group];
+                        v[e] = r < rv ? x : 0.f;
+                    }
+                    u16x8_t f[1];
+                    frag_terms<1>(v, f);
+                    bvf[0][ks] = f[0];
+                }
+        }
+    }
     for (int e = tid; e < 16 * rpad; e += kThreads) {
         const int g = e / rpad, r = e - g * rpad;
         float M = -INFINITY;
