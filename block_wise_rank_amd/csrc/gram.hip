@@ -11,12 +11,9 @@
 // One workgroup (4 waves) per (block, token split); wave w owns the 64 x 64
 // quadrant (w / 2, w % 2) of G as 2 x 2 tiles of 32 x 32.
 //
-// bf16 inputs (the method's cache) have their own kernel: tiles are
-// double-buffered in LDS with the next tile's loads in flight during the
-// current tile's products, and the fragments are read with transposing LDS
-// loads (two per fragment instead of eight 16-bit reads), from rows of 288
-// bytes so that the 4 rows x 64 bytes of a half-wave's read cover every bank
-// exactly twice.
+// bf16 inputs (the method's cache) have their own kernel: tiles stream through
+// an LDS ring filled by DMA several tiles ahead, and the fragments are read with
+// transposing LDS loads (two per fragment instead of eight 16-bit reads).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -123,22 +120,106 @@ __global__ __launch_bounds__(256) void gram_kernel(const void *__restrict__ x,
             }
 }
 
-constexpr int kBP = 288;  // LDS row pitch in bytes (bf16 kernel)
+// bf16 X streams through a ring of kGRing 32-token tiles in LDS, filled by LDS
+// DMA (global_load_lds, 16 bytes per lane, no registers) kGAhead tiles ahead of
+// use; wave w moves rows 8 w .. 8 w + 7 of every tile.  Rows are 256 bytes,
+// unpadded; a row's 16-byte chunk c sits at chunk c ^ 4 (row % 4).  A
+// transposing read of 64 lanes touches rows {0..3, 8..11} (plus a multiple of
+// 4) and four consecutive chunks of each; with the swizzle the eight rows fall
+// on four distinct groups of four chunks, two rows each, so every bank is hit
+// exactly twice (512 bytes in two passes), as with a padded row.
+constexpr int kGT = 32;                      // tokens per ring tile
+constexpr int kGRing = 6;                    // ring slots (48 KiB: three workgroups per CU)
+constexpr int kGAhead = kGRing - 1;          // tiles in flight ahead of use
+constexpr int kGTileB = kGT * kD * 2;        // bytes of one tile
+constexpr int kGDma = kGTileB / 1024 / 4;    // 1 KiB DMA instructions per wave and tile
+
+// s_waitcnt immediate: at most n vector memory operations outstanding.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+
+// The sixteen transposing reads of one tile (four fragment bases, two k-steps
+// of 16 tokens, two 4-row halves), waited for inside the same asm block: the
+// compiler then sees no LDS read that the DMAs in flight might write (it would
+// wait for all of them), and no result is used before it has arrived.
+__device__ __forceinline__ void read_tile_tr(u16x4_t (&o)[16], const uint32_t (&b)[4], uint32_t so) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    v4s r[16];
+    const uint32_t a0 = b[0] + so, a1 = b[1] + so, a2 = b[2] + so, a3 = b[3] + so;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %2, %17\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %4, %18\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %6, %19\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:5120\n\t"
+        "ds_read_b64_tr_b16 %10, %17 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:5120\n\t"
+        "ds_read_b64_tr_b16 %12, %18 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %13, %18 offset:5120\n\t"
+        "ds_read_b64_tr_b16 %14, %19 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:5120\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
+          "=&v"(r[14]), "=&v"(r[15])
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o[k] = __builtin_bit_cast(u16x4_t, r[k]);
+}
 
 __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t *__restrict__ x,
                                                         const int64_t *__restrict__ row0,
                                                         int64_t row_stride, int T, int splits,
                                                         float *__restrict__ gpart) {
-    __shared__ __align__(16) uint8_t tile[2][kTT * kBP];
+    __shared__ __align__(16) uint8_t ring[kGRing * kGTileB];
     const int blk = blockIdx.x / splits;
     const int sp = blockIdx.x - blk * splits;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int span = T / splits;
     const int t_begin = sp * span;
-    const uint16_t *xb = x + (row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride);
+    const int n_tiles = span / kGT;
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(x + (row0 ? row0[blk] : static_cast<int64_t>(blk) * T * row_stride)) +
+                        static_cast<int64_t>(t_begin) * row_stride * 2;
     const int mb = wave >> 1, nb = wave & 1;
     const int g = lane >> 4, j = lane & 15;  // 16-lane group, lane within it
+
+    // DMA of tile tau (clamped to the last tile) into slot tau % kGRing: lane L
+    // of instruction q writes row 4 q + L / 16, physical chunk L % 16.
+    auto dma = [&](int tau) __attribute__((always_inline)) {
+        const int tt = tau < n_tiles ? tau : n_tiles - 1;
+#pragma unroll
+        for (int k = 0; k < kGDma; ++k) {
+            const int q = kGDma * wave + k;
+            const int r = 4 * q + (lane >> 4), c = (lane & 15) ^ (4 * (r & 3));
+            const uint8_t *src = xb + (static_cast<int64_t>(kGT * tt + r) * row_stride) * 2 + 16 * c;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(ring + (tau % kGRing) * kGTileB + 1024 * q),
+                                             16, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int tau = 0; tau < kGAhead; ++tau) dma(tau);
+
+    // Fragment bases in slot 0: lane (g, j) reads features f + 16 (g % 2) + 4 (j % 4) .. + 3
+    // of rows 8 (g / 2) + j / 4 (and + 4) of a 16-token k-step, f = 64 mb + 32 i (A) or
+    // 64 nb + 32 i (B), i.e. column j of rows r0 .. r0 + 3 as a transposing read delivers it.
+    const int rr = 8 * (g >> 1) + (j >> 2);
+    uint32_t fbase[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int f = (q < 2 ? 64 * mb + 32 * q : 64 * nb + 32 * (q - 2)) + 16 * (g & 1) + 4 * (j & 3);
+        fbase[q] = lds_addr(ring) + rr * (kD * 2) + 16 * ((f >> 3) ^ (4 * (rr & 3))) + 2 * (f & 7);
+    }
 
     f32x16_t acc[2][2];
 #pragma unroll
@@ -146,46 +227,26 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t *__restri
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) acc[i][jj] = zero16();
 
-    // tile loads: token row c >> 4, 16-byte piece c & 15 for c = tid + 256 u
-    const int64_t off0 = static_cast<int64_t>(tid >> 4) * row_stride + (tid & 15) * 8;
-    const int64_t rstep = 16 * row_stride;  // c + 256 is 16 token rows further
-    const int so = (tid >> 4) * kBP + (tid & 15) * 16;
-    uint4 x0, x1, x2, x3;
-    auto load = [&](int t0) {
-        const uint16_t *p = xb + static_cast<int64_t>(t0) * row_stride + off0;
-        x0 = *reinterpret_cast<const uint4 *>(p);
-        x1 = *reinterpret_cast<const uint4 *>(p + rstep);
-        x2 = *reinterpret_cast<const uint4 *>(p + 2 * rstep);
-        x3 = *reinterpret_cast<const uint4 *>(p + 3 * rstep);
-    };
-    const int n_tiles = span / kTT;
-    load(t_begin);
-    for (int it = 0; it < n_tiles; ++it) {
-        uint8_t *tb = tile[it & 1];
-        *reinterpret_cast<uint4 *>(tb + so) = x0;
-        *reinterpret_cast<uint4 *>(tb + so + 16 * kBP) = x1;
-        *reinterpret_cast<uint4 *>(tb + so + 32 * kBP) = x2;
-        *reinterpret_cast<uint4 *>(tb + so + 48 * kBP) = x3;
-        if (it + 1 < n_tiles) load(t_begin + (it + 1) * kTT);
+    for (int t = 0; t < n_tiles; ++t) {
+        // this wave's part of tile t has landed (each later tile added kGDma
+        // operations); the barrier makes every part visible and frees slot
+        // (t - 1) % kGRing for the tile kGAhead ahead
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kGAhead - 1) * kGDma));
         __syncthreads();
+        dma(t + kGAhead);
+        u16x4_t o[16];
+        read_tile_tr(o, fbase, (t % kGRing) * kGTileB);
 #pragma unroll
-        for (int ks = 0; ks < kTT; ks += 16) {
-            // lane (g, j): features base + 16 (g % 2) + j, tokens ks + 8 (g / 2) + 4 h + 0..3
-            const uint8_t *rowp = tb + (ks + 8 * (g >> 1) + (j >> 2)) * kBP + (16 * (g & 1) + 4 * (j & 3)) * 2;
-            u16x8_t fa[2], fb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint8_t *pa = rowp + (64 * mb + 32 * i) * 2;
-                const uint8_t *pb = rowp + (64 * nb + 32 * i) * 2;
-                fa[i] = cat8(lds_read_tr16(pa), lds_read_tr16(pa + 4 * kBP));
-                fb[i] = cat8(lds_read_tr16(pb), lds_read_tr16(pb + 4 * kBP));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mfma32x32x16(fa[i], fb[jj], acc[i][jj]);
+        for (int ks = 0; ks < 2; ++ks) {
+            const u16x8_t fa0 = cat8(o[8 * ks + 0], o[8 * ks + 1]), fa1 = cat8(o[8 * ks + 2], o[8 * ks + 3]);
+            const u16x8_t fb0 = cat8(o[8 * ks + 4], o[8 * ks + 5]), fb1 = cat8(o[8 * ks + 6], o[8 * ks + 7]);
+            acc[0][0] = mfma32x32x16(fa0, fb0, acc[0][0]);
+            acc[0][1] = mfma32x32x16(fa0, fb1, acc[0][1]);
+            acc[1][0] = mfma32x32x16(fa1, fb0, acc[1][0]);
+            acc[1][1] = mfma32x32x16(fa1, fb1, acc[1][1]);
         }
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing (discarded) tiles have landed
 
     float *gp = gpart + (static_cast<int64_t>(blk) * splits + sp) * kD * kD;
 #pragma unroll
