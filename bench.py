@@ -288,6 +288,46 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
 
 
+def hbm_reference(torch, gib=8, reps=5):
+    """What this board's HBM delivers to plain torch kernels, after the timed
+    regions: a streaming read (an fp32 tensor of `gib` GiB summed row-wise as
+    [65536, -1], the fastest torch read found) and a copy (read + write).  The
+    HBM-bound kernels are also reported as a fraction of the read rate."""
+    n = gib << 30
+    x = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    xf = x.view(torch.float32).view(65536, -1)
+
+    def med(fn):
+        ts = []
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts = sorted(ts[1:])
+        return ts[len(ts) // 2]
+    read_ms = med(lambda: xf.sum(dim=1))
+    copy_ms = med(lambda: y.copy_(x))
+    del x, y, xf
+    torch.cuda.empty_cache()
+    return {"read_GBs": round(n / read_ms / 1e6, 1), "copy_GBs": round(2 * n / copy_ms / 1e6, 1),
+            "bytes": n, "how": f"torch: {gib} GiB as fp32 [65536, -1].sum(dim=1) (read); copy_ (read + write); "
+                                  f"median of {reps}"}
+
+
+def annotate_reference(res, ref):
+    """frac_of_read_reference beside frac for every GB/s entry of a workload's result."""
+    for r in (res.get("rooflines") or {}).values():
+        if r.get("unit") == "GB/s":
+            r["frac_of_read_reference"] = round(r["achieved"] / ref["read_GBs"], 4)
+    for r in (res.get("decode_only_rooflines") or {}).values():
+        if "achieved_GBs" in r:
+            r["frac_of_read_reference"] = round(r["achieved_GBs"] / ref["read_GBs"], 4)
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -879,6 +919,10 @@ def main():
             extra[f"config{c}"] = r
         torch.cuda.empty_cache()
 
+    ref = hbm_reference(torch)
+    annotate_reference(main_res, ref)
+    for r in extra.values():
+        annotate_reference(r, ref)
     step_ms = main_res.pop("step_ms")
     out = {
         "metric": METRIC,
@@ -900,6 +944,7 @@ def main():
                             "alone: breakdown.blocks_per_s",
     }
     out.update(main_res)
+    out["hbm_reference"] = ref
     out["workloads"] = extra
     print(json.dumps(out))
     return 0
