@@ -91,12 +91,12 @@ constexpr int kD = 128;
 constexpr int kMaxSweeps = 30;
 constexpr float kJacobiTol = 1e-6f;
 // The solve ends after a sweep whose relative off-diagonals all stayed below
-// 5e-3: quadratic convergence leaves them far smaller, and the singular values
+// 3e-3: quadratic convergence leaves them far smaller, and the singular values
 // are then recomputed as Rayleigh quotients ||X v||, second order in the
 // eigenvector error.  On the planted workloads the worst singular value error
-// stays below 15% of its tolerance (3e-3: 2.4%; 1e-2 exceeds it on one block),
-// with 9.1 sweeps on average instead of 9.4.
-constexpr float kJacobiStopTol = 5e-3f;
+// is 2.4% of its tolerance at 9.4 sweeps on average; 5e-3 saves 0.3 sweeps but
+// raises it to 14%, and 1e-2 exceeds it on one block.
+constexpr float kJacobiStopTol = 3e-3f;
 constexpr size_t kMat = sizeof(float) * kD * kD;  // one 128 x 128 fp32 matrix
 
 // Split the token dimension of the Gram when there are too few blocks to fill

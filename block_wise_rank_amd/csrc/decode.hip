@@ -1133,9 +1133,18 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeParams 
             den_part += c * p.part_ml[((base + c0 + i) * G + g) * 2 + 1];
         }
         __syncthreads();
-        for (int i = 0; i < cn; ++i) {
-            const float c = coef[i];
-            if (c != 0.f) num += c * p.part_o[((base + c0 + i) * G + g) * kD + tid];
+        // eight loads in flight at a time (indices clamped; a split with weight 0
+        // may hold stale values, which the select keeps out), summed in order
+        for (int i0 = 0; i0 < cn; i0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = p.part_o[((base + c0 + min(i0 + u, cn - 1)) * G + g) * kD + tid];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u < cn) {
+                    const float c = coef[i0 + u];
+                    num += c != 0.f ? c * v[u] : 0.f;
+                }
         }
         __syncthreads();
     }
