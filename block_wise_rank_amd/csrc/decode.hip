@@ -65,7 +65,7 @@ constexpr int kQP = 132;
 // codes and scales of up to 128 ranks (80 bytes each)
 constexpr int kBkRows4 = 128 * (kD / 2 + 4 * (kD / kI4Group));
 
-__host__ __device__ inline int align16(int v) { return (v + 15) & ~15; }
+__host__ __device__ constexpr int align16(int v) { return (v + 15) & ~15; }
 
 // A_k staging pitch per rank row of a 32-token tile (bytes); fp32 factors are
 // read straight from memory.
@@ -75,8 +75,18 @@ __host__ __device__ inline int stage_pitch(int f) { return (f == kBF16 || f == k
 struct LdsLayout {
     int ang, qs, bk, rope, base, stage, loop_end;      // loop phase
     int uw, mlw, uacc, merge_end;                       // merge phase (aliases the loop phase)
+    int bvraw, bvrows;                                  // 4-bit B_v: codes, decoded rows
     int total;
 };
+
+// Merge-phase areas: per-wave u rows, per-wave (m, l), merged u
+constexpr int kMergeEnd = align16(align16(align16(kWaves * 16 * kUP * 4) + kWaves * 16 * 2 * 4) + 16 * kUP * 4);
+// 4-bit B_v: its codes and scales (at most 128 x 80 bytes) land in the last
+// 10 KiB of the staging area, the staging rows of waves 6 and 7; the decoded
+// bf16 rows (128 x 256 bytes) go between the merge areas and them, which needs
+// the staging area to start at least this far in
+constexpr int kBvRaw = kWaves * 128 * 64 - 128 * (kD / 2 + 4 * (kD / kI4Group));
+constexpr int kI4StageMin = kMergeEnd + 128 * kD * 2 - kBvRaw;
 
 __host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool tail, int G) {
     LdsLayout L;
@@ -86,6 +96,7 @@ __host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool
     L.rope = align16(L.bk + (tail ? 0 : ns * 8 * 4 * 64 * 16));
     L.base = align16(L.rope + 32 * kRP * 8);
     L.stage = align16(L.base + n_tiles * 64 * 8);
+    if (f == kI4 && !tail && L.stage < kI4StageMin) L.stage = kI4StageMin;
     int stage = 0;
     if (!tail) stage = kWaves * 128 * stage_pitch(f);
     else if (f == kBF16) stage = kWaves * 32 * kTVP;
@@ -97,6 +108,8 @@ __host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool
     L.mlw = align16(L.uw + kWaves * 16 * kUP * 4);
     L.uacc = align16(L.mlw + kWaves * 16 * 2 * 4);
     L.merge_end = align16(L.uacc + 16 * kUP * 4);
+    L.bvraw = L.stage + kBvRaw;
+    L.bvrows = L.stage > L.merge_end ? L.stage : L.merge_end;
     L.total = L.loop_end > L.merge_end ? L.loop_end : L.merge_end;
     return L;
 }
@@ -945,20 +958,21 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     }
     if constexpr (F == kI4 && !TAIL) {
         // B_v's code rows and scales (rv x 80 bytes, at most 640 16-byte chunks)
-        // go by LDS DMA into the staging rows of waves 4 and 5, which lie past the
-        // merge's own areas: chunk c at byte 16 c from the start of wave 4's rows.
-        // A wave writes only its own rows, which it no longer reads: wave 4
-        // chunks 0 .. 511, wave 5 chunks 512 .. 639 (chunks past the last repeat it).
-        if (wave == 4 || wave == 5) {
+        // go by LDS DMA into the last 10 KiB of the staging area, chunk c at byte
+        // 16 c: the staging rows of waves 6 (chunks 0 .. 127) and 7 (128 .. 639),
+        // which each writes only once its own tiles are done (chunks past the last
+        // repeat it).  They land before the second barrier of the merge.
+        if (wave >= 6) {
             const int n16v = rv * (kD / 2 + 4 * (kD / kI4Group)) / 16;
             const uint8_t *base = pick_uniform(n16v > 0, Bv, p.q);
             const int last = max(n16v - 1, 0), on = n16v > 0 ? 16 : 0;
-            uint8_t *dst = lds + L.stage + 4 * 128 * stage_pitch(F);
-            const int ninst = wave == 4 ? 8 : 2;
+            uint8_t *dst = lds + L.bvraw;
+            const int ninst = wave == 6 ? 2 : 8;
+            const int cbase = wave == 6 ? 0 : 128;
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 if (k < ninst) {
-                    const int c0 = 512 * (wave - 4) + 64 * k;
+                    const int c0 = cbase + 64 * k;
                     const uint32_t off = static_cast<uint32_t>(min(c0 + lane, last) * on);
                     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
                                                      (__attribute__((address_space(3))) void *)(dst + 16 * c0), 16, 0, 0);
@@ -973,7 +987,6 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     float *uw = reinterpret_cast<float *>(lds + L.uw);
     float *mlw = reinterpret_cast<float *>(lds + L.mlw);
     float *uacc = reinterpret_cast<float *>(lds + L.uacc);
-    const uint8_t *bv4 = lds + L.stage + 4 * 128 * stage_pitch(F);  // 4-bit B_v (DMA'd after the loop)
     if (c4 == 0) {
         mlw[(wave * 16 + ln) * 2] = m_run;
         mlw[(wave * 16 + ln) * 2 + 1] = l_run;
@@ -1026,28 +1039,28 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     }
     __syncthreads();
     if constexpr (F == kI4 && !TAIL) {
-        // 4-bit B_v fragments from the chunks DMA'd after the loop
-        if (rv > 0) {
-            const int dim = 16 * wave + ln;
-            const float *bsc = reinterpret_cast<const float *>(bv4 + rv * (kD / 2));
+        // 4-bit B_v -> bf16 rows (row r at 256 r bytes), the bf16 path's layout for
+        // the transposing fragment reads below.  Thread t: row t / 4, dims
+        // 32 (t % 4) .. + 31; rows past rv are zero.
+        const uint8_t *bv4 = lds + L.bvraw;
+        const int r = tid >> 2, qd = tid & 3;
+        uint32_t hw[16];
+        if (r < rv) {
+            const uint4 cw = *reinterpret_cast<const uint4 *>(bv4 + r * (kD / 2) + 16 * qd);
+            const float sc = reinterpret_cast<const float *>(bv4 + rv * (kD / 2))[r * (kD / kI4Group) + qd];
+            const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                if (ks < KSV) {
-                    float v[8];
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int r = 32 * ks + 8 * c4 + e;
-                        const int rc = min(r, rv - 1);
-                        const int byte = bv4[rc * (kD / 2) + (dim >> 1)];
-                        const int n = (dim & 1) ? (byte >> 4) : (byte & 15);
-                        const float x = static_cast<float>(n >= 8 ? n - 16 : n) * bsc[rc * (kD / kI4Group) + dim / kI4Group];
-                        v[e] = r < rv ? x : 0.f;
-                    }
-                    u16x8_t f[1];
-                    frag_terms<1>(v, f);
-                    bvf[0][ks] = f[0];
-                }
+                for (int e = 0; e < 4; ++e)
+                    hw[4 * c + e] = f32x2_to_bf16x2_bits(nib(w4[c], 2 * e) * sc, nib(w4[c], 2 * e + 1) * sc);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) hw[k] = 0u;
         }
+        uint4 *dst = reinterpret_cast<uint4 *>(lds + L.bvrows + r * (kD * 2) + 64 * qd);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[c] = make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]);
     }
     for (int e = tid; e < 16 * rpad; e += kThreads) {
         const int g = e / rpad, r = e - g * rpad;
@@ -1076,6 +1089,15 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         ml[2 * tid + 1] = Ls;
     }
     __syncthreads();
+    if constexpr (F == kI4 && !TAIL) {
+        // 4-bit B_v fragments from the rows decoded above, as for bf16
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            if (ks < KSV) {
+                const uint8_t *p0 = lds + L.bvrows + (32 * ks + 8 * c4 + (ln >> 2)) * (kD * 2) + (16 * wave + 4 * (ln & 3)) * 2;
+                bvf[0][ks] = cat8(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * kD * 2));
+            }
+    }
     if constexpr (TAIL) {
         for (int e = tid; e < G * kD; e += kThreads) po[e] = uacc[(e >> 7) * kUP + (e & 127)];
     } else {
@@ -1235,6 +1257,7 @@ bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int spli
     if (L.total > kMaxLds) return false;
     // bf16: B_v is staged in the upper half of the staging rows during the merge
     if (f_type == kBF16 && L.merge_end > L.stage + kWaves / 2 * 128 * stage_pitch(kBF16)) return false;
+    if (f_type == kI4 && L.bvrows + 128 * kD * 2 > L.bvraw) return false;
     if (has_tail) {
         const int tns = tail_type == kF32 ? 2 : 1;
         if (lds_layout(tail_type, tns, split / kTile, true, G).total > kMaxLds) return false;
