@@ -30,6 +30,7 @@ _dp = ctypes.POINTER(ctypes.c_double)
 _ip = ctypes.POINTER(ctypes.c_int32)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _i8p = ctypes.POINTER(ctypes.c_int8)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
 
 
 def build(force: bool = True) -> str:
@@ -87,6 +88,8 @@ def load(path: str):
     L.oracle_quant_int8_rows.restype = None
     L.oracle_quant_int4_groups.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _i8p, _dp]
     L.oracle_quant_int4_groups.restype = None
+    L.oracle_quant_int2_groups.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _u8p, _dp]
+    L.oracle_quant_int2_groups.restype = None
     L.oracle_rope.argtypes = [_dp, ctypes.c_int, ctypes.c_double, ctypes.c_double]
     L.oracle_rope.restype = None
     L.oracle_attention.argtypes = [_dp, ctypes.c_int, ctypes.c_int64, _dp, _dp, _i64p,
@@ -266,13 +269,34 @@ def quant_int4_groups(M, group: int = I4_GROUP):
     return scale, codes, deq
 
 
+I2_GROUP = 32  # elements per 2-bit scale group
+
+
+def quant_int2_groups(M, group: int = I2_GROUP):
+    """Symmetric 2-bit codes per run of `group` elements of each row: s =
+    max|x|/3, code c in 0..3 for the nearest level (2c - 3) s.  Returns (scale
+    [rows, cols/group], codes uint8 [rows, cols], dequant fp64)."""
+    M = _f64(M)
+    if M.ndim != 2:
+        raise ValueError("quant_int2_groups expects a 2-D array")
+    rows, cols = M.shape
+    if cols % group:
+        raise ValueError(f"row length {cols} is not a multiple of the group {group}")
+    scale = np.zeros((rows, cols // group))
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    deq = np.zeros((rows, cols))
+    if rows and cols:
+        lib().oracle_quant_int2_groups(_ptr(M), rows, cols, group, _ptr(scale), _ptr(codes, _u8p), _ptr(deq))
+    return scale, codes, deq
+
+
 def store(A, B, storage: str):
     """Apply the storage encoding to a factor pair; returns the decoded (A, B) in fp64.
 
-    storage: "f32" | "bf16" | "i8" | "i4".  For "i8" every row of A (one per
-    token) and every row of B (one per rank) gets its own absmax scale.  For "i4"
-    the rank rows of A^T (T tokens) and of B (d dims) are cut into groups of
-    I4_GROUP consecutive elements with a scale each.
+    storage: "f32" | "bf16" | "i8" | "i4" | "i2".  For "i8" every row of A (one
+    per token) and every row of B (one per rank) gets its own absmax scale.  For
+    "i4" and "i2" the rank rows of A^T (T tokens) and of B (d dims) are cut into
+    groups of 32 consecutive elements with a scale each.
     """
     if storage == "f32":
         return round_f32(A), round_f32(B)
@@ -290,6 +314,12 @@ def store(A, B, storage: str):
         if A.shape[1] == 0:
             return A.copy(), B.copy()
         return quant_int4_groups(A.T)[2].T.copy(), quant_int4_groups(B)[2]
+    if storage == "i2":
+        A = _f64(A)
+        B = _f64(B)
+        if A.shape[1] == 0:
+            return A.copy(), B.copy()
+        return quant_int2_groups(A.T)[2].T.copy(), quant_int2_groups(B)[2]
     raise ValueError(f"unknown storage {storage!r}")
 
 

@@ -48,6 +48,12 @@
  *                       absmax scale s = max|x| / 7 and codes rint(x / s) in
  *                       [-7, 7].  The quantiser itself is this project's own
  *                       (the pages do not specify one).
+ *   oracle_quant_int2_groups
+ *                       2-bit storage, the lowest width of that composition:
+ *                       every run of `group` consecutive elements of a row
+ *                       gets s = max|x| / 3 and one of four symmetric levels
+ *                       (2c - 3) s, c = 0..3, the nearest to x.  Also this
+ *                       project's own quantiser.
  *   oracle_rope / oracle_attention
  *                       exact softmax attention of a rotary-embedded query over
  *                       rotary-embedded reconstructed keys: keys are compressed
@@ -56,7 +62,7 @@
  *                       their absolute positions.
  *
  * All arithmetic is IEEE fp64 except where a storage format forces a narrower
- * decision (the INT8 and 4-bit code decisions are taken in fp32, the precision
+ * decision (the INT8, 4-bit and 2-bit code decisions are taken in fp32, the precision
  * the GPU kernel takes them in).
  */
 #include <float.h>
@@ -473,6 +479,46 @@ void oracle_quant_int4_groups(const double *M, int rows, int cols, int group, do
                 codes[i] = (int8_t)q;
                 if (dequant)
                     dequant[i] = (double)((float)q * s);
+            }
+        }
+    }
+}
+
+/* Symmetric 2-bit codes per group of `group` consecutive elements of each   */
+/* row (cols a multiple of group): s = max|x| / 3 and code c in 0..3 for the  */
+/* level (2c - 3) s nearest to x: with q = x / s, |q| >= 2 takes the outer    */
+/* level of x's sign and |q| < 2 the inner one (ties away from zero; x = 0   */
+/* takes +s).  A run with s = 0 gets code 2 (value 0).  Decided in fp32, the */
+/* precision the GPU kernel decides it in.  scale is [rows][cols/group].     */
+void oracle_quant_int2_groups(const double *M, int rows, int cols, int group, double *scale,
+                              uint8_t *codes, double *dequant)
+{
+    const int ng = cols / group;
+    for (int r = 0; r < rows; ++r) {
+        for (int g = 0; g < ng; ++g) {
+            const double *run = M + (size_t)r * cols + (size_t)g * group;
+            float m = 0.0f;
+            for (int c = 0; c < group; ++c) {
+                float a = fabsf((float)run[c]);
+                if (a > m)
+                    m = a;
+            }
+            float s = m / 3.0f;
+            scale[(size_t)r * ng + g] = (double)s;
+            for (int c = 0; c < group; ++c) {
+                int q = 2;
+                if (s > 0.0f) {
+                    float xf = (float)run[c];
+                    float v = xf / s;
+                    if (xf < 0.0f)
+                        q = v <= -2.0f ? 0 : 1;
+                    else
+                        q = v >= 2.0f ? 3 : 2;
+                }
+                const size_t i = (size_t)r * cols + (size_t)g * group + c;
+                codes[i] = (uint8_t)q;
+                if (dequant)
+                    dequant[i] = (double)((float)(2 * q - 3) * s);
             }
         }
     }

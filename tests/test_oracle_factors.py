@@ -157,13 +157,57 @@ def test_int4_error_bound_and_groups(oracle_lib):
     assert np.array_equal(c3, codes) and np.allclose(d3, deq, rtol=1e-6, atol=0)
 
 
+def test_int2_hand_values(oracle_lib):
+    """Groups of 4 for hand values: s = max|x|/3, code c for the nearest level
+    (2c - 3) s, |x|/s = 2 going to the outer level, 0 to +s, a zero run to code 2."""
+    M = np.array([[3.0, -1.0, 2.0, -2.0, 6.0, 0.0, -1.5, 1.0],
+                  [0.0, 0.0, 0.0, 0.0, -0.3, 0.1, 0.25, -0.19]])
+    scale, codes, deq = oracle_lib.quant_int2_groups(M, group=4)
+    assert scale[0].tolist() == [1.0, 2.0]
+    assert list(codes[0]) == [3, 1, 3, 0, 3, 2, 1, 2]
+    assert deq[0].tolist() == [3.0, -1.0, 3.0, -3.0, 6.0, 2.0, -2.0, 2.0]
+    assert scale[1][0] == 0.0 and list(codes[1][:4]) == [2, 2, 2, 2] and (deq[1][:4] == 0).all()
+    s = np.float32(np.float32(0.3) / np.float32(3.0))
+    assert scale[1][1] == float(s)
+    assert list(codes[1][4:]) == [0, 2, 3, 1]
+    assert deq[1][4:].tolist() == [float(np.float32(k) * s) for k in (-3, 1, 3, -1)]
+
+
+def test_int2_error_bound_and_groups(oracle_lib):
+    rng = np.random.default_rng(6)
+    M = rng.standard_normal((48, 256)) * np.exp(2 * rng.standard_normal((48, 8))).repeat(32, axis=1)
+    scale, codes, deq = oracle_lib.quant_int2_groups(M)
+    assert scale.shape == (48, 8) and codes.max() <= 3
+    # the largest element of every group lands on an outer level, +-3 s
+    g = M.reshape(48, 8, 32)
+    top = np.abs(g).argmax(axis=2)
+    ctop = np.take_along_axis(codes.reshape(48, 8, 32), top[..., None], axis=2)[..., 0]
+    assert np.array_equal(ctop, np.where(np.take_along_axis(g, top[..., None], axis=2)[..., 0] < 0, 0, 3))
+    # levels 2s apart, the outer ones at +-max: |x - x~| <= s plus fp32 rounding
+    bound = np.repeat(scale, 32, axis=1) * (1 + 1e-5) + np.abs(M) * 2e-7
+    assert (np.abs(deq - M) <= bound).all()
+    # the dequantised value has the sign of x
+    assert (np.sign(deq) == np.where(M < 0, -1, 1)).all()
+    M2 = M.copy()
+    M2[5, 160:192] *= -100.0
+    s2, c2, _ = oracle_lib.quant_int2_groups(M2)
+    keep = np.ones((48, 8), dtype=bool)
+    keep[5, 5] = False
+    assert np.array_equal(s2[keep], scale[keep])
+    assert np.array_equal(c2.reshape(48, 8, 32)[keep], codes.reshape(48, 8, 32)[keep])
+    # the dequantised values quantise to themselves
+    s3, c3, d3 = oracle_lib.quant_int2_groups(deq)
+    assert np.array_equal(c3, codes) and np.allclose(d3, deq, rtol=1e-6, atol=0)
+
+
 def test_store_roundtrip_shapes(oracle_lib, block):
     X, sigma, V = block
     A, B = oracle_lib.project(X, V, 50)
-    for st in ("f32", "bf16", "i8", "i4"):
+    for st in ("f32", "bf16", "i8", "i4", "i2"):
         As, Bs = oracle_lib.store(A, B, st)
         assert As.shape == A.shape and Bs.shape == B.shape
         rel = np.linalg.norm(oracle_lib.reconstruct(As, Bs) - oracle_lib.reconstruct(A, B)) / \
             np.linalg.norm(oracle_lib.reconstruct(A, B))
-        # 4-bit: each element moves by at most s/2 = max|group|/14
-        assert rel <= {"f32": 1e-6, "bf16": 1e-2, "i8": 3e-2, "i4": 0.2}[st]
+        # 4-bit: each element moves by at most s/2 = max|group|/14; 2-bit: by at
+        # most s = max|group|/3
+        assert rel <= {"f32": 1e-6, "bf16": 1e-2, "i8": 3e-2, "i4": 0.2, "i2": 0.8}[st]

@@ -55,6 +55,15 @@ MUTATIONS = [
     ("int4 groups overlap", "const double *x = M + (size_t)r * cols + (size_t)g * group;",
      "const double *x = M + (size_t)r * cols + (size_t)g;",
      lambda: PF.test_int4_hand_values(oracle)),
+    ("int2 scale over 4 levels", "float s = m / 3.0f;", "float s = m / 4.0f;",
+     lambda: PF.test_int2_hand_values(oracle)),
+    ("int2 ties toward zero", "q = v <= -2.0f ? 0 : 1;", "q = v < -2.0f ? 0 : 1;",
+     lambda: PF.test_int2_hand_values(oracle)),
+    ("int2 groups overlap", "const double *run = M + (size_t)r * cols + (size_t)g * group;",
+     "const double *run = M + (size_t)r * cols + (size_t)g;",
+     lambda: PF.test_int2_hand_values(oracle)),
+    ("int2 zero on the negative level", "q = v >= 2.0f ? 3 : 2;", "q = v >= 2.0f ? 3 : (v > 0.0f ? 2 : 1);",
+     lambda: PF.test_int2_hand_values(oracle)),
     ("rope second component sign", "x[j + h] = a * s + b * c;", "x[j + h] = a * s - b * c;",
      lambda: PT.test_rope_matches_complex_form(oracle)),
     ("rope frequency exponent", "pow(base, -2.0 * j / (double)d)", "pow(base, -1.0 * j / (double)d)",
