@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--factor-dtype", default=None, help="bf16 | i8 | i4 (default: the config's)")
+    ap.add_argument("--factor-dtype", default=None, help="bf16 | i8 | i4 | i2 (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-offloaded cache measurement (compressed vs full KV over PCIe)")
@@ -376,7 +376,8 @@ def load_mfma(kernel, src_hash):
 # term order <= 2) for fp32 X; project: (x dtype, factor dtype) -> products.
 REFINE_TERMS = {2: 2, 4: 6}
 PROJECT_TERMS = {("bf16", "bf16"): 1, ("bf16", "i8"): 1, ("bf16", "f32"): 3, ("bf16", "i4"): 3,
-                 ("f32", "bf16"): 3, ("f32", "i8"): 3, ("f32", "f32"): 6, ("f32", "i4"): 6}
+                 ("bf16", "i2"): 3, ("f32", "bf16"): 3, ("f32", "i8"): 3, ("f32", "f32"): 6,
+                 ("f32", "i4"): 6, ("f32", "i2"): 6}
 GRAM_TERMS = {2: 1, 4: 6}
 
 
@@ -608,8 +609,9 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     ranks = {k: F[k].rank.to(torch.int64) for k in ("k", "v")}
     sw = torch.cat([sweeps["k"], sweeps["v"]]).to(torch.float64)
     sweeps_mean = float(sw.abs().mean())
-    # bytes per factor element (4-bit: half a byte + an fp32 scale per 32 elements)
-    fe = {"f32": 4, "bf16": 2, "i8": 1, "i4": 5 / 8}[fdt]
+    # bytes per factor element (4-bit: half a byte + an fp32 scale per 32 elements;
+    # 2-bit: a quarter byte + the same scales)
+    fe = {"f32": 4, "bf16": 2, "i8": 1, "i4": 5 / 8, "i2": 3 / 8}[fdt]
     xe = 4 if cfg.storage == "f32" else 2
     xname = "f32" if xe == 4 else "bf16"
     tot_rank = int(ranks["k"].sum() + ranks["v"].sum())
@@ -966,7 +968,7 @@ def offload_measure(milo, torch, np, cfg, layer_factors, X, Q, q_pos, sel, nb_la
         sel_kw = dict(sel_ptr=torch.tensor(np.cumsum([0] + [len(x) for x in sel]), dtype=torch.int32, device=dev),
                       sel_blk=torch.tensor(sum(sel, []), dtype=torch.int32, device=dev), sel_max=cfg.sel_blocks)
     ids_t = torch.tensor(ids, dtype=torch.int32)
-    es = {"f32": 4, "bf16": 2, "i8": 1, "i4": 5 / 8}[fdt]
+    es = {"f32": 4, "bf16": 2, "i8": 1, "i4": 5 / 8, "i2": 3 / 8}[fdt]
 
     def layer_host_set(kind, layer):
         """A compact pinned-host copy of one layer's factor set (offsets rebased)."""

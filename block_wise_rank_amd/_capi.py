@@ -12,7 +12,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmilo.so")
 
 MILO_OK, MILO_E_INVALID, MILO_E_UNSUPPORTED, MILO_E_WORKSPACE, MILO_E_HIP = range(5)
-MILO_F32, MILO_BF16, MILO_I8, MILO_I4 = 0, 1, 2, 3
+MILO_F32, MILO_BF16, MILO_I8, MILO_I4, MILO_I2 = 0, 1, 2, 3, 4
 MILO_ALLOC_ENTROPY, MILO_ALLOC_UNIFORM, MILO_ALLOC_RANDOM = 0, 1, 2
 MILO_NOALLOC_SCRATCH_BYTES = 32 << 20
 

@@ -14,7 +14,7 @@ import torch
 from . import _capi as C
 
 _TORCH_TO_MILO = {torch.float32: C.MILO_F32, torch.bfloat16: C.MILO_BF16, torch.int8: C.MILO_I8}
-_NAME_TO_MILO = {"f32": C.MILO_F32, "bf16": C.MILO_BF16, "i8": C.MILO_I8, "i4": C.MILO_I4}
+_NAME_TO_MILO = {"f32": C.MILO_F32, "bf16": C.MILO_BF16, "i8": C.MILO_I8, "i4": C.MILO_I4, "i2": C.MILO_I2}
 _MILO_TO_TORCH = {C.MILO_F32: torch.float32, C.MILO_BF16: torch.bfloat16, C.MILO_I8: torch.int8}
 
 
@@ -182,6 +182,8 @@ class Factors:
         rs = int(self.rank.sum().item())
         if self.dtype == "i4":  # half a byte per element + an fp32 scale per 32 elements
             return rs * (self.block_len + self.head_dim) * 5 // 8
+        if self.dtype == "i2":  # a quarter byte per element + an fp32 scale per 32 elements
+            return rs * (self.block_len + self.head_dim) * 3 // 8
         used = rs * (self.block_len + self.head_dim) * {"f32": 4, "bf16": 2, "i8": 1}[self.dtype]
         if self.dtype == "i8":
             used += 4 * (self.n_blocks * self.block_len + int(self.rank.sum().item()))

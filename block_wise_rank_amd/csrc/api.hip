@@ -74,14 +74,29 @@ milo_status hip_fail(hipError_t e, const char *what) {
 }
 
 int elem_bytes(milo_dtype t) { return t == MILO_F32 ? 4 : (t == MILO_BF16 ? 2 : 1); }
-bool factor_dtype_ok(milo_dtype t) { return t == MILO_F32 || t == MILO_BF16 || t == MILO_I8 || t == MILO_I4; }
-int kernel_type(milo_dtype t) {
-    return t == MILO_F32 ? milo::kF32 : (t == MILO_BF16 ? milo::kBF16 : (t == MILO_I8 ? milo::kI8 : milo::kI4));
+bool factor_dtype_ok(milo_dtype t) {
+    return t == MILO_F32 || t == MILO_BF16 || t == MILO_I8 || t == MILO_I4 || t == MILO_I2;
 }
-// Bytes one rank takes in a block's A part (T elements) and B part (d elements):
-// MILO_I4 holds half a byte per element and an fp32 scale per 32 elements.
-int64_t a_rank_bytes(milo_dtype t, int T) { return t == MILO_I4 ? T / 2 + 4 * (T / 32) : static_cast<int64_t>(T) * elem_bytes(t); }
-int64_t b_rank_bytes(milo_dtype t, int d) { return t == MILO_I4 ? d / 2 + 4 * (d / 32) : static_cast<int64_t>(d) * elem_bytes(t); }
+bool grouped(milo_dtype t) { return t == MILO_I4 || t == MILO_I2; }
+int kernel_type(milo_dtype t) {
+    switch (t) {
+        case MILO_F32: return milo::kF32;
+        case MILO_BF16: return milo::kBF16;
+        case MILO_I8: return milo::kI8;
+        case MILO_I4: return milo::kI4;
+        default: return milo::kI2;
+    }
+}
+// Bytes one rank takes in a block's A part (n = T elements) and B part (n = d):
+// MILO_I4 holds half a byte per element, MILO_I2 a quarter, both with an fp32
+// scale per 32 elements after the codes.
+int64_t rank_bytes(milo_dtype t, int n) {
+    if (t == MILO_I4) return n / 2 + 4 * (n / 32);
+    if (t == MILO_I2) return n / 4 + 4 * (n / 32);
+    return static_cast<int64_t>(n) * elem_bytes(t);
+}
+int64_t a_rank_bytes(milo_dtype t, int T) { return rank_bytes(t, T); }
+int64_t b_rank_bytes(milo_dtype t, int d) { return rank_bytes(t, d); }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -267,8 +282,8 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
     // factor set
     if (!factor_dtype_ok(out->dtype))
         return fail(MILO_E_UNSUPPORTED, "unsupported factor dtype %d", static_cast<int>(out->dtype));
-    if (out->dtype == MILO_I4 && in->block_len % 128 != 0)
-        return fail(MILO_E_UNSUPPORTED, "MILO_I4 factors need block_len a multiple of 128");
+    if (grouped(out->dtype) && in->block_len % 128 != 0)
+        return fail(MILO_E_UNSUPPORTED, "MILO_I4 / MILO_I2 factors need block_len a multiple of 128");
     if (out->n_blocks != in->n_blocks || out->block_len != in->block_len || out->head_dim != in->head_dim)
         return fail(MILO_E_INVALID, "factor set geometry does not match the blocks");
     const size_t need_arena = milo_arena_bytes(out->dtype, in->block_len, in->head_dim, pool_ptr, n_pools, budget);
@@ -448,8 +463,8 @@ milo_status milo_reconstruct_ex(const milo_factors *f, const int32_t *block_ids,
     if (f->block_len < 128 || f->block_len % 64 != 0)
         return fail(MILO_E_UNSUPPORTED, "block_len must be a multiple of 64 and >= 128");
     if (!factor_dtype_ok(f->dtype)) return fail(MILO_E_INVALID, "unknown factor dtype");
-    if (f->dtype == MILO_I4 && f->block_len % 128 != 0)
-        return fail(MILO_E_UNSUPPORTED, "MILO_I4 factors need block_len a multiple of 128");
+    if (grouped(f->dtype) && f->block_len % 128 != 0)
+        return fail(MILO_E_UNSUPPORTED, "MILO_I4 / MILO_I2 factors need block_len a multiple of 128");
     if (out_dtype != MILO_F32 && out_dtype != MILO_BF16)
         return fail(MILO_E_UNSUPPORTED, "out_dtype must be MILO_F32 or MILO_BF16");
     if (n_ids < 0) return fail(MILO_E_INVALID, "n_ids must be >= 0");
@@ -488,8 +503,8 @@ milo_status milo_fetch_blocks(const milo_factors *host, const milo_factors *dev,
     if (i8 && (!host->a_scale || !host->b_scale || !dev->a_scale || !dev->b_scale))
         return fail(MILO_E_INVALID, "MILO_I8 factors need scales");
     const int64_t T = host->block_len, d = host->head_dim, cap = static_cast<int64_t>(host->arena_bytes);
-    if (host->dtype == MILO_I4 && (T % 32 != 0 || d % 32 != 0))
-        return fail(MILO_E_INVALID, "MILO_I4 geometry must hold whole 32-element groups");
+    if (grouped(host->dtype) && (T % 32 != 0 || d % 32 != 0))
+        return fail(MILO_E_INVALID, "MILO_I4 / MILO_I2 geometry must hold whole 32-element groups");
     const int64_t abpr = a_rank_bytes(host->dtype, static_cast<int>(T)), bbpr = b_rank_bytes(host->dtype, static_cast<int>(d));
     // byte runs [begin, end) of the arena, and of the two scale arrays, in list order
     struct Run { int64_t b, e; };
@@ -556,8 +571,8 @@ milo_status decode_attention(const milo_decode_args *a, size_t *workspace_needed
     if (k->block_len != v->block_len) return fail(MILO_E_INVALID, "K and V block_len differ");
     const int T = k->block_len;
     if (T < 128 || T % 64 != 0) return fail(MILO_E_UNSUPPORTED, "block_len must be a multiple of 64 and >= 128");
-    if (k->dtype == MILO_I4 && T % 128 != 0)
-        return fail(MILO_E_UNSUPPORTED, "MILO_I4 factors need block_len a multiple of 128");
+    if (grouped(k->dtype) && T % 128 != 0)
+        return fail(MILO_E_UNSUPPORTED, "MILO_I4 / MILO_I2 factors need block_len a multiple of 128");
     if (a->blocks_per_seq < 0) return fail(MILO_E_INVALID, "blocks_per_seq must be >= 0");
     const int64_t need_blocks = static_cast<int64_t>(a->batch) * a->n_kv_heads * a->blocks_per_seq;
     if (k->n_blocks < need_blocks || v->n_blocks < need_blocks)

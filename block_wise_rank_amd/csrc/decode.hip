@@ -61,16 +61,23 @@ constexpr int kTVP = 264;  // pitch (bytes) of staged tail V rows (32 tokens x 1
 // bytes, so the 16-byte reads of 8 consecutive rows fall on distinct banks.
 constexpr int kRP = 66;
 constexpr int kQP = 132;
-// 4-bit B_k: offset of its decoded bf16 rows in the staging area, past the raw
-// codes and scales of up to 128 ranks (80 bytes each)
-constexpr int kBkRows4 = 128 * (kD / 2 + 4 * (kD / kI4Group));
+// Grouped low-bit factors: 4- or 2-bit codes with an fp32 scale per 32
+// consecutive elements of a rank row (codes of all rows first, then scales).
+__host__ __device__ constexpr bool is_q(int f) { return f == kI4 || f == kI2; }
+__host__ __device__ constexpr int qbits(int f) { return f == kI4 ? 4 : 2; }
+// bytes one rank takes in a B part (d codes, then d / 32 scales)
+__host__ __device__ constexpr int q_b_bytes(int f) { return kD * qbits(f) / 8 + 4 * (kD / kI4Group); }
+
+// Quantised B_k: offset of its decoded bf16 rows in the staging area, past the
+// raw codes and scales of up to 128 ranks (at most 80 bytes each)
+constexpr int kBkRows4 = 128 * q_b_bytes(kI4);
 
 __host__ __device__ constexpr int align16(int v) { return (v + 15) & ~15; }
 
 // A_k staging pitch per rank row of a 32-token tile (bytes); fp32 factors are
 // read straight from memory.
-// 4-bit factors are dequantised into the bf16 layout as they are staged.
-__host__ __device__ inline int stage_pitch(int f) { return (f == kBF16 || f == kI4) ? 64 : (f == kI8 ? 40 : 0); }
+// 4- and 2-bit factors are dequantised into the bf16 layout as they are staged.
+__host__ __device__ inline int stage_pitch(int f) { return (f == kBF16 || is_q(f)) ? 64 : (f == kI8 ? 40 : 0); }
 
 struct LdsLayout {
     int ang, qs, bk, rope, base, stage, loop_end;      // loop phase
@@ -81,11 +88,11 @@ struct LdsLayout {
 
 // Merge-phase areas: per-wave u rows, per-wave (m, l), merged u
 constexpr int kMergeEnd = align16(align16(align16(kWaves * 16 * kUP * 4) + kWaves * 16 * 2 * 4) + 16 * kUP * 4);
-// 4-bit B_v: its codes and scales (at most 128 x 80 bytes) land in the last
+// Quantised B_v: its codes and scales (at most 128 x 80 bytes) land in the last
 // 10 KiB of the staging area, the staging rows of waves 6 and 7; the decoded
 // bf16 rows (128 x 256 bytes) go between the merge areas and them, which needs
 // the staging area to start at least this far in
-constexpr int kBvRaw = kWaves * 128 * 64 - 128 * (kD / 2 + 4 * (kD / kI4Group));
+constexpr int kBvRaw = kWaves * 128 * 64 - 128 * q_b_bytes(kI4);
 constexpr int kI4StageMin = kMergeEnd + 128 * kD * 2 - kBvRaw;
 
 __host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool tail, int G) {
@@ -96,12 +103,12 @@ __host__ __device__ inline LdsLayout lds_layout(int f, int ns, int n_tiles, bool
     L.rope = align16(L.bk + (tail ? 0 : ns * 8 * 4 * 64 * 16));
     L.base = align16(L.rope + 32 * kRP * 8);
     L.stage = align16(L.base + n_tiles * 64 * 8);
-    if (f == kI4 && !tail && L.stage < kI4StageMin) L.stage = kI4StageMin;
+    if (is_q(f) && !tail && L.stage < kI4StageMin) L.stage = kI4StageMin;
     int stage = 0;
     if (!tail) stage = kWaves * 128 * stage_pitch(f);
     else if (f == kBF16) stage = kWaves * 32 * kTVP;
     // the B_k rows for the fragment build are staged in this area too
-    const int bk_rows = (tail || f == kF32) ? 0 : (f == kI4 ? 128 * (kD / 2 + 4 * (kD / kI4Group)) : 128 * kD * (f == kBF16 ? 2 : 1));
+    const int bk_rows = (tail || f == kF32) ? 0 : (is_q(f) ? 128 * q_b_bytes(f) : 128 * kD * (f == kBF16 ? 2 : 1));
     if (stage < bk_rows) stage = bk_rows;
     L.loop_end = align16(L.stage + stage);
     L.uw = 0;
@@ -135,9 +142,35 @@ __device__ __forceinline__ const uint8_t *pick_uniform(bool c, const void *a, co
     return reinterpret_cast<const uint8_t *>(static_cast<uint64_t>(hi) << 32 | lo);
 }
 
-// Signed value of nibble k (0..7) of a word of eight 4-bit codes.
-__device__ __forceinline__ float nib(uint32_t w, int k) {
-    return static_cast<float>(static_cast<int32_t>(w << (28 - 4 * k)) >> 28);
+// Value, in units of its run's scale, of code k (0..7) of eight consecutive
+// codes held in the low bits of w: a two's-complement nibble (4-bit), or the
+// level 2c - 3 of a 2-bit code c.
+template <int F>
+__device__ __forceinline__ float qval(uint32_t w, int k) {
+    if constexpr (F == kI4) return static_cast<float>(static_cast<int32_t>(w << (28 - 4 * k)) >> 28);
+    else return static_cast<float>(static_cast<int>((w >> (2 * k)) & 3u) * 2 - 3);
+}
+
+// The 32 codes of one run starting at p as four words of eight codes each.
+template <int F>
+__device__ __forceinline__ void run_words(const uint8_t *p, uint32_t (&w4)[4]) {
+    if constexpr (F == kI4) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(p);
+        w4[0] = c.x; w4[1] = c.y; w4[2] = c.z; w4[3] = c.w;
+    } else {
+        const uint2 c = *reinterpret_cast<const uint2 *>(p);
+        w4[0] = c.x & 0xffffu; w4[1] = c.x >> 16; w4[2] = c.y & 0xffffu; w4[3] = c.y >> 16;
+    }
+}
+
+// A run of 32 codes (scale sc) -> 16 words of bf16 pairs, element order kept.
+template <int F>
+__device__ __forceinline__ void decode_run(const uint32_t (&w4)[4], float sc, uint32_t (&hw)[16]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            hw[4 * c + e] = f32x2_to_bf16x2_bits(qval<F>(w4[c], 2 * e) * sc, qval<F>(w4[c], 2 * e + 1) * sc);
 }
 
 template <int F>
@@ -193,7 +226,8 @@ __device__ __forceinline__ int stage_off_i8(int r, int t) {
 template <int F, bool TAIL>
 __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int sp, uint8_t *lds) {
     constexpr int NS = (F == kF32) ? 2 : 1;
-    constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);  // kI4: half a byte, see below
+    constexpr int ES = (F == kF32) ? 4 : (F == kBF16 ? 2 : 1);  // 4- and 2-bit: see below
+    constexpr int QRB = is_q(F) ? kTile * qbits(F) / 8 : 0;      // code bytes of a 32-token run
     const int G = p.group;
     const int n_tiles = p.split_len / kTile;
     const LdsLayout L = lds_layout(F, NS, n_tiles, TAIL, G);
@@ -282,16 +316,16 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
 
     // A_k tile loads: 16-byte pieces, LPR lanes per rank row; rows past rk
     // repeat row rk - 1 (finite; their B_k fragment rows are zero).
-    constexpr int RB = F == kI4 ? kTile / 2 : kTile * ES;  // bytes of one rank row of a tile
+    constexpr int RB = is_q(F) ? QRB : kTile * ES;  // bytes of one rank row of a tile
     constexpr int LPR = RB / 16 > 0 ? RB / 16 : 1;  // lanes per row
     constexpr int RPI = 64 / LPR;                   // rows per load instruction
     constexpr int NI = 128 / RPI;                   // load instructions for 128 ranks
-    uint4 kraw[(F == kF32 || F == kI4 || TAIL) ? 1 : NI];
-    // 4-bit: lane L stages, for ci = 0..7, the 16 bytes that the bf16 DMA would
-    // write (row 16 ci + L / 4, physical chunk L % 4): 8 codes and their row's
-    // scale for the tile.  Consecutive lanes then write consecutive 16 bytes.
-    uint32_t kcode[(F == kI4 && !TAIL) ? 8 : 1];
-    float kscl[(F == kI4 && !TAIL) ? 8 : 1];
+    uint4 kraw[(F == kF32 || is_q(F) || TAIL) ? 1 : NI];
+    // 4- and 2-bit: lane L stages, for ci = 0..7, the 16 bytes that the bf16 DMA
+    // would write (row 16 ci + L / 4, physical chunk L % 4): 8 codes and their
+    // row's scale for the tile.  Consecutive lanes then write consecutive 16 bytes.
+    uint32_t kcode[(is_q(F) && !TAIL) ? 8 : 1];
+    float kscl[(is_q(F) && !TAIL) ? 8 : 1];
     const int rk_pad = KS * 32;
     // Every load instruction is issued (rows clamped to rk - 1; identical
     // addresses coalesce), which keeps the registers free of partial paths.
@@ -299,16 +333,19 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         if constexpr (F != kF32 && !TAIL) {
             if (rk > 0) {
                 const int tt0 = tok0 + tile * kTile;
-                if constexpr (F == kI4) {
+                if constexpr (is_q(F)) {
                     const int pp = lane & 3;
+                    constexpr int QB = qbits(F);
 #pragma unroll
                     for (int ci = 0; ci < 8; ++ci) {
                         const int rp = 16 * ci + (lane >> 2);  // staging row
                         const int r = min(rp, rk - 1);         // rows past rk repeat the last
                         const int pc = ((((pp >> 1) ^ ((rp >> 1) & 1))) << 1) | (pp & 1);  // logical chunk
-                        kcode[ci] = *reinterpret_cast<const uint32_t *>(Ak + static_cast<uint32_t>(r * (T / 2) + tt0 / 2 + 4 * pc));
+                        const uint32_t co = static_cast<uint32_t>(r * (T * QB / 8) + (tt0 + 8 * pc) * QB / 8);
+                        if constexpr (F == kI4) kcode[ci] = *reinterpret_cast<const uint32_t *>(Ak + co);
+                        else kcode[ci] = *reinterpret_cast<const uint16_t *>(Ak + co);
                         kscl[ci] = *reinterpret_cast<const float *>(
-                            Ak + static_cast<uint32_t>(rk * (T / 2) + (r * (T / kI4Group) + tt0 / kI4Group) * 4));
+                            Ak + static_cast<uint32_t>(rk * (T * QB / 8) + (r * (T / kI4Group) + tt0 / kI4Group) * 4));
                     }
                 } else {
 #pragma unroll
@@ -324,14 +361,15 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
     };
     auto stage_k = [&](uint8_t *sdst) {
         if constexpr (F != kF32 && !TAIL) {
-            if constexpr (F == kI4) {
+            if constexpr (is_q(F)) {
 #pragma unroll
                 for (int ci = 0; ci < 8; ++ci)
                     if (16 * ci < rk_pad) {  // uniform
                         uint32_t hw[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            hw[e] = f32x2_to_bf16x2_bits(nib(kcode[ci], 2 * e) * kscl[ci], nib(kcode[ci], 2 * e + 1) * kscl[ci]);
+                            hw[e] = f32x2_to_bf16x2_bits(qval<F>(kcode[ci], 2 * e) * kscl[ci],
+                                                         qval<F>(kcode[ci], 2 * e + 1) * kscl[ci]);
                         *reinterpret_cast<uint4 *>(sdst + 1024 * ci + 16 * lane) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
                     }
             } else {
@@ -413,11 +451,15 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
 #pragma unroll
                 for (int mr = 0; mr < 8; ++mr) {
                     const int row = min(16 * mr + ln, rv - 1);
-                    if constexpr (F == kI4) {
+                    if constexpr (is_q(F)) {
                         // codes of tokens tb .. tb + 7, and the scale of the tile's run
-                        const uint32_t w = *reinterpret_cast<const uint32_t *>(Av + static_cast<uint32_t>(row * (T / 2) + tb / 2));
+                        constexpr int QB = qbits(F);
+                        const uint32_t co = static_cast<uint32_t>(row * (T * QB / 8) + tb * QB / 8);
+                        uint32_t w;
+                        if constexpr (F == kI4) w = *reinterpret_cast<const uint32_t *>(Av + co);
+                        else w = *reinterpret_cast<const uint16_t *>(Av + co);
                         const float sc = *reinterpret_cast<const float *>(
-                            Av + static_cast<uint32_t>(rv * (T / 2) + (row * (T / kI4Group) + t0 / kI4Group) * 4));
+                            Av + static_cast<uint32_t>(rv * (T * QB / 8) + (row * (T / kI4Group) + t0 / kI4Group) * 4));
                         vraw[mr] = make_uint4(w, __float_as_uint(sc), 0u, 0u);
                     } else {
                         const uint2 w = *reinterpret_cast<const uint2 *>(Av + static_cast<uint32_t>(row * T + tb));
@@ -436,9 +478,9 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         load_k(wt0);
         load_v(wt0);
     }
-    // B_k part of the arena as raw 16-byte chunks (4-bit: rk code rows of d/2
-    // bytes, then rk x d/32 fp32 scales)
-    constexpr int BKB = F == kI4 ? kD / 2 + 4 * (kD / kI4Group) : kD * ES;  // bytes per rank
+    // B_k part of the arena as raw 16-byte chunks (4- and 2-bit: rk code rows of
+    // d/2 or d/4 bytes, then rk x d/32 fp32 scales)
+    constexpr int BKB = is_q(F) ? q_b_bytes(F) : kD * ES;  // bytes per rank
     constexpr int NBK = (F == kF32 || TAIL) ? 1 : (128 * BKB / 16 + kThreads - 1) / kThreads;
     uint4 bkraw[NBK];
     const int n16 = (F == kF32 || TAIL) ? 0 : (rk * BKB) >> 4;
@@ -526,22 +568,20 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         uint16_t *bk = reinterpret_cast<uint16_t *>(lds + L.bk);
         const uint8_t *tmp = lds + L.stage;
         const float *bsc = reinterpret_cast<const float *>(tmp + 128 * kD);  // int8 only
-        // 4-bit: B_k's rows are first decoded into bf16 rows (row r at 256 r bytes,
-        // after the raw codes and scales), so that the fragments come from them by
-        // the bf16 path's transposing reads.  Thread t: row t / 4, dims 32 (t % 4) ..
+        // 4- and 2-bit: B_k's rows are first decoded into bf16 rows (row r at 256 r
+        // bytes, after the raw codes and scales), so that the fragments come from
+        // them by the bf16 path's transposing reads.  Thread t: row t / 4, dims
+        // 32 (t % 4) ..
         uint8_t *rows4 = lds + L.stage + kBkRows4;
-        if constexpr (F == kI4) {
+        if constexpr (is_q(F)) {
+            constexpr int CRB = kD * qbits(F) / 8;  // code bytes of a B row
             const int r = tid >> 2, qd = tid & 3;
             uint32_t hw[16];
             if (r < rk) {
-                const uint4 cw = *reinterpret_cast<const uint4 *>(tmp + r * (kD / 2) + 16 * qd);
-                const float sc = reinterpret_cast<const float *>(tmp + rk * (kD / 2))[r * (kD / kI4Group) + qd];
-                const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        hw[4 * c + e] = f32x2_to_bf16x2_bits(nib(w4[c], 2 * e) * sc, nib(w4[c], 2 * e + 1) * sc);
+                uint32_t w4[4];
+                run_words<F>(tmp + r * CRB + qd * (CRB / 4), w4);
+                const float sc = reinterpret_cast<const float *>(tmp + rk * CRB)[r * (kD / kI4Group) + qd];
+                decode_run<F>(w4, sc, hw);
             } else {
 #pragma unroll
                 for (int k = 0; k < 16; ++k) hw[k] = 0u;
@@ -555,11 +595,11 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
             const int l2 = q & 63, ks = (q >> 6) & 3, mt = q >> 8;
             if (ks >= KS) continue;
             const int j = 16 * mt + (l2 & 15), r0 = 32 * ks + 8 * (l2 >> 4);
-            if constexpr (F == kBF16 || F == kI4) {
+            if constexpr (F == kBF16 || is_q(F)) {
                 // ranks r0 .. r0 + 7 of dim j by two transposing reads of the staged
                 // rows (lane (c, i) of a 16-lane group addresses row r0 + i / 4 (+ 4),
                 // dims 16 mt + 4 (i % 4) ..); rows past rk (repeats) become zero
-                const uint8_t *p0 = (F == kI4 ? rows4 : tmp) + (r0 + ((l2 & 15) >> 2)) * (kD * 2) + (16 * mt + 4 * (l2 & 3)) * 2;
+                const uint8_t *p0 = (is_q(F) ? rows4 : tmp) + (r0 + ((l2 & 15) >> 2)) * (kD * 2) + (16 * mt + 4 * (l2 & 3)) * 2;
                 u16x8_t f0 = cat8(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * kD * 2));
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -693,7 +733,7 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
                 for (int ks = 0; ks < KS; ++ks) {
                     const bool first = ks == 0;  // zero accumulator input (inline constant)
                     u16x8_t bfr[NS];
-                    if constexpr (F == kBF16 || F == kI4) {
+                    if constexpr (F == kBF16 || is_q(F)) {
                         // ranks 32 ks + 8 c .. + 7 of token t by two transposing reads: lane
                         // (c, j) addresses rank row 32 ks + 8 c + j / 4 (+ 4), tokens
                         // 8 (j % 4) + 4 nt .. + 3, and lane (c, j) receives token tk(nt, j)
@@ -848,11 +888,11 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
                 if (mr < NTU) {
                     if (rescale) u[mr] *= alpha;
                     u16x8_t af;
-                    if constexpr (F == kI4) {
+                    if constexpr (is_q(F)) {
                         const float sc = __uint_as_float(vraw[mr].y);
                         float v[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] = nib(vraw[mr].x, e) * sc;
+                        for (int e = 0; e < 8; ++e) v[e] = qval<F>(vraw[mr].x, e) * sc;
                         u16x8_t f[1];
                         frag_terms<1>(v, f);
                         af = f[0];
@@ -956,14 +996,14 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         asm volatile("" ::: "memory");
         if (my_tiles > 0) u_update_bf16();  // the last tile's
     }
-    if constexpr (F == kI4 && !TAIL) {
-        // B_v's code rows and scales (rv x 80 bytes, at most 640 16-byte chunks)
+    if constexpr (is_q(F) && !TAIL) {
+        // B_v's code rows and scales (rv x 80 or rv x 48 bytes, at most 640 16-byte chunks)
         // go by LDS DMA into the last 10 KiB of the staging area, chunk c at byte
         // 16 c: the staging rows of waves 6 (chunks 0 .. 127) and 7 (128 .. 639),
         // which each writes only once its own tiles are done (chunks past the last
         // repeat it).  They land before the second barrier of the merge.
         if (wave >= 6) {
-            const int n16v = rv * (kD / 2 + 4 * (kD / kI4Group)) / 16;
+            const int n16v = rv * q_b_bytes(F) / 16;
             const uint8_t *base = pick_uniform(n16v > 0, Bv, p.q);
             const int last = max(n16v - 1, 0), on = n16v > 0 ? 16 : 0;
             uint8_t *dst = lds + L.bvraw;
@@ -1012,7 +1052,7 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
                 const uint8_t *p0 = bvl + (32 * ks + 8 * c4 + (ln >> 2)) * (kD * 2) + (16 * wave + 4 * (ln & 3)) * 2;
                 bvf[0][ks] = cat8(lds_read_tr16(p0), lds_read_tr16(p0 + 4 * kD * 2));
             }
-    } else if constexpr (!TAIL && F != kI4) {
+    } else if constexpr (!TAIL && !is_q(F)) {
         if (rv > 0) {
             const int dim = 16 * wave + ln;
 #pragma unroll
@@ -1033,27 +1073,24 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
             }
         }
     }
-    if constexpr (F == kI4 && !TAIL) {
+    if constexpr (is_q(F) && !TAIL) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the B_v DMA has landed (before the barrier)
         asm volatile("" ::: "memory");
     }
     __syncthreads();
-    if constexpr (F == kI4 && !TAIL) {
-        // 4-bit B_v -> bf16 rows (row r at 256 r bytes), the bf16 path's layout for
-        // the transposing fragment reads below.  Thread t: row t / 4, dims
+    if constexpr (is_q(F) && !TAIL) {
+        // quantised B_v -> bf16 rows (row r at 256 r bytes), the bf16 path's layout
+        // for the transposing fragment reads below.  Thread t: row t / 4, dims
         // 32 (t % 4) .. + 31; rows past rv are zero.
+        constexpr int CRB = kD * qbits(F) / 8;
         const uint8_t *bv4 = lds + L.bvraw;
         const int r = tid >> 2, qd = tid & 3;
         uint32_t hw[16];
         if (r < rv) {
-            const uint4 cw = *reinterpret_cast<const uint4 *>(bv4 + r * (kD / 2) + 16 * qd);
-            const float sc = reinterpret_cast<const float *>(bv4 + rv * (kD / 2))[r * (kD / kI4Group) + qd];
-            const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    hw[4 * c + e] = f32x2_to_bf16x2_bits(nib(w4[c], 2 * e) * sc, nib(w4[c], 2 * e + 1) * sc);
+            uint32_t w4[4];
+            run_words<F>(bv4 + r * CRB + qd * (CRB / 4), w4);
+            const float sc = reinterpret_cast<const float *>(bv4 + rv * CRB)[r * (kD / kI4Group) + qd];
+            decode_run<F>(w4, sc, hw);
         } else {
 #pragma unroll
             for (int k = 0; k < 16; ++k) hw[k] = 0u;
@@ -1089,8 +1126,8 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
         ml[2 * tid + 1] = Ls;
     }
     __syncthreads();
-    if constexpr (F == kI4 && !TAIL) {
-        // 4-bit B_v fragments from the rows decoded above, as for bf16
+    if constexpr (is_q(F) && !TAIL) {
+        // quantised B_v fragments from the rows decoded above, as for bf16
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             if (ks < KSV) {
@@ -1257,7 +1294,7 @@ bool decode_split_fits(int f_type, int tail_type, bool has_tail, int G, int spli
     if (L.total > kMaxLds) return false;
     // bf16: B_v is staged in the upper half of the staging rows during the merge
     if (f_type == kBF16 && L.merge_end > L.stage + kWaves / 2 * 128 * stage_pitch(kBF16)) return false;
-    if (f_type == kI4 && L.bvrows + 128 * kD * 2 > L.bvraw) return false;
+    if (is_q(f_type) && L.bvrows + 128 * kD * 2 > L.bvraw) return false;
     if (has_tail) {
         const int tns = tail_type == kF32 ? 2 : 1;
         if (lds_layout(tail_type, tns, split / kTile, true, G).total > kMaxLds) return false;
@@ -1296,6 +1333,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t st) {
     if (p.n_sel * p.block_splits == 0 || p.f_type == kBF16) return launch_decode_f<kBF16>(p, st);
     if (p.f_type == kI8) return launch_decode_f<kI8>(p, st);
     if (p.f_type == kI4) return launch_decode_f<kI4>(p, st);
+    if (p.f_type == kI2) return launch_decode_f<kI2>(p, st);
     return launch_decode_f<kF32>(p, st);
 }
 

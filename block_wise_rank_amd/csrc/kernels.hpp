@@ -8,9 +8,12 @@
 
 namespace milo {
 
-enum ElemType : int { kF32 = 0, kBF16 = 1, kI8 = 2, kI4 = 3 };
+enum ElemType : int { kF32 = 0, kBF16 = 1, kI8 = 2, kI4 = 3, kI2 = 4 };
 // 4-bit factors: symmetric codes in [-7, 7], two per byte (element 2k in the low
 // nibble), one fp32 scale per kI4Group consecutive elements of a row.
+// 2-bit factors: codes c in 0..3 for the levels (2c - 3) s, four per byte
+// (element 4k + j in bits 2j, 2j + 1 of byte k), one fp32 scale s per kI4Group
+// consecutive elements of a row.
 constexpr int kI4Group = 32;
 // Rank allocation policies (values of milo_alloc_policy).
 enum AllocPolicy : int { kAllocEntropy = 0, kAllocUniform = 1, kAllocRandom = 2 };

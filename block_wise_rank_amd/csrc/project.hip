@@ -10,6 +10,9 @@
 // fp32 storage's, bit for bit), then every run of 32 consecutive elements of a
 // rank row of A^T (tokens) and of B (features) gets s = max|run| / 7 and codes
 // rint(x / s) in [-7, 7], decided in fp32.
+// 2-bit: the same runs with s = max|run| / 3 and a code c in 0..3 for the
+// level (2c - 3) s nearest to x: |x / s| >= 2 (the IEEE quotient) takes the
+// outer level of x's sign, else the inner one; x = 0 and s = 0 give code 2.
 //
 // A^T = B~ X^T runs on bf16 MFMA (M = rank, N = token, K = feature): the
 // fragments of B~ stay in registers (one 32-rank tile per wave) while 32-token
@@ -62,6 +65,51 @@ __device__ __forceinline__ void store_b_i4(const float (&v)[8][8], int i, int r,
             make_float4(sB4[0], sB4[1], sB4[2], sB4[3]);
 }
 
+// 2-bit code of x in a run of scale s, the decision taken by the IEEE quotient.
+__device__ __forceinline__ uint32_t code2(float x, float s) {
+    if (!(s > 0.f)) return 2u;
+    const bool outer = __fdiv_rn(fabsf(x), s) >= 2.f;
+    return x < 0.f ? (outer ? 0u : 1u) : (outer ? 3u : 2u);
+}
+
+// The same decision from |x| * inv, inv = fl(1 / s): that product is within
+// 1e-6 of |x / s| (|x / s| <= 3), and so is fl(|x / s|), so unless it lies
+// within 1e-5 of 2 both fall on the same side; there the quotient decides.
+__device__ __forceinline__ uint32_t code2_fast(float x, float s, float inv) {
+    if (!(s > 0.f)) return 2u;
+    float p = fabsf(x) * inv;
+    if (fabsf(p - 2.f) <= 1e-5f) p = __fdiv_rn(fabsf(x), s);
+    const bool outer = p >= 2.f;
+    return x < 0.f ? (outer ? 0u : 1u) : (outer ? 3u : 2u);
+}
+
+// 2-bit B row i (the lane layout of store_b_i4): codes of features 16 ks +
+// 8 (lane / 32) .. + 7 as one 16-bit piece, then the row's four run scales.
+__device__ __forceinline__ void store_b_i2(const float (&v)[8][8], int i, int r, int lane, bool store,
+                                           uint8_t *Bb) {
+    float sB4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fmaxf(fabsf(v[2 * g][e]), fabsf(v[2 * g + 1][e])));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        sB4[g] = __fdiv_rn(m, 3.f);
+    }
+    if (!store) return;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        uint32_t h = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h |= code2(v[ks][e], sB4[ks >> 1]) << (2 * e);
+        *reinterpret_cast<uint16_t *>(Bb + static_cast<int64_t>(i) * (kD / 4) + 4 * ks + 2 * (lane >> 5)) =
+            static_cast<uint16_t>(h);
+    }
+    if (lane < 32)
+        *reinterpret_cast<float4 *>(Bb + static_cast<int64_t>(r) * (kD / 4) + 16 * i) =
+            make_float4(sB4[0], sB4[1], sB4[2], sB4[3]);
+}
+
 template <int NX, int OUT>
 __global__ __launch_bounds__(256) void project_kernel(
     const void *__restrict__ x, const int64_t *__restrict__ row0, int64_t row_stride, int T,
@@ -69,7 +117,7 @@ __global__ __launch_bounds__(256) void project_kernel(
     const int32_t *__restrict__ rank,
     const int64_t *__restrict__ a_off, const int64_t *__restrict__ b_off,
     uint8_t *__restrict__ arena, float *__restrict__ a_scale, float *__restrict__ b_scale) {
-    constexpr int NS = (OUT == kF32 || OUT == kI4) ? 3 : 1;  // bf16 terms of the B operand
+    constexpr int NS = (OUT == kF32 || OUT == kI4 || OUT == kI2) ? 3 : 1;  // bf16 terms of the B operand
     __shared__ float sB_rows[kD];
     __shared__ float tmax[4][32];
 
@@ -122,7 +170,7 @@ __global__ __launch_bounds__(256) void project_kernel(
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            if constexpr (OUT == kF32 || OUT == kI4) {
+            if constexpr (OUT == kF32 || OUT == kI4 || OUT == kI2) {
                 uint16_t h, mm, l;
                 split3_bf16(v[ks][e], h, mm, l);
                 fa[0][ks][e] = h;
@@ -140,7 +188,8 @@ __global__ __launch_bounds__(256) void project_kernel(
 
     // ---- B rows (first part only) and B scales.
     if constexpr (OUT == kI4) store_b_i4(v, i, r, lane, part == 0 && row_ok, Bb);
-    if (OUT != kI4 && part == 0 && row_ok) {
+    if constexpr (OUT == kI2) store_b_i2(v, i, r, lane, part == 0 && row_ok, Bb);
+    if (OUT != kI4 && OUT != kI2 && part == 0 && row_ok) {
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int j0 = 16 * ks + 8 * (lane >> 5);
@@ -232,6 +281,31 @@ __global__ __launch_bounds__(256) void project_kernel(
                             *reinterpret_cast<uint32_t *>(Ab + static_cast<int64_t>(ir) * (T / 2) + t / 2) = w;
                         if ((lane & 31) == 0)
                             *reinterpret_cast<float *>(Ab + static_cast<int64_t>(r) * (T / 2) +
+                                                       (static_cast<int64_t>(ir) * (T / kI4Group) + t0 / kI4Group) * 4) = sA;
+                    }
+                }
+            }
+        } else if constexpr (OUT == kI2) {
+            // 32-token run of row i' = this tile, held by the lanes of one half
+            if (wave_active) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int ir = 32 * wave + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    float m = fabsf(acc[q]);
+#pragma unroll
+                    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                    const float sA = __fdiv_rn(m, 3.f);
+                    // sixteen tokens' codes into one word (token t0 + 16k + e at bits 2e)
+                    uint32_t w = code2(acc[q], sA) << (2 * (lane & 15));
+                    w |= __shfl_xor(w, 1, 64);
+                    w |= __shfl_xor(w, 2, 64);
+                    w |= __shfl_xor(w, 4, 64);
+                    w |= __shfl_xor(w, 8, 64);
+                    if (ir < r) {
+                        if ((lane & 15) == 0)
+                            *reinterpret_cast<uint32_t *>(Ab + static_cast<int64_t>(ir) * (T / 4) + t / 4) = w;
+                        if ((lane & 31) == 0)
+                            *reinterpret_cast<float *>(Ab + static_cast<int64_t>(r) * (T / 4) +
                                                        (static_cast<int64_t>(ir) * (T / kI4Group) + t0 / kI4Group) * 4) = sA;
                     }
                 }
@@ -436,13 +510,13 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(
     });
 }
 
-// bf16 X -> fp32 or 4-bit factors: the B operand in three bf16 terms (the
-// products are fp32-accurate and identical for both storages, so the 4-bit
+// bf16 X -> fp32, 4-bit or 2-bit factors: the B operand in three bf16 terms
+// (the products are fp32-accurate and identical for all three storages, so the
 // codes are those of the fp32 factors), 1024-token parts, X through the LDS
 // ring above.  Each wave's 32 rank rows are collected in LDS as fp32 for 64
 // tokens; the flush writes fp32 rows as whole pieces, or quantises each 32-token
-// run (one run per lane: max, scale, codes) and writes its 16 code bytes and its
-// scale.
+// run (one run per lane: max, scale, codes) and writes its code bytes (16 for
+// 4-bit, 8 for 2-bit) and its scale.
 constexpr int kRunP = 36;           // LDS floats per staged 32-token run (16-byte aligned pieces)
 constexpr int kRowP = 2 * kRunP;    // LDS floats per staged rank row (64 tokens)
 
@@ -492,6 +566,7 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
             }
     }
     if constexpr (OUT == kI4) store_b_i4(v, i, r, lane, part == 0 && row_ok, Bb);
+    if constexpr (OUT == kI2) store_b_i2(v, i, r, lane, part == 0 && row_ok, Bb);
     u16x8_t fa[3][8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -541,6 +616,33 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
                     if (ir < r)
                         *reinterpret_cast<float4 *>(Ab + (static_cast<int64_t>(ir) * T + tok0 + 4 * piece) * 4) =
                             *reinterpret_cast<const float4 *>(stg + row * kRowP + (piece >> 3) * kRunP + 4 * (piece & 7));
+                }
+            } else if constexpr (OUT == kI2) {
+                // 64 runs (32 rows x 2), one per lane: 8 code bytes and a scale each
+                const int row = lane >> 1, gg = lane & 1;
+                const int ir = 32 * wave + row;
+                const float4 *src = reinterpret_cast<const float4 *>(stg + row * kRowP + gg * kRunP);
+                float m = 0.f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float4 a = src[k];
+                    m = fmaxf(fmaxf(m, fmaxf(fabsf(a.x), fabsf(a.y))), fmaxf(fabsf(a.z), fabsf(a.w)));
+                }
+                const float sA = __fdiv_rn(m, 3.f);
+                const float inv = sA > 0.f ? __fdiv_rn(1.f, sA) : 0.f;
+                uint32_t w[2] = {0u, 0u};
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float4 a = src[k];
+                    const float f[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[k >> 2] |= code2_fast(f[e], sA, inv) << (2 * (4 * (k & 3) + e));
+                }
+                if (ir < r) {
+                    *reinterpret_cast<uint2 *>(Ab + static_cast<int64_t>(ir) * (T / 4) + (tok0 + 32 * gg) / 4) =
+                        make_uint2(w[0], w[1]);
+                    *reinterpret_cast<float *>(Ab + static_cast<int64_t>(r) * (T / 4) +
+                                               (static_cast<int64_t>(ir) * (T / kI4Group) + tok0 / kI4Group + gg) * 4) = sA;
                 }
             } else {
                 // 64 runs (32 rows x 2), one per lane
@@ -601,14 +703,19 @@ hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_
                            row_stride, block_len, vt, perm, vscale, rank, a_off, b_off, static_cast<uint8_t *>(arena));
         return hipGetLastError();
     }
-    if (x_type == kBF16 && (out_type == kF32 || out_type == kI4)) {
+    if (x_type == kBF16 && (out_type == kF32 || out_type == kI4 || out_type == kI2)) {
         const dim3 g(static_cast<unsigned>(n_blocks), static_cast<unsigned>((block_len + kPartBF - 1) / kPartBF));
+        const uint16_t *xb = static_cast<const uint16_t *>(x);
+        uint8_t *ar = static_cast<uint8_t *>(arena);
         if (out_type == kF32)
-            hipLaunchKernelGGL(project_split_kernel<kF32>, g, dim3(256), 0, st, static_cast<const uint16_t *>(x), row0,
-                               row_stride, block_len, vt, perm, vscale, rank, a_off, b_off, static_cast<uint8_t *>(arena));
+            hipLaunchKernelGGL(project_split_kernel<kF32>, g, dim3(256), 0, st, xb, row0, row_stride, block_len, vt,
+                               perm, vscale, rank, a_off, b_off, ar);
+        else if (out_type == kI4)
+            hipLaunchKernelGGL(project_split_kernel<kI4>, g, dim3(256), 0, st, xb, row0, row_stride, block_len, vt,
+                               perm, vscale, rank, a_off, b_off, ar);
         else
-            hipLaunchKernelGGL(project_split_kernel<kI4>, g, dim3(256), 0, st, static_cast<const uint16_t *>(x), row0,
-                               row_stride, block_len, vt, perm, vscale, rank, a_off, b_off, static_cast<uint8_t *>(arena));
+            hipLaunchKernelGGL(project_split_kernel<kI2>, g, dim3(256), 0, st, xb, row0, row_stride, block_len, vt,
+                               perm, vscale, rank, a_off, b_off, ar);
         return hipGetLastError();
     }
     const dim3 grid(static_cast<unsigned>(n_blocks),
@@ -625,6 +732,8 @@ hipError_t launch_project(const void *x, int x_type, const int64_t *row0, int64_
         MILO_PROJECT(3, kBF16);
     else if (x_type == kF32 && out_type == kI4)
         MILO_PROJECT(3, kI4);
+    else if (x_type == kF32 && out_type == kI2)
+        MILO_PROJECT(3, kI2);
     else
         MILO_PROJECT(3, kI8);
 #undef MILO_PROJECT

@@ -11,7 +11,7 @@
 // registers; each output tile goes through LDS so that every row is written
 // with 16-byte stores.
 //
-// fp32 and INT8 factors (parity formats): fp32 arithmetic on the decoded
+// fp32, INT8, 4-bit and 2-bit factors: fp32 arithmetic on the decoded
 // values, grid (listed block, 64-token tile), B_b and the 64-token slice of
 // A_b^T staged in LDS, each thread accumulating 32 tokens of one column.
 #include "common.hpp"
@@ -35,6 +35,13 @@ __device__ __forceinline__ float i4_code(const uint8_t *p, int64_t idx) {
     return static_cast<float>(n >= 8 ? n - 16 : n);
 }
 
+// Element idx of a 2-bit code row starting at p (element 4k + j in bits 2j of
+// byte k): the level 2c - 3 in units of the run's scale.
+__device__ __forceinline__ float i2_code(const uint8_t *p, int64_t idx) {
+    const int c = (p[idx >> 2] >> (2 * (idx & 3))) & 3;
+    return static_cast<float>(2 * c - 3);
+}
+
 template <int F, int OUT>
 __global__ __launch_bounds__(256) void reconstruct_kernel(
     const uint8_t *__restrict__ arena, const int32_t *__restrict__ rank,
@@ -56,6 +63,9 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(
             // code row i at Bb + i * d / 2, scales (r x d / 32) after the r code rows
             const float *bs = reinterpret_cast<const float *>(Bb + static_cast<int64_t>(r) * (kD / 2));
             v = i4_code(Bb, e) * bs[e / kI4Group];
+        } else if constexpr (F == kI2) {
+            const float *bs = reinterpret_cast<const float *>(Bb + static_cast<int64_t>(r) * (kD / 4));
+            v = i2_code(Bb, e) * bs[e / kI4Group];
         } else {
             v = load_code<F>(Bb, e);
             if constexpr (F == kI8) v *= b_scale[static_cast<int64_t>(id) * kD + e / kD];
@@ -69,6 +79,10 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(
             const float *as = reinterpret_cast<const float *>(Ab + static_cast<int64_t>(r) * (T / 2));
             const int64_t idx = static_cast<int64_t>(i) * T + t0 + tt;
             v = i4_code(Ab, idx) * as[idx / kI4Group];
+        } else if constexpr (F == kI2) {
+            const float *as = reinterpret_cast<const float *>(Ab + static_cast<int64_t>(r) * (T / 4));
+            const int64_t idx = static_cast<int64_t>(i) * T + t0 + tt;
+            v = i2_code(Ab, idx) * as[idx / kI4Group];
         } else {
             v = load_code<F>(Ab, static_cast<int64_t>(i) * T + t0 + tt);
             if constexpr (F == kI8) v *= a_scale[static_cast<int64_t>(id) * T + t0 + tt];
@@ -250,6 +264,8 @@ hipError_t launch_reconstruct(const void *arena, int f_type, const int32_t *rank
         if (out_type == kF32) MILO_RECON(kF32, kF32); else MILO_RECON(kF32, kBF16);
     } else if (f_type == kI4) {
         if (out_type == kF32) MILO_RECON(kI4, kF32); else MILO_RECON(kI4, kBF16);
+    } else if (f_type == kI2) {
+        if (out_type == kF32) MILO_RECON(kI2, kF32); else MILO_RECON(kI2, kBF16);
     } else {
         if (out_type == kF32) MILO_RECON(kI8, kF32); else MILO_RECON(kI8, kBF16);
     }

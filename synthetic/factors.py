@@ -34,6 +34,38 @@ def unpack_i4(raw: np.ndarray, n: int) -> np.ndarray:
     return np.where(out >= 8, out - 16, out).astype(np.int8)
 
 
+def pack_i2(codes: np.ndarray) -> np.ndarray:
+    """Rows of 2-bit codes in 0..3 -> bytes, element 4k + j in bits 2j, 2j + 1 of
+    byte k (the arena's order)."""
+    c = (codes.astype(np.uint8) & 3)
+    return (c[..., 0::4] | (c[..., 1::4] << 2) | (c[..., 2::4] << 4) | (c[..., 3::4] << 6)).astype(np.uint8)
+
+
+def unpack_i2(raw: np.ndarray, n: int) -> np.ndarray:
+    """Inverse of pack_i2 for rows of n codes."""
+    raw = raw.astype(np.uint8)
+    out = np.empty(raw.shape[:-1] + (n,), dtype=np.uint8)
+    for j in range(4):
+        out[..., j::4] = (raw >> (2 * j)) & 3
+    return out
+
+
+def i2_rank_bytes(T: int, d: int):
+    """Bytes one rank takes in a block's A part and B part (2-bit codes + fp32 scales)."""
+    return T // 4 + 4 * (T // I4_GROUP), d // 4 + 4 * (d // I4_GROUP)
+
+
+def read_i2_block(arena: np.ndarray, a_off: int, b_off: int, r: int, T: int, d: int):
+    """(A codes [r, T], A scales [r, T/32], B codes [r, d], B scales [r, d/32]) of a block."""
+    a_codes = unpack_i2(arena[a_off:a_off + r * T // 4].reshape(r, T // 4), T)
+    o = a_off + r * T // 4
+    a_sc = arena[o:o + 4 * r * (T // I4_GROUP)].view(np.float32).reshape(r, T // I4_GROUP)
+    b_codes = unpack_i2(arena[b_off:b_off + r * d // 4].reshape(r, d // 4), d)
+    o = b_off + r * d // 4
+    b_sc = arena[o:o + 4 * r * (d // I4_GROUP)].view(np.float32).reshape(r, d // I4_GROUP)
+    return a_codes, a_sc, b_codes, b_sc
+
+
 def i4_rank_bytes(T: int, d: int):
     """Bytes one rank takes in a block's A part and B part (codes + fp32 scales)."""
     return T // 2 + 4 * (T // I4_GROUP), d // 2 + 4 * (d // I4_GROUP)
@@ -61,6 +93,8 @@ def random_factor_set(n_blocks: int, T: int, d: int, storage: str, seed: int,
     ranks = np.asarray(ranks, dtype=np.int32)
     if storage == "i4":
         abpr, bbpr = i4_rank_bytes(T, d)
+    elif storage == "i2":
+        abpr, bbpr = i2_rank_bytes(T, d)
     else:
         abpr, bbpr = T * _ELEM[storage], d * _ELEM[storage]
     sizes = ranks.astype(np.int64) * (abpr + bbpr)
@@ -102,6 +136,24 @@ def random_factor_set(n_blocks: int, T: int, d: int, storage: str, seed: int,
             raw_b = np.concatenate([pack_i4(cb).reshape(-1), sb.reshape(-1).view(np.uint8)])
             A_dec.append((ca.astype(np.float32) * np.repeat(sa, I4_GROUP, axis=1)).astype(np.float64).T.copy())
             B_dec.append((cb.astype(np.float32) * np.repeat(sb, I4_GROUP, axis=1)).astype(np.float64))
+        elif storage == "i2":
+            # codes in 0..3 for the levels (2c - 3) s, one positive scale per 32
+            # elements of a row (some runs all code 2 with a zero scale, as the
+            # quantiser leaves an all-zero run)
+            ca = rng.integers(0, 4, size=(r, T)).astype(np.uint8)
+            cb = rng.integers(0, 4, size=(r, d)).astype(np.uint8)
+            sa = (rng.uniform(0.5, 1.5, size=(r, T // I4_GROUP)) * a_std / 3).astype(np.float32)
+            sb = (rng.uniform(0.5, 1.5, size=(r, d // I4_GROUP)) / np.sqrt(max(r, 1)) / 3).astype(np.float32)
+            if r > 0:
+                i, g = rng.integers(0, r), rng.integers(0, T // I4_GROUP)
+                ca[i, g * I4_GROUP:(g + 1) * I4_GROUP] = 2
+                sa[i, g] = 0.0
+            raw_a = np.concatenate([pack_i2(ca).reshape(-1), sa.reshape(-1).view(np.uint8)])
+            raw_b = np.concatenate([pack_i2(cb).reshape(-1), sb.reshape(-1).view(np.uint8)])
+            lv_a = (2 * ca.astype(np.int16) - 3).astype(np.float32)
+            lv_b = (2 * cb.astype(np.int16) - 3).astype(np.float32)
+            A_dec.append((lv_a * np.repeat(sa, I4_GROUP, axis=1)).astype(np.float64).T.copy())
+            B_dec.append((lv_b * np.repeat(sb, I4_GROUP, axis=1)).astype(np.float64))
         else:
             qa = rng.integers(-127, 128, size=(T, r)).astype(np.int8)
             qb = rng.integers(-127, 128, size=(r, d)).astype(np.int8)

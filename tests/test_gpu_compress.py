@@ -130,7 +130,7 @@ def _int8_invariants(f, T, d):
 
 
 @pytest.mark.parametrize("frac", [0.25, 0.5, 0.75])
-@pytest.mark.parametrize("storage", ["bf16", "i8", "i4"])
+@pytest.mark.parametrize("storage", ["bf16", "i8", "i4", "i2"])
 def test_config3_budget_precision_sweep(frac, storage):
     cfg, X64, pp, bud, f, sig, obj, sweeps, comp = _case(3, "k", storage=storage, frac=frac)
     r_gpu = f.rank.cpu().numpy()
@@ -253,7 +253,7 @@ def test_block_len_128():
     X = planted_blocks(n, T, 128, (4.0, 24.0), seed=8201, out_dtype="bf16")
     pp, bud = [0, 5, 8], [5 * 64, 3 * 64]
     eps2 = 1e-4
-    for storage in ("bf16", "f32", "i8", "i4"):
+    for storage in ("bf16", "f32", "i8", "i4", "i2"):
         f, sig, obj, sweeps = run_gpu_compress(X.to(DEV), pp, bud, eps2, storage)
         X64 = X.to(torch.float64).numpy()
         comp = oracle.compress(X64, pp, bud, eps2, storage)
@@ -267,25 +267,29 @@ def test_block_len_128():
         print(f"\n[T=128 {storage}] sigma worst/bound {worst:.3g}, recon rel-F {rec:.3g}")
 
 
+@pytest.mark.parametrize("storage", ["i4", "i2"])
 @pytest.mark.parametrize("kind", ["k", "v"])
-def test_int4_factors(kind):
-    """4-bit factors on the config-1 shapes (1024-token bf16 blocks, 50% budget).
+def test_grouped_lowbit_factors(kind, storage):
+    """4- and 2-bit factors on the config-1 shapes (1024-token bf16 blocks, 50%
+    budget).
 
-    The 4-bit path computes its factors as the fp32 storage does (the same
-    products), then quantises them.  So every code and scale must equal the
+    The low-bit paths compute their factors as the fp32 storage does (the same
+    products), then quantise them.  So every code and scale must equal the
     oracle's quantiser applied to the fp32 factors of a call on the same blocks
     (the code decided in fp32 on both sides): exact parity.  The quantised
     factors themselves differ from the oracle's by the eigenvector differences
-    the fp32 parity allows, which move codes at rounding boundaries; the rebuilt
-    blocks are therefore compared with X against the oracle's own 4-bit error."""
-    from synthetic.factors import read_i4_block
+    the fp32 parity allows, which move codes at decision boundaries; the rebuilt
+    blocks are therefore compared with X against the oracle's own low-bit error."""
+    from synthetic.factors import read_i2_block, read_i4_block
 
+    quant = oracle.quant_int4_groups if storage == "i4" else oracle.quant_int2_groups
+    read_block = read_i4_block if storage == "i4" else read_i2_block
     cfg = CONFIGS[1]
     X = layer_inputs(cfg, 0, kind, device="cpu")
     pp, bud = layer_pools(cfg)
     Xg = X.to(DEV)
     f32, s32, _, _ = run_gpu_compress(Xg, pp, bud, cfg.eps2, "f32")
-    f4, s4, _, _ = run_gpu_compress(Xg, pp, bud, cfg.eps2, "i4")
+    f4, s4, _, _ = run_gpu_compress(Xg, pp, bud, cfg.eps2, storage)
     assert torch.equal(f32.rank, f4.rank) and torch.equal(s32, s4)
     n, T, d = X.shape
     ar32, ar4 = f32.arena.cpu().numpy(), f4.arena.cpu().numpy()
@@ -297,9 +301,9 @@ def test_int4_factors(kind):
         ao, bo = int(f32.a_off[b]), int(f32.b_off[b])
         A32 = ar32[ao:ao + 4 * r * T].view(np.float32).reshape(r, T)
         B32 = ar32[bo:bo + 4 * r * d].view(np.float32).reshape(r, d)
-        sa, ca, _ = oracle.quant_int4_groups(A32)
-        sb, cb, _ = oracle.quant_int4_groups(B32)
-        ac, asc, bc, bsc = read_i4_block(ar4, int(f4.a_off[b]), int(f4.b_off[b]), r, T, d)
+        sa, ca, _ = quant(A32)
+        sb, cb, _ = quant(B32)
+        ac, asc, bc, bsc = read_block(ar4, int(f4.a_off[b]), int(f4.b_off[b]), r, T, d)
         assert np.array_equal(ac, ca), f"block {b}: A codes"
         assert np.array_equal(bc, cb), f"block {b}: B codes"
         assert np.array_equal(asc, sa.astype(np.float32)) and np.array_equal(bsc, sb.astype(np.float32)), b
@@ -308,12 +312,12 @@ def test_int4_factors(kind):
     key = (1, kind, n)
     if key not in _SVD:
         _SVD[key] = oracle.svd_blocks(X64)
-    comp = oracle.compress(X64, pp, bud, cfg.eps2, "i4", svd=_SVD[key])
+    comp = oracle.compress(X64, pp, bud, cfg.eps2, storage, svd=_SVD[key])
     xh = reconstruct_all(f4).cpu().numpy()
     e_gpu = np.array([np.linalg.norm(xh[b] - X64[b]) / np.linalg.norm(X64[b]) for b in range(n)])
     e_ora = np.array([np.linalg.norm(oracle.reconstruct(comp.A[b], comp.B[b]) - X64[b]) / np.linalg.norm(X64[b])
                       for b in range(n)])
-    print(f"\n[i4 {kind}] rel-F to X: gpu mean {e_gpu.mean():.4f} max {e_gpu.max():.4f}; "
+    print(f"\n[{storage} {kind}] rel-F to X: gpu mean {e_gpu.mean():.4f} max {e_gpu.max():.4f}; "
           f"oracle mean {e_ora.mean():.4f} max {e_ora.max():.4f}; memory ratio "
           f"{f4.nbytes() / (n * T * d * 2):.4f}")
     assert (e_gpu <= 1.1 * e_ora + 2e-3).all(), np.max(e_gpu - 1.1 * e_ora)

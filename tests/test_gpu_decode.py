@@ -11,9 +11,9 @@ Two kinds of cases:
 Tolerances: the kernels round the rebuilt keys, the
 rotated queries and the softmax weights to bf16 MFMA operands (fp32 factors:
 split into two bf16 terms), so errors scale with max|v|: 2e-2 * max|v| for bf16
-and INT8 factors, 1e-4 * max|v| for fp32 factors, and 5e-2 * max|v| for 4-bit
-factors, whose decoded values (code * scale, not bf16 numbers) are rounded to
-bf16 operands on both the key and the value side.
+and INT8 factors, 1e-4 * max|v| for fp32 factors, and 5e-2 * max|v| for 4- and
+2-bit factors, whose decoded values (level * scale, not bf16 numbers) are
+rounded to bf16 operands on both the key and the value side.
 """
 import numpy as np
 import pytest
@@ -28,7 +28,7 @@ from _parity import layer_pools, run_gpu_compress
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-TOL = {"bf16": 2e-2, "i8": 2e-2, "i4": 5e-2, "f32": 1e-4}
+TOL = {"bf16": 2e-2, "i8": 2e-2, "i4": 5e-2, "i2": 5e-2, "f32": 1e-4}
 
 
 def _factors_on_gpu(tensors, storage, n_blocks, T, d=128):
@@ -58,7 +58,7 @@ def _check(got, ref, vmax, storage, label):
     assert err <= bound, f"{label}: {err} > {bound}"
 
 
-@pytest.mark.parametrize("storage", ["bf16", "f32", "i8", "i4"])
+@pytest.mark.parametrize("storage", ["bf16", "f32", "i8", "i4", "i2"])
 @pytest.mark.parametrize("q_scale", [1.0, 10.0])
 def test_kernel_level_all_blocks(storage, q_scale):
     batch, hkv, hq, T, bps, d = 2, 2, 16, 256, 6, 128
@@ -81,7 +81,7 @@ def test_kernel_level_all_blocks(storage, q_scale):
         _check(got, ref, vmax, storage, f"{storage} q*{q_scale} split {split}")
 
 
-@pytest.mark.parametrize("storage", ["bf16", "i8", "i4"])
+@pytest.mark.parametrize("storage", ["bf16", "i8", "i4", "i2"])
 def test_kernel_level_selection_and_tail(storage):
     """GQA 7:1, a per-sequence block selection (one sequence selects nothing),
     and an uncompressed tail of different lengths per sequence."""
@@ -155,7 +155,7 @@ def test_segmented_tail_positions():
         assert worst <= 2e-2 * vmax
 
 
-@pytest.mark.parametrize("storage", ["bf16", "f32", "i8", "i4"])
+@pytest.mark.parametrize("storage", ["bf16", "f32", "i8", "i4", "i2"])
 def test_kernel_level_long_blocks(storage):
     """2048-token blocks with the longest split (one workgroup per block, 64 tiles)
     and a shorter one; GQA 8:1, ranks 0, 128 and ragged."""

@@ -15,7 +15,7 @@ import torch
 import oracle
 
 from block_wise_rank_amd import Factors, MiloError, milo_decode_attention, milo_fetch_blocks
-from synthetic.factors import i4_rank_bytes, random_factor_set
+from synthetic.factors import i2_rank_bytes, i4_rank_bytes, random_factor_set
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -37,7 +37,7 @@ def _decode(q, q_pos, kf, vf, bps, hkv, sel_ptr, sel_blk, sel_max):
     return out
 
 
-@pytest.mark.parametrize("storage", ["bf16", "i8", "i4", "f32"])
+@pytest.mark.parametrize("storage", ["bf16", "i8", "i4", "i2", "f32"])
 def test_fetch_then_decode_equals_resident(storage):
     batch, hkv, hq, T, bps = 2, 2, 16, 512, 8
     n = batch * hkv * bps
@@ -67,6 +67,8 @@ def test_fetch_then_decode_equals_resident(storage):
 
     if storage == "i4":
         abpr, bbpr = i4_rank_bytes(T, 128)
+    elif storage == "i2":
+        abpr, bbpr = i2_rank_bytes(T, 128)
     else:
         e = {"f32": 4, "bf16": 2, "i8": 1}[storage]
         abpr, bbpr = T * e, 128 * e
@@ -100,7 +102,7 @@ def test_fetch_then_decode_equals_resident(storage):
     vmax = max(float(np.abs(Vh[(s * hkv + h) * bps + b]).max()) for s in range(batch) for h in range(hkv)
                for b in sel[s])
     err = float(np.abs(got.cpu().numpy() - ref).max())
-    tol = {"bf16": 2e-2, "i8": 2e-2, "i4": 5e-2, "f32": 1e-4}[storage]
+    tol = {"bf16": 2e-2, "i8": 2e-2, "i4": 5e-2, "i2": 5e-2, "f32": 1e-4}[storage]
     print(f"\n[offload {storage}] max|err| vs oracle {err:.3g}, bound {tol * vmax:.3g}")
     assert err <= tol * vmax
 
