@@ -11,7 +11,7 @@
 // rank row of A^T (tokens) and of B (features) gets s = max|run| / 7 and codes
 // rint(x / s) in [-7, 7], decided in fp32.
 // 2-bit: the same runs with s = max|run| / 3 and a code c in 0..3 for the
-// level (2c - 3) s nearest to x: |x / s| >= 2 (the IEEE quotient) takes the
+// level (2c - 3) s nearest to x: |x / s| >= 2 (the fp32 quotient) takes the
 // outer level of x's sign, else the inner one; x = 0 and s = 0 give code 2.
 //
 // A^T = B~ X^T runs on bf16 MFMA (M = rank, N = token, K = feature): the
@@ -65,21 +65,13 @@ __device__ __forceinline__ void store_b_i4(const float (&v)[8][8], int i, int r,
             make_float4(sB4[0], sB4[1], sB4[2], sB4[3]);
 }
 
-// 2-bit code of x in a run of scale s, the decision taken by the IEEE quotient.
+// 2-bit code of x in a run of scale s.  The quotient's test fl(|x| / s) >= 2
+// holds exactly when |x| >= 2 s: 2 s is exact in fp32, and any fp32 value below
+// 2 s has a quotient of at most 2 - 2^-23, which rounds below 2.  So no division
+// is needed for the same decision.
 __device__ __forceinline__ uint32_t code2(float x, float s) {
     if (!(s > 0.f)) return 2u;
-    const bool outer = __fdiv_rn(fabsf(x), s) >= 2.f;
-    return x < 0.f ? (outer ? 0u : 1u) : (outer ? 3u : 2u);
-}
-
-// The same decision from |x| * inv, inv = fl(1 / s): that product is within
-// 1e-6 of |x / s| (|x / s| <= 3), and so is fl(|x / s|), so unless it lies
-// within 1e-5 of 2 both fall on the same side; there the quotient decides.
-__device__ __forceinline__ uint32_t code2_fast(float x, float s, float inv) {
-    if (!(s > 0.f)) return 2u;
-    float p = fabsf(x) * inv;
-    if (fabsf(p - 2.f) <= 1e-5f) p = __fdiv_rn(fabsf(x), s);
-    const bool outer = p >= 2.f;
+    const bool outer = fabsf(x) >= 2.f * s;
     return x < 0.f ? (outer ? 0u : 1u) : (outer ? 3u : 2u);
 }
 
@@ -629,14 +621,13 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
                     m = fmaxf(fmaxf(m, fmaxf(fabsf(a.x), fabsf(a.y))), fmaxf(fabsf(a.z), fabsf(a.w)));
                 }
                 const float sA = __fdiv_rn(m, 3.f);
-                const float inv = sA > 0.f ? __fdiv_rn(1.f, sA) : 0.f;
                 uint32_t w[2] = {0u, 0u};
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const float4 a = src[k];
                     const float f[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[k >> 2] |= code2_fast(f[e], sA, inv) << (2 * (4 * (k & 3) + e));
+                    for (int e = 0; e < 4; ++e) w[k >> 2] |= code2(f[e], sA) << (2 * (4 * (k & 3) + e));
                 }
                 if (ir < r) {
                     *reinterpret_cast<uint2 *>(Ab + static_cast<int64_t>(ir) * (T / 4) + (tok0 + 32 * gg) / 4) =
@@ -659,9 +650,10 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
                 // code = rint(x / s) with the IEEE quotient.  x * fl(1 / s) is within
                 // 1e-6 of x / s (|x / s| <= 7.5), and so is fl(x / s): unless x * (1 / s)
                 // lies within 1e-5 of a half-integer, both round to the same code.
-                // Near one, the quotient itself decides.
+                // A run with such an element (rare) takes every code from the quotient.
                 const float inv = sA > 0.f ? __fdiv_rn(1.f, sA) : 0.f;
                 uint32_t w[4] = {0u, 0u, 0u, 0u};
+                bool near = false;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const float4 a = src[k];
@@ -670,9 +662,23 @@ __global__ __launch_bounds__(256, 2) void project_split_kernel(
                     for (int e = 0; e < 4; ++e) {
                         const float qf = f[e] * inv;
                         float c = rintf(qf);
-                        if (fabsf(qf - c) > 0.5f - 1e-5f) c = rintf(__fdiv_rn(f[e], sA));
+                        near |= fabsf(qf - c) > 0.5f - 1e-5f;
                         c = fminf(fmaxf(c, -7.f), 7.f);
                         w[k >> 1] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xfu) << (4 * (4 * (k & 1) + e));
+                    }
+                }
+                if (near) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) w[k] = 0u;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float4 a = src[k];
+                        const float f[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float c = fminf(fmaxf(rintf(__fdiv_rn(f[e], sA)), -7.f), 7.f);
+                            w[k >> 1] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xfu) << (4 * (4 * (k & 1) + e));
+                        }
                     }
                 }
                 if (ir < r) {

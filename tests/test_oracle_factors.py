@@ -200,6 +200,24 @@ def test_int2_error_bound_and_groups(oracle_lib):
     assert np.array_equal(c3, codes) and np.allclose(d3, deq, rtol=1e-6, atol=0)
 
 
+def test_int2_decision_without_division():
+    """The 2-bit decision fl(|x| / s) >= 2 (fp32, correctly rounded) equals
+    |x| >= 2 s for every fp32 x and s > 0: the projection kernel takes it that
+    way.  Checked on random scales over many binades, at 2 s and its fp32
+    neighbours, and on random values."""
+    rng = np.random.default_rng(7)
+    s = (rng.uniform(1, 2, 20000) * 2.0 ** rng.integers(-140, 120, 20000)).astype(np.float32)
+    s = np.concatenate([s, np.float32(2.0) ** np.arange(-149, 127).astype(np.float32)])
+    two_s = (np.float32(2) * s).astype(np.float32)
+    xs = [two_s, np.nextafter(two_s, np.float32(0)), np.nextafter(two_s, np.float32(np.inf)),
+          (s * rng.uniform(0, 3, s.size)).astype(np.float32)]
+    with np.errstate(all="ignore"):
+        for x in xs:
+            ok = np.isfinite(x) & (s > 0)
+            q = (x[ok] / s[ok]).astype(np.float32)
+            assert np.array_equal(q >= np.float32(2), x[ok] >= two_s[ok])
+
+
 def test_store_roundtrip_shapes(oracle_lib, block):
     X, sigma, V = block
     A, B = oracle_lib.project(X, V, 50)
