@@ -9,8 +9,10 @@
 // (sigma desc, block asc, index asc), and r_b counts block b's share.  This
 // kernel computes that selection directly:
 //   1. the R'-th largest sigma, tau, by a bitwise search over the fp32 bit
-//      patterns (monotone for sigma >= 0): 31 rounds, each counting per block
-//      with a binary search over its sorted row;
+//      patterns (monotone for sigma >= 0): 31 rounds, each counting the keys
+//      >= a candidate.  Pools of up to 8192 keys hold them in registers (32 per
+//      thread) and each round is a register count plus one barrier; larger pools
+//      count per block with a binary search over its sorted row;
 //   2. every value > tau is taken; the remaining R' - #{> tau} ranks go to the
 //      values == tau in block order (an exclusive scan over the blocks).
 // Exact integer work on fp32 keys: the ranks do not depend on eps, and equal
@@ -82,20 +84,26 @@ __device__ Tv block_sum(Tv v, Tv *red) {
     return tot;
 }
 
-// Exclusive prefix over the 256 threads (thread order), returns the prefix.
+// Exclusive prefix over the 256 threads (thread order), returns the prefix:
+// an inclusive scan inside each wave (shuffles), then the totals of the waves
+// before (one barrier).  buf holds at least 4 entries.
 __device__ int64_t block_exclusive_scan(int64_t v, int64_t *buf) {
-    const int tid = threadIdx.x;
-    __syncthreads();
-    buf[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        const int64_t add = tid >= o ? buf[tid - o] : 0;
-        __syncthreads();
-        buf[tid] += add;
-        __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int64_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
     }
-    return buf[tid] - v;
+    __syncthreads();  // earlier readers of buf are done
+    if (lane == 63) buf[wave] = x;
+    __syncthreads();
+    int64_t before = 0;
+    for (int w = 0; w < wave; ++w) before += buf[w];
+    return before + x - v;
 }
+
+constexpr int kKeysPerThread = 32;  // pools of up to 8192 keys are searched in registers
 
 __global__ __launch_bounds__(256) void alloc_kernel(
     const float *__restrict__ sigma, int pitch, int k, const int32_t *__restrict__ pool_ptr,
@@ -104,6 +112,8 @@ __global__ __launch_bounds__(256) void alloc_kernel(
     int64_t *__restrict__ a_off, int64_t *__restrict__ b_off, int a_bpr, int b_bpr, int policy,
     uint64_t seed) {
     __shared__ int64_t red64[4];
+    __shared__ int red32[2][4];
+    __shared__ int s_ge[256], s_gt[256], s_rank[256];
     __shared__ double redd[4];
     __shared__ int64_t scan_buf[256];
 
@@ -127,7 +137,55 @@ __global__ __launch_bounds__(256) void alloc_kernel(
     // 1. tau = key of the R-th largest value (only needed when 0 < R < cap).
     uint32_t tau = 0;
     const bool partial = R > 0 && R < cap && policy != kAllocUniform;
-    if (partial) {
+    // small pools: keys in registers, per-block counts and the objective spread
+    // over all threads (a thread owns at most one block then)
+    const bool cached = cap <= 256 * kKeysPerThread && n <= 256;
+    if (partial && cached) {
+        // keys in registers: thread t holds keys t, t + 256, ... of the pool in
+        // (block, index) order; padding keys are 0, which no candidate (>= 1)
+        // counts, exactly as a zero sigma
+        uint32_t keys[kKeysPerThread];
+#pragma unroll
+        for (int q = 0; q < kKeysPerThread; ++q) {
+            const int idx = tid + 256 * q;
+            uint32_t key = 0;
+            if (idx < cap) {
+                const int j = idx / k, i = idx - j * k;
+                key = rnd ? random_key(seed, pool, j, i)
+                          : key_bits(sigma[static_cast<int64_t>(b_lo + j - blk_lo) * pitch + i]);
+            }
+            keys[q] = key;
+        }
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int bit = rnd ? 31 : 30, round = 0; bit >= 0; --bit, ++round) {  // sigma keys have a clear sign bit
+            const uint32_t cand = tau | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int q = 0; q < kKeysPerThread; ++q) cnt += keys[q] >= cand ? 1 : 0;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+            // two buffers: a wave writes round r + 1's counts only after every wave
+            // has passed round r's barrier, that is after all reads of round r - 1
+            if (lane == 0) red32[round & 1][wave] = cnt;
+            __syncthreads();
+            const int64_t tot = static_cast<int64_t>(red32[round & 1][0]) + red32[round & 1][1] +
+                                red32[round & 1][2] + red32[round & 1][3];
+            if (tot >= R) tau = cand;  // uniform decision
+        }
+        // per block: keys >= tau and keys > tau
+        for (int j = tid; j < n; j += 256) s_ge[j] = s_gt[j] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kKeysPerThread; ++q) {
+            const int idx = tid + 256 * q;
+            if (idx < cap) {
+                const int j = idx / k;
+                if (keys[q] >= tau) atomicAdd(&s_ge[j], 1);
+                if (keys[q] > tau) atomicAdd(&s_gt[j], 1);
+            }
+        }
+        __syncthreads();
+    } else if (partial) {
         for (int bit = rnd ? 31 : 30; bit >= 0; --bit) {  // sigma keys have a clear sign bit
             const uint32_t cand = tau | (1u << bit);
             int64_t cnt = 0;
@@ -138,11 +196,20 @@ __global__ __launch_bounds__(256) void alloc_kernel(
     }
 
     // 2. ranks: strictly greater values, then ties in block order.
+    auto ge_gt = [&](int b, int &ge, int &gt) {
+        if (cached) {
+            ge = s_ge[b - b_lo];
+            gt = s_gt[b - b_lo];
+        } else {
+            ge = count(b, tau);
+            gt = tau == 0xffffffffu ? 0 : count(b, tau + 1);
+        }
+    };
     int64_t gt_sum = 0, eq_sum = 0;
     for (int b = my_lo; b < my_hi; ++b) {
         if (partial) {
-            const int ge = count(b, tau);
-            const int gt = tau == 0xffffffffu ? 0 : count(b, tau + 1);
+            int ge, gt;
+            ge_gt(b, ge, gt);
             gt_sum += gt;
             eq_sum += ge - gt;
         }
@@ -164,8 +231,8 @@ __global__ __launch_bounds__(256) void alloc_kernel(
         } else if (!partial) {
             r = R == 0 ? 0 : k;
         } else {
-            const int ge = count(b, tau);
-            const int gt = tau == 0xffffffffu ? 0 : count(b, tau + 1);
+            int ge, gt;
+            ge_gt(b, ge, gt);
             int64_t extra = need - eq_before;
             extra = extra < 0 ? 0 : (extra > ge - gt ? ge - gt : extra);
             eq_before += ge - gt;
@@ -173,9 +240,26 @@ __global__ __launch_bounds__(256) void alloc_kernel(
         }
         rank[b] = r;
         rank_sum += r;
-        for (int i = 0; i < r; ++i) {
-            const double s = static_cast<double>(row[i]);
-            obj += log1p(s * s / eps2);
+        if (cached) {
+            s_rank[b - b_lo] = r;
+        } else {
+            for (int i = 0; i < r; ++i) {
+                const double s = static_cast<double>(row[i]);
+                obj += log1p(s * s / eps2);
+            }
+        }
+    }
+    if (cached) {
+        __syncthreads();
+        for (int q = 0; q < kKeysPerThread; ++q) {
+            const int idx = tid + 256 * q;
+            if (idx < cap) {
+                const int j = idx / k, i = idx - j * k;
+                if (i < s_rank[j]) {
+                    const double s = static_cast<double>(sigma[static_cast<int64_t>(b_lo + j - blk_lo) * pitch + i]);
+                    obj += log1p(s * s / eps2);
+                }
+            }
         }
     }
     // Objective (reduction order is fixed by the thread layout: deterministic).
