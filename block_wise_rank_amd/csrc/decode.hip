@@ -1099,19 +1099,27 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
 #pragma unroll
         for (int c = 0; c < 4; ++c) dst[c] = make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]);
     }
-    for (int e = tid; e < 16 * rpad; e += kThreads) {
-        const int g = e / rpad, r = e - g * rpad;
+    {
+        // thread t: head g = t / 32, ranks t % 32 + 32 j; the head's wave weights
+        // exp2(m_w - M) are computed once per thread
+        static_assert(kThreads == 16 * 32, "one head per 32 threads");
+        const int g = tid >> 5;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mlw[(w * 16 + g) * 2]);
-        float uvs = 0.f;
+        float cf[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float mw = mlw[(w * 16 + g) * 2];
-            const float cf = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-            if (cf != 0.f && r < rv) uvs += cf * uw[(w * 16 + g) * kUP + r];
+            cf[w] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
         }
-        uacc[g * kUP + r] = uvs;
+        for (int r = tid & 31; r < rpad; r += 32) {
+            float uvs = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+                if (cf[w] != 0.f && r < rv) uvs += cf[w] * uw[(w * 16 + g) * kUP + r];
+            uacc[g * kUP + r] = uvs;
+        }
     }
     if (tid < G) {  // (max, sum) of every head, also when rpad == 0 (rank-0 values)
         float M = -INFINITY, Ls = 0.f;
