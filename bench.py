@@ -554,6 +554,35 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
         prof_dec = milo.milo_profile_read()
         milo.milo_profile_enable(False)
 
+    # the same decode-only pass recorded once into a graph and replayed (launch
+    # gaps between the 3 L kernels of a step removed); each replay's outputs are
+    # checked against the eager pass's
+    dec_graph = None
+    if decode_only_steps > 0:
+        try:
+            ref = [o.clone() for o in outs]
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for layer in range(L):
+                    decode_layer(layer, dws)
+            graph.replay()
+            torch.cuda.synchronize()
+            same = all(torch.equal(o, r) for o, r in zip(outs, ref))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(decode_only_steps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            same = same and all(torch.equal(o, r) for o, r in zip(outs, ref))
+            g_ms = e0.elapsed_time(e1) / decode_only_steps
+            dec_graph = {"ms_per_step": round(g_ms, 3),
+                         "context_tokens_per_s": cfg.context_tokens_per_step / (g_ms / 1e3),
+                         "outputs_equal_eager": bool(same)}
+            del graph
+        except Exception as ex:  # a runtime that cannot record these launches
+            dec_graph = {"error": str(ex)[:200]}
+
     # the unfused alternative: rebuild every attended block into a staging cache,
     # then attend over it as an uncompressed cache (one pass over all layers)
     rebuild = None
@@ -742,6 +771,7 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
             "decode_context_tokens_per_s": ctx_tokens / (dec_ms / 1e3),
             "decode_only_ms_per_step": None if dec_only_ms is None else round(dec_only_ms, 3),
             "decode_only_context_tokens_per_s": None if dec_only_ms is None else ctx_tokens / (dec_only_ms / 1e3),
+            "decode_only_graph": dec_graph,
             "jacobi_sweeps_mean": round(sweeps_mean, 3),
             "blocks_at_sweep_cap": n_bad,
             "kernels_ms_per_step": {n: round(v[1] / steps, 3) for n, v in prof.items()},

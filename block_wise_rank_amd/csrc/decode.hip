@@ -53,6 +53,7 @@ constexpr int kTile = 32;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kMaxDevices = 64;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kUP = 132;   // pitch (floats) of per-head u rows in the merge
@@ -1278,9 +1279,19 @@ hipError_t launch_decode_kernel(const DecodeParams &p, hipStream_t st) {
         const int tl = lds_layout(TF, TF == kF32 ? 2 : 1, n_tiles, true, p.group).total;
         lds = lds > tl ? lds : tl;
     }
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_kernel<F, TF>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    // The kernel's dynamic LDS limit is raised to the CU's maximum once per
+    // device, so that a launch recorded into a graph is a plain launch.
+    static bool limit_set[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices || !limit_set[dev]) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_kernel<F, TF>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < kMaxDevices) limit_set[dev] = true;
+    }
+    if (lds > kMaxLds) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(p.n_splits), static_cast<unsigned>(p.n_kv_heads),
                     static_cast<unsigned>(p.batch));
     hipLaunchKernelGGL((decode_kernel<F, TF>), grid, dim3(kThreads), lds, st, p);
