@@ -1174,27 +1174,38 @@ __device__ __forceinline__ void decode_partial(const DecodeParams &p, const int 
 }
 
 // One workgroup per (sequence, query head): the split maxima and weights are
-// computed by all threads in parallel, then thread j sums its output column.
+// computed by all threads in parallel; thread (k, j) then sums dimension j over
+// the splits k, k + kCG, ... (eight loads in flight), and the kCG partial sums
+// are added in group order.
+constexpr int kCG = 4;  // split groups per output column
+
 template <int OT>
-__global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kD * kCG) void decode_combine_kernel(const DecodeParams p) {
     __shared__ float coef[1024];
-    __shared__ float red[2];
+    __shared__ float red[kD * kCG / 64];
+    __shared__ float part[kCG][kD];
     const int hq = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+    const int dim = tid & (kD - 1), grp = tid / kD;
+    const int lane = tid & 63, wave = tid >> 6;
+    constexpr int kNW = kD * kCG / 64;
+    constexpr int kNT = kD * kCG;
     const int G = p.group;
     const int h = hq / G, g = hq - h * G;
     const int64_t base = static_cast<int64_t>(s * p.n_kv_heads + h) * p.n_splits;
     float num = 0.f, den_part = 0.f;
     // chunks of up to 1024 splits (the weights of one chunk fit in LDS)
     float M = -INFINITY;
-    for (int sp = tid; sp < p.n_splits; sp += 128) M = fmaxf(M, p.part_ml[((base + sp) * G + g) * 2]);
+    for (int sp = tid; sp < p.n_splits; sp += kNT) M = fmaxf(M, p.part_ml[((base + sp) * G + g) * 2]);
     M = wave_max(M);
-    if ((tid & 63) == 0) red[tid >> 6] = M;
+    if (lane == 0) red[wave] = M;
     __syncthreads();
-    M = fmaxf(red[0], red[1]);
+    M = red[0];
+#pragma unroll
+    for (int w = 1; w < kNW; ++w) M = fmaxf(M, red[w]);
     __syncthreads();
     for (int c0 = 0; c0 < p.n_splits; c0 += 1024) {
         const int cn = min(1024, p.n_splits - c0);
-        for (int i = tid; i < cn; i += 128) {
+        for (int i = tid; i < cn; i += kNT) {
             const float m = p.part_ml[((base + c0 + i) * G + g) * 2];
             const float c = (m == -INFINITY || M == -INFINITY) ? 0.f : exp2f(m - M);
             coef[i] = c;
@@ -1203,29 +1214,37 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeParams 
         __syncthreads();
         // eight loads in flight at a time (indices clamped; a split with weight 0
         // may hold stale values, which the select keeps out), summed in order
-        for (int i0 = 0; i0 < cn; i0 += 8) {
+        for (int i0 = grp; i0 < cn; i0 += 8 * kCG) {
             float v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = p.part_o[((base + c0 + min(i0 + u, cn - 1)) * G + g) * kD + tid];
+            for (int u = 0; u < 8; ++u) v[u] = p.part_o[((base + c0 + min(i0 + kCG * u, cn - 1)) * G + g) * kD + dim];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (i0 + u < cn) {
-                    const float c = coef[i0 + u];
+                if (i0 + kCG * u < cn) {
+                    const float c = coef[i0 + kCG * u];
                     num += c != 0.f ? c * v[u] : 0.f;
                 }
         }
         __syncthreads();
     }
+    part[grp][dim] = num;
     den_part = wave_sum(den_part);
-    if ((tid & 63) == 0) red[tid >> 6] = den_part;
+    if (lane == 0) red[wave] = den_part;
     __syncthreads();
-    const float den = red[0] + red[1];
-    const float o = den > 0.f ? num / den : 0.f;
-    const int64_t oi = (static_cast<int64_t>(s) * p.n_q_heads + hq) * kD + tid;
-    if constexpr (OT == kF32)
-        static_cast<float *>(p.out)[oi] = o;
-    else
-        static_cast<uint16_t *>(p.out)[oi] = f32_to_bf16_bits(o);
+    if (grp == 0) {
+        float den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) den += red[w];
+        float o = part[0][dim];
+#pragma unroll
+        for (int k = 1; k < kCG; ++k) o += part[k][dim];
+        o = den > 0.f ? o / den : 0.f;
+        const int64_t oi = (static_cast<int64_t>(s) * p.n_q_heads + hq) * kD + dim;
+        if constexpr (OT == kF32)
+            static_cast<float *>(p.out)[oi] = o;
+        else
+            static_cast<uint16_t *>(p.out)[oi] = f32_to_bf16_bits(o);
+    }
 }
 
 // One launch for every split of a call: workgroup x < n_sel * block_splits
@@ -1341,9 +1360,9 @@ hipError_t launch_decode_tables(const DecodeParams &p, hipStream_t st) {
 hipError_t launch_decode_combine(const DecodeParams &p, hipStream_t st) {
     const dim3 cgrid(static_cast<unsigned>(p.n_q_heads), static_cast<unsigned>(p.batch));
     if (p.out_type == kF32)
-        hipLaunchKernelGGL(decode_combine_kernel<kF32>, cgrid, dim3(128), 0, st, p);
+        hipLaunchKernelGGL(decode_combine_kernel<kF32>, cgrid, dim3(kD * kCG), 0, st, p);
     else
-        hipLaunchKernelGGL(decode_combine_kernel<kBF16>, cgrid, dim3(128), 0, st, p);
+        hipLaunchKernelGGL(decode_combine_kernel<kBF16>, cgrid, dim3(kD * kCG), 0, st, p);
     return hipGetLastError();
 }
 
