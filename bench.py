@@ -66,9 +66,10 @@ def parse():
                     help="compression calls per kind (runs of whole layers)")
     ap.add_argument("--filter-csv", nargs=2, metavar=("IN", "OUT"),
                     help="copy the rows of a rocprofv3 CSV that belong to libmilo's kernels (no GPU)")
-    ap.add_argument("--extra", default="2,1",
+    ap.add_argument("--extra", default="2,1,4:i4,4:i2",
                     help="other workloads measured after the main one (config indices, or 'none'): "
-                         "multi-layer ones as whole steps, one-layer ones warm and cold")
+                         "multi-layer ones as whole steps, one-layer ones warm and cold; "
+                         "'c:fmt' runs config c with factor format fmt (with its offload step)")
     ap.add_argument("--command", action="append", default=[],
                     help="with --ingest-*: the command(s) that produced the CSV files")
     return ap.parse_args()
@@ -937,10 +938,23 @@ def main():
                             compress_streams=args.compress_streams, compress_chunks=args.compress_chunks)
     torch.cuda.empty_cache()
     extra = {}
-    for c in [int(x) for x in args.extra.split(",") if x.strip()] if args.extra != "none" else []:
+    for item in [x.strip() for x in args.extra.split(",") if x.strip()] if args.extra != "none" else []:
+        c, _, edt = item.partition(":")
+        c = int(c)
+        ecfg = CONFIGS[c]
+        if edt:
+            # the same workload with another factor format (its offload step included)
+            if edt == fdt and c == args.config:
+                continue
+            r = run_workload(ecfg, edt, 2, 1, decode_only_steps=10, want_rebuild=False,
+                             want_offload=True, want_cpu=False, counters=False)
+            r["ms_per_step"] = round(r.pop("step_ms"), 3)
+            r["value"] = ecfg.context_tokens_per_step / (r["ms_per_step"] / 1e3)
+            extra[f"config{c}_{edt}"] = r
+            torch.cuda.empty_cache()
+            continue
         if c == args.config:
             continue
-        ecfg = CONFIGS[c]
         if ecfg.layers == 1:
             extra[f"config{c}"] = run_warm_cold(ecfg, ecfg.storage)
         else:
