@@ -324,6 +324,42 @@ def test_grouped_lowbit_factors(kind, storage):
     assert abs(e_gpu.mean() - e_ora.mean()) <= 0.05 * e_ora.mean()
 
 
+@pytest.mark.parametrize("storage", ["i4", "i2"])
+def test_grouped_lowbit_factors_fp32_input(storage):
+    """The fp32-input projection (X split into three bf16 terms) into 4- and 2-bit
+    factors, on the config-0 shapes (256-token fp32 blocks, K and V of the planted
+    spectra): every code and scale equals the oracle's quantiser applied to the
+    fp32 factors a call with fp32 storage writes for the same blocks."""
+    from synthetic.factors import read_i2_block, read_i4_block
+
+    quant = oracle.quant_int4_groups if storage == "i4" else oracle.quant_int2_groups
+    read_block = read_i4_block if storage == "i4" else read_i2_block
+    cfg = CONFIGS[0]
+    pp, bud = layer_pools(cfg)
+    for kind in ("k", "v"):
+        X = layer_inputs(cfg, 0, kind, device=DEV)
+        assert X.dtype == torch.float32
+        f32, s32, _, _ = run_gpu_compress(X, pp, bud, cfg.eps2, "f32")
+        fq, sq, _, _ = run_gpu_compress(X, pp, bud, cfg.eps2, storage)
+        assert torch.equal(f32.rank, fq.rank) and torch.equal(s32, sq)
+        n, T, d = X.shape
+        ar32, arq = f32.arena.cpu().numpy(), fq.arena.cpu().numpy()
+        rk = fq.rank.cpu().numpy()
+        for b in range(n):
+            r = int(rk[b])
+            if r == 0:
+                continue
+            ao, bo = int(f32.a_off[b]), int(f32.b_off[b])
+            A32 = ar32[ao:ao + 4 * r * T].view(np.float32).reshape(r, T)
+            B32 = ar32[bo:bo + 4 * r * d].view(np.float32).reshape(r, d)
+            sa, ca, _ = quant(A32)
+            sb, cb, _ = quant(B32)
+            ac, asc, bc, bsc = read_block(arq, int(fq.a_off[b]), int(fq.b_off[b]), r, T, d)
+            assert np.array_equal(ac, ca), f"{kind} block {b}: A codes"
+            assert np.array_equal(bc, cb), f"{kind} block {b}: B codes"
+            assert np.array_equal(asc, sa.astype(np.float32)) and np.array_equal(bsc, sb.astype(np.float32))
+
+
 @pytest.mark.parametrize("T", [192, 1088])
 @pytest.mark.parametrize("storage", ["bf16", "f32", "i8"])
 def test_ragged_tile_counts(T, storage):
