@@ -96,17 +96,20 @@ def test_ranks_bit_exact_given_oracle_sigma():
         torch.cuda.synchronize()
         r_o, _, _ = oracle.allocate(sig.astype(np.float64), R, 1e-4)
         assert np.array_equal(rank.cpu().numpy(), r_o), R
-    # random multi-pool layout with uneven pool sizes and max_rank < d
-    sig = -np.sort(-rng.uniform(0, 1, size=(37, 128)).astype(np.float32), axis=1)
-    pp = [0, 5, 5, 17, 37]
-    bud = [100, 7, 0, 2000]
-    rank = torch.empty(37, dtype=torch.int32, device=DEV)
-    milo_allocate_ranks(torch.from_numpy(sig).to(DEV), 64, pp, bud, 1e-4, rank)
-    torch.cuda.synchronize()
-    rg = rank.cpu().numpy()
-    for p in range(4):
-        r_o, _, _ = oracle.allocate(sig[pp[p]:pp[p + 1], :64].astype(np.float64), bud[p], 1e-4)
-        assert np.array_equal(rg[pp[p]:pp[p + 1]], r_o), p
+    # random multi-pool layout with uneven pool sizes and max_rank < d; the last
+    # pool (150 x 64 keys, and 150 x 128 below) is past what the kernel searches
+    # in registers
+    sig = -np.sort(-rng.uniform(0, 1, size=(187, 128)).astype(np.float32), axis=1)
+    pp = [0, 5, 5, 17, 37, 187]
+    bud = [100, 7, 0, 2000, 5000]
+    for k in (64, 128):
+        rank = torch.empty(187, dtype=torch.int32, device=DEV)
+        milo_allocate_ranks(torch.from_numpy(sig).to(DEV), k, pp, bud, 1e-4, rank)
+        torch.cuda.synchronize()
+        rg = rank.cpu().numpy()
+        for p in range(5):
+            r_o, _, _ = oracle.allocate(sig[pp[p]:pp[p + 1], :k].astype(np.float64), bud[p], 1e-4)
+            assert np.array_equal(rg[pp[p]:pp[p + 1]], r_o), (k, p)
 
 
 def _int8_invariants(f, T, d):
