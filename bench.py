@@ -638,7 +638,7 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     # ---------------- algorithmic work per kernel launch ----------------
     ranks = {k: F[k].rank.to(torch.int64) for k in ("k", "v")}
     sw = torch.cat([sweeps["k"], sweeps["v"]]).to(torch.float64)
-    sweeps_mean = float(sw.abs().mean())
+    sweeps_mean = float(sw.abs().mean()) / 127  # sweeps_out counts rounds, 127 per sweep
     # bytes per factor element (4-bit: half a byte + an fp32 scale per 32 elements;
     # 2-bit: a quarter byte + the same scales)
     fe = {"f32": 4, "bf16": 2, "i8": 1, "i4": 5 / 8, "i2": 3 / 8}[fdt]

@@ -105,13 +105,15 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 constexpr int kD = 128;
 constexpr int kMaxSweeps = 30;
 constexpr float kJacobiTol = 1e-6f;
-// The solve ends after a sweep whose relative off-diagonals all stayed below
-// 3e-3: quadratic convergence leaves them far smaller, and the singular values
-// are then recomputed as Rayleigh quotients ||X v||, second order in the
-// eigenvector error.  On the planted workloads the worst singular value error
-// is 2.4% of its tolerance at 9.4 sweeps on average; 5e-3 saves 0.3 sweeps but
-// raises it to 14%, and 1e-2 exceeds it on one block.
-constexpr float kJacobiStopTol = 3e-3f;
+// The solve ends after the first half sweep that closes 127 consecutive rounds
+// whose relative off-diagonals all stayed below 2.5e-3: quadratic convergence
+// leaves them far smaller, and the singular values are then recomputed as
+// Rayleigh quotients ||X v||, second order in the eigenvector error.  Over 28
+// pools of the long-context workload the worst singular value error is 1.8% of
+// its tolerance at 9.2 sweeps on average, as with whole sweeps at 3e-3 (9.4
+// sweeps); half sweeps at 3e-3 raise it to 3.5%, whole sweeps at 5e-3 to 14%,
+// and 1e-2 exceeds it on one block.
+constexpr float kJacobiStopTol = 2.5e-3f;
 constexpr size_t kMat = sizeof(float) * kD * kD;  // one 128 x 128 fp32 matrix
 
 // Split the token dimension of the Gram when there are too few blocks to fill

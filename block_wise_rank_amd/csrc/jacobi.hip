@@ -54,9 +54,11 @@
 // from true values (diagonal entries are tracked unscaled, g = s_p s_q G_pq).
 //
 // A pair whose rotation is the identity has alpha = beta = 0, which moves its
-// rows unchanged.  The solve ends after a sweep whose every relative
-// off-diagonal |g| / sqrt|a b| was at most stop_tol, without the sweep that
-// would only confirm it: cyclic Jacobi converges quadratically once the
+// rows unchanged.  The solve ends at the first half of a sweep (after round
+// 63 or 126, where the scales are folded back anyway) that closes 127
+// consecutive rounds, every pair once, in which every relative off-diagonal
+// |g| / sqrt|a b| was at most stop_tol, without the rounds that would only
+// confirm it: cyclic Jacobi converges quadratically once the
 // off-diagonal part is small (Golub & Van Loan sec. 8.5.3), but for clustered
 // eigenvalues that says little about each eigenvector.  The accuracy of the
 // singular values rests instead on the pass that follows, which recomputes
@@ -215,7 +217,7 @@ __shared__ __align__(16) uint8_t g_lds[kLdsBytes];
 constexpr int kPrmOff = kGBytes;                                   // [2][64] (alpha, beta)
 constexpr int kXchOff = kPrmOff + kPrmBytes;                       // [2][2][7][64] rows crossing waves
 constexpr int kStabOff = kXchOff + kXchBytes;                      // [128] scales by position
-constexpr int kFlagOff = kStabOff + kStabBytes;                    // [2] "a sweep rotated" flags
+constexpr int kFlagOff = kStabOff + kStabBytes;                    // "this half sweep ends the solve"
 // Per pair, after the current round's rotation: its diagonal entries (true) and
 // the scales of its first and second row.  Only wave 7 touches it; a round reads
 // its neighbours' entries before any lane rewrites its own, so one buffer suffices.
@@ -249,14 +251,18 @@ struct LaneState {
 };
 
 struct Solve {
-    int k, sweep, used;     // round within the sweep, sweeps done, result
+    int k, sweep, used;     // round within the sweep, sweeps done, result (rounds)
+    int run;                // wave 7: consecutive rounds below stop_tol, the next round included
+    bool fin;               // wave 7: the next round ends the solve
     int wave, lane, tid, sel, blk, max_sweeps;
     float tol, stop_tol;
     float *vt_out;
     int32_t *sweeps_out;
 };
 
-// V^T rows out: after 127 rounds slot P again holds indices P and 127 - P.
+// V^T rows out, by position after the last round (after whole sweeps slot P
+// holds indices P and 127 - P again, otherwise a permutation of them: the
+// refine pass that follows sorts the vectors by their singular values).
 template <int NPH>
 __device__ __forceinline__ void write_rows(const LaneState &L, const Solve &C, int ln) {
     float2 *dstv = reinterpret_cast<float2 *>(C.vt_out + static_cast<int64_t>(C.blk) * kD * kD) + ln;
@@ -330,7 +336,9 @@ __device__ __forceinline__ bool jacobi_round(LaneState &L, Solve &C) {
     // registers the round needs
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) asm volatile("" : "+v"(L.pq[j]), "+v"(L.d[j][0]), "+v"(L.d[j][1]));
-    // rounds after which G and V^T are multiplied back by their scales
+    // rounds after which G and V^T are multiplied back by their scales, and
+    // after which the solve can end (wave 7 knows it one round ahead and
+    // flags it; the others read the flag after the round)
     const bool renorm = (k == 63) | (k == 126);
     const bool last_round = (k == 126);
 
@@ -392,8 +400,12 @@ __device__ __forceinline__ bool jacobi_round(LaneState &L, Solve &C) {
         L.d[3][0] = __float_as_uint(s1 * r.c);
         L.d[3][1] = __float_as_uint(s2 * r.c);
         L.rotp = r.rot;
-        if (r.rot && gt * gt > C.stop_tol * C.stop_tol * fabsf(an * bn))
-            lds_i(kFlagOff + 4 * ((C.sweep + (last_round ? 1 : 0)) & 1)) = 1;
+        // every pair once in the 127 rounds up to the next one below stop_tol,
+        // and the next round ends a half sweep: it ends the solve
+        const bool big = __any(r.rot && gt * gt > C.stop_tol * C.stop_tol * fabsf(an * bn));
+        C.run = big ? 0 : C.run + 1;
+        C.fin = C.run >= 127 && (k == 62 || k == 125);
+        if (C.fin && ln == 0) lds_i(kFlagOff) = 1;
         __builtin_amdgcn_s_setprio(0);
     } else {
         rotate_rows<PH>(L, pc, wave, ln, xb);
@@ -428,12 +440,13 @@ __device__ __forceinline__ bool jacobi_round(LaneState &L, Solve &C) {
                 }
         }
     }
-    if (k == 1 && C.tid == 0) lds_i(kFlagOff + 4 * ((C.sweep + 1) & 1)) = 0;
     __syncthreads();
 
     // ---- receive the rows that crossed a wave boundary
     if (wave < kNW - 1) L.F[f0] = lds_f2(xb + 8 * (wave * 64 + ln));
     if (wave > 0) L.S[s7] = lds_f2(xb + 8 * (((kNW - 1) + wave - 1) * 64 + ln));
+    // after a half sweep: does the solve end here (flag written by wave 7 last round)
+    const bool final = renorm && __builtin_amdgcn_readfirstlane(lds_i(kFlagOff)) != 0;
 
     // ---- multiply G and V^T back by the scales (gathered by position above)
     if (renorm) {
@@ -444,25 +457,26 @@ __device__ __forceinline__ bool jacobi_round(LaneState &L, Solve &C) {
             fr = make_float2(fr.x * sf, fr.y * sf);
             sr = make_float2(sr.x * ss, sr.y * ss);
         }
-        for (int e = C.tid; e < kBufWords; e += kThreads) {
-            const int r = e / kRoleWords, b = e - r * kRoleWords;
-            const int c = kTab.pq[b];
-            lds_f(nxt + 4 * e) *= lds_f(kStabOff + 4 * pos_of(c & 0xff, r >> 1)) *
-                                  lds_f(kStabOff + 4 * pos_of(c >> 8, r & 1));
+        if (!final) {
+            for (int e = C.tid; e < kBufWords; e += kThreads) {
+                const int r = e / kRoleWords, b = e - r * kRoleWords;
+                const int c = kTab.pq[b];
+                lds_f(nxt + 4 * e) *= lds_f(kStabOff + 4 * pos_of(c & 0xff, r >> 1)) *
+                                      lds_f(kStabOff + 4 * pos_of(c >> 8, r & 1));
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 
-    // ---- end of a sweep
+    // ---- the end of the solve: converged, or the last round of the last sweep
+    if (final || (last_round && C.sweep + 1 == C.max_sweeps)) {
+        if (final) C.used = C.sweep * 127 + k + 1;
+        write_rows<(PH + 1) & 7>(L, C, ln);
+        if (C.tid == 0 && C.sweeps_out) C.sweeps_out[C.blk] = C.used;
+        return true;
+    }
     if (last_round) {
-        const int rot = lds_i(kFlagOff + 4 * (C.sweep & 1));
         ++C.sweep;
-        if (!rot || C.sweep == C.max_sweeps) {
-            if (!rot) C.used = C.sweep;
-            write_rows<(PH + 1) & 7>(L, C, ln);
-            if (C.tid == 0 && C.sweeps_out) C.sweeps_out[C.blk] = C.used;
-            return true;
-        }
         C.k = 0;
     } else {
         C.k = k + 1;
@@ -489,10 +503,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
         const int code = kTab.pq[b];
         lds_f(4 * e) = gram(pos_of(code & 0xff, r >> 1), pos_of(code >> 8, r & 1));
     }
-    if (tid == 0) {
-        lds_i(kFlagOff) = 0;
-        lds_i(kFlagOff + 4) = 0;
-    }
+    if (tid == 0) lds_i(kFlagOff) = 0;
 
     LaneState L;
     const int Pn = lane;
@@ -521,6 +532,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
     // record stay in slot registers this wave does not use otherwise.
     L.gp = 0.f;
     L.rotp = false;
+    int run0 = 0;
     if (wave == kNW - 1) {
         const float a = gram(Pn, Pn), b = gram(127 - Pn, 127 - Pn);
         L.gp = gram(Pn, 127 - Pn);
@@ -531,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
         L.d[2][1] = __float_as_uint(r.nb);
         L.d[3][0] = L.d[3][1] = __float_as_uint(r.c);
         L.rotp = r.rot;
-        if (r.rot && L.gp * L.gp > stop_tol * stop_tol * fabsf(a * b)) lds_i(kFlagOff) = 1;
+        run0 = __any(r.rot && L.gp * L.gp > stop_tol * stop_tol * fabsf(a * b)) ? 0 : 1;
     }
     // opaque from here on: kept as whole registers, not repacked
 #pragma unroll
@@ -541,7 +553,8 @@ __global__ __launch_bounds__(kThreads, 4) void jacobi_kernel(const float *__rest
     L.has4 = wave < kNW - 1 && tid + kGenLanes * (kPerLane - 1) < kGeneric;  // slot 4 is partial
     __syncthreads();
 
-    Solve C{0, 0, -max_sweeps, wave, lane, tid, sel, blk, max_sweeps, tol, stop_tol, vt_out, sweeps_out};
+    Solve C{0, 0, -max_sweeps * 127, run0, false, wave, lane, tid, sel, blk, max_sweeps, tol, stop_tol, vt_out,
+            sweeps_out};
     // The rows kept for this path spill 24 registers (written before the first
     // sweep, read after the last, outside the round loop); the builds without
     // that spill schedule the round loop worse and solve 1.6% slower.

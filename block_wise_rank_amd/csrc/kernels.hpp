@@ -25,8 +25,10 @@ hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t r
 
 // Symmetric eigensolve of G_b (sum of the partials) by parallel-order cyclic
 // Jacobi in LDS.  Pairs with |g| <= tol sqrt|a b| are not rotated; the solve
-// ends after a sweep with no rotation above stop_tol.  vt[b][i][:] = eigenvector
-// i (unsorted); sweeps[b] = sweeps used (negative when max_sweeps was hit).
+// ends after the first half sweep that closes 127 rounds with no rotation above
+// stop_tol.  vt[b][i][:] = eigenvector
+// i (unsorted); sweeps[b] = rounds used, 127 per sweep (negative when
+// max_sweeps was hit).
 // sweeps may be null.
 hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt,
                          int32_t *sweeps, int max_sweeps, float tol, float stop_tol, int n_cus,
