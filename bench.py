@@ -76,7 +76,7 @@ def parse():
 
 
 # kernel -> the sources that define it (the traffic records are tied to their hash)
-KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "jacobi": ["jacobi.hip"],
+KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "tridiag": ["eigh.hip"], "ql": ["eigh.hip"],
                   "refine": ["refine.hip", "common.hpp"], "alloc": ["alloc.hip"],
                   "project": ["project.hip", "common.hpp"], "reconstruct": ["reconstruct.hip", "common.hpp"],
                   "decode": ["decode.hip", "common.hpp"], "decode_tail": ["decode.hip", "common.hpp"],
@@ -86,7 +86,7 @@ KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "jacobi": ["jacobi.hip"],
 
 def kernel_key(name):
     """libmilo kernel name (as rocprofv3 prints it) -> bench kernel key."""
-    for frag, key in (("gram_kernel", "gram"), ("gram_bf16_kernel", "gram"), ("jacobi_kernel", "jacobi"),
+    for frag, key in (("gram_kernel", "gram"), ("gram_bf16_kernel", "gram"), ("tridiag_kernel", "tridiag"), ("ql_kernel", "ql"),
                       ("refine_kernel", "refine"), ("alloc_kernel", "alloc"), ("project_kernel", "project"),
                       ("project_bf16_kernel", "project"), ("reconstruct_kernel", "reconstruct"),
                       ("reconstruct_bf16_kernel", "reconstruct"), ("decode_tables_kernel", "decode_tables"),
@@ -382,12 +382,18 @@ PROJECT_TERMS = {("bf16", "bf16"): 1, ("bf16", "i8"): 1, ("bf16", "f32"): 3, ("b
 GRAM_TERMS = {2: 1, 4: 6}
 
 
-def jacobi_executed_flops_per_sweep(d=128):
-    """Flops the eigensolve kernel issues per sweep: 127 rounds, each updating the
-    (d/2)(d/2 - 1)/2 off-diagonal 2 x 2 blocks of G from both sides (one FMA per
-    element and side) and every entry of the d x d eigenvector matrix (one FMA)."""
-    blocks = (d // 2) * (d // 2 - 1) // 2
-    return (d - 1) * 2 * (blocks * 4 * 2 + d * d)
+def tridiag_executed_flops(d=128):
+    """Flops the tridiagonalisation kernel issues per matrix: d - 2 steps, each
+    with every thread (one per row) taking a full-row dot product (d FMAs), its
+    w_j for every column (d FMAs) and the rank-2 update of its row (2d FMAs)."""
+    return (d - 2) * d * 4 * d * 2
+
+
+def ql_executed_flops(rotations, d=128):
+    """Flops the QR kernel issues per matrix: the rows of Q (d - 2 reflectors, a
+    full-row dot product and update per row: 2d FMAs) and every rotation applied
+    to every row (two products and two FMAs: 6 flops)."""
+    return (d - 2) * d * 2 * d * 2 + 6.0 * d * rotations
 
 
 def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=True, want_offload=True,
@@ -638,7 +644,7 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     # ---------------- algorithmic work per kernel launch ----------------
     ranks = {k: F[k].rank.to(torch.int64) for k in ("k", "v")}
     sw = torch.cat([sweeps["k"], sweeps["v"]]).to(torch.float64)
-    sweeps_mean = float(sw.abs().mean()) / 127  # sweeps_out counts rounds, 127 per sweep
+    rot_mean = float(sw.abs().mean())  # plane rotations of the QR iteration per block
     # bytes per factor element (4-bit: half a byte + an fp32 scale per 32 elements;
     # 2-bit: a quarter byte + the same scales)
     fe = {"f32": 4, "bf16": 2, "i8": 1, "i4": 5 / 8, "i2": 3 / 8}[fdt]
@@ -669,7 +675,10 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     work = {
         # kernel: (algorithmic amount for the whole step, unit, bound, peak)
         "gram": (n_blocks_step * T * d * xe, "GB/s", "hbm", PEAK_HBM_GBS),
-        "jacobi": (n_blocks_step * sweeps_mean * 9 * d * d * (d - 1), "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
+        # Householder tridiagonalisation: 4 d^3 / 3 flops; the QR kernel: Q formed
+        # from its reflectors (4 d^3 / 3) and 6 flops per rotation and row
+        "tridiag": (n_blocks_step * 4.0 * d ** 3 / 3, "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
+        "ql": (n_blocks_step * (4.0 * d ** 3 / 3 + 6.0 * d * rot_mean), "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
         # bf16 MFMA products executed: for bf16 X, V^T split in 2 bf16 terms (2
         # products); for fp32 X both in 3 terms, term pairs of order <= 2 kept (6)
         "refine": (n_blocks_step * 2.0 * T * d * d * REFINE_TERMS[xe], "TFLOP/s", "mfma",
@@ -722,8 +731,9 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
                           "counter_frac": round(cnt["mfma_flops_per_launch"] / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4),
                           "counter_mfma_busy_pct": cnt.get("mfma_busy_pct")})
             r["mfma"] = m
-        if name == "jacobi":
-            exe = n_blocks_step * sweeps_mean * jacobi_executed_flops_per_sweep(d) / (launches / steps)
+        if name in ("tridiag", "ql"):
+            per_blk = tridiag_executed_flops(d) if name == "tridiag" else ql_executed_flops(rot_mean, d)
+            exe = n_blocks_step * per_blk / (launches / steps)
             r["executed"] = {"flops_per_launch": exe, "TFLOPs": round(exe / avg_s / 1e12, 3),
                              "peak_TFLOPs": PEAK_FP32_VEC_NONPACKED_TFLOPS,
                              "frac": round(exe / avg_s / 1e12 / PEAK_FP32_VEC_NONPACKED_TFLOPS, 4)}
@@ -773,8 +783,8 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
             "decode_only_ms_per_step": None if dec_only_ms is None else round(dec_only_ms, 3),
             "decode_only_context_tokens_per_s": None if dec_only_ms is None else ctx_tokens / (dec_only_ms / 1e3),
             "decode_only_graph": dec_graph,
-            "jacobi_sweeps_mean": round(sweeps_mean, 3),
-            "blocks_at_sweep_cap": n_bad,
+            "eig_rotations_mean": round(rot_mean, 1),
+            "blocks_at_step_cap": n_bad,
             "kernels_ms_per_step": {n: round(v[1] / steps, 3) for n, v in prof.items()},
             "input_generation_s": round(gen_s, 1),
         },

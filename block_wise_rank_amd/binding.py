@@ -26,11 +26,11 @@ class MiloError(RuntimeError):
 
 class NotConvergedError(MiloError):
     """Raised by milo_compress_blocks(check_convergence=True) when the eigensolve
-    of some block reached the sweep cap (a negative entry of sweeps_out)."""
+    of some block reached its iteration cap (a negative entry of sweeps_out)."""
 
     def __init__(self, blocks):
         self.blocks = list(blocks)
-        super().__init__(C.MILO_OK, f"eigensolve reached its sweep cap on {len(self.blocks)} block(s): "
+        super().__init__(C.MILO_OK, f"eigensolve reached its iteration cap on {len(self.blocks)} block(s): "
                                     f"{self.blocks[:8]}")
 
 
@@ -242,8 +242,9 @@ def milo_compress_blocks(x: torch.Tensor, pool_ptr, budget, eps2: float, sigma_o
     """Compress blocks of ``x``: a contiguous [n_blocks, T, d] tensor, or any tensor
     addressed through ``row0``/``row_stride`` (with n_blocks and block_len given).
 
-    The call is asynchronous, so a block whose eigensolve reached the sweep cap
-    shows only as a negative entry of ``sweeps_out``.  With
+    The call is asynchronous, so a block whose eigensolve reached its iteration
+    cap shows only as a negative entry of ``sweeps_out`` (which counts the plane
+    rotations each block's eigensolve applied).  With
     ``check_convergence=True`` the binding supplies ``sweeps_out`` if none is
     given, waits for the stream and raises NotConvergedError naming such blocks."""
     milo_compress_blocks_ex(x, pool_ptr, budget, eps2, sigma_out, factors, objective_out, sweeps_out,

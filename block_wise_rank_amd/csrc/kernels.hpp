@@ -23,16 +23,17 @@ enum AllocPolicy : int { kAllocEntropy = 0, kAllocUniform = 1, kAllocRandom = 2 
 hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
                        int block_len, int n_blocks, int splits, float *gpart, hipStream_t st);
 
-// Symmetric eigensolve of G_b (sum of the partials) by parallel-order cyclic
-// Jacobi in LDS.  Pairs with |g| <= tol sqrt|a b| are not rotated; the solve
-// ends after the first half sweep that closes 127 rounds with no rotation above
-// stop_tol.  vt[b][i][:] = eigenvector
-// i (unsorted); sweeps[b] = rounds used, 127 per sweep (negative when
-// max_sweeps was hit).
-// sweeps may be null.
-hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt,
-                         int32_t *sweeps, int max_sweeps, float tol, float stop_tol, int n_cus,
-                         hipStream_t st);
+// Eigenvectors of the 128 x 128 Grams in two launches.  launch_tridiag reduces
+// each Gram (the sum of its `splits` partials in gpart) to tridiagonal form by
+// Householder reflections, keeping the reflectors in the block's first partial
+// and the tridiagonal matrix in vt[b]; launch_ql then runs implicit shifted QR
+// steps on it and writes the eigenvectors as the rows of vt[b] (in no
+// particular order, unit length to working accuracy).  rotations[b] = the plane
+// rotations applied, negated when the cap of max_steps QR steps stopped the
+// iteration.
+hipError_t launch_tridiag(float *gpart, int splits, int n_blocks, float *vt, hipStream_t st);
+hipError_t launch_ql(const float *gpart, int splits, int n_blocks, float *vt, int32_t *rotations, int max_steps,
+                     hipStream_t st);
 
 // sigma_i = ||X_b v_i|| in fp32-accurate arithmetic, sorted descending into
 // sigma[b][0..128); perm[b][k] = the eigenvector (row of vt[b]) of sorted rank k

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MILO_ABI_VERSION 3
+#define MILO_ABI_VERSION 4
 
 typedef enum milo_status {
     MILO_OK = 0,
@@ -147,11 +147,13 @@ typedef struct milo_factors {
  *              handed out: the R_p largest singular values of the pool in the
  *              order (sigma desc, block asc, index asc), which is what the
  *              greedy on the gains selects.
- *  sweeps_out  device [n_blocks] int32 (may be NULL): Jacobi rounds used per
- *              block (127 rounds make a sweep; the solve ends after a half
- *              sweep); -3810 if the eigensolve of that block reached its
- *              cap of 30 sweeps (its results are then those of the last sweep).
- *              (ABI version 3; version 2 counted whole sweeps.)  The
+ *  sweeps_out  device [n_blocks] int32 (may be NULL): the work of each block's
+ *              eigensolve, as the number of plane rotations its QR iteration
+ *              applied (0 for a block whose Gram is diagonal once reduced to
+ *              tridiagonal form); negated if the iteration reached its cap of
+ *              30 QR steps per eigenvalue (the results are then those of the
+ *              last step).  (ABI version 4; versions 2 and 3 counted the sweeps
+ *              and rounds of a Jacobi eigensolve.)  The
  *              call returns before its kernels run, so it cannot report this in
  *              its status: a caller that must know passes sweeps_out and checks
  *              it once the stream has reached the call.

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_versions_and_strings(L):
-    assert L.milo_abi_version() == 3
+    assert L.milo_abi_version() == 4
     assert L.milo_status_string(0) == b"MILO_OK"
     assert L.milo_status_string(3) == b"MILO_E_WORKSPACE"
 
