@@ -76,7 +76,8 @@ def parse():
 
 
 # kernel -> the sources that define it (the traffic records are tied to their hash)
-KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "tridiag": ["eigh.hip"], "ql": ["eigh.hip"],
+KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "tridiag": ["eigh.hip"], "qr_chain": ["eigh.hip"],
+                  "qr_apply": ["eigh.hip"],
                   "refine": ["refine.hip", "common.hpp"], "alloc": ["alloc.hip"],
                   "project": ["project.hip", "common.hpp"], "reconstruct": ["reconstruct.hip", "common.hpp"],
                   "decode": ["decode.hip", "common.hpp"], "decode_tail": ["decode.hip", "common.hpp"],
@@ -86,7 +87,8 @@ KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "tridiag": ["eigh.hip"], "
 
 def kernel_key(name):
     """libmilo kernel name (as rocprofv3 prints it) -> bench kernel key."""
-    for frag, key in (("gram_kernel", "gram"), ("gram_bf16_kernel", "gram"), ("tridiag_kernel", "tridiag"), ("ql_kernel", "ql"),
+    for frag, key in (("gram_kernel", "gram"), ("gram_bf16_kernel", "gram"), ("tridiag_kernel", "tridiag"), ("qr_chain_kernel", "qr_chain"),
+                      ("qr_apply_kernel", "qr_apply"),
                       ("refine_kernel", "refine"), ("alloc_kernel", "alloc"), ("project_kernel", "project"),
                       ("project_bf16_kernel", "project"), ("reconstruct_kernel", "reconstruct"),
                       ("reconstruct_bf16_kernel", "reconstruct"), ("decode_tables_kernel", "decode_tables"),
@@ -383,17 +385,29 @@ GRAM_TERMS = {2: 1, 4: 6}
 
 
 def tridiag_executed_flops(d=128):
-    """Flops the tridiagonalisation kernel issues per matrix: d - 2 steps, each
-    with every thread (one per row) taking a full-row dot product (d FMAs), its
-    w_j for every column (d FMAs) and the rank-2 update of its row (2d FMAs)."""
-    return (d - 2) * d * 4 * d * 2
+    """Flops the tridiagonalisation kernel issues per matrix.  Step k (of d - 2)
+    runs on the waves that hold a row > k; each of their threads (one per row)
+    takes the dot product of its row with v over the groups of eight columns not
+    wholly <= k (2 flops a column) and updates its row over the groups of four
+    columns not wholly <= k (two FMAs an entry)."""
+    total = 0
+    for k in range(d - 2):
+        threads = sum(64 for w in range(d // 64) if 64 * w + 63 > k)
+        dot = d - 8 * ((k + 1) // 8)
+        upd = d - 4 * ((k + 1) // 4)
+        total += threads * (2 * dot + 4 * upd)
+    return total
 
 
-def ql_executed_flops(rotations, d=128):
-    """Flops the QR kernel issues per matrix: the rows of Q (d - 2 reflectors, a
-    full-row dot product and update per row: 2d FMAs) and every rotation applied
-    to every row (two products and two FMAs: 6 flops)."""
-    return (d - 2) * d * 2 * d * 2 + 6.0 * d * rotations
+def qr_apply_executed_flops(rotations, d=128):
+    """Flops the rotation kernel issues per matrix: the rows of Q (d - 2
+    reflectors, a dot product and an update per row over the entries the
+    reflector touches, in groups of eight: about d^3 / 2 FMAs in all) and every
+    rotation applied to every row (two products and two FMAs: 6 flops; the
+    identity rotations that fill a step's first and last groups of eight are not
+    counted)."""
+    touched = sum(d - (k + 1) // 8 * 8 for k in range(d - 2))
+    return 2 * d * touched * 2 + 6.0 * d * rotations
 
 
 def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=True, want_offload=True,
@@ -675,10 +689,13 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     work = {
         # kernel: (algorithmic amount for the whole step, unit, bound, peak)
         "gram": (n_blocks_step * T * d * xe, "GB/s", "hbm", PEAK_HBM_GBS),
-        # Householder tridiagonalisation: 4 d^3 / 3 flops; the QR kernel: Q formed
-        # from its reflectors (4 d^3 / 3) and 6 flops per rotation and row
+        # Householder tridiagonalisation: 4 d^3 / 3 flops; the rotation kernel: Q
+        # formed from its reflectors (4 d^3 / 3) and 6 flops per rotation and row;
+        # the QR chain itself: about 20 flops per rotation
         "tridiag": (n_blocks_step * 4.0 * d ** 3 / 3, "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
-        "ql": (n_blocks_step * (4.0 * d ** 3 / 3 + 6.0 * d * rot_mean), "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
+        "qr_chain": (n_blocks_step * 20.0 * rot_mean, "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
+        "qr_apply": (n_blocks_step * (4.0 * d ** 3 / 3 + 6.0 * d * rot_mean), "TFLOP/s", "alu",
+                     PEAK_FP32_VEC_TFLOPS),
         # bf16 MFMA products executed: for bf16 X, V^T split in 2 bf16 terms (2
         # products); for fp32 X both in 3 terms, term pairs of order <= 2 kept (6)
         "refine": (n_blocks_step * 2.0 * T * d * d * REFINE_TERMS[xe], "TFLOP/s", "mfma",
@@ -731,8 +748,8 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
                           "counter_frac": round(cnt["mfma_flops_per_launch"] / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4),
                           "counter_mfma_busy_pct": cnt.get("mfma_busy_pct")})
             r["mfma"] = m
-        if name in ("tridiag", "ql"):
-            per_blk = tridiag_executed_flops(d) if name == "tridiag" else ql_executed_flops(rot_mean, d)
+        if name in ("tridiag", "qr_apply"):
+            per_blk = tridiag_executed_flops(d) if name == "tridiag" else qr_apply_executed_flops(rot_mean, d)
             exe = n_blocks_step * per_blk / (launches / steps)
             r["executed"] = {"flops_per_launch": exe, "TFLOPs": round(exe / avg_s / 1e12, 3),
                              "peak_TFLOPs": PEAK_FP32_VEC_NONPACKED_TFLOPS,

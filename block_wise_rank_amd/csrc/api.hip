@@ -103,9 +103,6 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kD = 128;
-// QR steps allowed per matrix: 30 per eigenvalue, the classical cap of the
-// implicit QL/QR iteration (about 1.3 per eigenvalue are taken on Gram matrices).
-constexpr int kMaxSteps = 30 * kD;
 constexpr size_t kMat = sizeof(float) * kD * kD;  // one 128 x 128 fp32 matrix
 
 // Split the token dimension of the Gram when there are too few blocks to fill
@@ -123,10 +120,13 @@ size_t tables_bytes(int n_pools) {
 
 // Per block: the sorted order of its eigenvectors and their scales (refine -> project).
 constexpr size_t kOrder = sizeof(int32_t) * kD + sizeof(float) * kD;
+// Per block, besides its Gram partials and eigenvectors: the QR iteration's
+// step and rotation counts and its recorded rotations (milo::kStreamBytes).
+constexpr size_t kEigExtra = kOrder + 2 * sizeof(int32_t) + milo::kStreamBytes;
 
 size_t chunk_bytes(int n_blocks, int block_len) {
     const int s = gram_splits(n_blocks, block_len);
-    return static_cast<size_t>(n_blocks) * ((s + 1) * kMat + kOrder);
+    return static_cast<size_t>(n_blocks) * ((s + 1) * kMat + kEigExtra);
 }
 
 milo_status check_pools(const int32_t *pool_ptr, int32_t n_pools, const int64_t *budget,
@@ -276,8 +276,9 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
     const size_t full = tab + chunk_bytes(in->n_blocks, in->block_len);
     int max_pool = 0;
     for (int p = 0; p < n_pools; ++p) max_pool = std::max(max_pool, pool_ptr[p + 1] - pool_ptr[p]);
-    // a chunk needs at least one Gram partial, the eigenvectors and their order per block
-    const size_t minimum = tab + static_cast<size_t>(max_pool) * (2 * kMat + kOrder);
+    // a chunk needs at least one Gram partial, the eigenvectors, their order and
+    // the QR iteration's record per block
+    const size_t minimum = tab + static_cast<size_t>(max_pool) * (2 * kMat + kEigExtra);
     if (!workspace || *workspace_bytes < minimum) {
         *workspace_bytes = full;
         return fail(MILO_E_WORKSPACE, "workspace of %zu bytes needed (minimum %zu)", full, minimum);
@@ -322,12 +323,12 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
         // grow the chunk while its workspace fits
         int p1 = p0 + 1;
         while (p1 < n_pools &&
-               static_cast<size_t>(pool_ptr[p1 + 1] - pool_ptr[p0]) * (2 * kMat + kOrder) <= chunk_cap)
+               static_cast<size_t>(pool_ptr[p1 + 1] - pool_ptr[p0]) * (2 * kMat + kEigExtra) <= chunk_cap)
             ++p1;
         const int b0 = pool_ptr[p0], nb = pool_ptr[p1] - b0;
         if (nb > 0) {
             // Gram token splits: enough workgroups to fill the chip, within the workspace.
-            const int fit = static_cast<int>((chunk_cap - static_cast<size_t>(nb) * kOrder) /
+            const int fit = static_cast<int>((chunk_cap - static_cast<size_t>(nb) * kEigExtra) /
                                              (static_cast<size_t>(nb) * kMat)) - 1;
             int splits = gram_splits(nb, T);
             while (splits > 1 && splits > fit) splits /= 2;  // powers of two keep T / splits % 64 == 0
@@ -335,6 +336,8 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
             float *vt = reinterpret_cast<float *>(chunk_ws + static_cast<size_t>(nb) * splits * kMat);
             int32_t *vperm = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(vt) + static_cast<size_t>(nb) * kMat);
             float *vscale = reinterpret_cast<float *>(vperm + static_cast<size_t>(nb) * kD);
+            int32_t *qr_counts = reinterpret_cast<int32_t *>(vscale + static_cast<size_t>(nb) * kD);
+            uint8_t *qr_stream = reinterpret_cast<uint8_t *>(qr_counts + 2 * static_cast<size_t>(nb));
             // block b of the chunk: row0 points into the caller's table, else blocks back to back
             const int64_t *row0 = in->row0 ? in->row0 + b0 : nullptr;
             const void *xc = in->row0 ? static_cast<const void *>(xb)
@@ -344,10 +347,15 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
                 return hip_fail(e, "gram launch");
             if ((e = timed("tridiag", s, [&] { return milo::launch_tridiag(gpart, splits, nb, vt, s); })) != hipSuccess)
                 return hip_fail(e, "tridiagonalisation launch");
-            if ((e = timed("ql", s, [&] {
-                     return milo::launch_ql(gpart, splits, nb, vt, sweeps_out ? sweeps_out + b0 : nullptr, kMaxSteps, s);
+            if ((e = timed("qr_chain", s, [&] {
+                     return milo::launch_qr_chain(vt, nb, qr_stream, qr_counts, sweeps_out ? sweeps_out + b0 : nullptr,
+                                                  s);
                  })) != hipSuccess)
                 return hip_fail(e, "QR iteration launch");
+            if ((e = timed("qr_apply", s, [&] {
+                     return milo::launch_qr_apply(gpart, splits, nb, qr_stream, qr_counts, vt, s);
+                 })) != hipSuccess)
+                return hip_fail(e, "QR rotation launch");
             if ((e = timed("refine", s, [&] { return milo::launch_refine(xc, x_type, row0, in->row_stride, T, nb, vt, sig, vperm, vscale, s); })) != hipSuccess)
                 return hip_fail(e, "refine launch");
             if ((e = timed("alloc", s, [&] {

@@ -11,7 +11,7 @@
 //    from column k below the diagonal (held, by symmetry, as entry k of every
 //    row), p = beta A v, w = p - (beta/2)(p^T v) v and A <- A - v w^T - w v^T:
 //    two barriers per step, the vectors exchanged through small double-buffered
-//    LDS arrays.  The reflectors go to the Gram's own workspace area (no longer
+//    LDS arrays; rows and columns already reduced are skipped.  The reflectors go to the Gram's own workspace area (no longer
 //    needed once summed), the diagonal and off-diagonal of T to the first two
 //    rows of the eigenvector area.
 //  * ql_kernel: thread r forms row r of Q (e_r^T H_0 H_1 ... H_125, reflector
@@ -43,6 +43,8 @@ constexpr int kThreads = kD;     // one thread per row, two waves
 constexpr int kRefl = kD - 2;    // reflectors H_0 .. H_125
 constexpr int kBetaRow = kD - 2; // row of the reflector area holding beta_k
 constexpr float kDeflTol = 1.1920929e-7f;  // 2^-23
+constexpr int kRing = 12, kAhead = 10;      // rotation staging of the apply kernel (steps)
+constexpr int kSetupEvery = 8;              // passes of the chain kernel between step starts
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -58,7 +60,8 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __global__ __launch_bounds__(kThreads) void tridiag_kernel(float *__restrict__ gpart, int splits,
                                                           float *__restrict__ vt) {
-    const int blk = blockIdx.x, r = threadIdx.x, lane = r & 63, wave = r >> 6;
+    const int blk = blockIdx.x, r = threadIdx.x, lane = r & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(r >> 6);
     float *src = gpart + static_cast<int64_t>(blk) * splits * kD * kD;
     float *tri = vt + static_cast<int64_t>(blk) * kD * kD;  // row 0: d, row 1: e
     __shared__ float4 xb[2][kD / 4], vb[2][kD / 4], pb[2][kD / 4];
@@ -127,14 +130,25 @@ __global__ __launch_bounds__(kThreads) void tridiag_kernel(float *__restrict__ g
             beta = 1.f / (nx2 + fabsf(x1) * nx);  // 2 / v^T v
         }
         const float vr = xk - (r == k + 1 ? alpha : 0.f);
+        // Rows and columns 0..k are done: v and p vanish there, so a wave whose
+        // rows are all <= k skips the products, and so does every group of
+        // eight columns <= k (uniform branches).
+        const bool live = 64 * wave + 63 > k;
         float dot = 0.f;
+        if (live) {
 #pragma unroll
-        for (int j = 0; j < kD / 4; ++j) {
-            const float4 x = xb[par][j];
-            dot = fmaf(a[4 * j], x.x, dot);
-            dot = fmaf(a[4 * j + 1], x.y, dot);
-            dot = fmaf(a[4 * j + 2], x.z, dot);
-            dot = fmaf(a[4 * j + 3], x.w, dot);
+            for (int j = 0; j < kD / 4; j += 2) {
+                if (4 * j + 7 <= k) continue;
+                const float4 x = xb[par][j], x2 = xb[par][j + 1];
+                dot = fmaf(a[4 * j], x.x, dot);
+                dot = fmaf(a[4 * j + 1], x.y, dot);
+                dot = fmaf(a[4 * j + 2], x.z, dot);
+                dot = fmaf(a[4 * j + 3], x.w, dot);
+                dot = fmaf(a[4 * j + 4], x2.x, dot);
+                dot = fmaf(a[4 * j + 5], x2.y, dot);
+                dot = fmaf(a[4 * j + 6], x2.z, dot);
+                dot = fmaf(a[4 * j + 7], x2.w, dot);
+            }
         }
         dot = fmaf(-alpha, ak1, dot);
         const float pr = r > k ? beta * dot : 0.f;
@@ -148,16 +162,17 @@ __global__ __launch_bounds__(kThreads) void tridiag_kernel(float *__restrict__ g
             tri[kD + k] = alpha;
         }
         __syncthreads();
+        // A - v w^T - w v^T with w = p - K v is A - v p^T - (p - 2 K v) v^T
         const float K = 0.5f * beta * (red[par][1][0] + red[par][1][1]);
-        const float wr = fmaf(-K, vr, pr);
+        const float ur = fmaf(-2.f * K, vr, pr);
+        if (live) {
 #pragma unroll
-        for (int j = 0; j < kD / 4; ++j) {
-            const float4 p = pb[par][j], v = vb[par][j];
-            const float pj[4] = {p.x, p.y, p.z, p.w}, vj[4] = {v.x, v.y, v.z, v.w};
+            for (int j = 0; j < kD / 4; ++j) {
+                if (4 * j + 3 <= k) continue;
+                const float4 p = pb[par][j], v = vb[par][j];
+                const float pj[4] = {p.x, p.y, p.z, p.w}, vj[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float wj = fmaf(-K, vj[i], pj[i]);
-                a[4 * j + i] = fmaf(-vr, wj, fmaf(-wr, vj[i], a[4 * j + i]));
+                for (int i = 0; i < 4; ++i) a[4 * j + i] = fmaf(-vr, pj[i], fmaf(-ur, vj[i], a[4 * j + i]));
             }
         }
     }
@@ -168,123 +183,340 @@ __global__ __launch_bounds__(kThreads) void tridiag_kernel(float *__restrict__ g
     }
 }
 
-__global__ __launch_bounds__(kThreads) void ql_kernel(const float *__restrict__ gpart, int splits,
-                                                     float *__restrict__ vt, int32_t *__restrict__ rot_out,
-                                                     int max_steps) {
-    const int blk = blockIdx.x, r = threadIdx.x, lane = r & 63, wave = r >> 6;
-    const float *hv = gpart + static_cast<int64_t>(blk) * splits * kD * kD;
-    float *out = vt + static_cast<int64_t>(blk) * kD * kD;
-    // per wave: D[0..127] = diagonal, E[j + 1] = T[j][j+1] (E[0], E[128], E[129] pads)
-    __shared__ float sd[2][kD + 4], se[2][kD + 4];
-    float *D = sd[wave], *E = se[wave];
-    D[lane] = out[lane];
-    D[lane + 64] = out[lane + 64];
-    E[lane + 1] = out[kD + lane];
-    E[lane + 65] = lane + 64 < kD - 1 ? out[kD + lane + 64] : 0.f;
-    if (lane == 0) {
-        E[0] = 0.f;
-        E[kD + 1] = 0.f;
-    }
-    __syncthreads();  // every read of T is done before the rows of V^T overwrite it
+__device__ __forceinline__ bool negligible(float e, float d0, float d1) {
+    return fabsf(e) <= kDeflTol * (fabsf(d0) + fabsf(d1));
+}
 
-    // row r of Q = e_r^T H_0 H_1 ... H_125
-    float y[kD];
+// Highest bit j < lim of a 128-bit mask (four words) that is set, or -1.
+__device__ __forceinline__ int highest_below(const uint32_t (&w)[4], int lim) {
+    int j = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int n = lim - 32 * i;  // bits of word i below lim
+        const uint32_t keep = n >= 32 ? ~0u : (n > 0 ? (1u << n) - 1u : 0u);
+        const uint32_t x = w[i] & keep;
+        j = x ? 32 * i + 31 - __builtin_clz(x) : j;
+    }
+    return j;
+}
+
+__device__ __forceinline__ void set_bit(uint32_t (&w)[4], int j, bool on) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t bit = (j >> 5) == i ? 1u << (j & 31) : 0u;
+        w[i] = on ? (w[i] | bit) : (w[i] & ~bit);
+    }
+}
+
+// The QR iteration of 64 tridiagonal matrices per wave, one per lane: every
+// pass of the loop takes one rotation of each lane's current step, or starts
+// its next step.  T lives in LDS as [row][lane] (each lane its own column, so
+// no bank conflicts whatever row each lane is at); the negligible off-diagonal
+// entries are kept as a per-lane 128-bit mask, updated as the chase writes
+// them, from which each step's block [l, m] follows: m - 1 is the last entry
+// above the converged bottom that is not negligible, l is one past the last
+// negligible entry above it.  Each step's rotations (c, s) and its header go to
+// the block's stream area in order.
+__global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ vt, int n_blocks,
+                                                      uint8_t *__restrict__ stream, int32_t *__restrict__ counts,
+                                                      int32_t *__restrict__ rot_out) {
+    const int lane = threadIdx.x, b = blockIdx.x * 64 + lane;
+    const bool act = b < n_blocks;
+    __shared__ float Ds[kD + 2][64], Es[kD + 2][64];  // d_j, e_j = T[j][j+1] (rows 127.. pads)
+    {
+        const float4 *tri = reinterpret_cast<const float4 *>(vt + static_cast<int64_t>(act ? b : 0) * kD * kD);
+#pragma unroll 4
+        for (int q = 0; q < kD / 4; ++q) {
+            const float4 dv = act ? tri[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 ev = act ? tri[kD / 4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            Ds[4 * q][lane] = dv.x; Ds[4 * q + 1][lane] = dv.y; Ds[4 * q + 2][lane] = dv.z; Ds[4 * q + 3][lane] = dv.w;
+            Es[4 * q][lane] = ev.x; Es[4 * q + 1][lane] = ev.y; Es[4 * q + 2][lane] = ev.z;
+            Es[4 * q + 3][lane] = 4 * q + 3 < kD - 1 ? ev.w : 0.f;
+        }
+        Ds[kD][lane] = Ds[kD + 1][lane] = 0.f;
+        Es[kD][lane] = Es[kD + 1][lane] = 0.f;
+    }
+    uint32_t nm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kD - 1; ++j)
+        if (negligible(Es[j][lane], Ds[j][lane], Ds[j + 1][lane])) nm[j >> 5] |= 1u << (j & 31);
+
+    uint8_t *mine = stream + static_cast<int64_t>(act ? b : 0) * kStreamBytes;
+    float2 *rot = reinterpret_cast<float2 *>(mine) + kRotPad;
+    uint32_t *hdr = reinterpret_cast<uint32_t *>(mine + sizeof(float) * 2 * (kRotCap + 2 * kRotPad));
+    // st: 0 ready for its next step, 1 in a chase, 2 done, 3 chase ended (its
+    // closing writes pending).  Steps end and start only in every kSetupEvery-th
+    // pass, so that their code (far longer than a rotation's) runs in few
+    // passes; a lane whose chase has ended waits for that pass.
+    int m = kD - 1, l = 0, K = 0, steps = 0, rots = 0, st = act ? 0 : 2;
+    bool capped = false;
+    float g = 0.f, p = 0.f, sn = 1.f, cn = 1.f, dk = 0.f, dk1 = 0.f, ek = 0.f, dprev = 0.f;
+    for (int pass = 0; __any(st != 2); ++pass) {
+        if (pass % kSetupEvery == 0) {
+            if (st == 3) {
+                const float dm = dk - p;  // d_m
+                Ds[m][lane] = dm;
+                Es[m - 1][lane] = g;
+                set_bit(nm, m - 1, negligible(g, dprev, dm));
+                if (l > 0) set_bit(nm, l - 1, negligible(Es[l - 1][lane], Ds[l - 1][lane], Ds[l][lane]));
+                if (m < kD - 1) set_bit(nm, m, negligible(Es[m][lane], dm, Ds[m + 1][lane]));
+                st = 0;
+            }
+            if (st == 0) {
+                uint32_t nc[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) nc[i] = ~nm[i];
+                const int jb = highest_below(nc, m);  // last non-negligible e_j, j < m
+                if (jb < 0) {
+                    st = 2;
+                } else {
+                    const int mm = jb + 1, ll = highest_below(nm, mm - 1) + 1;
+                    if (steps == kStepCap || rots + (mm - ll) > kRotCap) {
+                        capped = true;
+                        st = 2;
+                    } else {
+                        m = mm;
+                        l = ll;
+                        hdr[steps] = static_cast<uint32_t>(l) | static_cast<uint32_t>(m) << 16;
+                        ++steps;
+                        // Wilkinson shift from the trailing 2 x 2, carried as g = d_l - mu
+                        // (the shift only steers convergence: rcp and sqrt at their
+                        // hardware accuracy)
+                        const float em = Es[m - 1][lane], dm = Ds[m][lane];
+                        const float g0 = (Ds[m - 1][lane] - dm) * __builtin_amdgcn_rcpf(2.f * em);
+                        const float h = __builtin_amdgcn_sqrtf(fmaf(g0, g0, 1.f));
+                        dk = Ds[l][lane];
+                        dk1 = Ds[l + 1][lane];
+                        ek = Es[l][lane];
+                        g = dk - dm + em * __builtin_amdgcn_rcpf(g0 + (g0 >= 0.f ? h : -h));
+                        p = 0.f;
+                        sn = cn = 1.f;
+                        K = l;
+                        st = 1;
+                    }
+                }
+            }
+        }
+        if (st == 1) {
+            // rotation K (rows/columns K, K + 1) zeroes the bulge f = s e_K against
+            // g; p carries the change of the diagonal entry the next one starts
+            // from.  With q = f^2 + g^2, c = g / sqrt q, s = f / sqrt q and
+            // w = (d_{K+1} - d_K + p) f + 2 g b (b = c_prev e_K):
+            // p' = f w / q, g' = g w / q - b.
+            const float dn = Ds[K + 2][lane], en = Es[K + 1][lane];
+            const float f = sn * ek, bb = cn * ek;
+            const float q = fmaf(f, f, g * g);
+            const bool ok = q > 0.f;  // f = g = 0: the identity (c = 1, s = 0)
+            const float g2 = dk - p;
+            const float w = fmaf(dk1 - g2, f, 2.f * (g * bb));
+            const float rs = __builtin_amdgcn_rsqf(ok ? q : 1.f);
+            const float rs2 = rs * rs;
+            p = (f * w) * rs2;
+            const float dK = g2 + p;
+            const float gn = fmaf(g * w, rs2, -bb);
+            sn = f * rs;
+            cn = ok ? g * rs : 1.f;
+            g = ok ? gn : bb;
+            if (K > l) {
+                const float r = q * rs;  // e_{K-1}
+                Es[K - 1][lane] = r;
+                set_bit(nm, K - 1, negligible(r, dprev, dK));
+            }
+            Ds[K][lane] = dK;
+            dprev = dK;
+            rot[rots] = make_float2(cn, sn);
+            ++rots;
+            dk = dk1;
+            dk1 = dn;
+            ek = en;
+            ++K;
+            if (K == m) st = 3;
+        }
+    }
+    if (act) {
+        counts[2 * b] = steps;
+        counts[2 * b + 1] = rots;
+        if (rot_out) rot_out[b] = capped ? -rots : rots;
+    }
+}
+
+// Row r of Q = e_r^T H_0 H_1 ... H_125, the reflectors staged through LDS eight
+// at a time (double-buffered, the next group's loads in flight during the
+// current group); v_k vanishes in entries 0..k, so each reflector skips the
+// groups of eight entries it does not touch.
+__device__ __forceinline__ void form_q_row(float (&y)[kD], const float *__restrict__ hv, int r,
+                                           float4 (*hb)[8][kD / 4], float *beta) {
 #pragma unroll
     for (int j = 0; j < kD; ++j) y[j] = j == r ? 1.f : 0.f;
-    for (int k = 0; k < kRefl; ++k) {
-        const float *v = hv + k * kD;
-        float t0 = 0.f, t1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < kD; j += 2) {
-            t0 = fmaf(y[j], v[j], t0);
-            t1 = fmaf(y[j + 1], v[j + 1], t1);
+    if (r < kRefl) beta[r] = hv[kBetaRow * kD + r];
+    // thread r stages entries 8 (r & 15) .. + 7 of reflector 8 c + (r >> 4)
+    const int rr = r >> 4, cc = 2 * (r & 15);
+    const float4 *src = reinterpret_cast<const float4 *>(hv);
+    float4 a0 = src[rr * (kD / 4) + cc], a1 = src[rr * (kD / 4) + cc + 1];
+    for (int c = 0; c < kD / 8; ++c) {
+        hb[c & 1][rr][cc] = a0;
+        hb[c & 1][rr][cc + 1] = a1;
+        __syncthreads();
+        if (c + 1 < kD / 8) {
+            const int k = 8 * (c + 1) + rr;
+            const bool in = k < kRefl;
+            a0 = in ? src[k * (kD / 4) + cc] : make_float4(0.f, 0.f, 0.f, 0.f);
+            a1 = in ? src[k * (kD / 4) + cc + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        const float t = (t0 + t1) * hv[kBetaRow * kD + k];
+#pragma unroll 1
+        for (int i = 0; i < 8; ++i) {
+            const int k = 8 * c + i;
+            if (k >= kRefl) break;
+            const float4 *v = hb[c & 1][i];
+            float t0 = 0.f, t1 = 0.f;
 #pragma unroll
-        for (int j = 0; j < kD; ++j) y[j] = fmaf(-t, v[j], y[j]);
+            for (int j = 0; j < kD; j += 8) {
+                if (j + 7 <= k) continue;
+                const float4 u0 = v[j / 4], u1 = v[j / 4 + 1];
+                t0 = fmaf(y[j], u0.x, t0);
+                t1 = fmaf(y[j + 1], u0.y, t1);
+                t0 = fmaf(y[j + 2], u0.z, t0);
+                t1 = fmaf(y[j + 3], u0.w, t1);
+                t0 = fmaf(y[j + 4], u1.x, t0);
+                t1 = fmaf(y[j + 5], u1.y, t1);
+                t0 = fmaf(y[j + 6], u1.z, t0);
+                t1 = fmaf(y[j + 7], u1.w, t1);
+            }
+            const float t = (t0 + t1) * beta[k];
+#pragma unroll
+            for (int j = 0; j < kD; j += 8) {
+                if (j + 7 <= k) continue;
+                const float4 u0 = v[j / 4], u1 = v[j / 4 + 1];
+                y[j] = fmaf(-t, u0.x, y[j]);
+                y[j + 1] = fmaf(-t, u0.y, y[j + 1]);
+                y[j + 2] = fmaf(-t, u0.z, y[j + 2]);
+                y[j + 3] = fmaf(-t, u0.w, y[j + 3]);
+                y[j + 4] = fmaf(-t, u1.x, y[j + 4]);
+                y[j + 5] = fmaf(-t, u1.y, y[j + 5]);
+                y[j + 6] = fmaf(-t, u1.z, y[j + 6]);
+                y[j + 7] = fmaf(-t, u1.w, y[j + 7]);
+            }
+        }
     }
+}
 
-    int m = kD - 1, steps = 0, rotations = 0;
-    bool capped = false;
-    for (;;) {
-        // negligible off-diagonal entries: bit j of (lo, hi) for e_j, j = lane, lane + 64
-        const auto negl = [&](int j) {
-            return fabsf(E[j + 1]) <= kDeflTol * (fabsf(D[j]) + fabsf(D[j + 1]));
-        };
-        const uint64_t lo = __ballot(negl(lane));
-        const uint64_t hi = __ballot(lane + 64 >= kD - 1 || negl(lane + 64));
-        // bottom of the unreduced block: the last non-negligible e_j with j < m
-        int jb = -1;
-        {
-            const uint64_t hm = m > 64 ? (~hi & ((m - 64 >= 64) ? ~0ull : ((1ull << (m - 64)) - 1))) : 0ull;
-            if (hm) {
-                jb = 64 + 63 - __builtin_clzll(hm);
-            } else {
-                const uint64_t lm = ~lo & (m >= 64 ? ~0ull : ((1ull << m) - 1));
-                if (lm) jb = 63 - __builtin_clzll(lm);
-            }
+// The rotation of rows/columns K, K + 1 applied to a row of V (columns of V
+// are eigenvectors; the rotation mixes two of them).
+__device__ __forceinline__ void rotate_pair(float &y0, float &y1, float c, float s) {
+    const float a = y0, b = y1;
+    y0 = fmaf(s, b, c * a);
+    y1 = fmaf(c, b, -s * a);
+}
+
+// Thread r forms row r of Q and applies every recorded rotation to it (V = Q Z,
+// Z the eigenvectors of T), then writes entry r of every eigenvector: the rows
+// of V^T, coalesced.  Each step's rotations are staged into LDS by the
+// workgroup's first wave (LDS DMA, kAhead steps ahead of their use), then
+// applied by every thread to its row with the rotation index unrolled, so that
+// each row entry stays at a fixed register.
+__global__ __launch_bounds__(kThreads) void qr_apply_kernel(const float *__restrict__ gpart, int splits,
+                                                           const uint8_t *__restrict__ stream,
+                                                           const int32_t *__restrict__ counts,
+                                                           float *__restrict__ vt) {
+    const int blk = blockIdx.x, r = threadIdx.x, lane = r & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(r >> 6);
+    const float *hv = gpart + static_cast<int64_t>(blk) * splits * kD * kD;
+    const uint8_t *mine = stream + static_cast<int64_t>(blk) * kStreamBytes;
+    const float2 *rot = reinterpret_cast<const float2 *>(mine) + kRotPad;
+    const uint32_t *hdr = reinterpret_cast<const uint32_t *>(mine + sizeof(float) * 2 * (kRotCap + 2 * kRotPad));
+    __shared__ float4 hb[2][8][kD / 4];
+    __shared__ float beta[kD];
+    __shared__ float4 cs[kRing][kD / 2];  // ring of steps: rotation K of a step at (c, s) pair K
+    __shared__ uint32_t hs[kStepCap];
+    const int S = __builtin_amdgcn_readfirstlane(counts[2 * blk]);
+    for (int t = r; t < S; t += kThreads) hs[t] = hdr[t];
+
+    float y[kD];
+    form_q_row(y, hv, r, hb, beta);  // its barriers make hs visible
+
+    // Step t's rotations sit at rot[pos_t ..] and its rows in hs[t].  Wave 0
+    // copies each step into ring slot t % kRing by LDS DMA kAhead steps ahead of
+    // its use (the stream comes from HBM): the 128 rotation slots from pos_t - l_t on, so that rotation K lands
+    // at pair K (the slots outside [l, m) belong to neighbouring steps or the
+    // padding and are applied as the identity).
+    int pos = 0, tf = 0;
+    const auto fetch = [&]() {
+        if (tf < S) {
+            const uint32_t h = __builtin_amdgcn_readfirstlane(hs[tf]);  // uniform: scalar branches below
+            const int l = static_cast<int>(h & 0xffffu), n = static_cast<int>(h >> 16) - l;
+            if (wave == 0)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(rot + pos - l + 2 * lane),
+                    (__attribute__((address_space(3))) void *)(cs[tf % kRing]), 16, 0, 0);
+            pos += n;
+            ++tf;
         }
-        if (jb < 0) break;
-        m = jb + 1;
-        // top: one past the last negligible e_j with j < m - 1
-        int l = 0;
-        {
-            const int t = m - 1;
-            const uint64_t hm = t > 64 ? (hi & ((1ull << (t - 64)) - 1)) : 0ull;
-            if (hm) {
-                l = 64 + 64 - __builtin_clzll(hm);
-            } else {
-                const uint64_t lm = lo & (t >= 64 ? ~0ull : ((1ull << t) - 1));
-                if (lm) l = 64 - __builtin_clzll(lm);
-            }
+    };
+    // at most n DMAs outstanding (n < kAhead)
+    const auto wait_dma = [](int n) {
+        switch (n < 0 ? 0 : n) {
+#define MILO_WAIT(N) \
+    case N:          \
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (N)); \
+        break;
+            MILO_WAIT(0) MILO_WAIT(1) MILO_WAIT(2) MILO_WAIT(3) MILO_WAIT(4) MILO_WAIT(5) MILO_WAIT(6)
+            MILO_WAIT(7) MILO_WAIT(8)
+#undef MILO_WAIT
+            default:
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (kAhead - 1));
         }
-        if (steps == max_steps) {
-            capped = true;
-            break;
+    };
+    // After step t's DMA has landed: the identity into the slots of its first and
+    // last groups of eight that lie outside [l, m) (they hold neighbouring
+    // steps' rotations or padding).
+    const auto identity_edges = [&](int t) {
+        if (t < S && wave == 0) {
+            const uint32_t h = __builtin_amdgcn_readfirstlane(hs[t]);
+            const int l = static_cast<int>(h & 0xffffu), m = static_cast<int>(h >> 16);
+            const int lo = l & ~7, hi = (m + 7) & ~7;
+            const int K = lane < 8 ? lo + lane : m + (lane - 8);  // 8 slots below l, up to 8 from m
+            if ((lane < 8 && K < l) || (lane >= 8 && lane < 16 && K < hi && K < kD))
+                reinterpret_cast<float2 *>(cs[t % kRing])[K] = make_float2(1.f, 0.f);
         }
-        ++steps;
-        rotations += m - l;
-        // Wilkinson shift: the eigenvalue of the trailing 2 x 2 nearer its last entry
-        float mu;
-        {
-            const float p = D[m - 1], b = D[m], g = E[m];
-            const float del = 0.5f * (p - b);
-            const float h = sqrtf(fmaf(del, del, g * g));
-            mu = b - g * g / (del + (del >= 0.f ? h : -h));
-        }
-        const float keep = E[l];  // T[l-1][l]: the first rotation writes this slot
-        float a = D[l], f = E[l + 1], x = a - mu, z = f;
-        // the chase over rows l .. m, one rotation per index K (rows/columns K, K + 1):
-        // (c, s) zeroes the bulge z against x; a, f are the current T[K][K],
-        // T[K][K+1], and b, en the untouched T[K+1][K+1], T[K+1][K+2]
+    };
+    static_assert(kAhead - 1 <= 15 && kAhead < kRing, "DMA ring");
+    for (int i = 0; i < kAhead; ++i) fetch();
+    wait_dma(tf - 1);
+    identity_edges(0);
+    __syncthreads();
+    for (int t = 0; t < S; ++t) {
+        fetch();  // step t + kAhead
+        const uint32_t h = __builtin_amdgcn_readfirstlane(hs[t]);
+        const int l = static_cast<int>(h & 0xffffu), m = static_cast<int>(h >> 16);
+        const float4 *cst = cs[t % kRing];
+        // whole groups of eight rotations (the slots of a group outside [l, m)
+        // hold the identity)
 #pragma unroll
-        for (int K = 0; K < kD - 1; ++K) {
-            if (K < l) continue;
-            if (K >= m) break;
-            const float b = D[K + 1], en = E[K + 2];
-            const float q = fmaf(x, x, z * z);
-            const float rs = q > 0.f ? __builtin_amdgcn_rsqf(q) : 0.f;
-            const float c = q > 0.f ? x * rs : 1.f, s = z * rs;
-            E[K] = q * rs;  // T[K-1][K] (at K = l this slot is restored below)
-            const float cc = c * c, ss = s * s, cs = c * s;
-            const float t2 = 2.f * cs * f;
-            D[K] = fmaf(cc, a, fmaf(ss, b, t2));
-            const float an = fmaf(ss, a, fmaf(cc, b, -t2));
-            x = fmaf(cs, b - a, (cc - ss) * f);
-            a = an;
-            z = s * en;
-            f = c * en;
-            const float y0 = y[K], y1 = y[K + 1];
-            y[K] = fmaf(c, y0, s * y1);
-            y[K + 1] = fmaf(c, y1, -s * y0);
+        for (int K0 = 0; K0 < kD - 1; K0 += 8) {
+            if (K0 + 8 <= l) continue;
+            if (K0 >= m) break;
+            float c8[8], s8[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 v = cst[K0 / 2 + i];
+                c8[2 * i] = v.x;
+                s8[2 * i] = v.y;
+                c8[2 * i + 1] = v.z;
+                s8[2 * i + 1] = v.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int K = K0 + i;
+                if (K >= kD - 1) break;
+                rotate_pair(y[K], y[K + 1], c8[i], s8[i]);
+            }
         }
-        E[m] = x;
-        D[m] = a;
-        E[l] = keep;
+        wait_dma(tf - (t + 2));  // step t + 1 has landed; the later steps may be in flight
+        identity_edges(t + 1);
+        __syncthreads();
     }
 #pragma unroll
-    for (int c = 0; c < kD; ++c) out[c * kD + r] = y[c];
-    if (r == 0 && rot_out) rot_out[blk] = capped ? -rotations : rotations;
+    for (int c = 0; c < kD; ++c) vt[static_cast<int64_t>(blk) * kD * kD + c * kD + r] = y[c];
 }
 
 }  // namespace
@@ -296,11 +528,19 @@ hipError_t launch_tridiag(float *gpart, int splits, int n_blocks, float *vt, hip
     return hipGetLastError();
 }
 
-hipError_t launch_ql(const float *gpart, int splits, int n_blocks, float *vt, int32_t *rotations, int max_steps,
-                     hipStream_t st) {
+hipError_t launch_qr_chain(const float *vt, int n_blocks, void *stream, int32_t *counts, int32_t *rotations,
+                           hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(ql_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), 0, st, gpart, splits, vt,
-                       rotations, max_steps);
+    hipLaunchKernelGGL(qr_chain_kernel, dim3(static_cast<unsigned>((n_blocks + 63) / 64)), dim3(64), 0, st, vt,
+                       n_blocks, static_cast<uint8_t *>(stream), counts, rotations);
+    return hipGetLastError();
+}
+
+hipError_t launch_qr_apply(const float *gpart, int splits, int n_blocks, const void *stream, const int32_t *counts,
+                           float *vt, hipStream_t st) {
+    if (n_blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(qr_apply_kernel, dim3(static_cast<unsigned>(n_blocks)), dim3(kThreads), 0, st, gpart, splits,
+                       static_cast<const uint8_t *>(stream), counts, vt);
     return hipGetLastError();
 }
 

@@ -23,17 +23,30 @@ enum AllocPolicy : int { kAllocEntropy = 0, kAllocUniform = 1, kAllocRandom = 2 
 hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t row_stride,
                        int block_len, int n_blocks, int splits, float *gpart, hipStream_t st);
 
-// Eigenvectors of the 128 x 128 Grams in two launches.  launch_tridiag reduces
-// each Gram (the sum of its `splits` partials in gpart) to tridiagonal form by
-// Householder reflections, keeping the reflectors in the block's first partial
-// and the tridiagonal matrix in vt[b]; launch_ql then runs implicit shifted QR
-// steps on it and writes the eigenvectors as the rows of vt[b] (in no
-// particular order, unit length to working accuracy).  rotations[b] = the plane
-// rotations applied, negated when the cap of max_steps QR steps stopped the
-// iteration.
+// Eigenvectors of the 128 x 128 Grams in three launches.
+//  * launch_tridiag reduces each Gram (the sum of its `splits` partials in
+//    gpart) to tridiagonal form by Householder reflections, keeping the
+//    reflectors in the block's first partial and the tridiagonal matrix in
+//    vt[b].
+//  * launch_qr_chain runs the implicit shifted QR steps on the tridiagonal
+//    matrices, one per lane, and records each block's plane rotations in its
+//    stream area: up to kRotCap rotations (c, s) after kRotPad unused slots,
+//    kRotPad more unused slots, then up to kStepCap step headers (first row |
+//    last row << 16); counts[b] = (steps, rotations).
+//    rotations[b] (may be null) = the rotations, negated when a cap stopped
+//    the iteration.
+//  * launch_qr_apply forms the rows of Q from the reflectors, applies the
+//    recorded rotations to them and writes the eigenvectors as the rows of
+//    vt[b] (in no particular order, unit length to working accuracy).
+constexpr int kRotCap = 20480;  // rotations per block (about 11.5 k are taken on planted Grams)
+constexpr int kStepCap = 512;   // QR steps per block (about 170 are taken)
+constexpr int kRotPad = 128;     // rotation slots before and after a block's rotations
+constexpr size_t kStreamBytes = sizeof(float) * 2 * (kRotCap + 2 * kRotPad) + sizeof(uint32_t) * kStepCap;
 hipError_t launch_tridiag(float *gpart, int splits, int n_blocks, float *vt, hipStream_t st);
-hipError_t launch_ql(const float *gpart, int splits, int n_blocks, float *vt, int32_t *rotations, int max_steps,
-                     hipStream_t st);
+hipError_t launch_qr_chain(const float *vt, int n_blocks, void *stream, int32_t *counts, int32_t *rotations,
+                           hipStream_t st);
+hipError_t launch_qr_apply(const float *gpart, int splits, int n_blocks, const void *stream, const int32_t *counts,
+                           float *vt, hipStream_t st);
 
 // sigma_i = ||X_b v_i|| in fp32-accurate arithmetic, sorted descending into
 // sigma[b][0..128); perm[b][k] = the eigenvector (row of vt[b]) of sorted rank k
