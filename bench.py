@@ -60,8 +60,9 @@ def parse():
                     help="rocprofv3 counter_collection.csv of the bench with SQ_INSTS_VALU_MFMA_MOPS_BF16, "
                          "SQ_INSTS_VALU_MFMA_MOPS_F32, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE -> "
                          "profiles/<kernel>_mfma.json (no GPU)")
-    ap.add_argument("--compress-streams", type=int, default=1,
-                    help="streams the compression calls of a step alternate between (1 or 2)")
+    ap.add_argument("--compress-streams", type=int, default=2,
+                    help="streams the compression calls of a step alternate between (1 or 2; with 2 the K "
+                         "and V calls overlap, so one's QR chain runs beside the other's Gram)")
     ap.add_argument("--compress-chunks", type=int, default=1,
                     help="compression calls per kind (runs of whole layers)")
     ap.add_argument("--filter-csv", nargs=2, metavar=("IN", "OUT"),
@@ -76,7 +77,7 @@ def parse():
 
 
 # kernel -> the sources that define it (the traffic records are tied to their hash)
-KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "tridiag": ["eigh.hip"], "qr_chain": ["eigh.hip"],
+KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "jacobi": ["jacobi.hip"], "tridiag": ["eigh.hip"], "qr_chain": ["eigh.hip"],
                   "qr_apply": ["eigh.hip"],
                   "refine": ["refine.hip", "common.hpp"], "alloc": ["alloc.hip"],
                   "project": ["project.hip", "common.hpp"], "reconstruct": ["reconstruct.hip", "common.hpp"],
@@ -87,7 +88,7 @@ KERNEL_SOURCES = {"gram": ["gram.hip", "common.hpp"], "tridiag": ["eigh.hip"], "
 
 def kernel_key(name):
     """libmilo kernel name (as rocprofv3 prints it) -> bench kernel key."""
-    for frag, key in (("gram_kernel", "gram"), ("gram_bf16_kernel", "gram"), ("tridiag_kernel", "tridiag"), ("qr_chain_kernel", "qr_chain"),
+    for frag, key in (("gram_kernel", "gram"), ("gram_bf16_kernel", "gram"), ("jacobi_kernel", "jacobi"), ("tridiag_kernel", "tridiag"), ("qr_chain_kernel", "qr_chain"),
                       ("qr_apply_kernel", "qr_apply"),
                       ("refine_kernel", "refine"), ("alloc_kernel", "alloc"), ("project_kernel", "project"),
                       ("project_bf16_kernel", "project"), ("reconstruct_kernel", "reconstruct"),
@@ -510,8 +511,9 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     dws = torch.empty(dws_bytes, dtype=torch.uint8, device=dev)
     main_stream = torch.cuda.current_stream()
 
-    def compress_all():
-        if side is not None:
+    def compress_all(one_stream=False):
+        two = side is not None and not one_stream
+        if two:
             side.wait_stream(main_stream)
         for i, (kind, c) in enumerate(calls):
             l0, l1, f = CF[kind][c]
@@ -519,17 +521,17 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
             p0 = l0 * len(bud1)
             npl = (l1 - l0) * len(bud1)
             ppc = [pp[p0 + j] - pp[p0] for j in range(npl + 1)]
-            st = main_stream if (side is None or i % 2 == 0) else side
+            st = main_stream if (not two or i % 2 == 0) else side
             milo.milo_compress_blocks(X[kind][lo:lo + n], ppc, bud[p0:p0 + npl], cfg.eps2,
                                       sigma[kind][lo:lo + n], f, sweeps_out=sweeps[kind][lo:lo + n],
                                       workspace=ws if st is main_stream else ws2, stream=st)
-        if side is not None:
+        if two:
             main_stream.wait_stream(side)
 
-    def step(record=None):
+    def step(record=None, one_stream=False):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ev[0].record()
-        compress_all()
+        compress_all(one_stream)
         ev[1].record()
         for layer in range(L):
             decode_layer(layer, dws)
@@ -542,22 +544,31 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    milo.milo_profile_read()
-    milo.milo_profile_enable(True)
     rec = []
-    torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
         step(rec)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    prof = milo.milo_profile_read()
-    milo.milo_profile_enable(False)
     comp_ms = sum(e[0].elapsed_time(e[1]) for e in rec) / steps
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in rec) / steps
     step_ms = wall * 1e3 / steps
     log(f"[cfg{cfg.idx}] timed {steps} step(s): {step_ms:.1f} ms/step "
         f"(compress {comp_ms:.1f}, decode {dec_ms:.2f})")
+    # per-kernel times for the rooflines: the same steps again with every call on
+    # one stream, so that no kernel's duration includes another's
+    milo.milo_profile_read()
+    milo.milo_profile_enable(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        step(None, one_stream=True)
+    torch.cuda.synchronize()
+    one_ms = (time.perf_counter() - t1) * 1e3 / steps
+    prof = milo.milo_profile_read()
+    milo.milo_profile_enable(False)
+    if side is not None:
+        log(f"[cfg{cfg.idx}] one stream: {one_ms:.1f} ms/step")
     n_bad = int((sweeps["k"] < 0).sum() + (sweeps["v"] < 0).sum())
 
     # decode-only passes over the same compressed cache (the per-token regime)
@@ -693,6 +704,10 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
         # formed from its reflectors (4 d^3 / 3) and 6 flops per rotation and row;
         # the QR chain itself: about 20 flops per rotation
         "tridiag": (n_blocks_step * 4.0 * d ** 3 / 3, "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
+        # Jacobi (launches of few blocks): 9 d^2 (d - 1) flops a sweep, 64 x 127
+        # rotations a sweep
+        "jacobi": (n_blocks_step * rot_mean / (64 * 127) * 9 * d * d * (d - 1), "TFLOP/s", "alu",
+                   PEAK_FP32_VEC_TFLOPS),
         "qr_chain": (n_blocks_step * 20.0 * rot_mean, "TFLOP/s", "alu", PEAK_FP32_VEC_TFLOPS),
         "qr_apply": (n_blocks_step * (4.0 * d ** 3 / 3 + 6.0 * d * rot_mean), "TFLOP/s", "alu",
                      PEAK_FP32_VEC_TFLOPS),
@@ -800,6 +815,7 @@ def run_workload(cfg, fdt, steps, warmup, *, decode_only_steps=20, want_rebuild=
             "decode_only_ms_per_step": None if dec_only_ms is None else round(dec_only_ms, 3),
             "decode_only_context_tokens_per_s": None if dec_only_ms is None else ctx_tokens / (dec_only_ms / 1e3),
             "decode_only_graph": dec_graph,
+            "one_stream_ms_per_step": round(one_ms, 3),
             "eig_rotations_mean": round(rot_mean, 1),
             "blocks_at_step_cap": n_bad,
             "kernels_ms_per_step": {n: round(v[1] / steps, 3) for n, v in prof.items()},
@@ -974,7 +990,8 @@ def main():
             if edt == fdt and c == args.config:
                 continue
             r = run_workload(ecfg, edt, 2, 1, decode_only_steps=10, want_rebuild=False,
-                             want_offload=True, want_cpu=False, counters=False)
+                             want_offload=True, want_cpu=False, counters=False,
+                             compress_streams=args.compress_streams)
             r["ms_per_step"] = round(r.pop("step_ms"), 3)
             r["value"] = ecfg.context_tokens_per_step / (r["ms_per_step"] / 1e3)
             extra[f"config{c}_{edt}"] = r
@@ -986,7 +1003,8 @@ def main():
             extra[f"config{c}"] = run_warm_cold(ecfg, ecfg.storage)
         else:
             r = run_workload(ecfg, ecfg.storage, 3, 1, decode_only_steps=10, want_rebuild=True,
-                             want_offload=False, want_cpu=False, counters=False)
+                             want_offload=False, want_cpu=False, counters=False,
+                             compress_streams=args.compress_streams)
             r["ms_per_step"] = round(r.pop("step_ms"), 3)
             r["value"] = ecfg.context_tokens_per_step / (r["ms_per_step"] / 1e3)
             extra[f"config{c}"] = r

@@ -103,6 +103,22 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kD = 128;
+// The Jacobi eigensolve of small launches: at most 30 sweeps; pairs below 1e-6
+// relative are not rotated.  It ends after the first half sweep that closes 127
+// consecutive rounds whose relative off-diagonals all stayed below 2.5e-3:
+// quadratic convergence leaves them far smaller, and the singular values are then
+// recomputed as Rayleigh quotients ||X v||, second order in the eigenvector
+// error.  Over 28 pools of the long-context workload the worst singular value
+// error is 1.8% of its tolerance at 9.2 sweeps on average; half sweeps at 3e-3
+// raise it to 3.5%, whole sweeps at 5e-3 to 14%, and 1e-2 exceeds it.
+constexpr int kMaxSweeps = 30;
+constexpr float kJacobiTol = 1e-6f;
+constexpr float kJacobiStopTol = 2.5e-3f;
+// Launches of at most this many blocks per CU take the Jacobi eigensolve (about
+// 1.2 ms for two blocks per CU, a workgroup's latency); larger ones take
+// Householder + QR, whose rotation chain is sequential per block (about 4 ms
+// whatever the launch) but whose throughput is three times the Jacobi's.
+constexpr int kJacobiBlocksPerCu = 8;
 constexpr size_t kMat = sizeof(float) * kD * kD;  // one 128 x 128 fp32 matrix
 
 // Split the token dimension of the Gram when there are too few blocks to fill
@@ -143,6 +159,26 @@ milo_status check_pools(const int32_t *pool_ptr, int32_t n_pools, const int64_t 
     if (pool_ptr[n_pools] != n_blocks)
         return fail(MILO_E_INVALID, "pool_ptr[n_pools] = %d but n_blocks = %d", pool_ptr[n_pools],
                     n_blocks);
+    return MILO_OK;
+}
+
+// Compute units of the current device (looked up once per device).
+milo_status device_cus(int *n) {
+    static std::mutex mu;
+    static int cus[64] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < 64 && cus[dev] > 0) {
+        *n = cus[dev];
+        return MILO_OK;
+    }
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+    if (dev >= 0 && dev < 64) cus[dev] = v;
+    *n = v;
     return MILO_OK;
 }
 
@@ -287,6 +323,8 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
     const size_t ws_cap = *workspace_bytes;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    int n_cus = 0;
+    if (milo_status cs = device_cus(&n_cus); cs != MILO_OK) return cs;
     const int T = in->block_len;
     const int k = T < kD ? T : kD;
     const int a_bpr = static_cast<int>(a_rank_bytes(out->dtype, T)), b_bpr = static_cast<int>(b_rank_bytes(out->dtype, kD));
@@ -345,17 +383,26 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
             float *sig = sigma_out + static_cast<size_t>(b0) * kD;
             if ((e = timed("gram", s, [&] { return milo::launch_gram(xc, x_type, row0, in->row_stride, T, nb, splits, gpart, s); })) != hipSuccess)
                 return hip_fail(e, "gram launch");
-            if ((e = timed("tridiag", s, [&] { return milo::launch_tridiag(gpart, splits, nb, vt, s); })) != hipSuccess)
-                return hip_fail(e, "tridiagonalisation launch");
-            if ((e = timed("qr_chain", s, [&] {
-                     return milo::launch_qr_chain(vt, nb, qr_stream, qr_counts, sweeps_out ? sweeps_out + b0 : nullptr,
-                                                  s);
-                 })) != hipSuccess)
-                return hip_fail(e, "QR iteration launch");
-            if ((e = timed("qr_apply", s, [&] {
-                     return milo::launch_qr_apply(gpart, splits, nb, qr_stream, qr_counts, vt, s);
-                 })) != hipSuccess)
-                return hip_fail(e, "QR rotation launch");
+            int32_t *rot_out = sweeps_out ? sweeps_out + b0 : nullptr;
+            if (nb <= kJacobiBlocksPerCu * n_cus) {
+                if ((e = timed("jacobi", s, [&] {
+                         return milo::launch_jacobi(gpart, splits, nb, vt, rot_out, kMaxSweeps, kJacobiTol,
+                                                    kJacobiStopTol, n_cus, s);
+                     })) != hipSuccess)
+                    return hip_fail(e, "jacobi launch");
+            } else {
+                if ((e = timed("tridiag", s, [&] { return milo::launch_tridiag(gpart, splits, nb, vt, s); })) !=
+                    hipSuccess)
+                    return hip_fail(e, "tridiagonalisation launch");
+                if ((e = timed("qr_chain", s, [&] {
+                         return milo::launch_qr_chain(vt, nb, qr_stream, qr_counts, rot_out, s);
+                     })) != hipSuccess)
+                    return hip_fail(e, "QR iteration launch");
+                if ((e = timed("qr_apply", s, [&] {
+                         return milo::launch_qr_apply(gpart, splits, nb, qr_stream, qr_counts, vt, s);
+                     })) != hipSuccess)
+                    return hip_fail(e, "QR rotation launch");
+            }
             if ((e = timed("refine", s, [&] { return milo::launch_refine(xc, x_type, row0, in->row_stride, T, nb, vt, sig, vperm, vscale, s); })) != hipSuccess)
                 return hip_fail(e, "refine launch");
             if ((e = timed("alloc", s, [&] {

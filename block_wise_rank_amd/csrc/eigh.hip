@@ -342,27 +342,37 @@ __global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ 
 
 // Row r of Q = e_r^T H_0 H_1 ... H_125, the reflectors staged through LDS eight
 // at a time (double-buffered, the next group's loads in flight during the
-// current group); v_k vanishes in entries 0..k, so each reflector skips the
-// groups of eight entries it does not touch.
-__device__ __forceinline__ void form_q_row(float (&y)[kD], const float *__restrict__ hv, int r,
+// current group) by threads tid < 128; v_k vanishes in entries 0..k, so each
+// reflector skips the groups of eight entries it does not touch.  Every thread
+// of the workgroup calls it (it holds barriers); a thread with r >= 128 holds
+// no row and only stages.
+__device__ __forceinline__ void form_q_row(float (&y)[kD], const float *__restrict__ hv, int r, int tid,
                                            float4 (*hb)[8][kD / 4], float *beta) {
 #pragma unroll
     for (int j = 0; j < kD; ++j) y[j] = j == r ? 1.f : 0.f;
-    if (r < kRefl) beta[r] = hv[kBetaRow * kD + r];
-    // thread r stages entries 8 (r & 15) .. + 7 of reflector 8 c + (r >> 4)
-    const int rr = r >> 4, cc = 2 * (r & 15);
+    if (tid < kRefl) beta[tid] = hv[kBetaRow * kD + tid];
+    // thread tid stages entries 8 (tid & 15) .. + 7 of reflector 8 c + (tid >> 4)
+    const bool stager = tid < kD;
+    const int rr = (tid >> 4) & 7, cc = 2 * (tid & 15);
     const float4 *src = reinterpret_cast<const float4 *>(hv);
-    float4 a0 = src[rr * (kD / 4) + cc], a1 = src[rr * (kD / 4) + cc + 1];
+    float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+    if (stager) {
+        a0 = src[rr * (kD / 4) + cc];
+        a1 = src[rr * (kD / 4) + cc + 1];
+    }
     for (int c = 0; c < kD / 8; ++c) {
-        hb[c & 1][rr][cc] = a0;
-        hb[c & 1][rr][cc + 1] = a1;
+        if (stager) {
+            hb[c & 1][rr][cc] = a0;
+            hb[c & 1][rr][cc + 1] = a1;
+        }
         __syncthreads();
-        if (c + 1 < kD / 8) {
+        if (stager && c + 1 < kD / 8) {
             const int k = 8 * (c + 1) + rr;
             const bool in = k < kRefl;
             a0 = in ? src[k * (kD / 4) + cc] : make_float4(0.f, 0.f, 0.f, 0.f);
             a1 = in ? src[k * (kD / 4) + cc + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        if (r >= kD) continue;  // uniform: a wave without rows
 #pragma unroll 1
         for (int i = 0; i < 8; ++i) {
             const int k = 8 * c + i;
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void qr_apply_kernel(const float *__restr
     for (int t = r; t < S; t += kThreads) hs[t] = hdr[t];
 
     float y[kD];
-    form_q_row(y, hv, r, hb, beta);  // its barriers make hs visible
+    form_q_row(y, hv, r, r, hb, beta);  // its barriers make hs visible
 
     // Step t's rotations sit at rot[pos_t ..] and its rows in hs[t].  Wave 0
     // copies each step into ring slot t % kRing by LDS DMA kAhead steps ahead of

@@ -48,6 +48,17 @@ hipError_t launch_qr_chain(const float *vt, int n_blocks, void *stream, int32_t 
 hipError_t launch_qr_apply(const float *gpart, int splits, int n_blocks, const void *stream, const int32_t *counts,
                            float *vt, hipStream_t st);
 
+// The eigensolve of launches with few blocks (at most eight per CU), where each
+// block's latency counts: parallel-order cyclic Jacobi on G_b (the sum of the
+// partials) in LDS, 64 disjoint rotations per round.  Pairs with
+// |g| <= tol sqrt|a b| are not rotated; the solve ends after the first half
+// sweep that closes 127 rounds with no rotation above stop_tol.  vt[b][i][:] =
+// eigenvector i (unsorted); sweeps[b] (may be null) = 64 x the rounds used
+// (64 rotations a round), negative when max_sweeps sweeps were reached.
+hipError_t launch_jacobi(const float *gpart, int splits, int n_blocks, float *vt,
+                         int32_t *sweeps, int max_sweeps, float tol, float stop_tol, int n_cus,
+                         hipStream_t st);
+
 // sigma_i = ||X_b v_i|| in fp32-accurate arithmetic, sorted descending into
 // sigma[b][0..128); perm[b][k] = the eigenvector (row of vt[b]) of sorted rank k
 // and scale[b][k] = its sign (largest-magnitude entry made positive) / ||v||:

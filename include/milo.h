@@ -148,12 +148,15 @@ typedef struct milo_factors {
  *              order (sigma desc, block asc, index asc), which is what the
  *              greedy on the gains selects.
  *  sweeps_out  device [n_blocks] int32 (may be NULL): the work of each block's
- *              eigensolve, as the number of plane rotations its QR iteration
- *              applied (0 for a block whose Gram is diagonal once reduced to
- *              tridiagonal form); negated if the iteration reached its cap of
- *              30 QR steps per eigenvalue (the results are then those of the
- *              last step).  (ABI version 4; versions 2 and 3 counted the sweeps
- *              and rounds of a Jacobi eigensolve.)  The
+ *              eigensolve, as the number of plane rotations it applied.  Calls
+ *              of more than eight blocks per compute unit reduce each Gram to
+ *              tridiagonal form and run implicit shifted QR steps (0 rotations
+ *              for a block that is diagonal once reduced; capped at 512 steps
+ *              and 20480 rotations per block); smaller calls run a parallel
+ *              Jacobi eigensolve (64 rotations per round, capped at 30 sweeps of
+ *              127 rounds).  Negated if a cap stopped the iteration (the
+ *              results are then those of its last step).  (ABI version 4;
+ *              versions 2 and 3 counted Jacobi sweeps and rounds.)  The
  *              call returns before its kernels run, so it cannot report this in
  *              its status: a caller that must know passes sweeps_out and checks
  *              it once the stream has reached the call.
