@@ -200,12 +200,15 @@ def test_int8_codes(kind):
     _int8_invariants(f8, T, d)
 
 
-def test_compress_edge_cases():
+@pytest.mark.parametrize("path", ["jacobi", "qr"])
+def test_compress_edge_cases(path):
     """Degenerate blocks through the whole compression, fp32 storage, against the
     oracle: an all-zero block, a rank-1 block, a block with orthonormal columns
     (every singular value 1, so the singular subspaces are not unique), and the
     same planted blocks at x1e-3, x1 and x1e3 in pools of their own (the method
-    is scale-invariant: equal ranks, singular values and relative errors)."""
+    is scale-invariant: equal ranks, singular values and relative errors).  The
+    ten blocks alone take the Jacobi eigensolve; with enough planted pools after
+    them (more than eight blocks per CU) the same call takes Householder + QR."""
     from synthetic import planted_blocks
     T, d = 256, 128
     P = planted_blocks(2, T, d, (4.0, 32.0), seed=8101, out_dtype="f64")
@@ -220,20 +223,31 @@ def test_compress_edge_cases():
     X = torch.stack(blocks).to(torch.float32)
     pp, bud = [0, 3, 4, 6, 8, 10], [100, 50, 128, 128, 128]
     eps2 = 1e-4
-    f, sig, obj, sweeps = run_gpu_compress(X.to(DEV), pp, bud, eps2, "f32")
+    Xg, ppg, budg = X, pp, bud
+    if path == "qr":
+        n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+        n_pad = 64 * (8 * n_cus // 64 + 1)
+        pad = planted_blocks(n_pad, T, d, (4.0, 32.0), seed=8103, out_dtype="f32")
+        Xg = torch.cat([X, pad])
+        ppg = pp + [10 + 64 * (i + 1) for i in range(n_pad // 64)]
+        budg = bud + [64 * 64] * (n_pad // 64)
+    f, sig, obj, sweeps = run_gpu_compress(Xg.to(DEV), ppg, budg, eps2, "f32")
     sw = sweeps.cpu().numpy()
     assert (sw >= 0).all(), "no block may stop at an iteration cap"
     assert (sw[[2, 4, 5, 6, 7, 8, 9]] > 0).all()
+    if path == "qr":
+        assert sw[0] == 0  # the zero Gram is diagonal once reduced: no QR step
+    sig, obj, sw = sig[:10], obj[:5], sw[:10]
     X64 = X.to(torch.float64).numpy()
     comp = oracle.compress(X64, pp, bud, eps2, "f32")
     sg = sig.cpu().numpy().astype(np.float64)
     worst = check_sigma(sg / scale[:, None], comp.sigma / scale[:, None], np.sqrt(eps2), pp, comp.rank)
     assert (sg[0] == 0).all(), "zero block: singular values"
-    r_gpu = f.rank.cpu().numpy()
+    r_gpu = f.rank.cpu().numpy()[:10]
     check_ranks(r_gpu, comp.rank, comp.sigma, pp, bud)
     assert list(r_gpu[:4]) == [0, 1, 99, 50]
     assert np.array_equal(r_gpu[4:6], r_gpu[8:10]) and np.array_equal(r_gpu[6:8], r_gpu[8:10])
-    xh = reconstruct_all(f).cpu().numpy().astype(np.float64)
+    xh = reconstruct_all(f)[:10].cpu().numpy().astype(np.float64)
     assert (xh[0] == 0).all()
     rec = check_reconstruction(X64, comp, r_gpu, xh, "f32", blocks=[0, 1, 2, 4, 5, 6, 7, 8, 9])
     # orthonormal columns: any 50 of the equal singular directions are a best
