@@ -25,8 +25,8 @@
 //    unrolled over the rotation index, with uniform branches skipping to l and
 //    leaving at m, which keeps every row entry at a fixed register.
 //
-// Deflation: e_j is negligible when |e_j| <= u (|d_j| + |d_{j+1}|),
-// u = 2^-23.  After every QR step the bottom block shrinks past negligible
+// Deflation: e_j is negligible when |e_j| <= u max(|d_j| + |d_{j+1}|, 1),
+// u = 2^-23 (1: the scale of G's largest diagonal entry, below).  After every QR step the bottom block shrinks past negligible
 // entries and its top is the entry above the lowest negligible one below it
 // (flags for all j from one lane-parallel test and two ballots).  The Gram is
 // scaled by a power of two (1 / its largest diagonal entry, rounded to a power
@@ -183,8 +183,12 @@ __global__ __launch_bounds__(kThreads) void tridiag_kernel(float *__restrict__ g
     }
 }
 
+// T is scaled so that G's largest diagonal entry lies in [1, 2): the floor of 1
+// keeps entries far below that scale from being resolved to full relative
+// accuracy (the fp32 Gram carries errors of that order anyway, and the singular
+// values are recomputed from X).
 __device__ __forceinline__ bool negligible(float e, float d0, float d1) {
-    return fabsf(e) <= kDeflTol * (fabsf(d0) + fabsf(d1));
+    return fabsf(e) <= kDeflTol * fmaxf(fabsf(d0) + fabsf(d1), 1.f);
 }
 
 // Highest bit j < lim of a 128-bit mask (four words) that is set, or -1.
@@ -251,7 +255,17 @@ __global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ 
     int m = kD - 1, l = 0, K = 0, steps = 0, rots = 0, st = act ? 0 : 2;
     bool capped = false;
     float g = 0.f, p = 0.f, sn = 1.f, cn = 1.f, dk = 0.f, dk1 = 0.f, ek = 0.f, dprev = 0.f;
+    // A rotation's LDS writes are issued at the start of the next pass (before
+    // that pass's reads), so that waiting for those reads never waits for them.
+    int wk = -1;      // d_wk (and e_{wk-1} when we_on) still to be written
+    bool we_on = false;
+    float wd = 0.f, we = 0.f;
     for (int pass = 0; __any(st != 2); ++pass) {
+        if (wk >= 0) {
+            if (we_on) Es[wk - 1][lane] = we;
+            Ds[wk][lane] = wd;
+            wk = -1;
+        }
         if (pass % kSetupEvery == 0) {
             if (st == 3) {
                 const float dm = dk - p;  // d_m
@@ -317,12 +331,13 @@ __global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ 
             sn = f * rs;
             cn = ok ? g * rs : 1.f;
             g = ok ? gn : bb;
-            if (K > l) {
-                const float r = q * rs;  // e_{K-1}
-                Es[K - 1][lane] = r;
-                set_bit(nm, K - 1, negligible(r, dprev, dK));
+            we_on = K > l;
+            if (we_on) {
+                we = q * rs;  // e_{K-1}
+                set_bit(nm, K - 1, negligible(we, dprev, dK));
             }
-            Ds[K][lane] = dK;
+            wk = K;
+            wd = dK;
             dprev = dK;
             rot[rots] = make_float2(cn, sn);
             ++rots;
