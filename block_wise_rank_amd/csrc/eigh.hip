@@ -46,10 +46,23 @@ constexpr float kDeflTol = 1.1920929e-7f;  // 2^-23
 constexpr int kRing = 12, kAhead = 10;      // rotation staging of the apply kernel (steps)
 constexpr int kSetupEvery = 8;              // passes of the chain kernel between step starts
 
+// Sum over the wave by DPP (no LDS round trips): within each row of 16 lanes
+// by quad permutes and row rotations, then across rows by the row broadcasts
+// of lanes 15 and 31; the total ends in lane 63 and is returned to every lane.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, RowMask, 0xf, false);
+    return v + __int_as_float(o);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    v = dpp_add<0xB1, 0xf>(v);   // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E, 0xf>(v);   // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x124, 0xf>(v);  // row_ror:4
+    v = dpp_add<0x128, 0xf>(v);  // row_ror:8: every lane holds its row's sum
+    v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
