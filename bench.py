@@ -2,16 +2,17 @@
 """Benchmark of the MILO hot path on one MI355X.
 
 One step = one pass of the whole path over the workload's KV cache: compress
-every K block and every V block of every layer (Gram -> Jacobi eigensolve ->
+every K block and every V block of every layer (Gram -> eigensolve ->
 singular-value refinement -> rank allocation -> factors), then one decode step
 of every layer over the compressed blocks.  Inputs (planted-spectrum blocks and
 queries, seeded) are generated on the GPU and resident in HBM before timing.
 
 Prints ONE JSON line.  `value` is context tokens (sum over sequences of the
-tokens attended in the decode step) per second of step time; the breakdown
-reports compression blocks/s and decode context-tokens/s on their own, and a
-roofline entry for every kernel from per-kernel HIP-event timings taken inside
-the timed steps.
+tokens attended in the decode step) per second of step time, the K and V
+compression calls on two streams (--compress-streams); the breakdown reports
+compression blocks/s and decode context-tokens/s on their own, and a roofline
+entry for every kernel from per-kernel HIP-event timings taken in a second pass
+of the same steps with every call on one stream.
 
   python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
   python bench.py --calibrate-copy     # plain copy kernel for HBM counter calibration
