@@ -45,6 +45,7 @@ constexpr int kBetaRow = kD - 2; // row of the reflector area holding beta_k
 constexpr float kDeflTol = 1.1920929e-7f;  // 2^-23
 constexpr int kRing = 12, kAhead = 10;      // rotation staging of the apply kernel (steps)
 constexpr int kSetupEvery = 8;              // passes of the chain kernel between step starts
+static_assert(kSetupEvery <= 32, "a lane's buffered flags fit one word");
 
 // Sum over the wave by DPP (no LDS round trips): within each row of 16 lanes
 // by quad permutes and row rotations, then across rows by the row broadcasts
@@ -217,6 +218,28 @@ __device__ __forceinline__ int highest_below(const uint32_t (&w)[4], int lim) {
     return j;
 }
 
+// Bits j0 .. j0 + n - 1 (n <= 32, within the 128) of the mask set from the low
+// n bits of v.
+__device__ __forceinline__ void set_bits(uint32_t (&w)[4], int j0, int n, uint32_t v) {
+    const int w0 = j0 >> 5, sh = j0 & 31;
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo = i == w0 ? w[i] : lo;
+        hi = i == w0 + 1 ? w[i] : hi;
+    }
+    uint64_t both = static_cast<uint64_t>(hi) << 32 | lo;
+    const uint64_t keep = (n >= 32 ? 0xffffffffull : ((1ull << n) - 1)) << sh;
+    both = (both & ~keep) | ((static_cast<uint64_t>(v) << sh) & keep);
+    lo = static_cast<uint32_t>(both);
+    hi = static_cast<uint32_t>(both >> 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[i] = i == w0 ? lo : w[i];
+        w[i] = i == w0 + 1 ? hi : w[i];
+    }
+}
+
 __device__ __forceinline__ void set_bit(uint32_t (&w)[4], int j, bool on) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -273,6 +296,11 @@ __global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ 
     int wk = -1;      // d_wk (and e_{wk-1} when we_on) still to be written
     bool we_on = false;
     float wd = 0.f, we = 0.f;
+    // Negligibility of the e_j a chase writes, j = fj .. fj + fn - 1, kept as the
+    // bits of fv until the next step-start pass merges them into the mask (only
+    // step starts read it; at most kSetupEvery rotations come between).
+    int fj = 0, fn = 0;
+    uint32_t fv = 0u;
     for (int pass = 0; __any(st != 2); ++pass) {
         if (wk >= 0) {
             if (we_on) Es[wk - 1][lane] = we;
@@ -280,6 +308,11 @@ __global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ 
             wk = -1;
         }
         if (pass % kSetupEvery == 0) {
+            if (fn > 0) {
+                set_bits(nm, fj, fn, fv);
+                fn = 0;
+                fv = 0u;
+            }
             if (st == 3) {
                 const float dm = dk - p;  // d_m
                 Ds[m][lane] = dm;
@@ -347,7 +380,9 @@ __global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ 
             we_on = K > l;
             if (we_on) {
                 we = q * rs;  // e_{K-1}
-                set_bit(nm, K - 1, negligible(we, dprev, dK));
+                if (fn == 0) fj = K - 1;
+                fv |= static_cast<uint32_t>(negligible(we, dprev, dK)) << fn;
+                ++fn;
             }
             wk = K;
             wd = dK;
