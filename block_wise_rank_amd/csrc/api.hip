@@ -395,7 +395,7 @@ milo_status milo_compress_blocks_ex(const milo_blocks *in, const int32_t *pool_p
                     hipSuccess)
                     return hip_fail(e, "tridiagonalisation launch");
                 if ((e = timed("qr_chain", s, [&] {
-                         return milo::launch_qr_chain(vt, nb, qr_stream, qr_counts, rot_out, s);
+                         return milo::launch_qr_chain(vt, nb, qr_stream, qr_counts, rot_out, n_cus, s);
                      })) != hipSuccess)
                     return hip_fail(e, "QR iteration launch");
                 if ((e = timed("qr_apply", s, [&] {

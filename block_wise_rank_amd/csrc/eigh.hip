@@ -257,13 +257,20 @@ __device__ __forceinline__ void set_bit(uint32_t (&w)[4], int j, bool on) {
 // above the converged bottom that is not negligible, l is one past the last
 // negligible entry above it.  Each step's rotations (c, s) and its header go to
 // the block's stream area in order.
+// L matrices per wave (lanes L .. 63 idle): the LDS copy of T takes
+// (kD + 2) * 8 bytes per matrix, so L sets how many waves a CU holds (64: two,
+// 48: three, 36: four), and the launcher picks L so that a call's waves fill
+// the CUs in as few rounds as possible.
+template <int L>
 __global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ vt, int n_blocks,
                                                       uint8_t *__restrict__ stream, int32_t *__restrict__ counts,
                                                       int32_t *__restrict__ rot_out) {
-    const int lane = threadIdx.x, b = blockIdx.x * 64 + lane;
-    const bool act = b < n_blocks;
-    __shared__ float Ds[kD + 2][64], Es[kD + 2][64];  // d_j, e_j = T[j][j+1] (rows 127.. pads)
-    {
+    static_assert(L >= 1 && L <= 64, "one lane per matrix");
+    const int lane = threadIdx.x, b = blockIdx.x * L + lane;
+    const bool own = lane < L;  // only these lanes touch the LDS copy
+    const bool act = own && b < n_blocks;
+    __shared__ float Ds[kD + 2][L], Es[kD + 2][L];  // d_j, e_j = T[j][j+1] (rows 127.. pads)
+    if (own) {
         const float4 *tri = reinterpret_cast<const float4 *>(vt + static_cast<int64_t>(act ? b : 0) * kD * kD);
 #pragma unroll 4
         for (int q = 0; q < kD / 4; ++q) {
@@ -277,9 +284,11 @@ __global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ 
         Es[kD][lane] = Es[kD + 1][lane] = 0.f;
     }
     uint32_t nm[4] = {0u, 0u, 0u, 0u};
+    if (own) {
 #pragma unroll
-    for (int j = 0; j < kD - 1; ++j)
-        if (negligible(Es[j][lane], Ds[j][lane], Ds[j + 1][lane])) nm[j >> 5] |= 1u << (j & 31);
+        for (int j = 0; j < kD - 1; ++j)
+            if (negligible(Es[j][lane], Ds[j][lane], Ds[j + 1][lane])) nm[j >> 5] |= 1u << (j & 31);
+    }
 
     uint8_t *mine = stream + static_cast<int64_t>(act ? b : 0) * kStreamBytes;
     float2 *rot = reinterpret_cast<float2 *>(mine) + kRotPad;
@@ -602,10 +611,32 @@ hipError_t launch_tridiag(float *gpart, int splits, int n_blocks, float *vt, hip
 }
 
 hipError_t launch_qr_chain(const float *vt, int n_blocks, void *stream, int32_t *counts, int32_t *rotations,
-                           hipStream_t st) {
+                           int n_cus, hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qr_chain_kernel, dim3(static_cast<unsigned>((n_blocks + 63) / 64)), dim3(64), 0, st, vt,
-                       n_blocks, static_cast<uint8_t *>(stream), counts, rotations);
+    // a wave's time is its lanes' dependent chains, nearly whatever L is, so the
+    // launch takes about (rounds of resident waves) x (one wave's time): take the
+    // L with the fewest rounds, the larger L on a tie
+    const int lanes[3] = {64, 48, 36}, per_cu[3] = {2, 3, 4};  // 160 KiB of LDS / ((kD + 2) * 8 * L)
+    int pick = 0;
+    int64_t best = -1;
+    for (int i = 0; i < 3; ++i) {
+        const int64_t waves = (n_blocks + lanes[i] - 1) / lanes[i];
+        const int64_t slots = static_cast<int64_t>(n_cus > 0 ? n_cus : 1) * per_cu[i];
+        const int64_t rounds = (waves + slots - 1) / slots;
+        if (best < 0 || rounds < best) {
+            best = rounds;
+            pick = i;
+        }
+    }
+    const int L = lanes[pick];
+    const dim3 grid(static_cast<unsigned>((n_blocks + L - 1) / L));
+    uint8_t *sp = static_cast<uint8_t *>(stream);
+    if (L == 64)
+        hipLaunchKernelGGL(qr_chain_kernel<64>, grid, dim3(64), 0, st, vt, n_blocks, sp, counts, rotations);
+    else if (L == 48)
+        hipLaunchKernelGGL(qr_chain_kernel<48>, grid, dim3(64), 0, st, vt, n_blocks, sp, counts, rotations);
+    else
+        hipLaunchKernelGGL(qr_chain_kernel<36>, grid, dim3(64), 0, st, vt, n_blocks, sp, counts, rotations);
     return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t r
 //    reflectors in the block's first partial and the tridiagonal matrix in
 //    vt[b].
 //  * launch_qr_chain runs the implicit shifted QR steps on the tridiagonal
-//    matrices, one per lane, and records each block's plane rotations in its
+//    matrices, one per lane (64, 48 or 36 per wave, whichever lets the call's
+//    waves fill the n_cus CUs in the fewest rounds), and records each block's plane rotations in its
 //    stream area: up to kRotCap rotations (c, s) after kRotPad unused slots,
 //    kRotPad more unused slots, then up to kStepCap step headers (first row |
 //    last row << 16); counts[b] = (steps, rotations).
@@ -44,7 +45,7 @@ constexpr int kRotPad = 128;     // rotation slots before and after a block's ro
 constexpr size_t kStreamBytes = sizeof(float) * 2 * (kRotCap + 2 * kRotPad) + sizeof(uint32_t) * kStepCap;
 hipError_t launch_tridiag(float *gpart, int splits, int n_blocks, float *vt, hipStream_t st);
 hipError_t launch_qr_chain(const float *vt, int n_blocks, void *stream, int32_t *counts, int32_t *rotations,
-                           hipStream_t st);
+                           int n_cus, hipStream_t st);
 hipError_t launch_qr_apply(const float *gpart, int splits, int n_blocks, const void *stream, const int32_t *counts,
                            float *vt, hipStream_t st);
 
