@@ -615,7 +615,8 @@ hipError_t launch_qr_chain(const float *vt, int n_blocks, void *stream, int32_t 
     if (n_blocks <= 0) return hipSuccess;
     // a wave's time is its lanes' dependent chains, nearly whatever L is, so the
     // launch takes about (rounds of resident waves) x (one wave's time): take the
-    // L with the fewest rounds, the larger L on a tie
+    // L with the fewest rounds, the smaller L on a tie (its longest chain is
+    // shorter and its waves spread over more SIMDs)
     const int lanes[3] = {64, 48, 36}, per_cu[3] = {2, 3, 4};  // 160 KiB of LDS / ((kD + 2) * 8 * L)
     int pick = 0;
     int64_t best = -1;
@@ -623,7 +624,7 @@ hipError_t launch_qr_chain(const float *vt, int n_blocks, void *stream, int32_t 
         const int64_t waves = (n_blocks + lanes[i] - 1) / lanes[i];
         const int64_t slots = static_cast<int64_t>(n_cus > 0 ? n_cus : 1) * per_cu[i];
         const int64_t rounds = (waves + slots - 1) / slots;
-        if (best < 0 || rounds < best) {
+        if (best < 0 || rounds <= best) {
             best = rounds;
             pick = i;
         }

@@ -29,8 +29,8 @@ hipError_t launch_gram(const void *x, int x_type, const int64_t *row0, int64_t r
 //    reflectors in the block's first partial and the tridiagonal matrix in
 //    vt[b].
 //  * launch_qr_chain runs the implicit shifted QR steps on the tridiagonal
-//    matrices, one per lane (64, 48 or 36 per wave, whichever lets the call's
-//    waves fill the n_cus CUs in the fewest rounds), and records each block's plane rotations in its
+//    matrices, one per lane (64, 48 or 36 per wave: the fewest rounds of
+//    resident waves on the n_cus CUs, then the fewest per wave), and records each block's plane rotations in its
 //    stream area: up to kRotCap rotations (c, s) after kRotPad unused slots,
 //    kRotPad more unused slots, then up to kStepCap step headers (first row |
 //    last row << 16); counts[b] = (steps, rotations).
