@@ -72,7 +72,7 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-__global__ __launch_bounds__(kThreads) void tridiag_kernel(float *__restrict__ gpart, int splits,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void tridiag_kernel(float *__restrict__ gpart, int splits,
                                                           float *__restrict__ vt) {
     const int blk = blockIdx.x, r = threadIdx.x, lane = r & 63;
     const int wave = __builtin_amdgcn_readfirstlane(r >> 6);
@@ -148,20 +148,33 @@ __global__ __launch_bounds__(kThreads) void tridiag_kernel(float *__restrict__ g
         // rows are all <= k skips the products, and so does every group of
         // eight columns <= k (uniform branches).
         const bool live = 64 * wave + 63 > k;
+        // The loops below run over segments of 32 columns, skipping those with
+        // every column <= k; within a segment the LDS operands of each group of
+        // columns are loaded one group ahead, so that only a segment's first
+        // load waits (the columns <= k of a segment that is run add exact zeros:
+        // x, v and p vanish there).
         float dot = 0.f;
         if (live) {
 #pragma unroll
-            for (int j = 0; j < kD / 4; j += 2) {
-                if (4 * j + 7 <= k) continue;
-                const float4 x = xb[par][j], x2 = xb[par][j + 1];
-                dot = fmaf(a[4 * j], x.x, dot);
-                dot = fmaf(a[4 * j + 1], x.y, dot);
-                dot = fmaf(a[4 * j + 2], x.z, dot);
-                dot = fmaf(a[4 * j + 3], x.w, dot);
-                dot = fmaf(a[4 * j + 4], x2.x, dot);
-                dot = fmaf(a[4 * j + 5], x2.y, dot);
-                dot = fmaf(a[4 * j + 6], x2.z, dot);
-                dot = fmaf(a[4 * j + 7], x2.w, dot);
+            for (int sg = 0; sg < 4; ++sg) {
+                if (32 * sg + 31 <= k) continue;
+                float4 xn0 = xb[par][8 * sg], xn1 = xb[par][8 * sg + 1];
+#pragma unroll
+                for (int j = 8 * sg; j < 8 * sg + 8; j += 2) {  // columns 4j .. 4j + 7
+                    const float4 x = xn0, x2 = xn1;
+                    if (j + 2 < 8 * sg + 8) {
+                        xn0 = xb[par][j + 2];
+                        xn1 = xb[par][j + 3];
+                    }
+                    dot = fmaf(a[4 * j], x.x, dot);
+                    dot = fmaf(a[4 * j + 1], x.y, dot);
+                    dot = fmaf(a[4 * j + 2], x.z, dot);
+                    dot = fmaf(a[4 * j + 3], x.w, dot);
+                    dot = fmaf(a[4 * j + 4], x2.x, dot);
+                    dot = fmaf(a[4 * j + 5], x2.y, dot);
+                    dot = fmaf(a[4 * j + 6], x2.z, dot);
+                    dot = fmaf(a[4 * j + 7], x2.w, dot);
+                }
             }
         }
         dot = fmaf(-alpha, ak1, dot);
@@ -181,12 +194,21 @@ __global__ __launch_bounds__(kThreads) void tridiag_kernel(float *__restrict__ g
         const float ur = fmaf(-2.f * K, vr, pr);
         if (live) {
 #pragma unroll
-            for (int j = 0; j < kD / 4; ++j) {
-                if (4 * j + 3 <= k) continue;
-                const float4 p = pb[par][j], v = vb[par][j];
-                const float pj[4] = {p.x, p.y, p.z, p.w}, vj[4] = {v.x, v.y, v.z, v.w};
+            for (int sg = 0; sg < 4; ++sg) {
+                if (32 * sg + 31 <= k) continue;
+                float4 pn = pb[par][8 * sg], vn = vb[par][8 * sg];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[4 * j + i] = fmaf(-vr, pj[i], fmaf(-ur, vj[i], a[4 * j + i]));
+                for (int j = 8 * sg; j < 8 * sg + 8; ++j) {  // columns 4j .. 4j + 3
+                    const float4 p = pn, v = vn;
+                    if (j + 1 < 8 * sg + 8) {
+                        pn = pb[par][j + 1];
+                        vn = vb[par][j + 1];
+                    }
+                    a[4 * j] = fmaf(-vr, p.x, fmaf(-ur, v.x, a[4 * j]));
+                    a[4 * j + 1] = fmaf(-vr, p.y, fmaf(-ur, v.y, a[4 * j + 1]));
+                    a[4 * j + 2] = fmaf(-vr, p.z, fmaf(-ur, v.z, a[4 * j + 2]));
+                    a[4 * j + 3] = fmaf(-vr, p.w, fmaf(-ur, v.w, a[4 * j + 3]));
+                }
             }
         }
     }
