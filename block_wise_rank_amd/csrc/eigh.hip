@@ -148,21 +148,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         // rows are all <= k skips the products, and so does every group of
         // eight columns <= k (uniform branches).
         const bool live = 64 * wave + 63 > k;
-        // The loops below run over segments of 32 columns, skipping those with
+        // The loops below run over segments of 16 columns, skipping those with
         // every column <= k; within a segment the LDS operands of each group of
         // columns are loaded one group ahead, so that only a segment's first
         // load waits (the columns <= k of a segment that is run add exact zeros:
-        // x, v and p vanish there).
+        // x, v and p vanish there).  (Segments of 32 wasted more zero updates,
+        // a branch per group exposed every load.)
         float dot = 0.f;
         if (live) {
 #pragma unroll
-            for (int sg = 0; sg < 4; ++sg) {
-                if (32 * sg + 31 <= k) continue;
-                float4 xn0 = xb[par][8 * sg], xn1 = xb[par][8 * sg + 1];
+            for (int sg = 0; sg < 8; ++sg) {
+                if (16 * sg + 15 <= k) continue;
+                float4 xn0 = xb[par][4 * sg], xn1 = xb[par][4 * sg + 1];
 #pragma unroll
-                for (int j = 8 * sg; j < 8 * sg + 8; j += 2) {  // columns 4j .. 4j + 7
+                for (int j = 4 * sg; j < 4 * sg + 4; j += 2) {  // columns 4j .. 4j + 7
                     const float4 x = xn0, x2 = xn1;
-                    if (j + 2 < 8 * sg + 8) {
+                    if (j + 2 < 4 * sg + 4) {
                         xn0 = xb[par][j + 2];
                         xn1 = xb[par][j + 3];
                     }
@@ -194,13 +195,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const float ur = fmaf(-2.f * K, vr, pr);
         if (live) {
 #pragma unroll
-            for (int sg = 0; sg < 4; ++sg) {
-                if (32 * sg + 31 <= k) continue;
-                float4 pn = pb[par][8 * sg], vn = vb[par][8 * sg];
+            for (int sg = 0; sg < 8; ++sg) {
+                if (16 * sg + 15 <= k) continue;
+                float4 pn = pb[par][4 * sg], vn = vb[par][4 * sg];
 #pragma unroll
-                for (int j = 8 * sg; j < 8 * sg + 8; ++j) {  // columns 4j .. 4j + 3
+                for (int j = 4 * sg; j < 4 * sg + 4; ++j) {  // columns 4j .. 4j + 3
                     const float4 p = pn, v = vn;
-                    if (j + 1 < 8 * sg + 8) {
+                    if (j + 1 < 4 * sg + 4) {
                         pn = pb[par][j + 1];
                         vn = vb[par][j + 1];
                     }
