@@ -442,7 +442,7 @@ __global__ __launch_bounds__(64) void qr_chain_kernel(const float *__restrict__ 
 // of the workgroup calls it (it holds barriers); a thread with r >= 128 holds
 // no row and only stages.
 __device__ __forceinline__ void form_q_row(float (&y)[kD], const float *__restrict__ hv, int r, int tid,
-                                           float4 (*hb)[8][kD / 4], float *beta) {
+                                           float4 (*hb)[8][kD / 4], float *beta, float (*gp)[4]) {
 #pragma unroll
     for (int j = 0; j < kD; ++j) y[j] = j == r ? 1.f : 0.f;
     if (tid < kRefl) beta[tid] = hv[kBetaRow * kD + tid];
@@ -459,6 +459,25 @@ __device__ __forceinline__ void form_q_row(float (&y)[kD], const float *__restri
         if (stager) {
             hb[c & 1][rr][cc] = a0;
             hb[c & 1][rr][cc + 1] = a1;
+            // v_k . v_k+1 for the group's pairs (k = 8c + 2p): the stagers of
+            // reflectors 2p and 2p + 1 hold the same entries 16 lanes apart;
+            // products, then the sum over the 16 lanes of a row by DPP
+            const float o[8] = {__shfl_xor(a0.x, 16), __shfl_xor(a0.y, 16), __shfl_xor(a0.z, 16),
+                                __shfl_xor(a0.w, 16), __shfl_xor(a1.x, 16), __shfl_xor(a1.y, 16),
+                                __shfl_xor(a1.z, 16), __shfl_xor(a1.w, 16)};
+            float g = a0.x * o[0];
+            g = fmaf(a0.y, o[1], g);
+            g = fmaf(a0.z, o[2], g);
+            g = fmaf(a0.w, o[3], g);
+            g = fmaf(a1.x, o[4], g);
+            g = fmaf(a1.y, o[5], g);
+            g = fmaf(a1.z, o[6], g);
+            g = fmaf(a1.w, o[7], g);
+            g = dpp_add<0xB1, 0xf>(g);   // quad_perm [1, 0, 3, 2]
+            g = dpp_add<0x4E, 0xf>(g);   // quad_perm [2, 3, 0, 1]
+            g = dpp_add<0x124, 0xf>(g);  // row_ror:4
+            g = dpp_add<0x128, 0xf>(g);  // row_ror:8: the row's sum in every lane
+            if ((tid & 31) == 0) gp[c & 1][(tid >> 5) & 3] = g;
         }
         __syncthreads();
         if (stager && c + 1 < kD / 8) {
@@ -468,16 +487,20 @@ __device__ __forceinline__ void form_q_row(float (&y)[kD], const float *__restri
             a1 = in ? src[k * (kD / 4) + cc + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         if (r >= kD) continue;  // uniform: a wave without rows
+        // two reflectors at a time: with t = y.v_k and t' = y.v_k+1,
+        // y H_k H_k+1 = y - s v_k - s' v_k+1, s = beta_k t,
+        // s' = beta_k+1 (t' - s v_k.v_k+1): one pass of dots and one of
+        // updates for the pair (v_k+1 vanishes where v_k does)
 #pragma unroll 1
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 8; i += 2) {
             const int k = 8 * c + i;
             if (k >= kRefl) break;
-            const float4 *v = hb[c & 1][i];
-            float t0 = 0.f, t1 = 0.f;
+            const float4 *v = hb[c & 1][i], *w = hb[c & 1][i + 1];
+            float t0 = 0.f, t1 = 0.f, q0 = 0.f, q1 = 0.f;
 #pragma unroll
             for (int j = 0; j < kD; j += 8) {
                 if (j + 7 <= k) continue;
-                const float4 u0 = v[j / 4], u1 = v[j / 4 + 1];
+                const float4 u0 = v[j / 4], u1 = v[j / 4 + 1], w0 = w[j / 4], w1 = w[j / 4 + 1];
                 t0 = fmaf(y[j], u0.x, t0);
                 t1 = fmaf(y[j + 1], u0.y, t1);
                 t0 = fmaf(y[j + 2], u0.z, t0);
@@ -486,20 +509,29 @@ __device__ __forceinline__ void form_q_row(float (&y)[kD], const float *__restri
                 t1 = fmaf(y[j + 5], u1.y, t1);
                 t0 = fmaf(y[j + 6], u1.z, t0);
                 t1 = fmaf(y[j + 7], u1.w, t1);
+                q0 = fmaf(y[j], w0.x, q0);
+                q1 = fmaf(y[j + 1], w0.y, q1);
+                q0 = fmaf(y[j + 2], w0.z, q0);
+                q1 = fmaf(y[j + 3], w0.w, q1);
+                q0 = fmaf(y[j + 4], w1.x, q0);
+                q1 = fmaf(y[j + 5], w1.y, q1);
+                q0 = fmaf(y[j + 6], w1.z, q0);
+                q1 = fmaf(y[j + 7], w1.w, q1);
             }
             const float t = (t0 + t1) * beta[k];
+            const float tn = fmaf(-t, gp[c & 1][i >> 1], q0 + q1) * beta[k + 1];
 #pragma unroll
             for (int j = 0; j < kD; j += 8) {
                 if (j + 7 <= k) continue;
-                const float4 u0 = v[j / 4], u1 = v[j / 4 + 1];
-                y[j] = fmaf(-t, u0.x, y[j]);
-                y[j + 1] = fmaf(-t, u0.y, y[j + 1]);
-                y[j + 2] = fmaf(-t, u0.z, y[j + 2]);
-                y[j + 3] = fmaf(-t, u0.w, y[j + 3]);
-                y[j + 4] = fmaf(-t, u1.x, y[j + 4]);
-                y[j + 5] = fmaf(-t, u1.y, y[j + 5]);
-                y[j + 6] = fmaf(-t, u1.z, y[j + 6]);
-                y[j + 7] = fmaf(-t, u1.w, y[j + 7]);
+                const float4 u0 = v[j / 4], u1 = v[j / 4 + 1], w0 = w[j / 4], w1 = w[j / 4 + 1];
+                y[j] = fmaf(-t, u0.x, fmaf(-tn, w0.x, y[j]));
+                y[j + 1] = fmaf(-t, u0.y, fmaf(-tn, w0.y, y[j + 1]));
+                y[j + 2] = fmaf(-t, u0.z, fmaf(-tn, w0.z, y[j + 2]));
+                y[j + 3] = fmaf(-t, u0.w, fmaf(-tn, w0.w, y[j + 3]));
+                y[j + 4] = fmaf(-t, u1.x, fmaf(-tn, w1.x, y[j + 4]));
+                y[j + 5] = fmaf(-t, u1.y, fmaf(-tn, w1.y, y[j + 5]));
+                y[j + 6] = fmaf(-t, u1.z, fmaf(-tn, w1.z, y[j + 6]));
+                y[j + 7] = fmaf(-t, u1.w, fmaf(-tn, w1.w, y[j + 7]));
             }
         }
     }
@@ -519,7 +551,7 @@ __device__ __forceinline__ void rotate_pair(float &y0, float &y1, float c, float
 // workgroup's first wave (LDS DMA, kAhead steps ahead of their use), then
 // applied by every thread to its row with the rotation index unrolled, so that
 // each row entry stays at a fixed register.
-__global__ __launch_bounds__(kThreads) void qr_apply_kernel(const float *__restrict__ gpart, int splits,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void qr_apply_kernel(const float *__restrict__ gpart, int splits,
                                                            const uint8_t *__restrict__ stream,
                                                            const int32_t *__restrict__ counts,
                                                            float *__restrict__ vt) {
@@ -537,7 +569,8 @@ __global__ __launch_bounds__(kThreads) void qr_apply_kernel(const float *__restr
     for (int t = r; t < S; t += kThreads) hs[t] = hdr[t];
 
     float y[kD];
-    form_q_row(y, hv, r, r, hb, beta);  // its barriers make hs visible
+    __shared__ float gpair[2][4];
+    form_q_row(y, hv, r, r, hb, beta, gpair);  // its barriers make hs visible
 
     // Step t's rotations sit at rot[pos_t ..] and its rows in hs[t].  Wave 0
     // copies each step into ring slot t % kRing by LDS DMA kAhead steps ahead of
